@@ -1,0 +1,226 @@
+/*
+ * leyline.h - C ABI of the MI355X (gfx950) splice / evict library for a paged
+ * MLA KV cache.
+ *
+ * The operations come from two pages:
+ *   [Leyline]    "Leyline: KV Cache Directives for Agentic Inference"
+ *                (gist.science summary of paper 2606.01065);
+ *   [KV-streams] "KV-streams" (onedev.kr summary of paper 273).
+ *
+ * Cache layout (the MLA split of [Leyline] section 2.2 into the position-free
+ * latent K_nope / V and the RoPE band K_pe).  One token of one layer is a row
+ * of kv_lora_rank + rope_dim bf16 values: c_kv[0..511] then k_pe[0..63],
+ * 1152 bytes.  Each layer has its own pool, an array
+ * [num_pages][page_size][row] of bf16 in device memory.  A sequence owns a
+ * list of physical pages (its page table), shared by every layer: logical row
+ * j of the sequence lives at page table[j / page_size], offset j % page_size.
+ *
+ * Ownership.  Every device buffer named below (layer pools, page-table array,
+ * stub rows, keep masks) belongs to the caller and must stay valid until the
+ * stream work of the call that uses it has finished (pools and the page-table
+ * array: until ll_pool_destroy).  The library owns its host bookkeeping and a
+ * few small device and pinned host staging buffers.
+ *
+ * Streams.  `stream` is a hipStream_t passed as void* (NULL: the null stream).
+ * Each call enqueues its device work on that stream and returns; the work of a
+ * call is ordered after the work of the previous call on the same pool, also
+ * across streams.  kv_evict_compact waits once for a small device-to-host
+ * copy; no other call waits for the device.  A pool is not thread-safe.
+ *
+ * Errors.  Every function returns an ll_status.  All checks run before any
+ * state changes, so a call that returns LL_EINVAL, LL_ERANGE, LL_ENOMEM or
+ * LL_EUNSUPPORTED leaves the pool exactly as it was.  A HIP failure after
+ * state has changed returns LL_EDEVICE and poisons the pool: every later call
+ * on it returns LL_EPOISONED.  ll_last_error() gives a message for the
+ * calling thread's last failure.
+ *
+ * Page plan.  When a call rewrites a sequence, new logical page q reuses the
+ * old physical page of logical page p iff every live row of q comes from old
+ * page p at the same in-page offset; every other new page is fresh and takes
+ * the lowest-numbered free page, in order of (position in the batch, q), from
+ * the free set as it was when the call began; old pages that are not reused
+ * return to the free set after the call.  Rows beyond a sequence's length and
+ * rows of free pages hold unspecified values.
+ */
+#ifndef LEYLINE_H
+#define LEYLINE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LL_OK = 0,
+  LL_EINVAL = -1,       /* malformed request (bad span, unknown sequence, ...) */
+  LL_ERANGE = -2,       /* a sequence would outgrow its page-table row */
+  LL_ENOMEM = -3,       /* not enough free pages (or host memory) */
+  LL_EUNSUPPORTED = -4, /* reserved mode or unsupported shape */
+  LL_EDEVICE = -5,      /* a HIP call failed */
+  LL_EPOISONED = -6     /* an earlier device failure left the pool unusable */
+} ll_status;
+
+/* Directive modes, [Leyline] section 2.1.  PIN, DECAY and SCRATCH are the
+ * verbs that section 5 names for future work: reserved, LL_EUNSUPPORTED. */
+enum { LL_AMORTIZE = 0, LL_FORGET = 1, LL_PIN = 2, LL_DECAY = 3, LL_SCRATCH = 4 };
+
+/* RoPE pair layout of k_pe: interleaved pairs (2j, 2j+1), or half-split
+ * pairs (j, j + rope_dim/2). */
+enum { LL_ROPE_INTERLEAVED = 0, LL_ROPE_HALF = 1 };
+
+typedef struct ll_pool ll_pool;
+
+typedef struct {
+  int32_t num_layers;        /* >= 1 */
+  int32_t page_size;         /* rows per page: a power of two, 1 .. 256 */
+  int32_t num_pages;         /* physical pages per layer pool */
+  int32_t max_seqs;          /* page-table rows */
+  int32_t max_pages_per_seq; /* page-table columns */
+  int32_t kv_lora_rank;      /* c_kv width: must be 512 */
+  int32_t rope_dim;          /* k_pe width: must be 64 */
+  int32_t rope_pairing;      /* LL_ROPE_INTERLEAVED or LL_ROPE_HALF */
+  double rope_base;          /* theta_j = rope_base^(-2j/rope_dim), e.g. 10000 */
+  void* const* layer_base;   /* host array [num_layers] of device pointers, each
+                                16-byte aligned, to [num_pages][page_size][row] bf16 */
+  int32_t* page_table;       /* device int32 [max_seqs][max_pages_per_seq]; the
+                                library writes row s for sequence s */
+  int32_t device;            /* HIP device ordinal that holds all of the above */
+} ll_pool_desc;
+
+/* D = (s_start, s_end, R, m) for one sequence, [Leyline] section 2.1. */
+typedef struct {
+  int32_t seq_id;
+  int32_t mode;              /* LL_AMORTIZE or LL_FORGET */
+  int64_t s_start;           /* span [s_start, s_end), 0-based logical rows,
+                                0 <= s_start <= s_end <= length */
+  int64_t s_end;
+  int64_t r_len;             /* |R| >= 0 stub rows */
+  const void* r_rows;        /* device bf16 [num_layers][r_len][row], rows already
+                                prefilled at their final positions; NULL iff r_len == 0;
+                                16-byte aligned.  Ignored by LL_FORGET. */
+  int64_t r_layer_stride_bytes; /* bytes between layers of r_rows; 0 means
+                                   r_len * 1152; a multiple of 16 otherwise */
+} ll_directive;
+
+/* What the last splice / evict / reindex call on a pool did. */
+typedef struct {
+  int64_t alg_bytes;            /* row bytes the call must move, all layers:
+                                   2*1152 per live row of a fresh page plus
+                                   2*128 per row rotated in place */
+  int64_t rows_moved;           /* live rows written to fresh pages (per layer) */
+  int64_t rows_rotated_inplace; /* downstream rows of reused pages (per layer) */
+  int64_t fresh_pages;
+  int64_t freed_pages;
+  int64_t table_entries;        /* page-table entries written */
+} ll_plan_stats;
+
+/* Create a pool over caller-owned device memory.  Checks the descriptor,
+ * copies the layer pointer array to the device and allocates staging.  All
+ * pages start free and no sequence exists.  Errors: LL_EINVAL (bad field or
+ * NULL pointer), LL_EUNSUPPORTED (row shape other than 512 + 64),
+ * LL_EDEVICE. */
+ll_status ll_pool_create(const ll_pool_desc* desc, ll_pool** out);
+
+/* Wait for the pool's device work and free what the library allocated.  The
+ * caller's buffers are not touched.  NULL is ignored. */
+void ll_pool_destroy(ll_pool* pool);
+
+/* New sequence of n_tokens >= 0 rows: the lowest free sequence id and the
+ * ceil(n_tokens / page_size) lowest free pages; next position = n_tokens.
+ * Row contents are the caller's to write (prefill).  Errors: LL_EINVAL,
+ * LL_ERANGE, LL_ENOMEM (no free id or pages). */
+ll_status ll_seq_alloc(ll_pool* pool, int64_t n_tokens, int32_t* seq_id_out, void* stream);
+
+/* Give sequence seq_id (new or existing) an explicit page table: `pages` is a
+ * host array of ceil(n_tokens / page_size) distinct physical pages, each free
+ * or already owned by seq_id.  Pages the sequence held and no longer lists are
+ * freed; next position = n_tokens.  Errors: LL_EINVAL, LL_ERANGE. */
+ll_status ll_seq_set_pages(ll_pool* pool, int32_t seq_id, const int32_t* pages,
+                           int64_t n_tokens, void* stream);
+
+/* Release a sequence and all of its pages.  Errors: LL_EINVAL. */
+ll_status ll_seq_free(ll_pool* pool, int32_t seq_id);
+
+/* Host copy of a sequence's state: length, next RoPE position and up to `cap`
+ * page-table entries (pages_out may be NULL when cap == 0); *n_pages_out gets
+ * the page count.  Errors: LL_EINVAL. */
+ll_status ll_seq_get(const ll_pool* pool, int32_t seq_id, int64_t* len, int64_t* next_position,
+                     int32_t* pages_out, int32_t cap, int32_t* n_pages_out);
+
+/* Number of free pages. */
+ll_status ll_pool_free_pages(const ll_pool* pool, int64_t* n_free);
+
+/* Apply n directives, at most one per sequence ([Leyline] sections 2.1-2.3).
+ *
+ * LL_AMORTIZE: the sequence becomes old[0, s_start) ++ R ++ old[s_end, n),
+ * n' = n + Delta with Delta = r_len - (s_end - s_start) (section 2.2).
+ * Prefix rows and the R rows are copied bit-exactly.  Every downstream row
+ * keeps its c_kv bit-exactly and gets k_pe_new = R(Delta) k_pe: each pair
+ * (x, y) turns by the angle Delta*theta_j, with cos/sin evaluated in float64
+ * and rounded to float32, then x' = x*c - y*s and y' = x*s + y*c in float32
+ * (no fused multiply-add) and rounded to bf16, nearest-even.  The next
+ * position moves by Delta.
+ * LL_FORGET: the sequence is cut to its first s_start rows (the caller then
+ * re-prefills, section 2.1); the next position moves back by n - s_start.
+ *
+ * Fresh pages, page-table row updates and the rows are written by one kernel
+ * launch after one host-to-device copy.  n == 0 is a no-op.  Errors:
+ * LL_EINVAL (bad span, unknown or repeated sequence, r_rows NULL with
+ * r_len > 0, misaligned pointer or stride), LL_EUNSUPPORTED (reserved mode),
+ * LL_ERANGE (n' exceeds max_pages_per_seq pages), LL_ENOMEM (too few free
+ * pages), LL_EDEVICE. */
+ll_status leyline_splice(ll_pool* pool, const ll_directive* dirs, int32_t n, void* stream);
+
+/* KV-streams eviction ([KV-streams] "how it works"): for each of the n
+ * sequences seq_ids[i], keep exactly the rows whose keep byte is nonzero, in
+ * order, unchanged (no rotation, no position reset: the next position stays).
+ * keep_dev is a device uint8 buffer; sequence i's mask is its length-many
+ * bytes starting at keep_dev + keep_offsets[i] (keep_offsets is a host
+ * array).  A device prefix scan gives each kept row its new index; rows move
+ * only where a new page cannot reuse an old one (at page size 1 none move).
+ * Waits once for a small device-to-host copy of the per-page plan inputs.
+ * Errors: LL_EINVAL, LL_ENOMEM, LL_EDEVICE. */
+ll_status kv_evict_compact(ll_pool* pool, const int32_t* seq_ids, int32_t n,
+                           const uint8_t* keep_dev, const int64_t* keep_offsets, void* stream);
+
+/* Page-table re-index: page-granular eviction without row moves
+ * ([Leyline] section 3, edits decomposed into block-level operations;
+ * [KV-streams] "how it works").  keep_pages is a host array of n_keep strictly
+ * increasing logical pages of the sequence; the new table lists their physical
+ * pages in that order and the new length is the sum of their live rows; a
+ * partial last page may only be kept last.  Other pages are freed; the next
+ * position stays.  Errors: LL_EINVAL. */
+ll_status ll_ptable_reindex(ll_pool* pool, int32_t seq_id, const int32_t* keep_pages,
+                            int32_t n_keep, void* stream);
+
+/* The float32 cos/sin table of the delta-rotation ([Leyline] section 2.2):
+ * for j < rope_dim/2, the float64 angle delta * base^(-2j/rope_dim), its
+ * float64 cos and sin, each rounded to float32.  cos_out and sin_out are host
+ * arrays of rope_dim/2 floats.  Errors: LL_EINVAL. */
+ll_status ll_rope_delta_table(double base, int32_t rope_dim, int64_t delta,
+                              float* cos_out, float* sin_out);
+
+/* Counters of the last splice / evict / reindex call.  Errors: LL_EINVAL. */
+ll_status ll_last_plan_stats(const ll_pool* pool, ll_plan_stats* out);
+
+/* Kernel timing: while enabled, HIP events bracket every launch of the
+ * row-moving kernel (kernel 0) and of the keep-mask scan (kernel 1).
+ * ll_profile_read waits for the recorded events, returns the launch count,
+ * the summed milliseconds and the summed algorithmic bytes of `kernel`, and
+ * clears its record.  Errors: LL_EINVAL, LL_EDEVICE. */
+ll_status ll_pool_set_profiling(ll_pool* pool, int32_t enable);
+ll_status ll_profile_read(ll_pool* pool, int32_t kernel, int64_t* launches, double* total_ms,
+                          int64_t* total_bytes);
+
+/* Message for the calling thread's last failure ("" if none). */
+const char* ll_last_error(void);
+
+/* Name of a status code. */
+const char* ll_status_str(ll_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LEYLINE_H */

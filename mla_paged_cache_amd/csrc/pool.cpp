@@ -1,0 +1,1025 @@
+// Host side of the splice / evict library: the paged pool, the lowest-free
+// page allocator, directive validation, the page planner and the C ABI
+// (include/leyline.h).  Device work goes through the launchers in
+// kernels.hip; every call enqueues it on the caller's stream.
+//
+// Operations: "Leyline: KV Cache Directives for Agentic Inference" (sections
+// 2.1 directive and modes, 2.2 shift and delta-rotation, 2.3 serving steps);
+// "KV-streams" ("how it works": in-engine eviction with kept entries
+// unchanged; "assumptions and limits": 16-token and 1-token blocks).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/leyline.h"
+#include "leyline_internal.h"
+
+namespace {
+
+thread_local std::string g_error;
+
+ll_status fail(ll_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return s;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Lowest-free-first page allocator over a bitmap (bit set = free).
+class FreePages {
+ public:
+  void init(int64_t n) {
+    n_ = n;
+    words_.assign(static_cast<size_t>(ceil_div(n, 64)), ~0ull);
+    if (n % 64) words_.back() = (1ull << (n % 64)) - 1;
+    count_ = n;
+    hint_ = 0;
+  }
+  int64_t count() const { return count_; }
+  bool is_free(int64_t p) const { return (words_[p >> 6] >> (p & 63)) & 1ull; }
+  void take(int64_t p) {
+    words_[p >> 6] &= ~(1ull << (p & 63));
+    --count_;
+  }
+  void give(int64_t p) {
+    words_[p >> 6] |= 1ull << (p & 63);
+    ++count_;
+    hint_ = std::min<int64_t>(hint_, p >> 6);
+  }
+  // The k lowest free pages, in increasing order (not taken).
+  void lowest(int64_t k, std::vector<int32_t>& out) const {
+    out.clear();
+    out.reserve(static_cast<size_t>(k));
+    for (size_t w = static_cast<size_t>(hint_); w < words_.size() && static_cast<int64_t>(out.size()) < k; ++w) {
+      uint64_t bits = words_[w];
+      while (bits && static_cast<int64_t>(out.size()) < k) {
+        const int b = __builtin_ctzll(bits);
+        out.push_back(static_cast<int32_t>(w * 64 + b));
+        bits &= bits - 1;
+      }
+    }
+  }
+  void advance_hint() {
+    while (hint_ < static_cast<int64_t>(words_.size()) && words_[hint_] == 0) ++hint_;
+  }
+
+ private:
+  int64_t n_ = 0, count_ = 0, hint_ = 0;
+  std::vector<uint64_t> words_;
+};
+
+struct SeqState {
+  bool used = false;
+  int64_t len = 0;
+  int64_t next_pos = 0;
+  std::vector<int32_t> pages;
+};
+
+// Pinned host buffer + device buffer of the same size, filled on the host and
+// sent with one copy.  `done` marks when the device has finished with it.
+struct Staging {
+  char* host = nullptr;
+  char* dev = nullptr;
+  size_t cap = 0;
+  size_t used = 0;
+  hipEvent_t done = nullptr;
+  bool pending = false;
+};
+
+struct ProfRec {
+  hipEvent_t start, stop;
+  int64_t bytes;
+};
+
+// Current-device guard.
+class DeviceGuard {
+ public:
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&old_) != hipSuccess) old_ = -1;
+    if (old_ != dev) ok_ = hipSetDevice(dev) == hipSuccess;
+  }
+  ~DeviceGuard() {
+    int cur = -1;
+    if (old_ >= 0 && hipGetDevice(&cur) == hipSuccess && cur != old_) (void)hipSetDevice(old_);
+  }
+  bool ok() const { return ok_; }
+
+ private:
+  int old_ = -1;
+  bool ok_ = true;
+};
+
+int env_int(const char* name, int dflt) {
+  const char* v = std::getenv(name);
+  return v && *v ? std::atoi(v) : dflt;
+}
+
+}  // namespace
+
+struct ll_pool {
+  ll_pool_desc desc{};
+  int page_shift = 0;
+  int64_t P = 1;
+  std::vector<void*> layer_ptrs;
+  void** d_layers = nullptr;
+  std::vector<SeqState> seqs;
+  FreePages free;
+  Staging stage[2];
+  int stage_next = 0;
+  // eviction scratch: device [counts | reuse | src_of_dst], pinned readback
+  char* d_scratch = nullptr;
+  size_t scratch_cap = 0;
+  char* h_readback = nullptr;
+  size_t readback_cap = 0;
+  hipEvent_t readback_ev = nullptr;
+  hipEvent_t last_done = nullptr;  // end of the last call's device work
+  bool poisoned = false;
+  ll_plan_stats last{};
+  bool profiling = false;
+  std::vector<ProfRec> prof[2];
+  std::vector<hipEvent_t> spare_events;
+  int layers_per_block = 1;
+};
+
+namespace {
+
+ll_status device_fail(ll_pool* p, hipError_t e, const char* what) {
+  p->poisoned = true;
+  return fail(LL_EDEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+ll_status check_pool(const ll_pool* p) {
+  if (!p) return fail(LL_EINVAL, "pool is NULL");
+  if (p->poisoned) return fail(LL_EPOISONED, "pool is poisoned by an earlier device failure");
+  return LL_OK;
+}
+
+hipEvent_t take_event(ll_pool* p) {
+  if (!p->spare_events.empty()) {
+    hipEvent_t e = p->spare_events.back();
+    p->spare_events.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Reserve `bytes` of a staging slot: wait until the device is done with its
+// last use, grow if needed.  Returns the slot.
+ll_status stage_acquire(ll_pool* p, size_t bytes, Staging** out) {
+  Staging& s = p->stage[p->stage_next];
+  p->stage_next ^= 1;
+  if (s.pending) {
+    hipError_t e = hipEventSynchronize(s.done);
+    if (e != hipSuccess) return device_fail(p, e, "hipEventSynchronize(staging)");
+    s.pending = false;
+  }
+  if (bytes > s.cap) {
+    size_t cap = std::max<size_t>(align_up(bytes, 1 << 20), 2 * s.cap);
+    if (s.host) (void)hipHostFree(s.host);
+    if (s.dev) (void)hipFree(s.dev);
+    s.host = nullptr;
+    s.dev = nullptr;
+    s.cap = 0;
+    if (hipHostMalloc(reinterpret_cast<void**>(&s.host), cap, hipHostMallocDefault) != hipSuccess ||
+        hipMalloc(reinterpret_cast<void**>(&s.dev), cap) != hipSuccess)
+      return fail(LL_ENOMEM, "cannot allocate %zu bytes of staging", cap);
+    s.cap = cap;
+  }
+  s.used = 0;
+  *out = &s;
+  return LL_OK;
+}
+
+// Append `bytes` to the staging slot; returns the offset.
+size_t stage_put(Staging* s, const void* src, size_t bytes) {
+  const size_t off = align_up(s->used, 256);
+  if (bytes) std::memcpy(s->host + off, src, bytes);
+  s->used = off + bytes;
+  return off;
+}
+
+size_t stage_bytes_for(std::initializer_list<size_t> parts) {
+  size_t t = 0;
+  for (size_t x : parts) t = align_up(t, 256) + x;
+  return t + 256;
+}
+
+// Order this call after the previous call on the pool (any stream).
+ll_status begin_call(ll_pool* p, hipStream_t st) {
+  if (p->last_done) {
+    hipError_t e = hipStreamWaitEvent(st, p->last_done, 0);
+    if (e != hipSuccess) return device_fail(p, e, "hipStreamWaitEvent");
+  }
+  return LL_OK;
+}
+
+ll_status end_call(ll_pool* p, Staging* s, hipStream_t st) {
+  hipError_t e = hipEventRecord(s->done, st);
+  if (e != hipSuccess) return device_fail(p, e, "hipEventRecord");
+  s->pending = true;
+  p->last_done = s->done;
+  return LL_OK;
+}
+
+ll_status upload(ll_pool* p, Staging* s, hipStream_t st) {
+  if (s->used == 0) return LL_OK;
+  hipError_t e = hipMemcpyAsync(s->dev, s->host, s->used, hipMemcpyHostToDevice, st);
+  if (e != hipSuccess) return device_fail(p, e, "hipMemcpyAsync(H2D staging)");
+  return LL_OK;
+}
+
+void rope_table(double base, int rope_dim, int64_t delta, float* c, float* s) {
+  for (int j = 0; j < rope_dim / 2; ++j) {
+    const double theta = std::pow(base, -2.0 * j / rope_dim);
+    const double ang = static_cast<double>(delta) * theta;
+    c[j] = static_cast<float>(std::cos(ang));
+    s[j] = static_cast<float>(std::sin(ang));
+  }
+}
+
+// Page-table rewrite of whole rows, via the packed table array in staging.
+struct TablePlan {
+  std::vector<ll::TableWrite> writes;
+  std::vector<int32_t> packed;
+  void add(int32_t seq, const std::vector<int32_t>& t) {
+    ll::TableWrite w{};
+    w.src_off = static_cast<int64_t>(packed.size());
+    w.seq = seq;
+    w.count = static_cast<int32_t>(t.size());
+    packed.insert(packed.end(), t.begin(), t.end());
+    writes.push_back(w);
+  }
+};
+
+// Upload and launch a stand-alone page-table rewrite on `st`.
+ll_status write_tables(ll_pool* p, const TablePlan& tp, hipStream_t st) {
+  ll_status rc = begin_call(p, st);
+  if (rc) return rc;
+  Staging* s = nullptr;
+  rc = stage_acquire(p, stage_bytes_for({tp.writes.size() * sizeof(ll::TableWrite), tp.packed.size() * 4}), &s);
+  if (rc) return rc;
+  const size_t o_w = stage_put(s, tp.writes.data(), tp.writes.size() * sizeof(ll::TableWrite));
+  const size_t o_t = stage_put(s, tp.packed.data(), tp.packed.size() * 4);
+  if ((rc = upload(p, s, st))) return rc;
+  ll::TableLaunch a{};
+  a.twrites = reinterpret_cast<const ll::TableWrite*>(s->dev + o_w);
+  a.tables = reinterpret_cast<const int32_t*>(s->dev + o_t);
+  a.n_twrites = static_cast<int32_t>(tp.writes.size());
+  a.max_pages_per_seq = p->desc.max_pages_per_seq;
+  a.page_table = p->desc.page_table;
+  hipError_t e = ll::launch_table_write(a, st);
+  if (e != hipSuccess) return device_fail(p, e, "table_write_kernel launch");
+  return end_call(p, s, st);
+}
+
+ll_status prof_begin(ll_pool* p, int kernel, hipStream_t st, ProfRec* rec) {
+  rec->start = take_event(p);
+  rec->stop = take_event(p);
+  if (!rec->start || !rec->stop) return fail(LL_EDEVICE, "hipEventCreate failed");
+  (void)kernel;
+  hipError_t e = hipEventRecord(rec->start, st);
+  if (e != hipSuccess) return device_fail(p, e, "hipEventRecord(profile)");
+  return LL_OK;
+}
+
+ll_status prof_end(ll_pool* p, int kernel, hipStream_t st, ProfRec* rec) {
+  hipError_t e = hipEventRecord(rec->stop, st);
+  if (e != hipSuccess) return device_fail(p, e, "hipEventRecord(profile)");
+  p->prof[kernel].push_back(*rec);
+  return LL_OK;
+}
+
+// ------------------------------------------------------------------ splice --
+
+struct SplicePlan {
+  int32_t seq = 0;
+  int32_t mode = LL_AMORTIZE;
+  int64_t n_old = 0, n_new = 0, delta = 0, next_pos = 0;
+  std::vector<int32_t> reuse;     // per new page: old logical page, or -1 (fresh)
+  std::vector<char> inplace;      // per new page: rotate k_pe in place
+  int64_t fresh = 0;
+};
+
+// The page plan of one directive in closed form (no per-row loop):
+// a new page reuses an old one iff all its live rows are old rows of one old
+// page at unchanged offsets.
+void plan_splice(const ll_pool* p, const ll_directive& d, const SeqState& s, SplicePlan* out) {
+  const int64_t P = p->P;
+  out->seq = d.seq_id;
+  out->mode = d.mode;
+  out->n_old = s.len;
+  if (d.mode == LL_FORGET) {
+    out->n_new = d.s_start;
+    out->delta = 0;
+    out->next_pos = s.next_pos - (s.len - d.s_start);
+  } else {
+    out->delta = d.r_len - (d.s_end - d.s_start);
+    out->n_new = s.len + out->delta;
+    out->next_pos = s.next_pos + out->delta;
+  }
+  const int64_t pages = ceil_div(out->n_new, P);
+  out->reuse.assign(static_cast<size_t>(pages), -1);
+  out->inplace.assign(static_cast<size_t>(pages), 0);
+  out->fresh = 0;
+  const int64_t s0 = d.s_start;
+  const int64_t r = d.mode == LL_FORGET ? 0 : d.r_len;
+  const int64_t delta = out->delta;
+  for (int64_t q = 0; q < pages; ++q) {
+    const int64_t a = q * P, b = std::min(a + P, out->n_new);
+    const bool has_pre = a < s0;
+    const bool has_stub = r > 0 && a < s0 + r && b > s0;
+    const bool has_down = b > s0 + r;
+    int64_t reuse = -1;
+    if (has_stub) {
+      reuse = -1;
+    } else if (has_pre && has_down) {
+      reuse = delta == 0 ? q : -1;  // span and stub both empty
+    } else if (has_pre) {
+      reuse = q;
+    } else {
+      const int64_t src0 = a - delta;  // first source row, page-aligned iff delta % P == 0
+      if ((src0 & (P - 1)) == 0) reuse = src0 / P;
+    }
+    out->reuse[q] = static_cast<int32_t>(reuse);
+    if (reuse < 0) ++out->fresh;
+    else if (has_down && delta != 0 && d.mode == LL_AMORTIZE) out->inplace[q] = 1;
+  }
+}
+
+ll_status validate_directives(const ll_pool* p, const ll_directive* dirs, int32_t n) {
+  std::vector<char> seen(static_cast<size_t>(p->desc.max_seqs), 0);
+  for (int32_t i = 0; i < n; ++i) {
+    const ll_directive& d = dirs[i];
+    if (d.mode == LL_PIN || d.mode == LL_DECAY || d.mode == LL_SCRATCH)
+      return fail(LL_EUNSUPPORTED, "directive %d: mode %d is reserved", i, d.mode);
+    if (d.mode != LL_AMORTIZE && d.mode != LL_FORGET) return fail(LL_EINVAL, "directive %d: unknown mode %d", i, d.mode);
+    if (d.seq_id < 0 || d.seq_id >= p->desc.max_seqs || !p->seqs[d.seq_id].used)
+      return fail(LL_EINVAL, "directive %d: unknown sequence %d", i, d.seq_id);
+    if (seen[d.seq_id]) return fail(LL_EINVAL, "directive %d: sequence %d appears twice", i, d.seq_id);
+    seen[d.seq_id] = 1;
+    const int64_t len = p->seqs[d.seq_id].len;
+    if (d.s_start < 0 || d.s_start > d.s_end || d.s_end > len)
+      return fail(LL_EINVAL, "directive %d: span [%lld, %lld) outside [0, %lld]", i, (long long)d.s_start,
+                  (long long)d.s_end, (long long)len);
+    if (d.mode == LL_FORGET) continue;
+    if (d.r_len < 0) return fail(LL_EINVAL, "directive %d: r_len < 0", i);
+    if ((d.r_len > 0) != (d.r_rows != nullptr))
+      return fail(LL_EINVAL, "directive %d: r_rows must be given iff r_len > 0", i);
+    if (d.r_rows && (reinterpret_cast<uintptr_t>(d.r_rows) & 15))
+      return fail(LL_EINVAL, "directive %d: r_rows is not 16-byte aligned", i);
+    if (d.r_layer_stride_bytes < 0 || (d.r_layer_stride_bytes & 15) ||
+        (d.r_layer_stride_bytes && d.r_layer_stride_bytes < d.r_len * ll::kRowBytes && p->desc.num_layers > 1))
+      return fail(LL_EINVAL, "directive %d: bad r_layer_stride_bytes", i);
+    const int64_t n_new = len + d.r_len - (d.s_end - d.s_start);
+    if (ceil_div(n_new, p->P) > p->desc.max_pages_per_seq)
+      return fail(LL_ERANGE, "directive %d: %lld rows exceed the page-table row", i, (long long)n_new);
+  }
+  return LL_OK;
+}
+
+}  // namespace
+
+// =================================================================== C ABI ==
+
+extern "C" {
+
+const char* ll_last_error(void) { return g_error.c_str(); }
+
+const char* ll_status_str(ll_status s) {
+  switch (s) {
+    case LL_OK: return "LL_OK";
+    case LL_EINVAL: return "LL_EINVAL";
+    case LL_ERANGE: return "LL_ERANGE";
+    case LL_ENOMEM: return "LL_ENOMEM";
+    case LL_EUNSUPPORTED: return "LL_EUNSUPPORTED";
+    case LL_EDEVICE: return "LL_EDEVICE";
+    case LL_EPOISONED: return "LL_EPOISONED";
+  }
+  return "unknown";
+}
+
+ll_status ll_rope_delta_table(double base, int32_t rope_dim, int64_t delta, float* cos_out, float* sin_out) {
+  if (!cos_out || !sin_out) return fail(LL_EINVAL, "NULL output");
+  if (rope_dim <= 0 || (rope_dim & 1)) return fail(LL_EINVAL, "rope_dim must be even and positive");
+  if (!(base > 0.0)) return fail(LL_EINVAL, "base must be positive");
+  rope_table(base, rope_dim, delta, cos_out, sin_out);
+  return LL_OK;
+}
+
+ll_status ll_pool_create(const ll_pool_desc* desc, ll_pool** out) {
+  if (!desc || !out) return fail(LL_EINVAL, "NULL argument");
+  *out = nullptr;
+  const ll_pool_desc& d = *desc;
+  if (d.num_layers < 1 || d.num_pages < 1 || d.max_seqs < 1 || d.max_pages_per_seq < 1)
+    return fail(LL_EINVAL, "num_layers, num_pages, max_seqs and max_pages_per_seq must be >= 1");
+  if (d.page_size < 1 || d.page_size > 256 || (d.page_size & (d.page_size - 1)))
+    return fail(LL_EINVAL, "page_size must be a power of two in [1, 256]");
+  if (d.kv_lora_rank != ll::kKvLoraRank || d.rope_dim != ll::kRopeDim)
+    return fail(LL_EUNSUPPORTED, "row shape %d + %d is not supported (512 + 64 only)", d.kv_lora_rank, d.rope_dim);
+  if (d.rope_pairing != LL_ROPE_INTERLEAVED && d.rope_pairing != LL_ROPE_HALF)
+    return fail(LL_EINVAL, "unknown rope_pairing");
+  if (!(d.rope_base > 0.0)) return fail(LL_EINVAL, "rope_base must be positive");
+  if (!d.layer_base || !d.page_table) return fail(LL_EINVAL, "layer_base and page_table are required");
+  for (int i = 0; i < d.num_layers; ++i) {
+    if (!d.layer_base[i]) return fail(LL_EINVAL, "layer_base[%d] is NULL", i);
+    if (reinterpret_cast<uintptr_t>(d.layer_base[i]) & 15) return fail(LL_EINVAL, "layer_base[%d] is not 16-byte aligned", i);
+  }
+  if (static_cast<int64_t>(d.num_pages) * d.page_size >= (int64_t{1} << 31))
+    return fail(LL_EUNSUPPORTED, "more than 2^31 rows per layer");
+  if (d.device < 0) return fail(LL_EINVAL, "device must be >= 0");
+
+  DeviceGuard g(d.device);
+  if (!g.ok()) return fail(LL_EDEVICE, "hipSetDevice(%d) failed", d.device);
+  ll_pool* p = new ll_pool();
+  p->desc = d;
+  p->layer_ptrs.assign(d.layer_base, d.layer_base + d.num_layers);
+  p->desc.layer_base = nullptr;
+  p->P = d.page_size;
+  while ((1 << p->page_shift) < d.page_size) ++p->page_shift;
+  p->seqs.resize(static_cast<size_t>(d.max_seqs));
+  p->free.init(d.num_pages);
+  p->layers_per_block = std::min(4, std::max(1, env_int("LEYLINE_LAYERS_PER_BLOCK", 1)));
+  hipError_t e = hipMalloc(reinterpret_cast<void**>(&p->d_layers), sizeof(void*) * d.num_layers);
+  if (e == hipSuccess)
+    e = hipMemcpy(p->d_layers, p->layer_ptrs.data(), sizeof(void*) * d.num_layers, hipMemcpyHostToDevice);
+  for (int i = 0; i < 2 && e == hipSuccess; ++i) e = hipEventCreateWithFlags(&p->stage[i].done, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&p->readback_ev, hipEventDisableTiming);
+  if (e != hipSuccess) {
+    ll_pool_destroy(p);
+    return fail(LL_EDEVICE, "pool setup: %s", hipGetErrorString(e));
+  }
+  *out = p;
+  return LL_OK;
+}
+
+void ll_pool_destroy(ll_pool* p) {
+  if (!p) return;
+  DeviceGuard g(p->desc.device);
+  if (p->last_done) (void)hipEventSynchronize(p->last_done);
+  for (auto& s : p->stage) {
+    if (s.host) (void)hipHostFree(s.host);
+    if (s.dev) (void)hipFree(s.dev);
+    if (s.done) (void)hipEventDestroy(s.done);
+  }
+  for (auto& v : p->prof)
+    for (auto& r : v) {
+      (void)hipEventDestroy(r.start);
+      (void)hipEventDestroy(r.stop);
+    }
+  for (auto e : p->spare_events) (void)hipEventDestroy(e);
+  if (p->readback_ev) (void)hipEventDestroy(p->readback_ev);
+  if (p->h_readback) (void)hipHostFree(p->h_readback);
+  if (p->d_scratch) (void)hipFree(p->d_scratch);
+  if (p->d_layers) (void)hipFree(p->d_layers);
+  delete p;
+}
+
+ll_status ll_pool_free_pages(const ll_pool* p, int64_t* n_free) {
+  if (!p || !n_free) return fail(LL_EINVAL, "NULL argument");
+  *n_free = p->free.count();
+  return LL_OK;
+}
+
+ll_status ll_seq_get(const ll_pool* p, int32_t seq, int64_t* len, int64_t* next_position, int32_t* pages_out,
+                     int32_t cap, int32_t* n_pages_out) {
+  if (!p) return fail(LL_EINVAL, "pool is NULL");
+  if (seq < 0 || seq >= p->desc.max_seqs || !p->seqs[seq].used) return fail(LL_EINVAL, "unknown sequence %d", seq);
+  if (cap > 0 && !pages_out) return fail(LL_EINVAL, "pages_out is NULL");
+  const SeqState& s = p->seqs[seq];
+  if (len) *len = s.len;
+  if (next_position) *next_position = s.next_pos;
+  if (n_pages_out) *n_pages_out = static_cast<int32_t>(s.pages.size());
+  const int32_t k = std::min<int32_t>(cap, static_cast<int32_t>(s.pages.size()));
+  if (k > 0) std::memcpy(pages_out, s.pages.data(), sizeof(int32_t) * k);
+  return LL_OK;
+}
+
+ll_status ll_seq_alloc(ll_pool* p, int64_t n_tokens, int32_t* seq_id_out, void* stream) {
+  ll_status rc = check_pool(p);
+  if (rc) return rc;
+  if (!seq_id_out || n_tokens < 0) return fail(LL_EINVAL, "bad argument");
+  const int64_t need = ceil_div(n_tokens, p->P);
+  if (need > p->desc.max_pages_per_seq) return fail(LL_ERANGE, "%lld rows exceed the page-table row", (long long)n_tokens);
+  int32_t seq = -1;
+  for (int32_t i = 0; i < p->desc.max_seqs; ++i)
+    if (!p->seqs[i].used) {
+      seq = i;
+      break;
+    }
+  if (seq < 0) return fail(LL_ENOMEM, "no free sequence id");
+  if (need > p->free.count()) return fail(LL_ENOMEM, "need %lld pages, %lld free", (long long)need, (long long)p->free.count());
+  std::vector<int32_t> pages;
+  p->free.lowest(need, pages);
+  DeviceGuard g(p->desc.device);
+  TablePlan tp;
+  tp.add(seq, pages);
+  rc = write_tables(p, tp, static_cast<hipStream_t>(stream));
+  if (rc) return rc;
+  for (int32_t pg : pages) p->free.take(pg);
+  p->free.advance_hint();
+  SeqState& s = p->seqs[seq];
+  s.used = true;
+  s.len = n_tokens;
+  s.next_pos = n_tokens;
+  s.pages = std::move(pages);
+  *seq_id_out = seq;
+  return LL_OK;
+}
+
+ll_status ll_seq_set_pages(ll_pool* p, int32_t seq, const int32_t* pages, int64_t n_tokens, void* stream) {
+  ll_status rc = check_pool(p);
+  if (rc) return rc;
+  if (seq < 0 || seq >= p->desc.max_seqs) return fail(LL_EINVAL, "bad sequence id %d", seq);
+  if (n_tokens < 0) return fail(LL_EINVAL, "n_tokens < 0");
+  const int64_t need = ceil_div(n_tokens, p->P);
+  if (need > p->desc.max_pages_per_seq) return fail(LL_ERANGE, "%lld rows exceed the page-table row", (long long)n_tokens);
+  if (need > 0 && !pages) return fail(LL_EINVAL, "pages is NULL");
+  SeqState& s = p->seqs[seq];
+  std::vector<char> own(static_cast<size_t>(p->desc.num_pages), 0), seen(static_cast<size_t>(p->desc.num_pages), 0);
+  if (s.used)
+    for (int32_t pg : s.pages) own[pg] = 1;
+  for (int64_t i = 0; i < need; ++i) {
+    const int32_t pg = pages[i];
+    if (pg < 0 || pg >= p->desc.num_pages) return fail(LL_EINVAL, "page %d out of range", pg);
+    if (seen[pg]) return fail(LL_EINVAL, "page %d listed twice", pg);
+    seen[pg] = 1;
+    if (!p->free.is_free(pg) && !own[pg]) return fail(LL_EINVAL, "page %d is not free", pg);
+  }
+  std::vector<int32_t> t(pages, pages + need);
+  DeviceGuard g(p->desc.device);
+  TablePlan tp;
+  tp.add(seq, t);
+  rc = write_tables(p, tp, static_cast<hipStream_t>(stream));
+  if (rc) return rc;
+  if (s.used)
+    for (int32_t pg : s.pages)
+      if (!seen[pg]) p->free.give(pg);
+  for (int32_t pg : t)
+    if (!own[pg]) p->free.take(pg);
+  p->free.advance_hint();
+  s.used = true;
+  s.len = n_tokens;
+  s.next_pos = n_tokens;
+  s.pages = std::move(t);
+  return LL_OK;
+}
+
+ll_status ll_seq_free(ll_pool* p, int32_t seq) {
+  ll_status rc = check_pool(p);
+  if (rc) return rc;
+  if (seq < 0 || seq >= p->desc.max_seqs || !p->seqs[seq].used) return fail(LL_EINVAL, "unknown sequence %d", seq);
+  SeqState& s = p->seqs[seq];
+  for (int32_t pg : s.pages) p->free.give(pg);
+  s = SeqState();
+  return LL_OK;
+}
+
+ll_status leyline_splice(ll_pool* p, const ll_directive* dirs, int32_t n, void* stream) {
+  ll_status rc = check_pool(p);
+  if (rc) return rc;
+  if (n < 0 || (n > 0 && !dirs)) return fail(LL_EINVAL, "bad directive array");
+  if (n == 0) return LL_OK;
+  if ((rc = validate_directives(p, dirs, n))) return rc;
+
+  // --- plan (host only, no state change yet)
+  const int64_t P = p->P;
+  std::vector<SplicePlan> plans(static_cast<size_t>(n));
+  int64_t need = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    plan_splice(p, dirs[i], p->seqs[dirs[i].seq_id], &plans[i]);
+    need += plans[i].fresh;
+  }
+  if (need > p->free.count())
+    return fail(LL_ENOMEM, "need %lld fresh pages, %lld free", (long long)need, (long long)p->free.count());
+  std::vector<int32_t> fresh;
+  p->free.lowest(need, fresh);
+
+  std::vector<ll::SpliceDir> ddirs(static_cast<size_t>(n));
+  std::vector<ll::SpliceTask> tasks;
+  TablePlan tp;
+  std::vector<std::vector<int32_t>> new_tables(static_cast<size_t>(n));
+  ll_plan_stats stats{};
+  size_t cursor = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const ll_directive& d = dirs[i];
+    const SplicePlan& pl = plans[i];
+    const SeqState& s = p->seqs[d.seq_id];
+    const std::vector<int32_t>& T = s.pages;
+    const int64_t old_pages = static_cast<int64_t>(T.size());
+    ll::SpliceDir& dd = ddirs[i];
+    std::memset(&dd, 0, sizeof dd);
+    const int64_t r = d.mode == LL_FORGET ? 0 : d.r_len;
+    dd.stub = static_cast<const ll::chunk_t*>(d.mode == LL_FORGET ? nullptr : d.r_rows);
+    const int64_t stride = d.r_layer_stride_bytes ? d.r_layer_stride_bytes : r * ll::kRowBytes;
+    dd.stub_layer_chunks = stride / 16;
+    dd.s_start = d.s_start;
+    dd.r_len = r;
+    dd.delta = pl.delta;
+    dd.n_new = pl.n_new;
+    dd.rotate = (d.mode == LL_AMORTIZE && pl.delta != 0) ? 1 : 0;
+    rope_table(p->desc.rope_base, ll::kRopeDim, pl.delta, dd.cos_, dd.sin_);
+    std::vector<int32_t>& nt = new_tables[i];
+    nt.resize(pl.reuse.size());
+    for (size_t q = 0; q < pl.reuse.size(); ++q) {
+      const int64_t a = static_cast<int64_t>(q) * P, b = std::min(a + P, pl.n_new);
+      if (pl.reuse[q] >= 0) {
+        nt[q] = T[pl.reuse[q]];
+        if (pl.inplace[q]) {
+          ll::SpliceTask t{};
+          t.dir = i;
+          t.q = static_cast<int32_t>(q);
+          t.dst_page = nt[q];
+          t.kind = ll::kRotateInPlace;
+          t.pre_page = t.down_page0 = t.down_page1 = -1;
+          tasks.push_back(t);
+          stats.rows_rotated_inplace += b - a;
+        }
+        continue;
+      }
+      nt[q] = fresh[cursor++];
+      ll::SpliceTask t{};
+      t.dir = i;
+      t.q = static_cast<int32_t>(q);
+      t.dst_page = nt[q];
+      t.kind = ll::kMoveRows;
+      t.pre_page = (a < d.s_start && static_cast<int64_t>(q) < old_pages) ? T[q] : -1;
+      const int64_t jd = std::max(a, d.s_start + r);  // first downstream row of the page
+      t.down_lp0 = -1;
+      t.down_page0 = t.down_page1 = -1;
+      if (jd < b) {
+        const int64_t lp0 = (jd - pl.delta) / P;
+        t.down_lp0 = static_cast<int32_t>(lp0);
+        t.down_page0 = T[lp0];
+        t.down_page1 = lp0 + 1 < old_pages ? T[lp0 + 1] : -1;
+      }
+      tasks.push_back(t);
+      stats.rows_moved += b - a;
+    }
+    tp.add(d.seq_id, nt);
+  }
+  stats.fresh_pages = need;
+  stats.table_entries = static_cast<int64_t>(tp.packed.size());
+  for (int32_t i = 0; i < n; ++i) {
+    const SeqState& s = p->seqs[dirs[i].seq_id];
+    std::vector<char> kept(s.pages.size(), 0);
+    for (int32_t x : plans[i].reuse)
+      if (x >= 0) kept[x] = 1;
+    for (size_t k = 0; k < kept.size(); ++k) stats.freed_pages += kept[k] ? 0 : 1;
+  }
+  const int64_t L = p->desc.num_layers;
+  stats.alg_bytes = L * (2 * ll::kRowBytes * stats.rows_moved + 2 * ll::kRopeDim * 2 * stats.rows_rotated_inplace);
+
+  // --- device work: one upload, one launch
+  DeviceGuard g(p->desc.device);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if ((rc = begin_call(p, st))) return rc;
+  Staging* sg = nullptr;
+  rc = stage_acquire(p, stage_bytes_for({ddirs.size() * sizeof(ll::SpliceDir), tasks.size() * sizeof(ll::SpliceTask),
+                                         tp.writes.size() * sizeof(ll::TableWrite), tp.packed.size() * 4}),
+                     &sg);
+  if (rc) return rc;
+  const size_t o_d = stage_put(sg, ddirs.data(), ddirs.size() * sizeof(ll::SpliceDir));
+  const size_t o_t = stage_put(sg, tasks.data(), tasks.size() * sizeof(ll::SpliceTask));
+  const size_t o_w = stage_put(sg, tp.writes.data(), tp.writes.size() * sizeof(ll::TableWrite));
+  const size_t o_p = stage_put(sg, tp.packed.data(), tp.packed.size() * 4);
+  if ((rc = upload(p, sg, st))) return rc;
+
+  ll::SpliceLaunch a{};
+  a.layers = reinterpret_cast<const ll::chunk_t* const*>(p->d_layers);
+  a.num_layers = p->desc.num_layers;
+  a.page_shift = p->page_shift;
+  a.tasks = reinterpret_cast<const ll::SpliceTask*>(sg->dev + o_t);
+  a.n_tasks = static_cast<int64_t>(tasks.size());
+  a.n_slabs = ceil_div(a.n_tasks * P, ll::kSlabRows);
+  const int lpb = p->layers_per_block;
+  a.n_move_blocks = a.n_slabs * ll::layer_groups(a.num_layers, lpb);
+  a.dirs = reinterpret_cast<const ll::SpliceDir*>(sg->dev + o_d);
+  a.twrites = reinterpret_cast<const ll::TableWrite*>(sg->dev + o_w);
+  a.tables = reinterpret_cast<const int32_t*>(sg->dev + o_p);
+  a.n_twrites = static_cast<int32_t>(tp.writes.size());
+  a.max_pages_per_seq = p->desc.max_pages_per_seq;
+  a.page_table = p->desc.page_table;
+  ProfRec rec{};
+  if (p->profiling && (rc = prof_begin(p, 0, st, &rec))) return rc;
+  hipError_t e = ll::launch_splice(a, lpb, p->desc.rope_pairing, st);
+  if (e != hipSuccess) return device_fail(p, e, "splice_kernel launch");
+  if (p->profiling) {
+    rec.bytes = stats.alg_bytes + 4 * stats.table_entries;
+    if ((rc = prof_end(p, 0, st, &rec))) return rc;
+  }
+  if ((rc = end_call(p, sg, st))) return rc;
+
+  // --- commit host state
+  for (int32_t pg : fresh) p->free.take(pg);
+  p->free.advance_hint();
+  for (int32_t i = 0; i < n; ++i) {
+    SeqState& s = p->seqs[dirs[i].seq_id];
+    std::vector<char> kept(s.pages.size(), 0);
+    for (int32_t x : plans[i].reuse)
+      if (x >= 0) kept[x] = 1;
+    for (size_t k = 0; k < kept.size(); ++k)
+      if (!kept[k]) p->free.give(s.pages[k]);
+    s.pages = std::move(new_tables[i]);
+    s.len = plans[i].n_new;
+    s.next_pos = plans[i].next_pos;
+  }
+  p->last = stats;
+  return LL_OK;
+}
+
+ll_status kv_evict_compact(ll_pool* p, const int32_t* seq_ids, int32_t n, const uint8_t* keep_dev,
+                           const int64_t* keep_offsets, void* stream) {
+  ll_status rc = check_pool(p);
+  if (rc) return rc;
+  if (n < 0 || (n > 0 && (!seq_ids || !keep_offsets))) return fail(LL_EINVAL, "bad arguments");
+  if (n == 0) return LL_OK;
+  std::vector<char> seen(static_cast<size_t>(p->desc.max_seqs), 0);
+  int64_t total_rows = 0, total_pages = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t s = seq_ids[i];
+    if (s < 0 || s >= p->desc.max_seqs || !p->seqs[s].used) return fail(LL_EINVAL, "entry %d: unknown sequence %d", i, s);
+    if (seen[s]) return fail(LL_EINVAL, "entry %d: sequence %d appears twice", i, s);
+    seen[s] = 1;
+    if (keep_offsets[i] < 0) return fail(LL_EINVAL, "entry %d: negative mask offset", i);
+    total_rows += p->seqs[s].len;
+    total_pages += static_cast<int64_t>(p->seqs[s].pages.size());
+  }
+  if (total_rows > 0 && !keep_dev) return fail(LL_EINVAL, "keep mask is NULL");
+  const int64_t P = p->P;
+  DeviceGuard g(p->desc.device);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+
+  // --- scratch: [counts (int64) n | reuse (int32) total_pages | src_of_dst (int32) total_rows]
+  const size_t off_reuse = align_up(8 * static_cast<size_t>(n), 256);
+  const size_t off_src = align_up(off_reuse + 4 * static_cast<size_t>(total_pages), 256);
+  const size_t scratch = off_src + 4 * static_cast<size_t>(total_rows) + 256;
+  const size_t readback = off_src;
+  if ((rc = begin_call(p, st))) return rc;
+  if (scratch > p->scratch_cap || readback > p->readback_cap) {
+    if (p->last_done) (void)hipEventSynchronize(p->last_done);
+    if (scratch > p->scratch_cap) {
+      if (p->d_scratch) (void)hipFree(p->d_scratch);
+      p->d_scratch = nullptr;
+      p->scratch_cap = 0;
+      if (hipMalloc(reinterpret_cast<void**>(&p->d_scratch), scratch) != hipSuccess)
+        return fail(LL_ENOMEM, "cannot allocate %zu bytes of eviction scratch", scratch);
+      p->scratch_cap = scratch;
+    }
+    if (readback > p->readback_cap) {
+      if (p->h_readback) (void)hipHostFree(p->h_readback);
+      p->h_readback = nullptr;
+      p->readback_cap = 0;
+      if (hipHostMalloc(reinterpret_cast<void**>(&p->h_readback), readback, hipHostMallocDefault) != hipSuccess)
+        return fail(LL_ENOMEM, "cannot allocate %zu bytes of pinned readback", readback);
+      p->readback_cap = readback;
+    }
+  }
+
+  std::vector<ll::EvictSeq> es(static_cast<size_t>(n));
+  std::vector<int64_t> reuse_off(static_cast<size_t>(n)), src_off(static_cast<size_t>(n));
+  {
+    int64_t ro = 0, so = 0;
+    for (int32_t i = 0; i < n; ++i) {
+      const SeqState& s = p->seqs[seq_ids[i]];
+      es[i].mask_off = keep_offsets[i];
+      es[i].n_old = s.len;
+      es[i].src_off = src_off[i] = so;
+      es[i].reuse_off = reuse_off[i] = ro;
+      so += s.len;
+      ro += static_cast<int64_t>(s.pages.size());
+    }
+  }
+  Staging* s1 = nullptr;
+  if ((rc = stage_acquire(p, stage_bytes_for({es.size() * sizeof(ll::EvictSeq)}), &s1))) return rc;
+  const size_t o_es = stage_put(s1, es.data(), es.size() * sizeof(ll::EvictSeq));
+  if ((rc = upload(p, s1, st))) return rc;
+  ll::ScanLaunch sc{};
+  sc.keep = keep_dev;
+  sc.seqs = reinterpret_cast<const ll::EvictSeq*>(s1->dev + o_es);
+  sc.n_seqs = n;
+  sc.page_shift = p->page_shift;
+  sc.counts = reinterpret_cast<int64_t*>(p->d_scratch);
+  sc.reuse = reinterpret_cast<int32_t*>(p->d_scratch + off_reuse);
+  sc.src_of_dst = reinterpret_cast<int32_t*>(p->d_scratch + off_src);
+  ProfRec rec1{};
+  if (p->profiling && (rc = prof_begin(p, 1, st, &rec1))) return rc;
+  hipError_t e = ll::launch_keep_scan(sc, st);
+  if (e != hipSuccess) return fail(LL_EDEVICE, "keep_scan_kernel launch: %s", hipGetErrorString(e));
+  if (p->profiling) {
+    rec1.bytes = total_rows + 4 * total_rows;
+    if ((rc = prof_end(p, 1, st, &rec1))) return rc;
+  }
+  e = hipMemcpyAsync(p->h_readback, p->d_scratch, readback, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipEventRecord(s1->done, st);
+  s1->pending = true;
+  p->last_done = s1->done;
+  if (e == hipSuccess) e = hipEventSynchronize(s1->done);
+  if (e != hipSuccess) return fail(LL_EDEVICE, "eviction readback: %s", hipGetErrorString(e));
+  // Nothing has changed yet: the scan only wrote scratch.
+
+  const int64_t* counts = reinterpret_cast<const int64_t*>(p->h_readback);
+  const int32_t* reuse = reinterpret_cast<const int32_t*>(p->h_readback + off_reuse);
+  int64_t need = 0;
+  std::vector<int64_t> n_new(static_cast<size_t>(n));
+  for (int32_t i = 0; i < n; ++i) {
+    const SeqState& s = p->seqs[seq_ids[i]];
+    n_new[i] = counts[i];
+    if (n_new[i] < 0 || n_new[i] > s.len) return fail(LL_EDEVICE, "keep scan returned a bad count");
+    const int64_t pages = ceil_div(n_new[i], P);
+    int64_t prev = -1;
+    for (int64_t q = 0; q < pages; ++q) {
+      const int32_t x = reuse[reuse_off[i] + q];
+      if (x < 0) {
+        ++need;
+        continue;
+      }
+      if (x <= prev || x >= static_cast<int64_t>(s.pages.size())) return fail(LL_EDEVICE, "keep scan returned a bad page plan");
+      prev = x;
+    }
+  }
+  if (need > p->free.count())
+    return fail(LL_ENOMEM, "need %lld fresh pages, %lld free", (long long)need, (long long)p->free.count());
+  std::vector<int32_t> fresh;
+  p->free.lowest(need, fresh);
+
+  std::vector<ll::EvictTask> tasks;
+  TablePlan tp;
+  std::vector<std::vector<int32_t>> new_tables(static_cast<size_t>(n));
+  std::vector<std::vector<char>> kept(static_cast<size_t>(n));
+  ll_plan_stats stats{};
+  size_t cursor = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const SeqState& s = p->seqs[seq_ids[i]];
+    const int64_t pages = ceil_div(n_new[i], P);
+    std::vector<int32_t>& nt = new_tables[i];
+    nt.resize(static_cast<size_t>(pages));
+    kept[i].assign(s.pages.size(), 0);
+    for (int64_t q = 0; q < pages; ++q) {
+      const int32_t x = reuse[reuse_off[i] + q];
+      if (x >= 0) {
+        nt[q] = s.pages[x];
+        kept[i][x] = 1;
+        continue;
+      }
+      nt[q] = fresh[cursor++];
+      ll::EvictTask t{};
+      t.src_off = src_off[i];
+      t.seq = seq_ids[i];
+      t.q = static_cast<int32_t>(q);
+      t.dst_page = nt[q];
+      t.n_new = static_cast<int32_t>(n_new[i]);
+      tasks.push_back(t);
+      stats.rows_moved += std::min(P, n_new[i] - q * P);
+    }
+    for (char k : kept[i]) stats.freed_pages += k ? 0 : 1;
+    tp.add(seq_ids[i], nt);
+  }
+  stats.fresh_pages = need;
+  stats.table_entries = static_cast<int64_t>(tp.packed.size());
+  stats.alg_bytes = p->desc.num_layers * 2 * ll::kRowBytes * stats.rows_moved;
+
+  Staging* s2 = nullptr;
+  rc = stage_acquire(p, stage_bytes_for({tasks.size() * sizeof(ll::EvictTask), tp.writes.size() * sizeof(ll::TableWrite),
+                                         tp.packed.size() * 4}),
+                     &s2);
+  if (rc) return rc;
+  const size_t o_t = stage_put(s2, tasks.data(), tasks.size() * sizeof(ll::EvictTask));
+  const size_t o_w = stage_put(s2, tp.writes.data(), tp.writes.size() * sizeof(ll::TableWrite));
+  const size_t o_p = stage_put(s2, tp.packed.data(), tp.packed.size() * 4);
+  if ((rc = upload(p, s2, st))) return rc;
+  ll::EvictLaunch a{};
+  a.layers = reinterpret_cast<const ll::chunk_t* const*>(p->d_layers);
+  a.num_layers = p->desc.num_layers;
+  a.page_shift = p->page_shift;
+  a.tasks = reinterpret_cast<const ll::EvictTask*>(s2->dev + o_t);
+  a.n_tasks = static_cast<int64_t>(tasks.size());
+  a.n_slabs = ceil_div(a.n_tasks * P, ll::kSlabRows);
+  const int lpb = p->layers_per_block;
+  a.n_move_blocks = a.n_slabs * ll::layer_groups(a.num_layers, lpb);
+  a.src_of_dst = sc.src_of_dst;
+  a.page_table = p->desc.page_table;
+  a.max_pages_per_seq = p->desc.max_pages_per_seq;
+  ProfRec rec{};
+  if (p->profiling && a.n_move_blocks && (rc = prof_begin(p, 0, st, &rec))) return rc;
+  e = ll::launch_evict_move(a, lpb, st);
+  if (e != hipSuccess) return device_fail(p, e, "evict_move_kernel launch");
+  if (p->profiling && a.n_move_blocks) {
+    rec.bytes = stats.alg_bytes;
+    if ((rc = prof_end(p, 0, st, &rec))) return rc;
+  }
+  ll::TableLaunch ta{};
+  ta.twrites = reinterpret_cast<const ll::TableWrite*>(s2->dev + o_w);
+  ta.tables = reinterpret_cast<const int32_t*>(s2->dev + o_p);
+  ta.n_twrites = static_cast<int32_t>(tp.writes.size());
+  ta.max_pages_per_seq = p->desc.max_pages_per_seq;
+  ta.page_table = p->desc.page_table;
+  e = ll::launch_table_write(ta, st);
+  if (e != hipSuccess) return device_fail(p, e, "table_write_kernel launch");
+  if ((rc = end_call(p, s2, st))) return rc;
+
+  for (int32_t pg : fresh) p->free.take(pg);
+  p->free.advance_hint();
+  for (int32_t i = 0; i < n; ++i) {
+    SeqState& s = p->seqs[seq_ids[i]];
+    for (size_t k = 0; k < kept[i].size(); ++k)
+      if (!kept[i][k]) p->free.give(s.pages[k]);
+    s.pages = std::move(new_tables[i]);
+    s.len = n_new[i];
+  }
+  p->last = stats;
+  return LL_OK;
+}
+
+ll_status ll_ptable_reindex(ll_pool* p, int32_t seq, const int32_t* keep_pages, int32_t n_keep, void* stream) {
+  ll_status rc = check_pool(p);
+  if (rc) return rc;
+  if (seq < 0 || seq >= p->desc.max_seqs || !p->seqs[seq].used) return fail(LL_EINVAL, "unknown sequence %d", seq);
+  if (n_keep < 0 || (n_keep > 0 && !keep_pages)) return fail(LL_EINVAL, "bad keep_pages");
+  SeqState& s = p->seqs[seq];
+  const int64_t P = p->P;
+  const int64_t old_pages = static_cast<int64_t>(s.pages.size());
+  const bool tail_partial = s.len % P != 0;
+  int64_t new_len = 0;
+  for (int32_t i = 0; i < n_keep; ++i) {
+    const int32_t k = keep_pages[i];
+    if (k < 0 || k >= old_pages) return fail(LL_EINVAL, "keep_pages[%d] = %d out of range", i, k);
+    if (i > 0 && k <= keep_pages[i - 1]) return fail(LL_EINVAL, "keep_pages must be strictly increasing");
+    if (tail_partial && k == old_pages - 1 && i != n_keep - 1)
+      return fail(LL_EINVAL, "a partial tail page may only be kept last");
+    new_len += std::min(P, s.len - k * P);
+  }
+  std::vector<int32_t> nt(static_cast<size_t>(n_keep));
+  std::vector<char> kept(static_cast<size_t>(old_pages), 0);
+  for (int32_t i = 0; i < n_keep; ++i) {
+    nt[i] = s.pages[keep_pages[i]];
+    kept[keep_pages[i]] = 1;
+  }
+  DeviceGuard g(p->desc.device);
+  TablePlan tp;
+  tp.add(seq, nt);
+  if ((rc = write_tables(p, tp, static_cast<hipStream_t>(stream)))) return rc;
+  ll_plan_stats stats{};
+  for (int64_t k = 0; k < old_pages; ++k)
+    if (!kept[k]) {
+      p->free.give(s.pages[k]);
+      ++stats.freed_pages;
+    }
+  stats.table_entries = n_keep;
+  s.pages = std::move(nt);
+  s.len = new_len;
+  p->last = stats;
+  return LL_OK;
+}
+
+ll_status ll_last_plan_stats(const ll_pool* p, ll_plan_stats* out) {
+  if (!p || !out) return fail(LL_EINVAL, "NULL argument");
+  *out = p->last;
+  return LL_OK;
+}
+
+ll_status ll_pool_set_profiling(ll_pool* p, int32_t enable) {
+  if (!p) return fail(LL_EINVAL, "pool is NULL");
+  p->profiling = enable != 0;
+  return LL_OK;
+}
+
+ll_status ll_profile_read(ll_pool* p, int32_t kernel, int64_t* launches, double* total_ms, int64_t* total_bytes) {
+  if (!p || kernel < 0 || kernel > 1) return fail(LL_EINVAL, "bad argument");
+  DeviceGuard g(p->desc.device);
+  int64_t cnt = 0, bytes = 0;
+  double ms = 0.0;
+  for (ProfRec& r : p->prof[kernel]) {
+    hipError_t e = hipEventSynchronize(r.stop);
+    float t = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&t, r.start, r.stop);
+    if (e != hipSuccess) return fail(LL_EDEVICE, "profile events: %s", hipGetErrorString(e));
+    ms += t;
+    bytes += r.bytes;
+    ++cnt;
+    p->spare_events.push_back(r.start);
+    p->spare_events.push_back(r.stop);
+  }
+  p->prof[kernel].clear();
+  if (launches) *launches = cnt;
+  if (total_ms) *total_ms = ms;
+  if (total_bytes) *total_bytes = bytes;
+  return LL_OK;
+}
+
+}  // extern "C"

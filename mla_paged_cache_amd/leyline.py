@@ -1,0 +1,297 @@
+"""Python binding of libleyline.so (include/leyline.h): argument marshalling only.
+
+Every step of the splice / evict path runs in the library's HIP kernels and
+C++ host planner; this module turns torch tensors into device pointers and
+the current torch stream into a hipStream_t, and turns status codes into
+exceptions.  If the library is missing, importing this module fails loudly.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libleyline.so")
+
+LL_OK, LL_EINVAL, LL_ERANGE, LL_ENOMEM, LL_EUNSUPPORTED, LL_EDEVICE, LL_EPOISONED = 0, -1, -2, -3, -4, -5, -6
+AMORTIZE, FORGET, PIN, DECAY, SCRATCH = 0, 1, 2, 3, 4
+ROPE_INTERLEAVED, ROPE_HALF = 0, 1
+KV_LORA_RANK, ROPE_DIM = 512, 64
+ROW = KV_LORA_RANK + ROPE_DIM
+
+# Every symbol include/leyline.h declares.
+EXPORTS = (
+    "ll_pool_create", "ll_pool_destroy", "ll_seq_alloc", "ll_seq_set_pages", "ll_seq_free",
+    "ll_seq_get", "ll_pool_free_pages", "leyline_splice", "kv_evict_compact", "ll_ptable_reindex",
+    "ll_rope_delta_table", "ll_last_plan_stats", "ll_pool_set_profiling", "ll_profile_read",
+    "ll_last_error", "ll_status_str",
+)
+
+
+class LeylineError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_status_name(status)}: {message}")
+        self.status = status
+
+
+class _PoolDesc(ctypes.Structure):
+    _fields_ = [
+        ("num_layers", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32),
+        ("max_seqs", ctypes.c_int32),
+        ("max_pages_per_seq", ctypes.c_int32),
+        ("kv_lora_rank", ctypes.c_int32),
+        ("rope_dim", ctypes.c_int32),
+        ("rope_pairing", ctypes.c_int32),
+        ("rope_base", ctypes.c_double),
+        ("layer_base", ctypes.POINTER(ctypes.c_void_p)),
+        ("page_table", ctypes.c_void_p),
+        ("device", ctypes.c_int32),
+    ]
+
+
+class _Directive(ctypes.Structure):
+    _fields_ = [
+        ("seq_id", ctypes.c_int32),
+        ("mode", ctypes.c_int32),
+        ("s_start", ctypes.c_int64),
+        ("s_end", ctypes.c_int64),
+        ("r_len", ctypes.c_int64),
+        ("r_rows", ctypes.c_void_p),
+        ("r_layer_stride_bytes", ctypes.c_int64),
+    ]
+
+
+class _PlanStats(ctypes.Structure):
+    _fields_ = [
+        ("alg_bytes", ctypes.c_int64),
+        ("rows_moved", ctypes.c_int64),
+        ("rows_rotated_inplace", ctypes.c_int64),
+        ("fresh_pages", ctypes.c_int64),
+        ("freed_pages", ctypes.c_int64),
+        ("table_entries", ctypes.c_int64),
+    ]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with mla_paged_cache_amd._build.build() "
+                          "(the splice path has no fallback)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, i32, i64, vp = ctypes.POINTER, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+    sig = {
+        "ll_pool_create": (i32, [P(_PoolDesc), P(vp)]),
+        "ll_pool_destroy": (None, [vp]),
+        "ll_seq_alloc": (i32, [vp, i64, P(i32), vp]),
+        "ll_seq_set_pages": (i32, [vp, i32, P(i32), i64, vp]),
+        "ll_seq_free": (i32, [vp, i32]),
+        "ll_seq_get": (i32, [vp, i32, P(i64), P(i64), P(i32), i32, P(i32)]),
+        "ll_pool_free_pages": (i32, [vp, P(i64)]),
+        "leyline_splice": (i32, [vp, P(_Directive), i32, vp]),
+        "kv_evict_compact": (i32, [vp, P(i32), i32, vp, P(i64), vp]),
+        "ll_ptable_reindex": (i32, [vp, i32, P(i32), i32, vp]),
+        "ll_rope_delta_table": (i32, [ctypes.c_double, i32, i64, P(ctypes.c_float), P(ctypes.c_float)]),
+        "ll_last_plan_stats": (i32, [vp, P(_PlanStats)]),
+        "ll_pool_set_profiling": (i32, [vp, i32]),
+        "ll_profile_read": (i32, [vp, i32, P(i64), P(ctypes.c_double), P(i64)]),
+        "ll_last_error": (ctypes.c_char_p, []),
+        "ll_status_str": (ctypes.c_char_p, [i32]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+
+def _status_name(s: int) -> str:
+    return _lib.ll_status_str(s).decode()
+
+
+def _check(status: int) -> None:
+    if status != LL_OK:
+        raise LeylineError(status, _lib.ll_last_error().decode())
+
+
+def _i32_array(values):
+    a = np.ascontiguousarray(np.asarray(values, dtype=np.int32))
+    return a, a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def _stream_handle(stream) -> int | None:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def rope_delta_table(delta: int, rope_dim: int = ROPE_DIM, base: float = 10000.0):
+    """float32 (cos, sin) of delta * theta_j, as the library computes them."""
+    c = np.zeros(rope_dim // 2, np.float32)
+    s = np.zeros(rope_dim // 2, np.float32)
+    _check(_lib.ll_rope_delta_table(base, rope_dim, int(delta),
+                                    c.ctypes.data_as(ctypes.POINTER(ctypes.c_float)),
+                                    s.ctypes.data_as(ctypes.POINTER(ctypes.c_float))))
+    return c, s
+
+
+@dataclass
+class Directive:
+    """D = (s_start, s_end, R, m).  `stub` is a device bf16 tensor [L][r_len][576]
+    (or [r_len][576] for a one-layer pool), or None for r_len = 0."""
+    seq: int
+    s_start: int
+    s_end: int
+    stub: object = None
+    mode: int = AMORTIZE
+
+
+@dataclass
+class PlanStats:
+    alg_bytes: int
+    rows_moved: int
+    rows_rotated_inplace: int
+    fresh_pages: int
+    freed_pages: int
+    table_entries: int
+
+
+class Pool:
+    """A paged MLA cache over caller-owned torch memory.
+
+    layers: a bf16 CUDA tensor [L][num_pages][page_size][576] or a list of L
+    tensors [num_pages][page_size][576]; page_table: int32 CUDA tensor
+    [max_seqs][max_pages_per_seq].  Both are kept referenced by the pool."""
+
+    def __init__(self, layers, page_table, rope_base: float = 10000.0, pairing: int = ROPE_INTERLEAVED):
+        import torch
+        if isinstance(layers, torch.Tensor):
+            layer_list = [layers[i] for i in range(layers.shape[0])]
+        else:
+            layer_list = list(layers)
+        if not layer_list:
+            raise ValueError("no layers")
+        shape = tuple(layer_list[0].shape)
+        for t in layer_list:
+            if t.dtype != torch.bfloat16 or not t.is_cuda or tuple(t.shape) != shape or not t.is_contiguous():
+                raise ValueError("layers must be contiguous bf16 CUDA tensors of one shape [pages][P][576]")
+        if len(shape) != 3 or shape[2] != ROW:
+            raise ValueError("layer shape must be [num_pages][page_size][576]")
+        if page_table.dtype != torch.int32 or not page_table.is_cuda or page_table.dim() != 2 \
+                or not page_table.is_contiguous():
+            raise ValueError("page_table must be a contiguous int32 CUDA tensor [max_seqs][max_pages_per_seq]")
+        self._layers = layer_list
+        self._keep = layers
+        self.page_table = page_table
+        self.num_layers = len(layer_list)
+        self.num_pages, self.page_size = shape[0], shape[1]
+        self.max_seqs, self.max_pages_per_seq = page_table.shape
+        self.device = layer_list[0].device
+        self._ptrs = (ctypes.c_void_p * self.num_layers)(*[t.data_ptr() for t in layer_list])
+        d = _PoolDesc(self.num_layers, self.page_size, self.num_pages, self.max_seqs, self.max_pages_per_seq,
+                      KV_LORA_RANK, ROPE_DIM, pairing, rope_base,
+                      ctypes.cast(self._ptrs, ctypes.POINTER(ctypes.c_void_p)),
+                      page_table.data_ptr(), self.device.index or 0)
+        h = ctypes.c_void_p()
+        _check(_lib.ll_pool_create(ctypes.byref(d), ctypes.byref(h)))
+        self._h = h
+
+    # -- lifetime
+    def close(self):
+        if getattr(self, "_h", None):
+            _lib.ll_pool_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # -- sequences
+    def seq_alloc(self, n_tokens: int, stream=None) -> int:
+        sid = ctypes.c_int32()
+        _check(_lib.ll_seq_alloc(self._h, int(n_tokens), ctypes.byref(sid), _stream_handle(stream)))
+        return sid.value
+
+    def seq_set_pages(self, seq: int, pages, n_tokens: int, stream=None) -> None:
+        arr, ptr = _i32_array(pages)
+        _check(_lib.ll_seq_set_pages(self._h, int(seq), ptr, int(n_tokens), _stream_handle(stream)))
+
+    def seq_free(self, seq: int) -> None:
+        _check(_lib.ll_seq_free(self._h, int(seq)))
+
+    def seq_get(self, seq: int):
+        """(length, next_position, page table as np.int32)."""
+        n, pos, cnt = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int32()
+        _check(_lib.ll_seq_get(self._h, int(seq), ctypes.byref(n), ctypes.byref(pos), None, 0, ctypes.byref(cnt)))
+        pages = np.zeros(cnt.value, np.int32)
+        _check(_lib.ll_seq_get(self._h, int(seq), None, None,
+                               pages.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), cnt.value, None))
+        return n.value, pos.value, pages
+
+    def free_pages(self) -> int:
+        n = ctypes.c_int64()
+        _check(_lib.ll_pool_free_pages(self._h, ctypes.byref(n)))
+        return n.value
+
+    # -- the path
+    def splice(self, directives, stream=None) -> None:
+        import torch
+        n = len(directives)
+        arr = (_Directive * max(1, n))()
+        for i, d in enumerate(directives):
+            r_len, ptr, stride = 0, None, 0
+            if d.stub is not None and d.mode == AMORTIZE:
+                st = d.stub
+                if st.dtype != torch.bfloat16 or not st.is_cuda or st.shape[-1] != ROW:
+                    raise ValueError("stub must be a bf16 CUDA tensor [..., r_len, 576]")
+                if st.dim() == 2:
+                    st = st.unsqueeze(0)
+                if st.shape[0] != self.num_layers or st.stride(2) != 1 or st.stride(1) != ROW:
+                    raise ValueError("stub must be [num_layers][r_len][576] with contiguous rows")
+                r_len = st.shape[1]
+                ptr = st.data_ptr() if r_len else None
+                stride = st.stride(0) * 2
+            arr[i] = _Directive(int(d.seq), int(d.mode), int(d.s_start), int(d.s_end), int(r_len), ptr, stride)
+        _check(_lib.leyline_splice(self._h, arr, n, _stream_handle(stream)))
+
+    def evict(self, seqs, keep, offsets, stream=None) -> None:
+        """keep: uint8 CUDA tensor holding every mask; offsets[i]: start of
+        sequence seqs[i]'s mask in it (its length is the sequence length)."""
+        import torch
+        if keep.dtype != torch.uint8 or not keep.is_cuda or not keep.is_contiguous():
+            raise ValueError("keep must be a contiguous uint8 CUDA tensor")
+        s_arr, s_ptr = _i32_array(seqs)
+        o_arr = np.ascontiguousarray(np.asarray(offsets, dtype=np.int64))
+        _check(_lib.kv_evict_compact(self._h, s_ptr, len(s_arr), keep.data_ptr(),
+                                     o_arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                     _stream_handle(stream)))
+
+    def ptable_reindex(self, seq: int, keep_pages, stream=None) -> None:
+        arr, ptr = _i32_array(keep_pages)
+        _check(_lib.ll_ptable_reindex(self._h, int(seq), ptr, len(arr), _stream_handle(stream)))
+
+    # -- counters
+    def last_stats(self) -> PlanStats:
+        s = _PlanStats()
+        _check(_lib.ll_last_plan_stats(self._h, ctypes.byref(s)))
+        return PlanStats(s.alg_bytes, s.rows_moved, s.rows_rotated_inplace, s.fresh_pages, s.freed_pages,
+                         s.table_entries)
+
+    def set_profiling(self, enable: bool) -> None:
+        _check(_lib.ll_pool_set_profiling(self._h, 1 if enable else 0))
+
+    def profile_read(self, kernel: int = 0):
+        """(launches, total_ms, total_bytes) of kernel 0 (row moves) or 1 (keep scan)."""
+        n, ms, b = ctypes.c_int64(), ctypes.c_double(), ctypes.c_int64()
+        _check(_lib.ll_profile_read(self._h, kernel, ctypes.byref(n), ctypes.byref(ms), ctypes.byref(b)))
+        return n.value, ms.value, b.value

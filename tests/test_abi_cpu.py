@@ -1,0 +1,92 @@
+"""Host-side checks of the C ABI that need no GPU: the built library loads and
+exports every function include/leyline.h declares, the binding declares the
+same set, descriptor validation fails before any device call, and the host's
+float32 cos/sin table of the delta-rotation (Leyline summary, section 2.2) is
+the oracle's."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "leyline.h")
+LIB = os.path.join(ROOT, "mla_paged_cache_amd", "libleyline.so")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libleyline.so is not built: run __graft_entry__.build()")
+    return ctypes.CDLL(LIB)
+
+
+def test_header_declares_the_path_entry_points():
+    names = _declared()
+    for n in ("leyline_splice", "kv_evict_compact", "ll_ptable_reindex", "ll_pool_create"):
+        assert n in names
+    assert len(names) == 16
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_binding_covers_the_header():
+    from mla_paged_cache_amd import leyline
+    assert sorted(leyline.EXPORTS) == _declared()
+
+
+def test_pool_create_rejects_bad_descriptors_before_touching_a_device():
+    from mla_paged_cache_amd import leyline as L
+    ptrs = (ctypes.c_void_p * 2)(16, 32)
+    base = dict(num_layers=2, page_size=16, num_pages=8, max_seqs=1, max_pages_per_seq=8,
+                kv_lora_rank=512, rope_dim=64, rope_pairing=0, rope_base=10000.0,
+                layer_base=ctypes.cast(ptrs, ctypes.POINTER(ctypes.c_void_p)), page_table=64, device=0)
+    cases = [
+        (dict(page_size=12), L.LL_EINVAL),
+        (dict(page_size=512), L.LL_EINVAL),
+        (dict(num_layers=0), L.LL_EINVAL),
+        (dict(kv_lora_rank=128), L.LL_EUNSUPPORTED),
+        (dict(rope_dim=32), L.LL_EUNSUPPORTED),
+        (dict(rope_pairing=7), L.LL_EINVAL),
+        (dict(rope_base=-1.0), L.LL_EINVAL),
+        (dict(page_table=None), L.LL_EINVAL),
+        (dict(device=-1), L.LL_EINVAL),
+    ]
+    for change, code in cases:
+        d = L._PoolDesc(**{**base, **change})
+        h = ctypes.c_void_p()
+        assert L._lib.ll_pool_create(ctypes.byref(d), ctypes.byref(h)) == code, change
+        assert not h.value
+        assert L._lib.ll_last_error().decode()
+    misaligned = (ctypes.c_void_p * 2)(16, 40)
+    d = L._PoolDesc(**{**base, "layer_base": ctypes.cast(misaligned, ctypes.POINTER(ctypes.c_void_p))})
+    assert L._lib.ll_pool_create(ctypes.byref(d), ctypes.byref(ctypes.c_void_p())) == L.LL_EINVAL
+
+
+def test_null_pool_calls_fail_cleanly():
+    from mla_paged_cache_amd import leyline as L
+    assert L._lib.leyline_splice(None, None, 0, None) == L.LL_EINVAL
+    assert L._lib.kv_evict_compact(None, None, 0, None, None, None) == L.LL_EINVAL
+    assert L._lib.ll_ptable_reindex(None, 0, None, 0, None) == L.LL_EINVAL
+    assert L._lib.ll_status_str(L.LL_ENOMEM).decode() == "LL_ENOMEM"
+
+
+def test_host_rope_table_equals_oracle():
+    from mla_paged_cache_amd import leyline as L
+    from oracle import leyline_oracle as O
+    for delta in (-6120, -1984, 0, 1, 7, 8191, -131071, 10 ** 6):
+        c, s = L.rope_delta_table(delta)
+        co, so = O.delta_cos_sin(delta)
+        assert np.array_equal(c, co) and np.array_equal(s, so), delta
