@@ -7,16 +7,18 @@
 //    launch ("Leyline: KV Cache Directives for Agentic Inference", sections
 //    2.1-2.3).
 //  * keep_scan_kernel: per-sequence exclusive prefix sum of a keep mask built
-//    from wave64 ballots, giving each kept row its new index, plus the
-//    per-new-page reuse test ("KV-streams", "how it works").
-//  * evict_move_kernel: copies kept rows into fresh pages, no rotation.
-//  * table_write_kernel: page-table row rewrites.
+//    from wave64 ballots, giving each kept row its new index and physical
+//    source row, plus the per-new-page reuse test ("KV-streams", "how it
+//    works").
+//  * evict_move_kernel: copies kept rows into fresh pages, no rotation, and
+//    rewrites the page-table rows.
+//  * table_write_kernel: page-table row rewrites on their own.
 //
 // The row kernels are bound by HBM bandwidth (0.08 flop per byte), so they
-// are plain 16-byte vector copies: a block is 8 rows x 72 chunks = 576
-// threads, each thread owns one 16-byte column for the whole launch, loads of
-// all the layers it carries are issued before any store, and only the 8 k_pe
-// columns do arithmetic.
+// are flat 16-byte gathers: one chunk per thread, 256-thread blocks, each
+// block inside one layer, one 64-byte descriptor load before the data load,
+// non-temporal loads and stores.  Only k_pe chunks (8 of every 72) do
+// arithmetic.
 #include "leyline_internal.h"
 
 namespace ll {
@@ -82,7 +84,7 @@ __device__ __forceinline__ uint32_t rot_half_word(uint32_t own, uint32_t other, 
 }
 
 __device__ __forceinline__ chunk_t rotate_half(chunk_t own, chunk_t other, bool x_side, const float* c,
-                                             const float* s) {
+                                               const float* s) {
   chunk_t r;
   r.x = rot_half_word(own.x, other.x, x_side, c, s, 0);
   r.y = rot_half_word(own.y, other.y, x_side, c, s, 1);
@@ -107,142 +109,152 @@ __device__ __forceinline__ void table_write_block(const TableWrite* tw, const in
   for (int e = threadIdx.x; e < w.count; e += blockDim.x) dst[e] = tables[w.src_off + e];
 }
 
-// PAIRING: 0 interleaved, 1 half-split.
-template <int LPB, int PAIRING>
-__global__ __launch_bounds__(kMoveThreads) void splice_kernel(SpliceLaunch a) {
-  const int64_t b = blockIdx.x;
-  if (b >= a.n_move_blocks) {
-    table_write_block(a.twrites, a.tables, a.page_table, a.max_pages_per_seq, b - a.n_move_blocks);
-    return;
-  }
-  const int64_t lg = b / a.n_slabs;
-  const int64_t slab = b - lg * a.n_slabs;
-  const int tid = threadIdx.x;
-  const int srow = tid / kRowChunks;
-  const int col = tid - srow * kRowChunks;
-  const int shift = a.page_shift;
-  const int64_t pmask = (int64_t{1} << shift) - 1;
-
-  // Row `flat` of the task list: task flat >> shift, row flat & pmask.  For
-  // page sizes >= 8 a slab lies inside one task, so `t` is block-uniform.
-  const int64_t flat = slab * kSlabRows + srow;
-  const int64_t ti = flat >> shift;
-  const bool in_range = ti < a.n_tasks;
-  const SpliceTask t = a.tasks[in_range ? ti : 0];
-  const SpliceDir& d = a.dirs[t.dir];
-  const int64_t r = flat & pmask;
-  const int64_t j = (static_cast<int64_t>(t.q) << shift) + r;
-  const bool live = in_range && j < d.n_new;
-  const bool kpe = col >= kKpeChunk0;
-
-  bool active = live;
-  bool from_stub = false;
-  bool rot = false;
-  int64_t src_row = 0;
-  if (t.kind == kRotateInPlace) {
-    active = live && kpe;
-    src_row = (static_cast<int64_t>(t.dst_page) << shift) + r;
-    rot = true;
-  } else if (j < d.s_start) {
-    src_row = (static_cast<int64_t>(t.pre_page) << shift) + (j & pmask);
-  } else if (j < d.s_start + d.r_len) {
-    from_stub = true;
-    src_row = j - d.s_start;
+// Turn the k_pe chunk `v` (chunk kc = 0..7 of the band) by the directive's
+// table.  Every lane of the wave must call this (the half-split layout trades
+// chunks between lanes kc and kc ^ 4 of the same row); `on` selects the lanes
+// whose chunk really turns.
+template <int PAIRING>
+__device__ __forceinline__ chunk_t rotate_kpe(chunk_t v, bool on, int kc, const SpliceDir* d) {
+  if constexpr (PAIRING == 0) {
+    if (on) {
+      float cs[4], sn[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        cs[e] = d->cos_[4 * kc + e];
+        sn[e] = d->sin_[4 * kc + e];
+      }
+      v = rotate_interleaved(v, cs, sn);
+    }
+    return v;
   } else {
-    const int64_t o = j - d.delta;
-    const int32_t pg = ((o >> shift) == t.down_lp0) ? t.down_page0 : t.down_page1;
-    src_row = (static_cast<int64_t>(pg) << shift) + (o & pmask);
-    rot = d.rotate != 0;
-  }
-  const int64_t src_chunk = src_row * kRowChunks + col;
-  const int64_t dst_chunk = ((static_cast<int64_t>(t.dst_page) << shift) + r) * kRowChunks + col;
-
-  constexpr int NC = PAIRING == 0 ? 4 : 8;
-  float cs[NC], sn[NC];
-  const int k = col - kKpeChunk0;
-  if (kpe) {
-    const int j0 = PAIRING == 0 ? 4 * k : 8 * (k & 3);
+    const chunk_t other = shfl_xor4(v);
+    if (on) {
+      float cs[8], sn[8];
 #pragma unroll
-    for (int e = 0; e < NC; ++e) {
-      cs[e] = d.cos_[j0 + e];
-      sn[e] = d.sin_[j0 + e];
+      for (int e = 0; e < 8; ++e) {
+        cs[e] = d->cos_[8 * (kc & 3) + e];
+        sn[e] = d->sin_[8 * (kc & 3) + e];
+      }
+      v = rotate_half(v, other, kc < 4, cs, sn);
     }
-  }
-
-  const int l0 = static_cast<int>(lg) * LPB;
-  chunk_t v[LPB];
-#pragma unroll
-  for (int i = 0; i < LPB; ++i) {
-    const int l = l0 + i;
-    v[i] = chunk_t{0u, 0u, 0u, 0u};
-    if (active && l < a.num_layers) {
-      const chunk_t* base = from_stub ? d.stub + l * d.stub_layer_chunks : a.layers[l];
-      v[i] = __builtin_nontemporal_load(base + src_chunk);
-    }
-  }
-  const bool do_rot = active && rot && kpe;
-#pragma unroll
-  for (int i = 0; i < LPB; ++i) {
-    if (PAIRING == 0) {
-      if (do_rot) v[i] = rotate_interleaved(v[i], cs, sn);
-    } else {
-      // every lane takes part in the exchange; the partner of a k_pe lane is
-      // the k_pe lane 4 columns away in the same row (same wave, same flags)
-      const chunk_t other = shfl_xor4(v[i]);
-      if (do_rot) v[i] = rotate_half(v[i], other, k < 4, cs, sn);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < LPB; ++i) {
-    const int l = l0 + i;
-    if (active && l < a.num_layers) {
-      chunk_t* base = const_cast<chunk_t*>(a.layers[l]);
-      __builtin_nontemporal_store(v[i], base + dst_chunk);
-    }
+    return v;
   }
 }
 
-template <int LPB>
-__global__ __launch_bounds__(kMoveThreads) void evict_move_kernel(EvictLaunch a) {
+// Descriptor load: when every lane of the wave needs the same task (page size
+// >= 8: a page is 72 * P chunks, a multiple of 64, and waves start on multiples
+// of 64), the index is made wave-uniform and read through the constant
+// address space, i.e. with one scalar load instead of a 64-byte load per lane.
+template <bool WAVE_TASK, typename T>
+__device__ __forceinline__ T load_task(const T* tasks, int64_t i) {
+  if constexpr (WAVE_TASK) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(i));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(static_cast<uint64_t>(i) >> 32));
+    const int64_t u = static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+    static_assert(sizeof(T) % 16 == 0, "descriptors are whole 16-byte words");
+    using word_ptr = const __attribute__((address_space(4))) chunk_t*;
+    const word_ptr src = reinterpret_cast<word_ptr>(reinterpret_cast<uintptr_t>(tasks + u));
+    T out;
+    chunk_t* dst = reinterpret_cast<chunk_t*>(&out);
+#pragma unroll
+    for (int k = 0; k < static_cast<int>(sizeof(T) / 16); ++k) dst[k] = src[k];
+    return out;
+  } else {
+    return tasks[i];
+  }
+}
+
+// Flat gather.  Blocks [0, L * move_blocks_per_layer) move rows of fresh
+// pages: chunk c of a layer is chunk c % 72 of row c / 72 of the move-task
+// list.  The next L * rot_blocks_per_layer blocks rotate k_pe in place:
+// chunk c is k_pe chunk c % 8 of row c / 8 of the rotate-task list.  The
+// remaining blocks rewrite page-table rows (no block reads the table).
+// PAIRING: 0 interleaved, 1 half-split.  WAVE_TASK: page size >= 8.
+template <int PAIRING, bool WAVE_TASK>
+__global__ __launch_bounds__(kFlatThreads) void splice_kernel(SpliceLaunch a) {
   const int64_t b = blockIdx.x;
-  const int64_t lg = b / a.n_slabs;
-  const int64_t slab = b - lg * a.n_slabs;
-  const int tid = threadIdx.x;
-  const int srow = tid / kRowChunks;
-  const int col = tid - srow * kRowChunks;
+  const int64_t move_blocks = a.move_blocks_per_layer * a.num_layers;
+  const int64_t rot_blocks = a.rot_blocks_per_layer * a.num_layers;
+  if (b >= move_blocks + rot_blocks) {
+    table_write_block(a.twrites, a.tables, a.page_table, a.max_pages_per_seq, b - move_blocks - rot_blocks);
+    return;
+  }
+  const bool in_place = b >= move_blocks;
+  const int64_t bb = in_place ? b - move_blocks : b;
+  const int64_t bpl = in_place ? a.rot_blocks_per_layer : a.move_blocks_per_layer;
+  const int l = static_cast<int>(bb / bpl);
+  const uint32_t c = static_cast<uint32_t>((bb - static_cast<int64_t>(l) * bpl) * kFlatThreads + threadIdx.x);
   const int shift = a.page_shift;
-  const int64_t pmask = (int64_t{1} << shift) - 1;
-  const int64_t flat = slab * kSlabRows + srow;
-  const int64_t ti = flat >> shift;
-  const bool in_range = ti < a.n_tasks;
-  const EvictTask t = a.tasks[in_range ? ti : 0];
-  const int64_t r = flat & pmask;
+  const uint32_t pmask = (1u << shift) - 1u;
+
+  uint32_t row_flat, col;
+  if (in_place) {
+    row_flat = c >> 3;
+    col = kKpeChunk0 + (c & 7u);
+  } else {
+    row_flat = c / kRowChunks;
+    col = c - row_flat * kRowChunks;
+  }
+  const int64_t ti = static_cast<int64_t>(row_flat >> shift) + (in_place ? a.n_move_tasks : 0);
+  const int64_t t_end = in_place ? a.n_move_tasks + a.n_rot_tasks : a.n_move_tasks;
+  bool live = ti < t_end;
+  const SpliceTask t = load_task<WAVE_TASK>(a.tasks, live ? ti : 0);
+  const uint32_t r = row_flat & pmask;
   const int64_t j = (static_cast<int64_t>(t.q) << shift) + r;
-  const bool live = in_range && j < t.n_new;
-  int64_t src_row = 0;
-  if (live) {
-    const int64_t o = a.src_of_dst[t.src_off + j];
-    const int32_t pg = a.page_table[static_cast<int64_t>(t.seq) * a.max_pages_per_seq + (o >> shift)];
-    src_row = (static_cast<int64_t>(pg) << shift) + (o & pmask);
+  live = live && j < t.n_new;
+
+  const chunk_t* layer = a.layers[l];
+  const int64_t dst_row = (static_cast<int64_t>(t.dst_page) << shift) + r;
+  const chunk_t* src;
+  bool rot = false;
+  if (in_place) {
+    src = layer + dst_row * kRowChunks;
+    rot = true;
+  } else if (j < t.s_start) {
+    src = layer + ((static_cast<int64_t>(t.pre_page) << shift) + (j & pmask)) * kRowChunks;
+  } else if (j < t.stub_end) {
+    const SpliceDir& d = a.dirs[t.dir];
+    src = d.stub + l * d.stub_layer_chunks + (j - t.s_start) * kRowChunks;
+  } else {
+    const int64_t o = j - t.delta;
+    const int32_t pg = ((o >> shift) == t.down_lp0) ? t.down_page0 : t.down_page1;
+    src = layer + ((static_cast<int64_t>(pg) << shift) + (o & pmask)) * kRowChunks;
+    rot = t.rotate != 0;
   }
-  const int64_t src_chunk = src_row * kRowChunks + col;
-  const int64_t dst_chunk = ((static_cast<int64_t>(t.dst_page) << shift) + r) * kRowChunks + col;
-  const int l0 = static_cast<int>(lg) * LPB;
-  chunk_t v[LPB];
-#pragma unroll
-  for (int i = 0; i < LPB; ++i) {
-    const int l = l0 + i;
-    v[i] = chunk_t{0u, 0u, 0u, 0u};
-    if (live && l < a.num_layers) v[i] = __builtin_nontemporal_load(a.layers[l] + src_chunk);
+  chunk_t v = chunk_t{0u, 0u, 0u, 0u};
+  if (live) v = __builtin_nontemporal_load(src + col);
+  const int kc = static_cast<int>(col) - kKpeChunk0;
+  v = rotate_kpe<PAIRING>(v, live && rot && kc >= 0, kc, a.dirs + t.dir);
+  if (live) __builtin_nontemporal_store(v, const_cast<chunk_t*>(layer) + dst_row * kRowChunks + col);
+}
+
+// Flat copy of the kept rows that land in fresh pages (rotation off), then
+// the page-table rewrites in the blocks after the row blocks.
+template <bool WAVE_TASK>
+__global__ __launch_bounds__(kFlatThreads) void evict_move_kernel(EvictLaunch a) {
+  const int64_t b = blockIdx.x;
+  const int64_t move_blocks = a.blocks_per_layer * a.num_layers;
+  if (b >= move_blocks) {
+    table_write_block(a.twrites, a.tables, a.page_table, a.max_pages_per_seq, b - move_blocks);
+    return;
   }
-#pragma unroll
-  for (int i = 0; i < LPB; ++i) {
-    const int l = l0 + i;
-    if (live && l < a.num_layers) {
-      chunk_t* base = const_cast<chunk_t*>(a.layers[l]);
-      __builtin_nontemporal_store(v[i], base + dst_chunk);
-    }
-  }
+  const int l = static_cast<int>(b / a.blocks_per_layer);
+  const uint32_t c = static_cast<uint32_t>((b - static_cast<int64_t>(l) * a.blocks_per_layer) * kFlatThreads +
+                                           threadIdx.x);
+  const int shift = a.page_shift;
+  const uint32_t row_flat = c / kRowChunks;
+  const uint32_t col = c - row_flat * kRowChunks;
+  const int64_t ti = row_flat >> shift;
+  if (ti >= a.n_tasks) return;
+  const EvictTask t = load_task<WAVE_TASK>(a.tasks, ti);
+  const uint32_t r = row_flat & ((1u << shift) - 1u);
+  const int64_t j = (static_cast<int64_t>(t.q) << shift) + r;
+  if (j >= t.n_new) return;
+  const int64_t src_row = a.src_rows[t.src_off + j];
+  const chunk_t* layer = a.layers[l];
+  const chunk_t v = __builtin_nontemporal_load(layer + src_row * kRowChunks + col);
+  __builtin_nontemporal_store(v, const_cast<chunk_t*>(layer) +
+                                     ((static_cast<int64_t>(t.dst_page) << shift) + r) * kRowChunks + col);
 }
 
 __global__ __launch_bounds__(256) void table_write_kernel(TableLaunch a) {
@@ -254,12 +266,17 @@ constexpr int kScanWaves = kScanThreads / 64;
 
 // One block per sequence.  Each thread takes 16 mask bytes per tile; the
 // count of kept bytes (0..16) is scanned across the wave with one ballot per
-// bit of the count, then across the 16 waves through LDS.
+// bit of the count, then across the 16 waves through LDS.  Kept row i of the
+// sequence gets new index = number of kept rows before it, and its physical
+// source row (old page table) is stored there.
 __global__ __launch_bounds__(kScanThreads) void keep_scan_kernel(ScanLaunch a) {
   __shared__ int32_t wave_total[kScanWaves];
   const EvictSeq e = a.seqs[blockIdx.x];
   const uint8_t* m = a.keep + e.mask_off;
-  int32_t* out = a.src_of_dst + e.src_off;
+  int32_t* out = a.src_rows + e.src_off;
+  const int32_t* table = a.page_table + static_cast<int64_t>(e.seq) * a.max_pages_per_seq;
+  const int shift = a.page_shift;
+  const int64_t pmask = (int64_t{1} << shift) - 1;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const uint64_t lanes_below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
@@ -298,13 +315,15 @@ __global__ __launch_bounds__(kScanThreads) void keep_scan_kernel(ScanLaunch a) {
     }
     int64_t pos = carry + wave_below + below;
     for (int c = 0; c < 16; ++c)
-      if ((bits >> c) & 1u) out[pos++] = static_cast<int32_t>(i0 + c);
+      if ((bits >> c) & 1u) {
+        const int64_t i = i0 + c;
+        out[pos++] = static_cast<int32_t>((static_cast<int64_t>(table[i >> shift]) << shift) + (i & pmask));
+      }
     carry += block_total;
     __syncthreads();
   }
-  // Per new page: reusable iff its live rows are old rows f .. f+k-1 with f
-  // on a page boundary (so one old page, same offsets).
-  const int shift = a.page_shift;
+  // Per new page: reusable iff its live rows are the physical rows f .. f+k-1
+  // with f on a page boundary -- one old page, rows at their old offsets.
   const int64_t P = int64_t{1} << shift;
   const int64_t n_new = carry;
   const int64_t pages = (n_new + P - 1) >> shift;
@@ -313,53 +332,36 @@ __global__ __launch_bounds__(kScanThreads) void keep_scan_kernel(ScanLaunch a) {
     const int64_t k = (n_new - (q << shift)) < P ? (n_new - (q << shift)) : P;
     const int64_t f = out[q << shift];
     const int64_t l = out[(q << shift) + k - 1];
-    reuse[q] = ((f & (P - 1)) == 0 && l - f == k - 1) ? static_cast<int32_t>(f >> shift) : -1;
+    reuse[q] = ((f & pmask) == 0 && l - f == k - 1) ? static_cast<int32_t>(f >> shift) : -1;
   }
   if (threadIdx.x == 0) a.counts[blockIdx.x] = n_new;
 }
 
-template <int LPB>
-hipError_t launch_splice_lpb(const SpliceLaunch& a, int pairing, hipStream_t s) {
-  const int64_t grid = a.n_move_blocks + a.n_twrites;
-  if (grid == 0) return hipSuccess;
-  if (pairing == 0)
-    splice_kernel<LPB, 0><<<dim3(static_cast<unsigned>(grid)), dim3(kMoveThreads), 0, s>>>(a);
-  else
-    splice_kernel<LPB, 1><<<dim3(static_cast<unsigned>(grid)), dim3(kMoveThreads), 0, s>>>(a);
-  return hipGetLastError();
-}
-
-template <int LPB>
-hipError_t launch_evict_lpb(const EvictLaunch& a, hipStream_t s) {
-  if (a.n_move_blocks == 0) return hipSuccess;
-  evict_move_kernel<LPB><<<dim3(static_cast<unsigned>(a.n_move_blocks)), dim3(kMoveThreads), 0, s>>>(a);
-  return hipGetLastError();
-}
-
 }  // namespace
 
-int64_t layer_groups(int num_layers, int layers_per_block) {
-  return (num_layers + layers_per_block - 1) / layers_per_block;
+hipError_t launch_splice(const SpliceLaunch& a, int pairing, hipStream_t s) {
+  const int64_t grid = (a.move_blocks_per_layer + a.rot_blocks_per_layer) * a.num_layers + a.n_twrites;
+  if (grid == 0) return hipSuccess;
+  const dim3 g(static_cast<unsigned>(grid)), blk(kFlatThreads);
+  const bool wave_task = a.page_shift >= 3;
+  if (pairing == 0) {
+    if (wave_task) splice_kernel<0, true><<<g, blk, 0, s>>>(a);
+    else splice_kernel<0, false><<<g, blk, 0, s>>>(a);
+  } else {
+    if (wave_task) splice_kernel<1, true><<<g, blk, 0, s>>>(a);
+    else splice_kernel<1, false><<<g, blk, 0, s>>>(a);
+  }
+  return hipGetLastError();
 }
 
-hipError_t launch_splice(const SpliceLaunch& a, int layers_per_block, int pairing, hipStream_t s) {
-  switch (layers_per_block) {
-    case 1: return launch_splice_lpb<1>(a, pairing, s);
-    case 2: return launch_splice_lpb<2>(a, pairing, s);
-    case 3: return launch_splice_lpb<3>(a, pairing, s);
-    case 4: return launch_splice_lpb<4>(a, pairing, s);
-    default: return hipErrorInvalidValue;
-  }
-}
-
-hipError_t launch_evict_move(const EvictLaunch& a, int layers_per_block, hipStream_t s) {
-  switch (layers_per_block) {
-    case 1: return launch_evict_lpb<1>(a, s);
-    case 2: return launch_evict_lpb<2>(a, s);
-    case 3: return launch_evict_lpb<3>(a, s);
-    case 4: return launch_evict_lpb<4>(a, s);
-    default: return hipErrorInvalidValue;
-  }
+hipError_t launch_evict_move(const EvictLaunch& a, hipStream_t s) {
+  const int64_t grid = a.blocks_per_layer * a.num_layers + a.n_twrites;
+  if (grid == 0) return hipSuccess;
+  if (a.page_shift >= 3)
+    evict_move_kernel<true><<<dim3(static_cast<unsigned>(grid)), dim3(kFlatThreads), 0, s>>>(a);
+  else
+    evict_move_kernel<false><<<dim3(static_cast<unsigned>(grid)), dim3(kFlatThreads), 0, s>>>(a);
+  return hipGetLastError();
 }
 
 hipError_t launch_table_write(const TableLaunch& a, hipStream_t s) {

@@ -13,7 +13,6 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
-#include <cstdlib>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -123,11 +122,6 @@ class DeviceGuard {
   bool ok_ = true;
 };
 
-int env_int(const char* name, int dflt) {
-  const char* v = std::getenv(name);
-  return v && *v ? std::atoi(v) : dflt;
-}
-
 }  // namespace
 
 struct ll_pool {
@@ -152,7 +146,7 @@ struct ll_pool {
   bool profiling = false;
   std::vector<ProfRec> prof[2];
   std::vector<hipEvent_t> spare_events;
-  int layers_per_block = 1;
+  std::vector<int32_t> page_slot;  // per physical page: index in its table, during an eviction
 };
 
 namespace {
@@ -454,7 +448,7 @@ ll_status ll_pool_create(const ll_pool_desc* desc, ll_pool** out) {
   while ((1 << p->page_shift) < d.page_size) ++p->page_shift;
   p->seqs.resize(static_cast<size_t>(d.max_seqs));
   p->free.init(d.num_pages);
-  p->layers_per_block = std::min(4, std::max(1, env_int("LEYLINE_LAYERS_PER_BLOCK", 1)));
+  p->page_slot.assign(static_cast<size_t>(d.num_pages), -1);
   hipError_t e = hipMalloc(reinterpret_cast<void**>(&p->d_layers), sizeof(void*) * d.num_layers);
   if (e == hipSuccess)
     e = hipMemcpy(p->d_layers, p->layer_ptrs.data(), sizeof(void*) * d.num_layers, hipMemcpyHostToDevice);
@@ -611,7 +605,7 @@ ll_status leyline_splice(ll_pool* p, const ll_directive* dirs, int32_t n, void* 
   p->free.lowest(need, fresh);
 
   std::vector<ll::SpliceDir> ddirs(static_cast<size_t>(n));
-  std::vector<ll::SpliceTask> tasks;
+  std::vector<ll::SpliceTask> tasks, rot_tasks;
   TablePlan tp;
   std::vector<std::vector<int32_t>> new_tables(static_cast<size_t>(n));
   ll_plan_stats stats{};
@@ -628,40 +622,35 @@ ll_status leyline_splice(ll_pool* p, const ll_directive* dirs, int32_t n, void* 
     dd.stub = static_cast<const ll::chunk_t*>(d.mode == LL_FORGET ? nullptr : d.r_rows);
     const int64_t stride = d.r_layer_stride_bytes ? d.r_layer_stride_bytes : r * ll::kRowBytes;
     dd.stub_layer_chunks = stride / 16;
-    dd.s_start = d.s_start;
-    dd.r_len = r;
-    dd.delta = pl.delta;
-    dd.n_new = pl.n_new;
-    dd.rotate = (d.mode == LL_AMORTIZE && pl.delta != 0) ? 1 : 0;
     rope_table(p->desc.rope_base, ll::kRopeDim, pl.delta, dd.cos_, dd.sin_);
+    ll::SpliceTask base{};
+    base.dir = i;
+    base.rotate = (d.mode == LL_AMORTIZE && pl.delta != 0) ? 1 : 0;
+    base.s_start = d.s_start;
+    base.stub_end = d.s_start + r;
+    base.delta = pl.delta;
+    base.n_new = pl.n_new;
+    base.pre_page = base.down_page0 = base.down_page1 = -1;
+    base.down_lp0 = -1;
     std::vector<int32_t>& nt = new_tables[i];
     nt.resize(pl.reuse.size());
     for (size_t q = 0; q < pl.reuse.size(); ++q) {
       const int64_t a = static_cast<int64_t>(q) * P, b = std::min(a + P, pl.n_new);
+      ll::SpliceTask t = base;
+      t.q = static_cast<int32_t>(q);
       if (pl.reuse[q] >= 0) {
         nt[q] = T[pl.reuse[q]];
         if (pl.inplace[q]) {
-          ll::SpliceTask t{};
-          t.dir = i;
-          t.q = static_cast<int32_t>(q);
           t.dst_page = nt[q];
-          t.kind = ll::kRotateInPlace;
-          t.pre_page = t.down_page0 = t.down_page1 = -1;
-          tasks.push_back(t);
+          rot_tasks.push_back(t);
           stats.rows_rotated_inplace += b - a;
         }
         continue;
       }
       nt[q] = fresh[cursor++];
-      ll::SpliceTask t{};
-      t.dir = i;
-      t.q = static_cast<int32_t>(q);
       t.dst_page = nt[q];
-      t.kind = ll::kMoveRows;
-      t.pre_page = (a < d.s_start && static_cast<int64_t>(q) < old_pages) ? T[q] : -1;
+      if (a < d.s_start && static_cast<int64_t>(q) < old_pages) t.pre_page = T[q];
       const int64_t jd = std::max(a, d.s_start + r);  // first downstream row of the page
-      t.down_lp0 = -1;
-      t.down_page0 = t.down_page1 = -1;
       if (jd < b) {
         const int64_t lp0 = (jd - pl.delta) / P;
         t.down_lp0 = static_cast<int32_t>(lp0);
@@ -673,6 +662,11 @@ ll_status leyline_splice(ll_pool* p, const ll_directive* dirs, int32_t n, void* 
     }
     tp.add(d.seq_id, nt);
   }
+  const int64_t n_move_tasks = static_cast<int64_t>(tasks.size());
+  const int64_t n_rot_tasks = static_cast<int64_t>(rot_tasks.size());
+  tasks.insert(tasks.end(), rot_tasks.begin(), rot_tasks.end());
+  if (n_move_tasks * P * ll::kRowChunks >= (int64_t{1} << 32))
+    return fail(LL_EUNSUPPORTED, "one splice may move at most 2^32 / 72 rows per layer");
   stats.fresh_pages = need;
   stats.table_entries = static_cast<int64_t>(tp.packed.size());
   for (int32_t i = 0; i < n; ++i) {
@@ -705,10 +699,10 @@ ll_status leyline_splice(ll_pool* p, const ll_directive* dirs, int32_t n, void* 
   a.num_layers = p->desc.num_layers;
   a.page_shift = p->page_shift;
   a.tasks = reinterpret_cast<const ll::SpliceTask*>(sg->dev + o_t);
-  a.n_tasks = static_cast<int64_t>(tasks.size());
-  a.n_slabs = ceil_div(a.n_tasks * P, ll::kSlabRows);
-  const int lpb = p->layers_per_block;
-  a.n_move_blocks = a.n_slabs * ll::layer_groups(a.num_layers, lpb);
+  a.n_move_tasks = n_move_tasks;
+  a.n_rot_tasks = n_rot_tasks;
+  a.move_blocks_per_layer = ll::flat_blocks(n_move_tasks * P * ll::kRowChunks);
+  a.rot_blocks_per_layer = ll::flat_blocks(n_rot_tasks * P * (ll::kRowChunks - ll::kKpeChunk0));
   a.dirs = reinterpret_cast<const ll::SpliceDir*>(sg->dev + o_d);
   a.twrites = reinterpret_cast<const ll::TableWrite*>(sg->dev + o_w);
   a.tables = reinterpret_cast<const int32_t*>(sg->dev + o_p);
@@ -717,7 +711,7 @@ ll_status leyline_splice(ll_pool* p, const ll_directive* dirs, int32_t n, void* 
   a.page_table = p->desc.page_table;
   ProfRec rec{};
   if (p->profiling && (rc = prof_begin(p, 0, st, &rec))) return rc;
-  hipError_t e = ll::launch_splice(a, lpb, p->desc.rope_pairing, st);
+  hipError_t e = ll::launch_splice(a, p->desc.rope_pairing, st);
   if (e != hipSuccess) return device_fail(p, e, "splice_kernel launch");
   if (p->profiling) {
     rec.bytes = stats.alg_bytes + 4 * stats.table_entries;
@@ -801,6 +795,7 @@ ll_status kv_evict_compact(ll_pool* p, const int32_t* seq_ids, int32_t n, const 
       es[i].n_old = s.len;
       es[i].src_off = src_off[i] = so;
       es[i].reuse_off = reuse_off[i] = ro;
+      es[i].seq = seq_ids[i];
       so += s.len;
       ro += static_cast<int64_t>(s.pages.size());
     }
@@ -814,9 +809,11 @@ ll_status kv_evict_compact(ll_pool* p, const int32_t* seq_ids, int32_t n, const 
   sc.seqs = reinterpret_cast<const ll::EvictSeq*>(s1->dev + o_es);
   sc.n_seqs = n;
   sc.page_shift = p->page_shift;
+  sc.page_table = p->desc.page_table;
+  sc.max_pages_per_seq = p->desc.max_pages_per_seq;
   sc.counts = reinterpret_cast<int64_t*>(p->d_scratch);
   sc.reuse = reinterpret_cast<int32_t*>(p->d_scratch + off_reuse);
-  sc.src_of_dst = reinterpret_cast<int32_t*>(p->d_scratch + off_src);
+  sc.src_rows = reinterpret_cast<int32_t*>(p->d_scratch + off_src);
   ProfRec rec1{};
   if (p->profiling && (rc = prof_begin(p, 1, st, &rec1))) return rc;
   hipError_t e = ll::launch_keep_scan(sc, st);
@@ -834,25 +831,44 @@ ll_status kv_evict_compact(ll_pool* p, const int32_t* seq_ids, int32_t n, const 
   // Nothing has changed yet: the scan only wrote scratch.
 
   const int64_t* counts = reinterpret_cast<const int64_t*>(p->h_readback);
-  const int32_t* reuse = reinterpret_cast<const int32_t*>(p->h_readback + off_reuse);
-  int64_t need = 0;
-  std::vector<int64_t> n_new(static_cast<size_t>(n));
+  const int32_t* reuse_phys = reinterpret_cast<const int32_t*>(p->h_readback + off_reuse);
+  // The scan names reused pages physically; map them back to old logical
+  // pages (each sequence's pages are its own, so one slot array serves all).
   for (int32_t i = 0; i < n; ++i) {
     const SeqState& s = p->seqs[seq_ids[i]];
+    for (size_t k = 0; k < s.pages.size(); ++k) p->page_slot[s.pages[k]] = static_cast<int32_t>(k);
+  }
+  std::vector<int32_t> reuse(static_cast<size_t>(total_pages), -1);
+  int64_t need = 0;
+  std::vector<int64_t> n_new(static_cast<size_t>(n));
+  ll_status bad = LL_OK;
+  for (int32_t i = 0; i < n && bad == LL_OK; ++i) {
+    const SeqState& s = p->seqs[seq_ids[i]];
     n_new[i] = counts[i];
-    if (n_new[i] < 0 || n_new[i] > s.len) return fail(LL_EDEVICE, "keep scan returned a bad count");
+    if (n_new[i] < 0 || n_new[i] > s.len) {
+      bad = fail(LL_EDEVICE, "keep scan returned a bad count");
+      break;
+    }
     const int64_t pages = ceil_div(n_new[i], P);
     int64_t prev = -1;
     for (int64_t q = 0; q < pages; ++q) {
-      const int32_t x = reuse[reuse_off[i] + q];
+      const int32_t x = reuse_phys[reuse_off[i] + q];
       if (x < 0) {
         ++need;
         continue;
       }
-      if (x <= prev || x >= static_cast<int64_t>(s.pages.size())) return fail(LL_EDEVICE, "keep scan returned a bad page plan");
-      prev = x;
+      const int32_t lp = (x < p->desc.num_pages) ? p->page_slot[x] : -1;
+      if (lp <= prev || lp >= static_cast<int64_t>(s.pages.size()) || s.pages[lp] != x) {
+        bad = fail(LL_EDEVICE, "keep scan returned a bad page plan");
+        break;
+      }
+      reuse[reuse_off[i] + q] = lp;
+      prev = lp;
     }
   }
+  for (int32_t i = 0; i < n; ++i)
+    for (int32_t pg : p->seqs[seq_ids[i]].pages) p->page_slot[pg] = -1;
+  if (bad) return bad;
   if (need > p->free.count())
     return fail(LL_ENOMEM, "need %lld fresh pages, %lld free", (long long)need, (long long)p->free.count());
   std::vector<int32_t> fresh;
@@ -880,7 +896,6 @@ ll_status kv_evict_compact(ll_pool* p, const int32_t* seq_ids, int32_t n, const 
       nt[q] = fresh[cursor++];
       ll::EvictTask t{};
       t.src_off = src_off[i];
-      t.seq = seq_ids[i];
       t.q = static_cast<int32_t>(q);
       t.dst_page = nt[q];
       t.n_new = static_cast<int32_t>(n_new[i]);
@@ -909,28 +924,23 @@ ll_status kv_evict_compact(ll_pool* p, const int32_t* seq_ids, int32_t n, const 
   a.page_shift = p->page_shift;
   a.tasks = reinterpret_cast<const ll::EvictTask*>(s2->dev + o_t);
   a.n_tasks = static_cast<int64_t>(tasks.size());
-  a.n_slabs = ceil_div(a.n_tasks * P, ll::kSlabRows);
-  const int lpb = p->layers_per_block;
-  a.n_move_blocks = a.n_slabs * ll::layer_groups(a.num_layers, lpb);
-  a.src_of_dst = sc.src_of_dst;
-  a.page_table = p->desc.page_table;
+  if (a.n_tasks * P * ll::kRowChunks >= (int64_t{1} << 32))
+    return fail(LL_EUNSUPPORTED, "one eviction may move at most 2^32 / 72 rows per layer");
+  a.blocks_per_layer = ll::flat_blocks(a.n_tasks * P * ll::kRowChunks);
+  a.src_rows = sc.src_rows;
+  a.twrites = reinterpret_cast<const ll::TableWrite*>(s2->dev + o_w);
+  a.tables = reinterpret_cast<const int32_t*>(s2->dev + o_p);
+  a.n_twrites = static_cast<int32_t>(tp.writes.size());
   a.max_pages_per_seq = p->desc.max_pages_per_seq;
+  a.page_table = p->desc.page_table;
   ProfRec rec{};
-  if (p->profiling && a.n_move_blocks && (rc = prof_begin(p, 0, st, &rec))) return rc;
-  e = ll::launch_evict_move(a, lpb, st);
+  if (p->profiling && (rc = prof_begin(p, 0, st, &rec))) return rc;
+  e = ll::launch_evict_move(a, st);
   if (e != hipSuccess) return device_fail(p, e, "evict_move_kernel launch");
-  if (p->profiling && a.n_move_blocks) {
-    rec.bytes = stats.alg_bytes;
+  if (p->profiling) {
+    rec.bytes = stats.alg_bytes + 4 * stats.table_entries;
     if ((rc = prof_end(p, 0, st, &rec))) return rc;
   }
-  ll::TableLaunch ta{};
-  ta.twrites = reinterpret_cast<const ll::TableWrite*>(s2->dev + o_w);
-  ta.tables = reinterpret_cast<const int32_t*>(s2->dev + o_p);
-  ta.n_twrites = static_cast<int32_t>(tp.writes.size());
-  ta.max_pages_per_seq = p->desc.max_pages_per_seq;
-  ta.page_table = p->desc.page_table;
-  e = ll::launch_table_write(ta, st);
-  if (e != hipSuccess) return device_fail(p, e, "table_write_kernel launch");
   if ((rc = end_call(p, s2, st))) return rc;
 
   for (int32_t pg : fresh) p->free.take(pg);

@@ -168,7 +168,7 @@ def test_splice_successive_directives_and_forget():
     rotated several times), then a FORGET."""
     say("successive splices")
     dp = _pool(2, 200, 16, 2, 200, seed=41)
-    dp.set_pages(0, permuted_pages(41, 200)[:64], 1000)
+    dp.set_pages(0, permuted_pages(41, 200)[:63], 1000)
     dp.set_pages(1, permuted_pages(41, 200)[64:100], 570)
     dp.snapshot_rows()
     rng = np.random.default_rng(41)
