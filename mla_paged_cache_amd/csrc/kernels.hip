@@ -165,11 +165,14 @@ __device__ __forceinline__ T load_task(const T* tasks, int64_t i) {
 }
 
 // Flat gather.  Blocks [0, L * move_blocks_per_layer) move rows of fresh
-// pages: chunk c of a layer is chunk c % 72 of row c / 72 of the move-task
-// list.  The next L * rot_blocks_per_layer blocks rotate k_pe in place:
-// chunk c is k_pe chunk c % 8 of row c / 8 of the rotate-task list.  The
-// remaining blocks rewrite page-table rows (no block reads the table).
-// PAIRING: 0 interleaved, 1 half-split.  WAVE_TASK: page size >= 8.
+// pages.  Within one page-task of P rows the 72 * P chunks are ordered c_kv
+// first (chunk 64 * row + k, k < 64) and then k_pe (64 * P + 8 * row + k,
+// k < 8): for P >= 8 every wave is then either a pure copy wave or a pure
+// rotate wave, and the rotation code is skipped by the copy waves.  The next
+// L * rot_blocks_per_layer blocks rotate k_pe in place (chunk 8 * row + k of
+// the rotate-task list).  The remaining blocks rewrite page-table rows (no
+// block reads the table).  PAIRING: 0 interleaved, 1 half-split.
+// WAVE_TASK: page size >= 8.
 template <int PAIRING, bool WAVE_TASK>
 __global__ __launch_bounds__(kFlatThreads) void splice_kernel(SpliceLaunch a) {
   const int64_t b = blockIdx.x;
@@ -186,21 +189,32 @@ __global__ __launch_bounds__(kFlatThreads) void splice_kernel(SpliceLaunch a) {
   const uint32_t c = static_cast<uint32_t>((bb - static_cast<int64_t>(l) * bpl) * kFlatThreads + threadIdx.x);
   const int shift = a.page_shift;
   const uint32_t pmask = (1u << shift) - 1u;
+  constexpr uint32_t kKpeChunks = kRowChunks - kKpeChunk0;
 
-  uint32_t row_flat, col;
+  uint32_t task, r, col;
   if (in_place) {
-    row_flat = c >> 3;
-    col = kKpeChunk0 + (c & 7u);
+    const uint32_t row_flat = c / kKpeChunks;
+    task = row_flat >> shift;
+    r = row_flat & pmask;
+    col = kKpeChunk0 + (c - row_flat * kKpeChunks);
   } else {
-    row_flat = c / kRowChunks;
-    col = c - row_flat * kRowChunks;
+    task = (c / kRowChunks) >> shift;
+    const uint32_t lc = c - task * (static_cast<uint32_t>(kRowChunks) << shift);
+    const uint32_t ckv_chunks = static_cast<uint32_t>(kKpeChunk0) << shift;
+    if (lc < ckv_chunks) {
+      r = lc / kKpeChunk0;
+      col = lc - r * kKpeChunk0;
+    } else {
+      const uint32_t k = lc - ckv_chunks;
+      r = k / kKpeChunks;
+      col = kKpeChunk0 + (k - r * kKpeChunks);
+    }
   }
-  const int64_t ti = static_cast<int64_t>(row_flat >> shift) + (in_place ? a.n_move_tasks : 0);
+  const int64_t ti = static_cast<int64_t>(task) + (in_place ? a.n_move_tasks : 0);
   const int64_t t_end = in_place ? a.n_move_tasks + a.n_rot_tasks : a.n_move_tasks;
   bool live = ti < t_end;
   const SpliceTask t = load_task<WAVE_TASK>(a.tasks, live ? ti : 0);
-  const uint32_t r = row_flat & pmask;
-  const int64_t j = (static_cast<int64_t>(t.q) << shift) + r;
+  const int32_t j = (t.q << shift) + static_cast<int32_t>(r);
   live = live && j < t.n_new;
 
   const chunk_t* layer = a.layers[l];
@@ -213,10 +227,9 @@ __global__ __launch_bounds__(kFlatThreads) void splice_kernel(SpliceLaunch a) {
   } else if (j < t.s_start) {
     src = layer + ((static_cast<int64_t>(t.pre_page) << shift) + (j & pmask)) * kRowChunks;
   } else if (j < t.stub_end) {
-    const SpliceDir& d = a.dirs[t.dir];
-    src = d.stub + l * d.stub_layer_chunks + (j - t.s_start) * kRowChunks;
+    src = t.stub + l * t.stub_layer_chunks + static_cast<int64_t>(j - t.s_start) * kRowChunks;
   } else {
-    const int64_t o = j - t.delta;
+    const int32_t o = j - t.delta;
     const int32_t pg = ((o >> shift) == t.down_lp0) ? t.down_page0 : t.down_page1;
     src = layer + ((static_cast<int64_t>(pg) << shift) + (o & pmask)) * kRowChunks;
     rot = t.rotate != 0;
@@ -224,7 +237,10 @@ __global__ __launch_bounds__(kFlatThreads) void splice_kernel(SpliceLaunch a) {
   chunk_t v = chunk_t{0u, 0u, 0u, 0u};
   if (live) v = __builtin_nontemporal_load(src + col);
   const int kc = static_cast<int>(col) - kKpeChunk0;
-  v = rotate_kpe<PAIRING>(v, live && rot && kc >= 0, kc, a.dirs + t.dir);
+  if (!WAVE_TASK || kc >= 0) {
+    // k_pe waves (or mixed waves at page sizes below 8)
+    v = rotate_kpe<PAIRING>(v, live && rot && kc >= 0, kc, a.dirs + t.dir);
+  }
   if (live) __builtin_nontemporal_store(v, const_cast<chunk_t*>(layer) + dst_row * kRowChunks + col);
 }
 

@@ -32,7 +32,8 @@ enum TaskKind : int32_t {
 
 // One destination page of a splice, self-contained (64 bytes) so that a
 // thread needs one descriptor load before its data load.  Sources are
-// physical pages, so the kernel never reads the page table it rewrites.
+// physical pages, so the kernel never reads the page table it rewrites.  Row
+// indices fit in 32 bits (the pool checks max_pages_per_seq * page_size).
 struct alignas(16) SpliceTask {
   int32_t dst_page;    // physical page written (or rotated in place)
   int32_t pre_page;    // physical page of old logical page q (prefix rows), or -1
@@ -40,18 +41,18 @@ struct alignas(16) SpliceTask {
   int32_t down_page1;  // physical page of down_lp0 + 1, or -1
   int32_t q;           // new logical page
   int32_t down_lp0;    // first old logical page feeding downstream rows
-  int32_t dir;         // index into the SpliceDir array (stub rows, cos/sin)
+  int32_t dir;         // index into the SpliceDir array (cos/sin)
   int32_t rotate;      // 1 when downstream k_pe turns (AMORTIZE, delta != 0)
-  int64_t s_start;
-  int64_t stub_end;    // s_start + r_len
-  int64_t delta;
-  int64_t n_new;
-};
-
-// Per-directive data only some threads need: stub rows and the rotation.
-struct alignas(16) SpliceDir {
+  int32_t s_start;
+  int32_t stub_end;    // s_start + r_len
+  int32_t delta;
+  int32_t n_new;
   const chunk_t* stub;         // R rows of layer 0, in 16-byte chunks
   int64_t stub_layer_chunks;   // chunks between layers of R
+};
+
+// The rotation table of a directive, read only by k_pe chunks.
+struct alignas(16) SpliceDir {
   float cos_[kHalfPairs];      // float32 of float64 cos(delta * theta_j)
   float sin_[kHalfPairs];
 };

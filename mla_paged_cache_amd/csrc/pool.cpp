@@ -434,8 +434,9 @@ ll_status ll_pool_create(const ll_pool_desc* desc, ll_pool** out) {
     if (!d.layer_base[i]) return fail(LL_EINVAL, "layer_base[%d] is NULL", i);
     if (reinterpret_cast<uintptr_t>(d.layer_base[i]) & 15) return fail(LL_EINVAL, "layer_base[%d] is not 16-byte aligned", i);
   }
-  if (static_cast<int64_t>(d.num_pages) * d.page_size >= (int64_t{1} << 31))
-    return fail(LL_EUNSUPPORTED, "more than 2^31 rows per layer");
+  if (static_cast<int64_t>(d.num_pages) * d.page_size >= (int64_t{1} << 31) ||
+      static_cast<int64_t>(d.max_pages_per_seq) * d.page_size >= (int64_t{1} << 31))
+    return fail(LL_EUNSUPPORTED, "more than 2^31 rows per layer or per sequence");
   if (d.device < 0) return fail(LL_EINVAL, "device must be >= 0");
 
   DeviceGuard g(d.device);
@@ -619,17 +620,16 @@ ll_status leyline_splice(ll_pool* p, const ll_directive* dirs, int32_t n, void* 
     ll::SpliceDir& dd = ddirs[i];
     std::memset(&dd, 0, sizeof dd);
     const int64_t r = d.mode == LL_FORGET ? 0 : d.r_len;
-    dd.stub = static_cast<const ll::chunk_t*>(d.mode == LL_FORGET ? nullptr : d.r_rows);
-    const int64_t stride = d.r_layer_stride_bytes ? d.r_layer_stride_bytes : r * ll::kRowBytes;
-    dd.stub_layer_chunks = stride / 16;
     rope_table(p->desc.rope_base, ll::kRopeDim, pl.delta, dd.cos_, dd.sin_);
     ll::SpliceTask base{};
     base.dir = i;
     base.rotate = (d.mode == LL_AMORTIZE && pl.delta != 0) ? 1 : 0;
-    base.s_start = d.s_start;
-    base.stub_end = d.s_start + r;
-    base.delta = pl.delta;
-    base.n_new = pl.n_new;
+    base.s_start = static_cast<int32_t>(d.s_start);
+    base.stub_end = static_cast<int32_t>(d.s_start + r);
+    base.delta = static_cast<int32_t>(pl.delta);
+    base.n_new = static_cast<int32_t>(pl.n_new);
+    base.stub = static_cast<const ll::chunk_t*>(d.mode == LL_FORGET ? nullptr : d.r_rows);
+    base.stub_layer_chunks = (d.r_layer_stride_bytes ? d.r_layer_stride_bytes : r * ll::kRowBytes) / 16;
     base.pre_page = base.down_page0 = base.down_page1 = -1;
     base.down_lp0 = -1;
     std::vector<int32_t>& nt = new_tables[i];
