@@ -1,29 +1,40 @@
-"""Benchmark of the splice hot path on one MI355X.
+"""Benchmark of the splice / evict hot path on one MI355X.
 
-Workload (default): a DeepSeek-V2-Lite shaped MLA cache, 27 layers, one
-sequence of 32768 tokens, rows c_kv 512 + k_pe 64 bf16 ~ N(0,1), page size 16,
-pages randomly permuted in a pool of 4096 pages; one AMORTIZE splice drops
-three 2048-token tool turns [8192, 14336) for a 24-row stub (Delta = -6120),
-moving and rotating every downstream row ("Leyline: KV Cache Directives for
-Agentic Inference", sections 2.1-2.3).
+Default workload (the headline): a DeepSeek-V2-Lite shaped MLA cache, 27
+layers, one sequence of 32768 tokens, rows c_kv 512 + k_pe 64 bf16 ~ N(0,1),
+page size 16, pages randomly permuted in a pool of 4096 pages; one AMORTIZE
+splice drops three 2048-token tool turns [8192, 14336) for a 24-row stub
+(Delta = -6120), moving and rotating every downstream row ("Leyline: KV Cache
+Directives for Agentic Inference", sections 2.1-2.3).
 
 A step is one whole splice call through the C ABI (host plan, one upload, one
 kernel launch that moves rows, rotates k_pe and rewrites the page table),
 preceded by restoring the sequence's original page table (the splice never
 writes the old pages, so the pristine state comes back by table alone).
 `value` is the row bytes the splice must move per step divided by the wall
-time per step.  The roofline object times the row kernel alone with HIP
-events recorded on the stream it runs on.  The CPU baseline runs the oracle
-on the same workload on the host and checks the GPU result against it.
+time per step.  The roofline object times the row kernel alone with HIP events
+recorded on the stream it runs on; its `traffic` is the HBM traffic per launch
+from the rocprofv3 counter summary in profiles/, used only while that summary
+was taken on the current kernel source.  The CPU baseline runs the oracle on
+the same workload on the host and checks the GPU result against it.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+Other workloads (one JSON line each, not the headline):
+  --workload splice_16x32k_27layer   16 sequences x 32768 tokens, one random
+                                     directive each, one batched call
+  --workload evict_256x16k_27layer_p16 / _p1
+                                     KV-streams eviction of 256 rollouts x
+                                     16384 tokens under random turn drops
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
 
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import statistics
 import sys
 import time
@@ -35,8 +46,6 @@ sys.path.insert(0, ROOT)
 
 METRIC = "downstream KV GB/s moved+rotated (% HBM peak); splice latency @32k ctx"
 HBM_PEAK_GBS = 8000.0
-LAYERS, TOKENS, PAGE, POOL_PAGES = 27, 32768, 16, 4096
-S_START, S_END, STUB = 8192, 14336, 24
 ROW = 576
 
 
@@ -48,22 +57,89 @@ def parse():
     ap.add_argument("--latency-runs", type=int, default=25)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--workload", default="splice_32k_27layer",
+                    choices=["splice_32k_27layer", "splice_16x32k_27layer", "evict_256x16k_27layer_p16",
+                             "evict_256x16k_27layer_p1"])
     return ap.parse_args()
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only: the splice path runs per GPU with no cross-GPU exchange "
-              f"(--gpus {args.gpus} is not supported)", file=sys.stderr)
-        sys.exit(2)
+def profiled_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, or None when
+    the summary is missing or was taken on other kernel source."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"traffic_bytes_per_launch: (\d+)", text)
+    h = re.search(r"kernels_hip_sha256_16: ([0-9a-f]+)", text)
+    src = open(os.path.join(ROOT, "mla_paged_cache_amd", "csrc", "kernels.hip"), "rb").read()
+    if not m or not h or hashlib.sha256(src).hexdigest()[:16] != h.group(1):
+        return None
+    return int(m.group(1))
+
+
+def copy_ceiling(torch, dev, n_bytes):
+    """Plain device copy of n_bytes (read + write), for context."""
+    src = torch.empty(n_bytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(20):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    return 2 * n_bytes * 20 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+
+
+def roofline(kernel, workload, launches, kernel_ms, kernel_bytes):
+    k_avg_ms = kernel_ms / max(1, launches)
+    per = kernel_bytes // max(1, launches)
+    achieved = per / (k_avg_ms * 1e-3) / 1e9 if k_avg_ms > 0 else 0.0
+    return {
+        "bound": "hbm",
+        "achieved": round(achieved, 2),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBS, 4),
+        "traffic": profiled_traffic(kernel, workload),
+        "kernel": kernel,
+        "kernel_avg_us": round(k_avg_ms * 1e3, 2),
+        "bytes_per_launch": per,
+    }
+
+
+def base_line(args, workload, value, ms_per_step, config):
+    return {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": workload, **config},
+    }
+
+
+# ------------------------------------------------------------------ splice --
+
+def bench_splice_32k(args):
     import torch
     from mla_paged_cache_amd import leyline as L
     from synth import permuted_pages, random_rows_torch
 
+    LAYERS, TOKENS, PAGE, POOL_PAGES = 27, 32768, 16, 4096
+    S_START, S_END, STUB = 8192, 14336, 24
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    stream = torch.cuda.current_stream()
     data = random_rows_torch(0, (LAYERS, POOL_PAGES, PAGE, ROW), dev)
     stub = random_rows_torch(1, (LAYERS, STUB, ROW), dev)
     table = torch.full((1, TOKENS // PAGE + 8), -1, dtype=torch.int32, device=dev)
@@ -74,7 +150,6 @@ def main():
     def restore():
         pool.seq_set_pages(0, T, TOKENS)
 
-    # snapshot for the CPU baseline / parity check, taken before any splice
     host_before = None
     if not args.no_cpu_baseline:
         torch.cuda.synchronize()
@@ -83,8 +158,7 @@ def main():
     restore()
     pool.splice(directive)
     torch.cuda.synchronize()
-    stats = pool.last_stats()
-    alg_bytes = stats.alg_bytes
+    alg_bytes = pool.last_stats().alg_bytes
     _, _, new_table = pool.seq_get(0)
     gpu_after = None
     if host_before is not None:
@@ -92,7 +166,7 @@ def main():
         phys = torch.from_numpy(new_table.astype(np.int64)[j // PAGE] * PAGE + j % PAGE).to(dev)
         gpu_after = data.view(LAYERS, -1, ROW)[:, phys].view(torch.int16).cpu().numpy().view(np.uint16)
 
-    # ---- throughput: K whole steps, bracketed by synchronize
+    # throughput: K whole steps, bracketed by synchronize
     for _ in range(args.warmup):
         restore()
         pool.splice(directive)
@@ -110,10 +184,8 @@ def main():
     launches, kernel_ms, kernel_bytes = pool.profile_read(0)
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     value = alg_bytes / (ms_per_step * 1e-3) / 1e9
-    k_avg_ms = kernel_ms / max(1, launches)
-    achieved = (kernel_bytes / max(1, launches)) / (k_avg_ms * 1e-3) / 1e9
 
-    # ---- latency: API call to stream completion, MALL flushed before each
+    # latency: API call to stream completion, MALL flushed before each run
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     lat = []
     for _ in range(args.latency_runs):
@@ -126,72 +198,30 @@ def main():
         lat.append((time.perf_counter() - a) * 1e6)
     del flush
 
-    # ---- plain device copy of the same byte count, for context
-    n_copy = alg_bytes // 2
-    src = torch.empty(n_copy, dtype=torch.uint8, device=dev)
-    dst = torch.empty_like(src)
-    for _ in range(3):
-        dst.copy_(src)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(20):
-        dst.copy_(src)
-    e1.record()
-    torch.cuda.synchronize()
-    copy_gbs = 2 * n_copy * 20 / (e0.elapsed_time(e1) * 1e-3) / 1e9
-    del src, dst
-
-    out = {
-        "metric": METRIC,
-        "value": round(value, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic",
-        "config": {
-            "workload": "splice_32k_27layer",
-            "layers": LAYERS, "tokens": TOKENS, "page_size": PAGE, "pool_pages": POOL_PAGES,
-            "span": [S_START, S_END], "stub_rows": STUB, "delta": STUB - (S_END - S_START),
-            "storage": "bf16 rows c_kv 512 + k_pe 64, rotation in f32",
-            "alg_bytes_per_step": alg_bytes,
-        },
-        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
-        "splice_latency_us": {"median": round(statistics.median(lat), 1), "min": round(min(lat), 1),
-                              "max": round(max(lat), 1), "runs": len(lat)},
-        "roofline": {
-            "bound": "hbm",
-            "achieved": round(achieved, 2),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
-            "kernel": "splice_kernel",
-            "kernel_avg_us": round(k_avg_ms * 1e3, 2),
-            "bytes_per_launch": kernel_bytes // max(1, launches),
-        },
-        "copy_ceiling_gbs": round(copy_gbs, 1),
-        "cpu_baseline": None,
-    }
-
+    out = base_line(args, "splice_32k_27layer", value, ms_per_step, {
+        "layers": LAYERS, "tokens": TOKENS, "page_size": PAGE, "pool_pages": POOL_PAGES,
+        "span": [S_START, S_END], "stub_rows": STUB, "delta": STUB - (S_END - S_START),
+        "storage": "bf16 rows c_kv 512 + k_pe 64, rotation in f32", "alg_bytes_per_step": alg_bytes})
+    out["pct_hbm_peak"] = round(100.0 * value / HBM_PEAK_GBS, 2)
+    out["splice_latency_us"] = {"median": round(statistics.median(lat), 1), "min": round(min(lat), 1),
+                                "max": round(max(lat), 1), "runs": len(lat)}
+    out["roofline"] = roofline("splice_kernel", "splice_32k_27layer", launches, kernel_ms, kernel_bytes)
+    out["copy_ceiling_gbs"] = round(copy_ceiling(torch, dev, alg_bytes // 2), 1)
+    out["cpu_baseline"] = None
     if host_before is not None:
-        out["cpu_baseline"] = cpu_baseline(host_before, gpu_after, T, alg_bytes, args.cpu_seconds)
-    print(json.dumps(out), flush=True)
+        out["cpu_baseline"] = cpu_baseline_splice(host_before, gpu_after, T, alg_bytes, args.cpu_seconds,
+                                                  LAYERS, TOKENS, PAGE, POOL_PAGES, S_START, S_END, STUB)
     pool.close()
+    return out
 
 
-def cpu_baseline(host_before, gpu_after, T, alg_bytes, seconds):
+def cpu_baseline_splice(host_before, gpu_after, T, alg_bytes, seconds, LAYERS, TOKENS, PAGE, POOL_PAGES,
+                        S_START, S_END, STUB):
     """The oracle, as it stands, on the same splice on the host: repeated
     until `seconds` have passed; also checks the GPU result against it."""
-    from oracle import leyline_oracle as O
-    from synth import random_rows_torch  # noqa: F401  (same generator as the device pool)
     import torch
+    from oracle import leyline_oracle as O
+    from synth import random_rows_torch
 
     st = O.CacheState.empty(0, POOL_PAGES, PAGE, TOKENS // PAGE + 8, with_rows=False)
     st.layers = [host_before[i] for i in range(LAYERS)]
@@ -205,11 +235,8 @@ def cpu_baseline(host_before, gpu_after, T, alg_bytes, seconds):
         new, _ = O.splice(st, d)
         t += time.perf_counter() - a
         runs += 1
-    # parity of the timed GPU workload against the oracle
     for layer in range(LAYERS):
-        exp = new.logical_rows(0, layer)
-        got = gpu_after[layer]
-        if not np.array_equal(exp[:, :512], got[:, :512]) or not np.array_equal(exp[:, 512:], got[:, 512:]):
+        if not np.array_equal(new.logical_rows(0, layer), gpu_after[layer]):
             raise SystemExit(f"GPU splice differs from the oracle on layer {layer}")
     return {
         "value": round(alg_bytes * runs / t / 1e9, 4),
@@ -219,6 +246,150 @@ def cpu_baseline(host_before, gpu_after, T, alg_bytes, seconds):
         "sample": f"the full 27-layer splice, run {runs} times ({t:.1f} s) by the numpy oracle on one core "
                   f"({len(os.sched_getaffinity(0))} available); GPU result matched it bit-exactly",
     }
+
+
+def bench_splice_batched(args):
+    """16 sequences x 32768 tokens x 27 layers in one pool, one random
+    directive each (span U[256,8192], stub U[8,64], start U[1024,len-span]),
+    applied in one call."""
+    import torch
+    from mla_paged_cache_amd import leyline as L
+    from synth import draw_span, np_rng, permuted_pages, random_rows_torch
+
+    LAYERS, TOKENS, PAGE, SEQS = 27, 32768, 16, 16
+    per = TOKENS // PAGE
+    POOL_PAGES = 2 * SEQS * per
+    dev = torch.device("cuda:0")
+    data = random_rows_torch(0, (LAYERS, POOL_PAGES, PAGE, ROW), dev)
+    table = torch.full((SEQS, per + 8), -1, dtype=torch.int32, device=dev)
+    pool = L.Pool(data, table)
+    perm = permuted_pages(0, SEQS * per)
+    rng = np_rng(0, 4)
+    dirs = []
+    for s in range(SEQS):
+        d = draw_span(rng, TOKENS, 256, 8192, 8, 64)
+        stub = random_rows_torch(100 + s, (LAYERS, d.r_len, ROW), dev)
+        dirs.append(L.Directive(s, d.s_start, d.s_end, stub))
+
+    def restore():
+        for s in range(SEQS):
+            pool.seq_set_pages(s, perm[s * per:(s + 1) * per], TOKENS)
+
+    restore()
+    pool.splice(dirs)
+    torch.cuda.synchronize()
+    alg_bytes = pool.last_stats().alg_bytes
+    for _ in range(args.warmup):
+        restore()
+        pool.splice(dirs)
+    torch.cuda.synchronize()
+    pool.profile_read(0)
+    pool.set_profiling(True)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        restore()
+        pool.splice(dirs)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    pool.set_profiling(False)
+    launches, kernel_ms, kernel_bytes = pool.profile_read(0)
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    out = base_line(args, "splice_16x32k_27layer", alg_bytes / (ms_per_step * 1e-3) / 1e9, ms_per_step, {
+        "layers": LAYERS, "tokens": TOKENS, "sequences": SEQS, "page_size": PAGE, "pool_pages": POOL_PAGES,
+        "alg_bytes_per_step": alg_bytes, "restore_in_step": "16 page-table rows"})
+    out["roofline"] = roofline("splice_kernel", "splice_16x32k_27layer", launches, kernel_ms, kernel_bytes)
+    out["cpu_baseline"] = None
+    pool.close()
+    return out
+
+
+# ------------------------------------------------------------------- evict --
+
+def bench_evict(args, page):
+    """256 rollouts x 16384 tokens x 27 layers; per-rollout keep masks from
+    random turn drops (turns U[200,2000], each dropped with p = 0.5); one
+    eviction call for all rollouts.  Restoring the tables between steps is
+    outside the timed call."""
+    import torch
+    from mla_paged_cache_amd import leyline as L
+    from synth import np_rng, permuted_pages, turn_drop_mask
+
+    LAYERS, ROLL, TOKENS = 27, 256, 16384
+    per = TOKENS // page
+    extra = ROLL * per // 2 if page > 1 else 0
+    POOL_PAGES = ROLL * per + extra
+    dev = torch.device("cuda:0")
+    data = torch.empty((LAYERS, POOL_PAGES, page, ROW), dtype=torch.int16, device=dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    flat = data.view(-1)
+    step = 1 << 28
+    for i in range(0, flat.numel(), step):
+        k = min(step, flat.numel() - i)
+        flat[i:i + k] = torch.randint(-32768, 32767, (k,), generator=g, device=dev, dtype=torch.int16)
+    data = data.view(torch.bfloat16)
+    table = torch.full((ROLL, per), -1, dtype=torch.int32, device=dev)
+    pool = L.Pool(data, table)
+    perm = permuted_pages(0, ROLL * per)
+    rng = np_rng(0, 6)
+    masks = np.concatenate([turn_drop_mask(rng, TOKENS) for _ in range(ROLL)])
+    keep = torch.from_numpy(masks).to(dev)
+    offsets = np.arange(ROLL, dtype=np.int64) * TOKENS
+    seqs = list(range(ROLL))
+
+    def restore():
+        for s in range(ROLL):
+            pool.seq_set_pages(s, perm[s * per:(s + 1) * per], TOKENS)
+
+    restore()
+    pool.evict(seqs, keep, offsets)
+    torch.cuda.synchronize()
+    stats = pool.last_stats()
+    alg_bytes = stats.alg_bytes
+    times = []
+    pool.profile_read(0)
+    pool.profile_read(1)
+    for i in range(args.warmup + args.steps):
+        restore()
+        torch.cuda.synchronize()
+        if i == args.warmup:
+            pool.set_profiling(True)
+        a = time.perf_counter()
+        pool.evict(seqs, keep, offsets)
+        torch.cuda.synchronize()
+        if i >= args.warmup:
+            times.append(time.perf_counter() - a)
+    pool.set_profiling(False)
+    launches, kernel_ms, kernel_bytes = pool.profile_read(0)
+    s_launches, scan_ms, _ = pool.profile_read(1)
+    ms_per_step = 1e3 * statistics.median(times)
+    name = f"evict_256x16k_27layer_p{page}"
+    out = base_line(args, name, alg_bytes / (ms_per_step * 1e-3) / 1e9, ms_per_step, {
+        "layers": LAYERS, "rollouts": ROLL, "tokens": TOKENS, "page_size": page, "pool_pages": POOL_PAGES,
+        "mask": "turn drops U[200,2000], p=0.5", "rows_kept": int(masks.sum()),
+        "rows_moved_per_layer": stats.rows_moved, "fresh_pages": stats.fresh_pages,
+        "alg_bytes_per_step": alg_bytes, "step": "one kv_evict_compact call, median"})
+    out["metric"] = "KV-streams eviction: row bytes moved GB/s; call latency"
+    out["roofline"] = roofline("evict_move_kernel", name, launches, kernel_ms, kernel_bytes)
+    out["keep_scan_us"] = round(scan_ms * 1e3 / max(1, s_launches), 2)
+    out["cpu_baseline"] = None
+    pool.close()
+    return out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: the splice path runs per GPU with no cross-GPU exchange "
+              f"(--gpus {args.gpus} is not supported)", file=sys.stderr)
+        sys.exit(2)
+    if args.workload == "splice_32k_27layer":
+        out = bench_splice_32k(args)
+    elif args.workload == "splice_16x32k_27layer":
+        out = bench_splice_batched(args)
+    else:
+        out = bench_evict(args, 16 if args.workload.endswith("p16") else 1)
+    print(json.dumps(out), flush=True)
 
 
 if __name__ == "__main__":

@@ -99,6 +99,10 @@ struct Staging {
   bool pending = false;
 };
 
+// Staging slots used round-robin: the host can run this many calls ahead of
+// the device before it waits for a slot to come back.
+constexpr int kStagingSlots = 8;
+
 struct ProfRec {
   hipEvent_t start, stop;
   int64_t bytes;
@@ -132,7 +136,7 @@ struct ll_pool {
   void** d_layers = nullptr;
   std::vector<SeqState> seqs;
   FreePages free;
-  Staging stage[2];
+  Staging stage[kStagingSlots];
   int stage_next = 0;
   // eviction scratch: device [counts | reuse | src_of_dst], pinned readback
   char* d_scratch = nullptr;
@@ -177,7 +181,7 @@ hipEvent_t take_event(ll_pool* p) {
 // last use, grow if needed.  Returns the slot.
 ll_status stage_acquire(ll_pool* p, size_t bytes, Staging** out) {
   Staging& s = p->stage[p->stage_next];
-  p->stage_next ^= 1;
+  p->stage_next = (p->stage_next + 1) % kStagingSlots;
   if (s.pending) {
     hipError_t e = hipEventSynchronize(s.done);
     if (e != hipSuccess) return device_fail(p, e, "hipEventSynchronize(staging)");
@@ -266,6 +270,18 @@ ll_status write_tables(ll_pool* p, const TablePlan& tp, hipStream_t st) {
   ll_status rc = begin_call(p, st);
   if (rc) return rc;
   Staging* s = nullptr;
+  if (tp.writes.size() == 1) {
+    // one row: copy it straight from pinned staging into the page table
+    const ll::TableWrite& w = tp.writes[0];
+    if ((rc = stage_acquire(p, stage_bytes_for({tp.packed.size() * 4}), &s))) return rc;
+    const size_t o = stage_put(s, tp.packed.data(), tp.packed.size() * 4);
+    if (w.count > 0) {
+      hipError_t e = hipMemcpyAsync(p->desc.page_table + static_cast<int64_t>(w.seq) * p->desc.max_pages_per_seq,
+                                    s->host + o, static_cast<size_t>(w.count) * 4, hipMemcpyHostToDevice, st);
+      if (e != hipSuccess) return device_fail(p, e, "hipMemcpyAsync(page table row)");
+    }
+    return end_call(p, s, st);
+  }
   rc = stage_acquire(p, stage_bytes_for({tp.writes.size() * sizeof(ll::TableWrite), tp.packed.size() * 4}), &s);
   if (rc) return rc;
   const size_t o_w = stage_put(s, tp.writes.data(), tp.writes.size() * sizeof(ll::TableWrite));
@@ -453,7 +469,8 @@ ll_status ll_pool_create(const ll_pool_desc* desc, ll_pool** out) {
   hipError_t e = hipMalloc(reinterpret_cast<void**>(&p->d_layers), sizeof(void*) * d.num_layers);
   if (e == hipSuccess)
     e = hipMemcpy(p->d_layers, p->layer_ptrs.data(), sizeof(void*) * d.num_layers, hipMemcpyHostToDevice);
-  for (int i = 0; i < 2 && e == hipSuccess; ++i) e = hipEventCreateWithFlags(&p->stage[i].done, hipEventDisableTiming);
+  for (int i = 0; i < kStagingSlots && e == hipSuccess; ++i)
+    e = hipEventCreateWithFlags(&p->stage[i].done, hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&p->readback_ev, hipEventDisableTiming);
   if (e != hipSuccess) {
     ll_pool_destroy(p);
@@ -546,27 +563,45 @@ ll_status ll_seq_set_pages(ll_pool* p, int32_t seq, const int32_t* pages, int64_
   if (need > p->desc.max_pages_per_seq) return fail(LL_ERANGE, "%lld rows exceed the page-table row", (long long)n_tokens);
   if (need > 0 && !pages) return fail(LL_EINVAL, "pages is NULL");
   SeqState& s = p->seqs[seq];
-  std::vector<char> own(static_cast<size_t>(p->desc.num_pages), 0), seen(static_cast<size_t>(p->desc.num_pages), 0);
+  // page_slot marks (reset before returning): -2 owned, -3 listed, -4 both
+  std::vector<int32_t>& mark = p->page_slot;
   if (s.used)
-    for (int32_t pg : s.pages) own[pg] = 1;
-  for (int64_t i = 0; i < need; ++i) {
-    const int32_t pg = pages[i];
-    if (pg < 0 || pg >= p->desc.num_pages) return fail(LL_EINVAL, "page %d out of range", pg);
-    if (seen[pg]) return fail(LL_EINVAL, "page %d listed twice", pg);
-    seen[pg] = 1;
-    if (!p->free.is_free(pg) && !own[pg]) return fail(LL_EINVAL, "page %d is not free", pg);
+    for (int32_t pg : s.pages) mark[pg] = -2;
+  ll_status bad = LL_OK;
+  int64_t listed = 0;
+  for (; listed < need; ++listed) {
+    const int32_t pg = pages[listed];
+    if (pg < 0 || pg >= p->desc.num_pages) {
+      bad = fail(LL_EINVAL, "page %d out of range", pg);
+      break;
+    }
+    if (mark[pg] == -3 || mark[pg] == -4) {
+      bad = fail(LL_EINVAL, "page %d listed twice", pg);
+      break;
+    }
+    if (!p->free.is_free(pg) && mark[pg] != -2) {
+      bad = fail(LL_EINVAL, "page %d is not free", pg);
+      break;
+    }
+    mark[pg] = mark[pg] == -2 ? -4 : -3;
   }
+  std::vector<int32_t> released;
+  if (s.used)
+    for (int32_t pg : s.pages)
+      if (mark[pg] == -2) released.push_back(pg);
+  for (int64_t i = 0; i < listed; ++i) mark[pages[i]] = -1;
+  if (s.used)
+    for (int32_t pg : s.pages) mark[pg] = -1;
+  if (bad) return bad;
   std::vector<int32_t> t(pages, pages + need);
   DeviceGuard g(p->desc.device);
   TablePlan tp;
   tp.add(seq, t);
   rc = write_tables(p, tp, static_cast<hipStream_t>(stream));
   if (rc) return rc;
-  if (s.used)
-    for (int32_t pg : s.pages)
-      if (!seen[pg]) p->free.give(pg);
+  for (int32_t pg : released) p->free.give(pg);
   for (int32_t pg : t)
-    if (!own[pg]) p->free.take(pg);
+    if (p->free.is_free(pg)) p->free.take(pg);
   p->free.advance_hint();
   s.used = true;
   s.len = n_tokens;
