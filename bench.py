@@ -31,6 +31,7 @@ Other workloads (one JSON line each, not the headline):
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -53,7 +54,7 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--latency-runs", type=int, default=25)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -76,6 +77,14 @@ def profiled_traffic(kernel: str, workload: str):
     if not m or not h or hashlib.sha256(src).hexdigest()[:16] != h.group(1):
         return None
     return int(m.group(1))
+
+
+def quiet_gc():
+    """Collect now and keep Python's cyclic collector off until the timed
+    region ends: its pauses (tens of ms with torch loaded) would otherwise land
+    inside the timed host loop and starve the GPU."""
+    gc.collect()
+    gc.disable()
 
 
 def copy_ceiling(torch, dev, n_bytes):
@@ -174,12 +183,14 @@ def bench_splice_32k(args):
     pool.profile_read(0)
     pool.set_profiling(True)
     torch.cuda.synchronize()
+    quiet_gc()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         restore()
         pool.splice(directive)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    gc.enable()
     pool.set_profiling(False)
     launches, kernel_ms, kernel_bytes = pool.profile_read(0)
     ms_per_step = (t1 - t0) * 1e3 / args.steps
@@ -188,6 +199,7 @@ def bench_splice_32k(args):
     # latency: API call to stream completion, MALL flushed before each run
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     lat = []
+    quiet_gc()
     for _ in range(args.latency_runs):
         restore()
         flush.zero_()
@@ -196,6 +208,7 @@ def bench_splice_32k(args):
         pool.splice(directive)
         torch.cuda.synchronize()
         lat.append((time.perf_counter() - a) * 1e6)
+    gc.enable()
     del flush
 
     out = base_line(args, "splice_32k_27layer", value, ms_per_step, {
@@ -285,12 +298,14 @@ def bench_splice_batched(args):
     torch.cuda.synchronize()
     pool.profile_read(0)
     pool.set_profiling(True)
+    quiet_gc()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         restore()
         pool.splice(dirs)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    gc.enable()
     pool.set_profiling(False)
     launches, kernel_ms, kernel_bytes = pool.profile_read(0)
     ms_per_step = (t1 - t0) * 1e3 / args.steps
@@ -349,6 +364,7 @@ def bench_evict(args, page):
     times = []
     pool.profile_read(0)
     pool.profile_read(1)
+    quiet_gc()
     for i in range(args.warmup + args.steps):
         restore()
         torch.cuda.synchronize()
@@ -359,6 +375,7 @@ def bench_evict(args, page):
         torch.cuda.synchronize()
         if i >= args.warmup:
             times.append(time.perf_counter() - a)
+    gc.enable()
     pool.set_profiling(False)
     launches, kernel_ms, kernel_bytes = pool.profile_read(0)
     s_launches, scan_ms, _ = pool.profile_read(1)

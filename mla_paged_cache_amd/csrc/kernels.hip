@@ -283,13 +283,14 @@ constexpr int kScanWaves = kScanThreads / 64;
 // One block per sequence.  Each thread takes 16 mask bytes per tile; the
 // count of kept bytes (0..16) is scanned across the wave with one ballot per
 // bit of the count, then across the 16 waves through LDS.  Kept row i of the
-// sequence gets new index = number of kept rows before it, and its physical
-// source row (old page table) is stored there.
+// sequence gets new index = number of kept rows before it; its logical index
+// i and its physical source row (old page table) are stored there.
 __global__ __launch_bounds__(kScanThreads) void keep_scan_kernel(ScanLaunch a) {
   __shared__ int32_t wave_total[kScanWaves];
   const EvictSeq e = a.seqs[blockIdx.x];
   const uint8_t* m = a.keep + e.mask_off;
   int32_t* out = a.src_rows + e.src_off;
+  int32_t* out_logical = a.src_logical + e.src_off;
   const int32_t* table = a.page_table + static_cast<int64_t>(e.seq) * a.max_pages_per_seq;
   const int shift = a.page_shift;
   const int64_t pmask = (int64_t{1} << shift) - 1;
@@ -333,21 +334,22 @@ __global__ __launch_bounds__(kScanThreads) void keep_scan_kernel(ScanLaunch a) {
     for (int c = 0; c < 16; ++c)
       if ((bits >> c) & 1u) {
         const int64_t i = i0 + c;
+        out_logical[pos] = static_cast<int32_t>(i);
         out[pos++] = static_cast<int32_t>((static_cast<int64_t>(table[i >> shift]) << shift) + (i & pmask));
       }
     carry += block_total;
     __syncthreads();
   }
-  // Per new page: reusable iff its live rows are the physical rows f .. f+k-1
-  // with f on a page boundary -- one old page, rows at their old offsets.
+  // Per new page: reusable iff its live rows are the old rows f .. f+k-1 with
+  // f on a page boundary -- one old page, rows at their old offsets.
   const int64_t P = int64_t{1} << shift;
   const int64_t n_new = carry;
   const int64_t pages = (n_new + P - 1) >> shift;
   int32_t* reuse = a.reuse + e.reuse_off;
   for (int64_t q = threadIdx.x; q < pages; q += kScanThreads) {
     const int64_t k = (n_new - (q << shift)) < P ? (n_new - (q << shift)) : P;
-    const int64_t f = out[q << shift];
-    const int64_t l = out[(q << shift) + k - 1];
+    const int64_t f = out_logical[q << shift];
+    const int64_t l = out_logical[(q << shift) + k - 1];
     reuse[q] = ((f & pmask) == 0 && l - f == k - 1) ? static_cast<int32_t>(f >> shift) : -1;
   }
   if (threadIdx.x == 0) a.counts[blockIdx.x] = n_new;

@@ -131,8 +131,9 @@ struct ScanLaunch {
   const int32_t* page_table;   // old tables (read)
   int32_t max_pages_per_seq;
   int32_t* src_rows;           // out: physical source row of each kept row
+  int32_t* src_logical;        // out: old logical index of each kept row
   int64_t* counts;             // out: [n_seqs] rows kept
-  int32_t* reuse;              // out: per new page, the old physical page it keeps, or -1
+  int32_t* reuse;              // out: per new page, the old logical page it keeps, or -1
 };
 
 // Launchers (kernels.hip).

@@ -14,7 +14,10 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <deque>
+#include <memory>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "../../include/leyline.h"
@@ -88,20 +91,28 @@ struct SeqState {
   std::vector<int32_t> pages;
 };
 
-// Pinned host buffer + device buffer of the same size, filled on the host and
-// sent with one copy.  `done` marks when the device has finished with it.
+// The region of the staging ring one call fills on the host and sends to the
+// device with one copy (pinned host memory and device memory at the same
+// offsets).
 struct Staging {
   char* host = nullptr;
   char* dev = nullptr;
+  size_t start = 0;
   size_t cap = 0;
   size_t used = 0;
-  hipEvent_t done = nullptr;
-  bool pending = false;
 };
 
-// Staging slots used round-robin: the host can run this many calls ahead of
-// the device before it waits for a slot to come back.
-constexpr int kStagingSlots = 8;
+// A region still in use by device work, and the event that marks its end.
+struct RingRegion {
+  size_t start, end;
+  hipEvent_t done;
+};
+
+// The staging ring starts this large and doubles when one call needs more.
+constexpr size_t kRingBytes = size_t{16} << 20;
+// Uploads at least this large go through the pool's copy stream, so they can
+// run while earlier work still occupies the caller's stream.
+constexpr size_t kCopyStreamBytes = size_t{16} << 10;
 
 struct ProfRec {
   hipEvent_t start, stop;
@@ -136,21 +147,30 @@ struct ll_pool {
   void** d_layers = nullptr;
   std::vector<SeqState> seqs;
   FreePages free;
-  Staging stage[kStagingSlots];
-  int stage_next = 0;
+  // staging ring: one pinned + one device buffer; calls take consecutive
+  // regions and a region is reused once its call's event has fired
+  char* ring_host = nullptr;
+  char* ring_dev = nullptr;
+  size_t ring_cap = 0;
+  size_t ring_head = 0;
+  std::deque<RingRegion> ring_inflight;
+  std::vector<hipEvent_t> ring_events;  // idle events for new regions
+  Staging cur;                          // region of the call in progress
+  hipEvent_t upload_ev = nullptr;
   // eviction scratch: device [counts | reuse | src_of_dst], pinned readback
   char* d_scratch = nullptr;
   size_t scratch_cap = 0;
   char* h_readback = nullptr;
   size_t readback_cap = 0;
   hipEvent_t readback_ev = nullptr;
+  hipStream_t copy_stream = nullptr;
   hipEvent_t last_done = nullptr;  // end of the last call's device work
   bool poisoned = false;
   ll_plan_stats last{};
   bool profiling = false;
   std::vector<ProfRec> prof[2];
   std::vector<hipEvent_t> spare_events;
-  std::vector<int32_t> page_slot;  // per physical page: index in its table, during an eviction
+  std::vector<int32_t> page_slot;  // per physical page: scratch marks of ll_seq_set_pages
 };
 
 namespace {
@@ -177,28 +197,67 @@ hipEvent_t take_event(ll_pool* p) {
   return e;
 }
 
-// Reserve `bytes` of a staging slot: wait until the device is done with its
-// last use, grow if needed.  Returns the slot.
+// Drop finished regions from the front of the ring's in-flight list.
+void ring_reap(ll_pool* p) {
+  while (!p->ring_inflight.empty() && hipEventQuery(p->ring_inflight.front().done) == hipSuccess) {
+    p->ring_events.push_back(p->ring_inflight.front().done);
+    p->ring_inflight.pop_front();
+  }
+}
+
+// Wait until every region up to and including `upto` (an index into the
+// in-flight list) has finished.  Calls on one pool are ordered on the device,
+// so regions finish in the order they were taken.
+ll_status ring_wait(ll_pool* p, size_t upto) {
+  hipError_t e = hipEventSynchronize(p->ring_inflight[upto].done);
+  if (e != hipSuccess) return device_fail(p, e, "hipEventSynchronize(staging)");
+  for (size_t k = 0; k <= upto; ++k) {
+    p->ring_events.push_back(p->ring_inflight.front().done);
+    p->ring_inflight.pop_front();
+  }
+  return LL_OK;
+}
+
+// Take `bytes` of the staging ring for the current call.  Waits only if the
+// region still holds data of unfinished earlier calls.
 ll_status stage_acquire(ll_pool* p, size_t bytes, Staging** out) {
-  Staging& s = p->stage[p->stage_next];
-  p->stage_next = (p->stage_next + 1) % kStagingSlots;
-  if (s.pending) {
-    hipError_t e = hipEventSynchronize(s.done);
-    if (e != hipSuccess) return device_fail(p, e, "hipEventSynchronize(staging)");
-    s.pending = false;
-  }
-  if (bytes > s.cap) {
-    size_t cap = std::max<size_t>(align_up(bytes, 1 << 20), 2 * s.cap);
-    if (s.host) (void)hipHostFree(s.host);
-    if (s.dev) (void)hipFree(s.dev);
-    s.host = nullptr;
-    s.dev = nullptr;
-    s.cap = 0;
-    if (hipHostMalloc(reinterpret_cast<void**>(&s.host), cap, hipHostMallocDefault) != hipSuccess ||
-        hipMalloc(reinterpret_cast<void**>(&s.dev), cap) != hipSuccess)
+  bytes = align_up(std::max<size_t>(bytes, 256), 256);
+  ring_reap(p);
+  if (bytes > p->ring_cap) {
+    // rare: one call needs more than the whole ring
+    if (!p->ring_inflight.empty()) {
+      ll_status rc = ring_wait(p, p->ring_inflight.size() - 1);
+      if (rc) return rc;
+    }
+    if (p->ring_host) (void)hipHostFree(p->ring_host);
+    if (p->ring_dev) (void)hipFree(p->ring_dev);
+    p->ring_host = nullptr;
+    p->ring_dev = nullptr;
+    const size_t cap = std::max(2 * p->ring_cap, align_up(2 * bytes, size_t{1} << 20));
+    p->ring_cap = 0;
+    if (hipHostMalloc(reinterpret_cast<void**>(&p->ring_host), cap, hipHostMallocDefault) != hipSuccess ||
+        hipMalloc(reinterpret_cast<void**>(&p->ring_dev), cap) != hipSuccess)
       return fail(LL_ENOMEM, "cannot allocate %zu bytes of staging", cap);
-    s.cap = cap;
+    p->ring_cap = cap;
+    p->ring_head = 0;
   }
+  if (p->ring_head + bytes > p->ring_cap) p->ring_head = 0;
+  const size_t lo = p->ring_head, hi = lo + bytes;
+  size_t last = SIZE_MAX;
+  for (size_t k = 0; k < p->ring_inflight.size(); ++k) {
+    const RingRegion& r = p->ring_inflight[k];
+    if (r.start < hi && lo < r.end) last = k;
+  }
+  if (last != SIZE_MAX) {
+    ll_status rc = ring_wait(p, last);
+    if (rc) return rc;
+  }
+  p->ring_head = hi;
+  Staging& s = p->cur;
+  s.host = p->ring_host + lo;
+  s.dev = p->ring_dev + lo;
+  s.start = lo;
+  s.cap = bytes;
   s.used = 0;
   *out = &s;
   return LL_OK;
@@ -207,6 +266,8 @@ ll_status stage_acquire(ll_pool* p, size_t bytes, Staging** out) {
 // Append `bytes` to the staging slot; returns the offset.
 size_t stage_put(Staging* s, const void* src, size_t bytes) {
   const size_t off = align_up(s->used, 256);
+  // stage_bytes_for() sized the region for every part of the call
+  if (off + bytes > s->cap) std::abort();
   if (bytes) std::memcpy(s->host + off, src, bytes);
   s->used = off + bytes;
   return off;
@@ -228,16 +289,38 @@ ll_status begin_call(ll_pool* p, hipStream_t st) {
 }
 
 ll_status end_call(ll_pool* p, Staging* s, hipStream_t st) {
-  hipError_t e = hipEventRecord(s->done, st);
-  if (e != hipSuccess) return device_fail(p, e, "hipEventRecord");
-  s->pending = true;
-  p->last_done = s->done;
+  hipEvent_t ev = nullptr;
+  if (!p->ring_events.empty()) {
+    ev = p->ring_events.back();
+    p->ring_events.pop_back();
+  } else {
+    hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+    if (e != hipSuccess) return device_fail(p, e, "hipEventCreate(staging)");
+  }
+  hipError_t e = hipEventRecord(ev, st);
+  if (e != hipSuccess) {
+    p->ring_events.push_back(ev);
+    return device_fail(p, e, "hipEventRecord");
+  }
+  p->ring_inflight.push_back({s->start, s->start + s->cap, ev});
+  p->last_done = ev;
   return LL_OK;
 }
 
+// Send the staging region to the device before the work that `st` runs next.
+// The region is free (the device finished its last use), so a large upload does
+// not have to wait behind earlier work on `st`: it runs on the copy stream and
+// `st` waits for it.
 ll_status upload(ll_pool* p, Staging* s, hipStream_t st) {
   if (s->used == 0) return LL_OK;
-  hipError_t e = hipMemcpyAsync(s->dev, s->host, s->used, hipMemcpyHostToDevice, st);
+  hipError_t e;
+  if (s->used >= kCopyStreamBytes) {
+    e = hipMemcpyAsync(s->dev, s->host, s->used, hipMemcpyHostToDevice, p->copy_stream);
+    if (e == hipSuccess) e = hipEventRecord(p->upload_ev, p->copy_stream);
+    if (e == hipSuccess) e = hipStreamWaitEvent(st, p->upload_ev, 0);
+  } else {
+    e = hipMemcpyAsync(s->dev, s->host, s->used, hipMemcpyHostToDevice, st);
+  }
   if (e != hipSuccess) return device_fail(p, e, "hipMemcpyAsync(H2D staging)");
   return LL_OK;
 }
@@ -469,9 +552,12 @@ ll_status ll_pool_create(const ll_pool_desc* desc, ll_pool** out) {
   hipError_t e = hipMalloc(reinterpret_cast<void**>(&p->d_layers), sizeof(void*) * d.num_layers);
   if (e == hipSuccess)
     e = hipMemcpy(p->d_layers, p->layer_ptrs.data(), sizeof(void*) * d.num_layers, hipMemcpyHostToDevice);
-  for (int i = 0; i < kStagingSlots && e == hipSuccess; ++i)
-    e = hipEventCreateWithFlags(&p->stage[i].done, hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&p->readback_ev, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipStreamCreateWithFlags(&p->copy_stream, hipStreamNonBlocking);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&p->upload_ev, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipHostMalloc(reinterpret_cast<void**>(&p->ring_host), kRingBytes, hipHostMallocDefault);
+  if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void**>(&p->ring_dev), kRingBytes);
+  if (e == hipSuccess) p->ring_cap = kRingBytes;
   if (e != hipSuccess) {
     ll_pool_destroy(p);
     return fail(LL_EDEVICE, "pool setup: %s", hipGetErrorString(e));
@@ -484,11 +570,11 @@ void ll_pool_destroy(ll_pool* p) {
   if (!p) return;
   DeviceGuard g(p->desc.device);
   if (p->last_done) (void)hipEventSynchronize(p->last_done);
-  for (auto& s : p->stage) {
-    if (s.host) (void)hipHostFree(s.host);
-    if (s.dev) (void)hipFree(s.dev);
-    if (s.done) (void)hipEventDestroy(s.done);
-  }
+  for (auto& r : p->ring_inflight) (void)hipEventDestroy(r.done);
+  for (auto e : p->ring_events) (void)hipEventDestroy(e);
+  if (p->upload_ev) (void)hipEventDestroy(p->upload_ev);
+  if (p->ring_host) (void)hipHostFree(p->ring_host);
+  if (p->ring_dev) (void)hipFree(p->ring_dev);
   for (auto& v : p->prof)
     for (auto& r : v) {
       (void)hipEventDestroy(r.start);
@@ -496,6 +582,10 @@ void ll_pool_destroy(ll_pool* p) {
     }
   for (auto e : p->spare_events) (void)hipEventDestroy(e);
   if (p->readback_ev) (void)hipEventDestroy(p->readback_ev);
+  if (p->copy_stream) {
+    (void)hipStreamSynchronize(p->copy_stream);
+    (void)hipStreamDestroy(p->copy_stream);
+  }
   if (p->h_readback) (void)hipHostFree(p->h_readback);
   if (p->d_scratch) (void)hipFree(p->d_scratch);
   if (p->d_layers) (void)hipFree(p->d_layers);
@@ -794,10 +884,12 @@ ll_status kv_evict_compact(ll_pool* p, const int32_t* seq_ids, int32_t n, const 
   DeviceGuard g(p->desc.device);
   hipStream_t st = static_cast<hipStream_t>(stream);
 
-  // --- scratch: [counts (int64) n | reuse (int32) total_pages | src_of_dst (int32) total_rows]
+  // --- scratch: [counts (int64) n | reuse (int32) total_pages | src_rows (int32)
+  //     total_rows | src_logical (int32) total_rows]; the first two come back
   const size_t off_reuse = align_up(8 * static_cast<size_t>(n), 256);
   const size_t off_src = align_up(off_reuse + 4 * static_cast<size_t>(total_pages), 256);
-  const size_t scratch = off_src + 4 * static_cast<size_t>(total_rows) + 256;
+  const size_t off_logical = align_up(off_src + 4 * static_cast<size_t>(total_rows), 256);
+  const size_t scratch = off_logical + 4 * static_cast<size_t>(total_rows) + 256;
   const size_t readback = off_src;
   if ((rc = begin_call(p, st))) return rc;
   if (scratch > p->scratch_cap || readback > p->readback_cap) {
@@ -849,6 +941,7 @@ ll_status kv_evict_compact(ll_pool* p, const int32_t* seq_ids, int32_t n, const 
   sc.counts = reinterpret_cast<int64_t*>(p->d_scratch);
   sc.reuse = reinterpret_cast<int32_t*>(p->d_scratch + off_reuse);
   sc.src_rows = reinterpret_cast<int32_t*>(p->d_scratch + off_src);
+  sc.src_logical = reinterpret_cast<int32_t*>(p->d_scratch + off_logical);
   ProfRec rec1{};
   if (p->profiling && (rc = prof_begin(p, 1, st, &rec1))) return rc;
   hipError_t e = ll::launch_keep_scan(sc, st);
@@ -858,52 +951,32 @@ ll_status kv_evict_compact(ll_pool* p, const int32_t* seq_ids, int32_t n, const 
     if ((rc = prof_end(p, 1, st, &rec1))) return rc;
   }
   e = hipMemcpyAsync(p->h_readback, p->d_scratch, readback, hipMemcpyDeviceToHost, st);
-  if (e == hipSuccess) e = hipEventRecord(s1->done, st);
-  s1->pending = true;
-  p->last_done = s1->done;
-  if (e == hipSuccess) e = hipEventSynchronize(s1->done);
+  if (e != hipSuccess) return fail(LL_EDEVICE, "eviction readback: %s", hipGetErrorString(e));
+  if ((rc = end_call(p, s1, st))) return rc;
+  e = hipEventSynchronize(p->last_done);
   if (e != hipSuccess) return fail(LL_EDEVICE, "eviction readback: %s", hipGetErrorString(e));
   // Nothing has changed yet: the scan only wrote scratch.
 
   const int64_t* counts = reinterpret_cast<const int64_t*>(p->h_readback);
-  const int32_t* reuse_phys = reinterpret_cast<const int32_t*>(p->h_readback + off_reuse);
-  // The scan names reused pages physically; map them back to old logical
-  // pages (each sequence's pages are its own, so one slot array serves all).
-  for (int32_t i = 0; i < n; ++i) {
-    const SeqState& s = p->seqs[seq_ids[i]];
-    for (size_t k = 0; k < s.pages.size(); ++k) p->page_slot[s.pages[k]] = static_cast<int32_t>(k);
-  }
-  std::vector<int32_t> reuse(static_cast<size_t>(total_pages), -1);
+  const int32_t* reuse = reinterpret_cast<const int32_t*>(p->h_readback + off_reuse);
   int64_t need = 0;
   std::vector<int64_t> n_new(static_cast<size_t>(n));
-  ll_status bad = LL_OK;
-  for (int32_t i = 0; i < n && bad == LL_OK; ++i) {
+  for (int32_t i = 0; i < n; ++i) {
     const SeqState& s = p->seqs[seq_ids[i]];
     n_new[i] = counts[i];
-    if (n_new[i] < 0 || n_new[i] > s.len) {
-      bad = fail(LL_EDEVICE, "keep scan returned a bad count");
-      break;
-    }
+    if (n_new[i] < 0 || n_new[i] > s.len) return fail(LL_EDEVICE, "keep scan returned a bad count");
     const int64_t pages = ceil_div(n_new[i], P);
     int64_t prev = -1;
     for (int64_t q = 0; q < pages; ++q) {
-      const int32_t x = reuse_phys[reuse_off[i] + q];
+      const int32_t x = reuse[reuse_off[i] + q];
       if (x < 0) {
         ++need;
         continue;
       }
-      const int32_t lp = (x < p->desc.num_pages) ? p->page_slot[x] : -1;
-      if (lp <= prev || lp >= static_cast<int64_t>(s.pages.size()) || s.pages[lp] != x) {
-        bad = fail(LL_EDEVICE, "keep scan returned a bad page plan");
-        break;
-      }
-      reuse[reuse_off[i] + q] = lp;
-      prev = lp;
+      if (x <= prev || x >= static_cast<int64_t>(s.pages.size())) return fail(LL_EDEVICE, "keep scan returned a bad page plan");
+      prev = x;
     }
   }
-  for (int32_t i = 0; i < n; ++i)
-    for (int32_t pg : p->seqs[seq_ids[i]].pages) p->page_slot[pg] = -1;
-  if (bad) return bad;
   if (need > p->free.count())
     return fail(LL_ENOMEM, "need %lld fresh pages, %lld free", (long long)need, (long long)p->free.count());
   std::vector<int32_t> fresh;
