@@ -165,6 +165,7 @@ struct ll_pool {
   hipEvent_t readback_ev = nullptr;
   hipStream_t copy_stream = nullptr;
   hipEvent_t last_done = nullptr;  // end of the last call's device work
+  hipStream_t last_stream = nullptr;  // the stream that work ran on
   bool poisoned = false;
   ll_plan_stats last{};
   bool profiling = false;
@@ -268,7 +269,7 @@ size_t stage_put(Staging* s, const void* src, size_t bytes) {
   const size_t off = align_up(s->used, 256);
   // stage_bytes_for() sized the region for every part of the call
   if (off + bytes > s->cap) std::abort();
-  if (bytes) std::memcpy(s->host + off, src, bytes);
+  if (bytes && src) std::memcpy(s->host + off, src, bytes);
   s->used = off + bytes;
   return off;
 }
@@ -279,9 +280,10 @@ size_t stage_bytes_for(std::initializer_list<size_t> parts) {
   return t + 256;
 }
 
-// Order this call after the previous call on the pool (any stream).
+// Order this call after the previous call on the pool (any stream; calls on
+// one stream are ordered already).
 ll_status begin_call(ll_pool* p, hipStream_t st) {
-  if (p->last_done) {
+  if (p->last_done && st != p->last_stream) {
     hipError_t e = hipStreamWaitEvent(st, p->last_done, 0);
     if (e != hipSuccess) return device_fail(p, e, "hipStreamWaitEvent");
   }
@@ -304,6 +306,7 @@ ll_status end_call(ll_pool* p, Staging* s, hipStream_t st) {
   }
   p->ring_inflight.push_back({s->start, s->start + s->cap, ev});
   p->last_done = ev;
+  p->last_stream = st;
   return LL_OK;
 }
 
@@ -314,7 +317,10 @@ ll_status end_call(ll_pool* p, Staging* s, hipStream_t st) {
 ll_status upload(ll_pool* p, Staging* s, hipStream_t st) {
   if (s->used == 0) return LL_OK;
   hipError_t e;
-  if (s->used >= kCopyStreamBytes) {
+  // Only this call's region is in flight: nothing earlier is queued, so the
+  // copy goes straight onto `st` (fewer calls, lower latency).
+  const bool idle = p->ring_inflight.empty();
+  if (s->used >= kCopyStreamBytes && !idle) {
     e = hipMemcpyAsync(s->dev, s->host, s->used, hipMemcpyHostToDevice, p->copy_stream);
     if (e == hipSuccess) e = hipEventRecord(p->upload_ev, p->copy_stream);
     if (e == hipSuccess) e = hipStreamWaitEvent(st, p->upload_ev, 0);
@@ -730,12 +736,40 @@ ll_status leyline_splice(ll_pool* p, const ll_directive* dirs, int32_t n, void* 
   std::vector<int32_t> fresh;
   p->free.lowest(need, fresh);
 
-  std::vector<ll::SpliceDir> ddirs(static_cast<size_t>(n));
-  std::vector<ll::SpliceTask> tasks, rot_tasks;
-  TablePlan tp;
+  int64_t n_move_tasks = 0, n_rot_tasks = 0, n_entries = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    n_move_tasks += plans[i].fresh;
+    for (char x : plans[i].inplace) n_rot_tasks += x;
+    n_entries += static_cast<int64_t>(plans[i].reuse.size());
+  }
+  if (n_move_tasks * P * ll::kRowChunks >= (int64_t{1} << 32) ||
+      n_rot_tasks * P * ll::kRowChunks >= (int64_t{1} << 32))
+    return fail(LL_EUNSUPPORTED, "one splice may write at most 2^32 / 72 rows per layer");
+
+  // --- device work: descriptors written straight into pinned staging, one
+  // upload, one launch
+  DeviceGuard g(p->desc.device);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if ((rc = begin_call(p, st))) return rc;
+  Staging* sg = nullptr;
+  rc = stage_acquire(p, stage_bytes_for({n * sizeof(ll::SpliceDir), (n_move_tasks + n_rot_tasks) * sizeof(ll::SpliceTask),
+                                         n * sizeof(ll::TableWrite), static_cast<size_t>(n_entries) * 4}),
+                     &sg);
+  if (rc) return rc;
+  const size_t o_d = stage_put(sg, nullptr, n * sizeof(ll::SpliceDir));
+  const size_t o_t = stage_put(sg, nullptr, (n_move_tasks + n_rot_tasks) * sizeof(ll::SpliceTask));
+  const size_t o_w = stage_put(sg, nullptr, n * sizeof(ll::TableWrite));
+  const size_t o_p = stage_put(sg, nullptr, static_cast<size_t>(n_entries) * 4);
+  ll::SpliceDir* ddirs = reinterpret_cast<ll::SpliceDir*>(sg->host + o_d);
+  ll::SpliceTask* move_out = reinterpret_cast<ll::SpliceTask*>(sg->host + o_t);
+  ll::SpliceTask* rot_out = move_out + n_move_tasks;
+  ll::TableWrite* writes = reinterpret_cast<ll::TableWrite*>(sg->host + o_w);
+  int32_t* packed = reinterpret_cast<int32_t*>(sg->host + o_p);
+
   std::vector<std::vector<int32_t>> new_tables(static_cast<size_t>(n));
   ll_plan_stats stats{};
   size_t cursor = 0;
+  int64_t packed_at = 0;
   for (int32_t i = 0; i < n; ++i) {
     const ll_directive& d = dirs[i];
     const SplicePlan& pl = plans[i];
@@ -743,7 +777,6 @@ ll_status leyline_splice(ll_pool* p, const ll_directive* dirs, int32_t n, void* 
     const std::vector<int32_t>& T = s.pages;
     const int64_t old_pages = static_cast<int64_t>(T.size());
     ll::SpliceDir& dd = ddirs[i];
-    std::memset(&dd, 0, sizeof dd);
     const int64_t r = d.mode == LL_FORGET ? 0 : d.r_len;
     rope_table(p->desc.rope_base, ll::kRopeDim, pl.delta, dd.cos_, dd.sin_);
     ll::SpliceTask base{};
@@ -767,7 +800,7 @@ ll_status leyline_splice(ll_pool* p, const ll_directive* dirs, int32_t n, void* 
         nt[q] = T[pl.reuse[q]];
         if (pl.inplace[q]) {
           t.dst_page = nt[q];
-          rot_tasks.push_back(t);
+          *rot_out++ = t;
           stats.rows_rotated_inplace += b - a;
         }
         continue;
@@ -782,18 +815,17 @@ ll_status leyline_splice(ll_pool* p, const ll_directive* dirs, int32_t n, void* 
         t.down_page0 = T[lp0];
         t.down_page1 = lp0 + 1 < old_pages ? T[lp0 + 1] : -1;
       }
-      tasks.push_back(t);
+      *move_out++ = t;
       stats.rows_moved += b - a;
     }
-    tp.add(d.seq_id, nt);
+    writes[i].src_off = packed_at;
+    writes[i].seq = d.seq_id;
+    writes[i].count = static_cast<int32_t>(nt.size());
+    if (!nt.empty()) std::memcpy(packed + packed_at, nt.data(), nt.size() * 4);
+    packed_at += static_cast<int64_t>(nt.size());
   }
-  const int64_t n_move_tasks = static_cast<int64_t>(tasks.size());
-  const int64_t n_rot_tasks = static_cast<int64_t>(rot_tasks.size());
-  tasks.insert(tasks.end(), rot_tasks.begin(), rot_tasks.end());
-  if (n_move_tasks * P * ll::kRowChunks >= (int64_t{1} << 32))
-    return fail(LL_EUNSUPPORTED, "one splice may move at most 2^32 / 72 rows per layer");
   stats.fresh_pages = need;
-  stats.table_entries = static_cast<int64_t>(tp.packed.size());
+  stats.table_entries = n_entries;
   for (int32_t i = 0; i < n; ++i) {
     const SeqState& s = p->seqs[dirs[i].seq_id];
     std::vector<char> kept(s.pages.size(), 0);
@@ -803,20 +835,6 @@ ll_status leyline_splice(ll_pool* p, const ll_directive* dirs, int32_t n, void* 
   }
   const int64_t L = p->desc.num_layers;
   stats.alg_bytes = L * (2 * ll::kRowBytes * stats.rows_moved + 2 * ll::kRopeDim * 2 * stats.rows_rotated_inplace);
-
-  // --- device work: one upload, one launch
-  DeviceGuard g(p->desc.device);
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  if ((rc = begin_call(p, st))) return rc;
-  Staging* sg = nullptr;
-  rc = stage_acquire(p, stage_bytes_for({ddirs.size() * sizeof(ll::SpliceDir), tasks.size() * sizeof(ll::SpliceTask),
-                                         tp.writes.size() * sizeof(ll::TableWrite), tp.packed.size() * 4}),
-                     &sg);
-  if (rc) return rc;
-  const size_t o_d = stage_put(sg, ddirs.data(), ddirs.size() * sizeof(ll::SpliceDir));
-  const size_t o_t = stage_put(sg, tasks.data(), tasks.size() * sizeof(ll::SpliceTask));
-  const size_t o_w = stage_put(sg, tp.writes.data(), tp.writes.size() * sizeof(ll::TableWrite));
-  const size_t o_p = stage_put(sg, tp.packed.data(), tp.packed.size() * 4);
   if ((rc = upload(p, sg, st))) return rc;
 
   ll::SpliceLaunch a{};
@@ -831,7 +849,7 @@ ll_status leyline_splice(ll_pool* p, const ll_directive* dirs, int32_t n, void* 
   a.dirs = reinterpret_cast<const ll::SpliceDir*>(sg->dev + o_d);
   a.twrites = reinterpret_cast<const ll::TableWrite*>(sg->dev + o_w);
   a.tables = reinterpret_cast<const int32_t*>(sg->dev + o_p);
-  a.n_twrites = static_cast<int32_t>(tp.writes.size());
+  a.n_twrites = n;
   a.max_pages_per_seq = p->desc.max_pages_per_seq;
   a.page_table = p->desc.page_table;
   ProfRec rec{};

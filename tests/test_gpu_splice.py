@@ -257,3 +257,43 @@ def test_splice_is_deterministic():
     assert np.array_equal(t0, t1) and np.array_equal(pt0[0, :len(t0)], pt1[0, :len(t1)])
     rows = (t0.astype(np.int64)[:, None] * 16 + np.arange(16)).ravel()
     assert np.array_equal(d0.reshape(2, -1, O.ROW)[:, rows], d1.reshape(2, -1, O.ROW)[:, rows])
+
+
+def test_splice_batch_of_40_takes_several_launches():
+    """40 directives in one call (more than one launch's worth), mixed
+    shapes: page-aligned shifts (in-place rotation), ragged shifts, pure
+    insertions, deletions to empty, FORGET; every row compared."""
+    say("batch of 40")
+    rng = np.random.default_rng(81)
+    n_seq = 40
+    lengths = [int(x) for x in rng.integers(1, 700, size=n_seq)]
+    total = sum(-(-n // 16) for n in lengths)
+    dp = _pool(2, 3 * total + 64, 16, n_seq, 200, seed=81)
+    perm = permuted_pages(81, 3 * total + 64)
+    at = 0
+    for s, n in enumerate(lengths):
+        k = -(-n // 16)
+        dp.set_pages(s, perm[at:at + k], n)
+        at += k
+    dp.snapshot_rows()
+    dirs = []
+    for s, n in enumerate(lengths):
+        kind = s % 5
+        if kind == 0:    # delta = -32: downstream pages reused, rotated in place
+            s0 = int(rng.integers(0, max(1, n - 40))); s1 = min(n, s0 + 40); r = 8 if s1 - s0 == 40 else 0
+        elif kind == 1:  # ragged shift
+            s0 = int(rng.integers(0, n)); s1 = int(rng.integers(s0, n + 1)); r = int(rng.integers(0, 30))
+        elif kind == 2:  # pure insertion
+            s0 = s1 = int(rng.integers(0, n + 1)); r = int(rng.integers(1, 20))
+        elif kind == 3:  # delete everything
+            s0, s1, r = 0, n, 0
+        else:
+            s0, s1, r = int(rng.integers(0, n + 1)), n, 0
+        mode = O.FORGET if kind == 4 else O.AMORTIZE
+        dirs.append((s, s0, s1, r, 500 + s, mode))
+    order = list(rng.permutation(n_seq))
+    expected, _ = _splice_both(dp, [dirs[i] for i in order])
+    for s in range(n_seq):
+        compare_seq(dp, expected, s)
+    assert_same_free(dp, expected)
+    dp.close()
