@@ -52,6 +52,13 @@ Row layout (from the MLA cache split of section 2.2): one token of one layer is
 (the RoPE band, 64 values): 1152 bytes.  A layer's pool is an array
 [num_pages][page_size][576] of uint16 bit patterns; one page table per sequence
 is shared by all layers.
+
+GQA / MHA caches (Leyline section 5: the directive carries over to GQA/MHA,
+only the rotation step differs) are described by the same machinery with other
+row layouts (`RowSpec`): a K array row holds H heads of D values and the first
+rotary_dim values of every head are a RoPE band; a V array row has no band.
+Every band turns by R(Delta) exactly as k_pe does, with theta_j computed over
+the band's own width.
 """
 
 from __future__ import annotations
@@ -64,6 +71,28 @@ import numpy as np
 KV_LORA_RANK = 512
 ROPE_DIM = 64
 ROW = KV_LORA_RANK + ROPE_DIM
+
+
+@dataclass(frozen=True)
+class RowSpec:
+    """One token's row in one layer array: `width` bf16 values, of which each
+    (offset, dim) band is RoPE-rotated (pairs inside the band)."""
+    width: int
+    bands: tuple = ()
+
+
+MLA_ROW = RowSpec(ROW, ((KV_LORA_RANK, ROPE_DIM),))
+
+
+def gqa_k_row(heads: int, head_dim: int, rotary_dim: int) -> RowSpec:
+    """K row of a GQA/MHA cache: H heads of head_dim values, the first
+    rotary_dim values of each head rotated."""
+    return RowSpec(heads * head_dim, tuple((h * head_dim, rotary_dim) for h in range(heads)))
+
+
+def plain_row(width: int) -> RowSpec:
+    """A row with no RoPE band (a V row)."""
+    return RowSpec(width, ())
 
 AMORTIZE = 0
 FORGET = 1
@@ -195,6 +224,7 @@ class CacheState:
     num_pages: int
     max_pages_per_seq: int
     layers: list | None
+    specs: list | None = None                       # RowSpec per layer array (None: MLA rows)
     tables: dict = field(default_factory=dict)      # seq -> list of physical pages
     lengths: dict = field(default_factory=dict)     # seq -> tokens
     next_pos: dict = field(default_factory=dict)    # seq -> next RoPE position
@@ -202,15 +232,20 @@ class CacheState:
 
     @staticmethod
     def empty(num_layers: int, num_pages: int, page_size: int, max_pages_per_seq: int,
-              with_rows: bool = True) -> "CacheState":
-        layers = ([np.zeros((num_pages, page_size, ROW), np.uint16) for _ in range(num_layers)]
+              with_rows: bool = True, specs=None) -> "CacheState":
+        specs = list(specs) if specs is not None else [MLA_ROW] * num_layers
+        layers = ([np.zeros((num_pages, page_size, sp.width), np.uint16) for sp in specs]
                   if with_rows else None)
-        return CacheState(page_size, num_pages, max_pages_per_seq, layers,
+        return CacheState(page_size, num_pages, max_pages_per_seq, layers, specs,
                           free=set(range(num_pages)))
+
+    def spec(self, layer: int) -> RowSpec:
+        return self.specs[layer] if self.specs is not None else MLA_ROW
 
     def copy(self) -> "CacheState":
         return CacheState(self.page_size, self.num_pages, self.max_pages_per_seq,
                           None if self.layers is None else [a.copy() for a in self.layers],
+                          None if self.specs is None else list(self.specs),
                           {k: list(v) for k, v in self.tables.items()},
                           dict(self.lengths), dict(self.next_pos), set(self.free))
 
@@ -231,7 +266,8 @@ class CacheState:
         self.next_pos[seq] = n_tokens
 
     def logical_rows(self, seq: int, layer: int) -> np.ndarray:
-        """The sequence's rows of one layer in logical order: uint16 [n, 576]."""
+        """The sequence's rows of one layer array in logical order: uint16
+        [n, width]."""
         P = self.page_size
         n = self.lengths[seq]
         t = np.asarray(self.tables[seq], dtype=np.int64)
@@ -246,7 +282,8 @@ class CacheState:
 @dataclass
 class Directive:
     """D = (s_start, s_end, R, m) for one sequence.  `stub` holds the |R|
-    prefilled rows per layer: uint16 [L][r_len][576] (or None with r_len)."""
+    prefilled rows per layer array: uint16 [r_len][width] for each array (an
+    MLA cache: [L][r_len][576]), or None when r_len is 0."""
     seq: int
     s_start: int
     s_end: int
@@ -363,8 +400,8 @@ def _move_rows(old: CacheState, new: CacheState, seq, new_t, plan, n_new, kind, 
                downstream, stub, delta, pairing, base):
     """Write the rows of the sequence's new pages.  Fresh pages receive every
     live row (old rows copied bit-exactly, stub rows copied bit-exactly,
-    downstream k_pe rotated by delta).  Reused pages already hold their rows;
-    only the downstream k_pe band is rotated there when delta != 0."""
+    downstream RoPE bands rotated by delta).  Reused pages already hold their
+    rows; only the downstream bands are rotated there when delta != 0."""
     P = old.page_size
     old_t = np.asarray(old.tables[seq], dtype=np.int64)
     new_t = np.asarray(new_t, dtype=np.int64)
@@ -377,8 +414,9 @@ def _move_rows(old: CacheState, new: CacheState, seq, new_t, plan, n_new, kind, 
     src[is_old] = old_t[index[is_old] // P] * P + index[is_old] % P
     rot = downstream & (delta != 0)
     for L in range(len(old.layers)):
-        a_old = old.layers[L].reshape(-1, ROW)
-        a_new = new.layers[L].reshape(-1, ROW)
+        spec = old.spec(L)
+        a_old = old.layers[L].reshape(-1, spec.width)
+        a_new = new.layers[L].reshape(-1, spec.width)
         m = fresh & is_old
         a_new[dst[m]] = a_old[src[m]]
         m = fresh & ~is_old
@@ -386,8 +424,9 @@ def _move_rows(old: CacheState, new: CacheState, seq, new_t, plan, n_new, kind, 
             a_new[dst[m]] = stub[L][index[m]]
         m = rot
         if np.any(m):
-            a_new[dst[m], KV_LORA_RANK:] = rotate_kpe_bf16(a_old[src[m], KV_LORA_RANK:], delta,
-                                                           pairing=pairing, base=base)
+            for off, dim in spec.bands:
+                a_new[dst[m], off:off + dim] = rotate_kpe_bf16(a_old[src[m], off:off + dim], delta,
+                                                               rope_dim=dim, pairing=pairing, base=base)
 
 
 # ---------------------------------------------------------------------------
@@ -460,12 +499,14 @@ def ptable_reindex(state: CacheState, seq: int, keep_pages):
     return new
 
 
-def algorithmic_bytes(plan, n_new, P, kind, downstream, delta, num_layers, rotate=True):
-    """Bytes the method must move for one request (its row data only):
-    2*1152 per live row of a fresh page and 2*128 per downstream row of a
-    reused page whose k_pe is rotated in place, per layer."""
+def algorithmic_bytes(plan, n_new, P, kind, downstream, delta, num_layers, rotate=True, specs=None):
+    """Bytes the method must move for one request (its row data only): per
+    layer array, 2 * row bytes per live row of a fresh page and 2 * band bytes
+    per downstream row of a reused page whose bands are rotated in place
+    (MLA rows: 2*1152 and 2*128)."""
     j = np.arange(n_new)
     fresh = np.asarray(plan, dtype=np.int64)[j // P] < 0 if n_new else np.zeros(0, bool)
     moved = int(np.count_nonzero(fresh))
     inplace = int(np.count_nonzero(~fresh & downstream)) if (rotate and delta != 0) else 0
-    return num_layers * (2 * ROW * 2 * moved + 2 * ROPE_DIM * 2 * inplace)
+    specs = list(specs) if specs is not None else [MLA_ROW] * num_layers
+    return sum(2 * sp.width * 2 * moved + sum(2 * dim * 2 for _, dim in sp.bands) * inplace for sp in specs)
