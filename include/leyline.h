@@ -41,6 +41,18 @@
  * the free set as it was when the call began; old pages that are not reused
  * return to the free set after the call.  Rows beyond a sequence's length and
  * rows of free pages hold unspecified values.
+ *
+ * GQA / MHA caches ([Leyline] section 5: the directive applies unchanged to
+ * GQA and MHA caches; only the rotation step differs).  A pool made by
+ * ll_pool_create_gqa has, per layer, a K pool and a V pool, each
+ * [num_pages][page_size][num_kv_heads][head_dim] bf16 and indexed by the same
+ * page table.  The first rotary_dim values of every K head are its RoPE band
+ * (pairs interleaved or half-split inside the band); the rest of K and all of
+ * V are position-free.  A splice copies V and the non-rotary part of K
+ * bit-exactly and turns every downstream K band by R(Delta), with
+ * theta_j = rope_base^(-2j/rotary_dim); an eviction moves both K and V rows
+ * unchanged.  Every other rule above holds as written, with "row" meaning the
+ * K row and the V row of a token together.
  */
 #ifndef LEYLINE_H
 #define LEYLINE_H
@@ -100,14 +112,22 @@ typedef struct {
                                 prefilled at their final positions; NULL iff r_len == 0;
                                 16-byte aligned.  Ignored by LL_FORGET. */
   int64_t r_layer_stride_bytes; /* bytes between layers of r_rows; 0 means
-                                   r_len * 1152; a multiple of 16 otherwise */
+                                   r_len * row bytes; a multiple of 16 otherwise */
+  const void* r_rows_v;      /* GQA / MHA pools: r_rows holds the K rows of R,
+                                [num_layers][r_len][num_kv_heads][head_dim], and this
+                                the V rows, same shape; NULL iff r_len == 0; 16-byte
+                                aligned.  MLA pools: must be NULL. */
+  int64_t r_layer_stride_bytes_v; /* bytes between layers of r_rows_v, as above */
 } ll_directive;
 
 /* What the last splice / evict / reindex call on a pool did. */
 typedef struct {
   int64_t alg_bytes;            /* row bytes the call must move, all layers:
-                                   2*1152 per live row of a fresh page plus
-                                   2*128 per row rotated in place */
+                                   read + write of every live row of a fresh
+                                   page, plus read + write of the RoPE bands of
+                                   each row rotated in place (MLA: 2*1152 and
+                                   2*128 bytes per row and layer; GQA: 2*2*H*D*2
+                                   and 2*H*rotary_dim*2) */
   int64_t rows_moved;           /* live rows written to fresh pages (per layer) */
   int64_t rows_rotated_inplace; /* downstream rows of reused pages (per layer) */
   int64_t fresh_pages;
@@ -121,6 +141,31 @@ typedef struct {
  * NULL pointer), LL_EUNSUPPORTED (row shape other than 512 + 64),
  * LL_EDEVICE. */
 ll_status ll_pool_create(const ll_pool_desc* desc, ll_pool** out);
+
+/* A GQA / MHA cache (MHA: num_kv_heads = number of attention heads). */
+typedef struct {
+  int32_t num_layers;        /* >= 1 */
+  int32_t page_size;         /* rows per page: a power of two, 1 .. 256 */
+  int32_t num_pages;
+  int32_t max_seqs;
+  int32_t max_pages_per_seq;
+  int32_t num_kv_heads;      /* >= 1 */
+  int32_t head_dim;          /* a multiple of 8; num_kv_heads * head_dim <= 32768 */
+  int32_t rotary_dim;        /* RoPE band of each K head: a power of two in
+                                [16, 256] that divides head_dim */
+  int32_t rope_pairing;      /* LL_ROPE_INTERLEAVED or LL_ROPE_HALF, inside the band */
+  double rope_base;          /* theta_j = rope_base^(-2j/rotary_dim) */
+  void* const* k_layer_base; /* host arrays [num_layers] of device pointers, each */
+  void* const* v_layer_base; /*   16-byte aligned, to [num_pages][page_size][H][D] bf16 */
+  int32_t* page_table;       /* device int32 [max_seqs][max_pages_per_seq] */
+  int32_t device;
+} ll_gqa_pool_desc;
+
+/* Create a GQA / MHA pool over caller-owned device memory; the same calls as
+ * for an MLA pool then apply to it.  Errors: LL_EINVAL (bad field or NULL
+ * pointer), LL_EUNSUPPORTED (head_dim, rotary_dim or row width outside the
+ * ranges above), LL_EDEVICE. */
+ll_status ll_pool_create_gqa(const ll_gqa_pool_desc* desc, ll_pool** out);
 
 /* Wait for the pool's device work and free what the library allocated.  The
  * caller's buffers are not touched.  NULL is ignored. */
@@ -160,14 +205,17 @@ ll_status ll_pool_free_pages(const ll_pool* pool, int64_t* n_free);
  * (x, y) turns by the angle Delta*theta_j, with cos/sin evaluated in float64
  * and rounded to float32, then x' = x*c - y*s and y' = x*s + y*c in float32
  * (no fused multiply-add) and rounded to bf16, nearest-even.  The next
- * position moves by Delta.
+ * position moves by Delta.  On a GQA / MHA pool the K and V rows of R are
+ * copied, V and the non-rotary K values of downstream rows stay bit-exact and
+ * each K head's RoPE band turns as k_pe does.
  * LL_FORGET: the sequence is cut to its first s_start rows (the caller then
  * re-prefills, section 2.1); the next position moves back by n - s_start.
  *
  * Fresh pages, page-table row updates and the rows are written by one kernel
  * launch after one host-to-device copy.  n == 0 is a no-op.  Errors:
- * LL_EINVAL (bad span, unknown or repeated sequence, r_rows NULL with
- * r_len > 0, misaligned pointer or stride), LL_EUNSUPPORTED (reserved mode),
+ * LL_EINVAL (bad span, unknown or repeated sequence, r_rows (GQA: or
+ * r_rows_v) NULL with r_len > 0, r_rows_v given to an MLA pool, misaligned
+ * pointer or stride), LL_EUNSUPPORTED (reserved mode),
  * LL_ERANGE (n' exceeds max_pages_per_seq pages), LL_ENOMEM (too few free
  * pages), LL_EDEVICE. */
 ll_status leyline_splice(ll_pool* pool, const ll_directive* dirs, int32_t n, void* stream);

@@ -123,6 +123,58 @@ struct TableLaunch {
   int32_t* page_table;
 };
 
+// GQA / MHA pools.  A K or V row is H heads of D bf16 = H * D / 8 chunks; the
+// RoPE band of a K head is its first rotary_dim values = 2^rot_shift chunks.
+constexpr int kMaxBandPairs = 128;  // rotary_dim <= 256
+
+// The rotation table of a directive on a GQA pool and its V stub rows (the K
+// stub rows are in the task).
+struct alignas(16) GqaDir {
+  const chunk_t* stub_v;       // V rows of R, layer 0
+  int64_t stub_v_layer_chunks;
+  float cos_[kMaxBandPairs];   // float32 of float64 cos(delta * theta_j)
+  float sin_[kMaxBandPairs];
+};
+
+struct GqaSpliceLaunch {
+  const chunk_t* const* planes;  // device array [2L]: K of layers 0..L-1, then V
+  int32_t num_layers;
+  int32_t page_shift;
+  int32_t row_chunks;          // H * D / 8
+  int32_t head_chunks;         // D / 8
+  int32_t rot_shift;           // log2(rotary_dim / 8)
+  int32_t heads;
+  const SpliceTask* tasks;     // move tasks, then rotate-in-place tasks
+  int64_t n_move_tasks;
+  int64_t n_rot_tasks;
+  int64_t move_blocks_per_plane;  // over all 2L planes
+  int64_t rot_blocks_per_plane;   // over the L K planes
+  const GqaDir* dirs;
+  const TableWrite* twrites;
+  const int32_t* tables;
+  int32_t n_twrites;
+  int32_t max_pages_per_seq;
+  int32_t* page_table;
+};
+
+// Eviction on pools whose rows are not MLA rows: every plane (K and V of
+// every layer) has rows of row_chunks chunks.
+struct PlaneEvictLaunch {
+  const chunk_t* const* planes;
+  int32_t num_planes;
+  int32_t page_shift;
+  int32_t row_chunks;
+  const EvictTask* tasks;
+  int64_t n_tasks;
+  int64_t blocks_per_plane;
+  const int32_t* src_rows;
+  const TableWrite* twrites;
+  const int32_t* tables;
+  int32_t n_twrites;
+  int32_t max_pages_per_seq;
+  int32_t* page_table;
+};
+
 struct ScanLaunch {
   const uint8_t* keep;
   const EvictSeq* seqs;
@@ -141,6 +193,8 @@ hipError_t launch_splice(const SpliceLaunch& a, int pairing, hipStream_t s);
 hipError_t launch_evict_move(const EvictLaunch& a, hipStream_t s);
 hipError_t launch_table_write(const TableLaunch& a, hipStream_t s);
 hipError_t launch_keep_scan(const ScanLaunch& a, hipStream_t s);
+hipError_t launch_gqa_splice(const GqaSpliceLaunch& a, int pairing, hipStream_t s);
+hipError_t launch_plane_evict(const PlaneEvictLaunch& a, hipStream_t s);
 
 // Blocks of kFlatThreads that cover `chunks` chunks of one layer.
 inline int64_t flat_blocks(int64_t chunks) { return (chunks + kFlatThreads - 1) / kFlatThreads; }

@@ -140,10 +140,15 @@ class DeviceGuard {
 }  // namespace
 
 struct ll_pool {
-  ll_pool_desc desc{};
+  ll_pool_desc desc{};       // GQA pools: kv_lora_rank 0, rope_dim = rotary_dim
   int page_shift = 0;
   int64_t P = 1;
-  std::vector<void*> layer_ptrs;
+  bool gqa = false;          // K and V planes with per-head RoPE bands
+  int32_t num_planes = 0;    // MLA: num_layers; GQA: 2 * num_layers (K then V)
+  int64_t row_bytes = 0;     // one row of one plane
+  int64_t band_bytes = 0;    // RoPE bytes of one row of a rotated plane
+  int32_t heads = 0, head_chunks = 0, rot_shift = 0;  // GQA row shape
+  std::vector<void*> layer_ptrs;  // the planes
   void** d_layers = nullptr;
   std::vector<SeqState> seqs;
   FreePages free;
@@ -483,8 +488,19 @@ ll_status validate_directives(const ll_pool* p, const ll_directive* dirs, int32_
     if (d.r_rows && (reinterpret_cast<uintptr_t>(d.r_rows) & 15))
       return fail(LL_EINVAL, "directive %d: r_rows is not 16-byte aligned", i);
     if (d.r_layer_stride_bytes < 0 || (d.r_layer_stride_bytes & 15) ||
-        (d.r_layer_stride_bytes && d.r_layer_stride_bytes < d.r_len * ll::kRowBytes && p->desc.num_layers > 1))
+        (d.r_layer_stride_bytes && d.r_layer_stride_bytes < d.r_len * p->row_bytes && p->desc.num_layers > 1))
       return fail(LL_EINVAL, "directive %d: bad r_layer_stride_bytes", i);
+    if (!p->gqa) {
+      if (d.r_rows_v) return fail(LL_EINVAL, "directive %d: r_rows_v is for GQA / MHA pools only", i);
+    } else {
+      if ((d.r_len > 0) != (d.r_rows_v != nullptr))
+        return fail(LL_EINVAL, "directive %d: r_rows_v must be given iff r_len > 0", i);
+      if (d.r_rows_v && (reinterpret_cast<uintptr_t>(d.r_rows_v) & 15))
+        return fail(LL_EINVAL, "directive %d: r_rows_v is not 16-byte aligned", i);
+      if (d.r_layer_stride_bytes_v < 0 || (d.r_layer_stride_bytes_v & 15) ||
+          (d.r_layer_stride_bytes_v && d.r_layer_stride_bytes_v < d.r_len * p->row_bytes && p->desc.num_layers > 1))
+        return fail(LL_EINVAL, "directive %d: bad r_layer_stride_bytes_v", i);
+    }
     const int64_t n_new = len + d.r_len - (d.s_end - d.s_start);
     if (ceil_div(n_new, p->P) > p->desc.max_pages_per_seq)
       return fail(LL_ERANGE, "directive %d: %lld rows exceed the page-table row", i, (long long)n_new);
@@ -521,43 +537,55 @@ ll_status ll_rope_delta_table(double base, int32_t rope_dim, int64_t delta, floa
   return LL_OK;
 }
 
-ll_status ll_pool_create(const ll_pool_desc* desc, ll_pool** out) {
-  if (!desc || !out) return fail(LL_EINVAL, "NULL argument");
-  *out = nullptr;
-  const ll_pool_desc& d = *desc;
-  if (d.num_layers < 1 || d.num_pages < 1 || d.max_seqs < 1 || d.max_pages_per_seq < 1)
-    return fail(LL_EINVAL, "num_layers, num_pages, max_seqs and max_pages_per_seq must be >= 1");
-  if (d.page_size < 1 || d.page_size > 256 || (d.page_size & (d.page_size - 1)))
-    return fail(LL_EINVAL, "page_size must be a power of two in [1, 256]");
-  if (d.kv_lora_rank != ll::kKvLoraRank || d.rope_dim != ll::kRopeDim)
-    return fail(LL_EUNSUPPORTED, "row shape %d + %d is not supported (512 + 64 only)", d.kv_lora_rank, d.rope_dim);
-  if (d.rope_pairing != LL_ROPE_INTERLEAVED && d.rope_pairing != LL_ROPE_HALF)
-    return fail(LL_EINVAL, "unknown rope_pairing");
-  if (!(d.rope_base > 0.0)) return fail(LL_EINVAL, "rope_base must be positive");
-  if (!d.layer_base || !d.page_table) return fail(LL_EINVAL, "layer_base and page_table are required");
-  for (int i = 0; i < d.num_layers; ++i) {
-    if (!d.layer_base[i]) return fail(LL_EINVAL, "layer_base[%d] is NULL", i);
-    if (reinterpret_cast<uintptr_t>(d.layer_base[i]) & 15) return fail(LL_EINVAL, "layer_base[%d] is not 16-byte aligned", i);
-  }
-  if (static_cast<int64_t>(d.num_pages) * d.page_size >= (int64_t{1} << 31) ||
-      static_cast<int64_t>(d.max_pages_per_seq) * d.page_size >= (int64_t{1} << 31))
-    return fail(LL_EUNSUPPORTED, "more than 2^31 rows per layer or per sequence");
-  if (d.device < 0) return fail(LL_EINVAL, "device must be >= 0");
+}  // extern "C"
 
+namespace {
+
+// Checks shared by both pool kinds.
+ll_status check_common(int32_t num_layers, int32_t page_size, int32_t num_pages, int32_t max_seqs,
+                       int32_t max_pages_per_seq, int32_t rope_pairing, double rope_base,
+                       const int32_t* page_table, int32_t device) {
+  if (num_layers < 1 || num_pages < 1 || max_seqs < 1 || max_pages_per_seq < 1)
+    return fail(LL_EINVAL, "num_layers, num_pages, max_seqs and max_pages_per_seq must be >= 1");
+  if (page_size < 1 || page_size > 256 || (page_size & (page_size - 1)))
+    return fail(LL_EINVAL, "page_size must be a power of two in [1, 256]");
+  if (rope_pairing != LL_ROPE_INTERLEAVED && rope_pairing != LL_ROPE_HALF) return fail(LL_EINVAL, "unknown rope_pairing");
+  if (!(rope_base > 0.0)) return fail(LL_EINVAL, "rope_base must be positive");
+  if (!page_table) return fail(LL_EINVAL, "page_table is required");
+  if (static_cast<int64_t>(num_pages) * page_size >= (int64_t{1} << 31) ||
+      static_cast<int64_t>(max_pages_per_seq) * page_size >= (int64_t{1} << 31))
+    return fail(LL_EUNSUPPORTED, "more than 2^31 rows per layer or per sequence");
+  if (device < 0) return fail(LL_EINVAL, "device must be >= 0");
+  return LL_OK;
+}
+
+ll_status check_planes(void* const* base, int32_t n, const char* name) {
+  if (!base) return fail(LL_EINVAL, "%s is required", name);
+  for (int i = 0; i < n; ++i) {
+    if (!base[i]) return fail(LL_EINVAL, "%s[%d] is NULL", name, i);
+    if (reinterpret_cast<uintptr_t>(base[i]) & 15) return fail(LL_EINVAL, "%s[%d] is not 16-byte aligned", name, i);
+  }
+  return LL_OK;
+}
+
+// Allocation and device setup shared by both pool kinds; p->desc, the row
+// shape and p->layer_ptrs (the planes) are filled in by the caller.
+ll_status setup_pool(ll_pool* p, ll_pool** out) {
+  const ll_pool_desc& d = p->desc;
   DeviceGuard g(d.device);
-  if (!g.ok()) return fail(LL_EDEVICE, "hipSetDevice(%d) failed", d.device);
-  ll_pool* p = new ll_pool();
-  p->desc = d;
-  p->layer_ptrs.assign(d.layer_base, d.layer_base + d.num_layers);
-  p->desc.layer_base = nullptr;
+  if (!g.ok()) {
+    delete p;
+    return fail(LL_EDEVICE, "hipSetDevice(%d) failed", d.device);
+  }
+  p->num_planes = static_cast<int32_t>(p->layer_ptrs.size());
   p->P = d.page_size;
   while ((1 << p->page_shift) < d.page_size) ++p->page_shift;
   p->seqs.resize(static_cast<size_t>(d.max_seqs));
   p->free.init(d.num_pages);
   p->page_slot.assign(static_cast<size_t>(d.num_pages), -1);
-  hipError_t e = hipMalloc(reinterpret_cast<void**>(&p->d_layers), sizeof(void*) * d.num_layers);
+  hipError_t e = hipMalloc(reinterpret_cast<void**>(&p->d_layers), sizeof(void*) * p->num_planes);
   if (e == hipSuccess)
-    e = hipMemcpy(p->d_layers, p->layer_ptrs.data(), sizeof(void*) * d.num_layers, hipMemcpyHostToDevice);
+    e = hipMemcpy(p->d_layers, p->layer_ptrs.data(), sizeof(void*) * p->num_planes, hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&p->readback_ev, hipEventDisableTiming);
   if (e == hipSuccess) e = hipStreamCreateWithFlags(&p->copy_stream, hipStreamNonBlocking);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&p->upload_ev, hipEventDisableTiming);
@@ -570,6 +598,70 @@ ll_status ll_pool_create(const ll_pool_desc* desc, ll_pool** out) {
   }
   *out = p;
   return LL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ll_status ll_pool_create(const ll_pool_desc* desc, ll_pool** out) {
+  if (!desc || !out) return fail(LL_EINVAL, "NULL argument");
+  *out = nullptr;
+  const ll_pool_desc& d = *desc;
+  ll_status rc = check_common(d.num_layers, d.page_size, d.num_pages, d.max_seqs, d.max_pages_per_seq, d.rope_pairing,
+                              d.rope_base, d.page_table, d.device);
+  if (rc) return rc;
+  if (d.kv_lora_rank != ll::kKvLoraRank || d.rope_dim != ll::kRopeDim)
+    return fail(LL_EUNSUPPORTED, "row shape %d + %d is not supported (512 + 64 only)", d.kv_lora_rank, d.rope_dim);
+  if ((rc = check_planes(d.layer_base, d.num_layers, "layer_base"))) return rc;
+  ll_pool* p = new ll_pool();
+  p->desc = d;
+  p->desc.layer_base = nullptr;
+  p->layer_ptrs.assign(d.layer_base, d.layer_base + d.num_layers);
+  p->row_bytes = ll::kRowBytes;
+  p->band_bytes = 2 * ll::kRopeDim;
+  return setup_pool(p, out);
+}
+
+ll_status ll_pool_create_gqa(const ll_gqa_pool_desc* desc, ll_pool** out) {
+  if (!desc || !out) return fail(LL_EINVAL, "NULL argument");
+  *out = nullptr;
+  const ll_gqa_pool_desc& d = *desc;
+  ll_status rc = check_common(d.num_layers, d.page_size, d.num_pages, d.max_seqs, d.max_pages_per_seq, d.rope_pairing,
+                              d.rope_base, d.page_table, d.device);
+  if (rc) return rc;
+  if (d.num_kv_heads < 1 || d.head_dim < 8 || d.head_dim % 8)
+    return fail(LL_EUNSUPPORTED, "num_kv_heads must be >= 1 and head_dim a multiple of 8");
+  if (static_cast<int64_t>(d.num_kv_heads) * d.head_dim > 32768)
+    return fail(LL_EUNSUPPORTED, "num_kv_heads * head_dim above 32768");
+  if (d.rotary_dim < 16 || d.rotary_dim > 2 * ll::kMaxBandPairs || (d.rotary_dim & (d.rotary_dim - 1)) ||
+      d.head_dim % d.rotary_dim)
+    return fail(LL_EUNSUPPORTED, "rotary_dim must be a power of two in [16, 256] that divides head_dim");
+  if ((rc = check_planes(d.k_layer_base, d.num_layers, "k_layer_base"))) return rc;
+  if ((rc = check_planes(d.v_layer_base, d.num_layers, "v_layer_base"))) return rc;
+  ll_pool* p = new ll_pool();
+  ll_pool_desc& pd = p->desc;
+  pd.num_layers = d.num_layers;
+  pd.page_size = d.page_size;
+  pd.num_pages = d.num_pages;
+  pd.max_seqs = d.max_seqs;
+  pd.max_pages_per_seq = d.max_pages_per_seq;
+  pd.kv_lora_rank = 0;
+  pd.rope_dim = d.rotary_dim;
+  pd.rope_pairing = d.rope_pairing;
+  pd.rope_base = d.rope_base;
+  pd.layer_base = nullptr;
+  pd.page_table = d.page_table;
+  pd.device = d.device;
+  p->gqa = true;
+  p->layer_ptrs.assign(d.k_layer_base, d.k_layer_base + d.num_layers);
+  p->layer_ptrs.insert(p->layer_ptrs.end(), d.v_layer_base, d.v_layer_base + d.num_layers);
+  p->heads = d.num_kv_heads;
+  p->head_chunks = d.head_dim / 8;
+  while ((8 << p->rot_shift) < d.rotary_dim) ++p->rot_shift;
+  p->row_bytes = static_cast<int64_t>(d.num_kv_heads) * d.head_dim * 2;
+  p->band_bytes = static_cast<int64_t>(d.num_kv_heads) * d.rotary_dim * 2;
+  return setup_pool(p, out);
 }
 
 void ll_pool_destroy(ll_pool* p) {
@@ -742,9 +834,10 @@ ll_status leyline_splice(ll_pool* p, const ll_directive* dirs, int32_t n, void* 
     for (char x : plans[i].inplace) n_rot_tasks += x;
     n_entries += static_cast<int64_t>(plans[i].reuse.size());
   }
-  if (n_move_tasks * P * ll::kRowChunks >= (int64_t{1} << 32) ||
-      n_rot_tasks * P * ll::kRowChunks >= (int64_t{1} << 32))
-    return fail(LL_EUNSUPPORTED, "one splice may write at most 2^32 / 72 rows per layer");
+  const int64_t row_chunks = p->row_bytes / 16;
+  if (n_move_tasks * P * row_chunks >= (int64_t{1} << 32) || n_rot_tasks * P * row_chunks >= (int64_t{1} << 32))
+    return fail(LL_EUNSUPPORTED, "one splice may write at most 2^32 16-byte chunks per layer");
+  const size_t dir_bytes = p->gqa ? sizeof(ll::GqaDir) : sizeof(ll::SpliceDir);
 
   // --- device work: descriptors written straight into pinned staging, one
   // upload, one launch
@@ -752,15 +845,16 @@ ll_status leyline_splice(ll_pool* p, const ll_directive* dirs, int32_t n, void* 
   hipStream_t st = static_cast<hipStream_t>(stream);
   if ((rc = begin_call(p, st))) return rc;
   Staging* sg = nullptr;
-  rc = stage_acquire(p, stage_bytes_for({n * sizeof(ll::SpliceDir), (n_move_tasks + n_rot_tasks) * sizeof(ll::SpliceTask),
+  rc = stage_acquire(p, stage_bytes_for({n * dir_bytes, (n_move_tasks + n_rot_tasks) * sizeof(ll::SpliceTask),
                                          n * sizeof(ll::TableWrite), static_cast<size_t>(n_entries) * 4}),
                      &sg);
   if (rc) return rc;
-  const size_t o_d = stage_put(sg, nullptr, n * sizeof(ll::SpliceDir));
+  const size_t o_d = stage_put(sg, nullptr, n * dir_bytes);
   const size_t o_t = stage_put(sg, nullptr, (n_move_tasks + n_rot_tasks) * sizeof(ll::SpliceTask));
   const size_t o_w = stage_put(sg, nullptr, n * sizeof(ll::TableWrite));
   const size_t o_p = stage_put(sg, nullptr, static_cast<size_t>(n_entries) * 4);
   ll::SpliceDir* ddirs = reinterpret_cast<ll::SpliceDir*>(sg->host + o_d);
+  ll::GqaDir* gdirs = reinterpret_cast<ll::GqaDir*>(sg->host + o_d);
   ll::SpliceTask* move_out = reinterpret_cast<ll::SpliceTask*>(sg->host + o_t);
   ll::SpliceTask* rot_out = move_out + n_move_tasks;
   ll::TableWrite* writes = reinterpret_cast<ll::TableWrite*>(sg->host + o_w);
@@ -776,9 +870,16 @@ ll_status leyline_splice(ll_pool* p, const ll_directive* dirs, int32_t n, void* 
     const SeqState& s = p->seqs[d.seq_id];
     const std::vector<int32_t>& T = s.pages;
     const int64_t old_pages = static_cast<int64_t>(T.size());
-    ll::SpliceDir& dd = ddirs[i];
     const int64_t r = d.mode == LL_FORGET ? 0 : d.r_len;
-    rope_table(p->desc.rope_base, ll::kRopeDim, pl.delta, dd.cos_, dd.sin_);
+    if (p->gqa) {
+      ll::GqaDir& gd = gdirs[i];
+      rope_table(p->desc.rope_base, p->desc.rope_dim, pl.delta, gd.cos_, gd.sin_);
+      gd.stub_v = static_cast<const ll::chunk_t*>(d.mode == LL_FORGET ? nullptr : d.r_rows_v);
+      gd.stub_v_layer_chunks = (d.r_layer_stride_bytes_v ? d.r_layer_stride_bytes_v : r * p->row_bytes) / 16;
+    } else {
+      ll::SpliceDir& dd = ddirs[i];
+      rope_table(p->desc.rope_base, ll::kRopeDim, pl.delta, dd.cos_, dd.sin_);
+    }
     ll::SpliceTask base{};
     base.dir = i;
     base.rotate = (d.mode == LL_AMORTIZE && pl.delta != 0) ? 1 : 0;
@@ -787,7 +888,7 @@ ll_status leyline_splice(ll_pool* p, const ll_directive* dirs, int32_t n, void* 
     base.delta = static_cast<int32_t>(pl.delta);
     base.n_new = static_cast<int32_t>(pl.n_new);
     base.stub = static_cast<const ll::chunk_t*>(d.mode == LL_FORGET ? nullptr : d.r_rows);
-    base.stub_layer_chunks = (d.r_layer_stride_bytes ? d.r_layer_stride_bytes : r * ll::kRowBytes) / 16;
+    base.stub_layer_chunks = (d.r_layer_stride_bytes ? d.r_layer_stride_bytes : r * p->row_bytes) / 16;
     base.pre_page = base.down_page0 = base.down_page1 = -1;
     base.down_lp0 = -1;
     std::vector<int32_t>& nt = new_tables[i];
@@ -834,28 +935,53 @@ ll_status leyline_splice(ll_pool* p, const ll_directive* dirs, int32_t n, void* 
     for (size_t k = 0; k < kept.size(); ++k) stats.freed_pages += kept[k] ? 0 : 1;
   }
   const int64_t L = p->desc.num_layers;
-  stats.alg_bytes = L * (2 * ll::kRowBytes * stats.rows_moved + 2 * ll::kRopeDim * 2 * stats.rows_rotated_inplace);
+  stats.alg_bytes = p->num_planes * 2 * p->row_bytes * stats.rows_moved + L * 2 * p->band_bytes * stats.rows_rotated_inplace;
   if ((rc = upload(p, sg, st))) return rc;
-
-  ll::SpliceLaunch a{};
-  a.layers = reinterpret_cast<const ll::chunk_t* const*>(p->d_layers);
-  a.num_layers = p->desc.num_layers;
-  a.page_shift = p->page_shift;
-  a.tasks = reinterpret_cast<const ll::SpliceTask*>(sg->dev + o_t);
-  a.n_move_tasks = n_move_tasks;
-  a.n_rot_tasks = n_rot_tasks;
-  a.move_blocks_per_layer = ll::flat_blocks(n_move_tasks * P * ll::kRowChunks);
-  a.rot_blocks_per_layer = ll::flat_blocks(n_rot_tasks * P * (ll::kRowChunks - ll::kKpeChunk0));
-  a.dirs = reinterpret_cast<const ll::SpliceDir*>(sg->dev + o_d);
-  a.twrites = reinterpret_cast<const ll::TableWrite*>(sg->dev + o_w);
-  a.tables = reinterpret_cast<const int32_t*>(sg->dev + o_p);
-  a.n_twrites = n;
-  a.max_pages_per_seq = p->desc.max_pages_per_seq;
-  a.page_table = p->desc.page_table;
   ProfRec rec{};
-  if (p->profiling && (rc = prof_begin(p, 0, st, &rec))) return rc;
-  hipError_t e = ll::launch_splice(a, p->desc.rope_pairing, st);
-  if (e != hipSuccess) return device_fail(p, e, "splice_kernel launch");
+  hipError_t e;
+  if (p->gqa) {
+    ll::GqaSpliceLaunch a{};
+    a.planes = reinterpret_cast<const ll::chunk_t* const*>(p->d_layers);
+    a.num_layers = p->desc.num_layers;
+    a.page_shift = p->page_shift;
+    a.row_chunks = static_cast<int32_t>(row_chunks);
+    a.head_chunks = p->head_chunks;
+    a.rot_shift = p->rot_shift;
+    a.heads = p->heads;
+    a.tasks = reinterpret_cast<const ll::SpliceTask*>(sg->dev + o_t);
+    a.n_move_tasks = n_move_tasks;
+    a.n_rot_tasks = n_rot_tasks;
+    a.move_blocks_per_plane = ll::flat_blocks(n_move_tasks * P * row_chunks);
+    a.rot_blocks_per_plane = ll::flat_blocks(n_rot_tasks * P * (p->heads << p->rot_shift));
+    a.dirs = reinterpret_cast<const ll::GqaDir*>(sg->dev + o_d);
+    a.twrites = reinterpret_cast<const ll::TableWrite*>(sg->dev + o_w);
+    a.tables = reinterpret_cast<const int32_t*>(sg->dev + o_p);
+    a.n_twrites = n;
+    a.max_pages_per_seq = p->desc.max_pages_per_seq;
+    a.page_table = p->desc.page_table;
+    if (p->profiling && (rc = prof_begin(p, 0, st, &rec))) return rc;
+    e = ll::launch_gqa_splice(a, p->desc.rope_pairing, st);
+    if (e != hipSuccess) return device_fail(p, e, "gqa_splice_kernel launch");
+  } else {
+    ll::SpliceLaunch a{};
+    a.layers = reinterpret_cast<const ll::chunk_t* const*>(p->d_layers);
+    a.num_layers = p->desc.num_layers;
+    a.page_shift = p->page_shift;
+    a.tasks = reinterpret_cast<const ll::SpliceTask*>(sg->dev + o_t);
+    a.n_move_tasks = n_move_tasks;
+    a.n_rot_tasks = n_rot_tasks;
+    a.move_blocks_per_layer = ll::flat_blocks(n_move_tasks * P * ll::kRowChunks);
+    a.rot_blocks_per_layer = ll::flat_blocks(n_rot_tasks * P * (ll::kRowChunks - ll::kKpeChunk0));
+    a.dirs = reinterpret_cast<const ll::SpliceDir*>(sg->dev + o_d);
+    a.twrites = reinterpret_cast<const ll::TableWrite*>(sg->dev + o_w);
+    a.tables = reinterpret_cast<const int32_t*>(sg->dev + o_p);
+    a.n_twrites = n;
+    a.max_pages_per_seq = p->desc.max_pages_per_seq;
+    a.page_table = p->desc.page_table;
+    if (p->profiling && (rc = prof_begin(p, 0, st, &rec))) return rc;
+    e = ll::launch_splice(a, p->desc.rope_pairing, st);
+    if (e != hipSuccess) return device_fail(p, e, "splice_kernel launch");
+  }
   if (p->profiling) {
     rec.bytes = stats.alg_bytes + 4 * stats.table_entries;
     if ((rc = prof_end(p, 0, st, &rec))) return rc;
@@ -1033,7 +1159,9 @@ ll_status kv_evict_compact(ll_pool* p, const int32_t* seq_ids, int32_t n, const 
   }
   stats.fresh_pages = need;
   stats.table_entries = static_cast<int64_t>(tp.packed.size());
-  stats.alg_bytes = p->desc.num_layers * 2 * ll::kRowBytes * stats.rows_moved;
+  stats.alg_bytes = p->num_planes * 2 * p->row_bytes * stats.rows_moved;
+  if (static_cast<int64_t>(tasks.size()) * P * (p->row_bytes / 16) >= (int64_t{1} << 32))
+    return fail(LL_EUNSUPPORTED, "one eviction may move at most 2^32 16-byte chunks per layer");
 
   Staging* s2 = nullptr;
   rc = stage_acquire(p, stage_bytes_for({tasks.size() * sizeof(ll::EvictTask), tp.writes.size() * sizeof(ll::TableWrite),
@@ -1044,25 +1172,45 @@ ll_status kv_evict_compact(ll_pool* p, const int32_t* seq_ids, int32_t n, const 
   const size_t o_w = stage_put(s2, tp.writes.data(), tp.writes.size() * sizeof(ll::TableWrite));
   const size_t o_p = stage_put(s2, tp.packed.data(), tp.packed.size() * 4);
   if ((rc = upload(p, s2, st))) return rc;
-  ll::EvictLaunch a{};
-  a.layers = reinterpret_cast<const ll::chunk_t* const*>(p->d_layers);
-  a.num_layers = p->desc.num_layers;
-  a.page_shift = p->page_shift;
-  a.tasks = reinterpret_cast<const ll::EvictTask*>(s2->dev + o_t);
-  a.n_tasks = static_cast<int64_t>(tasks.size());
-  if (a.n_tasks * P * ll::kRowChunks >= (int64_t{1} << 32))
-    return fail(LL_EUNSUPPORTED, "one eviction may move at most 2^32 / 72 rows per layer");
-  a.blocks_per_layer = ll::flat_blocks(a.n_tasks * P * ll::kRowChunks);
-  a.src_rows = sc.src_rows;
-  a.twrites = reinterpret_cast<const ll::TableWrite*>(s2->dev + o_w);
-  a.tables = reinterpret_cast<const int32_t*>(s2->dev + o_p);
-  a.n_twrites = static_cast<int32_t>(tp.writes.size());
-  a.max_pages_per_seq = p->desc.max_pages_per_seq;
-  a.page_table = p->desc.page_table;
+  const int64_t row_chunks = p->row_bytes / 16;
+  const int64_t n_tasks = static_cast<int64_t>(tasks.size());
   ProfRec rec{};
-  if (p->profiling && (rc = prof_begin(p, 0, st, &rec))) return rc;
-  e = ll::launch_evict_move(a, st);
-  if (e != hipSuccess) return device_fail(p, e, "evict_move_kernel launch");
+  if (p->gqa) {
+    ll::PlaneEvictLaunch a{};
+    a.planes = reinterpret_cast<const ll::chunk_t* const*>(p->d_layers);
+    a.num_planes = p->num_planes;
+    a.page_shift = p->page_shift;
+    a.row_chunks = static_cast<int32_t>(row_chunks);
+    a.tasks = reinterpret_cast<const ll::EvictTask*>(s2->dev + o_t);
+    a.n_tasks = n_tasks;
+    a.blocks_per_plane = ll::flat_blocks(n_tasks * P * row_chunks);
+    a.src_rows = sc.src_rows;
+    a.twrites = reinterpret_cast<const ll::TableWrite*>(s2->dev + o_w);
+    a.tables = reinterpret_cast<const int32_t*>(s2->dev + o_p);
+    a.n_twrites = static_cast<int32_t>(tp.writes.size());
+    a.max_pages_per_seq = p->desc.max_pages_per_seq;
+    a.page_table = p->desc.page_table;
+    if (p->profiling && (rc = prof_begin(p, 0, st, &rec))) return rc;
+    e = ll::launch_plane_evict(a, st);
+    if (e != hipSuccess) return device_fail(p, e, "plane_evict_kernel launch");
+  } else {
+    ll::EvictLaunch a{};
+    a.layers = reinterpret_cast<const ll::chunk_t* const*>(p->d_layers);
+    a.num_layers = p->desc.num_layers;
+    a.page_shift = p->page_shift;
+    a.tasks = reinterpret_cast<const ll::EvictTask*>(s2->dev + o_t);
+    a.n_tasks = n_tasks;
+    a.blocks_per_layer = ll::flat_blocks(n_tasks * P * row_chunks);
+    a.src_rows = sc.src_rows;
+    a.twrites = reinterpret_cast<const ll::TableWrite*>(s2->dev + o_w);
+    a.tables = reinterpret_cast<const int32_t*>(s2->dev + o_p);
+    a.n_twrites = static_cast<int32_t>(tp.writes.size());
+    a.max_pages_per_seq = p->desc.max_pages_per_seq;
+    a.page_table = p->desc.page_table;
+    if (p->profiling && (rc = prof_begin(p, 0, st, &rec))) return rc;
+    e = ll::launch_evict_move(a, st);
+    if (e != hipSuccess) return device_fail(p, e, "evict_move_kernel launch");
+  }
   if (p->profiling) {
     rec.bytes = stats.alg_bytes + 4 * stats.table_entries;
     if ((rc = prof_end(p, 0, st, &rec))) return rc;

@@ -28,7 +28,7 @@ EXPORTS = (
     "ll_pool_create", "ll_pool_destroy", "ll_seq_alloc", "ll_seq_set_pages", "ll_seq_free",
     "ll_seq_get", "ll_pool_free_pages", "leyline_splice", "kv_evict_compact", "ll_ptable_reindex",
     "ll_rope_delta_table", "ll_last_plan_stats", "ll_pool_set_profiling", "ll_profile_read",
-    "ll_last_error", "ll_status_str",
+    "ll_last_error", "ll_status_str", "ll_pool_create_gqa",
 )
 
 
@@ -55,6 +55,25 @@ class _PoolDesc(ctypes.Structure):
     ]
 
 
+class _GqaPoolDesc(ctypes.Structure):
+    _fields_ = [
+        ("num_layers", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32),
+        ("max_seqs", ctypes.c_int32),
+        ("max_pages_per_seq", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("rotary_dim", ctypes.c_int32),
+        ("rope_pairing", ctypes.c_int32),
+        ("rope_base", ctypes.c_double),
+        ("k_layer_base", ctypes.POINTER(ctypes.c_void_p)),
+        ("v_layer_base", ctypes.POINTER(ctypes.c_void_p)),
+        ("page_table", ctypes.c_void_p),
+        ("device", ctypes.c_int32),
+    ]
+
+
 class _Directive(ctypes.Structure):
     _fields_ = [
         ("seq_id", ctypes.c_int32),
@@ -64,6 +83,8 @@ class _Directive(ctypes.Structure):
         ("r_len", ctypes.c_int64),
         ("r_rows", ctypes.c_void_p),
         ("r_layer_stride_bytes", ctypes.c_int64),
+        ("r_rows_v", ctypes.c_void_p),
+        ("r_layer_stride_bytes_v", ctypes.c_int64),
     ]
 
 
@@ -86,6 +107,7 @@ def _load():
     P, i32, i64, vp = ctypes.POINTER, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
     sig = {
         "ll_pool_create": (i32, [P(_PoolDesc), P(vp)]),
+        "ll_pool_create_gqa": (i32, [P(_GqaPoolDesc), P(vp)]),
         "ll_pool_destroy": (None, [vp]),
         "ll_seq_alloc": (i32, [vp, i64, P(i32), vp]),
         "ll_seq_set_pages": (i32, [vp, i32, P(i32), i64, vp]),
@@ -145,13 +167,16 @@ def rope_delta_table(delta: int, rope_dim: int = ROPE_DIM, base: float = 10000.0
 
 @dataclass
 class Directive:
-    """D = (s_start, s_end, R, m).  `stub` is a device bf16 tensor [L][r_len][576]
-    (or [r_len][576] for a one-layer pool), or None for r_len = 0."""
+    """D = (s_start, s_end, R, m).  MLA pools: `stub` is a device bf16 tensor
+    [L][r_len][576] (or [r_len][576] for a one-layer pool), or None for
+    r_len = 0.  GQA / MHA pools: `stub` holds the K rows and `stub_v` the V
+    rows, each [L][r_len][H][D]."""
     seq: int
     s_start: int
     s_end: int
     stub: object = None
     mode: int = AMORTIZE
+    stub_v: object = None
 
 
 @dataclass
@@ -170,6 +195,8 @@ class Pool:
     layers: a bf16 CUDA tensor [L][num_pages][page_size][576] or a list of L
     tensors [num_pages][page_size][576]; page_table: int32 CUDA tensor
     [max_seqs][max_pages_per_seq].  Both are kept referenced by the pool."""
+
+    gqa = False
 
     def __init__(self, layers, page_table, rope_base: float = 10000.0, pairing: int = ROPE_INTERLEAVED):
         import torch
@@ -244,24 +271,35 @@ class Pool:
         return n.value
 
     # -- the path
-    def splice(self, directives, stream=None) -> None:
+    def _stub(self, st):
+        """(r_len, pointer, layer stride in bytes) of one stub tensor."""
         import torch
+        if st.dtype != torch.bfloat16 or not st.is_cuda or st.shape[-1] != ROW:
+            raise ValueError("stub must be a bf16 CUDA tensor [..., r_len, 576]")
+        if st.dim() == 2:
+            st = st.unsqueeze(0)
+        if st.shape[0] != self.num_layers or st.stride(2) != 1 or st.stride(1) != ROW:
+            raise ValueError("stub must be [num_layers][r_len][576] with contiguous rows")
+        r_len = st.shape[1]
+        return r_len, (st.data_ptr() if r_len else None), st.stride(0) * 2
+
+    def splice(self, directives, stream=None) -> None:
         n = len(directives)
         arr = (_Directive * max(1, n))()
         for i, d in enumerate(directives):
-            r_len, ptr, stride = 0, None, 0
+            r_len, ptr, stride, ptr_v, stride_v = 0, None, 0, None, 0
             if d.stub is not None and d.mode == AMORTIZE:
-                st = d.stub
-                if st.dtype != torch.bfloat16 or not st.is_cuda or st.shape[-1] != ROW:
-                    raise ValueError("stub must be a bf16 CUDA tensor [..., r_len, 576]")
-                if st.dim() == 2:
-                    st = st.unsqueeze(0)
-                if st.shape[0] != self.num_layers or st.stride(2) != 1 or st.stride(1) != ROW:
-                    raise ValueError("stub must be [num_layers][r_len][576] with contiguous rows")
-                r_len = st.shape[1]
-                ptr = st.data_ptr() if r_len else None
-                stride = st.stride(0) * 2
-            arr[i] = _Directive(int(d.seq), int(d.mode), int(d.s_start), int(d.s_end), int(r_len), ptr, stride)
+                r_len, ptr, stride = self._stub(d.stub)
+                if self.gqa:
+                    if d.stub_v is None:
+                        raise ValueError("a GQA / MHA directive needs stub_v with stub")
+                    r_v, ptr_v, stride_v = self._stub(d.stub_v)
+                    if r_v != r_len:
+                        raise ValueError("stub and stub_v hold different row counts")
+            elif d.stub_v is not None and d.mode == AMORTIZE:
+                raise ValueError("stub_v without stub")
+            arr[i] = _Directive(int(d.seq), int(d.mode), int(d.s_start), int(d.s_end), int(r_len), ptr, stride,
+                                ptr_v, stride_v)
         _check(_lib.leyline_splice(self._h, arr, n, _stream_handle(stream)))
 
     def evict(self, seqs, keep, offsets, stream=None) -> None:
@@ -295,3 +333,64 @@ class Pool:
         n, ms, b = ctypes.c_int64(), ctypes.c_double(), ctypes.c_int64()
         _check(_lib.ll_profile_read(self._h, kernel, ctypes.byref(n), ctypes.byref(ms), ctypes.byref(b)))
         return n.value, ms.value, b.value
+
+
+class GqaPool(Pool):
+    """A paged GQA / MHA cache over caller-owned torch memory.
+
+    k_layers, v_layers: bf16 CUDA tensors [L][num_pages][page_size][H][D] (or
+    lists of L tensors [num_pages][page_size][H][D]); the first rotary_dim
+    values of every K head are its RoPE band.  page_table as for Pool."""
+
+    gqa = True
+
+    def __init__(self, k_layers, v_layers, page_table, rotary_dim: int | None = None,
+                 rope_base: float = 10000.0, pairing: int = ROPE_INTERLEAVED):
+        import torch
+
+        def planes(x):
+            return [x[i] for i in range(x.shape[0])] if isinstance(x, torch.Tensor) else list(x)
+
+        k_list, v_list = planes(k_layers), planes(v_layers)
+        if not k_list or len(k_list) != len(v_list):
+            raise ValueError("k_layers and v_layers must hold the same number (>= 1) of layers")
+        shape = tuple(k_list[0].shape)
+        if len(shape) != 4:
+            raise ValueError("layer shape must be [num_pages][page_size][H][D]")
+        for t in k_list + v_list:
+            if t.dtype != torch.bfloat16 or not t.is_cuda or tuple(t.shape) != shape or not t.is_contiguous():
+                raise ValueError("K and V layers must be contiguous bf16 CUDA tensors of one shape [pages][P][H][D]")
+        if page_table.dtype != torch.int32 or not page_table.is_cuda or page_table.dim() != 2 \
+                or not page_table.is_contiguous():
+            raise ValueError("page_table must be a contiguous int32 CUDA tensor [max_seqs][max_pages_per_seq]")
+        self._layers = k_list + v_list
+        self._keep = (k_layers, v_layers)
+        self.page_table = page_table
+        self.num_layers = len(k_list)
+        self.num_pages, self.page_size, self.heads, self.head_dim = shape
+        self.rotary_dim = self.head_dim if rotary_dim is None else int(rotary_dim)
+        self.row = self.heads * self.head_dim
+        self.max_seqs, self.max_pages_per_seq = page_table.shape
+        self.device = k_list[0].device
+        self._kptrs = (ctypes.c_void_p * self.num_layers)(*[t.data_ptr() for t in k_list])
+        self._vptrs = (ctypes.c_void_p * self.num_layers)(*[t.data_ptr() for t in v_list])
+        d = _GqaPoolDesc(self.num_layers, self.page_size, self.num_pages, self.max_seqs, self.max_pages_per_seq,
+                         self.heads, self.head_dim, self.rotary_dim, pairing, rope_base,
+                         ctypes.cast(self._kptrs, ctypes.POINTER(ctypes.c_void_p)),
+                         ctypes.cast(self._vptrs, ctypes.POINTER(ctypes.c_void_p)),
+                         page_table.data_ptr(), self.device.index or 0)
+        h = ctypes.c_void_p()
+        _check(_lib.ll_pool_create_gqa(ctypes.byref(d), ctypes.byref(h)))
+        self._h = h
+
+    def _stub(self, st):
+        import torch
+        if st.dtype != torch.bfloat16 or not st.is_cuda or tuple(st.shape[-2:]) != (self.heads, self.head_dim):
+            raise ValueError("stub rows must be bf16 CUDA tensors [..., r_len, H, D]")
+        if st.dim() == 3:
+            st = st.unsqueeze(0)
+        if st.shape[0] != self.num_layers or st.stride(3) != 1 or st.stride(2) != self.head_dim \
+                or st.stride(1) != self.row:
+            raise ValueError("stub rows must be [num_layers][r_len][H][D] with contiguous rows")
+        r_len = st.shape[1]
+        return r_len, (st.data_ptr() if r_len else None), st.stride(0) * 2

@@ -34,7 +34,7 @@ def test_header_declares_the_path_entry_points():
     names = _declared()
     for n in ("leyline_splice", "kv_evict_compact", "ll_ptable_reindex", "ll_pool_create"):
         assert n in names
-    assert len(names) == 16
+    assert len(names) == 17
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -73,6 +73,37 @@ def test_pool_create_rejects_bad_descriptors_before_touching_a_device():
     misaligned = (ctypes.c_void_p * 2)(16, 40)
     d = L._PoolDesc(**{**base, "layer_base": ctypes.cast(misaligned, ctypes.POINTER(ctypes.c_void_p))})
     assert L._lib.ll_pool_create(ctypes.byref(d), ctypes.byref(ctypes.c_void_p())) == L.LL_EINVAL
+
+
+def test_gqa_pool_create_rejects_bad_descriptors_before_touching_a_device():
+    from mla_paged_cache_amd import leyline as L
+    kp = (ctypes.c_void_p * 2)(16, 32)
+    vp = (ctypes.c_void_p * 2)(48, 64)
+    base = dict(num_layers=2, page_size=16, num_pages=8, max_seqs=1, max_pages_per_seq=8,
+                num_kv_heads=8, head_dim=128, rotary_dim=128, rope_pairing=1, rope_base=500000.0,
+                k_layer_base=ctypes.cast(kp, ctypes.POINTER(ctypes.c_void_p)),
+                v_layer_base=ctypes.cast(vp, ctypes.POINTER(ctypes.c_void_p)), page_table=64, device=0)
+    cases = [
+        (dict(page_size=3), L.LL_EINVAL),
+        (dict(num_kv_heads=0), L.LL_EUNSUPPORTED),
+        (dict(head_dim=100), L.LL_EUNSUPPORTED),
+        (dict(rotary_dim=96), L.LL_EUNSUPPORTED),        # not a power of two
+        (dict(rotary_dim=8), L.LL_EUNSUPPORTED),         # below 16
+        (dict(rotary_dim=256), L.LL_EUNSUPPORTED),       # does not divide head_dim 128
+        (dict(head_dim=512, rotary_dim=512), L.LL_EUNSUPPORTED),
+        (dict(num_kv_heads=512, head_dim=128), L.LL_EUNSUPPORTED),  # row wider than 32768
+        (dict(rope_pairing=3), L.LL_EINVAL),
+        (dict(v_layer_base=None), L.LL_EINVAL),
+        (dict(page_table=None), L.LL_EINVAL),
+    ]
+    for change, code in cases:
+        d = L._GqaPoolDesc(**{**base, **change})
+        h = ctypes.c_void_p()
+        assert L._lib.ll_pool_create_gqa(ctypes.byref(d), ctypes.byref(h)) == code, change
+        assert not h.value
+    misaligned = (ctypes.c_void_p * 2)(48, 72)
+    d = L._GqaPoolDesc(**{**base, "v_layer_base": ctypes.cast(misaligned, ctypes.POINTER(ctypes.c_void_p))})
+    assert L._lib.ll_pool_create_gqa(ctypes.byref(d), ctypes.byref(ctypes.c_void_p())) == L.LL_EINVAL
 
 
 def test_null_pool_calls_fail_cleanly():
