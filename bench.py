@@ -24,6 +24,10 @@ Other workloads (one JSON line each, not the headline):
   --workload evict_256x16k_27layer_p16 / _p1
                                      KV-streams eviction of 256 rollouts x
                                      16384 tokens under random turn drops
+  --workload splice_32k_llama8b      the headline splice on a GQA cache of
+                                     Llama-3-8B shape (32 layers, K and V of 8
+                                     heads x 128, RoPE on all 128, half-split,
+                                     base 500000)
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -60,8 +64,22 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--workload", default="splice_32k_27layer",
                     choices=["splice_32k_27layer", "splice_16x32k_27layer", "evict_256x16k_27layer_p16",
-                             "evict_256x16k_27layer_p1"])
+                             "evict_256x16k_27layer_p1", "splice_32k_llama8b"])
     return ap.parse_args()
+
+
+# The source file of each measured kernel; its hash also covers the shared
+# device helpers and the launch structures.
+KERNEL_SOURCE = {"splice_kernel": "kernels.hip", "evict_move_kernel": "kernels.hip",
+                 "gqa_splice_kernel": "kernels_gqa.hip", "plane_evict_kernel": "kernels_gqa.hip"}
+
+
+def kernel_source_sha(kernel: str) -> str:
+    csrc = os.path.join(ROOT, "mla_paged_cache_amd", "csrc")
+    h = hashlib.sha256()
+    for name in ("device_common.h", "leyline_internal.h", KERNEL_SOURCE[kernel]):
+        h.update(open(os.path.join(csrc, name), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def profiled_traffic(kernel: str, workload: str):
@@ -72,9 +90,8 @@ def profiled_traffic(kernel: str, workload: str):
         return None
     text = open(path).read()
     m = re.search(r"traffic_bytes_per_launch: (\d+)", text)
-    h = re.search(r"kernels_hip_sha256_16: ([0-9a-f]+)", text)
-    src = open(os.path.join(ROOT, "mla_paged_cache_amd", "csrc", "kernels.hip"), "rb").read()
-    if not m or not h or hashlib.sha256(src).hexdigest()[:16] != h.group(1):
+    h = re.search(r"kernel_source_sha256_16: ([0-9a-f]+)", text)
+    if not m or not h or kernel_source_sha(kernel) != h.group(1):
         return None
     return int(m.group(1))
 
@@ -318,6 +335,64 @@ def bench_splice_batched(args):
     return out
 
 
+def bench_splice_gqa(args):
+    """The headline splice ([8192, 14336) -> 24 stub rows on one 32768-token
+    sequence, page size 16, permuted pages) on a GQA cache of Llama-3-8B
+    shape: 32 layers, K and V planes of 8 KV heads x 128, RoPE on all 128
+    dims of each K head (half-split pairs, base 500000)."""
+    import torch
+    from mla_paged_cache_amd import leyline as L
+    from synth import permuted_pages, random_rows_torch
+
+    LAYERS, HEADS, HEAD_DIM, TOKENS, PAGE, POOL_PAGES = 32, 8, 128, 32768, 16, 4096
+    S_START, S_END, STUB = 8192, 14336, 24
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    k = random_rows_torch(0, (LAYERS, POOL_PAGES, PAGE, HEADS, HEAD_DIM), dev)
+    v = random_rows_torch(1, (LAYERS, POOL_PAGES, PAGE, HEADS, HEAD_DIM), dev)
+    k_stub = random_rows_torch(2, (LAYERS, STUB, HEADS, HEAD_DIM), dev)
+    v_stub = random_rows_torch(3, (LAYERS, STUB, HEADS, HEAD_DIM), dev)
+    table = torch.full((1, TOKENS // PAGE + 8), -1, dtype=torch.int32, device=dev)
+    pool = L.GqaPool(k, v, table, rotary_dim=HEAD_DIM, rope_base=500000.0, pairing=L.ROPE_HALF)
+    T = permuted_pages(0, TOKENS // PAGE)
+    directive = [L.Directive(0, S_START, S_END, k_stub, stub_v=v_stub)]
+
+    def restore():
+        pool.seq_set_pages(0, T, TOKENS)
+
+    restore()
+    pool.splice(directive)
+    torch.cuda.synchronize()
+    alg_bytes = pool.last_stats().alg_bytes
+    for _ in range(args.warmup):
+        restore()
+        pool.splice(directive)
+    torch.cuda.synchronize()
+    pool.profile_read(0)
+    pool.set_profiling(True)
+    quiet_gc()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        restore()
+        pool.splice(directive)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    gc.enable()
+    pool.set_profiling(False)
+    launches, kernel_ms, kernel_bytes = pool.profile_read(0)
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    out = base_line(args, "splice_32k_llama8b", alg_bytes / (ms_per_step * 1e-3) / 1e9, ms_per_step, {
+        "layers": LAYERS, "kv_heads": HEADS, "head_dim": HEAD_DIM, "rotary_dim": HEAD_DIM, "tokens": TOKENS,
+        "page_size": PAGE, "pool_pages": POOL_PAGES, "span": [S_START, S_END], "stub_rows": STUB,
+        "delta": STUB - (S_END - S_START), "storage": "bf16 K and V planes, rotation in f32",
+        "alg_bytes_per_step": alg_bytes})
+    out["pct_hbm_peak"] = round(100.0 * out["value"] / HBM_PEAK_GBS, 2)
+    out["roofline"] = roofline("gqa_splice_kernel", "splice_32k_llama8b", launches, kernel_ms, kernel_bytes)
+    out["cpu_baseline"] = None
+    pool.close()
+    return out
+
+
 # ------------------------------------------------------------------- evict --
 
 def bench_evict(args, page):
@@ -404,6 +479,8 @@ def main():
         out = bench_splice_32k(args)
     elif args.workload == "splice_16x32k_27layer":
         out = bench_splice_batched(args)
+    elif args.workload == "splice_32k_llama8b":
+        out = bench_splice_gqa(args)
     else:
         out = bench_evict(args, 16 if args.workload.endswith("p16") else 1)
     print(json.dumps(out), flush=True)
