@@ -1,8 +1,9 @@
 """Seeded synthetic inputs shared by the tests, the benchmark and the smoke check.
 
 This module draws random numbers and builds input shapes only: random bf16
-rows, page permutations, directive spans and keep masks.  It holds none of the
-splice or eviction arithmetic (no shift, no rotation, no page plan), so both
+rows, page permutations, directive spans, keep masks and turn-level
+compaction logs.  It holds none of the splice, eviction or visibility
+arithmetic (no shift, no rotation, no page plan, no death times), so both
 the CPU oracle and the HIP library can be fed from it without sharing code.
 
 Workload shapes stand in for the workloads the pages describe: tool-turn stubs
@@ -102,6 +103,64 @@ def turn_drop_mask(rng: np.random.Generator, n: int, turn_lo: int = 200, turn_hi
             m[i:i + t] = 0
         i += t
     return m
+
+
+@dataclass(frozen=True)
+class EvictionEvent:
+    """One compaction of a rollout: `time` tokens had been generated when it
+    ran; `keep` is the keep mask (uint8) over the rows the cache held then, in
+    order -- the mask the inference engine hands to its eviction call."""
+    time: int
+    keep: np.ndarray
+
+
+def compaction_log(rng: np.random.Generator, n_tokens: int, strategy: str, budget: int,
+                   turn_lo: int = 64, turn_hi: int = 512, every_turns: int = 10) -> list:
+    """Eviction log of one synthetic rollout of `n_tokens` tokens, cut into
+    turns of U[turn_lo, turn_hi] tokens, compacted after every `every_turns`
+    completed turns while tokens remain (the KV-streams strategies, at turn
+    granularity; the newest turn is always kept):
+
+      * "window": keep the newest turns that fit in `budget` tokens
+        (Sliding Window, o close to B);
+      * "half": keep the newest turns that fit in budget // 2 (Markovian
+        Thinker, o = B/2, s = 0);
+      * "pick": drop each older turn with probability 1/2 (a random stand-in
+        for Markovian Pick, where the model chooses).
+
+    The generator tracks the cache as a list of (turn, length) segments; it
+    never looks at individual token indices."""
+    turns = []
+    i = 0
+    while i < n_tokens:
+        t = min(int(rng.integers(turn_lo, turn_hi + 1)), n_tokens - i)
+        turns.append(t)
+        i += t
+    held = []          # lengths of the turns the cache holds, oldest first
+    log = []
+    done = 0
+    for k, t in enumerate(turns):
+        held.append(t)
+        done += t
+        if (k + 1) % every_turns or done >= n_tokens:
+            continue
+        keep_turn = np.ones(len(held), bool)
+        if strategy in ("window", "half"):
+            cap = budget if strategy == "window" else budget // 2
+            total = 0
+            for h in range(len(held) - 1, -1, -1):
+                if h < len(held) - 1 and total + held[h] > cap:
+                    keep_turn[:h + 1] = False
+                    break
+                total += held[h]
+        elif strategy == "pick":
+            keep_turn[:-1] = rng.random(len(held) - 1) >= 0.5
+        else:
+            raise ValueError(strategy)
+        mask = np.concatenate([np.full(h, 1 if kt else 0, np.uint8) for h, kt in zip(held, keep_turn)])
+        log.append(EvictionEvent(done, mask))
+        held = [h for h, kt in zip(held, keep_turn) if kt]
+    return log
 
 
 # ---------------------------------------------------------------------------
