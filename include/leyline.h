@@ -261,6 +261,76 @@ ll_status ll_pool_set_profiling(ll_pool* pool, int32_t enable);
 ll_status ll_profile_read(ll_pool* pool, int32_t kernel, int64_t* launches, double* total_ms,
                           int64_t* total_bytes);
 
+/* ------------------------------------------------------------------------
+ * KV-streams trainer-side attention mask ([KV-streams] "how it works": the
+ * trainer reproduces the engine's evictions with a custom attention mask, so
+ * that one forward pass over a whole rollout lets every token see exactly the
+ * keys the cache held when that token was generated).
+ *
+ * A rollout is n_tokens tokens in generation order.  An eviction event
+ * (time t, keep) ran after t tokens had been generated and before token t:
+ * keep is the keep mask over the rows the cache held then, in order -- the
+ * mask the engine passed to kv_evict_compact.  The death time d_k of token k
+ * is the time of the event that dropped it (n_pad if none; k for padding keys
+ * k >= n_tokens of a batch padded to n_pad), and query q sees key k iff
+ * k <= q < d_k.  Positions are the original token indices (no reset).
+ *
+ * The calls below take a context (staging and scratch on one device) and
+ * enqueue their work on `stream`; a context is not thread-safe.  All buffers
+ * are caller-owned device memory and must stay valid until the work is done.
+ */
+typedef struct kvs_ctx kvs_ctx;
+
+typedef struct {
+  int64_t n_tokens;          /* rollout length, <= n_pad */
+  int32_t n_events;
+  const int64_t* event_time; /* host [n_events]: strictly increasing, in (0, n_tokens] */
+  const int64_t* mask_len;   /* host [n_events]: rows the cache held at each event */
+  int64_t mask_offset;       /* bytes into keep_dev of the rollout's first keep mask;
+                                its other masks follow back to back */
+} kvs_rollout_log;
+
+/* Create / destroy a context on HIP device `device`.  Errors: LL_EINVAL,
+ * LL_EDEVICE. */
+ll_status kvs_ctx_create(int32_t device, kvs_ctx** out);
+void kvs_ctx_destroy(kvs_ctx* ctx);
+
+/* Death times of n rollouts: death_dev is int32 [n][n_pad] (rollout i at
+ * i * n_pad), status_dev int32 [n].  The logs are replayed on the device: at
+ * each event a block prefix scan numbers the tokens still held, and the i-th
+ * of them dies at the event's time when keep byte i is 0.  status_dev[i] is
+ * 0, or 1 when some event's mask_len differs from the number of rows the
+ * cache held at that time (the rollout's death times are then unspecified).
+ * The host arrays are read before the call returns; the call first waits
+ * for the previous kvs_death_times call of the same context to finish on the
+ * device (it reuses that call's staging).  Errors: LL_EINVAL
+ * (n_pad outside [1, 2^31 - 2], n_tokens > n_pad, event times not increasing
+ * inside (0, n_tokens], mask_len outside [0, time], NULL pointers),
+ * LL_ENOMEM, LL_EDEVICE. */
+ll_status kvs_death_times(kvs_ctx* ctx, const kvs_rollout_log* logs, int32_t n, int64_t n_pad,
+                          const uint8_t* keep_dev, int32_t* death_dev, int32_t* status_dev, void* stream);
+
+/* Block mask from death times: the n_pad x n_pad mask of each rollout cut
+ * into block_q x block_k tiles (powers of two in [16, 1024]; edge tiles are
+ * cut at n_pad).  A tile is full when every entry is visible, empty when none
+ * is, partial otherwise.  With nq = ceil(n_pad / block_q) and
+ * nk = ceil(n_pad / block_k): partial_num / full_num are int32 [n][nq] and
+ * partial_idx / full_idx int32 [n][nq][nk]; row (i, b) lists the partial
+ * (full) key blocks of query block b in increasing order, the entries past
+ * the count are left as they were.  An attention kernel skips empty tiles,
+ * needs no mask on full tiles and applies k <= q < d_k on partial ones.
+ * Errors: LL_EINVAL, LL_ENOMEM, LL_EDEVICE. */
+ll_status kvs_block_mask(kvs_ctx* ctx, const int32_t* death_dev, int32_t n, int64_t n_pad,
+                         int32_t block_q, int32_t block_k, int32_t* partial_num, int32_t* partial_idx,
+                         int32_t* full_num, int32_t* full_idx, void* stream);
+
+/* Dense bit mask from death times: bits_dev is uint32 [n][n_pad][n_pad / 32]
+ * (16-byte aligned; n_pad a multiple of 128); bit b of word w of row q of
+ * rollout i is 1 iff query q sees key 32 w + b.  Errors: LL_EINVAL,
+ * LL_EUNSUPPORTED, LL_EDEVICE. */
+ll_status kvs_dense_mask(kvs_ctx* ctx, const int32_t* death_dev, int32_t n, int64_t n_pad,
+                         uint32_t* bits_dev, void* stream);
+
 /* Message for the calling thread's last failure ("" if none). */
 const char* ll_last_error(void);
 

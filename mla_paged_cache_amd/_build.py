@@ -1,8 +1,9 @@
 """Build the gfx950 library libleyline.so in-tree with hipcc.
 
 The library holds the HIP kernels (csrc/kernels.hip for MLA pools,
-csrc/kernels_gqa.hip for GQA / MHA pools, helpers in csrc/device_common.h) and
-the C++ host planner and C ABI (csrc/pool.cpp).  Flags:
+csrc/kernels_gqa.hip for GQA / MHA pools, csrc/kernels_kvs.hip for the
+KV-streams trainer mask, helpers in csrc/device_common.h) and the C++ host
+side and C ABI (csrc/pool.cpp, csrc/kvs_mask.cpp).  Flags:
   * --offload-arch=gfx950 only (MI355X);
   * -ffp-contract=off so the delta-rotation keeps its separately rounded
     float32 products (the kernels also say so with a pragma);
@@ -23,7 +24,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libleyline.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 
-SOURCES = [os.path.join(CSRC, "kernels.hip"), os.path.join(CSRC, "kernels_gqa.hip"), os.path.join(CSRC, "pool.cpp")]
+SOURCES = [os.path.join(CSRC, n) for n in ("kernels.hip", "kernels_gqa.hip", "kernels_kvs.hip", "pool.cpp",
+                                           "kvs_mask.cpp")]
 
 FLAGS = [
     "--offload-arch=gfx950",

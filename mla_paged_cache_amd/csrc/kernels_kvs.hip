@@ -1,0 +1,269 @@
+// gfx950 kernels of the KV-streams trainer-side attention mask ("KV-streams",
+// "how it works": the trainer reproduces the engine's evictions with a custom
+// attention mask, so one forward pass over a rollout lets each token see the
+// keys the cache held when that token was generated).
+//
+// Token k's death time d_k is the time of the eviction event that dropped it
+// (n_pad if none, k for padding keys); query q sees key k iff k <= q < d_k.
+//
+//  * kvs_death_kernel: replays a rollout's eviction log -- per event, a block
+//    prefix scan over the tokens still held gives each its row index in the
+//    event's keep mask; dropped tokens get the event's time.
+//  * kvs_minmax_kernel / kvs_block_kernel: per key block the smallest and
+//    largest death time, then per query block the sorted lists of partial and
+//    full key blocks (FlexAttention-style block mask).
+//  * kvs_dense_kernel: the packed bit mask, one 16-byte store per thread and
+//    row; a thread carries its 128 keys' bits down the rows, adds keys as the
+//    rows reach them and looks at all 128 death times again only at rows where
+//    one of them dies.
+#include "kvs_internal.h"
+
+namespace ll {
+namespace {
+
+typedef uint32_t word4 __attribute__((ext_vector_type(4)));
+
+constexpr int kDeathThreads = 1024;
+constexpr int kDeathWaves = kDeathThreads / 64;
+constexpr int kPerThread = 16;  // tokens per thread per tile
+
+// One block per rollout.  d is initialised to n_pad (held) for real tokens and
+// to k (never visible) for padding keys.  Per event at time t: the tokens
+// k < t still held (d_k == n_pad) are numbered in order by a block-wide
+// exclusive scan (wave64 ballot bit-planes, then the 16 wave totals through
+// LDS); the i-th held token is dropped, d_k = t, when keep[i] == 0.  A mask
+// whose length differs from the number of held rows sets the status word.
+__global__ __launch_bounds__(kDeathThreads) void kvs_death_kernel(KvsDeathLaunch a) {
+  __shared__ int32_t wave_total[kDeathWaves];
+  const KvsRollout r = a.rollouts[blockIdx.x];
+  const int64_t n_pad = a.n_pad;
+  const int32_t held = static_cast<int32_t>(n_pad);
+  int32_t* d = a.death + static_cast<int64_t>(blockIdx.x) * n_pad;
+  for (int64_t k = threadIdx.x; k < n_pad; k += kDeathThreads)
+    d[k] = k < r.n_tokens ? held : static_cast<int32_t>(k);
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const uint64_t lanes_below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  bool bad = false;
+  for (int e = 0; e < r.n_events; ++e) {
+    const KvsEvent ev = a.events[r.first_event + e];
+    const int64_t t = ev.time;
+    const uint8_t* m = a.keep + ev.mask_off;
+    int64_t carry = 0;
+    for (int64_t base = 0; base < t; base += int64_t{kPerThread} * kDeathThreads) {
+      const int64_t k0 = base + int64_t{kPerThread} * threadIdx.x;
+      uint32_t bits = 0;
+#pragma unroll
+      for (int c = 0; c < kPerThread; ++c)
+        if (k0 + c < t && d[k0 + c] == held) bits |= 1u << c;
+      const int cnt = __popc(bits);
+      int below = 0, total = 0;
+#pragma unroll
+      for (int bit = 0; bit < 5; ++bit) {
+        const uint64_t bal = __ballot((cnt >> bit) & 1);
+        below += __popcll(bal & lanes_below) << bit;
+        total += __popcll(bal) << bit;
+      }
+      if (lane == 0) wave_total[wave] = total;
+      __syncthreads();
+      int wave_below = 0, block_total = 0;
+#pragma unroll
+      for (int w = 0; w < kDeathWaves; ++w) {
+        const int x = wave_total[w];
+        wave_below += w < wave ? x : 0;
+        block_total += x;
+      }
+      int64_t i = carry + wave_below + below;
+      for (int c = 0; c < kPerThread; ++c)
+        if ((bits >> c) & 1u) {
+          if (i < ev.mask_len) {
+            if (m[i] == 0) d[k0 + c] = static_cast<int32_t>(t);
+          }
+          ++i;
+        }
+      carry += block_total;
+      __syncthreads();
+    }
+    bad = bad || carry != ev.mask_len;
+  }
+  if (threadIdx.x == 0) a.status[blockIdx.x] = bad ? 1 : 0;
+}
+
+// Smallest and largest death time of each key block: one wave per block.
+__global__ __launch_bounds__(256) void kvs_minmax_kernel(KvsBlockLaunch a) {
+  const int64_t gw = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) >> 6;
+  const int lane = threadIdx.x & 63;
+  if (gw >= static_cast<int64_t>(a.n) * a.nk) return;
+  const int64_t roll = gw / a.nk;
+  const int64_t j = gw - roll * a.nk;
+  const int32_t* d = a.death + roll * a.n_pad;
+  const int64_t k0 = j << a.bk_shift;
+  const int64_t k1 = min(k0 + (int64_t{1} << a.bk_shift), a.n_pad);
+  int32_t mn = INT32_MAX, mx = INT32_MIN;
+  for (int64_t k = k0 + lane; k < k1; k += 64) {
+    const int32_t x = d[k];
+    mn = min(mn, x);
+    mx = max(mx, x);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    mn = min(mn, __shfl_xor(mn, o));
+    mx = max(mx, __shfl_xor(mx, o));
+  }
+  if (lane == 0) a.minmax[gw] = make_int2(mn, mx);
+}
+
+// One wave per query block [q0, q1).  Key block j = [k0, k1) is
+//   empty   if k0 > q1 - 1 (above the diagonal);
+//   below the diagonal (k1 - 1 <= q0): full iff min d >= q1, empty iff
+//           max d <= q0, else partial;
+//   across the diagonal: never full; partial iff some key k < q1 of the
+//           block has max(k, q0) < min(d_k, q1) (an exact scan of its keys).
+// Lanes classify 64 key blocks at a time; ballots give each listed block its
+// slot, so both lists come out in increasing order.
+__global__ __launch_bounds__(256) void kvs_block_kernel(KvsBlockLaunch a) {
+  const int64_t gw = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) >> 6;
+  const int lane = threadIdx.x & 63;
+  if (gw >= static_cast<int64_t>(a.n) * a.nq) return;
+  const int64_t roll = gw / a.nq;
+  const int64_t i = gw - roll * a.nq;
+  const int32_t* d = a.death + roll * a.n_pad;
+  const int2* mm = a.minmax + roll * a.nk;
+  const int64_t q0 = i << a.bq_shift;
+  const int64_t q1 = min(q0 + (int64_t{1} << a.bq_shift), a.n_pad);
+  const int64_t bk = int64_t{1} << a.bk_shift;
+  const int32_t last = static_cast<int32_t>(min<int64_t>(a.nk, ((q1 - 1) >> a.bk_shift) + 1));
+  int32_t* p_idx = a.partial_idx + gw * a.nk;
+  int32_t* f_idx = a.full_idx + gw * a.nk;
+  const uint64_t lanes_below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  int32_t np_ = 0, nf = 0;
+  for (int32_t j0 = 0; j0 < last; j0 += 64) {
+    const int32_t j = j0 + lane;
+    bool part = false, full = false;
+    if (j < last) {
+      const int64_t k0 = int64_t{j} * bk;
+      const int64_t k1 = min(k0 + bk, a.n_pad);
+      if (k1 - 1 <= q0) {
+        const int2 x = mm[j];
+        full = x.x >= q1;
+        part = !full && x.y > q0;
+      } else {
+        const int64_t kend = min(k1, q1);
+        for (int64_t k = k0; k < kend && !part; ++k) {
+          const int64_t lo = k > q0 ? k : q0;
+          const int64_t hi = min<int64_t>(d[k], q1);
+          part = lo < hi;
+        }
+      }
+    }
+    const uint64_t bp = __ballot(part);
+    const uint64_t bf = __ballot(full);
+    if (part) p_idx[np_ + __popcll(bp & lanes_below)] = j;
+    if (full) f_idx[nf + __popcll(bf & lanes_below)] = j;
+    np_ += __popcll(bp);
+    nf += __popcll(bf);
+  }
+  if (lane == 0) {
+    a.partial_num[gw] = np_;
+    a.full_num[gw] = nf;
+  }
+}
+
+// Bits of the 128 keys [k0, k0 + 128) visible to row q: k <= q < d_k.
+__device__ __forceinline__ word4 row_bits(const int32_t* d, int64_t k0, int64_t q) {
+  word4 w = word4{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    uint32_t x = 0;
+    for (int b = 0; b < 32; ++b) {
+      const int64_t k = k0 + 32 * c + b;
+      if (k <= q && q < d[k]) x |= 1u << b;
+    }
+    w[c] = x;
+  }
+  return w;
+}
+
+// The first row after q at which one of the 128 keys [k0, k0 + 128) dies
+// while visible (a row d_k with d_k > q and d_k > k); INT64_MAX if none.
+__device__ __forceinline__ int64_t next_death(const int32_t* d, int64_t k0, int64_t q) {
+  int64_t nxt = INT64_MAX;
+  for (int b = 0; b < 128; ++b) {
+    const int64_t dk = d[k0 + b];
+    if (dk > q && dk > k0 + b) nxt = min(nxt, dk);
+  }
+  return nxt;
+}
+
+// Thread (rollout, strip of 128 keys, run of rows): a wave's 64 lanes take 64
+// consecutive strips, so each row is written as 1 KiB runs of 16-byte stores.
+// A thread computes its bits at its first row and carries them down the run:
+// on its diagonal, key q appears at row q (if d_q > q); at a row where one of
+// its keys dies it recomputes all 128 bits.  Death times take at most one
+// value per eviction event, so a run recomputes a handful of times.
+__global__ __launch_bounds__(256) void kvs_dense_kernel(KvsDenseLaunch a) {
+  const int64_t strips = a.n_pad >> 7;
+  const int64_t runs = (a.n_pad + a.rows_per_thread - 1) / a.rows_per_thread;
+  const int64_t tid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (tid >= static_cast<int64_t>(a.n) * runs * strips) return;
+  const int64_t s = tid % strips;
+  const int64_t rest = tid / strips;
+  const int64_t run = rest % runs;
+  const int64_t roll = rest / runs;
+  const int32_t* d = a.death + roll * a.n_pad;
+  const int64_t words = a.n_pad >> 5;
+  word4* out = reinterpret_cast<word4*>(a.bits + roll * a.n_pad * words) + s;
+  const int64_t pitch = words >> 2;  // word4 per row
+  const int64_t k0 = s << 7;
+  const int64_t q_begin = run * a.rows_per_thread;
+  const int64_t q_end = min(q_begin + a.rows_per_thread, a.n_pad);
+  if (q_end - 1 < k0) {  // the whole run lies above this strip's diagonal
+    for (int64_t q = q_begin; q < q_end; ++q)
+      __builtin_nontemporal_store(word4{0u, 0u, 0u, 0u}, out + q * pitch);
+    return;
+  }
+  word4 w = row_bits(d, k0, q_begin);
+  int64_t death = next_death(d, k0, q_begin);
+  __builtin_nontemporal_store(w, out + q_begin * pitch);
+  for (int64_t q = q_begin + 1; q < q_end; ++q) {
+    if (q == death) {
+      w = row_bits(d, k0, q);
+      death = next_death(d, k0, q);
+    } else if (q >= k0 && q < k0 + 128 && d[q] > q) {
+      const int b = static_cast<int>(q - k0);
+      w[b >> 5] |= 1u << (b & 31);
+    }
+    __builtin_nontemporal_store(w, out + q * pitch);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_kvs_death(const KvsDeathLaunch& a, hipStream_t s) {
+  if (a.n == 0) return hipSuccess;
+  kvs_death_kernel<<<dim3(a.n), dim3(kDeathThreads), 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_kvs_block(const KvsBlockLaunch& a, hipStream_t s) {
+  if (a.n == 0) return hipSuccess;
+  const int64_t w1 = static_cast<int64_t>(a.n) * a.nk;
+  kvs_minmax_kernel<<<dim3(static_cast<unsigned>((w1 + 3) / 4)), dim3(256), 0, s>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t w2 = static_cast<int64_t>(a.n) * a.nq;
+  kvs_block_kernel<<<dim3(static_cast<unsigned>((w2 + 3) / 4)), dim3(256), 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_kvs_dense(const KvsDenseLaunch& a, hipStream_t s) {
+  if (a.n == 0) return hipSuccess;
+  const int64_t runs = (a.n_pad + a.rows_per_thread - 1) / a.rows_per_thread;
+  const int64_t threads = static_cast<int64_t>(a.n) * runs * (a.n_pad >> 7);
+  kvs_dense_kernel<<<dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace ll

@@ -1,0 +1,263 @@
+// Host side of the KV-streams trainer-side attention mask (include/leyline.h,
+// "KV-streams trainer mask" section): argument checks, the upload of the
+// eviction logs, and the launches of kernels_kvs.hip.
+//
+// "KV-streams" ("how it works"): the trainer mirrors the engine's evictions
+// with a custom attention mask so that one forward pass over a rollout lets
+// every token see exactly the keys the cache held when it was generated.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+#include <vector>
+
+#include "../../include/leyline.h"
+#include "host_common.h"
+#include "kvs_internal.h"
+
+struct kvs_ctx {
+  int32_t device = 0;
+  char* host = nullptr;      // pinned staging for the event logs
+  char* dev = nullptr;       // its device copy
+  size_t cap = 0;
+  hipEvent_t staged = nullptr;  // the last upload's consumer has finished
+  bool staged_pending = false;
+  int2* minmax = nullptr;    // block-mask scratch
+  size_t minmax_cap = 0;     // elements
+  hipEvent_t minmax_done = nullptr;
+  bool minmax_pending = false;
+};
+
+namespace {
+
+using ll::fail;
+
+class DeviceGuard {
+ public:
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&old_) != hipSuccess) old_ = -1;
+    if (old_ != dev) ok_ = hipSetDevice(dev) == hipSuccess;
+  }
+  ~DeviceGuard() {
+    int cur = -1;
+    if (old_ >= 0 && hipGetDevice(&cur) == hipSuccess && cur != old_) (void)hipSetDevice(old_);
+  }
+  bool ok() const { return ok_; }
+
+ private:
+  int old_ = -1;
+  bool ok_ = true;
+};
+
+ll_status dev_fail(hipError_t e, const char* what) { return fail(LL_EDEVICE, "%s: %s", what, hipGetErrorString(e)); }
+
+int log2_exact(int32_t x) {
+  int s = 0;
+  while ((1 << s) < x) ++s;
+  return (1 << s) == x ? s : -1;
+}
+
+}  // namespace
+
+extern "C" {
+
+ll_status kvs_ctx_create(int32_t device, kvs_ctx** out) {
+  if (!out) return fail(LL_EINVAL, "NULL argument");
+  *out = nullptr;
+  if (device < 0) return fail(LL_EINVAL, "device must be >= 0");
+  DeviceGuard g(device);
+  if (!g.ok()) return fail(LL_EDEVICE, "hipSetDevice(%d) failed", device);
+  kvs_ctx* c = new kvs_ctx();
+  c->device = device;
+  hipError_t e = hipEventCreateWithFlags(&c->staged, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&c->minmax_done, hipEventDisableTiming);
+  if (e != hipSuccess) {
+    kvs_ctx_destroy(c);
+    return dev_fail(e, "kvs_ctx_create");
+  }
+  *out = c;
+  return LL_OK;
+}
+
+void kvs_ctx_destroy(kvs_ctx* c) {
+  if (!c) return;
+  DeviceGuard g(c->device);
+  if (c->staged_pending) (void)hipEventSynchronize(c->staged);
+  if (c->minmax_pending) (void)hipEventSynchronize(c->minmax_done);
+  if (c->staged) (void)hipEventDestroy(c->staged);
+  if (c->minmax_done) (void)hipEventDestroy(c->minmax_done);
+  if (c->host) (void)hipHostFree(c->host);
+  if (c->dev) (void)hipFree(c->dev);
+  if (c->minmax) (void)hipFree(c->minmax);
+  delete c;
+}
+
+ll_status kvs_death_times(kvs_ctx* c, const kvs_rollout_log* logs, int32_t n, int64_t n_pad, const uint8_t* keep_dev,
+                          int32_t* death_dev, int32_t* status_dev, void* stream) {
+  if (!c) return fail(LL_EINVAL, "context is NULL");
+  if (n < 0 || (n > 0 && (!logs || !death_dev || !status_dev))) return fail(LL_EINVAL, "bad arguments");
+  if (n_pad < 1 || n_pad >= (int64_t{1} << 31) - 1) return fail(LL_EINVAL, "n_pad must be in [1, 2^31 - 2]");
+  if (n == 0) return LL_OK;
+  int64_t n_events = 0;
+  bool any_mask = false;
+  for (int32_t i = 0; i < n; ++i) {
+    const kvs_rollout_log& l = logs[i];
+    if (l.n_tokens < 0 || l.n_tokens > n_pad) return fail(LL_EINVAL, "rollout %d: n_tokens outside [0, n_pad]", i);
+    if (l.n_events < 0 || (l.n_events > 0 && (!l.event_time || !l.mask_len)))
+      return fail(LL_EINVAL, "rollout %d: bad event arrays", i);
+    if (l.mask_offset < 0) return fail(LL_EINVAL, "rollout %d: negative mask_offset", i);
+    int64_t prev = 0;
+    for (int32_t e = 0; e < l.n_events; ++e) {
+      const int64_t t = l.event_time[e];
+      if (t <= prev || t > l.n_tokens)
+        return fail(LL_EINVAL, "rollout %d, event %d: times must increase inside (0, n_tokens]", i, e);
+      if (l.mask_len[e] < 0 || l.mask_len[e] > t)
+        return fail(LL_EINVAL, "rollout %d, event %d: mask_len outside [0, time]", i, e);
+      any_mask = any_mask || l.mask_len[e] > 0;
+      prev = t;
+    }
+    n_events += l.n_events;
+  }
+  if (any_mask && !keep_dev) return fail(LL_EINVAL, "keep masks are NULL");
+  if (n_events >= (int64_t{1} << 31)) return fail(LL_EUNSUPPORTED, "too many events");
+
+  DeviceGuard g(c->device);
+  if (!g.ok()) return fail(LL_EDEVICE, "hipSetDevice(%d) failed", c->device);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const size_t roll_bytes = sizeof(ll::KvsRollout) * static_cast<size_t>(n);
+  const size_t ev_off = (roll_bytes + 255) / 256 * 256;
+  const size_t need = ev_off + sizeof(ll::KvsEvent) * static_cast<size_t>(std::max<int64_t>(n_events, 1));
+  // the staging buffer is reused: wait until the previous call's kernel has read it
+  if (c->staged_pending) {
+    hipError_t e = hipEventSynchronize(c->staged);
+    if (e != hipSuccess) return dev_fail(e, "hipEventSynchronize(staging)");
+    c->staged_pending = false;
+  }
+  if (need > c->cap) {
+    if (c->host) (void)hipHostFree(c->host);
+    if (c->dev) (void)hipFree(c->dev);
+    c->host = nullptr;
+    c->dev = nullptr;
+    c->cap = 0;
+    const size_t cap = std::max<size_t>(need * 2, size_t{1} << 16);
+    if (hipHostMalloc(reinterpret_cast<void**>(&c->host), cap, hipHostMallocDefault) != hipSuccess ||
+        hipMalloc(reinterpret_cast<void**>(&c->dev), cap) != hipSuccess)
+      return fail(LL_ENOMEM, "cannot allocate %zu bytes of staging", cap);
+    c->cap = cap;
+  }
+  ll::KvsRollout* rolls = reinterpret_cast<ll::KvsRollout*>(c->host);
+  ll::KvsEvent* evs = reinterpret_cast<ll::KvsEvent*>(c->host + ev_off);
+  int64_t at = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const kvs_rollout_log& l = logs[i];
+    rolls[i].n_tokens = l.n_tokens;
+    rolls[i].first_event = static_cast<int32_t>(at);
+    rolls[i].n_events = l.n_events;
+    int64_t off = l.mask_offset;
+    for (int32_t e = 0; e < l.n_events; ++e) {
+      ll::KvsEvent& ev = evs[at++];
+      ev.time = l.event_time[e];
+      ev.mask_len = l.mask_len[e];
+      ev.mask_off = off;
+      ev.pad = 0;
+      off += l.mask_len[e];
+    }
+  }
+  hipError_t e = hipMemcpyAsync(c->dev, c->host, need, hipMemcpyHostToDevice, st);
+  if (e != hipSuccess) return dev_fail(e, "hipMemcpyAsync(event log)");
+  ll::KvsDeathLaunch a{};
+  a.rollouts = reinterpret_cast<const ll::KvsRollout*>(c->dev);
+  a.events = reinterpret_cast<const ll::KvsEvent*>(c->dev + ev_off);
+  a.keep = keep_dev;
+  a.death = death_dev;
+  a.status = status_dev;
+  a.n_pad = n_pad;
+  a.n = n;
+  e = ll::launch_kvs_death(a, st);
+  if (e != hipSuccess) return dev_fail(e, "kvs_death_kernel launch");
+  e = hipEventRecord(c->staged, st);
+  if (e != hipSuccess) return dev_fail(e, "hipEventRecord");
+  c->staged_pending = true;
+  return LL_OK;
+}
+
+ll_status kvs_block_mask(kvs_ctx* c, const int32_t* death_dev, int32_t n, int64_t n_pad, int32_t block_q,
+                         int32_t block_k, int32_t* partial_num, int32_t* partial_idx, int32_t* full_num,
+                         int32_t* full_idx, void* stream) {
+  if (!c) return fail(LL_EINVAL, "context is NULL");
+  if (n < 0 || (n > 0 && (!death_dev || !partial_num || !partial_idx || !full_num || !full_idx)))
+    return fail(LL_EINVAL, "bad arguments");
+  if (n_pad < 1 || n_pad >= (int64_t{1} << 31) - 1) return fail(LL_EINVAL, "n_pad must be in [1, 2^31 - 2]");
+  const int bq = log2_exact(block_q), bk = log2_exact(block_k);
+  if (bq < 4 || bq > 10 || bk < 4 || bk > 10)
+    return fail(LL_EINVAL, "block_q and block_k must be powers of two in [16, 1024]");
+  if (n == 0) return LL_OK;
+  const int64_t nq = (n_pad + block_q - 1) / block_q;
+  const int64_t nk = (n_pad + block_k - 1) / block_k;
+  const size_t mm = static_cast<size_t>(n) * static_cast<size_t>(nk);
+  DeviceGuard g(c->device);
+  if (!g.ok()) return fail(LL_EDEVICE, "hipSetDevice(%d) failed", c->device);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (mm > c->minmax_cap) {
+    if (c->minmax_pending) {
+      hipError_t e = hipEventSynchronize(c->minmax_done);
+      if (e != hipSuccess) return dev_fail(e, "hipEventSynchronize(scratch)");
+      c->minmax_pending = false;
+    }
+    if (c->minmax) (void)hipFree(c->minmax);
+    c->minmax = nullptr;
+    c->minmax_cap = 0;
+    if (hipMalloc(reinterpret_cast<void**>(&c->minmax), mm * 2 * sizeof(int2)) != hipSuccess)
+      return fail(LL_ENOMEM, "cannot allocate block-mask scratch");
+    c->minmax_cap = mm * 2;
+  } else if (c->minmax_pending) {
+    // the scratch is reused: order this call after the last one that used it
+    hipError_t e = hipStreamWaitEvent(st, c->minmax_done, 0);
+    if (e != hipSuccess) return dev_fail(e, "hipStreamWaitEvent(scratch)");
+  }
+  ll::KvsBlockLaunch a{};
+  a.death = death_dev;
+  a.minmax = c->minmax;
+  a.partial_num = partial_num;
+  a.partial_idx = partial_idx;
+  a.full_num = full_num;
+  a.full_idx = full_idx;
+  a.n_pad = n_pad;
+  a.n = n;
+  a.bq_shift = bq;
+  a.bk_shift = bk;
+  a.nq = static_cast<int32_t>(nq);
+  a.nk = static_cast<int32_t>(nk);
+  hipError_t e = ll::launch_kvs_block(a, st);
+  if (e != hipSuccess) return dev_fail(e, "kvs_block_kernel launch");
+  e = hipEventRecord(c->minmax_done, st);
+  if (e != hipSuccess) return dev_fail(e, "hipEventRecord");
+  c->minmax_pending = true;
+  return LL_OK;
+}
+
+ll_status kvs_dense_mask(kvs_ctx* c, const int32_t* death_dev, int32_t n, int64_t n_pad, uint32_t* bits_dev,
+                         void* stream) {
+  if (!c) return fail(LL_EINVAL, "context is NULL");
+  if (n < 0 || (n > 0 && (!death_dev || !bits_dev))) return fail(LL_EINVAL, "bad arguments");
+  if (n_pad < 128 || n_pad % 128 || n_pad >= (int64_t{1} << 31) - 1)
+    return fail(LL_EINVAL, "n_pad must be a positive multiple of 128 below 2^31");
+  if (reinterpret_cast<uintptr_t>(bits_dev) & 15) return fail(LL_EINVAL, "bits_dev is not 16-byte aligned");
+  if (n == 0) return LL_OK;
+  DeviceGuard g(c->device);
+  if (!g.ok()) return fail(LL_EDEVICE, "hipSetDevice(%d) failed", c->device);
+  ll::KvsDenseLaunch a{};
+  a.death = death_dev;
+  a.bits = bits_dev;
+  a.n_pad = n_pad;
+  a.n = n;
+  a.rows_per_thread = 512;
+  const int64_t runs = (n_pad + a.rows_per_thread - 1) / a.rows_per_thread;
+  if (static_cast<int64_t>(n) * runs * (n_pad / 128) / 256 >= (int64_t{1} << 31))
+    return fail(LL_EUNSUPPORTED, "dense mask too large for one launch");
+  hipError_t e = ll::launch_kvs_dense(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return dev_fail(e, "kvs_dense_kernel launch");
+  return LL_OK;
+}
+
+}  // extern "C"

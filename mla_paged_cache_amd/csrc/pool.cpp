@@ -21,11 +21,14 @@
 #include <vector>
 
 #include "../../include/leyline.h"
+#include "host_common.h"
 #include "leyline_internal.h"
 
-namespace {
+namespace ll {
 
+namespace {
 thread_local std::string g_error;
+}  // namespace
 
 ll_status fail(ll_status s, const char* fmt, ...) {
   char buf[512];
@@ -36,6 +39,14 @@ ll_status fail(ll_status s, const char* fmt, ...) {
   g_error = buf;
   return s;
 }
+
+const char* last_error() { return g_error.c_str(); }
+
+}  // namespace ll
+
+namespace {
+
+using ll::fail;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -514,7 +525,7 @@ ll_status validate_directives(const ll_pool* p, const ll_directive* dirs, int32_
 
 extern "C" {
 
-const char* ll_last_error(void) { return g_error.c_str(); }
+const char* ll_last_error(void) { return ll::last_error(); }
 
 const char* ll_status_str(ll_status s) {
   switch (s) {

@@ -29,6 +29,7 @@ EXPORTS = (
     "ll_seq_get", "ll_pool_free_pages", "leyline_splice", "kv_evict_compact", "ll_ptable_reindex",
     "ll_rope_delta_table", "ll_last_plan_stats", "ll_pool_set_profiling", "ll_profile_read",
     "ll_last_error", "ll_status_str", "ll_pool_create_gqa",
+    "kvs_ctx_create", "kvs_ctx_destroy", "kvs_death_times", "kvs_block_mask", "kvs_dense_mask",
 )
 
 
@@ -88,6 +89,16 @@ class _Directive(ctypes.Structure):
     ]
 
 
+class _KvsRolloutLog(ctypes.Structure):
+    _fields_ = [
+        ("n_tokens", ctypes.c_int64),
+        ("n_events", ctypes.c_int32),
+        ("event_time", ctypes.POINTER(ctypes.c_int64)),
+        ("mask_len", ctypes.POINTER(ctypes.c_int64)),
+        ("mask_offset", ctypes.c_int64),
+    ]
+
+
 class _PlanStats(ctypes.Structure):
     _fields_ = [
         ("alg_bytes", ctypes.c_int64),
@@ -121,6 +132,11 @@ def _load():
         "ll_last_plan_stats": (i32, [vp, P(_PlanStats)]),
         "ll_pool_set_profiling": (i32, [vp, i32]),
         "ll_profile_read": (i32, [vp, i32, P(i64), P(ctypes.c_double), P(i64)]),
+        "kvs_ctx_create": (i32, [i32, P(vp)]),
+        "kvs_ctx_destroy": (None, [vp]),
+        "kvs_death_times": (i32, [vp, P(_KvsRolloutLog), i32, i64, vp, vp, vp, vp]),
+        "kvs_block_mask": (i32, [vp, vp, i32, i64, i32, i32, vp, vp, vp, vp, vp]),
+        "kvs_dense_mask": (i32, [vp, vp, i32, i64, vp, vp]),
         "ll_last_error": (ctypes.c_char_p, []),
         "ll_status_str": (ctypes.c_char_p, [i32]),
     }
@@ -394,3 +410,77 @@ class GqaPool(Pool):
             raise ValueError("stub rows must be [num_layers][r_len][H][D] with contiguous rows")
         r_len = st.shape[1]
         return r_len, (st.data_ptr() if r_len else None), st.stride(0) * 2
+
+
+class KvsMask:
+    """KV-streams trainer-side attention mask on one device: death times from
+    the engine's eviction logs, then a block mask or a dense bit mask.
+
+    A log is a list of (time, keep) events per rollout, keep being the mask the
+    engine passed to its eviction call (uint8 over the rows held then)."""
+
+    def __init__(self, device: int = 0):
+        h = ctypes.c_void_p()
+        _check(_lib.kvs_ctx_create(int(device), ctypes.byref(h)))
+        self._h = h
+        self.device = device
+
+    def close(self):
+        if getattr(self, "_h", None):
+            _lib.kvs_ctx_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def death_times(self, rollouts, n_pad: int, stream=None):
+        """rollouts: list of (n_tokens, events), events a list of objects with
+        .time and .keep (host uint8 arrays).  Returns (death int32 [n][n_pad],
+        status int32 [n]) CUDA tensors; the keep masks are uploaded as one
+        buffer."""
+        import torch
+        n = len(rollouts)
+        dev = torch.device("cuda", self.device)
+        chunks, logs, keep_alive = [], (_KvsRolloutLog * max(1, n))(), []
+        off = 0
+        for i, (n_tokens, events) in enumerate(rollouts):
+            times = np.ascontiguousarray([int(e.time) for e in events], dtype=np.int64)
+            lens = np.ascontiguousarray([len(e.keep) for e in events], dtype=np.int64)
+            keep_alive += [times, lens]
+            logs[i] = _KvsRolloutLog(int(n_tokens), len(events),
+                                     times.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                     lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), off)
+            for e in events:
+                chunks.append(np.asarray(e.keep, dtype=np.uint8))
+                off += len(e.keep)
+        keep = torch.from_numpy(np.concatenate(chunks) if chunks else np.zeros(1, np.uint8)).to(dev)
+        death = torch.empty((n, n_pad), dtype=torch.int32, device=dev)
+        status = torch.empty(n, dtype=torch.int32, device=dev)
+        _check(_lib.kvs_death_times(self._h, logs, n, int(n_pad), keep.data_ptr(), death.data_ptr(),
+                                    status.data_ptr(), _stream_handle(stream)))
+        self._keep = keep  # alive until the next call (the kernel reads it)
+        return death, status
+
+    def block_mask(self, death, block_q: int, block_k: int, stream=None):
+        """(partial_num [n][nq], partial_idx [n][nq][nk], full_num, full_idx)."""
+        import torch
+        n, n_pad = death.shape
+        nq, nk = -(-n_pad // block_q), -(-n_pad // block_k)
+        kw = dict(dtype=torch.int32, device=death.device)
+        pn, fn = torch.zeros((n, nq), **kw), torch.zeros((n, nq), **kw)
+        pi, fi = torch.full((n, nq, nk), -1, **kw), torch.full((n, nq, nk), -1, **kw)
+        _check(_lib.kvs_block_mask(self._h, death.data_ptr(), n, n_pad, int(block_q), int(block_k), pn.data_ptr(),
+                                   pi.data_ptr(), fn.data_ptr(), fi.data_ptr(), _stream_handle(stream)))
+        return pn, pi, fn, fi
+
+    def dense_mask(self, death, out=None, stream=None):
+        """uint32 bits [n][n_pad][n_pad / 32] (as an int32 tensor)."""
+        import torch
+        n, n_pad = death.shape
+        if out is None:
+            out = torch.empty((n, n_pad, n_pad // 32), dtype=torch.int32, device=death.device)
+        _check(_lib.kvs_dense_mask(self._h, death.data_ptr(), n, n_pad, out.data_ptr(), _stream_handle(stream)))
+        return out

@@ -88,6 +88,25 @@ def visibility(death: np.ndarray) -> np.ndarray:
     return (k <= q) & (q < np.asarray(death)[None, :])
 
 
+def visibility_rows(death: np.ndarray, rows) -> np.ndarray:
+    """Rows `rows` of the mask of the definition (for masks too large to
+    build whole)."""
+    d = np.asarray(death)
+    q = np.asarray(rows)[:, None]
+    k = np.arange(len(d))[None, :]
+    return (k <= q) & (q < d[None, :])
+
+
+def tile_class(death: np.ndarray, q0: int, q1: int, k0: int, k1: int) -> str:
+    """'full', 'partial' or 'empty' for the tile [q0, q1) x [k0, k1) of the
+    mask of the definition."""
+    d = np.asarray(death)[k0:k1]
+    q = np.arange(q0, q1)[:, None]
+    k = np.arange(k0, k1)[None, :]
+    tile = (k <= q) & (q < d[None, :])
+    return "full" if tile.all() else ("partial" if tile.any() else "empty")
+
+
 def block_mask(vis: np.ndarray, block_q: int, block_k: int):
     """Tile classification of a dense mask.  Returns (partial, full): for each
     query block, the list of key blocks whose tile is partial, and the list of

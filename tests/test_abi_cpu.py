@@ -34,7 +34,7 @@ def test_header_declares_the_path_entry_points():
     names = _declared()
     for n in ("leyline_splice", "kv_evict_compact", "ll_ptable_reindex", "ll_pool_create"):
         assert n in names
-    assert len(names) == 17
+    assert len(names) == 22
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -104,6 +104,32 @@ def test_gqa_pool_create_rejects_bad_descriptors_before_touching_a_device():
     misaligned = (ctypes.c_void_p * 2)(48, 72)
     d = L._GqaPoolDesc(**{**base, "v_layer_base": ctypes.cast(misaligned, ctypes.POINTER(ctypes.c_void_p))})
     assert L._lib.ll_pool_create_gqa(ctypes.byref(d), ctypes.byref(ctypes.c_void_p())) == L.LL_EINVAL
+
+
+def test_trainer_mask_calls_reject_bad_arguments_before_touching_a_device():
+    """Argument checks run before the context is used (a dummy context is
+    enough) and before any device call."""
+    from mla_paged_cache_amd import leyline as L
+    fake = ctypes.create_string_buffer(512)
+    ctx = ctypes.cast(fake, ctypes.c_void_p)
+    vp = ctypes.c_void_p
+    times = (ctypes.c_int64 * 2)(10, 10)
+    lens = (ctypes.c_int64 * 2)(10, 10)
+    log = L._KvsRolloutLog(20, 2, times, lens, 0)
+    assert L._lib.kvs_death_times(None, ctypes.byref(log), 1, 32, vp(64), vp(64), vp(64), None) == L.LL_EINVAL
+    # event times must strictly increase
+    assert L._lib.kvs_death_times(ctx, ctypes.byref(log), 1, 32, vp(64), vp(64), vp(64), None) == L.LL_EINVAL
+    times[1] = 15
+    lens[1] = 16     # more rows than tokens generated
+    assert L._lib.kvs_death_times(ctx, ctypes.byref(log), 1, 32, vp(64), vp(64), vp(64), None) == L.LL_EINVAL
+    lens[1] = 12
+    assert L._lib.kvs_death_times(ctx, ctypes.byref(log), 1, 16, vp(64), vp(64), vp(64), None) == L.LL_EINVAL
+    times[1] = 21    # beyond n_tokens
+    assert L._lib.kvs_death_times(ctx, ctypes.byref(log), 1, 32, vp(64), vp(64), vp(64), None) == L.LL_EINVAL
+    for bq, bk in ((12, 16), (16, 2048), (8, 16)):
+        assert L._lib.kvs_block_mask(ctx, vp(64), 1, 256, bq, bk, vp(64), vp(64), vp(64), vp(64), None) == L.LL_EINVAL
+    assert L._lib.kvs_dense_mask(ctx, vp(64), 1, 200, vp(64), None) == L.LL_EINVAL   # not a multiple of 128
+    assert L._lib.kvs_dense_mask(ctx, vp(64), 1, 256, vp(72), None) == L.LL_EINVAL   # misaligned
 
 
 def test_null_pool_calls_fail_cleanly():

@@ -1,0 +1,190 @@
+"""GPU parity of the KV-streams trainer-side mask ("KV-streams", onedev.kr
+summary, "how it works") against the CPU oracle, through the C ABI: death
+times, block-mask lists and dense bit masks are integer results and must be
+bit-exact.  A last test drives the engine's own eviction (kv_evict_compact on
+a pool whose rows carry token ids) through the same log and checks that after
+every event the cache holds exactly the tokens the death times keep alive."""
+
+import numpy as np
+import pytest
+
+from oracle import kvs_mask_oracle as K
+from synth import EvictionEvent, compaction_log, np_rng, permuted_pages
+
+from gpu_common import need_gpu, say, torch
+
+pytestmark = pytest.mark.gpu
+
+
+def _logs(seed, lengths, strategies, budget, turn_lo, turn_hi, every):
+    out = []
+    for i, (n, st) in enumerate(zip(lengths, strategies)):
+        out.append((n, compaction_log(np_rng(seed, i), n, st, budget, turn_lo, turn_hi, every)))
+    return out
+
+
+def _check_blocks(ctx, death, d_host, bq, bk, full_check=True, sample=None):
+    pn, pi, fn, fi = ctx.block_mask(death, bq, bk)
+    torch.cuda.synchronize()
+    pn, pi, fn, fi = (x.cpu().numpy() for x in (pn, pi, fn, fi))
+    n, n_pad = d_host.shape
+    nq, nk = -(-n_pad // bq), -(-n_pad // bk)
+    for r in range(n):
+        if full_check:
+            partial, full = K.block_mask(K.visibility(d_host[r]), bq, bk)
+            for i in range(nq):
+                assert list(pi[r, i, :pn[r, i]]) == partial[i], (r, i)
+                assert list(fi[r, i, :fn[r, i]]) == full[i], (r, i)
+        else:
+            for i in sample:
+                q0, q1 = i * bq, min(i * bq + bq, n_pad)
+                part = [j for j in range(nk) if K.tile_class(d_host[r], q0, q1, j * bk, min(j * bk + bk, n_pad)) == "partial"]
+                full = [j for j in range(nk) if K.tile_class(d_host[r], q0, q1, j * bk, min(j * bk + bk, n_pad)) == "full"]
+                assert list(pi[r, i, :pn[r, i]]) == part, (r, i)
+                assert list(fi[r, i, :fn[r, i]]) == full, (r, i)
+
+
+def test_small_batches_all_outputs():
+    L = need_gpu()
+    ctx = L.KvsMask(0)
+    cases = [
+        (256, [256, 200, 131, 1], ["window", "half", "pick", "pick"]),
+        (384, [384, 383, 250], ["pick", "window", "half"]),
+        (1024, [1000, 1024], ["half", "pick"]),
+    ]
+    for seed, (n_pad, lengths, strategies) in enumerate(cases):
+        say(f"kvs small n_pad={n_pad} lengths={lengths}")
+        rolls = _logs(seed, lengths, strategies, budget=120, turn_lo=4, turn_hi=40, every=3)
+        death, status = ctx.death_times(rolls, n_pad)
+        torch.cuda.synchronize()
+        assert not status.cpu().numpy().any()
+        d_host = np.stack([K.death_times(n_pad, n, ev) for n, ev in rolls])
+        assert np.array_equal(death.cpu().numpy().astype(np.int64), d_host)
+        for bq, bk in ((16, 16), (32, 64), (64, 16), (128, 128)):
+            _check_blocks(ctx, death, d_host, bq, bk)
+        bits = ctx.dense_mask(death)
+        torch.cuda.synchronize()
+        got = bits.cpu().numpy().view(np.uint32)
+        for r in range(len(rolls)):
+            assert np.array_equal(got[r], K.dense_bits(K.visibility(d_host[r]))), r
+    ctx.close()
+
+
+def test_edge_logs():
+    """No events (causal), an event dropping everything, an event at the very
+    end, an empty rollout, and all-padding."""
+    L = need_gpu()
+    ctx = L.KvsMask(0)
+    n_pad = 256
+    rolls = [
+        (256, []),
+        (200, [EvictionEvent(100, np.zeros(100, np.uint8))]),
+        (256, [EvictionEvent(256, np.r_[np.ones(128, np.uint8), np.zeros(128, np.uint8)])]),
+        (0, []),
+        (130, [EvictionEvent(1, np.zeros(1, np.uint8)), EvictionEvent(2, np.ones(1, np.uint8))]),
+    ]
+    death, status = ctx.death_times(rolls, n_pad)
+    torch.cuda.synchronize()
+    assert not status.cpu().numpy().any()
+    d_host = np.stack([K.death_times(n_pad, n, ev) for n, ev in rolls])
+    assert np.array_equal(death.cpu().numpy().astype(np.int64), d_host)
+    _check_blocks(ctx, death, d_host, 32, 32)
+    bits = ctx.dense_mask(death)
+    torch.cuda.synchronize()
+    got = bits.cpu().numpy().view(np.uint32)
+    for r in range(len(rolls)):
+        assert np.array_equal(got[r], K.dense_bits(K.visibility(d_host[r])))
+    ctx.close()
+
+
+def test_mismatched_mask_sets_status_of_that_rollout_only():
+    L = need_gpu()
+    ctx = L.KvsMask(0)
+    good = compaction_log(np_rng(5, 0), 300, "pick", 100, 4, 30, 3)
+    bad = [EvictionEvent(good[0].time, good[0].keep)] + \
+          [EvictionEvent(good[1].time, np.ones(len(good[1].keep) + 1, np.uint8))]
+    death, status = ctx.death_times([(300, good), (300, bad), (300, good)], 384)
+    torch.cuda.synchronize()
+    assert list(status.cpu().numpy()) == [0, 1, 0]
+    d = death.cpu().numpy().astype(np.int64)
+    ref = K.death_times(384, 300, good)
+    assert np.array_equal(d[0], ref) and np.array_equal(d[2], ref)
+    ctx.close()
+
+
+@pytest.mark.slow
+def test_textworld_shaped_batch_32k():
+    """Eight 32768-token rollouts (turns U[64, 512], compaction every 10 turns,
+    budget 8192, the three strategies): death times bit-exact; block lists of
+    sampled query blocks (128 x 128 tiles); dense bit rows sampled."""
+    L = need_gpu()
+    ctx = L.KvsMask(0)
+    n_pad = 32768
+    strategies = ["window", "half", "pick"] * 3
+    rolls = _logs(77, [32768] * 8, strategies[:8], budget=8192, turn_lo=64, turn_hi=512, every=10)
+    say(f"kvs 8 x 32k, events per rollout {[len(ev) for _, ev in rolls]}")
+    death, status = ctx.death_times(rolls, n_pad)
+    torch.cuda.synchronize()
+    assert not status.cpu().numpy().any()
+    d_host = np.stack([K.death_times(n_pad, n, ev) for n, ev in rolls])
+    assert np.array_equal(death.cpu().numpy().astype(np.int64), d_host)
+    _check_blocks(ctx, death, d_host, 128, 128, full_check=False, sample=[0, 1, 63, 100, 200, 255])
+    bits = ctx.dense_mask(death)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 127, 128, 5000, 12345, 20000, 32767])
+    for r in (0, 3, 7):
+        got = bits[r, torch.from_numpy(rows).cuda()].cpu().numpy().view(np.uint32)
+        assert np.array_equal(got, K.dense_bits(K.visibility_rows(d_host[r], rows))), r
+    ctx.close()
+
+
+def test_engine_eviction_agrees_with_death_times():
+    """A one-layer MLA pool (page size 16) whose rows carry their token id in
+    the first two bf16 slots; tokens are appended event by event and each
+    event's keep mask goes to kv_evict_compact.  After each event the pool's
+    rows are exactly the tokens k < t with d_k > t."""
+    L = need_gpu()
+    P, n_tok = 16, 4000
+    log = compaction_log(np_rng(9, 0), n_tok, "pick", 1500, 32, 256, 4)
+    ctx = L.KvsMask(0)
+    death, status = ctx.death_times([(n_tok, log)], 4096)
+    torch.cuda.synchronize()
+    assert status.item() == 0
+    d = death[0].cpu().numpy().astype(np.int64)
+    pages = 2 * n_tok // P
+    ids = np.zeros((1, pages, P, 576), np.uint16)
+    data = torch.from_numpy(ids.view(np.int16)).view(torch.bfloat16).cuda()
+    table = torch.full((1, pages), -1, dtype=torch.int32, device="cuda")
+    pool = L.Pool(data, table)
+    held, t_prev = [], 0
+    perm = list(permuted_pages(9, pages))
+    for e in log:
+        # append tokens t_prev .. e.time - 1: write their ids into the next rows
+        n_before = len(held)
+        _, _, tab = pool.seq_get(0) if n_before or t_prev else (0, 0, np.zeros(0, np.int32))
+        tab = list(tab)
+        new = list(range(t_prev, e.time))
+        need = -(-(n_before + len(new)) // P)
+        free = [p for p in perm if p not in set(tab)]   # one sequence: every other page is free
+        tab += free[:need - len(tab)]
+        flat = data.view(torch.int16).view(-1, 576)
+        j = np.arange(n_before, n_before + len(new))
+        rows = torch.from_numpy(np.asarray(tab, np.int64)[j // P] * P + j % P).cuda()
+        vals = torch.from_numpy(np.asarray(new, np.int64))
+        flat[rows, 0] = (vals & 0x7FFF).to(torch.int16).cuda()
+        flat[rows, 1] = (vals >> 15).to(torch.int16).cuda()
+        pool.seq_set_pages(0, tab, n_before + len(new))
+        held = held + new
+        assert len(e.keep) == len(held)
+        pool.evict([0], torch.from_numpy(e.keep).cuda(), [0])
+        torch.cuda.synchronize()
+        n, _, tab = pool.seq_get(0)
+        j = np.arange(n)
+        rows = torch.from_numpy(tab.astype(np.int64)[j // P] * P + j % P).cuda()
+        got = flat[rows, :2].cpu().numpy().astype(np.int64)
+        alive = got[:, 0] + (got[:, 1] << 15)
+        assert np.array_equal(alive, np.flatnonzero(d[:e.time] > e.time)), e.time
+        held = list(alive)
+        t_prev = e.time
+    pool.close()
+    ctx.close()

@@ -162,3 +162,17 @@ def test_pins_catch_an_off_by_one_event_time(monkeypatch):
     monkeypatch.setattr(K, "death_times", planted)
     with pytest.raises(AssertionError):
         test_death_times_match_the_replay("pick")
+
+
+def test_row_and_tile_restrictions_agree_with_the_whole_mask():
+    n = 300
+    log = compaction_log(np_rng(8, 1), n, "half", budget=90, turn_lo=5, turn_hi=30, every_turns=2)
+    d = K.death_times(320, n, log)
+    v = K.visibility(d)
+    rows = [0, 17, 150, 299, 319]
+    assert np.array_equal(K.visibility_rows(d, rows), v[rows])
+    partial, full = K.block_mask(v, 32, 64)
+    for i in range(10):
+        for j in range(5):
+            c = K.tile_class(d, 32 * i, min(32 * i + 32, 320), 64 * j, min(64 * j + 64, 320))
+            assert c == ("full" if j in full[i] else "partial" if j in partial[i] else "empty")
