@@ -24,6 +24,10 @@ Other workloads (one JSON line each, not the headline):
   --workload evict_256x16k_27layer_p16 / _p1
                                      KV-streams eviction of 256 rollouts x
                                      16384 tokens under random turn drops
+  --workload kvs_mask_64x32k         KV-streams trainer mask for 64 rollouts x
+                                     32768 tokens: death times from the
+                                     eviction logs, 128 x 128 block mask and the
+                                     dense bit mask (8.6 GB written)
   --workload splice_32k_llama8b      the headline splice on a GQA cache of
                                      Llama-3-8B shape (32 layers, K and V of 8
                                      heads x 128, RoPE on all 128, half-split,
@@ -64,20 +68,23 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--workload", default="splice_32k_27layer",
                     choices=["splice_32k_27layer", "splice_16x32k_27layer", "evict_256x16k_27layer_p16",
-                             "evict_256x16k_27layer_p1", "splice_32k_llama8b"])
+                             "evict_256x16k_27layer_p1", "splice_32k_llama8b", "kvs_mask_64x32k"])
     return ap.parse_args()
 
 
 # The source file of each measured kernel; its hash also covers the shared
 # device helpers and the launch structures.
 KERNEL_SOURCE = {"splice_kernel": "kernels.hip", "evict_move_kernel": "kernels.hip",
-                 "gqa_splice_kernel": "kernels_gqa.hip", "plane_evict_kernel": "kernels_gqa.hip"}
+                 "gqa_splice_kernel": "kernels_gqa.hip", "plane_evict_kernel": "kernels_gqa.hip",
+                 "kvs_dense_kernel": "kernels_kvs.hip"}
 
 
 def kernel_source_sha(kernel: str) -> str:
     csrc = os.path.join(ROOT, "mla_paged_cache_amd", "csrc")
+    src = KERNEL_SOURCE[kernel]
+    headers = ("kvs_internal.h",) if src == "kernels_kvs.hip" else ("device_common.h", "leyline_internal.h")
     h = hashlib.sha256()
-    for name in ("device_common.h", "leyline_internal.h", KERNEL_SOURCE[kernel]):
+    for name in (*headers, src):
         h.update(open(os.path.join(csrc, name), "rb").read())
     return h.hexdigest()[:16]
 
@@ -393,6 +400,75 @@ def bench_splice_gqa(args):
     return out
 
 
+# --------------------------------------------------------- trainer mask --
+
+def bench_kvs_mask(args):
+    """KV-streams trainer-side mask for a batch of 64 rollouts of 32768 tokens
+    (turns U[64, 512], compaction after every 10 turns, budget 8192 tokens,
+    strategies window / half / pick in turn).  A step is one death-time call
+    (log upload + replay), one 128 x 128 block mask and one dense bit mask."""
+    import torch
+    from mla_paged_cache_amd import leyline as L
+    from synth import compaction_log, np_rng
+
+    ROLL, TOKENS = 64, 32768
+    strategies = ("window", "half", "pick")
+    rolls = [(TOKENS, compaction_log(np_rng(0, 10 + i), TOKENS, strategies[i % 3], 8192, 64, 512, 10))
+             for i in range(ROLL)]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ctx = L.KvsMask(0)
+    death, status = ctx.death_times(rolls, TOKENS)
+    bits = ctx.dense_mask(death)
+    blocks = ctx.block_mask(death, 128, 128)
+    torch.cuda.synchronize()
+    if status.any().item():
+        raise SystemExit("a synthetic eviction log did not match its own cache")
+    dense_bytes = bits.numel() * 4
+    ev = {k: [] for k in ("death", "block", "dense")}
+
+    def step(record):
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if record else None
+        if record:
+            marks[0].record()
+        ctx.death_times(rolls, TOKENS)
+        if record:
+            marks[1].record()
+        ctx.block_mask(death, 128, 128)
+        if record:
+            marks[2].record()
+        ctx.dense_mask(death, out=bits)
+        if record:
+            marks[3].record()
+            for key, a, b in (("death", 0, 1), ("block", 1, 2), ("dense", 2, 3)):
+                ev[key].append((marks[a], marks[b]))
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    quiet_gc()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    gc.enable()
+    ms = {k: statistics.mean(a.elapsed_time(b) for a, b in v) for k, v in ev.items()}
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    out = base_line(args, "kvs_mask_64x32k", dense_bytes / (ms_per_step * 1e-3) / 1e9, ms_per_step, {
+        "rollouts": ROLL, "tokens": TOKENS, "events_per_rollout": round(statistics.mean(len(r[1]) for r in rolls), 1),
+        "turns": "U[64,512], compaction every 10 turns, budget 8192", "block": [128, 128],
+        "dense_bytes": dense_bytes, "step": "death times + block mask + dense mask"})
+    out["metric"] = "KV-streams trainer mask: dense mask bytes written GB/s per step"
+    out["dtype"] = "int32"
+    out["roofline"] = roofline("kvs_dense_kernel", "kvs_mask_64x32k", args.steps, ms["dense"] * args.steps,
+                               dense_bytes * args.steps)
+    out["kernel_ms"] = {k: round(v, 4) for k, v in ms.items()}
+    out["cpu_baseline"] = None
+    ctx.close()
+    return out
+
+
 # ------------------------------------------------------------------- evict --
 
 def bench_evict(args, page):
@@ -481,6 +557,8 @@ def main():
         out = bench_splice_batched(args)
     elif args.workload == "splice_32k_llama8b":
         out = bench_splice_gqa(args)
+    elif args.workload == "kvs_mask_64x32k":
+        out = bench_kvs_mask(args)
     else:
         out = bench_evict(args, 16 if args.workload.endswith("p16") else 1)
     print(json.dumps(out), flush=True)

@@ -12,10 +12,10 @@
 //  * kvs_minmax_kernel / kvs_block_kernel: per key block the smallest and
 //    largest death time, then per query block the sorted lists of partial and
 //    full key blocks (FlexAttention-style block mask).
-//  * kvs_dense_kernel: the packed bit mask, one 16-byte store per thread and
-//    row; a thread carries its 128 keys' bits down the rows, adds keys as the
-//    rows reach them and looks at all 128 death times again only at rows where
-//    one of them dies.
+//  * kvs_dense_kernel: the packed bit mask, one 16-byte store per lane and
+//    row; a wave carries its 64 x 128 keys' bits down a run of rows, adds keys
+//    as the rows reach them and rebuilds the bits (coalesced loads, ballots)
+//    only at rows where one of its keys dies.
 #include "kvs_internal.h"
 
 namespace ll {
@@ -171,71 +171,97 @@ __global__ __launch_bounds__(256) void kvs_block_kernel(KvsBlockLaunch a) {
   }
 }
 
-// Bits of the 128 keys [k0, k0 + 128) visible to row q: k <= q < d_k.
-__device__ __forceinline__ word4 row_bits(const int32_t* d, int64_t k0, int64_t q) {
-  word4 w = word4{0u, 0u, 0u, 0u};
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    uint32_t x = 0;
-    for (int b = 0; b < 32; ++b) {
-      const int64_t k = k0 + 32 * c + b;
-      if (k <= q && q < d[k]) x |= 1u << b;
+// The wave's 64 strips of 128 keys are the 8192 consecutive keys
+// [wk0, wk0 + 8192).  Recompute every lane's 128 bits for row q, reading the
+// death times with coalesced loads (lane = key) and packing them with ballots:
+// iteration it covers keys wk0 + 64 it .. + 63, i.e. words 2 (it & 1) and
+// 2 (it & 1) + 1 of the strip it / 2, staged through the wave's 1 KiB of LDS.
+// Also returns the wave's next death row (the least d_k > q over its keys
+// that are visible at some row, d_k > k; INT32_MAX if none) and, in *real,
+// the lane's keys that are visible at some row, so that keys reached by the
+// diagonal later can be added without another load.
+__device__ __forceinline__ word4 wave_bits(const int32_t* d, int64_t n_pad, int64_t wk0, int64_t q,
+                                           uint64_t* lds, int lane, int32_t* next, word4* real) {
+  int32_t nd = INT32_MAX;
+  for (int it = 0; it < 128; ++it) {
+    const int64_t k = wk0 + 64 * it + lane;
+    bool vis = false, ever = false;
+    if (k < n_pad) {
+      const int32_t x = d[k];
+      vis = k <= q && q < x;
+      ever = x > k;
+      if (x > q && ever) nd = min(nd, x);
     }
-    w[c] = x;
+    const uint64_t bv = __ballot(vis);
+    const uint64_t be = __ballot(ever);
+    if (lane == 0) {
+      lds[it] = bv;
+      lds[128 + it] = be;
+    }
   }
-  return w;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) nd = min(nd, __shfl_xor(nd, o));
+  *next = nd;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const uint64_t lo = lds[2 * lane], hi = lds[2 * lane + 1];
+  const uint64_t elo = lds[128 + 2 * lane], ehi = lds[128 + 2 * lane + 1];
+  __builtin_amdgcn_wave_barrier();  // the next recompute overwrites lds only after every lane has read it
+  *real = word4{static_cast<uint32_t>(elo), static_cast<uint32_t>(elo >> 32), static_cast<uint32_t>(ehi),
+                static_cast<uint32_t>(ehi >> 32)};
+  return word4{static_cast<uint32_t>(lo), static_cast<uint32_t>(lo >> 32), static_cast<uint32_t>(hi),
+               static_cast<uint32_t>(hi >> 32)};
 }
 
-// The first row after q at which one of the 128 keys [k0, k0 + 128) dies
-// while visible (a row d_k with d_k > q and d_k > k); INT64_MAX if none.
-__device__ __forceinline__ int64_t next_death(const int32_t* d, int64_t k0, int64_t q) {
-  int64_t nxt = INT64_MAX;
-  for (int b = 0; b < 128; ++b) {
-    const int64_t dk = d[k0 + b];
-    if (dk > q && dk > k0 + b) nxt = min(nxt, dk);
-  }
-  return nxt;
-}
-
-// Thread (rollout, strip of 128 keys, run of rows): a wave's 64 lanes take 64
-// consecutive strips, so each row is written as 1 KiB runs of 16-byte stores.
-// A thread computes its bits at its first row and carries them down the run:
-// on its diagonal, key q appears at row q (if d_q > q); at a row where one of
-// its keys dies it recomputes all 128 bits.  Death times take at most one
-// value per eviction event, so a run recomputes a handful of times.
+// One wave per (rollout, run of rows, 64 consecutive strips of 128 keys);
+// lane s writes strip s, so each row is written as 1 KiB runs of 16-byte
+// stores.  The wave computes its bits at its first row and carries them down
+// the run: on its diagonal, key q appears at row q (if d_q > q); at a row
+// where one of its keys dies (death times take at most one value per eviction
+// event) it recomputes them with wave_bits.  The row loop itself loads
+// nothing, so its stores never wait behind a load.
 __global__ __launch_bounds__(256) void kvs_dense_kernel(KvsDenseLaunch a) {
+  __shared__ uint64_t stage[4][256];
+  const int lane = threadIdx.x & 63;
   const int64_t strips = a.n_pad >> 7;
+  const int64_t groups = (strips + 63) >> 6;
   const int64_t runs = (a.n_pad + a.rows_per_thread - 1) / a.rows_per_thread;
-  const int64_t tid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (tid >= static_cast<int64_t>(a.n) * runs * strips) return;
-  const int64_t s = tid % strips;
-  const int64_t rest = tid / strips;
+  const int64_t gw = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) >> 6;
+  if (gw >= static_cast<int64_t>(a.n) * runs * groups) return;
+  const int64_t grp = gw % groups;
+  const int64_t rest = gw / groups;
   const int64_t run = rest % runs;
   const int64_t roll = rest / runs;
   const int32_t* d = a.death + roll * a.n_pad;
+  const int64_t s = grp * 64 + lane;
+  const bool active = s < strips;
   const int64_t words = a.n_pad >> 5;
   word4* out = reinterpret_cast<word4*>(a.bits + roll * a.n_pad * words) + s;
   const int64_t pitch = words >> 2;  // word4 per row
-  const int64_t k0 = s << 7;
+  const int64_t wk0 = grp << 13;     // first key of the wave
+  const int64_t k0 = s << 7;         // first key of the lane's strip
   const int64_t q_begin = run * a.rows_per_thread;
   const int64_t q_end = min(q_begin + a.rows_per_thread, a.n_pad);
-  if (q_end - 1 < k0) {  // the whole run lies above this strip's diagonal
-    for (int64_t q = q_begin; q < q_end; ++q)
-      __builtin_nontemporal_store(word4{0u, 0u, 0u, 0u}, out + q * pitch);
+  if (q_end - 1 < wk0) {  // the whole run lies above the wave's diagonal
+    if (active)
+      for (int64_t q = q_begin; q < q_end; ++q)
+        __builtin_nontemporal_store(word4{0u, 0u, 0u, 0u}, out + q * pitch);
     return;
   }
-  word4 w = row_bits(d, k0, q_begin);
-  int64_t death = next_death(d, k0, q_begin);
-  __builtin_nontemporal_store(w, out + q_begin * pitch);
+  uint64_t* lds = stage[threadIdx.x >> 6];
+  int32_t death;
+  word4 real;
+  word4 w = wave_bits(d, a.n_pad, wk0, q_begin, lds, lane, &death, &real);
+  if (active) __builtin_nontemporal_store(w, out + q_begin * pitch);
   for (int64_t q = q_begin + 1; q < q_end; ++q) {
-    if (q == death) {
-      w = row_bits(d, k0, q);
-      death = next_death(d, k0, q);
-    } else if (q >= k0 && q < k0 + 128 && d[q] > q) {
+    if (q == death) {  // wave-uniform
+      w = wave_bits(d, a.n_pad, wk0, q, lds, lane, &death, &real);
+    } else if (q >= k0 && q < k0 + 128) {  // key q appears (if it is ever visible): no load needed
       const int b = static_cast<int>(q - k0);
-      w[b >> 5] |= 1u << (b & 31);
+      w[b >> 5] |= real[b >> 5] & (1u << (b & 31));
     }
-    __builtin_nontemporal_store(w, out + q * pitch);
+    if (active) __builtin_nontemporal_store(w, out + q * pitch);
   }
 }
 
@@ -261,8 +287,9 @@ hipError_t launch_kvs_block(const KvsBlockLaunch& a, hipStream_t s) {
 hipError_t launch_kvs_dense(const KvsDenseLaunch& a, hipStream_t s) {
   if (a.n == 0) return hipSuccess;
   const int64_t runs = (a.n_pad + a.rows_per_thread - 1) / a.rows_per_thread;
-  const int64_t threads = static_cast<int64_t>(a.n) * runs * (a.n_pad >> 7);
-  kvs_dense_kernel<<<dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0, s>>>(a);
+  const int64_t groups = ((a.n_pad >> 7) + 63) >> 6;
+  const int64_t waves = static_cast<int64_t>(a.n) * runs * groups;
+  kvs_dense_kernel<<<dim3(static_cast<unsigned>((waves + 3) / 4)), dim3(256), 0, s>>>(a);
   return hipGetLastError();
 }
 

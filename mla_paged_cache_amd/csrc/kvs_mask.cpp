@@ -251,9 +251,10 @@ ll_status kvs_dense_mask(kvs_ctx* c, const int32_t* death_dev, int32_t n, int64_
   a.bits = bits_dev;
   a.n_pad = n_pad;
   a.n = n;
-  a.rows_per_thread = 512;
+  a.rows_per_thread = 128;
   const int64_t runs = (n_pad + a.rows_per_thread - 1) / a.rows_per_thread;
-  if (static_cast<int64_t>(n) * runs * (n_pad / 128) / 256 >= (int64_t{1} << 31))
+  const int64_t groups = (n_pad / 128 + 63) / 64;  // waves per run of rows
+  if (static_cast<int64_t>(n) * runs * groups / 4 >= (int64_t{1} << 31))
     return fail(LL_EUNSUPPORTED, "dense mask too large for one launch");
   hipError_t e = ll::launch_kvs_dense(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return dev_fail(e, "kvs_dense_kernel launch");
