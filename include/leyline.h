@@ -296,9 +296,10 @@ ll_status kvs_ctx_create(int32_t device, kvs_ctx** out);
 void kvs_ctx_destroy(kvs_ctx* ctx);
 
 /* Death times of n rollouts: death_dev is int32 [n][n_pad] (rollout i at
- * i * n_pad), status_dev int32 [n].  The logs are replayed on the device: at
- * each event a block prefix scan numbers the tokens still held, and the i-th
- * of them dies at the event's time when keep byte i is 0.  status_dev[i] is
+ * i * n_pad), status_dev int32 [n].  The logs are replayed on the device:
+ * the rows held at an event are the tokens held after the previous event
+ * followed by the tokens generated since, and the token of row i dies at the
+ * event's time when keep byte i is 0.  status_dev[i] is
  * 0, or 1 when some event's mask_len differs from the number of rows the
  * cache held at that time (the rollout's death times are then unspecified).
  * The host arrays are read before the call returns; the call first waits

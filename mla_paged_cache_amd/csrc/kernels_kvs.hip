@@ -6,9 +6,10 @@
 // Token k's death time d_k is the time of the eviction event that dropped it
 // (n_pad if none, k for padding keys); query q sees key k iff k <= q < d_k.
 //
-//  * kvs_death_kernel: replays a rollout's eviction log -- per event, a block
-//    prefix scan over the tokens still held gives each its row index in the
-//    event's keep mask; dropped tokens get the event's time.
+//  * kvs_death_kernel: replays a rollout's eviction log -- per event, the rows
+//    held are the block's list of held tokens plus the tokens generated since;
+//    a block prefix scan over the keep mask compacts the list in place and
+//    dropped tokens get the event's time.
 //  * kvs_minmax_kernel / kvs_block_kernel: per key block the smallest and
 //    largest death time, then per query block the sorted lists of partial and
 //    full key blocks (FlexAttention-style block mask).
@@ -27,38 +28,51 @@ constexpr int kDeathThreads = 1024;
 constexpr int kDeathWaves = kDeathThreads / 64;
 constexpr int kPerThread = 16;  // tokens per thread per tile
 
-// One block per rollout.  d is initialised to n_pad (held) for real tokens and
-// to k (never visible) for padding keys.  Per event at time t: the tokens
-// k < t still held (d_k == n_pad) are numbered in order by a block-wide
-// exclusive scan (wave64 ballot bit-planes, then the 16 wave totals through
-// LDS); the i-th held token is dropped, d_k = t, when keep[i] == 0.  A mask
-// whose length differs from the number of held rows sets the status word.
+// One block per rollout.  d is initialised to n_pad (never dropped) for real
+// tokens and to k (never visible) for padding keys.  The block keeps the list
+// of token ids the cache holds, in order, in its scratch row; at an event at
+// time t the rows held are that list followed by the tokens generated since
+// the previous event, and row i is token list'[i].  Per tile of 16 rows per
+// thread, a block-wide exclusive scan of the kept counts (wave64 ballot
+// bit-planes, then the 16 wave totals through LDS) compacts the kept tokens in
+// place -- every write lands at or before the tile being read, and the tile's
+// reads finish before the scan's barrier -- and dropped tokens get d_k = t.
+// A mask whose length differs from the number of rows held sets the status.
 __global__ __launch_bounds__(kDeathThreads) void kvs_death_kernel(KvsDeathLaunch a) {
   __shared__ int32_t wave_total[kDeathWaves];
   const KvsRollout r = a.rollouts[blockIdx.x];
   const int64_t n_pad = a.n_pad;
-  const int32_t held = static_cast<int32_t>(n_pad);
   int32_t* d = a.death + static_cast<int64_t>(blockIdx.x) * n_pad;
+  int32_t* list = a.list + static_cast<int64_t>(blockIdx.x) * n_pad;
   for (int64_t k = threadIdx.x; k < n_pad; k += kDeathThreads)
-    d[k] = k < r.n_tokens ? held : static_cast<int32_t>(k);
+    d[k] = k < r.n_tokens ? static_cast<int32_t>(n_pad) : static_cast<int32_t>(k);
   __syncthreads();
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const uint64_t lanes_below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
   bool bad = false;
+  int64_t held = 0;    // entries of `list`
+  int64_t t_prev = 0;  // tokens generated at the previous event
   for (int e = 0; e < r.n_events; ++e) {
     const KvsEvent ev = a.events[r.first_event + e];
     const int64_t t = ev.time;
+    const int64_t rows = held + (t - t_prev);
+    bad = bad || rows != ev.mask_len;
+    const int64_t len = rows < ev.mask_len ? rows : ev.mask_len;
     const uint8_t* m = a.keep + ev.mask_off;
     int64_t carry = 0;
-    for (int64_t base = 0; base < t; base += int64_t{kPerThread} * kDeathThreads) {
-      const int64_t k0 = base + int64_t{kPerThread} * threadIdx.x;
-      uint32_t bits = 0;
+    for (int64_t base = 0; base < len; base += int64_t{kPerThread} * kDeathThreads) {
+      const int64_t i0 = base + int64_t{kPerThread} * threadIdx.x;
+      int32_t tok[kPerThread];
+      uint32_t kept = 0;
 #pragma unroll
-      for (int c = 0; c < kPerThread; ++c)
-        if (k0 + c < t && d[k0 + c] == held) bits |= 1u << c;
-      const int cnt = __popc(bits);
+      for (int c = 0; c < kPerThread; ++c) {
+        const int64_t i = i0 + c;
+        tok[c] = i < held ? list[i] : static_cast<int32_t>(t_prev + (i - held));
+        if (i < len && m[i] != 0) kept |= 1u << c;
+      }
+      const int cnt = __popc(kept);
       int below = 0, total = 0;
 #pragma unroll
       for (int bit = 0; bit < 5; ++bit) {
@@ -75,18 +89,18 @@ __global__ __launch_bounds__(kDeathThreads) void kvs_death_kernel(KvsDeathLaunch
         wave_below += w < wave ? x : 0;
         block_total += x;
       }
-      int64_t i = carry + wave_below + below;
-      for (int c = 0; c < kPerThread; ++c)
-        if ((bits >> c) & 1u) {
-          if (i < ev.mask_len) {
-            if (m[i] == 0) d[k0 + c] = static_cast<int32_t>(t);
-          }
-          ++i;
-        }
+      int64_t pos = carry + wave_below + below;
+#pragma unroll
+      for (int c = 0; c < kPerThread; ++c) {
+        if (i0 + c >= len) break;
+        if ((kept >> c) & 1u) list[pos++] = tok[c];
+        else d[tok[c]] = static_cast<int32_t>(t);
+      }
       carry += block_total;
       __syncthreads();
     }
-    bad = bad || carry != ev.mask_len;
+    held = carry;
+    t_prev = t;
   }
   if (threadIdx.x == 0) a.status[blockIdx.x] = bad ? 1 : 0;
 }

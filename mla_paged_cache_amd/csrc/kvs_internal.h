@@ -29,6 +29,7 @@ struct KvsDeathLaunch {
   const uint8_t* keep;
   int32_t* death;        // [n][n_pad]
   int32_t* status;       // [n]
+  int32_t* list;         // scratch [n][n_pad]: token ids the cache holds
   int64_t n_pad;
   int32_t n;
 };

@@ -22,6 +22,8 @@ struct kvs_ctx {
   size_t cap = 0;
   hipEvent_t staged = nullptr;  // the last upload's consumer has finished
   bool staged_pending = false;
+  int32_t* list = nullptr;   // death-time scratch: held token ids per rollout
+  size_t list_cap = 0;       // elements
   int2* minmax = nullptr;    // block-mask scratch
   size_t minmax_cap = 0;     // elements
   hipEvent_t minmax_done = nullptr;
@@ -89,6 +91,7 @@ void kvs_ctx_destroy(kvs_ctx* c) {
   if (c->host) (void)hipHostFree(c->host);
   if (c->dev) (void)hipFree(c->dev);
   if (c->minmax) (void)hipFree(c->minmax);
+  if (c->list) (void)hipFree(c->list);
   delete c;
 }
 
@@ -133,6 +136,15 @@ ll_status kvs_death_times(kvs_ctx* c, const kvs_rollout_log* logs, int32_t n, in
     if (e != hipSuccess) return dev_fail(e, "hipEventSynchronize(staging)");
     c->staged_pending = false;
   }
+  const size_t list_need = static_cast<size_t>(n) * static_cast<size_t>(n_pad);
+  if (list_need > c->list_cap) {  // the previous call has finished: its scratch is free
+    if (c->list) (void)hipFree(c->list);
+    c->list = nullptr;
+    c->list_cap = 0;
+    if (hipMalloc(reinterpret_cast<void**>(&c->list), list_need * sizeof(int32_t)) != hipSuccess)
+      return fail(LL_ENOMEM, "cannot allocate %zu bytes of death-time scratch", list_need * sizeof(int32_t));
+    c->list_cap = list_need;
+  }
   if (need > c->cap) {
     if (c->host) (void)hipHostFree(c->host);
     if (c->dev) (void)hipFree(c->dev);
@@ -171,6 +183,7 @@ ll_status kvs_death_times(kvs_ctx* c, const kvs_rollout_log* logs, int32_t n, in
   a.keep = keep_dev;
   a.death = death_dev;
   a.status = status_dev;
+  a.list = c->list;
   a.n_pad = n_pad;
   a.n = n;
   e = ll::launch_kvs_death(a, st);

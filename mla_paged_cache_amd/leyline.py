@@ -412,6 +412,14 @@ class GqaPool(Pool):
         return r_len, (st.data_ptr() if r_len else None), st.stride(0) * 2
 
 
+@dataclass
+class _Logs:
+    n: int
+    logs: object
+    host: list
+    keep: object
+
+
 class KvsMask:
     """KV-streams trainer-side attention mask on one device: death times from
     the engine's eviction logs, then a block mask or a dense bit mask.
@@ -436,32 +444,42 @@ class KvsMask:
         except Exception:
             pass
 
-    def death_times(self, rollouts, n_pad: int, stream=None):
-        """rollouts: list of (n_tokens, events), events a list of objects with
-        .time and .keep (host uint8 arrays).  Returns (death int32 [n][n_pad],
-        status int32 [n]) CUDA tensors; the keep masks are uploaded as one
-        buffer."""
+    def upload_logs(self, rollouts):
+        """Marshal eviction logs once: rollouts is a list of (n_tokens,
+        events), events a list of objects with .time and .keep (host uint8
+        arrays).  The keep masks go to the device as one buffer."""
         import torch
         n = len(rollouts)
-        dev = torch.device("cuda", self.device)
-        chunks, logs, keep_alive = [], (_KvsRolloutLog * max(1, n))(), []
+        chunks, logs, host = [], (_KvsRolloutLog * max(1, n))(), []
         off = 0
         for i, (n_tokens, events) in enumerate(rollouts):
             times = np.ascontiguousarray([int(e.time) for e in events], dtype=np.int64)
             lens = np.ascontiguousarray([len(e.keep) for e in events], dtype=np.int64)
-            keep_alive += [times, lens]
+            host += [times, lens]
             logs[i] = _KvsRolloutLog(int(n_tokens), len(events),
                                      times.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
                                      lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), off)
             for e in events:
                 chunks.append(np.asarray(e.keep, dtype=np.uint8))
                 off += len(e.keep)
-        keep = torch.from_numpy(np.concatenate(chunks) if chunks else np.zeros(1, np.uint8)).to(dev)
-        death = torch.empty((n, n_pad), dtype=torch.int32, device=dev)
-        status = torch.empty(n, dtype=torch.int32, device=dev)
-        _check(_lib.kvs_death_times(self._h, logs, n, int(n_pad), keep.data_ptr(), death.data_ptr(),
+        keep = torch.from_numpy(np.concatenate(chunks) if chunks else np.zeros(1, np.uint8)).to(
+            torch.device("cuda", self.device))
+        return _Logs(n, logs, host, keep)
+
+    def death_times(self, rollouts, n_pad: int, stream=None, out=None):
+        """Death times of the rollouts (a list as for upload_logs, or its
+        result).  Returns (death int32 [n][n_pad], status int32 [n]) CUDA
+        tensors."""
+        import torch
+        logs = rollouts if isinstance(rollouts, _Logs) else self.upload_logs(rollouts)
+        dev = torch.device("cuda", self.device)
+        if out is None:
+            out = (torch.empty((logs.n, n_pad), dtype=torch.int32, device=dev),
+                   torch.empty(logs.n, dtype=torch.int32, device=dev))
+        death, status = out
+        _check(_lib.kvs_death_times(self._h, logs.logs, logs.n, int(n_pad), logs.keep.data_ptr(), death.data_ptr(),
                                     status.data_ptr(), _stream_handle(stream)))
-        self._keep = keep  # alive until the next call (the kernel reads it)
+        self._last_logs = logs  # the kernel reads the keep buffer after this returns
         return death, status
 
     def block_mask(self, death, block_q: int, block_k: int, stream=None):
