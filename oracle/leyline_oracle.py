@@ -212,6 +212,34 @@ def rotate_f64(k: np.ndarray, angle_steps, rope_dim: int = ROPE_DIM,
     return out
 
 
+def row_cos_sin(angles, rope_dim: int = ROPE_DIM, base: float = 10000.0):
+    """Per-row tables for rows turned by their own angle steps a_i: the float64
+    angle a_i * theta_j, its float64 cos and sin (libm through `math`), each
+    rounded to float32.  Returns (cos, sin), float32 [n, rope_dim/2]."""
+    th = rope_theta(rope_dim, base)
+    a = [float(x) for x in np.asarray(angles, dtype=np.int64)]
+    c = np.array([[math.cos(x * t) for t in th] for x in a], dtype=np.float64).reshape(len(a), len(th))
+    s = np.array([[math.sin(x * t) for t in th] for x in a], dtype=np.float64).reshape(len(a), len(th))
+    return c.astype(np.float32), s.astype(np.float32)
+
+
+def rotate_rows_bf16(bits: np.ndarray, angles, rope_dim: int = ROPE_DIM, base: float = 10000.0,
+                     pairing: str = "interleaved") -> np.ndarray:
+    """Row i of `bits` (uint16 [n, rope_dim]) turned by R(angles[i]): the same
+    float32 arithmetic as rotate_kpe_bf16, with the row's own cos/sin."""
+    bits = np.asarray(bits, dtype=np.uint16)
+    ix, iy = pair_index(rope_dim, pairing)
+    c, s = row_cos_sin(angles, rope_dim, base)
+    x = bf16_to_f32(bits[:, ix])
+    y = bf16_to_f32(bits[:, iy])
+    x_new = np.subtract(np.multiply(x, c, dtype=np.float32), np.multiply(y, s, dtype=np.float32), dtype=np.float32)
+    y_new = np.add(np.multiply(x, s, dtype=np.float32), np.multiply(y, c, dtype=np.float32), dtype=np.float32)
+    out = np.empty_like(bits)
+    out[:, ix] = f32_to_bf16(x_new)
+    out[:, iy] = f32_to_bf16(y_new)
+    return out
+
+
 # ---------------------------------------------------------------------------
 # Paged cache state
 # ---------------------------------------------------------------------------
@@ -497,6 +525,45 @@ def ptable_reindex(state: CacheState, seq: int, keep_pages):
     new.lengths[seq] = sum(live)
     new.free |= {old_t[k] for k in range(n_pages) if k not in set(keep)}
     return new
+
+
+def rope_rows(state: CacheState, seq: int, row_begin: int, angles, pairing: str = "interleaved",
+              base: float = 10000.0, in_place: bool = False):
+    """Per-row RoPE rotation of the sequence's logical rows
+    [row_begin, row_begin + len(angles)): row row_begin + i has every RoPE band
+    turned by R(angles[i]) (an angle of -position turns a stored key back to
+    its position-free form, as VECTOR does before its K -> V map; "VECTOR",
+    gist.science summary, method, reconstructability through OLS).
+
+    Only layer arrays that carry bands take part.  in_place=False: returns the
+    list, one per such array, of the turned rows (uint16 [n, width]), the
+    state untouched.  in_place=True: returns a new state whose rows have their
+    bands turned there (the other values and arrays unchanged)."""
+    angles = np.asarray(angles, dtype=np.int64)
+    n = len(angles)
+    if seq not in state.tables:
+        raise InvalidRequest("unknown sequence")
+    if row_begin < 0 or row_begin + n > state.lengths[seq]:
+        raise InvalidRequest("rows outside the sequence")
+    P = state.page_size
+    t = np.asarray(state.tables[seq], dtype=np.int64)
+    j = np.arange(row_begin, row_begin + n)
+    phys = t[j // P] * P + j % P if n else np.zeros(0, np.int64)
+    new = state.copy() if in_place else None
+    outs = []
+    for L in range(len(state.layers)):
+        spec = state.spec(L)
+        if not spec.bands:
+            continue
+        rows = state.layers[L].reshape(-1, spec.width)[phys].copy()
+        for off, dim in spec.bands:
+            rows[:, off:off + dim] = rotate_rows_bf16(rows[:, off:off + dim], angles, rope_dim=dim,
+                                                      base=base, pairing=pairing)
+        if in_place:
+            new.layers[L].reshape(-1, spec.width)[phys] = rows
+        else:
+            outs.append(rows)
+    return new if in_place else outs
 
 
 def algorithmic_bytes(plan, n_new, P, kind, downstream, delta, num_layers, rotate=True, specs=None):
