@@ -242,6 +242,28 @@ ll_status kv_evict_compact(ll_pool* pool, const int32_t* seq_ids, int32_t n,
 ll_status ll_ptable_reindex(ll_pool* pool, int32_t seq_id, const int32_t* keep_pages,
                             int32_t n_keep, void* stream);
 
+/* Per-row-angle RoPE rotation of the rows [row_begin, row_begin + n_rows) of a
+ * sequence: row row_begin + i has every RoPE band (MLA: k_pe; GQA / MHA: the
+ * rotary part of each K head) turned by R(a_i), a_i = angle_dev[i] (device
+ * int64 [n_rows]).  An angle of minus the row's position turns a stored key
+ * back to its position-free form -- the step VECTOR takes before its static
+ * K -> V reconstruction ("VECTOR", gist.science summary of paper 2605.23258,
+ * method: reconstructability through OLS).  Per row and pair the float64
+ * angle a_i * theta_j and its float64 cos and sin (argument reduction on the
+ * device) are rounded to float32; the pair then turns with the float32
+ * arithmetic of leyline_splice.
+ *
+ * out_dev == NULL: in place, only the bands are written.  Otherwise the rows
+ * are gathered, bands turned, into out_dev (device, 16-byte aligned):
+ * [num_layers][n_rows][row] bf16 (MLA rows of 576; GQA: the K rows, H x D),
+ * layers out_layer_stride_bytes apart (0: n_rows * row bytes); the pool is
+ * not written.  V planes never take part.  Errors: LL_EINVAL (unknown
+ * sequence, rows outside it, NULL angles, misaligned output or stride),
+ * LL_EUNSUPPORTED, LL_ENOMEM, LL_EDEVICE. */
+ll_status ll_rope_rows(ll_pool* pool, int32_t seq_id, int64_t row_begin, int64_t n_rows,
+                       const int64_t* angle_dev, void* out_dev, int64_t out_layer_stride_bytes,
+                       void* stream);
+
 /* The float32 cos/sin table of the delta-rotation ([Leyline] section 2.2):
  * for j < rope_dim/2, the float64 angle delta * base^(-2j/rope_dim), its
  * float64 cos and sin, each rounded to float32.  cos_out and sin_out are host
@@ -253,7 +275,8 @@ ll_status ll_rope_delta_table(double base, int32_t rope_dim, int64_t delta,
 ll_status ll_last_plan_stats(const ll_pool* pool, ll_plan_stats* out);
 
 /* Kernel timing: while enabled, HIP events bracket every launch of the
- * row-moving kernel (kernel 0) and of the keep-mask scan (kernel 1).
+ * row-moving kernel (kernel 0), of the keep-mask scan (kernel 1) and of the
+ * per-row rotation (kernel 2: its table and row kernels together).
  * ll_profile_read waits for the recorded events, returns the launch count,
  * the summed milliseconds and the summed algorithmic bytes of `kernel`, and
  * clears its record.  Errors: LL_EINVAL, LL_EDEVICE. */

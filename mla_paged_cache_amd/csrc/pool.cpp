@@ -23,6 +23,7 @@
 #include "../../include/leyline.h"
 #include "host_common.h"
 #include "leyline_internal.h"
+#include "rows_internal.h"
 
 namespace ll {
 
@@ -174,6 +175,8 @@ struct ll_pool {
   Staging cur;                          // region of the call in progress
   hipEvent_t upload_ev = nullptr;
   // eviction scratch: device [counts | reuse | src_of_dst], pinned readback
+  float* d_rowtab = nullptr;    // per-row cos/sin tables of ll_rope_rows
+  size_t rowtab_cap = 0;        // floats
   char* d_scratch = nullptr;
   size_t scratch_cap = 0;
   char* h_readback = nullptr;
@@ -185,7 +188,7 @@ struct ll_pool {
   bool poisoned = false;
   ll_plan_stats last{};
   bool profiling = false;
-  std::vector<ProfRec> prof[2];
+  std::vector<ProfRec> prof[3];  // row-moving kernel, keep scan, per-row rotation
   std::vector<hipEvent_t> spare_events;
   std::vector<int32_t> page_slot;  // per physical page: scratch marks of ll_seq_set_pages
 };
@@ -697,6 +700,7 @@ void ll_pool_destroy(ll_pool* p) {
   }
   if (p->h_readback) (void)hipHostFree(p->h_readback);
   if (p->d_scratch) (void)hipFree(p->d_scratch);
+  if (p->d_rowtab) (void)hipFree(p->d_rowtab);
   if (p->d_layers) (void)hipFree(p->d_layers);
   delete p;
 }
@@ -1285,6 +1289,109 @@ ll_status ll_ptable_reindex(ll_pool* p, int32_t seq, const int32_t* keep_pages, 
   return LL_OK;
 }
 
+ll_status ll_rope_rows(ll_pool* p, int32_t seq, int64_t row_begin, int64_t n_rows, const int64_t* angle_dev,
+                       void* out_dev, int64_t out_layer_stride_bytes, void* stream) {
+  ll_status rc = check_pool(p);
+  if (rc) return rc;
+  if (seq < 0 || seq >= p->desc.max_seqs || !p->seqs[seq].used) return fail(LL_EINVAL, "unknown sequence %d", seq);
+  const SeqState& s = p->seqs[seq];
+  if (row_begin < 0 || n_rows < 0 || row_begin + n_rows > s.len)
+    return fail(LL_EINVAL, "rows [%lld, %lld) outside the sequence's %lld rows", (long long)row_begin,
+                (long long)(row_begin + n_rows), (long long)s.len);
+  if (n_rows > 0 && !angle_dev) return fail(LL_EINVAL, "angle_dev is NULL");
+  const int64_t L = p->desc.num_layers;
+  if (out_dev) {
+    if (reinterpret_cast<uintptr_t>(out_dev) & 15) return fail(LL_EINVAL, "out_dev is not 16-byte aligned");
+    if (out_layer_stride_bytes < 0 || (out_layer_stride_bytes & 15) ||
+        (out_layer_stride_bytes && L > 1 && out_layer_stride_bytes < n_rows * p->row_bytes))
+      return fail(LL_EINVAL, "bad out_layer_stride_bytes");
+  }
+  ll::RowShape sh{};
+  if (p->gqa) {
+    sh.row_chunks = static_cast<int32_t>(p->row_bytes / 16);
+    sh.heads = p->heads;
+    sh.head_chunks = p->head_chunks;
+    sh.band_off = 0;
+    sh.band_shift = p->rot_shift;
+  } else {
+    sh.row_chunks = ll::kRowChunks;
+    sh.heads = 1;
+    sh.head_chunks = ll::kRowChunks;
+    sh.band_off = ll::kKpeChunk0;
+    sh.band_shift = 3;
+  }
+  sh.pairs = 4 << sh.band_shift;
+  const int64_t per_row = out_dev ? sh.row_chunks / 2 : static_cast<int64_t>(sh.heads) << (sh.band_shift - 1);
+  if (n_rows * per_row >= (int64_t{1} << 32) || n_rows >= (int64_t{1} << 31))
+    return fail(LL_EUNSUPPORTED, "too many rows for one call");
+  if (n_rows == 0) return LL_OK;
+
+  DeviceGuard g(p->desc.device);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if ((rc = begin_call(p, st))) return rc;
+  const size_t tab_floats = static_cast<size_t>(n_rows) * 2 * sh.pairs;
+  if (tab_floats > p->rowtab_cap) {
+    if (p->last_done) {
+      hipError_t e = hipEventSynchronize(p->last_done);
+      if (e != hipSuccess) return device_fail(p, e, "hipEventSynchronize");
+    }
+    if (p->d_rowtab) (void)hipFree(p->d_rowtab);
+    p->d_rowtab = nullptr;
+    p->rowtab_cap = 0;
+    if (hipMalloc(reinterpret_cast<void**>(&p->d_rowtab), tab_floats * sizeof(float)) != hipSuccess)
+      return fail(LL_ENOMEM, "cannot allocate %zu bytes of rotation tables", tab_floats * sizeof(float));
+    p->rowtab_cap = tab_floats;
+  }
+  const int64_t P = p->P;
+  const int64_t first_page = row_begin / P;
+  const int64_t last_page = (row_begin + n_rows - 1) / P;
+  const int64_t n_pages = last_page - first_page + 1;
+  Staging* sg = nullptr;
+  if ((rc = stage_acquire(p, stage_bytes_for({sizeof(double) * sh.pairs, sizeof(int32_t) * n_pages}), &sg))) return rc;
+  const size_t o_th = stage_put(sg, nullptr, sizeof(double) * sh.pairs);
+  const size_t o_pg = stage_put(sg, s.pages.data() + first_page, sizeof(int32_t) * n_pages);
+  double* theta = reinterpret_cast<double*>(sg->host + o_th);
+  const int rope_dim = 2 * sh.pairs;
+  for (int j = 0; j < sh.pairs; ++j) theta[j] = std::pow(p->desc.rope_base, -2.0 * j / rope_dim);
+  if ((rc = upload(p, sg, st))) return rc;
+
+  ll::RopeTableLaunch t{};
+  t.angle = angle_dev;
+  t.theta = reinterpret_cast<const double*>(sg->dev + o_th);
+  t.tab = p->d_rowtab;
+  t.n = n_rows;
+  t.pairs = sh.pairs;
+  ll::RopeRowsLaunch a{};
+  a.planes = reinterpret_cast<const ll::chunk_t* const*>(p->d_layers);
+  a.num_planes = static_cast<int32_t>(L);  // MLA layers, or the K planes of a GQA pool
+  a.page_shift = p->page_shift;
+  a.shape = sh;
+  a.pages = reinterpret_cast<const int32_t*>(sg->dev + o_pg);
+  a.row_begin = row_begin;
+  a.first_page = first_page;
+  a.n = n_rows;
+  a.tab = p->d_rowtab;
+  a.out = static_cast<ll::chunk_t*>(out_dev);
+  a.out_plane_chunks = (out_layer_stride_bytes ? out_layer_stride_bytes : n_rows * p->row_bytes) / 16;
+  a.blocks_per_plane = ll::flat_blocks(n_rows * per_row);
+  ProfRec rec{};
+  if (p->profiling && (rc = prof_begin(p, 2, st, &rec))) return rc;
+  hipError_t e = ll::launch_rope_table(t, st);
+  if (e != hipSuccess) return device_fail(p, e, "rope_table_kernel launch");
+  e = ll::launch_rope_rows(a, p->desc.rope_pairing, st);
+  if (e != hipSuccess) return device_fail(p, e, "rope_rows_kernel launch");
+  ll_plan_stats stats{};
+  stats.alg_bytes = out_dev ? L * n_rows * 2 * p->row_bytes : L * n_rows * 2 * p->band_bytes;
+  stats.rows_rotated_inplace = out_dev ? 0 : n_rows;
+  if (p->profiling) {
+    rec.bytes = stats.alg_bytes;
+    if ((rc = prof_end(p, 2, st, &rec))) return rc;
+  }
+  if ((rc = end_call(p, sg, st))) return rc;
+  p->last = stats;
+  return LL_OK;
+}
+
 ll_status ll_last_plan_stats(const ll_pool* p, ll_plan_stats* out) {
   if (!p || !out) return fail(LL_EINVAL, "NULL argument");
   *out = p->last;
@@ -1298,7 +1405,7 @@ ll_status ll_pool_set_profiling(ll_pool* p, int32_t enable) {
 }
 
 ll_status ll_profile_read(ll_pool* p, int32_t kernel, int64_t* launches, double* total_ms, int64_t* total_bytes) {
-  if (!p || kernel < 0 || kernel > 1) return fail(LL_EINVAL, "bad argument");
+  if (!p || kernel < 0 || kernel > 2) return fail(LL_EINVAL, "bad argument");
   DeviceGuard g(p->desc.device);
   int64_t cnt = 0, bytes = 0;
   double ms = 0.0;

@@ -30,6 +30,7 @@ EXPORTS = (
     "ll_rope_delta_table", "ll_last_plan_stats", "ll_pool_set_profiling", "ll_profile_read",
     "ll_last_error", "ll_status_str", "ll_pool_create_gqa",
     "kvs_ctx_create", "kvs_ctx_destroy", "kvs_death_times", "kvs_block_mask", "kvs_dense_mask",
+    "ll_rope_rows",
 )
 
 
@@ -132,6 +133,7 @@ def _load():
         "ll_last_plan_stats": (i32, [vp, P(_PlanStats)]),
         "ll_pool_set_profiling": (i32, [vp, i32]),
         "ll_profile_read": (i32, [vp, i32, P(i64), P(ctypes.c_double), P(i64)]),
+        "ll_rope_rows": (i32, [vp, i32, i64, i64, vp, vp, i64, vp]),
         "kvs_ctx_create": (i32, [i32, P(vp)]),
         "kvs_ctx_destroy": (None, [vp]),
         "kvs_death_times": (i32, [vp, P(_KvsRolloutLog), i32, i64, vp, vp, vp, vp]),
@@ -330,6 +332,28 @@ class Pool:
                                      o_arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
                                      _stream_handle(stream)))
 
+    def rope_rows(self, seq: int, row_begin: int, angles, out=None, stream=None):
+        """Turn the RoPE bands of rows [row_begin, row_begin + len(angles)) of
+        a sequence by their own angle steps (angles: int64 CUDA tensor).  With
+        out=None the pool is rotated in place; with out=True (or a tensor) the
+        rows are gathered into [L][n][row] bf16 and returned, the pool left
+        as it was."""
+        import torch
+        if angles.dtype != torch.int64 or not angles.is_cuda or not angles.is_contiguous():
+            raise ValueError("angles must be a contiguous int64 CUDA tensor")
+        n = angles.numel()
+        ptr, stride = None, 0
+        if out is not None:
+            if out is True:
+                shape = (self.num_layers, n, self.heads, self.head_dim) if self.gqa else (self.num_layers, n, ROW)
+                out = torch.empty(shape, dtype=torch.bfloat16, device=angles.device)
+            if out.dtype != torch.bfloat16 or not out.is_cuda or out.shape[0] != self.num_layers:
+                raise ValueError("out must be a bf16 CUDA tensor [num_layers][n][row]")
+            ptr, stride = out.data_ptr(), out.stride(0) * 2
+        _check(_lib.ll_rope_rows(self._h, int(seq), int(row_begin), int(n), angles.data_ptr() if n else None,
+                                 ptr, stride, _stream_handle(stream)))
+        return out
+
     def ptable_reindex(self, seq: int, keep_pages, stream=None) -> None:
         arr, ptr = _i32_array(keep_pages)
         _check(_lib.ll_ptable_reindex(self._h, int(seq), ptr, len(arr), _stream_handle(stream)))
@@ -345,7 +369,8 @@ class Pool:
         _check(_lib.ll_pool_set_profiling(self._h, 1 if enable else 0))
 
     def profile_read(self, kernel: int = 0):
-        """(launches, total_ms, total_bytes) of kernel 0 (row moves) or 1 (keep scan)."""
+        """(launches, total_ms, total_bytes) of kernel 0 (row moves), 1 (keep
+        scan) or 2 (per-row rotation)."""
         n, ms, b = ctypes.c_int64(), ctypes.c_double(), ctypes.c_int64()
         _check(_lib.ll_profile_read(self._h, kernel, ctypes.byref(n), ctypes.byref(ms), ctypes.byref(b)))
         return n.value, ms.value, b.value
