@@ -28,6 +28,10 @@ Other workloads (one JSON line each, not the headline):
                                      32768 tokens: death times from the
                                      eviction logs, 128 x 128 block mask and the
                                      dense bit mask (8.6 GB written)
+  --workload rope_rows_32k_27layer   per-row-angle rotation: all 32768 rows of
+                                     the 27-layer MLA cache gathered with k_pe
+                                     turned back by its position (2.04 GB), and
+                                     the same rows turned in place
   --workload splice_32k_llama8b      the headline splice on a GQA cache of
                                      Llama-3-8B shape (32 layers, K and V of 8
                                      heads x 128, RoPE on all 128, half-split,
@@ -68,7 +72,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--workload", default="splice_32k_27layer",
                     choices=["splice_32k_27layer", "splice_16x32k_27layer", "evict_256x16k_27layer_p16",
-                             "evict_256x16k_27layer_p1", "splice_32k_llama8b", "kvs_mask_64x32k"])
+                             "evict_256x16k_27layer_p1", "splice_32k_llama8b", "kvs_mask_64x32k",
+                             "rope_rows_32k_27layer"])
     return ap.parse_args()
 
 
@@ -76,13 +81,15 @@ def parse():
 # device helpers and the launch structures.
 KERNEL_SOURCE = {"splice_kernel": "kernels.hip", "evict_move_kernel": "kernels.hip",
                  "gqa_splice_kernel": "kernels_gqa.hip", "plane_evict_kernel": "kernels_gqa.hip",
-                 "kvs_dense_kernel": "kernels_kvs.hip"}
+                 "kvs_dense_kernel": "kernels_kvs.hip", "rope_rows_kernel": "kernels_rows.hip"}
 
 
 def kernel_source_sha(kernel: str) -> str:
     csrc = os.path.join(ROOT, "mla_paged_cache_amd", "csrc")
     src = KERNEL_SOURCE[kernel]
-    headers = ("kvs_internal.h",) if src == "kernels_kvs.hip" else ("device_common.h", "leyline_internal.h")
+    headers = {"kernels_kvs.hip": ("kvs_internal.h",),
+               "kernels_rows.hip": ("device_common.h", "leyline_internal.h", "rows_internal.h")}.get(
+        src, ("device_common.h", "leyline_internal.h"))
     h = hashlib.sha256()
     for name in (*headers, src):
         h.update(open(os.path.join(csrc, name), "rb").read())
@@ -400,6 +407,62 @@ def bench_splice_gqa(args):
     return out
 
 
+# ------------------------------------------------------ per-row rotation --
+
+def bench_rope_rows(args):
+    """All 32768 rows of the 27-layer MLA cache (page size 16, permuted pages)
+    gathered into a dense [27][32768][576] buffer with k_pe turned back by
+    each row's position (angle -p), as VECTOR does before reconstructing V
+    from K.  A step is one ll_rope_rows call (per-row table kernel + row
+    kernel).  The same rows turned in place are timed after it."""
+    import torch
+    from mla_paged_cache_amd import leyline as L
+    from synth import permuted_pages, random_rows_torch
+
+    LAYERS, TOKENS, PAGE, POOL_PAGES = 27, 32768, 16, 4096
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    data = random_rows_torch(0, (LAYERS, POOL_PAGES, PAGE, ROW), dev)
+    table = torch.full((1, TOKENS // PAGE + 8), -1, dtype=torch.int32, device=dev)
+    pool = L.Pool(data, table)
+    pool.seq_set_pages(0, permuted_pages(0, TOKENS // PAGE), TOKENS)
+    angles = -torch.arange(TOKENS, dtype=torch.int64, device=dev)
+    out = torch.empty((LAYERS, TOKENS, ROW), dtype=torch.bfloat16, device=dev)
+    pool.rope_rows(0, 0, angles, out=out)
+    torch.cuda.synchronize()
+    alg = pool.last_stats().alg_bytes
+
+    def timed(in_place):
+        for _ in range(args.warmup):
+            pool.rope_rows(0, 0, angles, out=None if in_place else out)
+        torch.cuda.synchronize()
+        pool.profile_read(2)
+        pool.set_profiling(True)
+        quiet_gc()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            pool.rope_rows(0, 0, angles, out=None if in_place else out)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        gc.enable()
+        pool.set_profiling(False)
+        return (t1 - t0) * 1e3 / args.steps, pool.profile_read(2)
+
+    ms_per_step, (launches, kernel_ms, kernel_bytes) = timed(False)
+    ip_ms, (ip_launches, ip_kernel_ms, ip_bytes) = timed(True)
+    out_line = base_line(args, "rope_rows_32k_27layer", alg / (ms_per_step * 1e-3) / 1e9, ms_per_step, {
+        "layers": LAYERS, "tokens": TOKENS, "page_size": PAGE, "angles": "-position of each row",
+        "mode": "gather to a dense buffer", "alg_bytes_per_step": alg})
+    out_line["metric"] = "per-row-angle RoPE rotation: row bytes GB/s"
+    out_line["roofline"] = roofline("rope_rows_kernel", "rope_rows_32k_27layer", launches, kernel_ms, kernel_bytes)
+    out_line["in_place"] = {"ms_per_step": round(ip_ms, 5), "kernel_avg_us": round(ip_kernel_ms * 1e3 / max(1, ip_launches), 2),
+                            "alg_bytes": ip_bytes // max(1, ip_launches),
+                            "achieved_gbs": round(ip_bytes / max(1e-9, ip_kernel_ms * 1e-3) / 1e9, 1)}
+    out_line["cpu_baseline"] = None
+    pool.close()
+    return out_line
+
+
 # --------------------------------------------------------- trainer mask --
 
 def bench_kvs_mask(args):
@@ -567,6 +630,8 @@ def main():
         out = bench_splice_gqa(args)
     elif args.workload == "kvs_mask_64x32k":
         out = bench_kvs_mask(args)
+    elif args.workload == "rope_rows_32k_27layer":
+        out = bench_rope_rows(args)
     else:
         out = bench_evict(args, 16 if args.workload.endswith("p16") else 1)
     print(json.dumps(out), flush=True)
