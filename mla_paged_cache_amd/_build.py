@@ -3,7 +3,8 @@
 The library holds the HIP kernels (csrc/kernels.hip for MLA pools,
 csrc/kernels_gqa.hip for GQA / MHA pools, csrc/kernels_kvs.hip for the
 KV-streams trainer mask, csrc/kernels_rows.hip for the per-row-angle
-rotation, helpers in csrc/device_common.h) and the C++ host
+rotation, csrc/kernels_alloc.hip for the eviction's device-side page
+allocator, helpers in csrc/device_common.h) and the C++ host
 side and C ABI (csrc/pool.cpp, csrc/kvs_mask.cpp).  Flags:
   * --offload-arch=gfx950 only (MI355X);
   * -ffp-contract=off so the delta-rotation keeps its separately rounded
@@ -26,7 +27,7 @@ LIB_NAME = "libleyline.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 
 SOURCES = [os.path.join(CSRC, n) for n in ("kernels.hip", "kernels_gqa.hip", "kernels_kvs.hip", "kernels_rows.hip",
-                                           "pool.cpp", "kvs_mask.cpp")]
+                                           "kernels_alloc.hip", "pool.cpp", "kvs_mask.cpp")]
 
 FLAGS = [
     "--offload-arch=gfx950",
@@ -37,6 +38,7 @@ FLAGS = [
     "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall",
+    "-Winfinite-recursion",
     "-Wl,--no-undefined",
 ]
 

@@ -1,0 +1,41 @@
+// Internal types of the device-side page allocator of the eviction
+// (kernels_alloc.hip) and its host side (pool.cpp).  Not part of the C ABI.
+#pragma once
+
+#include "leyline_internal.h"
+
+namespace ll {
+
+struct AllocLaunch {
+  const EvictSeq* seqs;
+  int32_t n;
+  int32_t page_shift;
+  const int64_t* counts;      // rows kept per sequence (keep scan)
+  const int32_t* reuse;       // per new page: old logical page kept, or -1 (keep scan)
+  const int32_t* page_table;  // old tables (read only)
+  int32_t max_pages_per_seq;
+  int32_t n_words;            // words of the free bitmap
+  const uint64_t* free_words; // the free set at the call's start (bit set = free)
+  int32_t* rank;              // per new page: its index among the sequence's fresh pages
+  int32_t* fresh_count;       // [n]
+  int32_t* fresh_base;        // [n]: fresh pages of the sequences before
+  int32_t* word_base;         // [n_words]: free pages in the words before
+  int32_t* new_table;         // per sequence at reuse_off: the new page table
+  EvictTask* tasks;           // [fresh pages], in (sequence, page) order
+  int32_t* info;              // [0] fresh pages, [1] 1 if they exceed the free pages
+};
+
+struct DevMoveLaunch {
+  const chunk_t* const* planes;
+  int32_t num_planes;
+  int32_t page_shift;
+  int32_t row_chunks;
+  const EvictTask* tasks;
+  const int32_t* info;        // info[0]: tasks
+  const int32_t* src_rows;
+};
+
+hipError_t launch_alloc(const AllocLaunch& a, hipStream_t s);
+hipError_t launch_dev_move(const DevMoveLaunch& a, int64_t chunk_bound, hipStream_t s);
+
+}  // namespace ll

@@ -1,0 +1,198 @@
+// gfx950 kernels of the eviction's device-side page allocator: the same
+// lowest-free-first page plan the host makes, computed on the device so that
+// kv_evict_compact never waits for the keep scan ("KV-streams", "how it
+// works": evicted entries are reclaimed inside the engine, kept entries are
+// left as they were).
+//
+//  * fresh_rank_kernel: per sequence, a block scan over its new pages numbers
+//    the ones that cannot reuse an old page (fresh pages).
+//  * alloc_scan_kernel: one block; exclusive scans of the fresh counts over
+//    the batch and of the free bitmap's word popcounts.
+//  * alloc_tables_kernel: per new page, its physical page: the reused old page,
+//    or fresh page f = the f-th lowest free page (binary search over the word
+//    prefix, then the bit inside the word); fresh pages also get a move task.
+//  * table_copy_kernel: the new page-table rows, written after every read of
+//    the old ones.
+//  * dev_move_kernel: the row copy into fresh pages, grid-stride over a task
+//    count that only the device knows.
+#include "alloc_internal.h"
+#include "device_common.h"
+
+namespace ll {
+namespace {
+
+constexpr int kScanThreads = 1024;
+constexpr int kScanWaves = kScanThreads / 64;
+
+// Exclusive scan of one int per thread across a 1024-thread block; *total gets
+// the block's sum.  Uses `lds` (kScanWaves ints); all threads must call it.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* lds, int* total) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) lds[wave] = x;
+  __syncthreads();
+  int before = 0, sum = 0;
+#pragma unroll
+  for (int w = 0; w < kScanWaves; ++w) {
+    const int t = lds[w];
+    before += w < wave ? t : 0;
+    sum += t;
+  }
+  __syncthreads();  // lds is reused by the next call
+  *total = sum;
+  return before + x - v;
+}
+
+__global__ __launch_bounds__(kScanThreads) void fresh_rank_kernel(AllocLaunch a) {
+  __shared__ int lds[kScanWaves];
+  const EvictSeq e = a.seqs[blockIdx.x];
+  const int64_t P = int64_t{1} << a.page_shift;
+  const int64_t pages = (a.counts[blockIdx.x] + P - 1) >> a.page_shift;
+  int carry = 0;
+  for (int64_t base = 0; base < pages; base += kScanThreads) {
+    const int64_t q = base + threadIdx.x;
+    const int fresh = (q < pages && a.reuse[e.reuse_off + q] < 0) ? 1 : 0;
+    int total;
+    const int r = block_exclusive_scan(fresh, lds, &total);
+    if (q < pages) a.rank[e.reuse_off + q] = carry + r;
+    carry += total;
+  }
+  if (threadIdx.x == 0) a.fresh_count[blockIdx.x] = carry;
+}
+
+__global__ __launch_bounds__(kScanThreads) void alloc_scan_kernel(AllocLaunch a) {
+  __shared__ int lds[kScanWaves];
+  int carry = 0;
+  for (int base = 0; base < a.n; base += kScanThreads) {
+    const int i = base + threadIdx.x;
+    const int v = i < a.n ? a.fresh_count[i] : 0;
+    int total;
+    const int r = block_exclusive_scan(v, lds, &total);
+    if (i < a.n) a.fresh_base[i] = carry + r;
+    carry += total;
+  }
+  const int fresh = carry;
+  carry = 0;
+  for (int base = 0; base < a.n_words; base += kScanThreads) {
+    const int w = base + threadIdx.x;
+    const int v = w < a.n_words ? __popcll(a.free_words[w]) : 0;
+    int total;
+    const int r = block_exclusive_scan(v, lds, &total);
+    if (w < a.n_words) a.word_base[w] = carry + r;
+    carry += total;
+  }
+  if (threadIdx.x == 0) {
+    const bool short_of_pages = fresh > carry;
+    a.info[0] = short_of_pages ? 0 : fresh;
+    a.info[1] = short_of_pages ? 1 : 0;
+  }
+}
+
+// The f-th (0-based) lowest free page: the last word whose prefix is <= f,
+// then the (f - prefix)-th set bit of that word.
+__device__ __forceinline__ int32_t select_free(const AllocLaunch& a, int32_t f) {
+  int lo = 0, hi = a.n_words - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.word_base[mid] <= f) lo = mid;
+    else hi = mid - 1;
+  }
+  uint64_t w = a.free_words[lo];
+  for (int k = f - a.word_base[lo]; k > 0; --k) w &= w - 1;
+  return static_cast<int32_t>(lo * 64 + __builtin_ctzll(w));
+}
+
+__global__ __launch_bounds__(256) void alloc_tables_kernel(AllocLaunch a) {
+  if (a.info[1]) return;  // not enough free pages: nothing changes
+  const EvictSeq e = a.seqs[blockIdx.x];
+  const int64_t P = int64_t{1} << a.page_shift;
+  const int64_t n_new = a.counts[blockIdx.x];
+  const int64_t pages = (n_new + P - 1) >> a.page_shift;
+  const int32_t* old_t = a.page_table + static_cast<int64_t>(e.seq) * a.max_pages_per_seq;
+  const int32_t base = a.fresh_base[blockIdx.x];
+  for (int64_t q = threadIdx.x; q < pages; q += 256) {
+    const int32_t r = a.reuse[e.reuse_off + q];
+    int32_t page;
+    if (r >= 0) {
+      page = old_t[r];
+    } else {
+      const int32_t f = base + a.rank[e.reuse_off + q];
+      page = select_free(a, f);
+      EvictTask t{};
+      t.src_off = e.src_off;
+      t.q = static_cast<int32_t>(q);
+      t.dst_page = page;
+      t.n_new = static_cast<int32_t>(n_new);
+      a.tasks[f] = t;
+    }
+    a.new_table[e.reuse_off + q] = page;
+  }
+}
+
+__global__ __launch_bounds__(256) void table_copy_kernel(AllocLaunch a) {
+  if (a.info[1]) return;
+  const EvictSeq e = a.seqs[blockIdx.x];
+  const int64_t P = int64_t{1} << a.page_shift;
+  const int64_t pages = (a.counts[blockIdx.x] + P - 1) >> a.page_shift;
+  int32_t* t = const_cast<int32_t*>(a.page_table) + static_cast<int64_t>(e.seq) * a.max_pages_per_seq;
+  for (int64_t q = threadIdx.x; q < pages; q += 256) t[q] = a.new_table[e.reuse_off + q];
+}
+
+// blockIdx.y = plane; the x blocks stride over the info[0] * P * row_chunks
+// chunks of the fresh pages (task = page, then row, then chunk).
+template <bool WAVE_TASK>
+__global__ __launch_bounds__(256) void dev_move_kernel(DevMoveLaunch a) {
+  const int shift = a.page_shift;
+  const uint32_t rc = static_cast<uint32_t>(a.row_chunks);
+  const int64_t total = (static_cast<int64_t>(a.info[0]) << shift) * rc;
+  const chunk_t* layer = a.planes[blockIdx.y];
+  for (int64_t c = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; c < total;
+       c += static_cast<int64_t>(gridDim.x) * 256) {
+    const uint32_t row_flat = static_cast<uint32_t>(c / rc);
+    const uint32_t col = static_cast<uint32_t>(c - static_cast<int64_t>(row_flat) * rc);
+    const EvictTask t = load_task<WAVE_TASK>(a.tasks, row_flat >> shift);
+    const uint32_t r = row_flat & ((1u << shift) - 1u);
+    const int64_t j = (static_cast<int64_t>(t.q) << shift) + r;
+    if (j >= t.n_new) continue;
+    const int64_t src_row = a.src_rows[t.src_off + j];
+    const chunk_t v = __builtin_nontemporal_load(layer + src_row * rc + col);
+    __builtin_nontemporal_store(v, const_cast<chunk_t*>(layer) +
+                                       ((static_cast<int64_t>(t.dst_page) << shift) + r) * rc + col);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_alloc(const AllocLaunch& a, hipStream_t s) {
+  if (a.n == 0) return hipSuccess;
+  fresh_rank_kernel<<<dim3(a.n), dim3(kScanThreads), 0, s>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  alloc_scan_kernel<<<dim3(1), dim3(kScanThreads), 0, s>>>(a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  alloc_tables_kernel<<<dim3(a.n), dim3(256), 0, s>>>(a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  table_copy_kernel<<<dim3(a.n), dim3(256), 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_dev_move(const DevMoveLaunch& a, int64_t chunk_bound, hipStream_t s) {
+  if (a.num_planes == 0 || chunk_bound == 0) return hipSuccess;
+  // enough blocks to fill the chip several times over; each strides over the rest
+  const int64_t want = (chunk_bound + 255) / 256;
+  const unsigned gx = static_cast<unsigned>(want < 2048 ? want : 2048);
+  const dim3 grid(gx, static_cast<unsigned>(a.num_planes));
+  if ((int64_t{a.row_chunks} << a.page_shift) % 64 == 0)
+    dev_move_kernel<true><<<grid, dim3(256), 0, s>>>(a);
+  else
+    dev_move_kernel<false><<<grid, dim3(256), 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace ll

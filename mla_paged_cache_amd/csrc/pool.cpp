@@ -24,6 +24,7 @@
 #include "host_common.h"
 #include "leyline_internal.h"
 #include "rows_internal.h"
+#include "alloc_internal.h"
 
 namespace ll {
 
@@ -87,6 +88,8 @@ class FreePages {
       }
     }
   }
+  // The bitmap words (bit set = free), for the device's page plan.
+  void copy_words(uint64_t* out) const { std::memcpy(out, words_.data(), words_.size() * sizeof(uint64_t)); }
   void advance_hint() {
     while (hint_ < static_cast<int64_t>(words_.size()) && words_[hint_] == 0) ++hint_;
   }
@@ -191,6 +194,17 @@ struct ll_pool {
   std::vector<ProfRec> prof[3];  // row-moving kernel, keep scan, per-row rotation
   std::vector<hipEvent_t> spare_events;
   std::vector<int32_t> page_slot;  // per physical page: scratch marks of ll_seq_set_pages
+  // An eviction whose page plan the device made: the host learns its result
+  // from a readback and brings its bookkeeping up to date (settles) at the
+  // start of the next call on the pool.
+  struct PendingEvict {
+    bool active = false;
+    hipEvent_t done = nullptr;   // the readback has landed
+    std::vector<int32_t> seq_ids;
+    std::vector<int64_t> reuse_off;
+    size_t off_info = 0, off_table = 0;  // in h_readback (counts at 0)
+    int64_t prof_index = -1;     // prof[0] entry whose bytes are known only then
+  } pending;
 };
 
 namespace {
@@ -204,6 +218,86 @@ ll_status check_pool(const ll_pool* p) {
   if (!p) return fail(LL_EINVAL, "pool is NULL");
   if (p->poisoned) return fail(LL_EPOISONED, "pool is poisoned by an earlier device failure");
   return LL_OK;
+}
+
+// Bring the host bookkeeping up to date with an eviction planned on the
+// device: its new lengths and page tables come from the readback; fresh pages
+// leave the free set and old pages no longer listed return to it.
+ll_status settle(ll_pool* p) {
+  ll_pool::PendingEvict& pe = p->pending;
+  if (!pe.active) return LL_OK;
+  pe.active = false;
+  hipError_t e = hipEventSynchronize(pe.done);
+  if (e != hipSuccess) return device_fail(p, e, "eviction readback");
+  const int64_t* counts = reinterpret_cast<const int64_t*>(p->h_readback);
+  const int32_t* info = reinterpret_cast<const int32_t*>(p->h_readback + pe.off_info);
+  const int32_t* table = reinterpret_cast<const int32_t*>(p->h_readback + pe.off_table);
+  if (info[1]) {
+    p->poisoned = true;
+    return fail(LL_EDEVICE, "the device page plan ran out of free pages");
+  }
+  const int64_t P = p->P;
+  std::vector<int32_t>& mark = p->page_slot;
+  ll_plan_stats stats{};
+  std::vector<int32_t> taken, freed;
+  for (size_t i = 0; i < pe.seq_ids.size(); ++i) {
+    SeqState& s = p->seqs[pe.seq_ids[i]];
+    const int64_t n_new = counts[i];
+    if (n_new < 0 || n_new > s.len) {
+      p->poisoned = true;
+      return fail(LL_EDEVICE, "the device page plan returned a bad length");
+    }
+    const int64_t pages = ceil_div(n_new, P);
+    const int32_t* nt = table + pe.reuse_off[i];
+    for (int32_t pg : s.pages) mark[pg] = -2;
+    bool bad = false;
+    const size_t taken0 = taken.size();
+    for (int64_t q = 0; q < pages; ++q) {
+      const int32_t pg = nt[q];
+      if (pg < 0 || pg >= p->desc.num_pages) {
+        bad = true;
+        break;
+      }
+      if (mark[pg] == -2) {
+        mark[pg] = -4;  // an old page kept in place
+      } else if (mark[pg] == -1 && p->free.is_free(pg)) {
+        mark[pg] = -3;  // a fresh page
+        taken.push_back(pg);
+        stats.rows_moved += std::min(P, n_new - q * P);
+      } else {
+        bad = true;     // listed twice, or owned by another sequence
+        break;
+      }
+    }
+    for (int32_t pg : s.pages)
+      if (mark[pg] == -2) freed.push_back(pg);
+    for (int32_t pg : s.pages) mark[pg] = -1;
+    for (size_t k = taken0; k < taken.size(); ++k) mark[taken[k]] = -1;
+    if (bad) {
+      p->poisoned = true;
+      return fail(LL_EDEVICE, "the device page plan returned an invalid page");
+    }
+    s.pages.assign(nt, nt + pages);
+    s.len = n_new;
+    stats.table_entries += pages;
+  }
+  for (int32_t pg : taken) p->free.take(pg);
+  for (int32_t pg : freed) p->free.give(pg);
+  p->free.advance_hint();
+  stats.fresh_pages = static_cast<int64_t>(taken.size());
+  stats.freed_pages = static_cast<int64_t>(freed.size());
+  stats.alg_bytes = p->num_planes * 2 * p->row_bytes * stats.rows_moved;
+  if (pe.prof_index >= 0 && pe.prof_index < static_cast<int64_t>(p->prof[0].size()))
+    p->prof[0][pe.prof_index].bytes = stats.alg_bytes + 4 * stats.table_entries;
+  p->last = stats;
+  return LL_OK;
+}
+
+// check_pool, then settle a pending device-planned eviction.
+ll_status enter(ll_pool* p) {
+  ll_status rc = check_pool(p);
+  if (rc) return rc;
+  return settle(p);
 }
 
 hipEvent_t take_event(ll_pool* p) {
@@ -480,6 +574,142 @@ void plan_splice(const ll_pool* p, const ll_directive& d, const SeqState& s, Spl
   }
 }
 
+// Grow the eviction scratch (device) and readback (pinned) buffers; growing
+// waits for earlier device work, which may still use them.
+ll_status ensure_evict_buffers(ll_pool* p, size_t scratch, size_t readback) {
+  if (scratch <= p->scratch_cap && readback <= p->readback_cap) return LL_OK;
+  if (p->last_done) (void)hipEventSynchronize(p->last_done);
+  if (scratch > p->scratch_cap) {
+    if (p->d_scratch) (void)hipFree(p->d_scratch);
+    p->d_scratch = nullptr;
+    p->scratch_cap = 0;
+    if (hipMalloc(reinterpret_cast<void**>(&p->d_scratch), scratch) != hipSuccess)
+      return fail(LL_ENOMEM, "cannot allocate %zu bytes of eviction scratch", scratch);
+    p->scratch_cap = scratch;
+  }
+  if (readback > p->readback_cap) {
+    if (p->h_readback) (void)hipHostFree(p->h_readback);
+    p->h_readback = nullptr;
+    p->readback_cap = 0;
+    if (hipHostMalloc(reinterpret_cast<void**>(&p->h_readback), readback, hipHostMallocDefault) != hipSuccess)
+      return fail(LL_ENOMEM, "cannot allocate %zu bytes of pinned readback", readback);
+    p->readback_cap = readback;
+  }
+  return LL_OK;
+}
+
+// Eviction with the page plan made on the device (kernels_alloc.hip): keep
+// scan, fresh-page ranks, lowest-free-first selection from the free bitmap as
+// it stands now, new tables, row moves, then one readback that the next call
+// settles.  Nothing here waits for the device.
+ll_status evict_device_plan(ll_pool* p, const int32_t* seq_ids, int32_t n, const uint8_t* keep_dev,
+                            const std::vector<ll::EvictSeq>& es, const std::vector<int64_t>& reuse_off,
+                            int64_t total_rows, int64_t total_pages, hipStream_t st) {
+  const int64_t P = p->P;
+  const int64_t rc_chunks = p->row_bytes / 16;
+  if (total_pages * P * rc_chunks >= (int64_t{1} << 32))
+    return fail(LL_EUNSUPPORTED, "one eviction may move at most 2^32 16-byte chunks per layer");
+  const int32_t n_words = P == 1 ? 0 : static_cast<int32_t>(ceil_div(p->desc.num_pages, 64));
+  // device scratch: [counts n | info 4 | new_table tp] (read back in one copy),
+  // then reuse tp | src_rows rows | src_logical rows | rank tp | fresh_count n |
+  // fresh_base n | word_base n_words | tasks tp
+  const size_t tp = static_cast<size_t>(total_pages), rows = static_cast<size_t>(total_rows);
+  const size_t off_info = align_up(8 * static_cast<size_t>(n), 16);
+  const size_t off_nt = align_up(off_info + 16, 256);
+  const size_t readback = off_nt + 4 * tp;
+  const size_t off_reuse = align_up(readback, 256);
+  const size_t off_src = align_up(off_reuse + 4 * tp, 256);
+  const size_t off_logical = align_up(off_src + 4 * rows, 256);
+  const size_t off_rank = align_up(off_logical + 4 * rows, 256);
+  const size_t off_fc = align_up(off_rank + 4 * tp, 256);
+  const size_t off_fb = align_up(off_fc + 4 * static_cast<size_t>(n), 256);
+  const size_t off_wb = align_up(off_fb + 4 * static_cast<size_t>(n), 256);
+  const size_t off_tasks = align_up(off_wb + 4 * static_cast<size_t>(n_words), 256);
+  const size_t scratch = off_tasks + sizeof(ll::EvictTask) * tp + 256;
+  ll_status rc = begin_call(p, st);
+  if (rc) return rc;
+  if ((rc = ensure_evict_buffers(p, scratch, readback))) return rc;
+
+  Staging* sg = nullptr;
+  const size_t words_bytes = 8 * static_cast<size_t>(n_words);
+  if ((rc = stage_acquire(p, stage_bytes_for({es.size() * sizeof(ll::EvictSeq), words_bytes}), &sg))) return rc;
+  const size_t o_es = stage_put(sg, es.data(), es.size() * sizeof(ll::EvictSeq));
+  const size_t o_w = stage_put(sg, nullptr, words_bytes);
+  if (n_words) p->free.copy_words(reinterpret_cast<uint64_t*>(sg->host + o_w));
+  if ((rc = upload(p, sg, st))) return rc;
+
+  char* d = p->d_scratch;
+  ll::ScanLaunch sc{};
+  sc.keep = keep_dev;
+  sc.seqs = reinterpret_cast<const ll::EvictSeq*>(sg->dev + o_es);
+  sc.n_seqs = n;
+  sc.page_shift = p->page_shift;
+  sc.page_table = p->desc.page_table;
+  sc.max_pages_per_seq = p->desc.max_pages_per_seq;
+  sc.counts = reinterpret_cast<int64_t*>(d);
+  sc.reuse = reinterpret_cast<int32_t*>(d + off_reuse);
+  sc.src_rows = reinterpret_cast<int32_t*>(d + off_src);
+  sc.src_logical = reinterpret_cast<int32_t*>(d + off_logical);
+  ProfRec rec1{};
+  if (p->profiling && (rc = prof_begin(p, 1, st, &rec1))) return rc;
+  hipError_t e = ll::launch_keep_scan(sc, st);
+  if (e != hipSuccess) return device_fail(p, e, "keep_scan_kernel launch");
+  if (p->profiling) {
+    rec1.bytes = total_rows + 4 * total_rows;
+    if ((rc = prof_end(p, 1, st, &rec1))) return rc;
+  }
+
+  ll::AllocLaunch al{};
+  al.seqs = sc.seqs;
+  al.n = n;
+  al.page_shift = p->page_shift;
+  al.counts = sc.counts;
+  al.reuse = sc.reuse;
+  al.page_table = p->desc.page_table;
+  al.max_pages_per_seq = p->desc.max_pages_per_seq;
+  al.n_words = n_words;
+  al.free_words = reinterpret_cast<const uint64_t*>(sg->dev + o_w);
+  al.rank = reinterpret_cast<int32_t*>(d + off_rank);
+  al.fresh_count = reinterpret_cast<int32_t*>(d + off_fc);
+  al.fresh_base = reinterpret_cast<int32_t*>(d + off_fb);
+  al.word_base = reinterpret_cast<int32_t*>(d + off_wb);
+  al.new_table = reinterpret_cast<int32_t*>(d + off_nt);
+  al.tasks = reinterpret_cast<ll::EvictTask*>(d + off_tasks);
+  al.info = reinterpret_cast<int32_t*>(d + off_info);
+  if ((e = ll::launch_alloc(al, st)) != hipSuccess) return device_fail(p, e, "page allocator launch");
+
+  ll::DevMoveLaunch mv{};
+  mv.planes = reinterpret_cast<const ll::chunk_t* const*>(p->d_layers);
+  mv.num_planes = p->num_planes;
+  mv.page_shift = p->page_shift;
+  mv.row_chunks = static_cast<int32_t>(rc_chunks);
+  mv.tasks = al.tasks;
+  mv.info = al.info;
+  mv.src_rows = sc.src_rows;
+  ProfRec rec{};
+  if (p->profiling && (rc = prof_begin(p, 0, st, &rec))) return rc;
+  const int64_t chunk_bound = P == 1 ? 0 : total_pages * P * rc_chunks;
+  if ((e = ll::launch_dev_move(mv, chunk_bound, st)) != hipSuccess) return device_fail(p, e, "dev_move_kernel launch");
+  int64_t prof_index = -1;
+  if (p->profiling) {
+    rec.bytes = 0;  // known when the call settles
+    if ((rc = prof_end(p, 0, st, &rec))) return rc;
+    prof_index = static_cast<int64_t>(p->prof[0].size()) - 1;
+  }
+  e = hipMemcpyAsync(p->h_readback, d, readback, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipEventRecord(p->pending.done, st);
+  if (e != hipSuccess) return device_fail(p, e, "eviction readback");
+  if ((rc = end_call(p, sg, st))) return rc;
+  ll_pool::PendingEvict& pe = p->pending;
+  pe.active = true;
+  pe.seq_ids.assign(seq_ids, seq_ids + n);
+  pe.reuse_off = reuse_off;
+  pe.off_info = off_info;
+  pe.off_table = off_nt;
+  pe.prof_index = prof_index;
+  return LL_OK;
+}
+
 ll_status validate_directives(const ll_pool* p, const ll_directive* dirs, int32_t n) {
   std::vector<char> seen(static_cast<size_t>(p->desc.max_seqs), 0);
   for (int32_t i = 0; i < n; ++i) {
@@ -601,6 +831,7 @@ ll_status setup_pool(ll_pool* p, ll_pool** out) {
   if (e == hipSuccess)
     e = hipMemcpy(p->d_layers, p->layer_ptrs.data(), sizeof(void*) * p->num_planes, hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&p->readback_ev, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&p->pending.done, hipEventDisableTiming);
   if (e == hipSuccess) e = hipStreamCreateWithFlags(&p->copy_stream, hipStreamNonBlocking);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&p->upload_ev, hipEventDisableTiming);
   if (e == hipSuccess) e = hipHostMalloc(reinterpret_cast<void**>(&p->ring_host), kRingBytes, hipHostMallocDefault);
@@ -682,6 +913,7 @@ void ll_pool_destroy(ll_pool* p) {
   if (!p) return;
   DeviceGuard g(p->desc.device);
   if (p->last_done) (void)hipEventSynchronize(p->last_done);
+  if (p->pending.active) (void)hipEventSynchronize(p->pending.done);
   for (auto& r : p->ring_inflight) (void)hipEventDestroy(r.done);
   for (auto e : p->ring_events) (void)hipEventDestroy(e);
   if (p->upload_ev) (void)hipEventDestroy(p->upload_ev);
@@ -694,6 +926,7 @@ void ll_pool_destroy(ll_pool* p) {
     }
   for (auto e : p->spare_events) (void)hipEventDestroy(e);
   if (p->readback_ev) (void)hipEventDestroy(p->readback_ev);
+  if (p->pending.done) (void)hipEventDestroy(p->pending.done);
   if (p->copy_stream) {
     (void)hipStreamSynchronize(p->copy_stream);
     (void)hipStreamDestroy(p->copy_stream);
@@ -707,6 +940,8 @@ void ll_pool_destroy(ll_pool* p) {
 
 ll_status ll_pool_free_pages(const ll_pool* p, int64_t* n_free) {
   if (!p || !n_free) return fail(LL_EINVAL, "NULL argument");
+  ll_status rc = settle(const_cast<ll_pool*>(p));
+  if (rc) return rc;
   *n_free = p->free.count();
   return LL_OK;
 }
@@ -714,6 +949,8 @@ ll_status ll_pool_free_pages(const ll_pool* p, int64_t* n_free) {
 ll_status ll_seq_get(const ll_pool* p, int32_t seq, int64_t* len, int64_t* next_position, int32_t* pages_out,
                      int32_t cap, int32_t* n_pages_out) {
   if (!p) return fail(LL_EINVAL, "pool is NULL");
+  ll_status rc = settle(const_cast<ll_pool*>(p));
+  if (rc) return rc;
   if (seq < 0 || seq >= p->desc.max_seqs || !p->seqs[seq].used) return fail(LL_EINVAL, "unknown sequence %d", seq);
   if (cap > 0 && !pages_out) return fail(LL_EINVAL, "pages_out is NULL");
   const SeqState& s = p->seqs[seq];
@@ -726,7 +963,7 @@ ll_status ll_seq_get(const ll_pool* p, int32_t seq, int64_t* len, int64_t* next_
 }
 
 ll_status ll_seq_alloc(ll_pool* p, int64_t n_tokens, int32_t* seq_id_out, void* stream) {
-  ll_status rc = check_pool(p);
+  ll_status rc = enter(p);
   if (rc) return rc;
   if (!seq_id_out || n_tokens < 0) return fail(LL_EINVAL, "bad argument");
   const int64_t need = ceil_div(n_tokens, p->P);
@@ -758,7 +995,7 @@ ll_status ll_seq_alloc(ll_pool* p, int64_t n_tokens, int32_t* seq_id_out, void* 
 }
 
 ll_status ll_seq_set_pages(ll_pool* p, int32_t seq, const int32_t* pages, int64_t n_tokens, void* stream) {
-  ll_status rc = check_pool(p);
+  ll_status rc = enter(p);
   if (rc) return rc;
   if (seq < 0 || seq >= p->desc.max_seqs) return fail(LL_EINVAL, "bad sequence id %d", seq);
   if (n_tokens < 0) return fail(LL_EINVAL, "n_tokens < 0");
@@ -814,7 +1051,7 @@ ll_status ll_seq_set_pages(ll_pool* p, int32_t seq, const int32_t* pages, int64_
 }
 
 ll_status ll_seq_free(ll_pool* p, int32_t seq) {
-  ll_status rc = check_pool(p);
+  ll_status rc = enter(p);
   if (rc) return rc;
   if (seq < 0 || seq >= p->desc.max_seqs || !p->seqs[seq].used) return fail(LL_EINVAL, "unknown sequence %d", seq);
   SeqState& s = p->seqs[seq];
@@ -824,7 +1061,7 @@ ll_status ll_seq_free(ll_pool* p, int32_t seq) {
 }
 
 ll_status leyline_splice(ll_pool* p, const ll_directive* dirs, int32_t n, void* stream) {
-  ll_status rc = check_pool(p);
+  ll_status rc = enter(p);
   if (rc) return rc;
   if (n < 0 || (n > 0 && !dirs)) return fail(LL_EINVAL, "bad directive array");
   if (n == 0) return LL_OK;
@@ -1026,7 +1263,7 @@ ll_status leyline_splice(ll_pool* p, const ll_directive* dirs, int32_t n, void* 
 
 ll_status kv_evict_compact(ll_pool* p, const int32_t* seq_ids, int32_t n, const uint8_t* keep_dev,
                            const int64_t* keep_offsets, void* stream) {
-  ll_status rc = check_pool(p);
+  ll_status rc = enter(p);
   if (rc) return rc;
   if (n < 0 || (n > 0 && (!seq_ids || !keep_offsets))) return fail(LL_EINVAL, "bad arguments");
   if (n == 0) return LL_OK;
@@ -1045,6 +1282,28 @@ ll_status kv_evict_compact(ll_pool* p, const int32_t* seq_ids, int32_t n, const 
   const int64_t P = p->P;
   DeviceGuard g(p->desc.device);
   hipStream_t st = static_cast<hipStream_t>(stream);
+
+  std::vector<ll::EvictSeq> es(static_cast<size_t>(n));
+  std::vector<int64_t> reuse_off(static_cast<size_t>(n)), src_off(static_cast<size_t>(n));
+  {
+    int64_t ro = 0, so = 0;
+    for (int32_t i = 0; i < n; ++i) {
+      const SeqState& s = p->seqs[seq_ids[i]];
+      es[i].mask_off = keep_offsets[i];
+      es[i].n_old = s.len;
+      es[i].src_off = src_off[i] = so;
+      es[i].reuse_off = reuse_off[i] = ro;
+      es[i].seq = seq_ids[i];
+      so += s.len;
+      ro += static_cast<int64_t>(s.pages.size());
+    }
+  }
+  // When the free pages cover the worst case (every new page fresh; at page
+  // size 1 no page is ever fresh) the device makes the page plan and the call
+  // returns without waiting; otherwise the host makes it after one readback,
+  // so that a shortage is reported exactly.
+  if (P == 1 || p->free.count() >= total_pages)
+    return evict_device_plan(p, seq_ids, n, keep_dev, es, reuse_off, total_rows, total_pages, st);
 
   // --- scratch: [counts (int64) n | reuse (int32) total_pages | src_rows (int32)
   //     total_rows | src_logical (int32) total_rows]; the first two come back
@@ -1074,21 +1333,6 @@ ll_status kv_evict_compact(ll_pool* p, const int32_t* seq_ids, int32_t n, const 
     }
   }
 
-  std::vector<ll::EvictSeq> es(static_cast<size_t>(n));
-  std::vector<int64_t> reuse_off(static_cast<size_t>(n)), src_off(static_cast<size_t>(n));
-  {
-    int64_t ro = 0, so = 0;
-    for (int32_t i = 0; i < n; ++i) {
-      const SeqState& s = p->seqs[seq_ids[i]];
-      es[i].mask_off = keep_offsets[i];
-      es[i].n_old = s.len;
-      es[i].src_off = src_off[i] = so;
-      es[i].reuse_off = reuse_off[i] = ro;
-      es[i].seq = seq_ids[i];
-      so += s.len;
-      ro += static_cast<int64_t>(s.pages.size());
-    }
-  }
   Staging* s1 = nullptr;
   if ((rc = stage_acquire(p, stage_bytes_for({es.size() * sizeof(ll::EvictSeq)}), &s1))) return rc;
   const size_t o_es = stage_put(s1, es.data(), es.size() * sizeof(ll::EvictSeq));
@@ -1249,7 +1493,7 @@ ll_status kv_evict_compact(ll_pool* p, const int32_t* seq_ids, int32_t n, const 
 }
 
 ll_status ll_ptable_reindex(ll_pool* p, int32_t seq, const int32_t* keep_pages, int32_t n_keep, void* stream) {
-  ll_status rc = check_pool(p);
+  ll_status rc = enter(p);
   if (rc) return rc;
   if (seq < 0 || seq >= p->desc.max_seqs || !p->seqs[seq].used) return fail(LL_EINVAL, "unknown sequence %d", seq);
   if (n_keep < 0 || (n_keep > 0 && !keep_pages)) return fail(LL_EINVAL, "bad keep_pages");
@@ -1291,7 +1535,7 @@ ll_status ll_ptable_reindex(ll_pool* p, int32_t seq, const int32_t* keep_pages, 
 
 ll_status ll_rope_rows(ll_pool* p, int32_t seq, int64_t row_begin, int64_t n_rows, const int64_t* angle_dev,
                        void* out_dev, int64_t out_layer_stride_bytes, void* stream) {
-  ll_status rc = check_pool(p);
+  ll_status rc = enter(p);
   if (rc) return rc;
   if (seq < 0 || seq >= p->desc.max_seqs || !p->seqs[seq].used) return fail(LL_EINVAL, "unknown sequence %d", seq);
   const SeqState& s = p->seqs[seq];
@@ -1394,6 +1638,8 @@ ll_status ll_rope_rows(ll_pool* p, int32_t seq, int64_t row_begin, int64_t n_row
 
 ll_status ll_last_plan_stats(const ll_pool* p, ll_plan_stats* out) {
   if (!p || !out) return fail(LL_EINVAL, "NULL argument");
+  ll_status rc = settle(const_cast<ll_pool*>(p));
+  if (rc) return rc;
   *out = p->last;
   return LL_OK;
 }
@@ -1406,6 +1652,7 @@ ll_status ll_pool_set_profiling(ll_pool* p, int32_t enable) {
 
 ll_status ll_profile_read(ll_pool* p, int32_t kernel, int64_t* launches, double* total_ms, int64_t* total_bytes) {
   if (!p || kernel < 0 || kernel > 2) return fail(LL_EINVAL, "bad argument");
+  if (ll_status rc = settle(p)) return rc;
   DeviceGuard g(p->desc.device);
   int64_t cnt = 0, bytes = 0;
   double ms = 0.0;
