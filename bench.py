@@ -583,7 +583,7 @@ def bench_evict(args, page):
     torch.cuda.synchronize()
     stats = pool.last_stats()
     alg_bytes = stats.alg_bytes
-    times = []
+    times, call_times = [], []
     pool.profile_read(0)
     pool.profile_read(1)
     quiet_gc()
@@ -594,9 +594,12 @@ def bench_evict(args, page):
             pool.set_profiling(True)
         a = time.perf_counter()
         pool.evict(seqs, keep, offsets)
+        b = time.perf_counter()
         torch.cuda.synchronize()
+        pool.free_pages()  # settles the host bookkeeping of a device-planned call
         if i >= args.warmup:
             times.append(time.perf_counter() - a)
+            call_times.append(b - a)
     gc.enable()
     pool.set_profiling(False)
     launches, kernel_ms, kernel_bytes = pool.profile_read(0)
@@ -607,10 +610,16 @@ def bench_evict(args, page):
         "layers": LAYERS, "rollouts": ROLL, "tokens": TOKENS, "page_size": page, "pool_pages": POOL_PAGES,
         "mask": "turn drops U[200,2000], p=0.5", "rows_kept": int(masks.sum()),
         "rows_moved_per_layer": stats.rows_moved, "fresh_pages": stats.fresh_pages,
-        "alg_bytes_per_step": alg_bytes, "step": "one kv_evict_compact call, median"})
+        "alg_bytes_per_step": alg_bytes,
+        "page_plan": "device" if page == 1 or POOL_PAGES - ROLL * per >= ROLL * per else "host",
+        "step": "one kv_evict_compact call until its device work and host bookkeeping are done, median"})
     out["metric"] = "KV-streams eviction: row bytes moved GB/s; call latency"
     out["roofline"] = roofline("evict_move_kernel", name, launches, kernel_ms, kernel_bytes)
+    if out["config"]["page_plan"] == "device":
+        # the timed device work is the page plan (and the moves, none at page size 1)
+        out["roofline"]["kernel"] = "device page plan: fresh_rank/alloc_scan/alloc_tables/table_copy + dev_move"
     out["keep_scan_us"] = round(scan_ms * 1e3 / max(1, s_launches), 2)
+    out["call_return_us"] = round(1e6 * statistics.median(call_times), 1)
     out["cpu_baseline"] = None
     pool.close()
     return out

@@ -202,7 +202,7 @@ struct ll_pool {
     hipEvent_t done = nullptr;   // the readback has landed
     std::vector<int32_t> seq_ids;
     std::vector<int64_t> reuse_off;
-    size_t off_info = 0, off_table = 0;  // in h_readback (counts at 0)
+    size_t off_info = 0, off_table = 0, off_reuse = 0;  // in h_readback (counts at 0)
     int64_t prof_index = -1;     // prof[0] entry whose bytes are known only then
   } pending;
 };
@@ -236,8 +236,8 @@ ll_status settle(ll_pool* p) {
     p->poisoned = true;
     return fail(LL_EDEVICE, "the device page plan ran out of free pages");
   }
+  const int32_t* reuse = reinterpret_cast<const int32_t*>(p->h_readback + pe.off_reuse);
   const int64_t P = p->P;
-  std::vector<int32_t>& mark = p->page_slot;
   ll_plan_stats stats{};
   std::vector<int32_t> taken, freed;
   for (size_t i = 0; i < pe.seq_ids.size(); ++i) {
@@ -249,34 +249,36 @@ ll_status settle(ll_pool* p) {
     }
     const int64_t pages = ceil_div(n_new, P);
     const int32_t* nt = table + pe.reuse_off[i];
-    for (int32_t pg : s.pages) mark[pg] = -2;
+    const int32_t* ru = reuse + pe.reuse_off[i];
+    const int64_t old_pages = static_cast<int64_t>(s.pages.size());
+    // one merge walk: kept old pages appear in `ru` in increasing order;
+    // new pages with ru < 0 are fresh
+    int64_t k = 0;  // next old logical page not yet classified
     bool bad = false;
-    const size_t taken0 = taken.size();
-    for (int64_t q = 0; q < pages; ++q) {
-      const int32_t pg = nt[q];
-      if (pg < 0 || pg >= p->desc.num_pages) {
+    for (int64_t q = 0; q < pages && !bad; ++q) {
+      const int32_t r = ru[q];
+      if (r < 0) {
+        const int32_t pg = nt[q];
+        if (pg < 0 || pg >= p->desc.num_pages || !p->free.is_free(pg)) {
+          bad = true;
+          break;
+        }
+        taken.push_back(pg);
+        stats.rows_moved += std::min(P, n_new - q * P);
+        continue;
+      }
+      if (r < k || r >= old_pages || nt[q] != s.pages[r]) {
         bad = true;
         break;
       }
-      if (mark[pg] == -2) {
-        mark[pg] = -4;  // an old page kept in place
-      } else if (mark[pg] == -1 && p->free.is_free(pg)) {
-        mark[pg] = -3;  // a fresh page
-        taken.push_back(pg);
-        stats.rows_moved += std::min(P, n_new - q * P);
-      } else {
-        bad = true;     // listed twice, or owned by another sequence
-        break;
-      }
+      for (; k < r; ++k) freed.push_back(s.pages[k]);
+      k = r + 1;
     }
-    for (int32_t pg : s.pages)
-      if (mark[pg] == -2) freed.push_back(pg);
-    for (int32_t pg : s.pages) mark[pg] = -1;
-    for (size_t k = taken0; k < taken.size(); ++k) mark[taken[k]] = -1;
     if (bad) {
       p->poisoned = true;
       return fail(LL_EDEVICE, "the device page plan returned an invalid page");
     }
+    for (; k < old_pages; ++k) freed.push_back(s.pages[k]);
     s.pages.assign(nt, nt + pages);
     s.len = n_new;
     stats.table_entries += pages;
@@ -610,15 +612,15 @@ ll_status evict_device_plan(ll_pool* p, const int32_t* seq_ids, int32_t n, const
   if (total_pages * P * rc_chunks >= (int64_t{1} << 32))
     return fail(LL_EUNSUPPORTED, "one eviction may move at most 2^32 16-byte chunks per layer");
   const int32_t n_words = P == 1 ? 0 : static_cast<int32_t>(ceil_div(p->desc.num_pages, 64));
-  // device scratch: [counts n | info 4 | new_table tp] (read back in one copy),
-  // then reuse tp | src_rows rows | src_logical rows | rank tp | fresh_count n |
+  // device scratch: [counts n | info 4 | new_table tp | reuse tp] (read back in
+  // one copy), then src_rows rows | src_logical rows | rank tp | fresh_count n |
   // fresh_base n | word_base n_words | tasks tp
   const size_t tp = static_cast<size_t>(total_pages), rows = static_cast<size_t>(total_rows);
   const size_t off_info = align_up(8 * static_cast<size_t>(n), 16);
   const size_t off_nt = align_up(off_info + 16, 256);
-  const size_t readback = off_nt + 4 * tp;
-  const size_t off_reuse = align_up(readback, 256);
-  const size_t off_src = align_up(off_reuse + 4 * tp, 256);
+  const size_t off_reuse = off_nt + 4 * tp;
+  const size_t readback = off_reuse + 4 * tp;
+  const size_t off_src = align_up(readback, 256);
   const size_t off_logical = align_up(off_src + 4 * rows, 256);
   const size_t off_rank = align_up(off_logical + 4 * rows, 256);
   const size_t off_fc = align_up(off_rank + 4 * tp, 256);
@@ -676,6 +678,9 @@ ll_status evict_device_plan(ll_pool* p, const int32_t* seq_ids, int32_t n, const
   al.new_table = reinterpret_cast<int32_t*>(d + off_nt);
   al.tasks = reinterpret_cast<ll::EvictTask*>(d + off_tasks);
   al.info = reinterpret_cast<int32_t*>(d + off_info);
+  // kernel 0's record covers the page plan and the row moves of this path
+  ProfRec rec{};
+  if (p->profiling && (rc = prof_begin(p, 0, st, &rec))) return rc;
   if ((e = ll::launch_alloc(al, st)) != hipSuccess) return device_fail(p, e, "page allocator launch");
 
   ll::DevMoveLaunch mv{};
@@ -686,8 +691,6 @@ ll_status evict_device_plan(ll_pool* p, const int32_t* seq_ids, int32_t n, const
   mv.tasks = al.tasks;
   mv.info = al.info;
   mv.src_rows = sc.src_rows;
-  ProfRec rec{};
-  if (p->profiling && (rc = prof_begin(p, 0, st, &rec))) return rc;
   const int64_t chunk_bound = P == 1 ? 0 : total_pages * P * rc_chunks;
   if ((e = ll::launch_dev_move(mv, chunk_bound, st)) != hipSuccess) return device_fail(p, e, "dev_move_kernel launch");
   int64_t prof_index = -1;
@@ -706,6 +709,7 @@ ll_status evict_device_plan(ll_pool* p, const int32_t* seq_ids, int32_t n, const
   pe.reuse_off = reuse_off;
   pe.off_info = off_info;
   pe.off_table = off_nt;
+  pe.off_reuse = off_reuse;
   pe.prof_index = prof_index;
   return LL_OK;
 }
