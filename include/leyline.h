@@ -24,8 +24,12 @@
  * Streams.  `stream` is a hipStream_t passed as void* (NULL: the null stream).
  * Each call enqueues its device work on that stream and returns; the work of a
  * call is ordered after the work of the previous call on the same pool, also
- * across streams.  kv_evict_compact waits once for a small device-to-host
- * copy; no other call waits for the device.  A pool is not thread-safe.
+ * across streams.  No call waits for the device, with two exceptions: a
+ * kv_evict_compact whose host-made page plan needs one small device-to-host
+ * copy first (see there), and the first call after a device-planned
+ * kv_evict_compact, which waits for that call's results (a small readback)
+ * before it reads or changes the pool's bookkeeping.  A pool is not
+ * thread-safe.
  *
  * Errors.  Every function returns an ll_status.  All checks run before any
  * state changes, so a call that returns LL_EINVAL, LL_ERANGE, LL_ENOMEM or
@@ -227,7 +231,16 @@ ll_status leyline_splice(ll_pool* pool, const ll_directive* dirs, int32_t n, voi
  * bytes starting at keep_dev + keep_offsets[i] (keep_offsets is a host
  * array).  A device prefix scan gives each kept row its new index; rows move
  * only where a new page cannot reuse an old one (at page size 1 none move).
- * Waits once for a small device-to-host copy of the per-page plan inputs.
+ *
+ * Page plan.  When the free pages cover the worst case (every new page of the
+ * batch fresh; at page size 1 no page is ever fresh) the device makes the
+ * plan -- fresh pages are the lowest free pages in (batch position, page)
+ * order, found by rank/select on the free bitmap -- and writes the rows and
+ * page tables; the call returns without waiting and the pool's host
+ * bookkeeping (lengths, tables, free set, ll_last_plan_stats) catches up at
+ * the start of the next call on the pool.  Otherwise the call waits once for
+ * a small device-to-host copy of the per-page plan inputs and the host makes
+ * the same plan, so that a shortage returns LL_ENOMEM with nothing changed.
  * Errors: LL_EINVAL, LL_ENOMEM, LL_EDEVICE. */
 ll_status kv_evict_compact(ll_pool* pool, const int32_t* seq_ids, int32_t n,
                            const uint8_t* keep_dev, const int64_t* keep_offsets, void* stream);
