@@ -261,8 +261,9 @@ class CacheState:
     @staticmethod
     def empty(num_layers: int, num_pages: int, page_size: int, max_pages_per_seq: int,
               with_rows: bool = True, specs=None) -> "CacheState":
-        specs = list(specs) if specs is not None else [MLA_ROW] * num_layers
-        layers = ([np.zeros((num_pages, page_size, sp.width), np.uint16) for sp in specs]
+        specs = list(specs) if specs is not None else None   # None: every array holds MLA rows
+        widths = [sp.width for sp in specs] if specs is not None else [ROW] * num_layers
+        layers = ([np.zeros((num_pages, page_size, w), np.uint16) for w in widths]
                   if with_rows else None)
         return CacheState(page_size, num_pages, max_pages_per_seq, layers, specs,
                           free=set(range(num_pages)))

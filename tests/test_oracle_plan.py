@@ -319,3 +319,18 @@ def test_pins_catch_a_planted_off_by_one_in_sources(monkeypatch):
     rebuilt = old[:2] + old[5:]
     got = new.logical_rows(0, 0)
     assert any(not np.array_equal(got[j][:KV], rebuilt[j][:KV]) for j in range(len(rebuilt)))
+
+
+def test_state_without_specs_holds_mla_rows_for_any_layer_count():
+    """A state made with no row layouts and given its layer arrays afterwards
+    (as the benchmark's CPU leg does) splices MLA rows in every array."""
+    st = O.CacheState.empty(0, 64, 16, 64, with_rows=False)
+    st.layers = [random_rows_np(1 + L, (64, 16, O.ROW)) for L in range(3)]
+    st.set_pages(0, list(range(10)), 150)
+    stub = random_rows_np(9, (3, 4, O.ROW))
+    new, _ = O.splice(st, [O.Directive(0, 20, 40, 4, stub)])
+    assert new.lengths[0] == 134
+    for L in range(3):
+        rows = new.logical_rows(0, L)
+        assert np.array_equal(rows[20:24], stub[L])
+        assert np.array_equal(rows[24:, :KV], st.logical_rows(0, L)[40:, :KV])
