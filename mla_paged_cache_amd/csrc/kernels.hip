@@ -56,7 +56,10 @@ __device__ __forceinline__ chunk_t rotate_kpe(chunk_t v, bool on, int kc, const 
   }
 }
 
-// Flat gather.  Blocks [0, L * move_blocks_per_layer) move rows of fresh
+// Flat gather, two chunks per thread: block k of a layer covers chunks
+// 512 k .. 512 k + 511, thread t taking chunks 512 k + t and 512 k + 256 + t;
+// both loads are issued before either store, so a wave keeps twice the bytes
+// in flight.  Blocks [0, L * move_blocks_per_layer) move rows of fresh
 // pages.  Within one page-task of P rows the 72 * P chunks are ordered c_kv
 // first (chunk 64 * row + k, k < 64) and then k_pe (64 * P + 8 * row + k,
 // k < 8): for P >= 8 every wave is then either a pure copy wave or a pure
@@ -67,6 +70,7 @@ __device__ __forceinline__ chunk_t rotate_kpe(chunk_t v, bool on, int kc, const 
 // WAVE_TASK: page size >= 8.
 template <int PAIRING, bool WAVE_TASK>
 __global__ __launch_bounds__(kFlatThreads) void splice_kernel(SpliceLaunch a) {
+  constexpr int CPT = kSpliceChunksPerThread;
   const int64_t b = blockIdx.x;
   const int64_t move_blocks = a.move_blocks_per_layer * a.num_layers;
   const int64_t rot_blocks = a.rot_blocks_per_layer * a.num_layers;
@@ -78,62 +82,78 @@ __global__ __launch_bounds__(kFlatThreads) void splice_kernel(SpliceLaunch a) {
   const int64_t bb = in_place ? b - move_blocks : b;
   const int64_t bpl = in_place ? a.rot_blocks_per_layer : a.move_blocks_per_layer;
   const int l = static_cast<int>(bb / bpl);
-  const uint32_t c = static_cast<uint32_t>((bb - static_cast<int64_t>(l) * bpl) * kFlatThreads + threadIdx.x);
+  const uint32_t c0 = static_cast<uint32_t>((bb - static_cast<int64_t>(l) * bpl) * kFlatThreads * CPT + threadIdx.x);
   const int shift = a.page_shift;
   const uint32_t pmask = (1u << shift) - 1u;
   constexpr uint32_t kKpeChunks = kRowChunks - kKpeChunk0;
-
-  uint32_t task, r, col;
-  if (in_place) {
-    const uint32_t row_flat = c / kKpeChunks;
-    task = row_flat >> shift;
-    r = row_flat & pmask;
-    col = kKpeChunk0 + (c - row_flat * kKpeChunks);
-  } else {
-    task = (c / kRowChunks) >> shift;
-    const uint32_t lc = c - task * (static_cast<uint32_t>(kRowChunks) << shift);
-    const uint32_t ckv_chunks = static_cast<uint32_t>(kKpeChunk0) << shift;
-    if (lc < ckv_chunks) {
-      r = lc / kKpeChunk0;
-      col = lc - r * kKpeChunk0;
-    } else {
-      const uint32_t k = lc - ckv_chunks;
-      r = k / kKpeChunks;
-      col = kKpeChunk0 + (k - r * kKpeChunks);
-    }
-  }
-  const int64_t ti = static_cast<int64_t>(task) + (in_place ? a.n_move_tasks : 0);
-  const int64_t t_end = in_place ? a.n_move_tasks + a.n_rot_tasks : a.n_move_tasks;
-  bool live = ti < t_end;
-  const SpliceTask t = load_task<WAVE_TASK>(a.tasks, live ? ti : 0);
-  const int32_t j = (t.q << shift) + static_cast<int32_t>(r);
-  live = live && j < t.n_new;
-
   const chunk_t* layer = a.layers[l];
-  const int64_t dst_row = (static_cast<int64_t>(t.dst_page) << shift) + r;
-  const chunk_t* src;
-  bool rot = false;
-  if (in_place) {
-    src = layer + dst_row * kRowChunks;
-    rot = true;
-  } else if (j < t.s_start) {
-    src = layer + ((static_cast<int64_t>(t.pre_page) << shift) + (j & pmask)) * kRowChunks;
-  } else if (j < t.stub_end) {
-    src = t.stub + l * t.stub_layer_chunks + static_cast<int64_t>(j - t.s_start) * kRowChunks;
-  } else {
-    const int32_t o = j - t.delta;
-    const int32_t pg = ((o >> shift) == t.down_lp0) ? t.down_page0 : t.down_page1;
-    src = layer + ((static_cast<int64_t>(pg) << shift) + (o & pmask)) * kRowChunks;
-    rot = t.rotate != 0;
+  chunk_t v[CPT];
+  const chunk_t* srcs[CPT];
+  int64_t dsts[CPT];
+  bool lives[CPT], rots[CPT];
+  int kcs[CPT], dirs[CPT];
+#pragma unroll
+  for (int u = 0; u < CPT; ++u) {
+    const uint32_t c = c0 + u * kFlatThreads;
+    uint32_t task, r, col;
+    if (in_place) {
+      const uint32_t row_flat = c / kKpeChunks;
+      task = row_flat >> shift;
+      r = row_flat & pmask;
+      col = kKpeChunk0 + (c - row_flat * kKpeChunks);
+    } else {
+      task = (c / kRowChunks) >> shift;
+      const uint32_t lc = c - task * (static_cast<uint32_t>(kRowChunks) << shift);
+      const uint32_t ckv_chunks = static_cast<uint32_t>(kKpeChunk0) << shift;
+      if (lc < ckv_chunks) {
+        r = lc / kKpeChunk0;
+        col = lc - r * kKpeChunk0;
+      } else {
+        const uint32_t k = lc - ckv_chunks;
+        r = k / kKpeChunks;
+        col = kKpeChunk0 + (k - r * kKpeChunks);
+      }
+    }
+    const int64_t ti = static_cast<int64_t>(task) + (in_place ? a.n_move_tasks : 0);
+    const int64_t t_end = in_place ? a.n_move_tasks + a.n_rot_tasks : a.n_move_tasks;
+    bool live = ti < t_end;
+    const SpliceTask t = load_task<WAVE_TASK>(a.tasks, live ? ti : 0);
+    const int32_t j = (t.q << shift) + static_cast<int32_t>(r);
+    live = live && j < t.n_new;
+    const int64_t dst_row = (static_cast<int64_t>(t.dst_page) << shift) + r;
+    const chunk_t* src;
+    bool rot = false;
+    if (in_place) {
+      src = layer + dst_row * kRowChunks;
+      rot = true;
+    } else if (j < t.s_start) {
+      src = layer + ((static_cast<int64_t>(t.pre_page) << shift) + (j & pmask)) * kRowChunks;
+    } else if (j < t.stub_end) {
+      src = t.stub + l * t.stub_layer_chunks + static_cast<int64_t>(j - t.s_start) * kRowChunks;
+    } else {
+      const int32_t o = j - t.delta;
+      const int32_t pg = ((o >> shift) == t.down_lp0) ? t.down_page0 : t.down_page1;
+      src = layer + ((static_cast<int64_t>(pg) << shift) + (o & pmask)) * kRowChunks;
+      rot = t.rotate != 0;
+    }
+    srcs[u] = src + col;
+    dsts[u] = dst_row * kRowChunks + col;
+    lives[u] = live;
+    rots[u] = rot;
+    kcs[u] = static_cast<int>(col) - kKpeChunk0;
+    dirs[u] = t.dir;
   }
-  chunk_t v = chunk_t{0u, 0u, 0u, 0u};
-  if (live) v = __builtin_nontemporal_load(src + col);
-  const int kc = static_cast<int>(col) - kKpeChunk0;
-  if (!WAVE_TASK || kc >= 0) {
-    // k_pe waves (or mixed waves at page sizes below 8)
-    v = rotate_kpe<PAIRING>(v, live && rot && kc >= 0, kc, a.dirs + t.dir);
+#pragma unroll
+  for (int u = 0; u < CPT; ++u) {
+    v[u] = chunk_t{0u, 0u, 0u, 0u};
+    if (lives[u]) v[u] = __builtin_nontemporal_load(srcs[u]);
   }
-  if (live) __builtin_nontemporal_store(v, const_cast<chunk_t*>(layer) + dst_row * kRowChunks + col);
+#pragma unroll
+  for (int u = 0; u < CPT; ++u) {
+    if (!WAVE_TASK || kcs[u] >= 0)
+      v[u] = rotate_kpe<PAIRING>(v[u], lives[u] && rots[u] && kcs[u] >= 0, kcs[u], a.dirs + dirs[u]);
+    if (lives[u]) __builtin_nontemporal_store(v[u], const_cast<chunk_t*>(layer) + dsts[u]);
+  }
 }
 
 // Flat copy of the kept rows that land in fresh pages (rotation off), then

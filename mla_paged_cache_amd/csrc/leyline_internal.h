@@ -197,7 +197,14 @@ hipError_t launch_keep_scan(const ScanLaunch& a, hipStream_t s);
 hipError_t launch_gqa_splice(const GqaSpliceLaunch& a, int pairing, hipStream_t s);
 hipError_t launch_plane_evict(const PlaneEvictLaunch& a, hipStream_t s);
 
-// Blocks of kFlatThreads that cover `chunks` chunks of one layer.
-inline int64_t flat_blocks(int64_t chunks) { return (chunks + kFlatThreads - 1) / kFlatThreads; }
+// Chunks each thread of splice_kernel moves.
+constexpr int kSpliceChunksPerThread = 2;
+
+// Blocks of kFlatThreads that cover `chunks` chunks of one layer, each thread
+// taking `per_thread` of them.
+inline int64_t flat_blocks(int64_t chunks, int per_thread = 1) {
+  const int64_t per_block = int64_t{kFlatThreads} * per_thread;
+  return (chunks + per_block - 1) / per_block;
+}
 
 }  // namespace ll

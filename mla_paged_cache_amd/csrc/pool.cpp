@@ -1091,7 +1091,8 @@ ll_status leyline_splice(ll_pool* p, const ll_directive* dirs, int32_t n, void* 
     n_entries += static_cast<int64_t>(plans[i].reuse.size());
   }
   const int64_t row_chunks = p->row_bytes / 16;
-  if (n_move_tasks * P * row_chunks >= (int64_t{1} << 32) || n_rot_tasks * P * row_chunks >= (int64_t{1} << 32))
+  // chunk indices are 32-bit, with room for the last block's overhang
+  if (n_move_tasks * P * row_chunks >= (int64_t{1} << 32) - 1024 || n_rot_tasks * P * row_chunks >= (int64_t{1} << 32) - 1024)
     return fail(LL_EUNSUPPORTED, "one splice may write at most 2^32 16-byte chunks per layer");
   const size_t dir_bytes = p->gqa ? sizeof(ll::GqaDir) : sizeof(ll::SpliceDir);
 
@@ -1229,8 +1230,8 @@ ll_status leyline_splice(ll_pool* p, const ll_directive* dirs, int32_t n, void* 
     a.tasks = reinterpret_cast<const ll::SpliceTask*>(sg->dev + o_t);
     a.n_move_tasks = n_move_tasks;
     a.n_rot_tasks = n_rot_tasks;
-    a.move_blocks_per_layer = ll::flat_blocks(n_move_tasks * P * ll::kRowChunks);
-    a.rot_blocks_per_layer = ll::flat_blocks(n_rot_tasks * P * (ll::kRowChunks - ll::kKpeChunk0));
+    a.move_blocks_per_layer = ll::flat_blocks(n_move_tasks * P * ll::kRowChunks, ll::kSpliceChunksPerThread);
+    a.rot_blocks_per_layer = ll::flat_blocks(n_rot_tasks * P * (ll::kRowChunks - ll::kKpeChunk0), ll::kSpliceChunksPerThread);
     a.dirs = reinterpret_cast<const ll::SpliceDir*>(sg->dev + o_d);
     a.twrites = reinterpret_cast<const ll::TableWrite*>(sg->dev + o_w);
     a.tables = reinterpret_cast<const int32_t*>(sg->dev + o_p);
@@ -1426,7 +1427,7 @@ ll_status kv_evict_compact(ll_pool* p, const int32_t* seq_ids, int32_t n, const 
   stats.fresh_pages = need;
   stats.table_entries = static_cast<int64_t>(tp.packed.size());
   stats.alg_bytes = p->num_planes * 2 * p->row_bytes * stats.rows_moved;
-  if (static_cast<int64_t>(tasks.size()) * P * (p->row_bytes / 16) >= (int64_t{1} << 32))
+  if (static_cast<int64_t>(tasks.size()) * P * (p->row_bytes / 16) >= (int64_t{1} << 32) - 1024)
     return fail(LL_EUNSUPPORTED, "one eviction may move at most 2^32 16-byte chunks per layer");
 
   Staging* s2 = nullptr;
