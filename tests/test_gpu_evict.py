@@ -143,18 +143,21 @@ def test_ptable_reindex_matches_oracle():
 
 @pytest.mark.slow
 @pytest.mark.parametrize("P", [16, 1])
-def test_evict_256_rollouts_27_layers(P):
-    """256 rollouts x 16384 tokens x 27 layers, random turn drops, one call.
-    Page tables of all 256 compared; rows compared on layers 0 and 26 for 16
-    rollouts.  At page size 16 the pool also holds the fresh pages the call
-    needs (about 180 GB in all)."""
-    say(f"evict 256 x 16384 x 27, P={P}")
+@pytest.mark.parametrize("kind", ["turns", "sliding"])
+def test_evict_256_rollouts_27_layers(P, kind):
+    """256 rollouts x 16384 tokens x 27 layers, one call; keep masks: random
+    turn drops, or the sliding window that drops the oldest half.  Page tables
+    of all 256 compared; rows compared on layers 0 and 26 for 16 rollouts.  At
+    page size 16 the pool also holds the fresh pages the call needs (about
+    180 GB in all)."""
+    say(f"evict 256 x 16384 x 27, P={P}, {kind}")
     n_roll, n_tok = 256, 16384
     pages_per = n_tok // P
     extra = int(0.5 * n_roll * pages_per) if P == 16 else 0
     dp = _rollouts(27, n_roll, n_tok, P, seed=0, extra_pages=extra, oracle_layers=[], host_rows=False)
     rng = np_rng(0, 6)
-    masks = [turn_drop_mask(rng, n_tok) for _ in range(n_roll)]
+    masks = [turn_drop_mask(rng, n_tok) if kind == "turns" else sliding_window_mask(n_tok, n_tok // 2)
+             for _ in range(n_roll)]
     # rows of 16 rollouts on two layers, captured before the call
     check = list(range(0, n_roll, 16))
     before = {}

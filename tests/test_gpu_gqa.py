@@ -192,17 +192,19 @@ def test_gqa_llama8b_shape_32k_splice():
     dp.close()
 
 
-@pytest.mark.parametrize("P", [16, 1])
-def test_gqa_evict_turn_drops(P):
+@pytest.mark.parametrize("P,plan", [(16, "device"), (16, "host"), (1, "device")])
+def test_gqa_evict_turn_drops(P, plan):
     """KV-streams eviction on a GQA pool: two sequences of 4096 tokens, random
-    turn drops; K and V rows move unchanged."""
-    say(f"gqa evict P={P}")
+    turn drops; K and V rows move unchanged.  With free pages for every page of
+    both sequences the device makes the page plan, with fewer the host."""
+    say(f"gqa evict P={P}, {plan} plan")
     L_ = need_gpu()
     H, D, rot = 8, 64, 64
     n = 4096
     pages = n // P
-    dp = GqaDevicePool(2, 2 * pages + 2 * pages + 16, P, 2, pages, H, D, rot, seed=8 + P)
-    perm = permuted_pages(8, 4 * pages + 16)
+    extra = 2 * pages + 16 if plan == "device" else pages
+    dp = GqaDevicePool(2, 2 * pages + extra, P, 2, pages, H, D, rot, seed=8 + P)
+    perm = permuted_pages(8, 2 * pages + extra)
     dp.set_pages(0, perm[:pages], n)
     dp.set_pages(1, perm[pages:2 * pages], n)
     dp.snapshot_rows()
