@@ -118,6 +118,13 @@ def quiet_gc():
     gc.disable()
 
 
+def prof_every(steps: int) -> int:
+    """Time about a dozen launches, spread evenly over the timed region: each
+    timed launch costs the stream a few microseconds of event stamps, which
+    would otherwise be charged to every step."""
+    return max(1, steps // 12)
+
+
 def copy_ceiling(torch, dev, n_bytes):
     """Plain device copy of n_bytes (read + write), for context."""
     src = torch.empty(n_bytes, dtype=torch.uint8, device=dev)
@@ -147,6 +154,7 @@ def roofline(kernel, workload, launches, kernel_ms, kernel_bytes):
         "traffic": profiled_traffic(kernel, workload),
         "kernel": kernel,
         "kernel_avg_us": round(k_avg_ms * 1e3, 2),
+        "timed_launches": launches,
         "bytes_per_launch": per,
     }
 
@@ -212,7 +220,7 @@ def bench_splice_32k(args):
         pool.splice(directive)
     torch.cuda.synchronize()
     pool.profile_read(0)
-    pool.set_profiling(True)
+    pool.set_profiling(True, prof_every(args.steps))
     torch.cuda.synchronize()
     quiet_gc()
     t0 = time.perf_counter()
@@ -328,7 +336,7 @@ def bench_splice_batched(args):
         pool.splice(dirs)
     torch.cuda.synchronize()
     pool.profile_read(0)
-    pool.set_profiling(True)
+    pool.set_profiling(True, prof_every(args.steps))
     quiet_gc()
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -383,7 +391,7 @@ def bench_splice_gqa(args):
         pool.splice(directive)
     torch.cuda.synchronize()
     pool.profile_read(0)
-    pool.set_profiling(True)
+    pool.set_profiling(True, prof_every(args.steps))
     quiet_gc()
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -437,7 +445,7 @@ def bench_rope_rows(args):
             pool.rope_rows(0, 0, angles, out=None if in_place else out)
         torch.cuda.synchronize()
         pool.profile_read(2)
-        pool.set_profiling(True)
+        pool.set_profiling(True, prof_every(args.steps))
         quiet_gc()
         t0 = time.perf_counter()
         for _ in range(args.steps):
@@ -591,7 +599,7 @@ def bench_evict(args, page):
         restore()
         torch.cuda.synchronize()
         if i == args.warmup:
-            pool.set_profiling(True)
+            pool.set_profiling(True, prof_every(args.steps))
         a = time.perf_counter()
         pool.evict(seqs, keep, offsets)
         b = time.perf_counter()

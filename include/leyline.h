@@ -287,9 +287,14 @@ ll_status ll_rope_delta_table(double base, int32_t rope_dim, int64_t delta,
 /* Counters of the last splice / evict / reindex call.  Errors: LL_EINVAL. */
 ll_status ll_last_plan_stats(const ll_pool* pool, ll_plan_stats* out);
 
-/* Kernel timing: while enabled, HIP events bracket every launch of the
- * row-moving kernel (kernel 0), of the keep-mask scan (kernel 1) and of the
- * per-row rotation (kernel 2: its table and row kernels together).
+/* Kernel timing.  `enable` = n > 0 times every n-th launch (counted from
+ * this call; 1: every launch) of the row-moving kernel (kernel 0; on the
+ * device-planned eviction path its page-plan kernels too), of the keep-mask
+ * scan (kernel 1) and of the per-row rotation (kernel 2: its table and row
+ * kernels together); 0 stops timing.  A timed launch gets a pair of HIP
+ * events that it stamps from its own dispatch packets (the start of its
+ * first kernel, the end of its last); the stamps still cost the stream a few
+ * microseconds per timed launch, hence the sampling.
  * ll_profile_read waits for the recorded events, returns the launch count,
  * the summed milliseconds and the summed algorithmic bytes of `kernel`, and
  * clears its record.  Errors: LL_EINVAL, LL_EDEVICE. */

@@ -35,7 +35,7 @@ struct DevMoveLaunch {
   const int32_t* src_rows;
 };
 
-hipError_t launch_alloc(const AllocLaunch& a, hipStream_t s);
-hipError_t launch_dev_move(const DevMoveLaunch& a, int64_t chunk_bound, hipStream_t s);
+hipError_t launch_alloc(const AllocLaunch& a, hipStream_t s, const Stamp& t = Stamp{});
+hipError_t launch_dev_move(const DevMoveLaunch& a, int64_t chunk_bound, hipStream_t s, const Stamp& t = Stamp{});
 
 }  // namespace ll

@@ -5,10 +5,35 @@
 // page-table row rewrite.
 #pragma once
 
+#include <hip/hip_ext.h>
+
 #include "leyline_internal.h"
 
 namespace ll {
 namespace {
+
+// Launch `k` on `s`.  With events to stamp (the stamp's start if this is the
+// launcher's first kernel, its stop if the last) the launch goes through the
+// extended form, which takes them from this dispatch's own packet.
+template <typename A>
+hipError_t dispatch(void (*k)(A), dim3 g, dim3 b, hipStream_t s, const Stamp& t, bool first, bool last,
+                    const A& a) {
+  hipEvent_t start = first ? t.start : nullptr;
+  hipEvent_t stop = last ? t.stop : nullptr;
+  if (start || stop)
+    hipExtLaunchKernelGGL(k, g, b, 0, s, start, stop, 0, a);
+  else
+    k<<<g, b, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+// A launcher with nothing to launch still leaves its events recorded.
+inline hipError_t stamp_empty(hipStream_t s, const Stamp& t) {
+  hipError_t e = hipSuccess;
+  if (t.start) e = hipEventRecord(t.start, s);
+  if (e == hipSuccess && t.stop) e = hipEventRecord(t.stop, s);
+  return e;
+}
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }

@@ -269,29 +269,24 @@ __global__ __launch_bounds__(kScanThreads) void keep_scan_kernel(ScanLaunch a) {
 
 }  // namespace
 
-hipError_t launch_splice(const SpliceLaunch& a, int pairing, hipStream_t s) {
+hipError_t launch_splice(const SpliceLaunch& a, int pairing, hipStream_t s, const Stamp& t) {
   const int64_t grid = (a.move_blocks_per_layer + a.rot_blocks_per_layer) * a.num_layers + a.n_twrites;
-  if (grid == 0) return hipSuccess;
+  if (grid == 0) return stamp_empty(s, t);
   const dim3 g(static_cast<unsigned>(grid)), blk(kFlatThreads);
   const bool wave_task = a.page_shift >= 3;
-  if (pairing == 0) {
-    if (wave_task) splice_kernel<0, true><<<g, blk, 0, s>>>(a);
-    else splice_kernel<0, false><<<g, blk, 0, s>>>(a);
-  } else {
-    if (wave_task) splice_kernel<1, true><<<g, blk, 0, s>>>(a);
-    else splice_kernel<1, false><<<g, blk, 0, s>>>(a);
-  }
-  return hipGetLastError();
+  void (*k)(SpliceLaunch);
+  if (pairing == 0)
+    k = wave_task ? splice_kernel<0, true> : splice_kernel<0, false>;
+  else
+    k = wave_task ? splice_kernel<1, true> : splice_kernel<1, false>;
+  return dispatch(k, g, blk, s, t, true, true, a);
 }
 
-hipError_t launch_evict_move(const EvictLaunch& a, hipStream_t s) {
+hipError_t launch_evict_move(const EvictLaunch& a, hipStream_t s, const Stamp& t) {
   const int64_t grid = a.blocks_per_layer * a.num_layers + a.n_twrites;
-  if (grid == 0) return hipSuccess;
-  if (a.page_shift >= 3)
-    evict_move_kernel<true><<<dim3(static_cast<unsigned>(grid)), dim3(kFlatThreads), 0, s>>>(a);
-  else
-    evict_move_kernel<false><<<dim3(static_cast<unsigned>(grid)), dim3(kFlatThreads), 0, s>>>(a);
-  return hipGetLastError();
+  if (grid == 0) return stamp_empty(s, t);
+  void (*k)(EvictLaunch) = a.page_shift >= 3 ? evict_move_kernel<true> : evict_move_kernel<false>;
+  return dispatch(k, dim3(static_cast<unsigned>(grid)), dim3(kFlatThreads), s, t, true, true, a);
 }
 
 hipError_t launch_table_write(const TableLaunch& a, hipStream_t s) {
@@ -300,10 +295,9 @@ hipError_t launch_table_write(const TableLaunch& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_keep_scan(const ScanLaunch& a, hipStream_t s) {
-  if (a.n_seqs == 0) return hipSuccess;
-  keep_scan_kernel<<<dim3(a.n_seqs), dim3(kScanThreads), 0, s>>>(a);
-  return hipGetLastError();
+hipError_t launch_keep_scan(const ScanLaunch& a, hipStream_t s, const Stamp& t) {
+  if (a.n_seqs == 0) return stamp_empty(s, t);
+  return dispatch(keep_scan_kernel, dim3(a.n_seqs), dim3(kScanThreads), s, t, true, true, a);
 }
 
 }  // namespace ll

@@ -169,30 +169,24 @@ __global__ __launch_bounds__(256) void dev_move_kernel(DevMoveLaunch a) {
 
 }  // namespace
 
-hipError_t launch_alloc(const AllocLaunch& a, hipStream_t s) {
-  if (a.n == 0) return hipSuccess;
-  fresh_rank_kernel<<<dim3(a.n), dim3(kScanThreads), 0, s>>>(a);
-  hipError_t e = hipGetLastError();
+hipError_t launch_alloc(const AllocLaunch& a, hipStream_t s, const Stamp& t) {
+  if (a.n == 0) return stamp_empty(s, t);
+  hipError_t e = dispatch(fresh_rank_kernel, dim3(a.n), dim3(kScanThreads), s, t, true, false, a);
   if (e != hipSuccess) return e;
-  alloc_scan_kernel<<<dim3(1), dim3(kScanThreads), 0, s>>>(a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  alloc_tables_kernel<<<dim3(a.n), dim3(256), 0, s>>>(a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  table_copy_kernel<<<dim3(a.n), dim3(256), 0, s>>>(a);
-  return hipGetLastError();
+  if ((e = dispatch(alloc_scan_kernel, dim3(1), dim3(kScanThreads), s, t, false, false, a)) != hipSuccess) return e;
+  if ((e = dispatch(alloc_tables_kernel, dim3(a.n), dim3(256), s, t, false, false, a)) != hipSuccess) return e;
+  return dispatch(table_copy_kernel, dim3(a.n), dim3(256), s, t, false, true, a);
 }
 
-hipError_t launch_dev_move(const DevMoveLaunch& a, int64_t chunk_bound, hipStream_t s) {
-  if (a.num_planes == 0 || chunk_bound == 0) return hipSuccess;
+hipError_t launch_dev_move(const DevMoveLaunch& a, int64_t chunk_bound, hipStream_t s, const Stamp& t) {
+  if (a.num_planes == 0 || chunk_bound == 0) return stamp_empty(s, t);
   // enough blocks to fill the chip several times over; each strides over the rest
   const int64_t want = (chunk_bound + 255) / 256;
   const unsigned gx = static_cast<unsigned>(want < 2048 ? want : 2048);
   const dim3 grid(gx, static_cast<unsigned>(a.num_planes));
-  if ((int64_t{a.row_chunks} << a.page_shift) % 64 == 0)
-    dev_move_kernel<true><<<grid, dim3(256), 0, s>>>(a);
-  else
-    dev_move_kernel<false><<<grid, dim3(256), 0, s>>>(a);
-  return hipGetLastError();
+  void (*k)(DevMoveLaunch) =
+      (int64_t{a.row_chunks} << a.page_shift) % 64 == 0 ? dev_move_kernel<true> : dev_move_kernel<false>;
+  return dispatch(k, grid, dim3(256), s, t, true, true, a);
 }
 
 }  // namespace ll

@@ -220,9 +220,9 @@ __global__ __launch_bounds__(kFlatThreads) void plane_evict_kernel(PlaneEvictLau
 
 }  // namespace
 
-hipError_t launch_gqa_splice(const GqaSpliceLaunch& a, int pairing, hipStream_t s) {
+hipError_t launch_gqa_splice(const GqaSpliceLaunch& a, int pairing, hipStream_t s, const Stamp& t) {
   const int64_t grid = (a.move_blocks_k + a.move_blocks_v + a.rot_blocks_per_plane) * a.num_layers + a.n_twrites;
-  if (grid == 0) return hipSuccess;
+  if (grid == 0) return stamp_empty(s, t);
   const dim3 g(static_cast<unsigned>(grid)), blk(kFlatThreads);
   // one task per wave (per block) when a page's units are a whole number of
   // waves (blocks) in both the move and the in-place ranges
@@ -232,26 +232,22 @@ hipError_t launch_gqa_splice(const GqaSpliceLaunch& a, int pairing, hipStream_t 
   const bool wave_task = move_units % 64 == 0 && band_units % 64 == 0;
   const bool block_task = move_units % kFlatThreads == 0 && band_units % kFlatThreads == 0 &&
                           v_chunks % kFlatThreads == 0;
-  if (pairing == 0) {
-    if (block_task) gqa_splice_kernel<0, true, true><<<g, blk, 0, s>>>(a);
-    else if (wave_task) gqa_splice_kernel<0, true, false><<<g, blk, 0, s>>>(a);
-    else gqa_splice_kernel<0, false, false><<<g, blk, 0, s>>>(a);
-  } else {
-    if (block_task) gqa_splice_kernel<1, true, true><<<g, blk, 0, s>>>(a);
-    else if (wave_task) gqa_splice_kernel<1, true, false><<<g, blk, 0, s>>>(a);
-    else gqa_splice_kernel<1, false, false><<<g, blk, 0, s>>>(a);
-  }
-  return hipGetLastError();
+  void (*k)(GqaSpliceLaunch);
+  if (pairing == 0)
+    k = block_task ? gqa_splice_kernel<0, true, true>
+        : wave_task ? gqa_splice_kernel<0, true, false> : gqa_splice_kernel<0, false, false>;
+  else
+    k = block_task ? gqa_splice_kernel<1, true, true>
+        : wave_task ? gqa_splice_kernel<1, true, false> : gqa_splice_kernel<1, false, false>;
+  return dispatch(k, g, blk, s, t, true, true, a);
 }
 
-hipError_t launch_plane_evict(const PlaneEvictLaunch& a, hipStream_t s) {
+hipError_t launch_plane_evict(const PlaneEvictLaunch& a, hipStream_t s, const Stamp& t) {
   const int64_t grid = a.blocks_per_plane * a.num_planes + a.n_twrites;
-  if (grid == 0) return hipSuccess;
-  if ((int64_t{a.row_chunks} << a.page_shift) % 64 == 0)
-    plane_evict_kernel<true><<<dim3(static_cast<unsigned>(grid)), dim3(kFlatThreads), 0, s>>>(a);
-  else
-    plane_evict_kernel<false><<<dim3(static_cast<unsigned>(grid)), dim3(kFlatThreads), 0, s>>>(a);
-  return hipGetLastError();
+  if (grid == 0) return stamp_empty(s, t);
+  void (*k)(PlaneEvictLaunch) =
+      (int64_t{a.row_chunks} << a.page_shift) % 64 == 0 ? plane_evict_kernel<true> : plane_evict_kernel<false>;
+  return dispatch(k, dim3(static_cast<unsigned>(grid)), dim3(kFlatThreads), s, t, true, true, a);
 }
 
 }  // namespace ll

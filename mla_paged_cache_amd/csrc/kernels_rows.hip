@@ -120,21 +120,17 @@ __global__ __launch_bounds__(256) void rope_rows_kernel(RopeRowsLaunch a) {
 
 }  // namespace
 
-hipError_t launch_rope_table(const RopeTableLaunch& a, hipStream_t s) {
-  const int64_t t = a.n * a.pairs;
-  if (t == 0) return hipSuccess;
-  rope_table_kernel<<<dim3(static_cast<unsigned>((t + 255) / 256)), dim3(256), 0, s>>>(a);
-  return hipGetLastError();
+hipError_t launch_rope_table(const RopeTableLaunch& a, hipStream_t s, const Stamp& t) {
+  const int64_t pairs = a.n * a.pairs;
+  if (pairs == 0) return stamp_empty(s, t);
+  return dispatch(rope_table_kernel, dim3(static_cast<unsigned>((pairs + 255) / 256)), dim3(256), s, t, true, true, a);
 }
 
-hipError_t launch_rope_rows(const RopeRowsLaunch& a, int pairing, hipStream_t s) {
+hipError_t launch_rope_rows(const RopeRowsLaunch& a, int pairing, hipStream_t s, const Stamp& t) {
   const int64_t grid = a.blocks_per_plane * a.num_planes;
-  if (grid == 0) return hipSuccess;
-  if (pairing == 0)
-    rope_rows_kernel<0><<<dim3(static_cast<unsigned>(grid)), dim3(256), 0, s>>>(a);
-  else
-    rope_rows_kernel<1><<<dim3(static_cast<unsigned>(grid)), dim3(256), 0, s>>>(a);
-  return hipGetLastError();
+  if (grid == 0) return stamp_empty(s, t);
+  void (*k)(RopeRowsLaunch) = pairing == 0 ? rope_rows_kernel<0> : rope_rows_kernel<1>;
+  return dispatch(k, dim3(static_cast<unsigned>(grid)), dim3(256), s, t, true, true, a);
 }
 
 }  // namespace ll

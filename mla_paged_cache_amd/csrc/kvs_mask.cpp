@@ -155,6 +155,7 @@ ll_status kvs_death_times(kvs_ctx* c, const kvs_rollout_log* logs, int32_t n, in
     if (hipHostMalloc(reinterpret_cast<void**>(&c->host), cap, hipHostMallocDefault) != hipSuccess ||
         hipMalloc(reinterpret_cast<void**>(&c->dev), cap) != hipSuccess)
       return fail(LL_ENOMEM, "cannot allocate %zu bytes of staging", cap);
+    std::memset(c->host, 0, cap);  // fault the pinned pages in once
     c->cap = cap;
   }
   ll::KvsRollout* rolls = reinterpret_cast<ll::KvsRollout*>(c->host);

@@ -189,13 +189,22 @@ struct ScanLaunch {
   int32_t* reuse;              // out: per new page, the old logical page it keeps, or -1
 };
 
+// Timing events a launcher stamps from the dispatch packets themselves (no
+// marker packets of their own on the stream): `start` gets the start time of
+// the first kernel it launches, `stop` the end time of the last one.  Null
+// events are left alone.  A launcher that has no work records both at once.
+struct Stamp {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+
 // Launchers (kernels.hip).
-hipError_t launch_splice(const SpliceLaunch& a, int pairing, hipStream_t s);
-hipError_t launch_evict_move(const EvictLaunch& a, hipStream_t s);
+hipError_t launch_splice(const SpliceLaunch& a, int pairing, hipStream_t s, const Stamp& t = Stamp{});
+hipError_t launch_evict_move(const EvictLaunch& a, hipStream_t s, const Stamp& t = Stamp{});
 hipError_t launch_table_write(const TableLaunch& a, hipStream_t s);
-hipError_t launch_keep_scan(const ScanLaunch& a, hipStream_t s);
-hipError_t launch_gqa_splice(const GqaSpliceLaunch& a, int pairing, hipStream_t s);
-hipError_t launch_plane_evict(const PlaneEvictLaunch& a, hipStream_t s);
+hipError_t launch_keep_scan(const ScanLaunch& a, hipStream_t s, const Stamp& t = Stamp{});
+hipError_t launch_gqa_splice(const GqaSpliceLaunch& a, int pairing, hipStream_t s, const Stamp& t = Stamp{});
+hipError_t launch_plane_evict(const PlaneEvictLaunch& a, hipStream_t s, const Stamp& t = Stamp{});
 
 // Chunks each thread of splice_kernel moves.
 constexpr int kSpliceChunksPerThread = 2;

@@ -190,7 +190,8 @@ struct ll_pool {
   hipStream_t last_stream = nullptr;  // the stream that work ran on
   bool poisoned = false;
   ll_plan_stats last{};
-  bool profiling = false;
+  int32_t prof_every = 0;       // time every n-th launch of each kernel (0: none)
+  int64_t prof_tick[3] = {0, 0, 0};
   std::vector<ProfRec> prof[3];  // row-moving kernel, keep scan, per-row rotation
   std::vector<hipEvent_t> spare_events;
   std::vector<int32_t> page_slot;  // per physical page: scratch marks of ll_seq_set_pages
@@ -309,7 +310,9 @@ hipEvent_t take_event(ll_pool* p) {
     return e;
   }
   hipEvent_t e = nullptr;
-  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  // timing only: the host never reads device results behind these, so they
+  // skip the system-scope fence (a cache writeback and invalidate per event)
+  if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
   return e;
 }
 
@@ -354,6 +357,7 @@ ll_status stage_acquire(ll_pool* p, size_t bytes, Staging** out) {
     if (hipHostMalloc(reinterpret_cast<void**>(&p->ring_host), cap, hipHostMallocDefault) != hipSuccess ||
         hipMalloc(reinterpret_cast<void**>(&p->ring_dev), cap) != hipSuccess)
       return fail(LL_ENOMEM, "cannot allocate %zu bytes of staging", cap);
+    std::memset(p->ring_host, 0, cap);  // fault the pages in now, not call by call
     p->ring_cap = cap;
     p->ring_head = 0;
   }
@@ -411,7 +415,10 @@ ll_status end_call(ll_pool* p, Staging* s, hipStream_t st) {
     ev = p->ring_events.back();
     p->ring_events.pop_back();
   } else {
-    hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+    // These mark when the device has finished reading a staging region and
+    // order calls across streams of this device; the host never reads device
+    // results behind them, so they skip the system-scope fence.
+    hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableTiming | hipEventDisableSystemFence);
     if (e != hipSuccess) return device_fail(p, e, "hipEventCreate(staging)");
   }
   hipError_t e = hipEventRecord(ev, st);
@@ -502,22 +509,24 @@ ll_status write_tables(ll_pool* p, const TablePlan& tp, hipStream_t st) {
   return end_call(p, s, st);
 }
 
-ll_status prof_begin(ll_pool* p, int kernel, hipStream_t st, ProfRec* rec) {
+// Whether this launch of `kernel` is timed: every prof_every-th one.
+bool prof_pick(ll_pool* p, int kernel) {
+  if (p->prof_every <= 0) return false;
+  return p->prof_tick[kernel]++ % p->prof_every == 0;
+}
+
+// A timed launch takes two events; its launcher stamps them from the dispatch
+// packets, so timing adds no packets of its own to the stream.
+ll_status prof_begin(ll_pool* p, ProfRec* rec, ll::Stamp* t) {
   rec->start = take_event(p);
   rec->stop = take_event(p);
   if (!rec->start || !rec->stop) return fail(LL_EDEVICE, "hipEventCreate failed");
-  (void)kernel;
-  hipError_t e = hipEventRecord(rec->start, st);
-  if (e != hipSuccess) return device_fail(p, e, "hipEventRecord(profile)");
+  t->start = rec->start;
+  t->stop = rec->stop;
   return LL_OK;
 }
 
-ll_status prof_end(ll_pool* p, int kernel, hipStream_t st, ProfRec* rec) {
-  hipError_t e = hipEventRecord(rec->stop, st);
-  if (e != hipSuccess) return device_fail(p, e, "hipEventRecord(profile)");
-  p->prof[kernel].push_back(*rec);
-  return LL_OK;
-}
+void prof_end(ll_pool* p, int kernel, const ProfRec& rec) { p->prof[kernel].push_back(rec); }
 
 // ------------------------------------------------------------------ splice --
 
@@ -595,6 +604,7 @@ ll_status ensure_evict_buffers(ll_pool* p, size_t scratch, size_t readback) {
     p->readback_cap = 0;
     if (hipHostMalloc(reinterpret_cast<void**>(&p->h_readback), readback, hipHostMallocDefault) != hipSuccess)
       return fail(LL_ENOMEM, "cannot allocate %zu bytes of pinned readback", readback);
+    std::memset(p->h_readback, 0, readback);
     p->readback_cap = readback;
   }
   return LL_OK;
@@ -653,12 +663,13 @@ ll_status evict_device_plan(ll_pool* p, const int32_t* seq_ids, int32_t n, const
   sc.src_rows = reinterpret_cast<int32_t*>(d + off_src);
   sc.src_logical = reinterpret_cast<int32_t*>(d + off_logical);
   ProfRec rec1{};
-  if (p->profiling && (rc = prof_begin(p, 1, st, &rec1))) return rc;
-  hipError_t e = ll::launch_keep_scan(sc, st);
+  ll::Stamp t1;
+  if (prof_pick(p, 1) && (rc = prof_begin(p, &rec1, &t1))) return rc;
+  hipError_t e = ll::launch_keep_scan(sc, st, t1);
   if (e != hipSuccess) return device_fail(p, e, "keep_scan_kernel launch");
-  if (p->profiling) {
+  if (rec1.start) {
     rec1.bytes = total_rows + 4 * total_rows;
-    if ((rc = prof_end(p, 1, st, &rec1))) return rc;
+    prof_end(p, 1, rec1);
   }
 
   ll::AllocLaunch al{};
@@ -680,8 +691,10 @@ ll_status evict_device_plan(ll_pool* p, const int32_t* seq_ids, int32_t n, const
   al.info = reinterpret_cast<int32_t*>(d + off_info);
   // kernel 0's record covers the page plan and the row moves of this path
   ProfRec rec{};
-  if (p->profiling && (rc = prof_begin(p, 0, st, &rec))) return rc;
-  if ((e = ll::launch_alloc(al, st)) != hipSuccess) return device_fail(p, e, "page allocator launch");
+  ll::Stamp t0;
+  if (prof_pick(p, 0) && (rc = prof_begin(p, &rec, &t0))) return rc;
+  if ((e = ll::launch_alloc(al, st, ll::Stamp{t0.start, nullptr})) != hipSuccess)
+    return device_fail(p, e, "page allocator launch");
 
   ll::DevMoveLaunch mv{};
   mv.planes = reinterpret_cast<const ll::chunk_t* const*>(p->d_layers);
@@ -692,11 +705,12 @@ ll_status evict_device_plan(ll_pool* p, const int32_t* seq_ids, int32_t n, const
   mv.info = al.info;
   mv.src_rows = sc.src_rows;
   const int64_t chunk_bound = P == 1 ? 0 : total_pages * P * rc_chunks;
-  if ((e = ll::launch_dev_move(mv, chunk_bound, st)) != hipSuccess) return device_fail(p, e, "dev_move_kernel launch");
+  if ((e = ll::launch_dev_move(mv, chunk_bound, st, ll::Stamp{nullptr, t0.stop})) != hipSuccess)
+    return device_fail(p, e, "dev_move_kernel launch");
   int64_t prof_index = -1;
-  if (p->profiling) {
+  if (rec.start) {
     rec.bytes = 0;  // known when the call settles
-    if ((rc = prof_end(p, 0, st, &rec))) return rc;
+    prof_end(p, 0, rec);
     prof_index = static_cast<int64_t>(p->prof[0].size()) - 1;
   }
   e = hipMemcpyAsync(p->h_readback, d, readback, hipMemcpyDeviceToHost, st);
@@ -839,6 +853,9 @@ ll_status setup_pool(ll_pool* p, ll_pool** out) {
   if (e == hipSuccess) e = hipStreamCreateWithFlags(&p->copy_stream, hipStreamNonBlocking);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&p->upload_ev, hipEventDisableTiming);
   if (e == hipSuccess) e = hipHostMalloc(reinterpret_cast<void**>(&p->ring_host), kRingBytes, hipHostMallocDefault);
+  // touch every page now: first writes to fresh pinned pages fault one page
+  // at a time (tens of microseconds per call while the ring is new)
+  if (e == hipSuccess) std::memset(p->ring_host, 0, kRingBytes);
   if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void**>(&p->ring_dev), kRingBytes);
   if (e == hipSuccess) p->ring_cap = kRingBytes;
   if (e != hipSuccess) {
@@ -1195,6 +1212,7 @@ ll_status leyline_splice(ll_pool* p, const ll_directive* dirs, int32_t n, void* 
   stats.alg_bytes = p->num_planes * 2 * p->row_bytes * stats.rows_moved + L * 2 * p->band_bytes * stats.rows_rotated_inplace;
   if ((rc = upload(p, sg, st))) return rc;
   ProfRec rec{};
+  ll::Stamp ts;
   hipError_t e;
   if (p->gqa) {
     ll::GqaSpliceLaunch a{};
@@ -1219,8 +1237,8 @@ ll_status leyline_splice(ll_pool* p, const ll_directive* dirs, int32_t n, void* 
     a.n_twrites = n;
     a.max_pages_per_seq = p->desc.max_pages_per_seq;
     a.page_table = p->desc.page_table;
-    if (p->profiling && (rc = prof_begin(p, 0, st, &rec))) return rc;
-    e = ll::launch_gqa_splice(a, p->desc.rope_pairing, st);
+    if (prof_pick(p, 0) && (rc = prof_begin(p, &rec, &ts))) return rc;
+    e = ll::launch_gqa_splice(a, p->desc.rope_pairing, st, ts);
     if (e != hipSuccess) return device_fail(p, e, "gqa_splice_kernel launch");
   } else {
     ll::SpliceLaunch a{};
@@ -1238,13 +1256,13 @@ ll_status leyline_splice(ll_pool* p, const ll_directive* dirs, int32_t n, void* 
     a.n_twrites = n;
     a.max_pages_per_seq = p->desc.max_pages_per_seq;
     a.page_table = p->desc.page_table;
-    if (p->profiling && (rc = prof_begin(p, 0, st, &rec))) return rc;
-    e = ll::launch_splice(a, p->desc.rope_pairing, st);
+    if (prof_pick(p, 0) && (rc = prof_begin(p, &rec, &ts))) return rc;
+    e = ll::launch_splice(a, p->desc.rope_pairing, st, ts);
     if (e != hipSuccess) return device_fail(p, e, "splice_kernel launch");
   }
-  if (p->profiling) {
+  if (rec.start) {
     rec.bytes = stats.alg_bytes + 4 * stats.table_entries;
-    if ((rc = prof_end(p, 0, st, &rec))) return rc;
+    prof_end(p, 0, rec);
   }
   if ((rc = end_call(p, sg, st))) return rc;
 
@@ -1354,17 +1372,20 @@ ll_status kv_evict_compact(ll_pool* p, const int32_t* seq_ids, int32_t n, const 
   sc.src_rows = reinterpret_cast<int32_t*>(p->d_scratch + off_src);
   sc.src_logical = reinterpret_cast<int32_t*>(p->d_scratch + off_logical);
   ProfRec rec1{};
-  if (p->profiling && (rc = prof_begin(p, 1, st, &rec1))) return rc;
-  hipError_t e = ll::launch_keep_scan(sc, st);
+  ll::Stamp t1;
+  if (prof_pick(p, 1) && (rc = prof_begin(p, &rec1, &t1))) return rc;
+  hipError_t e = ll::launch_keep_scan(sc, st, t1);
   if (e != hipSuccess) return fail(LL_EDEVICE, "keep_scan_kernel launch: %s", hipGetErrorString(e));
-  if (p->profiling) {
+  if (rec1.start) {
     rec1.bytes = total_rows + 4 * total_rows;
-    if ((rc = prof_end(p, 1, st, &rec1))) return rc;
+    prof_end(p, 1, rec1);
   }
   e = hipMemcpyAsync(p->h_readback, p->d_scratch, readback, hipMemcpyDeviceToHost, st);
   if (e != hipSuccess) return fail(LL_EDEVICE, "eviction readback: %s", hipGetErrorString(e));
   if ((rc = end_call(p, s1, st))) return rc;
-  e = hipEventSynchronize(p->last_done);
+  // the host reads the readback next: wait on an event with the system fence
+  e = hipEventRecord(p->readback_ev, st);
+  if (e == hipSuccess) e = hipEventSynchronize(p->readback_ev);
   if (e != hipSuccess) return fail(LL_EDEVICE, "eviction readback: %s", hipGetErrorString(e));
   // Nothing has changed yet: the scan only wrote scratch.
 
@@ -1442,6 +1463,7 @@ ll_status kv_evict_compact(ll_pool* p, const int32_t* seq_ids, int32_t n, const 
   const int64_t row_chunks = p->row_bytes / 16;
   const int64_t n_tasks = static_cast<int64_t>(tasks.size());
   ProfRec rec{};
+  ll::Stamp ts;
   if (p->gqa) {
     ll::PlaneEvictLaunch a{};
     a.planes = reinterpret_cast<const ll::chunk_t* const*>(p->d_layers);
@@ -1457,8 +1479,8 @@ ll_status kv_evict_compact(ll_pool* p, const int32_t* seq_ids, int32_t n, const 
     a.n_twrites = static_cast<int32_t>(tp.writes.size());
     a.max_pages_per_seq = p->desc.max_pages_per_seq;
     a.page_table = p->desc.page_table;
-    if (p->profiling && (rc = prof_begin(p, 0, st, &rec))) return rc;
-    e = ll::launch_plane_evict(a, st);
+    if (prof_pick(p, 0) && (rc = prof_begin(p, &rec, &ts))) return rc;
+    e = ll::launch_plane_evict(a, st, ts);
     if (e != hipSuccess) return device_fail(p, e, "plane_evict_kernel launch");
   } else {
     ll::EvictLaunch a{};
@@ -1474,13 +1496,13 @@ ll_status kv_evict_compact(ll_pool* p, const int32_t* seq_ids, int32_t n, const 
     a.n_twrites = static_cast<int32_t>(tp.writes.size());
     a.max_pages_per_seq = p->desc.max_pages_per_seq;
     a.page_table = p->desc.page_table;
-    if (p->profiling && (rc = prof_begin(p, 0, st, &rec))) return rc;
-    e = ll::launch_evict_move(a, st);
+    if (prof_pick(p, 0) && (rc = prof_begin(p, &rec, &ts))) return rc;
+    e = ll::launch_evict_move(a, st, ts);
     if (e != hipSuccess) return device_fail(p, e, "evict_move_kernel launch");
   }
-  if (p->profiling) {
+  if (rec.start) {
     rec.bytes = stats.alg_bytes + 4 * stats.table_entries;
-    if ((rc = prof_end(p, 0, st, &rec))) return rc;
+    prof_end(p, 0, rec);
   }
   if ((rc = end_call(p, s2, st))) return rc;
 
@@ -1624,17 +1646,18 @@ ll_status ll_rope_rows(ll_pool* p, int32_t seq, int64_t row_begin, int64_t n_row
   a.out_plane_chunks = (out_layer_stride_bytes ? out_layer_stride_bytes : n_rows * p->row_bytes) / 16;
   a.blocks_per_plane = ll::flat_blocks(n_rows * per_row);
   ProfRec rec{};
-  if (p->profiling && (rc = prof_begin(p, 2, st, &rec))) return rc;
-  hipError_t e = ll::launch_rope_table(t, st);
+  ll::Stamp ts;
+  if (prof_pick(p, 2) && (rc = prof_begin(p, &rec, &ts))) return rc;
+  hipError_t e = ll::launch_rope_table(t, st, ll::Stamp{ts.start, nullptr});
   if (e != hipSuccess) return device_fail(p, e, "rope_table_kernel launch");
-  e = ll::launch_rope_rows(a, p->desc.rope_pairing, st);
+  e = ll::launch_rope_rows(a, p->desc.rope_pairing, st, ll::Stamp{nullptr, ts.stop});
   if (e != hipSuccess) return device_fail(p, e, "rope_rows_kernel launch");
   ll_plan_stats stats{};
   stats.alg_bytes = out_dev ? L * n_rows * 2 * p->row_bytes : L * n_rows * 2 * p->band_bytes;
   stats.rows_rotated_inplace = out_dev ? 0 : n_rows;
-  if (p->profiling) {
+  if (rec.start) {
     rec.bytes = stats.alg_bytes;
-    if ((rc = prof_end(p, 2, st, &rec))) return rc;
+    prof_end(p, 2, rec);
   }
   if ((rc = end_call(p, sg, st))) return rc;
   p->last = stats;
@@ -1651,7 +1674,8 @@ ll_status ll_last_plan_stats(const ll_pool* p, ll_plan_stats* out) {
 
 ll_status ll_pool_set_profiling(ll_pool* p, int32_t enable) {
   if (!p) return fail(LL_EINVAL, "pool is NULL");
-  p->profiling = enable != 0;
+  p->prof_every = enable > 0 ? enable : 0;
+  for (int64_t& t : p->prof_tick) t = 0;
   return LL_OK;
 }
 

@@ -42,7 +42,7 @@ struct RopeRowsLaunch {
   int64_t blocks_per_plane;
 };
 
-hipError_t launch_rope_table(const RopeTableLaunch& a, hipStream_t s);
-hipError_t launch_rope_rows(const RopeRowsLaunch& a, int pairing, hipStream_t s);
+hipError_t launch_rope_table(const RopeTableLaunch& a, hipStream_t s, const Stamp& t = Stamp{});
+hipError_t launch_rope_rows(const RopeRowsLaunch& a, int pairing, hipStream_t s, const Stamp& t = Stamp{});
 
 }  // namespace ll

@@ -365,8 +365,9 @@ class Pool:
         return PlanStats(s.alg_bytes, s.rows_moved, s.rows_rotated_inplace, s.fresh_pages, s.freed_pages,
                          s.table_entries)
 
-    def set_profiling(self, enable: bool) -> None:
-        _check(_lib.ll_pool_set_profiling(self._h, 1 if enable else 0))
+    def set_profiling(self, enable: bool, every: int = 1) -> None:
+        """Time every `every`-th launch of each profiled kernel while enabled."""
+        _check(_lib.ll_pool_set_profiling(self._h, max(1, int(every)) if enable else 0))
 
     def profile_read(self, kernel: int = 0):
         """(launches, total_ms, total_bytes) of kernel 0 (row moves), 1 (keep

@@ -297,3 +297,33 @@ def test_splice_batch_of_40_takes_several_launches():
         compare_seq(dp, expected, s)
     assert_same_free(dp, expected)
     dp.close()
+
+
+def test_sampled_profiling_times_every_nth_launch_and_keeps_results():
+    """ll_pool_set_profiling(n) stamps every n-th launch, counted from the
+    call; the timed bytes are the plan's algorithmic bytes plus its page-table
+    entries; results are those of the oracle whether a launch is timed or not."""
+    say("sampled profiling")
+    dp = _pool(2, 800, 16, 1, 300, seed=91)
+    dp.set_pages(0, permuted_pages(91, 800)[:250], 3990)
+    dp.snapshot_rows()
+    dp.pool.set_profiling(True, 3)
+    per_call = []
+    expected = None
+    for i in range(7):   # launches 0, 3 and 6 are timed
+        expected, _ = _splice_both(dp, [(0, 100 + 7 * i, 300 + 7 * i, 5 + i, 40 + i, O.AMORTIZE)])
+        dp.state = expected
+        st = dp.pool.last_stats()
+        per_call.append(st.alg_bytes + 4 * st.table_entries)
+    dp.pool.set_profiling(False)
+    n, ms, b = dp.pool.profile_read(0)
+    assert n == 3 and ms > 0
+    assert b == per_call[0] + per_call[3] + per_call[6]
+    assert dp.pool.profile_read(0) == (0, 0.0, 0)      # read clears
+    compare_seq(dp, expected, 0)
+    assert_same_free(dp, expected)
+    dp.pool.set_profiling(True)                          # every launch
+    _splice_both(dp, [(0, 0, 0, 3, 99, O.AMORTIZE)])
+    dp.pool.set_profiling(False)
+    assert dp.pool.profile_read(0)[0] == 1
+    dp.close()
