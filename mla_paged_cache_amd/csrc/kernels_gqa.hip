@@ -57,11 +57,13 @@ __device__ __forceinline__ void rotate_pair(chunk_t& xa, chunk_t& xb, int w, int
 // In a K plane each thread moves one unit of two chunks of a row: unit w of
 // head h is band chunks (w, w + half) for w < half, else two chunks of the
 // head's non-band part, one from each of its halves, so each load instruction
-// of a wave reads whole 128-byte runs.  In a V plane (a plain copy) each
-// thread moves one chunk.
+// of a wave reads whole 128-byte runs.  In a V plane (a plain copy) unit w is
+// chunks w and w + row_chunks / 2 of the row.
 //
-// Blocks [0, L * move_blocks_k) write the K rows of fresh pages, the next
-// L * move_blocks_v their V rows, the next L * rot_blocks_per_plane turn the
+// Blocks [0, 2 L * move_blocks_per_plane) write the rows of fresh pages, even
+// blocks in K planes and odd blocks in V planes (a K block that turns first
+// stages its table behind a barrier; V blocks in between keep the memory
+// streams busy meanwhile), the next L * rot_blocks_per_plane turn the
 // RoPE bands of reused pages' downstream rows in place (K planes only; units
 // (row, head, w < half)), and the remaining blocks rewrite page-table rows.
 // WAVE_TASK: every wave lies inside one page task in every block range.
@@ -71,17 +73,16 @@ template <int PAIRING, bool WAVE_TASK, bool BLOCK_TASK>
 __global__ __launch_bounds__(kFlatThreads) void gqa_splice_kernel(GqaSpliceLaunch a) {
   __shared__ float tab[2 * kMaxBandPairs];
   const int64_t b = blockIdx.x;
-  const int64_t k_blocks = a.move_blocks_k * a.num_layers;
-  const int64_t move_blocks = k_blocks + a.move_blocks_v * a.num_layers;
+  const int64_t move_blocks = 2 * a.move_blocks_per_plane * a.num_layers;
   const int64_t rot_blocks = a.rot_blocks_per_plane * a.num_layers;
   if (b >= move_blocks + rot_blocks) {
     table_write_block(a.twrites, a.tables, a.page_table, a.max_pages_per_seq, b - move_blocks - rot_blocks);
     return;
   }
   const bool in_place = b >= move_blocks;
-  const bool v_move = !in_place && b >= k_blocks;
-  const int64_t bb = in_place ? b - move_blocks : (v_move ? b - k_blocks : b);
-  const int64_t bpp = in_place ? a.rot_blocks_per_plane : (v_move ? a.move_blocks_v : a.move_blocks_k);
+  const bool v_move = !in_place && (b & 1);
+  const int64_t bb = in_place ? b - move_blocks : (b >> 1);
+  const int64_t bpp = in_place ? a.rot_blocks_per_plane : a.move_blocks_per_plane;
   const int plane = static_cast<int>(bb / bpp) + (v_move ? a.num_layers : 0);
   const uint32_t u = static_cast<uint32_t>((bb - static_cast<int64_t>(bb / bpp) * bpp) * kFlatThreads + threadIdx.x);
   const int shift = a.page_shift;
@@ -104,9 +105,10 @@ __global__ __launch_bounds__(kFlatThreads) void gqa_splice_kernel(GqaSpliceLaunc
     col_b = col_a + half;
     band_unit = true;
   } else if (v_move) {
-    row_flat = u / rc;
-    col_a = u - row_flat * rc;
-    col_b = col_a;
+    const uint32_t ru = rc >> 1;
+    row_flat = u / ru;
+    col_a = u - row_flat * ru;
+    col_b = col_a + ru;
   } else {
     const uint32_t ru = rc >> 1;
     row_flat = u / ru;
@@ -155,12 +157,6 @@ __global__ __launch_bounds__(kFlatThreads) void gqa_splice_kernel(GqaSpliceLaunc
     rot = t.rotate != 0;
   }
   chunk_t va = chunk_t{0u, 0u, 0u, 0u}, vb = va;
-  if (v_move) {
-    if (live)
-      __builtin_nontemporal_store(__builtin_nontemporal_load(src + col_a),
-                                  const_cast<chunk_t*>(layer) + dst_row * rc + col_a);
-    return;
-  }
   if (live) {
     va = __builtin_nontemporal_load(src + col_a);
     vb = __builtin_nontemporal_load(src + col_b);
@@ -221,17 +217,16 @@ __global__ __launch_bounds__(kFlatThreads) void plane_evict_kernel(PlaneEvictLau
 }  // namespace
 
 hipError_t launch_gqa_splice(const GqaSpliceLaunch& a, int pairing, hipStream_t s, const Stamp& t) {
-  const int64_t grid = (a.move_blocks_k + a.move_blocks_v + a.rot_blocks_per_plane) * a.num_layers + a.n_twrites;
+  const int64_t grid = (2 * a.move_blocks_per_plane + a.rot_blocks_per_plane) * a.num_layers + a.n_twrites;
   if (grid == 0) return stamp_empty(s, t);
   const dim3 g(static_cast<unsigned>(grid)), blk(kFlatThreads);
   // one task per wave (per block) when a page's units are a whole number of
-  // waves (blocks) in both the move and the in-place ranges
+  // waves (blocks) in both the move and the in-place ranges (K and V planes
+  // have the same units per page)
   const int64_t move_units = int64_t{a.row_chunks / 2} << a.page_shift;
   const int64_t band_units = (int64_t{a.heads} << (a.rot_shift - 1)) << a.page_shift;
-  const int64_t v_chunks = int64_t{a.row_chunks} << a.page_shift;
   const bool wave_task = move_units % 64 == 0 && band_units % 64 == 0;
-  const bool block_task = move_units % kFlatThreads == 0 && band_units % kFlatThreads == 0 &&
-                          v_chunks % kFlatThreads == 0;
+  const bool block_task = move_units % kFlatThreads == 0 && band_units % kFlatThreads == 0;
   void (*k)(GqaSpliceLaunch);
   if (pairing == 0)
     k = block_task ? gqa_splice_kernel<0, true, true>

@@ -1226,10 +1226,9 @@ ll_status leyline_splice(ll_pool* p, const ll_directive* dirs, int32_t n, void* 
     a.tasks = reinterpret_cast<const ll::SpliceTask*>(sg->dev + o_t);
     a.n_move_tasks = n_move_tasks;
     a.n_rot_tasks = n_rot_tasks;
-    // K: one thread per two chunks (row_chunks is even: head_dim is a
-    // multiple of 16); V: one thread per chunk
-    a.move_blocks_k = ll::flat_blocks(n_move_tasks * P * (row_chunks / 2));
-    a.move_blocks_v = ll::flat_blocks(n_move_tasks * P * row_chunks);
+    // one thread per two chunks in K and V planes (row_chunks is even:
+    // head_dim is a multiple of 16)
+    a.move_blocks_per_plane = ll::flat_blocks(n_move_tasks * P * (row_chunks / 2));
     a.rot_blocks_per_plane = ll::flat_blocks(n_rot_tasks * P * (p->heads << (p->rot_shift - 1)));
     a.dirs = reinterpret_cast<const ll::GqaDir*>(sg->dev + o_d);
     a.twrites = reinterpret_cast<const ll::TableWrite*>(sg->dev + o_w);
