@@ -19,6 +19,9 @@ was taken on the current kernel source.  The CPU baseline runs the oracle on
 the same workload on the host and checks the GPU result against it.
 
 Other workloads (one JSON line each, not the headline):
+  --workload splice_4k_1layer        the small case: 1 layer, 4096 tokens,
+                                     [1000, 3000) -> 16 rows on an identity
+                                     table; launch-latency bound
   --workload splice_16x32k_27layer   16 sequences x 32768 tokens, one random
                                      directive each, one batched call
   --workload evict_256x16k_27layer_p16 / _p1
@@ -73,7 +76,7 @@ def parse():
     ap.add_argument("--workload", default="splice_32k_27layer",
                     choices=["splice_32k_27layer", "splice_16x32k_27layer", "evict_256x16k_27layer_p16",
                              "evict_256x16k_27layer_p1", "splice_32k_llama8b", "kvs_mask_64x32k",
-                             "rope_rows_32k_27layer"])
+                             "rope_rows_32k_27layer", "splice_4k_1layer"])
     return ap.parse_args()
 
 
@@ -263,6 +266,9 @@ def bench_splice_32k(args):
     if host_before is not None:
         out["cpu_baseline"] = cpu_baseline_splice(host_before, gpu_after, T, alg_bytes, args.cpu_seconds,
                                                   LAYERS, TOKENS, PAGE, POOL_PAGES, S_START, S_END, STUB)
+        del host_before, gpu_after
+        out["cpu_baseline_layer_parallel"] = cpu_baseline_layer_parallel(
+            T, alg_bytes, args.cpu_seconds / 2, LAYERS, TOKENS, PAGE, POOL_PAGES, S_START, S_END, STUB)
     pool.close()
     return out
 
@@ -296,7 +302,151 @@ def cpu_baseline_splice(host_before, gpu_after, T, alg_bytes, seconds, LAYERS, T
         "cores": 1,
         "kind": "oracle",
         "sample": f"the full 27-layer splice, run {runs} times ({t:.1f} s) by the numpy oracle on one core "
-                  f"({len(os.sched_getaffinity(0))} available); GPU result matched it bit-exactly",
+                  f"({len(os.sched_getaffinity(0))} available, {cpu_model()}); GPU result matched it bit-exactly",
+    }
+
+
+def bench_splice_4k(args):
+    """The small case: one layer, 4096 tokens, page size 16, identity page
+    table (pages 0..255) in a pool of 512 pages; [1000, 3000) spliced for a
+    16-row stub (Delta = -1984, a whole number of pages: 68 downstream pages
+    are reused and turned in place, 2 pages are fresh).  Launch-latency bound;
+    the figure that matters is the call's latency.  Restoring the table does
+    not undo the in-place turn, so each step turns those rows again (the same
+    work every step)."""
+    import torch
+    from mla_paged_cache_amd import leyline as L
+    from synth import random_rows_torch
+
+    TOKENS, PAGE, POOL_PAGES, S_START, S_END, STUB = 4096, 16, 512, 1000, 3000, 16
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    data = random_rows_torch(0, (1, POOL_PAGES, PAGE, ROW), dev)
+    stub = random_rows_torch(1, (1, STUB, ROW), dev)
+    table = torch.full((1, TOKENS // PAGE + 8), -1, dtype=torch.int32, device=dev)
+    pool = L.Pool(data, table)
+    T = np.arange(TOKENS // PAGE, dtype=np.int32)
+    directive = [L.Directive(0, S_START, S_END, stub)]
+
+    def restore():
+        pool.seq_set_pages(0, T, TOKENS)
+
+    restore()
+    pool.splice(directive)
+    torch.cuda.synchronize()
+    st = pool.last_stats()
+    alg_bytes = st.alg_bytes
+    for _ in range(args.warmup):
+        restore()
+        pool.splice(directive)
+    torch.cuda.synchronize()
+    pool.profile_read(0)
+    pool.set_profiling(True, prof_every(args.steps))
+    quiet_gc()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        restore()
+        pool.splice(directive)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    gc.enable()
+    pool.set_profiling(False)
+    launches, kernel_ms, kernel_bytes = pool.profile_read(0)
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    lat, call = [], []
+    quiet_gc()
+    for _ in range(args.latency_runs):
+        restore()
+        flush.zero_()
+        torch.cuda.synchronize()
+        a = time.perf_counter()
+        pool.splice(directive)
+        b = time.perf_counter()
+        torch.cuda.synchronize()
+        lat.append((time.perf_counter() - a) * 1e6)
+        call.append((b - a) * 1e6)
+    gc.enable()
+    del flush
+    out = base_line(args, "splice_4k_1layer", alg_bytes / (ms_per_step * 1e-3) / 1e9, ms_per_step, {
+        "layers": 1, "tokens": TOKENS, "page_size": PAGE, "pool_pages": POOL_PAGES, "table": "identity",
+        "span": [S_START, S_END], "stub_rows": STUB, "delta": STUB - (S_END - S_START),
+        "reused_pages_turned_in_place": st.rows_rotated_inplace // PAGE, "fresh_pages": st.fresh_pages,
+        "alg_bytes_per_step": alg_bytes})
+    out["splice_latency_us"] = {"median": round(statistics.median(lat), 1), "min": round(min(lat), 1),
+                                "max": round(max(lat), 1), "runs": len(lat),
+                                "host_call_median": round(statistics.median(call), 1)}
+    out["roofline"] = roofline("splice_kernel", "splice_4k_1layer", launches, kernel_ms, kernel_bytes)
+    out["cpu_baseline"] = None
+    pool.close()
+    return out
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+_layer_barrier = None
+
+
+def _set_layer_barrier(b):
+    global _layer_barrier
+    _layer_barrier = b
+
+
+def _oracle_layers_worker(task):
+    """One process of the layer-parallel oracle leg: seeded N(0,1) bf16 rows
+    for its own layers of the same pool shape, then, once every process is
+    ready, the oracle's splice on them until `seconds` have passed."""
+    seed, n_layers, pool_pages, page, tokens, T, s_start, s_end, stub, seconds = task
+    from oracle import leyline_oracle as O
+    rng = np.random.default_rng(seed)
+    st = O.CacheState.empty(0, pool_pages, page, tokens // page + 8, with_rows=False)
+    st.layers = [O.f32_to_bf16(rng.standard_normal((pool_pages, page, ROW), dtype=np.float32))
+                 for _ in range(n_layers)]
+    st.set_pages(0, T, tokens)
+    stub_rows = O.f32_to_bf16(rng.standard_normal((n_layers, stub, ROW), dtype=np.float32))
+    d = [O.Directive(0, s_start, s_end, stub, stub_rows)]
+    _layer_barrier.wait(timeout=300)
+    runs, t = 0, 0.0
+    while t < seconds or runs == 0:
+        a = time.perf_counter()
+        O.splice(st, d)
+        t += time.perf_counter() - a
+        runs += 1
+    return runs, t
+
+
+def cpu_baseline_layer_parallel(T, alg_bytes, seconds, LAYERS, TOKENS, PAGE, POOL_PAGES, S_START, S_END, STUB):
+    """The same oracle on all host cores (at most 16 processes), the layers
+    dealt out among them: each process splices its own layers (same pool
+    shape, same directive, its own seeded rows).  Throughput is the sum over
+    processes of their layers' bytes per second of splice time."""
+    import multiprocessing as mp
+    n = max(1, min(16, len(os.sched_getaffinity(0)), LAYERS))
+    counts = [LAYERS // n + (1 if i < LAYERS % n else 0) for i in range(n)]
+    ctx = mp.get_context("spawn")
+    barrier = ctx.Barrier(n)
+    tasks = [(1000 + i, c, POOL_PAGES, PAGE, TOKENS, T, S_START, S_END, STUB, seconds) for i, c in enumerate(counts)]
+    with ctx.Pool(n, initializer=_set_layer_barrier, initargs=(barrier,)) as pool:
+        res = pool.map(_oracle_layers_worker, tasks, chunksize=1)
+    per_layer = alg_bytes / LAYERS
+    value = sum(c * per_layer * runs / t for c, (runs, t) in zip(counts, res))
+    return {
+        "value": round(value / 1e9, 4),
+        "unit": "GB/s",
+        "cores": n,
+        "kind": "oracle, layer-parallel",
+        "sample": f"the 27-layer splice, layers dealt over {n} processes ({counts[0]} or {counts[-1]} layers each, "
+                  f"same pool shape and directive, own seeded rows), each repeating its share for {seconds:.0f} s; "
+                  f"host {cpu_model()}",
     }
 
 
@@ -641,6 +791,8 @@ def main():
         sys.exit(2)
     if args.workload == "splice_32k_27layer":
         out = bench_splice_32k(args)
+    elif args.workload == "splice_4k_1layer":
+        out = bench_splice_4k(args)
     elif args.workload == "splice_16x32k_27layer":
         out = bench_splice_batched(args)
     elif args.workload == "splice_32k_llama8b":
