@@ -378,9 +378,148 @@ def bench_splice_4k(args):
                                 "max": round(max(lat), 1), "runs": len(lat),
                                 "host_call_median": round(statistics.median(call), 1)}
     out["roofline"] = roofline("splice_kernel", "splice_4k_1layer", launches, kernel_ms, kernel_bytes)
-    out["cpu_baseline"] = None
+    out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline_small(
+        args.cpu_seconds / 4, alg_bytes, TOKENS, PAGE, POOL_PAGES, S_START, S_END, STUB)
     pool.close()
     return out
+
+
+# ------------------------------------------------- oracle baselines --
+# Each workload's oracle leg: the oracle as it stands, on one host core, on
+# seeded host rows of the workload's shape (the values do not change the work
+# it does; parity of the GPU against the oracle is the tests' job), timed
+# around the oracle's own call only.
+
+def timed_oracle(run, seconds):
+    """Repeat `run` until `seconds` of its own time have passed; returns
+    (runs, seconds spent, the first run's result)."""
+    runs, t, first = 0, 0.0, None
+    while t < seconds or runs == 0:
+        a = time.perf_counter()
+        res = run()
+        t += time.perf_counter() - a
+        if runs == 0:
+            first = res
+        runs += 1
+    return runs, t, first
+
+
+def oracle_line(bytes_per_run, runs, t, sample, **extra):
+    out = {"value": round(bytes_per_run * runs / t / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+           "sample": f"{sample}; {runs} run(s) in {t:.1f} s on one core "
+                     f"({len(os.sched_getaffinity(0))} available, {cpu_model()})"}
+    out.update(extra)
+    return out
+
+
+def host_pool(n_arrays, pool_pages, page, width):
+    """Host layer arrays of bf16 1.0 (the oracle copies and turns bits; the
+    values do not change its work)."""
+    return [np.full((pool_pages, page, width), 0x3F80, np.uint16) for _ in range(n_arrays)]
+
+
+def cpu_baseline_evict(masks, page, seconds, LAYERS, TOKENS, ROLL):
+    """The oracle's eviction on 8 of the rollouts (all layers, the same masks,
+    the same pool shape per rollout)."""
+    from oracle import leyline_oracle as O
+    from synth import permuted_pages
+    k = 8
+    per = TOKENS // page
+    pool_pages = k * per + (k * per // 2 if page > 1 else 0)
+    st = O.CacheState.empty(0, pool_pages, page, per, with_rows=False)
+    st.layers = host_pool(LAYERS, pool_pages, page, ROW)
+    perm = permuted_pages(0, k * per)
+    for r in range(k):
+        st.set_pages(r, perm[r * per:(r + 1) * per], TOKENS)
+    ms = [masks[r * TOKENS:(r + 1) * TOKENS] for r in range(k)]
+    runs, t, (_, plans) = timed_oracle(lambda: O.evict(st, list(range(k)), ms), seconds)
+    nb = sum(O.algorithmic_bytes(pl, int(m.sum()), page, np.zeros(int(m.sum()), np.int64),
+                                 np.zeros(int(m.sum()), bool), 0, LAYERS, rotate=False) for pl, m in zip(plans, ms))
+    return oracle_line(nb, runs, t, f"{k} of the {ROLL} rollouts, all {LAYERS} layers, the same masks",
+                       ms_per_call_all_rollouts=round(t / runs * 1e3 * ROLL / k, 1))
+
+
+def cpu_baseline_batched(dir_spans, seconds, LAYERS, TOKENS, PAGE):
+    """The oracle's batched splice on 4 of the 16 sequences (their own
+    directives, all layers), pool pages twice theirs (as on the GPU)."""
+    from oracle import leyline_oracle as O
+    from synth import permuted_pages
+    k = 4
+    per = TOKENS // PAGE
+    pool_pages = 2 * k * per
+    st = O.CacheState.empty(0, pool_pages, PAGE, per + 8, with_rows=False)
+    st.layers = host_pool(LAYERS, pool_pages, PAGE, ROW)
+    perm = permuted_pages(0, k * per)
+    dirs, nb = [], 0
+    for s in range(k):
+        st.set_pages(s, perm[s * per:(s + 1) * per], TOKENS)
+        s0, s1, r = dir_spans[s]
+        dirs.append(O.Directive(s, s0, s1, r, [np.full((r, ROW), 0x3F80, np.uint16)] * LAYERS if r else None))
+    runs, t, (_, plans) = timed_oracle(lambda: O.splice(st, dirs), seconds)
+    for (s0, s1, r), pl in zip(dir_spans[:k], plans):
+        kind, index, down = O.splice_sources(TOKENS, s0, s1, r)
+        nb += O.algorithmic_bytes(pl, len(kind), PAGE, kind, down, r - (s1 - s0), LAYERS)
+    return oracle_line(nb, runs, t, f"{k} of the 16 sequences with their own directives, all {LAYERS} layers")
+
+
+def cpu_baseline_gqa(seconds, HEADS, HEAD_DIM, TOKENS, PAGE, POOL_PAGES, S_START, S_END, STUB, layers=8):
+    """The oracle's GQA splice (half-split pairs, base 500000) on `layers` of
+    the 32 layers (K and V arrays)."""
+    from oracle import leyline_oracle as O
+    from synth import permuted_pages
+    specs = []
+    for _ in range(layers):
+        specs += [O.gqa_k_row(HEADS, HEAD_DIM, HEAD_DIM), O.plain_row(HEADS * HEAD_DIM)]
+    st = O.CacheState.empty(len(specs), POOL_PAGES, PAGE, TOKENS // PAGE + 8, with_rows=False, specs=specs)
+    st.layers = host_pool(len(specs), POOL_PAGES, PAGE, HEADS * HEAD_DIM)
+    st.set_pages(0, permuted_pages(0, TOKENS // PAGE), TOKENS)
+    stub = [np.full((STUB, HEADS * HEAD_DIM), 0x3F80, np.uint16)] * len(specs)
+    d = [O.Directive(0, S_START, S_END, STUB, stub)]
+    runs, t, (_, plans) = timed_oracle(lambda: O.splice(st, d, pairing="half", base=500000.0), seconds)
+    kind, index, down = O.splice_sources(TOKENS, S_START, S_END, STUB)
+    nb = O.algorithmic_bytes(plans[0], len(kind), PAGE, kind, down, STUB - (S_END - S_START), layers, specs=specs)
+    return oracle_line(nb, runs, t, f"{layers} of the 32 layers (K and V), the same splice")
+
+
+def cpu_baseline_kvs(rolls, seconds, TOKENS):
+    """The mask oracle (death times, 128 x 128 block lists, dense bits) for
+    one rollout of the batch."""
+    from oracle import kvs_mask_oracle as K
+    n, events = rolls[0]
+
+    def run():
+        d = K.death_times(TOKENS, n, events)
+        vis = K.visibility(d)
+        K.block_mask(vis, 128, 128)
+        K.dense_bits(vis)
+
+    runs, t, _ = timed_oracle(run, seconds)
+    return oracle_line(TOKENS * TOKENS // 8, runs, t, f"rollout 0 of {len(rolls)}: death times, block lists, "
+                       "dense bits (dense bytes counted, as on the GPU line)")
+
+
+def cpu_baseline_rope(seconds, LAYERS, TOKENS, PAGE, POOL_PAGES):
+    """The oracle's per-row gather (angle -p for row p) of the whole sequence,
+    all layers."""
+    from oracle import leyline_oracle as O
+    from synth import permuted_pages
+    st = O.CacheState.empty(0, POOL_PAGES, PAGE, TOKENS // PAGE + 8, with_rows=False)
+    st.layers = host_pool(LAYERS, POOL_PAGES, PAGE, ROW)
+    st.set_pages(0, permuted_pages(0, TOKENS // PAGE), TOKENS)
+    angles = -np.arange(TOKENS, dtype=np.int64)
+    runs, t, _ = timed_oracle(lambda: O.rope_rows(st, 0, 0, angles), seconds)
+    return oracle_line(LAYERS * TOKENS * 2 * ROW * 2, runs, t, f"all {TOKENS} rows, all {LAYERS} layers, gathered")
+
+
+def cpu_baseline_small(seconds, alg_bytes, TOKENS, PAGE, POOL_PAGES, S_START, S_END, STUB):
+    """The oracle's splice of the one-layer 4k case."""
+    from oracle import leyline_oracle as O
+    st = O.CacheState.empty(0, POOL_PAGES, PAGE, TOKENS // PAGE + 8, with_rows=False)
+    st.layers = host_pool(1, POOL_PAGES, PAGE, ROW)
+    st.set_pages(0, np.arange(TOKENS // PAGE), TOKENS)
+    d = [O.Directive(0, S_START, S_END, STUB, [np.full((STUB, ROW), 0x3F80, np.uint16)])]
+    runs, t, _ = timed_oracle(lambda: O.splice(st, d), seconds)
+    return oracle_line(alg_bytes, runs, t, "the same one-layer splice", ms_per_call=round(t / runs * 1e3, 3))
 
 
 def cpu_model() -> str:
@@ -467,11 +606,12 @@ def bench_splice_batched(args):
     pool = L.Pool(data, table)
     perm = permuted_pages(0, SEQS * per)
     rng = np_rng(0, 4)
-    dirs = []
+    dirs, spans = [], []
     for s in range(SEQS):
         d = draw_span(rng, TOKENS, 256, 8192, 8, 64)
         stub = random_rows_torch(100 + s, (LAYERS, d.r_len, ROW), dev)
         dirs.append(L.Directive(s, d.s_start, d.s_end, stub))
+        spans.append((d.s_start, d.s_end, d.r_len))
 
     def restore():
         for s in range(SEQS):
@@ -502,7 +642,8 @@ def bench_splice_batched(args):
         "layers": LAYERS, "tokens": TOKENS, "sequences": SEQS, "page_size": PAGE, "pool_pages": POOL_PAGES,
         "alg_bytes_per_step": alg_bytes, "restore_in_step": "16 page-table rows"})
     out["roofline"] = roofline("splice_kernel", "splice_16x32k_27layer", launches, kernel_ms, kernel_bytes)
-    out["cpu_baseline"] = None
+    out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline_batched(
+        spans, args.cpu_seconds, LAYERS, TOKENS, PAGE)
     pool.close()
     return out
 
@@ -560,7 +701,8 @@ def bench_splice_gqa(args):
         "alg_bytes_per_step": alg_bytes})
     out["pct_hbm_peak"] = round(100.0 * out["value"] / HBM_PEAK_GBS, 2)
     out["roofline"] = roofline("gqa_splice_kernel", "splice_32k_llama8b", launches, kernel_ms, kernel_bytes)
-    out["cpu_baseline"] = None
+    out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline_gqa(
+        args.cpu_seconds, HEADS, HEAD_DIM, TOKENS, PAGE, POOL_PAGES, S_START, S_END, STUB)
     pool.close()
     return out
 
@@ -616,7 +758,8 @@ def bench_rope_rows(args):
     out_line["in_place"] = {"ms_per_step": round(ip_ms, 5), "kernel_avg_us": round(ip_kernel_ms * 1e3 / max(1, ip_launches), 2),
                             "alg_bytes": ip_bytes // max(1, ip_launches),
                             "achieved_gbs": round(ip_bytes / max(1e-9, ip_kernel_ms * 1e-3) / 1e9, 1)}
-    out_line["cpu_baseline"] = None
+    out_line["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline_rope(
+        args.cpu_seconds, LAYERS, TOKENS, PAGE, POOL_PAGES)
     pool.close()
     return out_line
 
@@ -693,7 +836,7 @@ def bench_kvs_mask(args):
                                dense_bytes * args.steps)
     out["kernel_ms"] = {k: round(v, 4) for k, v in ms.items()}
     out["log_upload_ms"] = round(upload_ms, 3)
-    out["cpu_baseline"] = None
+    out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline_kvs(rolls, args.cpu_seconds, TOKENS)
     ctx.close()
     return out
 
@@ -778,7 +921,8 @@ def bench_evict(args, page):
         out["roofline"]["kernel"] = "device page plan: fresh_rank/alloc_scan/alloc_tables/table_copy + dev_move"
     out["keep_scan_us"] = round(scan_ms * 1e3 / max(1, s_launches), 2)
     out["call_return_us"] = round(1e6 * statistics.median(call_times), 1)
-    out["cpu_baseline"] = None
+    out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline_evict(
+        masks, page, args.cpu_seconds, LAYERS, TOKENS, ROLL)
     pool.close()
     return out
 
