@@ -16,7 +16,9 @@ time per step.  The roofline object times the row kernel alone with HIP events
 recorded on the stream it runs on; its `traffic` is the HBM traffic per launch
 from the rocprofv3 counter summary in profiles/, used only while that summary
 was taken on the current kernel source.  The CPU baseline runs the oracle on
-the same workload on the host and checks the GPU result against it.
+the same workload on the host and checks the GPU result against it; a second
+leg deals the layers out over the host's cores.  Every other workload carries
+the oracle timed on a bounded sample of its own shape.
 
 Other workloads (one JSON line each, not the headline):
   --workload splice_4k_1layer        the small case: 1 layer, 4096 tokens,
