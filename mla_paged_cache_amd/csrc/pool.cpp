@@ -17,6 +17,7 @@
 #include <deque>
 #include <memory>
 #include <string>
+#include <thread>
 #include <utility>
 #include <vector>
 
@@ -88,6 +89,16 @@ class FreePages {
       }
     }
   }
+  // Pages marked in `bits` (all taken now) return to the free set.
+  void give_bits(const uint64_t* bits) {
+    for (size_t w = 0; w < words_.size(); ++w) {
+      if (!bits[w]) continue;
+      count_ += __builtin_popcountll(bits[w] & ~words_[w]);
+      words_[w] |= bits[w];
+      hint_ = std::min<int64_t>(hint_, static_cast<int64_t>(w));
+    }
+  }
+  size_t num_words() const { return words_.size(); }
   // The bitmap words (bit set = free), for the device's page plan.
   void copy_words(uint64_t* out) const { std::memcpy(out, words_.data(), words_.size() * sizeof(uint64_t)); }
   void advance_hint() {
@@ -195,6 +206,7 @@ struct ll_pool {
   std::vector<ProfRec> prof[3];  // row-moving kernel, keep scan, per-row rotation
   std::vector<hipEvent_t> spare_events;
   std::vector<int32_t> page_slot;  // per physical page: scratch marks of ll_seq_set_pages
+  std::vector<uint64_t> settle_bits;  // pages freed by a settle, one bitmap per host thread
   // An eviction whose page plan the device made: the host learns its result
   // from a readback and brings its bookkeeping up to date (settles) at the
   // start of the next call on the pool.
@@ -239,56 +251,97 @@ ll_status settle(ll_pool* p) {
   }
   const int32_t* reuse = reinterpret_cast<const int32_t*>(p->h_readback + pe.off_reuse);
   const int64_t P = p->P;
+  const size_t n_seqs = pe.seq_ids.size();
   ll_plan_stats stats{};
-  std::vector<int32_t> taken, freed;
-  for (size_t i = 0; i < pe.seq_ids.size(); ++i) {
-    SeqState& s = p->seqs[pe.seq_ids[i]];
-    const int64_t n_new = counts[i];
-    if (n_new < 0 || n_new > s.len) {
-      p->poisoned = true;
-      return fail(LL_EDEVICE, "the device page plan returned a bad length");
-    }
-    const int64_t pages = ceil_div(n_new, P);
-    const int32_t* nt = table + pe.reuse_off[i];
-    const int32_t* ru = reuse + pe.reuse_off[i];
-    const int64_t old_pages = static_cast<int64_t>(s.pages.size());
-    // one merge walk: kept old pages appear in `ru` in increasing order;
-    // new pages with ru < 0 are fresh
-    int64_t k = 0;  // next old logical page not yet classified
-    bool bad = false;
-    for (int64_t q = 0; q < pages && !bad; ++q) {
-      const int32_t r = ru[q];
-      if (r < 0) {
+  auto bad_plan = [p](const char* what) {
+    p->poisoned = true;
+    return fail(LL_EDEVICE, "the device page plan returned %s", what);
+  };
+  for (size_t i = 0; i < n_seqs; ++i)
+    if (counts[i] < 0 || counts[i] > p->seqs[pe.seq_ids[i]].len) return bad_plan("a bad length");
+  // Pass 1: fresh pages leave the free set, each checked against the free set
+  // as the call found it (no page of this call has returned to it yet).  At
+  // page size 1 no page is ever fresh.
+  if (P > 1) {
+    for (size_t i = 0; i < n_seqs; ++i) {
+      const int64_t n_new = counts[i];
+      const int32_t* nt = table + pe.reuse_off[i];
+      const int32_t* ru = reuse + pe.reuse_off[i];
+      for (int64_t q = 0, pages = ceil_div(n_new, P); q < pages; ++q) {
+        if (ru[q] >= 0) continue;
         const int32_t pg = nt[q];
-        if (pg < 0 || pg >= p->desc.num_pages || !p->free.is_free(pg)) {
-          bad = true;
-          break;
-        }
-        taken.push_back(pg);
+        if (pg < 0 || pg >= p->desc.num_pages || !p->free.is_free(pg)) return bad_plan("an invalid fresh page");
+        p->free.take(pg);
+        ++stats.fresh_pages;
         stats.rows_moved += std::min(P, n_new - q * P);
-        continue;
       }
-      if (r < k || r >= old_pages || nt[q] != s.pages[r]) {
-        bad = true;
-        break;
-      }
-      for (; k < r; ++k) freed.push_back(s.pages[k]);
-      k = r + 1;
     }
-    if (bad) {
-      p->poisoned = true;
-      return fail(LL_EDEVICE, "the device page plan returned an invalid page");
-    }
-    for (; k < old_pages; ++k) freed.push_back(s.pages[k]);
-    s.pages.assign(nt, nt + pages);
-    s.len = n_new;
-    stats.table_entries += pages;
   }
-  for (int32_t pg : taken) p->free.take(pg);
-  for (int32_t pg : freed) p->free.give(pg);
+  // Pass 2: one merge walk per sequence.  Kept old pages appear in `ru` in
+  // increasing order; the old pages between them are freed (marked in `bits`).
+  // A large settle (page size 1 over many rollouts: millions of pages) splits
+  // the sequences over a few host threads, each with a bitmap of its own.
+  int64_t old_total = 0;
+  for (size_t i = 0; i < n_seqs; ++i) old_total += static_cast<int64_t>(p->seqs[pe.seq_ids[i]].pages.size());
+  const unsigned hw = std::max(1u, std::thread::hardware_concurrency());
+  const int T = old_total >= (int64_t{1} << 18) ? static_cast<int>(std::min(8u, hw)) : 1;
+  const size_t W = p->free.num_words();
+  p->settle_bits.assign(static_cast<size_t>(T) * W, 0);
+  std::vector<int64_t> freed(T, 0), entries(T, 0);
+  std::vector<const char*> err(T, nullptr);
+  auto walk = [&](int t) {
+    uint64_t* bits = p->settle_bits.data() + static_cast<size_t>(t) * W;
+    for (size_t i = t; i < n_seqs; i += T) {
+      SeqState& s = p->seqs[pe.seq_ids[i]];
+      const int64_t n_new = counts[i];
+      const int64_t pages = ceil_div(n_new, P);
+      const int32_t* nt = table + pe.reuse_off[i];
+      const int32_t* ru = reuse + pe.reuse_off[i];
+      const int32_t* old = s.pages.data();
+      const int64_t old_pages = static_cast<int64_t>(s.pages.size());
+      int64_t k = 0;     // next old logical page not yet classified
+      int64_t kept = 0;  // old pages the sequence keeps
+      for (int64_t q = 0; q < pages; ++q) {
+        const int32_t r = ru[q];
+        if (r < 0) {
+          if (P == 1) {
+            err[t] = "a fresh page at page size 1";
+            return;
+          }
+          continue;
+        }
+        if (r < k || r >= old_pages || nt[q] != old[r]) {
+          err[t] = "an invalid reused page";
+          return;
+        }
+        for (; k < r; ++k) bits[old[k] >> 6] |= 1ull << (old[k] & 63);
+        k = r + 1;
+        ++kept;
+      }
+      for (; k < old_pages; ++k) bits[old[k] >> 6] |= 1ull << (old[k] & 63);
+      freed[t] += old_pages - kept;
+      s.pages.assign(nt, nt + pages);
+      s.len = n_new;
+      entries[t] += pages;
+    }
+  };
+  std::vector<std::thread> helpers;
+  int started = 1;
+  try {
+    for (; started < T; ++started) helpers.emplace_back(walk, started);
+  } catch (...) {
+    // no thread to be had: the shares not started run here
+  }
+  walk(0);
+  for (int t = started; t < T; ++t) walk(t);
+  for (std::thread& th : helpers) th.join();
+  for (int t = 0; t < T; ++t) {
+    if (err[t]) return bad_plan(err[t]);
+    stats.freed_pages += freed[t];
+    stats.table_entries += entries[t];
+  }
+  for (int t = 0; t < T; ++t) p->free.give_bits(p->settle_bits.data() + static_cast<size_t>(t) * W);
   p->free.advance_hint();
-  stats.fresh_pages = static_cast<int64_t>(taken.size());
-  stats.freed_pages = static_cast<int64_t>(freed.size());
   stats.alg_bytes = p->num_planes * 2 * p->row_bytes * stats.rows_moved;
   if (pe.prof_index >= 0 && pe.prof_index < static_cast<int64_t>(p->prof[0].size()))
     p->prof[0][pe.prof_index].bytes = stats.alg_bytes + 4 * stats.table_entries;
