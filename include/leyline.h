@@ -238,7 +238,8 @@ ll_status leyline_splice(ll_pool* pool, const ll_directive* dirs, int32_t n, voi
  * order, found by rank/select on the free bitmap -- and writes the rows and
  * page tables; the call returns without waiting and the pool's host
  * bookkeeping (lengths, tables, free set, ll_last_plan_stats) catches up at
- * the start of the next call on the pool.  Otherwise the call waits once for
+ * the start of the next call on the pool (above 256 Ki old pages it briefly
+ * uses up to 8 host threads for that).  Otherwise the call waits once for
  * a small device-to-host copy of the per-page plan inputs and the host makes
  * the same plan, so that a shortage returns LL_ENOMEM with nothing changed.
  * Errors: LL_EINVAL, LL_ENOMEM, LL_EDEVICE. */
