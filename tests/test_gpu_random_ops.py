@@ -3,7 +3,7 @@ operation: batched splices ("Leyline", sections 2.1-2.3; AMORTIZE and
 FORGET), evictions ("KV-streams", "how it works"; device and host page
 plans), page-granular reindex, per-row rotation in place ("VECTOR", method),
 sequence alloc / set_pages / free, and requests that must fail and leave the
-pool as it was.  Page sizes 1, 4 and 16.
+pool as it was.  Page sizes 1, 4 and 16; MLA pools and GQA pools.
 
 Rows that become live without a splice or eviction writing them (a new
 sequence, new pages) are filled with fresh seeded rows on both sides, as a
@@ -15,7 +15,8 @@ import pytest
 from oracle import leyline_oracle as O
 from synth import random_rows_np
 
-from gpu_common import DevicePool, compare_seq, need_gpu, say, torch, ulp_distance
+from gpu_common import DevicePool, compare_seq, need_gpu, say, torch
+from test_gpu_gqa import GqaDevicePool
 
 pytestmark = pytest.mark.gpu
 
@@ -23,6 +24,9 @@ LAYERS, MAX_SEQS, MAX_LEN = 2, 5, 700
 
 
 class Mirror:
+    """An MLA pool and its oracle state."""
+    pairing, base = "interleaved", 10000.0
+
     def __init__(self, P, seed):
         self.L = need_gpu()
         self.P = P
@@ -31,7 +35,7 @@ class Mirror:
         # host page plan now and then
         self.num_pages = {1: 1600, 4: 400, 16: 100}[P]
         self.max_pages = -(-MAX_LEN * 2 // P)
-        self.dp = DevicePool(LAYERS, self.num_pages, P, MAX_SEQS, self.max_pages, seed=seed)
+        self.dp = self.make_pool(seed)
         self.dp.snapshot_rows()
         self.rng = np.random.default_rng(seed)
         self.keep_alive = []
@@ -51,6 +55,24 @@ class Mirror:
         self.seed += 1
         return self.seed
 
+    # -- pool-kind specifics
+    def make_pool(self, seed):
+        return DevicePool(LAYERS, self.num_pages, self.P, MAX_SEQS, self.max_pages, seed=seed)
+
+    def device_arrays(self):
+        """(device tensor viewed [rows][width], index of its oracle array)."""
+        return [(self.dp.data[l].view(-1, O.ROW), l) for l in range(LAYERS)]
+
+    def stub(self, r):
+        """(keyword arguments of the library's Directive, the oracle's stub)."""
+        host = random_rows_np(self.next_seed(), (LAYERS, r, O.ROW))
+        dev = torch.from_numpy(host.view(np.int16)).cuda().view(torch.bfloat16)
+        self.keep_alive.append(dev)
+        return {"stub": dev}, host
+
+    def compare(self, seq, max_ulp):
+        compare_seq(self.dp, self.state, seq, max_ulp=max_ulp)
+
     def prefill(self, seq, first=0):
         """Fresh rows in the sequence's live rows [first, n) on both sides."""
         n = self.state.lengths[seq]
@@ -59,11 +81,11 @@ class Mirror:
         t = np.asarray(self.state.tables[seq], np.int64)
         j = np.arange(first, n)
         phys = t[j // self.P] * self.P + j % self.P
-        rows = random_rows_np(self.next_seed(), (LAYERS, len(j), O.ROW))
         idx = torch.from_numpy(phys).cuda()
-        for l in range(LAYERS):
-            self.dp.data[l].view(-1, O.ROW)[idx] = torch.from_numpy(rows[l].view(np.int16)).cuda().view(torch.bfloat16)
-            self.state.layers[l].reshape(-1, O.ROW)[phys] = rows[l]
+        for dev, a in self.device_arrays():
+            rows = random_rows_np(self.next_seed(), (len(j), dev.shape[1]))
+            dev[idx] = torch.from_numpy(rows.view(np.int16)).cuda().view(torch.bfloat16)
+            self.state.layers[a].reshape(-1, dev.shape[1])[phys] = rows
         torch.cuda.synchronize()
 
     def check_books(self):
@@ -80,7 +102,7 @@ class Mirror:
 
     def check_rows(self):
         for s in sorted(self.live):
-            compare_seq(self.dp, self.state, s, max_ulp=0)
+            self.compare(s, 0)
 
     # -- operations
     def op_alloc(self):
@@ -138,16 +160,11 @@ class Mirror:
             s1 = int(self.rng.integers(s0, n + 1))
             mode = O.FORGET if self.rng.random() < 0.15 else O.AMORTIZE
             r = int(self.rng.integers(0, 2 * self.P + 4)) if mode == O.AMORTIZE else 0
-            if r:
-                host = random_rows_np(self.next_seed(), (LAYERS, r, O.ROW))
-                dev = torch.from_numpy(host.view(np.int16)).cuda().view(torch.bfloat16)
-                self.keep_alive.append(dev)
-            else:
-                host = dev = None
-            lib.append(self.L.Directive(s, s0, s1, dev, mode))
+            kw, host = self.stub(r) if r else ({}, None)
+            lib.append(self.L.Directive(s, s0, s1, mode=mode, **kw))
             ora.append(O.Directive(s, s0, s1, r, host, mode))
         try:
-            expected, _ = O.splice(self.state, ora)
+            expected, _ = O.splice(self.state, ora, pairing=self.pairing, base=self.base)
         except O.OracleError:
             with pytest.raises(self.L.LeylineError):
                 self.dp.pool.splice(lib)
@@ -228,13 +245,11 @@ class Mirror:
             # insertion at row 1 of a stub that is not a whole number of
             # pages: every page from the first on is fresh
             r = self.P + 1
-            host = random_rows_np(self.next_seed(), (LAYERS, r, O.ROW))
-            dev = torch.from_numpy(host.view(np.int16)).cuda().view(torch.bfloat16)
-            self.keep_alive.append(dev)
+            kw, host = self.stub(r)
             with pytest.raises(O.OutOfPages):
-                O.splice(self.state, [O.Directive(0, 1, 1, r, host)])
+                O.splice(self.state, [O.Directive(0, 1, 1, r, host)], pairing=self.pairing, base=self.base)
             with pytest.raises(self.L.LeylineError):
-                self.dp.pool.splice([self.L.Directive(0, 1, 1, dev)])
+                self.dp.pool.splice([self.L.Directive(0, 1, 1, **kw)])
             self.check_books()
             self.check_rows()
             assert len(self.state.free) < sum(len(self.state.tables[s]) for s in (0, 1))
@@ -264,20 +279,47 @@ class Mirror:
         a = torch.from_numpy(angles).cuda()
         self.keep_alive.append(a)
         self.dp.pool.rope_rows(s, r0, a)
-        self.state = O.rope_rows(self.state, s, r0, angles, in_place=True)
+        self.state = O.rope_rows(self.state, s, r0, angles, pairing=self.pairing, base=self.base, in_place=True)
         torch.cuda.synchronize()
         # bands within 1 ulp (device and host float64 sincos may differ at a
         # rounding tie); then the oracle takes the device's rows so that later
         # operations start from identical bits
-        compare_seq(self.dp, self.state, s, max_ulp=1)
+        self.compare(s, 1)
         self.dp.snapshot_rows()
         return f"rope {s} [{r0}, {r0 + cnt})"
 
 
+class GqaMirror(Mirror):
+    """A GQA pool (3 KV heads x 64, RoPE on the first 32 values of each head,
+    half-split pairs, base 500000) and its oracle state (K and V arrays per
+    layer)."""
+    H, D, ROT = 3, 64, 32
+    pairing, base = "half", 500000.0
+
+    def make_pool(self, seed):
+        return GqaDevicePool(LAYERS, self.num_pages, self.P, MAX_SEQS, self.max_pages, self.H, self.D, self.ROT,
+                             seed=seed, pairing=1, base=self.base)
+
+    def device_arrays(self):
+        out = []
+        for l in range(LAYERS):
+            out += [(self.dp.k[l].view(-1, self.H * self.D), 2 * l), (self.dp.v[l].view(-1, self.H * self.D), 2 * l + 1)]
+        return out
+
+    def stub(self, r):
+        k, v, host = self.dp.stub(self.next_seed(), r)
+        self.keep_alive += [k, v]
+        return {"stub": k, "stub_v": v}, host
+
+    def compare(self, seq, max_ulp):
+        assert self.dp.compare(self.state, seq) <= max_ulp
+
+
+@pytest.mark.parametrize("kind", ["mla", "gqa"])
 @pytest.mark.parametrize("P", [1, 4, 16])
-def test_random_operation_sequences(P):
-    say(f"random operations, P={P}")
-    m = Mirror(P, seed=700 + P)
+def test_random_operation_sequences(P, kind):
+    say(f"random operations, {kind}, P={P}")
+    m = (Mirror if kind == "mla" else GqaMirror)(P, seed=700 + P + (50 if kind == "gqa" else 0))
     for _ in range(3):
         m.op_alloc()
     ops = [m.op_splice] * 5 + [m.op_evict] * 4 + [m.op_reindex, m.op_rope, m.op_alloc, m.op_free, m.op_set_pages]
