@@ -35,8 +35,10 @@
  * state changes, so a call that returns LL_EINVAL, LL_ERANGE, LL_ENOMEM or
  * LL_EUNSUPPORTED leaves the pool exactly as it was.  A HIP failure after
  * state has changed returns LL_EDEVICE and poisons the pool: every later call
- * on it returns LL_EPOISONED.  ll_last_error() gives a message for the
- * calling thread's last failure.
+ * on it returns LL_EPOISONED.  No C++ exception leaves the library: host
+ * memory running out inside a call returns LL_ENOMEM and also poisons the
+ * pool (the call may have stopped half-way).  ll_last_error() gives a message
+ * for the calling thread's last failure.
  *
  * Page plan.  When a call rewrites a sequence, new logical page q reuses the
  * old physical page of logical page p iff every live row of q comes from old

@@ -53,6 +53,10 @@ class DeviceGuard {
 
 ll_status dev_fail(hipError_t e, const char* what) { return fail(LL_EDEVICE, "%s: %s", what, hipGetErrorString(e)); }
 
+// No exception crosses the C ABI: an exported function that catches one (in
+// practice std::bad_alloc) returns LL_ENOMEM.
+ll_status host_exception(std::nullptr_t) noexcept { return fail(LL_ENOMEM, "host memory exhausted during the call"); }
+
 int log2_exact(int32_t x) {
   int s = 0;
   while ((1 << s) < x) ++s;
@@ -63,7 +67,7 @@ int log2_exact(int32_t x) {
 
 extern "C" {
 
-ll_status kvs_ctx_create(int32_t device, kvs_ctx** out) {
+ll_status kvs_ctx_create(int32_t device, kvs_ctx** out) try {
   if (!out) return fail(LL_EINVAL, "NULL argument");
   *out = nullptr;
   if (device < 0) return fail(LL_EINVAL, "device must be >= 0");
@@ -79,9 +83,11 @@ ll_status kvs_ctx_create(int32_t device, kvs_ctx** out) {
   }
   *out = c;
   return LL_OK;
+} catch (...) {
+  return host_exception(nullptr);
 }
 
-void kvs_ctx_destroy(kvs_ctx* c) {
+void kvs_ctx_destroy(kvs_ctx* c) try {
   if (!c) return;
   DeviceGuard g(c->device);
   if (c->staged_pending) (void)hipEventSynchronize(c->staged);
@@ -93,10 +99,12 @@ void kvs_ctx_destroy(kvs_ctx* c) {
   if (c->minmax) (void)hipFree(c->minmax);
   if (c->list) (void)hipFree(c->list);
   delete c;
+} catch (...) {
+  return;
 }
 
 ll_status kvs_death_times(kvs_ctx* c, const kvs_rollout_log* logs, int32_t n, int64_t n_pad, const uint8_t* keep_dev,
-                          int32_t* death_dev, int32_t* status_dev, void* stream) {
+                          int32_t* death_dev, int32_t* status_dev, void* stream) try {
   if (!c) return fail(LL_EINVAL, "context is NULL");
   if (n < 0 || (n > 0 && (!logs || !death_dev || !status_dev))) return fail(LL_EINVAL, "bad arguments");
   if (n_pad < 1 || n_pad >= (int64_t{1} << 31) - 1) return fail(LL_EINVAL, "n_pad must be in [1, 2^31 - 2]");
@@ -193,11 +201,13 @@ ll_status kvs_death_times(kvs_ctx* c, const kvs_rollout_log* logs, int32_t n, in
   if (e != hipSuccess) return dev_fail(e, "hipEventRecord");
   c->staged_pending = true;
   return LL_OK;
+} catch (...) {
+  return host_exception(nullptr);
 }
 
 ll_status kvs_block_mask(kvs_ctx* c, const int32_t* death_dev, int32_t n, int64_t n_pad, int32_t block_q,
                          int32_t block_k, int32_t* partial_num, int32_t* partial_idx, int32_t* full_num,
-                         int32_t* full_idx, void* stream) {
+                         int32_t* full_idx, void* stream) try {
   if (!c) return fail(LL_EINVAL, "context is NULL");
   if (n < 0 || (n > 0 && (!death_dev || !partial_num || !partial_idx || !full_num || !full_idx)))
     return fail(LL_EINVAL, "bad arguments");
@@ -248,10 +258,12 @@ ll_status kvs_block_mask(kvs_ctx* c, const int32_t* death_dev, int32_t n, int64_
   if (e != hipSuccess) return dev_fail(e, "hipEventRecord");
   c->minmax_pending = true;
   return LL_OK;
+} catch (...) {
+  return host_exception(nullptr);
 }
 
 ll_status kvs_dense_mask(kvs_ctx* c, const int32_t* death_dev, int32_t n, int64_t n_pad, uint32_t* bits_dev,
-                         void* stream) {
+                         void* stream) try {
   if (!c) return fail(LL_EINVAL, "context is NULL");
   if (n < 0 || (n > 0 && (!death_dev || !bits_dev))) return fail(LL_EINVAL, "bad arguments");
   if (n_pad < 128 || n_pad % 128 || n_pad >= (int64_t{1} << 31) - 1)
@@ -273,6 +285,8 @@ ll_status kvs_dense_mask(kvs_ctx* c, const int32_t* death_dev, int32_t n, int64_
   hipError_t e = ll::launch_kvs_dense(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return dev_fail(e, "kvs_dense_kernel launch");
   return LL_OK;
+} catch (...) {
+  return host_exception(nullptr);
 }
 
 }  // extern "C"

@@ -39,7 +39,11 @@ ll_status fail(ll_status s, const char* fmt, ...) {
   va_start(ap, fmt);
   std::vsnprintf(buf, sizeof buf, fmt, ap);
   va_end(ap);
-  g_error = buf;
+  try {
+    g_error = buf;
+  } catch (...) {
+    // no memory even for the message: the status still says what happened
+  }
   return s;
 }
 
@@ -222,6 +226,14 @@ struct ll_pool {
 
 namespace {
 
+// No exception crosses the C ABI: an exported function that catches one (in
+// practice std::bad_alloc from host bookkeeping) returns LL_ENOMEM, and its
+// pool, which the interrupted call may have left half-updated, is poisoned.
+ll_status host_exception(ll_pool* p) noexcept {
+  if (p) p->poisoned = true;
+  return fail(LL_ENOMEM, "host memory exhausted during the call%s", p ? "; the pool is poisoned" : "");
+}
+
 ll_status device_fail(ll_pool* p, hipError_t e, const char* what) {
   p->poisoned = true;
   return fail(LL_EDEVICE, "%s: %s", what, hipGetErrorString(e));
@@ -289,7 +301,8 @@ ll_status settle(ll_pool* p) {
   p->settle_bits.assign(static_cast<size_t>(T) * W, 0);
   std::vector<int64_t> freed(T, 0), entries(T, 0);
   std::vector<const char*> err(T, nullptr);
-  auto walk = [&](int t) {
+  std::vector<char> oom(T, 0);
+  auto walk_share = [&](int t) {
     uint64_t* bits = p->settle_bits.data() + static_cast<size_t>(t) * W;
     for (size_t i = t; i < n_seqs; i += T) {
       SeqState& s = p->seqs[pe.seq_ids[i]];
@@ -325,6 +338,13 @@ ll_status settle(ll_pool* p) {
       entries[t] += pages;
     }
   };
+  auto walk = [&](int t) noexcept {
+    try {
+      walk_share(t);
+    } catch (...) {
+      oom[t] = 1;
+    }
+  };
   std::vector<std::thread> helpers;
   int started = 1;
   try {
@@ -335,6 +355,8 @@ ll_status settle(ll_pool* p) {
   walk(0);
   for (int t = started; t < T; ++t) walk(t);
   for (std::thread& th : helpers) th.join();
+  for (int t = 0; t < T; ++t)
+    if (oom[t]) return host_exception(p);
   for (int t = 0; t < T; ++t) {
     if (err[t]) return bad_plan(err[t]);
     stats.freed_pages += freed[t];
@@ -844,12 +866,14 @@ const char* ll_status_str(ll_status s) {
   return "unknown";
 }
 
-ll_status ll_rope_delta_table(double base, int32_t rope_dim, int64_t delta, float* cos_out, float* sin_out) {
+ll_status ll_rope_delta_table(double base, int32_t rope_dim, int64_t delta, float* cos_out, float* sin_out) try {
   if (!cos_out || !sin_out) return fail(LL_EINVAL, "NULL output");
   if (rope_dim <= 0 || (rope_dim & 1)) return fail(LL_EINVAL, "rope_dim must be even and positive");
   if (!(base > 0.0)) return fail(LL_EINVAL, "base must be positive");
   rope_table(base, rope_dim, delta, cos_out, sin_out);
   return LL_OK;
+} catch (...) {
+  return host_exception(nullptr);
 }
 
 }  // extern "C"
@@ -923,7 +947,7 @@ ll_status setup_pool(ll_pool* p, ll_pool** out) {
 
 extern "C" {
 
-ll_status ll_pool_create(const ll_pool_desc* desc, ll_pool** out) {
+ll_status ll_pool_create(const ll_pool_desc* desc, ll_pool** out) try {
   if (!desc || !out) return fail(LL_EINVAL, "NULL argument");
   *out = nullptr;
   const ll_pool_desc& d = *desc;
@@ -940,9 +964,11 @@ ll_status ll_pool_create(const ll_pool_desc* desc, ll_pool** out) {
   p->row_bytes = ll::kRowBytes;
   p->band_bytes = 2 * ll::kRopeDim;
   return setup_pool(p, out);
+} catch (...) {
+  return host_exception(nullptr);
 }
 
-ll_status ll_pool_create_gqa(const ll_gqa_pool_desc* desc, ll_pool** out) {
+ll_status ll_pool_create_gqa(const ll_gqa_pool_desc* desc, ll_pool** out) try {
   if (!desc || !out) return fail(LL_EINVAL, "NULL argument");
   *out = nullptr;
   const ll_gqa_pool_desc& d = *desc;
@@ -981,9 +1007,11 @@ ll_status ll_pool_create_gqa(const ll_gqa_pool_desc* desc, ll_pool** out) {
   p->row_bytes = static_cast<int64_t>(d.num_kv_heads) * d.head_dim * 2;
   p->band_bytes = static_cast<int64_t>(d.num_kv_heads) * d.rotary_dim * 2;
   return setup_pool(p, out);
+} catch (...) {
+  return host_exception(nullptr);
 }
 
-void ll_pool_destroy(ll_pool* p) {
+void ll_pool_destroy(ll_pool* p) try {
   if (!p) return;
   DeviceGuard g(p->desc.device);
   if (p->last_done) (void)hipEventSynchronize(p->last_done);
@@ -1010,18 +1038,22 @@ void ll_pool_destroy(ll_pool* p) {
   if (p->d_rowtab) (void)hipFree(p->d_rowtab);
   if (p->d_layers) (void)hipFree(p->d_layers);
   delete p;
+} catch (...) {
+  return;
 }
 
-ll_status ll_pool_free_pages(const ll_pool* p, int64_t* n_free) {
+ll_status ll_pool_free_pages(const ll_pool* p, int64_t* n_free) try {
   if (!p || !n_free) return fail(LL_EINVAL, "NULL argument");
   ll_status rc = settle(const_cast<ll_pool*>(p));
   if (rc) return rc;
   *n_free = p->free.count();
   return LL_OK;
+} catch (...) {
+  return host_exception(const_cast<ll_pool*>(p));
 }
 
 ll_status ll_seq_get(const ll_pool* p, int32_t seq, int64_t* len, int64_t* next_position, int32_t* pages_out,
-                     int32_t cap, int32_t* n_pages_out) {
+                     int32_t cap, int32_t* n_pages_out) try {
   if (!p) return fail(LL_EINVAL, "pool is NULL");
   ll_status rc = settle(const_cast<ll_pool*>(p));
   if (rc) return rc;
@@ -1034,9 +1066,11 @@ ll_status ll_seq_get(const ll_pool* p, int32_t seq, int64_t* len, int64_t* next_
   const int32_t k = std::min<int32_t>(cap, static_cast<int32_t>(s.pages.size()));
   if (k > 0) std::memcpy(pages_out, s.pages.data(), sizeof(int32_t) * k);
   return LL_OK;
+} catch (...) {
+  return host_exception(const_cast<ll_pool*>(p));
 }
 
-ll_status ll_seq_alloc(ll_pool* p, int64_t n_tokens, int32_t* seq_id_out, void* stream) {
+ll_status ll_seq_alloc(ll_pool* p, int64_t n_tokens, int32_t* seq_id_out, void* stream) try {
   ll_status rc = enter(p);
   if (rc) return rc;
   if (!seq_id_out || n_tokens < 0) return fail(LL_EINVAL, "bad argument");
@@ -1066,9 +1100,11 @@ ll_status ll_seq_alloc(ll_pool* p, int64_t n_tokens, int32_t* seq_id_out, void* 
   s.pages = std::move(pages);
   *seq_id_out = seq;
   return LL_OK;
+} catch (...) {
+  return host_exception(p);
 }
 
-ll_status ll_seq_set_pages(ll_pool* p, int32_t seq, const int32_t* pages, int64_t n_tokens, void* stream) {
+ll_status ll_seq_set_pages(ll_pool* p, int32_t seq, const int32_t* pages, int64_t n_tokens, void* stream) try {
   ll_status rc = enter(p);
   if (rc) return rc;
   if (seq < 0 || seq >= p->desc.max_seqs) return fail(LL_EINVAL, "bad sequence id %d", seq);
@@ -1122,9 +1158,11 @@ ll_status ll_seq_set_pages(ll_pool* p, int32_t seq, const int32_t* pages, int64_
   s.next_pos = n_tokens;
   s.pages = std::move(t);
   return LL_OK;
+} catch (...) {
+  return host_exception(p);
 }
 
-ll_status ll_seq_free(ll_pool* p, int32_t seq) {
+ll_status ll_seq_free(ll_pool* p, int32_t seq) try {
   ll_status rc = enter(p);
   if (rc) return rc;
   if (seq < 0 || seq >= p->desc.max_seqs || !p->seqs[seq].used) return fail(LL_EINVAL, "unknown sequence %d", seq);
@@ -1132,9 +1170,11 @@ ll_status ll_seq_free(ll_pool* p, int32_t seq) {
   for (int32_t pg : s.pages) p->free.give(pg);
   s = SeqState();
   return LL_OK;
+} catch (...) {
+  return host_exception(p);
 }
 
-ll_status leyline_splice(ll_pool* p, const ll_directive* dirs, int32_t n, void* stream) {
+ll_status leyline_splice(ll_pool* p, const ll_directive* dirs, int32_t n, void* stream) try {
   ll_status rc = enter(p);
   if (rc) return rc;
   if (n < 0 || (n > 0 && !dirs)) return fail(LL_EINVAL, "bad directive array");
@@ -1334,10 +1374,12 @@ ll_status leyline_splice(ll_pool* p, const ll_directive* dirs, int32_t n, void* 
   }
   p->last = stats;
   return LL_OK;
+} catch (...) {
+  return host_exception(p);
 }
 
 ll_status kv_evict_compact(ll_pool* p, const int32_t* seq_ids, int32_t n, const uint8_t* keep_dev,
-                           const int64_t* keep_offsets, void* stream) {
+                           const int64_t* keep_offsets, void* stream) try {
   ll_status rc = enter(p);
   if (rc) return rc;
   if (n < 0 || (n > 0 && (!seq_ids || !keep_offsets))) return fail(LL_EINVAL, "bad arguments");
@@ -1569,9 +1611,11 @@ ll_status kv_evict_compact(ll_pool* p, const int32_t* seq_ids, int32_t n, const 
   }
   p->last = stats;
   return LL_OK;
+} catch (...) {
+  return host_exception(p);
 }
 
-ll_status ll_ptable_reindex(ll_pool* p, int32_t seq, const int32_t* keep_pages, int32_t n_keep, void* stream) {
+ll_status ll_ptable_reindex(ll_pool* p, int32_t seq, const int32_t* keep_pages, int32_t n_keep, void* stream) try {
   ll_status rc = enter(p);
   if (rc) return rc;
   if (seq < 0 || seq >= p->desc.max_seqs || !p->seqs[seq].used) return fail(LL_EINVAL, "unknown sequence %d", seq);
@@ -1610,10 +1654,12 @@ ll_status ll_ptable_reindex(ll_pool* p, int32_t seq, const int32_t* keep_pages, 
   s.len = new_len;
   p->last = stats;
   return LL_OK;
+} catch (...) {
+  return host_exception(p);
 }
 
 ll_status ll_rope_rows(ll_pool* p, int32_t seq, int64_t row_begin, int64_t n_rows, const int64_t* angle_dev,
-                       void* out_dev, int64_t out_layer_stride_bytes, void* stream) {
+                       void* out_dev, int64_t out_layer_stride_bytes, void* stream) try {
   ll_status rc = enter(p);
   if (rc) return rc;
   if (seq < 0 || seq >= p->desc.max_seqs || !p->seqs[seq].used) return fail(LL_EINVAL, "unknown sequence %d", seq);
@@ -1714,6 +1760,8 @@ ll_status ll_rope_rows(ll_pool* p, int32_t seq, int64_t row_begin, int64_t n_row
   if ((rc = end_call(p, sg, st))) return rc;
   p->last = stats;
   return LL_OK;
+} catch (...) {
+  return host_exception(p);
 }
 
 ll_status ll_last_plan_stats(const ll_pool* p, ll_plan_stats* out) {
@@ -1731,7 +1779,7 @@ ll_status ll_pool_set_profiling(ll_pool* p, int32_t enable) {
   return LL_OK;
 }
 
-ll_status ll_profile_read(ll_pool* p, int32_t kernel, int64_t* launches, double* total_ms, int64_t* total_bytes) {
+ll_status ll_profile_read(ll_pool* p, int32_t kernel, int64_t* launches, double* total_ms, int64_t* total_bytes) try {
   if (!p || kernel < 0 || kernel > 2) return fail(LL_EINVAL, "bad argument");
   if (ll_status rc = settle(p)) return rc;
   DeviceGuard g(p->desc.device);
@@ -1753,6 +1801,8 @@ ll_status ll_profile_read(ll_pool* p, int32_t kernel, int64_t* launches, double*
   if (total_ms) *total_ms = ms;
   if (total_bytes) *total_bytes = bytes;
   return LL_OK;
+} catch (...) {
+  return host_exception(p);
 }
 
 }  // extern "C"
