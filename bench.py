@@ -37,6 +37,10 @@ Other workloads (one JSON line each, not the headline):
                                      the 27-layer MLA cache gathered with k_pe
                                      turned back by its position (2.04 GB), and
                                      the same rows turned in place
+  --workload evict_32x16k_llama8b_p16
+                                     KV-streams eviction of 32 rollouts x
+                                     16384 tokens on a Llama-3-8B shaped GQA
+                                     cache (K and V planes), turn drops
   --workload splice_32k_llama8b      the headline splice on a GQA cache of
                                      Llama-3-8B shape (32 layers, K and V of 8
                                      heads x 128, RoPE on all 128, half-split,
@@ -78,7 +82,7 @@ def parse():
     ap.add_argument("--workload", default="splice_32k_27layer",
                     choices=["splice_32k_27layer", "splice_16x32k_27layer", "evict_256x16k_27layer_p16",
                              "evict_256x16k_27layer_p1", "splice_32k_llama8b", "kvs_mask_64x32k",
-                             "rope_rows_32k_27layer", "splice_4k_1layer"])
+                             "rope_rows_32k_27layer", "splice_4k_1layer", "evict_32x16k_llama8b_p16"])
     return ap.parse_args()
 
 
@@ -929,6 +933,106 @@ def bench_evict(args, page):
     return out
 
 
+def bench_evict_gqa(args):
+    """KV-streams eviction on a GQA cache of Llama-3-8B shape: 32 rollouts x
+    16384 tokens x 32 layers of K and V planes (8 KV heads x 128), page size
+    16, random turn drops (turns U[200,2000], p = 0.5); pool pages 1.5 x the
+    rollouts' (the host makes the page plan).  Restoring the tables between
+    steps is outside the timed call."""
+    import torch
+    from mla_paged_cache_amd import leyline as L
+    from synth import np_rng, permuted_pages, turn_drop_mask
+
+    LAYERS, HEADS, HEAD_DIM, ROLL, TOKENS, PAGE = 32, 8, 128, 32, 16384, 16
+    per = TOKENS // PAGE
+    POOL_PAGES = ROLL * per * 3 // 2
+    dev = torch.device("cuda:0")
+    planes = []
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    for _ in range(2):
+        t = torch.empty((LAYERS, POOL_PAGES, PAGE, HEADS, HEAD_DIM), dtype=torch.int16, device=dev)
+        flat = t.view(-1)
+        step = 1 << 28
+        for i in range(0, flat.numel(), step):
+            k = min(step, flat.numel() - i)
+            flat[i:i + k] = torch.randint(-32768, 32767, (k,), generator=g, device=dev, dtype=torch.int16)
+        planes.append(t.view(torch.bfloat16))
+    table = torch.full((ROLL, per), -1, dtype=torch.int32, device=dev)
+    pool = L.GqaPool(planes[0], planes[1], table, rotary_dim=HEAD_DIM, rope_base=500000.0, pairing=L.ROPE_HALF)
+    perm = permuted_pages(0, ROLL * per)
+    rng = np_rng(0, 7)
+    masks = np.concatenate([turn_drop_mask(rng, TOKENS) for _ in range(ROLL)])
+    keep = torch.from_numpy(masks).to(dev)
+    offsets = np.arange(ROLL, dtype=np.int64) * TOKENS
+    seqs = list(range(ROLL))
+
+    def restore():
+        for s in range(ROLL):
+            pool.seq_set_pages(s, perm[s * per:(s + 1) * per], TOKENS)
+
+    restore()
+    pool.evict(seqs, keep, offsets)
+    torch.cuda.synchronize()
+    stats = pool.last_stats()
+    alg_bytes = stats.alg_bytes
+    times = []
+    pool.profile_read(0)
+    quiet_gc()
+    for i in range(args.warmup + args.steps):
+        restore()
+        torch.cuda.synchronize()
+        if i == args.warmup:
+            pool.set_profiling(True, prof_every(args.steps))
+        a = time.perf_counter()
+        pool.evict(seqs, keep, offsets)
+        torch.cuda.synchronize()
+        pool.free_pages()
+        if i >= args.warmup:
+            times.append(time.perf_counter() - a)
+    gc.enable()
+    pool.set_profiling(False)
+    launches, kernel_ms, kernel_bytes = pool.profile_read(0)
+    ms_per_step = 1e3 * statistics.median(times)
+    name = "evict_32x16k_llama8b_p16"
+    out = base_line(args, name, alg_bytes / (ms_per_step * 1e-3) / 1e9, ms_per_step, {
+        "layers": LAYERS, "kv_heads": HEADS, "head_dim": HEAD_DIM, "rollouts": ROLL, "tokens": TOKENS,
+        "page_size": PAGE, "pool_pages": POOL_PAGES, "mask": "turn drops U[200,2000], p=0.5",
+        "rows_kept": int(masks.sum()), "rows_moved_per_plane": stats.rows_moved, "fresh_pages": stats.fresh_pages,
+        "alg_bytes_per_step": alg_bytes, "page_plan": "host",
+        "step": "one kv_evict_compact call until its device work and host bookkeeping are done, median"})
+    out["metric"] = "KV-streams eviction: row bytes moved GB/s; call latency"
+    out["roofline"] = roofline("plane_evict_kernel", name, launches, kernel_ms, kernel_bytes)
+    out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline_evict_gqa(
+        masks, args.cpu_seconds, LAYERS, HEADS, HEAD_DIM, TOKENS, PAGE, ROLL)
+    pool.close()
+    return out
+
+
+def cpu_baseline_evict_gqa(masks, seconds, LAYERS, HEADS, HEAD_DIM, TOKENS, PAGE, ROLL, k=2, layers=8):
+    """The oracle's GQA eviction on `k` of the rollouts and `layers` of the
+    layers (K and V arrays), the same masks and pool shape per rollout."""
+    from oracle import leyline_oracle as O
+    from synth import permuted_pages
+    per = TOKENS // PAGE
+    pool_pages = k * per * 3 // 2
+    specs = []
+    for _ in range(layers):
+        specs += [O.gqa_k_row(HEADS, HEAD_DIM, HEAD_DIM), O.plain_row(HEADS * HEAD_DIM)]
+    st = O.CacheState.empty(len(specs), pool_pages, PAGE, per, with_rows=False, specs=specs)
+    st.layers = host_pool(len(specs), pool_pages, PAGE, HEADS * HEAD_DIM)
+    perm = permuted_pages(0, k * per)
+    for r in range(k):
+        st.set_pages(r, perm[r * per:(r + 1) * per], TOKENS)
+    ms = [masks[r * TOKENS:(r + 1) * TOKENS] for r in range(k)]
+    runs, t, (_, plans) = timed_oracle(lambda: O.evict(st, list(range(k)), ms), seconds)
+    nb = sum(O.algorithmic_bytes(pl, int(m.sum()), PAGE, np.zeros(int(m.sum()), np.int64),
+                                 np.zeros(int(m.sum()), bool), 0, layers, rotate=False, specs=specs)
+             for pl, m in zip(plans, ms))
+    return oracle_line(nb, runs, t, f"{k} of the {ROLL} rollouts, {layers} of the {LAYERS} layers (K and V), "
+                                    "the same masks")
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -943,6 +1047,8 @@ def main():
         out = bench_splice_batched(args)
     elif args.workload == "splice_32k_llama8b":
         out = bench_splice_gqa(args)
+    elif args.workload == "evict_32x16k_llama8b_p16":
+        out = bench_evict_gqa(args)
     elif args.workload == "kvs_mask_64x32k":
         out = bench_kvs_mask(args)
     elif args.workload == "rope_rows_32k_27layer":
