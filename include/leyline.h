@@ -139,6 +139,9 @@ typedef struct {
   int64_t fresh_pages;
   int64_t freed_pages;
   int64_t table_entries;        /* page-table entries written */
+  int64_t planned_on_device;    /* 1: the device made or expanded the page plan
+                                   (device-planned eviction, or a splice planned
+                                   from kernel arguments); 0: the host did */
 } ll_plan_stats;
 
 /* Create a pool over caller-owned device memory.  Checks the descriptor,
@@ -217,8 +220,18 @@ ll_status ll_pool_free_pages(const ll_pool* pool, int64_t* n_free);
  * LL_FORGET: the sequence is cut to its first s_start rows (the caller then
  * re-prefills, section 2.1); the next position moves back by n - s_start.
  *
- * Fresh pages, page-table row updates and the rows are written by one kernel
- * launch after one host-to-device copy.  n == 0 is a no-op.  Errors:
+ * The host makes the page plan.  With the default planner
+ * (ll_pool_set_splice_planner) a batch of at most 8 directives (GQA / MHA
+ * pools: at most 512 / rotary_dim) whose fresh pages form at most 128 runs of
+ * consecutive page ids travels as kernel arguments: a small kernel expands it
+ * into per-page tasks and new page-table rows, reading the old rows from the
+ * device page table, and the row kernel (fresh pages, in-place rotation and
+ * the page-table rewrite in one launch) follows on the same stream; nothing
+ * is copied to the device and the call records no event of its own.  Other
+ * batches, and every batch under LL_SPLICE_PLAN_HOST, have their tasks written
+ * by the host into pinned staging and uploaded (one host-to-device copy, on
+ * the pool's copy stream when earlier work is queued) before the same row
+ * kernel.  Both planners give the same result.  n == 0 is a no-op.  Errors:
  * LL_EINVAL (bad span, unknown or repeated sequence, r_rows (GQA: or
  * r_rows_v) NULL with r_len > 0, r_rows_v given to an MLA pool, misaligned
  * pointer or stride), LL_EUNSUPPORTED (reserved mode),
@@ -289,6 +302,13 @@ ll_status ll_rope_delta_table(double base, int32_t rope_dim, int64_t delta,
 
 /* Counters of the last splice / evict / reindex call.  Errors: LL_EINVAL. */
 ll_status ll_last_plan_stats(const ll_pool* pool, ll_plan_stats* out);
+
+/* Who expands a splice batch's page plan (see leyline_splice):
+ * LL_SPLICE_PLAN_AUTO (the default) lets the device do it when the batch
+ * fits in kernel arguments; LL_SPLICE_PLAN_HOST always stages and uploads the
+ * host's tasks.  Results do not depend on the choice.  Errors: LL_EINVAL. */
+typedef enum { LL_SPLICE_PLAN_AUTO = 0, LL_SPLICE_PLAN_HOST = 1 } ll_splice_planner;
+ll_status ll_pool_set_splice_planner(ll_pool* pool, int32_t planner);
 
 /* Kernel timing.  `enable` = n > 0 times every n-th launch (counted from
  * this call; 1: every launch) of the row-moving kernel (kernel 0; on the

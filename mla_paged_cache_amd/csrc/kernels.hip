@@ -189,6 +189,120 @@ __global__ __launch_bounds__(256) void table_write_kernel(TableLaunch a) {
   table_write_block(a.twrites, a.tables, a.page_table, a.max_pages_per_seq, blockIdx.x);
 }
 
+// Physical page of fresh index f: run r holds fresh indices
+// run_first[r] .. run_first[r + 1] - 1 on pages run_page[r], run_page[r] + 1, ...
+__device__ __forceinline__ int32_t fresh_page(const DirectPlanArgs& a, int32_t f) {
+  int lo = 0, hi = a.n_runs - 1;  // the last run r with run_first[r] <= f
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.run_first[mid] <= f)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  return a.run_page[lo] + (f - a.run_first[lo]);
+}
+
+// Expands a splice batch planned on the device (blockIdx.y = directive, one
+// thread per new page) into
+// the per-page tasks, rotation tables and new page-table rows of the row
+// kernels.  Per new page q the rule is the closed form of the page plan: q
+// keeps old page p iff all its live rows are old rows of page p at unchanged
+// offsets -- pure prefix pages keep q, pure downstream pages keep
+// (q * P - Delta) / P when Delta is a multiple of P, a page holding R rows, or
+// prefix and downstream rows with Delta != 0, is fresh.  Old entries are read
+// from the page table, which the row kernel rewrites only after this launch.
+__global__ __launch_bounds__(256) void splice_plan_kernel(DirectPlanArgs a) {
+  const int di = blockIdx.y;
+  const DirectDir& D = a.d[di];
+  const int shift = a.page_shift;
+  const int32_t P = 1 << shift;
+  const int32_t* T = a.page_table + static_cast<int64_t>(D.seq) * a.max_pages_per_seq;
+  const int32_t pages = (D.n_new + P - 1) >> shift;
+  const int32_t s0 = D.s_start, se = D.stub_end, delta = D.delta;
+  const int32_t q = static_cast<int32_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (q < pages) {
+    const int32_t lo = q << shift;
+    const int32_t hi = min(lo + P, D.n_new);
+    const bool has_pre = lo < s0;
+    const bool has_stub = se > s0 && lo < se && hi > s0;
+    const bool has_down = hi > se;
+    int32_t reuse;
+    if (has_stub)
+      reuse = -1;
+    else if (has_pre && has_down)
+      reuse = delta == 0 ? q : -1;
+    else if (has_pre)
+      reuse = q;
+    else
+      reuse = ((lo - delta) & (P - 1)) == 0 ? (lo - delta) >> shift : -1;
+    // the host checked that its plan puts fresh and rotated pages in the
+    // ranges it sent; the guards only keep every access inside the buffers
+    if (reuse >= D.old_pages) reuse = D.old_pages - 1;
+    const int32_t f = D.fresh_base + (q - D.q_fresh0);
+    const bool no_page = reuse < 0 && (a.n_runs == 0 || f < 0 || f >= a.run_first[a.n_runs]);
+    const int32_t page = reuse >= 0 ? T[reuse] : (no_page ? 0 : fresh_page(a, f));
+    if (D.packed_off + q < a.n_entries) a.tables[D.packed_off + q] = page;
+    const bool in_place = reuse >= 0 && has_down && D.rotate != 0;
+    SpliceTask t;
+    t.dst_page = page;
+    t.pre_page = -1;
+    t.down_page0 = -1;
+    t.down_page1 = -1;
+    t.q = q;
+    t.down_lp0 = -1;
+    t.dir = di;
+    t.rotate = D.rotate;
+    t.s_start = s0;
+    t.stub_end = se;
+    t.delta = delta;
+    t.n_new = no_page ? 0 : D.n_new;  // no live rows: the row kernel skips the task
+    t.stub = D.stub;
+    t.stub_layer_chunks = D.stub_layer_chunks;
+    if (in_place) {
+      const int64_t k = D.rot_base + (q - D.q_rot0);
+      if (k >= 0 && k < a.n_rot_tasks) a.tasks[a.n_move_tasks + k] = t;
+    } else if (reuse < 0) {
+      if (has_pre && q < D.old_pages) t.pre_page = T[q];
+      const int32_t jd = max(lo, se);  // first downstream row of the page
+      if (jd < hi && ((jd - delta) >> shift) < D.old_pages) {
+        const int32_t lp0 = (jd - delta) >> shift;
+        t.down_lp0 = lp0;
+        t.down_page0 = T[lp0];
+        t.down_page1 = lp0 + 1 < D.old_pages ? T[lp0 + 1] : -1;
+      }
+      const int64_t k = D.move_base + (q - D.q_fresh0);
+      if (k >= 0 && k < a.n_move_tasks) a.tasks[k] = t;
+    }
+  }
+  if (blockIdx.x != 0) return;
+  if (threadIdx.x == 0) {
+    TableWrite w;
+    w.src_off = D.packed_off;
+    w.seq = D.seq;
+    w.count = pages;
+    a.twrites[di] = w;
+  }
+  const float* trig = a.trig + 2 * a.pairs * di;
+  if (a.gqa) {
+    GqaDir* g = static_cast<GqaDir*>(a.dirs) + di;
+    if (threadIdx.x == 0) {
+      g->stub_v = D.stub_v;
+      g->stub_v_layer_chunks = D.stub_v_layer_chunks;
+    }
+    for (int j = threadIdx.x; j < a.pairs; j += blockDim.x) {
+      g->cos_[j] = trig[j];
+      g->sin_[j] = trig[a.pairs + j];
+    }
+  } else {
+    SpliceDir* s = static_cast<SpliceDir*>(a.dirs) + di;
+    for (int j = threadIdx.x; j < a.pairs; j += blockDim.x) {
+      s->cos_[j] = trig[j];
+      s->sin_[j] = trig[a.pairs + j];
+    }
+  }
+}
+
 constexpr int kScanThreads = 1024;
 constexpr int kScanWaves = kScanThreads / 64;
 
@@ -292,6 +406,13 @@ hipError_t launch_evict_move(const EvictLaunch& a, hipStream_t s, const Stamp& t
 hipError_t launch_table_write(const TableLaunch& a, hipStream_t s) {
   if (a.n_twrites == 0) return hipSuccess;
   table_write_kernel<<<dim3(a.n_twrites), dim3(256), 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_splice_plan(const DirectPlanArgs& a, int32_t max_new_pages, hipStream_t s) {
+  if (a.n_dirs <= 0) return hipSuccess;
+  const unsigned bx = static_cast<unsigned>(std::max(1, (max_new_pages + 255) / 256));
+  splice_plan_kernel<<<dim3(bx, a.n_dirs), dim3(256), 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -188,6 +188,61 @@ struct ScanLaunch {
   int32_t* reuse;              // out: per new page, the old logical page it keeps, or -1
 };
 
+// A splice batch planned on the device.  The host sends the compact plan as
+// kernel arguments (no staging, no host-to-device copy): per directive its
+// fields and the ranges of its fresh and rotate-in-place pages, the fresh
+// physical pages as runs of consecutive ids, and the cos/sin tables.
+// splice_plan_kernel expands it, reading the old page tables on the device,
+// into the SpliceTask / SpliceDir (GqaDir) / TableWrite / table arrays the row
+// kernels take, so that the row kernel that follows is the same as on the
+// host-planned path.  Limits keep the arguments under 4 KiB.
+constexpr int kDirectMaxDirs = 8;
+constexpr int kDirectMaxRuns = 128;
+constexpr int kDirectTrigFloats = 512;  // cos and sin of every directive
+
+struct DirectDir {
+  const chunk_t* stub;         // K (MLA: whole) rows of R, layer 0
+  int64_t stub_layer_chunks;
+  const chunk_t* stub_v;       // GQA: V rows of R
+  int64_t stub_v_layer_chunks;
+  int32_t seq;
+  int32_t s_start;
+  int32_t stub_end;            // s_start + rows of R inserted (FORGET: s_start)
+  int32_t delta;               // FORGET: 0
+  int32_t n_new;
+  int32_t old_pages;           // pages of the old table
+  int32_t rotate;              // 1: downstream bands turn (AMORTIZE, delta != 0)
+  int32_t q_fresh0;            // fresh pages are new pages q_fresh0 .. + fresh - 1
+  int32_t q_rot0;              // rotate-in-place pages are q_rot0 .. + n_rot - 1
+  int32_t move_base;           // index of its first fresh page among the move tasks
+  int32_t rot_base;            // ... among the rotate tasks
+  int32_t fresh_base;          // index of its first fresh page in the fresh runs
+  int32_t packed_off;          // where its new table goes in the table array
+  int32_t pad[3];
+};
+
+struct DirectPlanArgs {
+  int32_t n_dirs;
+  int32_t page_shift;
+  int32_t pairs;               // RoPE pairs per table (MLA 32; GQA rotary_dim / 2)
+  int32_t n_runs;
+  int32_t max_pages_per_seq;
+  int32_t gqa;
+  int64_t n_move_tasks;
+  int64_t n_rot_tasks;
+  int64_t n_entries;           // length of the packed table array
+  const int32_t* page_table;   // old tables (read only)
+  SpliceTask* tasks;           // out: move tasks, then rotate tasks
+  void* dirs;                  // out: SpliceDir[n_dirs] or GqaDir[n_dirs]
+  TableWrite* twrites;         // out: one per directive
+  int32_t* tables;             // out: packed new tables
+  int32_t run_page[kDirectMaxRuns];       // first physical page of run r
+  int32_t run_first[kDirectMaxRuns + 1];  // fresh index of run r's first page
+  DirectDir d[kDirectMaxDirs];
+  float trig[kDirectTrigFloats];  // directive i: cos at 2*pairs*i, sin at 2*pairs*i + pairs
+};
+static_assert(sizeof(DirectPlanArgs) <= 4096, "the direct splice plan must fit the kernel argument space");
+
 // Timing events a launcher stamps from the dispatch packets themselves (no
 // marker packets of their own on the stream): `start` gets the start time of
 // the first kernel it launches, `stop` the end time of the last one.  Null
@@ -204,6 +259,7 @@ hipError_t launch_table_write(const TableLaunch& a, hipStream_t s);
 hipError_t launch_keep_scan(const ScanLaunch& a, hipStream_t s, const Stamp& t = Stamp{});
 hipError_t launch_gqa_splice(const GqaSpliceLaunch& a, int pairing, hipStream_t s, const Stamp& t = Stamp{});
 hipError_t launch_plane_evict(const PlaneEvictLaunch& a, hipStream_t s, const Stamp& t = Stamp{});
+hipError_t launch_splice_plan(const DirectPlanArgs& a, int32_t max_new_pages, hipStream_t s);
 
 // Chunks each thread of splice_kernel moves.
 constexpr int kSpliceChunksPerThread = 2;

@@ -203,6 +203,14 @@ struct ll_pool {
   hipStream_t copy_stream = nullptr;
   hipEvent_t last_done = nullptr;  // end of the last call's device work
   hipStream_t last_stream = nullptr;  // the stream that work ran on
+  // Calls that take no staging (splices planned on the device) record no
+  // event: last_done then lags, and last_work() records lazy_ev on
+  // last_stream when a later step needs the end of all work issued so far.
+  bool unevented = false;
+  hipEvent_t lazy_ev = nullptr;
+  int32_t splice_planner = LL_SPLICE_PLAN_AUTO;
+  char* d_direct = nullptr;     // tasks, tables and rotation tables of device-planned splices
+  size_t direct_cap = 0;
   bool poisoned = false;
   ll_plan_stats last{};
   int32_t prof_every = 0;       // time every n-th launch of each kernel (0: none)
@@ -365,6 +373,7 @@ ll_status settle(ll_pool* p) {
   for (int t = 0; t < T; ++t) p->free.give_bits(p->settle_bits.data() + static_cast<size_t>(t) * W);
   p->free.advance_hint();
   stats.alg_bytes = p->num_planes * 2 * p->row_bytes * stats.rows_moved;
+  stats.planned_on_device = 1;
   if (pe.prof_index >= 0 && pe.prof_index < static_cast<int64_t>(p->prof[0].size()))
     p->prof[0][pe.prof_index].bytes = stats.alg_bytes + 4 * stats.table_entries;
   p->last = stats;
@@ -474,11 +483,36 @@ size_t stage_bytes_for(std::initializer_list<size_t> parts) {
   return t + 256;
 }
 
+// An event that fires once every call issued so far on the pool has finished
+// on the device (nullptr: nothing issued yet).
+hipEvent_t last_work(ll_pool* p, hipError_t* err) {
+  *err = hipSuccess;
+  if (p->unevented) {
+    *err = hipEventRecord(p->lazy_ev, p->last_stream);
+    if (*err != hipSuccess) return nullptr;
+    p->last_done = p->lazy_ev;
+    p->unevented = false;
+  }
+  return p->last_done;
+}
+
+// Wait on the host until the pool's device work has finished (before buffers
+// it may still use are freed or grown).
+ll_status wait_idle(ll_pool* p) {
+  hipError_t e;
+  hipEvent_t ev = last_work(p, &e);
+  if (e == hipSuccess && ev) e = hipEventSynchronize(ev);
+  if (e != hipSuccess) return device_fail(p, e, "hipEventSynchronize");
+  return LL_OK;
+}
+
 // Order this call after the previous call on the pool (any stream; calls on
 // one stream are ordered already).
 ll_status begin_call(ll_pool* p, hipStream_t st) {
-  if (p->last_done && st != p->last_stream) {
-    hipError_t e = hipStreamWaitEvent(st, p->last_done, 0);
+  if (p->last_stream != st && (p->last_done || p->unevented)) {
+    hipError_t e;
+    hipEvent_t ev = last_work(p, &e);
+    if (e == hipSuccess && ev) e = hipStreamWaitEvent(st, ev, 0);
     if (e != hipSuccess) return device_fail(p, e, "hipStreamWaitEvent");
   }
   return LL_OK;
@@ -504,6 +538,7 @@ ll_status end_call(ll_pool* p, Staging* s, hipStream_t st) {
   p->ring_inflight.push_back({s->start, s->start + s->cap, ev});
   p->last_done = ev;
   p->last_stream = st;
+  p->unevented = false;
   return LL_OK;
 }
 
@@ -664,7 +699,7 @@ void plan_splice(const ll_pool* p, const ll_directive& d, const SeqState& s, Spl
 // waits for earlier device work, which may still use them.
 ll_status ensure_evict_buffers(ll_pool* p, size_t scratch, size_t readback) {
   if (scratch <= p->scratch_cap && readback <= p->readback_cap) return LL_OK;
-  if (p->last_done) (void)hipEventSynchronize(p->last_done);
+  if (ll_status rc = wait_idle(p)) return rc;
   if (scratch > p->scratch_cap) {
     if (p->d_scratch) (void)hipFree(p->d_scratch);
     p->d_scratch = nullptr;
@@ -929,6 +964,7 @@ ll_status setup_pool(ll_pool* p, ll_pool** out) {
   if (e == hipSuccess) e = hipEventCreateWithFlags(&p->pending.done, hipEventDisableTiming);
   if (e == hipSuccess) e = hipStreamCreateWithFlags(&p->copy_stream, hipStreamNonBlocking);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&p->upload_ev, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&p->lazy_ev, hipEventDisableTiming | hipEventDisableSystemFence);
   if (e == hipSuccess) e = hipHostMalloc(reinterpret_cast<void**>(&p->ring_host), kRingBytes, hipHostMallocDefault);
   // touch every page now: first writes to fresh pinned pages fault one page
   // at a time (tens of microseconds per call while the ring is new)
@@ -1014,7 +1050,11 @@ ll_status ll_pool_create_gqa(const ll_gqa_pool_desc* desc, ll_pool** out) try {
 void ll_pool_destroy(ll_pool* p) try {
   if (!p) return;
   DeviceGuard g(p->desc.device);
-  if (p->last_done) (void)hipEventSynchronize(p->last_done);
+  {
+    hipError_t e;
+    hipEvent_t ev = last_work(p, &e);
+    if (ev) (void)hipEventSynchronize(ev);
+  }
   if (p->pending.active) (void)hipEventSynchronize(p->pending.done);
   for (auto& r : p->ring_inflight) (void)hipEventDestroy(r.done);
   for (auto e : p->ring_events) (void)hipEventDestroy(e);
@@ -1036,6 +1076,8 @@ void ll_pool_destroy(ll_pool* p) try {
   if (p->h_readback) (void)hipHostFree(p->h_readback);
   if (p->d_scratch) (void)hipFree(p->d_scratch);
   if (p->d_rowtab) (void)hipFree(p->d_rowtab);
+  if (p->d_direct) (void)hipFree(p->d_direct);
+  if (p->lazy_ev) (void)hipEventDestroy(p->lazy_ev);
   if (p->d_layers) (void)hipFree(p->d_layers);
   delete p;
 } catch (...) {
@@ -1205,32 +1247,97 @@ ll_status leyline_splice(ll_pool* p, const ll_directive* dirs, int32_t n, void* 
   if (n_move_tasks * P * row_chunks >= (int64_t{1} << 32) - 1024 || n_rot_tasks * P * row_chunks >= (int64_t{1} << 32) - 1024)
     return fail(LL_EUNSUPPORTED, "one splice may write at most 2^32 16-byte chunks per layer");
   const size_t dir_bytes = p->gqa ? sizeof(ll::GqaDir) : sizeof(ll::SpliceDir);
+  const int pairs = p->gqa ? p->desc.rope_dim / 2 : ll::kHalfPairs;
 
-  // --- device work: descriptors written straight into pinned staging, one
-  // upload, one launch
+  // --- who expands the plan.  The device does (from kernel arguments, no
+  // staging and no upload) when the batch is small, its fresh pages form few
+  // runs of consecutive ids, and every directive's fresh pages and
+  // rotate-in-place pages each form one range of q.
+  bool direct = p->splice_planner == LL_SPLICE_PLAN_AUTO && n <= ll::kDirectMaxDirs &&
+                n * 2 * pairs <= ll::kDirectTrigFloats;
+  std::vector<int32_t> run_page, run_first;
+  std::vector<int32_t> q_fresh0(static_cast<size_t>(n), 0), q_rot0(static_cast<size_t>(n), 0);
+  for (size_t k = 0; direct && k < fresh.size(); ++k) {
+    if (k > 0 && fresh[k] == fresh[k - 1] + 1) continue;
+    if (run_page.size() == static_cast<size_t>(ll::kDirectMaxRuns)) direct = false;
+    run_page.push_back(fresh[k]);
+    run_first.push_back(static_cast<int32_t>(k));
+  }
+  for (int32_t i = 0; direct && i < n; ++i) {
+    const SplicePlan& pl = plans[i];
+    const int64_t pages = static_cast<int64_t>(pl.reuse.size());
+    int64_t f0 = -1, nf = 0, r0 = -1, nr = 0;
+    for (int64_t q = 0; q < pages; ++q) {
+      if (pl.reuse[q] < 0) {
+        if (f0 < 0) f0 = q;
+        direct = direct && q == f0 + nf;
+        ++nf;
+      } else if (pl.inplace[q]) {
+        if (r0 < 0) r0 = q;
+        direct = direct && q == r0 + nr;
+        ++nr;
+      }
+    }
+    q_fresh0[i] = static_cast<int32_t>(std::max<int64_t>(f0, 0));
+    q_rot0[i] = static_cast<int32_t>(std::max<int64_t>(r0, 0));
+  }
+  const size_t n_tasks = static_cast<size_t>(n_move_tasks + n_rot_tasks);
+  // offsets of the tasks, rotation tables, table writes and tables from the
+  // base of the plan space (device-planned) or of the staging region
+  size_t o_t = 0;
+  size_t o_d = align_up(o_t + n_tasks * sizeof(ll::SpliceTask), 256);
+  size_t o_w = align_up(o_d + n * dir_bytes, 256);
+  size_t o_p = align_up(o_w + n * sizeof(ll::TableWrite), 256);
+  const size_t direct_bytes = o_p + static_cast<size_t>(n_entries) * 4;
+  if (direct && direct_bytes > p->direct_cap) {
+    // grows rarely (a larger batch than any before); waits for earlier work
+    if ((rc = wait_idle(p))) return rc;
+    if (p->d_direct) (void)hipFree(p->d_direct);
+    p->d_direct = nullptr;
+    p->direct_cap = 0;
+    const size_t cap = std::max(align_up(direct_bytes, size_t{1} << 20), size_t{1} << 20);
+    if (hipMalloc(reinterpret_cast<void**>(&p->d_direct), cap) != hipSuccess)
+      return fail(LL_ENOMEM, "cannot allocate %zu bytes of splice plan space", cap);
+    p->direct_cap = cap;
+  }
+
+  // --- device work: one launch on the host-planned path (descriptors written
+  // straight into pinned staging, one upload), two on the device-planned one
+  // (plan expansion, then the same row kernel)
   DeviceGuard g(p->desc.device);
   hipStream_t st = static_cast<hipStream_t>(stream);
   if ((rc = begin_call(p, st))) return rc;
   Staging* sg = nullptr;
-  rc = stage_acquire(p, stage_bytes_for({n * dir_bytes, (n_move_tasks + n_rot_tasks) * sizeof(ll::SpliceTask),
-                                         n * sizeof(ll::TableWrite), static_cast<size_t>(n_entries) * 4}),
-                     &sg);
-  if (rc) return rc;
-  const size_t o_d = stage_put(sg, nullptr, n * dir_bytes);
-  const size_t o_t = stage_put(sg, nullptr, (n_move_tasks + n_rot_tasks) * sizeof(ll::SpliceTask));
-  const size_t o_w = stage_put(sg, nullptr, n * sizeof(ll::TableWrite));
-  const size_t o_p = stage_put(sg, nullptr, static_cast<size_t>(n_entries) * 4);
-  ll::SpliceDir* ddirs = reinterpret_cast<ll::SpliceDir*>(sg->host + o_d);
-  ll::GqaDir* gdirs = reinterpret_cast<ll::GqaDir*>(sg->host + o_d);
-  ll::SpliceTask* move_out = reinterpret_cast<ll::SpliceTask*>(sg->host + o_t);
-  ll::SpliceTask* rot_out = move_out + n_move_tasks;
-  ll::TableWrite* writes = reinterpret_cast<ll::TableWrite*>(sg->host + o_w);
-  int32_t* packed = reinterpret_cast<int32_t*>(sg->host + o_p);
+  char* dev_base = p->d_direct;
+  ll::DirectPlanArgs da{};
+  ll::SpliceDir* ddirs = nullptr;
+  ll::GqaDir* gdirs = nullptr;
+  ll::SpliceTask* move_out = nullptr;
+  ll::SpliceTask* rot_out = nullptr;
+  ll::TableWrite* writes = nullptr;
+  int32_t* packed = nullptr;
+  if (!direct) {
+    rc = stage_acquire(p, stage_bytes_for({n * dir_bytes, n_tasks * sizeof(ll::SpliceTask),
+                                           n * sizeof(ll::TableWrite), static_cast<size_t>(n_entries) * 4}),
+                       &sg);
+    if (rc) return rc;
+    o_d = stage_put(sg, nullptr, n * dir_bytes);
+    o_t = stage_put(sg, nullptr, n_tasks * sizeof(ll::SpliceTask));
+    o_w = stage_put(sg, nullptr, n * sizeof(ll::TableWrite));
+    o_p = stage_put(sg, nullptr, static_cast<size_t>(n_entries) * 4);
+    ddirs = reinterpret_cast<ll::SpliceDir*>(sg->host + o_d);
+    gdirs = reinterpret_cast<ll::GqaDir*>(sg->host + o_d);
+    move_out = reinterpret_cast<ll::SpliceTask*>(sg->host + o_t);
+    rot_out = move_out + n_move_tasks;
+    writes = reinterpret_cast<ll::TableWrite*>(sg->host + o_w);
+    packed = reinterpret_cast<int32_t*>(sg->host + o_p);
+    dev_base = sg->dev;
+  }
 
   std::vector<std::vector<int32_t>> new_tables(static_cast<size_t>(n));
   ll_plan_stats stats{};
   size_t cursor = 0;
-  int64_t packed_at = 0;
+  int64_t packed_at = 0, move_at = 0, rot_at = 0;
   for (int32_t i = 0; i < n; ++i) {
     const ll_directive& d = dirs[i];
     const SplicePlan& pl = plans[i];
@@ -1238,14 +1345,24 @@ ll_status leyline_splice(ll_pool* p, const ll_directive* dirs, int32_t n, void* 
     const std::vector<int32_t>& T = s.pages;
     const int64_t old_pages = static_cast<int64_t>(T.size());
     const int64_t r = d.mode == LL_FORGET ? 0 : d.r_len;
-    if (p->gqa) {
-      ll::GqaDir& gd = gdirs[i];
-      rope_table(p->desc.rope_base, p->desc.rope_dim, pl.delta, gd.cos_, gd.sin_);
-      gd.stub_v = static_cast<const ll::chunk_t*>(d.mode == LL_FORGET ? nullptr : d.r_rows_v);
-      gd.stub_v_layer_chunks = (d.r_layer_stride_bytes_v ? d.r_layer_stride_bytes_v : r * p->row_bytes) / 16;
+    float* cos_out;
+    float* sin_out;
+    if (direct) {
+      cos_out = da.trig + 2 * pairs * i;
+      sin_out = cos_out + pairs;
+    } else if (p->gqa) {
+      cos_out = gdirs[i].cos_;
+      sin_out = gdirs[i].sin_;
     } else {
-      ll::SpliceDir& dd = ddirs[i];
-      rope_table(p->desc.rope_base, ll::kRopeDim, pl.delta, dd.cos_, dd.sin_);
+      cos_out = ddirs[i].cos_;
+      sin_out = ddirs[i].sin_;
+    }
+    rope_table(p->desc.rope_base, 2 * pairs, pl.delta, cos_out, sin_out);
+    const ll::chunk_t* stub_v = static_cast<const ll::chunk_t*>(d.mode == LL_FORGET ? nullptr : d.r_rows_v);
+    const int64_t stub_v_chunks = (d.r_layer_stride_bytes_v ? d.r_layer_stride_bytes_v : r * p->row_bytes) / 16;
+    if (!direct && p->gqa) {
+      gdirs[i].stub_v = stub_v;
+      gdirs[i].stub_v_layer_chunks = stub_v_chunks;
     }
     ll::SpliceTask base{};
     base.dir = i;
@@ -1258,22 +1375,50 @@ ll_status leyline_splice(ll_pool* p, const ll_directive* dirs, int32_t n, void* 
     base.stub_layer_chunks = (d.r_layer_stride_bytes ? d.r_layer_stride_bytes : r * p->row_bytes) / 16;
     base.pre_page = base.down_page0 = base.down_page1 = -1;
     base.down_lp0 = -1;
+    if (direct) {
+      ll::DirectDir& dd = da.d[i];
+      dd.stub = base.stub;
+      dd.stub_layer_chunks = base.stub_layer_chunks;
+      dd.stub_v = p->gqa ? stub_v : nullptr;
+      dd.stub_v_layer_chunks = p->gqa ? stub_v_chunks : 0;
+      dd.seq = d.seq_id;
+      dd.s_start = base.s_start;
+      dd.stub_end = base.stub_end;
+      dd.delta = base.delta;
+      dd.n_new = base.n_new;
+      dd.old_pages = static_cast<int32_t>(old_pages);
+      dd.rotate = base.rotate;
+      dd.q_fresh0 = q_fresh0[i];
+      dd.q_rot0 = q_rot0[i];
+      dd.move_base = static_cast<int32_t>(move_at);
+      dd.rot_base = static_cast<int32_t>(rot_at);
+      dd.fresh_base = static_cast<int32_t>(cursor);
+      dd.packed_off = static_cast<int32_t>(packed_at);
+    }
     std::vector<int32_t>& nt = new_tables[i];
     nt.resize(pl.reuse.size());
     for (size_t q = 0; q < pl.reuse.size(); ++q) {
       const int64_t a = static_cast<int64_t>(q) * P, b = std::min(a + P, pl.n_new);
-      ll::SpliceTask t = base;
-      t.q = static_cast<int32_t>(q);
       if (pl.reuse[q] >= 0) {
         nt[q] = T[pl.reuse[q]];
         if (pl.inplace[q]) {
-          t.dst_page = nt[q];
-          *rot_out++ = t;
+          if (!direct) {
+            ll::SpliceTask t = base;
+            t.q = static_cast<int32_t>(q);
+            t.dst_page = nt[q];
+            *rot_out++ = t;
+          }
+          ++rot_at;
           stats.rows_rotated_inplace += b - a;
         }
         continue;
       }
       nt[q] = fresh[cursor++];
+      ++move_at;
+      stats.rows_moved += b - a;
+      if (direct) continue;
+      ll::SpliceTask t = base;
+      t.q = static_cast<int32_t>(q);
       t.dst_page = nt[q];
       if (a < d.s_start && static_cast<int64_t>(q) < old_pages) t.pre_page = T[q];
       const int64_t jd = std::max(a, d.s_start + r);  // first downstream row of the page
@@ -1284,16 +1429,18 @@ ll_status leyline_splice(ll_pool* p, const ll_directive* dirs, int32_t n, void* 
         t.down_page1 = lp0 + 1 < old_pages ? T[lp0 + 1] : -1;
       }
       *move_out++ = t;
-      stats.rows_moved += b - a;
     }
-    writes[i].src_off = packed_at;
-    writes[i].seq = d.seq_id;
-    writes[i].count = static_cast<int32_t>(nt.size());
-    if (!nt.empty()) std::memcpy(packed + packed_at, nt.data(), nt.size() * 4);
+    if (!direct) {
+      writes[i].src_off = packed_at;
+      writes[i].seq = d.seq_id;
+      writes[i].count = static_cast<int32_t>(nt.size());
+      if (!nt.empty()) std::memcpy(packed + packed_at, nt.data(), nt.size() * 4);
+    }
     packed_at += static_cast<int64_t>(nt.size());
   }
   stats.fresh_pages = need;
   stats.table_entries = n_entries;
+  stats.planned_on_device = direct ? 1 : 0;
   for (int32_t i = 0; i < n; ++i) {
     const SeqState& s = p->seqs[dirs[i].seq_id];
     std::vector<char> kept(s.pages.size(), 0);
@@ -1303,10 +1450,36 @@ ll_status leyline_splice(ll_pool* p, const ll_directive* dirs, int32_t n, void* 
   }
   const int64_t L = p->desc.num_layers;
   stats.alg_bytes = p->num_planes * 2 * p->row_bytes * stats.rows_moved + L * 2 * p->band_bytes * stats.rows_rotated_inplace;
-  if ((rc = upload(p, sg, st))) return rc;
+  hipError_t e;
+  if (direct) {
+    da.n_dirs = n;
+    da.page_shift = p->page_shift;
+    da.pairs = pairs;
+    da.n_runs = static_cast<int32_t>(run_page.size());
+    da.max_pages_per_seq = p->desc.max_pages_per_seq;
+    da.gqa = p->gqa ? 1 : 0;
+    da.n_move_tasks = n_move_tasks;
+    da.n_rot_tasks = n_rot_tasks;
+    da.n_entries = n_entries;
+    da.page_table = p->desc.page_table;
+    da.tasks = reinterpret_cast<ll::SpliceTask*>(dev_base + o_t);
+    da.dirs = dev_base + o_d;
+    da.twrites = reinterpret_cast<ll::TableWrite*>(dev_base + o_w);
+    da.tables = reinterpret_cast<int32_t*>(dev_base + o_p);
+    for (size_t k = 0; k < run_page.size(); ++k) {
+      da.run_page[k] = run_page[k];
+      da.run_first[k] = run_first[k];
+    }
+    da.run_first[run_page.size()] = static_cast<int32_t>(fresh.size());
+    int32_t max_new_pages = 0;
+    for (const auto& nt : new_tables) max_new_pages = std::max(max_new_pages, static_cast<int32_t>(nt.size()));
+    e = ll::launch_splice_plan(da, max_new_pages, st);
+    if (e != hipSuccess) return device_fail(p, e, "splice_plan_kernel launch");
+  } else if ((rc = upload(p, sg, st))) {
+    return rc;
+  }
   ProfRec rec{};
   ll::Stamp ts;
-  hipError_t e;
   if (p->gqa) {
     ll::GqaSpliceLaunch a{};
     a.planes = reinterpret_cast<const ll::chunk_t* const*>(p->d_layers);
@@ -1316,16 +1489,16 @@ ll_status leyline_splice(ll_pool* p, const ll_directive* dirs, int32_t n, void* 
     a.head_chunks = p->head_chunks;
     a.rot_shift = p->rot_shift;
     a.heads = p->heads;
-    a.tasks = reinterpret_cast<const ll::SpliceTask*>(sg->dev + o_t);
+    a.tasks = reinterpret_cast<const ll::SpliceTask*>(dev_base + o_t);
     a.n_move_tasks = n_move_tasks;
     a.n_rot_tasks = n_rot_tasks;
     // one thread per two chunks in K and V planes (row_chunks is even:
     // head_dim is a multiple of 16)
     a.move_blocks_per_plane = ll::flat_blocks(n_move_tasks * P * (row_chunks / 2));
     a.rot_blocks_per_plane = ll::flat_blocks(n_rot_tasks * P * (p->heads << (p->rot_shift - 1)));
-    a.dirs = reinterpret_cast<const ll::GqaDir*>(sg->dev + o_d);
-    a.twrites = reinterpret_cast<const ll::TableWrite*>(sg->dev + o_w);
-    a.tables = reinterpret_cast<const int32_t*>(sg->dev + o_p);
+    a.dirs = reinterpret_cast<const ll::GqaDir*>(dev_base + o_d);
+    a.twrites = reinterpret_cast<const ll::TableWrite*>(dev_base + o_w);
+    a.tables = reinterpret_cast<const int32_t*>(dev_base + o_p);
     a.n_twrites = n;
     a.max_pages_per_seq = p->desc.max_pages_per_seq;
     a.page_table = p->desc.page_table;
@@ -1337,14 +1510,14 @@ ll_status leyline_splice(ll_pool* p, const ll_directive* dirs, int32_t n, void* 
     a.layers = reinterpret_cast<const ll::chunk_t* const*>(p->d_layers);
     a.num_layers = p->desc.num_layers;
     a.page_shift = p->page_shift;
-    a.tasks = reinterpret_cast<const ll::SpliceTask*>(sg->dev + o_t);
+    a.tasks = reinterpret_cast<const ll::SpliceTask*>(dev_base + o_t);
     a.n_move_tasks = n_move_tasks;
     a.n_rot_tasks = n_rot_tasks;
     a.move_blocks_per_layer = ll::flat_blocks(n_move_tasks * P * ll::kRowChunks, ll::kSpliceChunksPerThread);
     a.rot_blocks_per_layer = ll::flat_blocks(n_rot_tasks * P * (ll::kRowChunks - ll::kKpeChunk0), ll::kSpliceChunksPerThread);
-    a.dirs = reinterpret_cast<const ll::SpliceDir*>(sg->dev + o_d);
-    a.twrites = reinterpret_cast<const ll::TableWrite*>(sg->dev + o_w);
-    a.tables = reinterpret_cast<const int32_t*>(sg->dev + o_p);
+    a.dirs = reinterpret_cast<const ll::SpliceDir*>(dev_base + o_d);
+    a.twrites = reinterpret_cast<const ll::TableWrite*>(dev_base + o_w);
+    a.tables = reinterpret_cast<const int32_t*>(dev_base + o_p);
     a.n_twrites = n;
     a.max_pages_per_seq = p->desc.max_pages_per_seq;
     a.page_table = p->desc.page_table;
@@ -1356,7 +1529,12 @@ ll_status leyline_splice(ll_pool* p, const ll_directive* dirs, int32_t n, void* 
     rec.bytes = stats.alg_bytes + 4 * stats.table_entries;
     prof_end(p, 0, rec);
   }
-  if ((rc = end_call(p, sg, st))) return rc;
+  if (direct) {
+    p->last_stream = st;
+    p->unevented = true;
+  } else if ((rc = end_call(p, sg, st))) {
+    return rc;
+  }
 
   // --- commit host state
   for (int32_t pg : fresh) p->free.take(pg);
@@ -1431,7 +1609,7 @@ ll_status kv_evict_compact(ll_pool* p, const int32_t* seq_ids, int32_t n, const 
   const size_t readback = off_src;
   if ((rc = begin_call(p, st))) return rc;
   if (scratch > p->scratch_cap || readback > p->readback_cap) {
-    if (p->last_done) (void)hipEventSynchronize(p->last_done);
+    if ((rc = wait_idle(p))) return rc;
     if (scratch > p->scratch_cap) {
       if (p->d_scratch) (void)hipFree(p->d_scratch);
       p->d_scratch = nullptr;
@@ -1700,10 +1878,7 @@ ll_status ll_rope_rows(ll_pool* p, int32_t seq, int64_t row_begin, int64_t n_row
   if ((rc = begin_call(p, st))) return rc;
   const size_t tab_floats = static_cast<size_t>(n_rows) * 2 * sh.pairs;
   if (tab_floats > p->rowtab_cap) {
-    if (p->last_done) {
-      hipError_t e = hipEventSynchronize(p->last_done);
-      if (e != hipSuccess) return device_fail(p, e, "hipEventSynchronize");
-    }
+    if ((rc = wait_idle(p))) return rc;
     if (p->d_rowtab) (void)hipFree(p->d_rowtab);
     p->d_rowtab = nullptr;
     p->rowtab_cap = 0;
@@ -1769,6 +1944,14 @@ ll_status ll_last_plan_stats(const ll_pool* p, ll_plan_stats* out) {
   ll_status rc = settle(const_cast<ll_pool*>(p));
   if (rc) return rc;
   *out = p->last;
+  return LL_OK;
+}
+
+ll_status ll_pool_set_splice_planner(ll_pool* p, int32_t planner) {
+  if (!p) return fail(LL_EINVAL, "pool is NULL");
+  if (planner != LL_SPLICE_PLAN_AUTO && planner != LL_SPLICE_PLAN_HOST)
+    return fail(LL_EINVAL, "unknown splice planner %d", planner);
+  p->splice_planner = planner;
   return LL_OK;
 }
 

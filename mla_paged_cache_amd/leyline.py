@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libleyline.so")
 LL_OK, LL_EINVAL, LL_ERANGE, LL_ENOMEM, LL_EUNSUPPORTED, LL_EDEVICE, LL_EPOISONED = 0, -1, -2, -3, -4, -5, -6
 AMORTIZE, FORGET, PIN, DECAY, SCRATCH = 0, 1, 2, 3, 4
 ROPE_INTERLEAVED, ROPE_HALF = 0, 1
+SPLICE_PLAN_AUTO, SPLICE_PLAN_HOST = 0, 1
 KV_LORA_RANK, ROPE_DIM = 512, 64
 ROW = KV_LORA_RANK + ROPE_DIM
 
@@ -30,7 +31,7 @@ EXPORTS = (
     "ll_rope_delta_table", "ll_last_plan_stats", "ll_pool_set_profiling", "ll_profile_read",
     "ll_last_error", "ll_status_str", "ll_pool_create_gqa",
     "kvs_ctx_create", "kvs_ctx_destroy", "kvs_death_times", "kvs_block_mask", "kvs_dense_mask",
-    "ll_rope_rows",
+    "ll_rope_rows", "ll_pool_set_splice_planner",
 )
 
 
@@ -108,6 +109,7 @@ class _PlanStats(ctypes.Structure):
         ("fresh_pages", ctypes.c_int64),
         ("freed_pages", ctypes.c_int64),
         ("table_entries", ctypes.c_int64),
+        ("planned_on_device", ctypes.c_int64),
     ]
 
 
@@ -132,6 +134,7 @@ def _load():
         "ll_rope_delta_table": (i32, [ctypes.c_double, i32, i64, P(ctypes.c_float), P(ctypes.c_float)]),
         "ll_last_plan_stats": (i32, [vp, P(_PlanStats)]),
         "ll_pool_set_profiling": (i32, [vp, i32]),
+        "ll_pool_set_splice_planner": (i32, [vp, i32]),
         "ll_profile_read": (i32, [vp, i32, P(i64), P(ctypes.c_double), P(i64)]),
         "ll_rope_rows": (i32, [vp, i32, i64, i64, vp, vp, i64, vp]),
         "kvs_ctx_create": (i32, [i32, P(vp)]),
@@ -205,6 +208,7 @@ class PlanStats:
     fresh_pages: int
     freed_pages: int
     table_entries: int
+    planned_on_device: int
 
 
 class Pool:
@@ -363,7 +367,13 @@ class Pool:
         s = _PlanStats()
         _check(_lib.ll_last_plan_stats(self._h, ctypes.byref(s)))
         return PlanStats(s.alg_bytes, s.rows_moved, s.rows_rotated_inplace, s.fresh_pages, s.freed_pages,
-                         s.table_entries)
+                         s.table_entries, s.planned_on_device)
+
+    def set_splice_planner(self, planner: int) -> None:
+        """SPLICE_PLAN_AUTO (default: small batches are planned on the device
+        from kernel arguments) or SPLICE_PLAN_HOST (always staged and
+        uploaded)."""
+        _check(_lib.ll_pool_set_splice_planner(self._h, int(planner)))
 
     def set_profiling(self, enable: bool, every: int = 1) -> None:
         """Time every `every`-th launch of each profiled kernel while enabled."""

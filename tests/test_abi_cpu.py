@@ -34,7 +34,13 @@ def test_header_declares_the_path_entry_points():
     names = _declared()
     for n in ("leyline_splice", "kv_evict_compact", "ll_ptable_reindex", "ll_pool_create"):
         assert n in names
-    assert len(names) == 23
+    assert len(names) == 24
+
+
+def test_splice_planner_setter_checks_its_arguments():
+    from mla_paged_cache_amd import leyline as L
+    assert L._lib.ll_pool_set_splice_planner(None, L.SPLICE_PLAN_HOST) == L.LL_EINVAL
+    assert "NULL" in L._lib.ll_last_error().decode()
 
 
 def test_library_exports_every_declared_symbol(lib):

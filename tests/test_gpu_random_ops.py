@@ -1,6 +1,7 @@
 """Random sequences of pool operations against the oracle, checked after every
 operation: batched splices ("Leyline", sections 2.1-2.3; AMORTIZE and
-FORGET), evictions ("KV-streams", "how it works"; device and host page
+FORGET; the page plan expanded on the device or staged by the host, picked at
+random per call), evictions ("KV-streams", "how it works"; device and host page
 plans), page-granular reindex, per-row rotation in place ("VECTOR", method),
 sequence alloc / set_pages / free, and requests that must fail and leave the
 pool as it was.  Page sizes 1, 4 and 16; MLA pools and GQA pools.
@@ -42,6 +43,10 @@ class Mirror:
         self.live = set()
         self.seed = seed * 100000
         self.host_plans = 0
+        # splice planner per call: its own stream of draws, so the operations
+        # themselves do not depend on it
+        self.plan_rng = np.random.default_rng(seed + 1)
+        self.splice_planned = {0: 0, 1: 0}
 
     @property
     def state(self):
@@ -169,7 +174,9 @@ class Mirror:
             with pytest.raises(self.L.LeylineError):
                 self.dp.pool.splice(lib)
             return "splice: refused"
+        self.dp.pool.set_splice_planner(int(self.plan_rng.integers(0, 2)))
         self.dp.pool.splice(lib)
+        self.splice_planned[self.dp.pool.last_stats().planned_on_device] += 1
         self.state = expected
         return f"splice {[(d.seq, d.s_start, d.s_end, d.r_len, d.mode) for d in ora]}"
 
@@ -341,7 +348,9 @@ def test_random_operation_sequences(P, kind):
     for x in log:
         kinds[x.split(" ")[0].rstrip(":")] = kinds.get(x.split(" ")[0].rstrip(":"), 0) + 1
     say(f"  {len(log)} operations {kinds}; {refused} refused as the oracle refused them; "
-        f"{m.host_plans} evictions planned on the host")
+        f"{m.host_plans} evictions planned on the host; splices planned on the device "
+        f"{m.splice_planned[1]}, staged {m.splice_planned[0]}")
+    assert m.splice_planned[0] and m.splice_planned[1]
     m.pressure()
     m.keep_alive.clear()
     m.dp.close()
