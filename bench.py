@@ -7,12 +7,13 @@ splice drops three 2048-token tool turns [8192, 14336) for a 24-row stub
 (Delta = -6120), moving and rotating every downstream row ("Leyline: KV Cache
 Directives for Agentic Inference", sections 2.1-2.3).
 
-A step is one whole splice call through the C ABI (host plan, one upload, one
-kernel launch that moves rows, rotates k_pe and rewrites the page table),
-preceded by restoring the sequence's original page table (the splice never
-writes the old pages, so the pristine state comes back by table alone).
-`value` is the row bytes the splice must move per step divided by the wall
-time per step.  The roofline object times the row kernel alone with HIP events
+A step is one whole splice call through the C ABI (host plan, the plan's
+expansion into page tasks on the device, one kernel launch that moves rows,
+rotates k_pe and rewrites the page table) on a sequence of its own: the pool
+holds one such sequence per timed step (up to 64; beyond that one sequence
+has its page table restored before every splice, which also serves as the
+context figure `step_with_table_restore_ms`).  `value` is the row bytes the
+splice must move per step divided by the wall time per step.  The roofline object times the row kernel alone with HIP events
 recorded on the stream it runs on; its `traffic` is the HBM traffic per launch
 from the rocprofv3 counter summary in profiles/, used only while that summary
 was taken on the current kernel source.  The CPU baseline runs the oracle on
@@ -188,34 +189,70 @@ def base_line(args, workload, value, ms_per_step, config):
 
 # ------------------------------------------------------------------ splice --
 
+MAX_DISTINCT_SEQS = 64
+
+
 def bench_splice_32k(args):
+    """The headline.  Every timed step splices its own 32k x 27 sequence: up to
+    64 identically shaped sequences, each a random permutation of its own 2048
+    pages, sit above a spare region that holds every step's fresh pages, so
+    each step's fresh pages are one run of consecutive ids (as in a pool that
+    holds the one sequence) and no table restore runs between steps.  The
+    JSON also gives, for context, the step that restores one sequence's table
+    before each splice, and the step with the host-staged page plan."""
     import torch
     from mla_paged_cache_amd import leyline as L
     from synth import permuted_pages, random_rows_torch
 
-    LAYERS, TOKENS, PAGE, POOL_PAGES = 27, 32768, 16, 4096
+    LAYERS, TOKENS, PAGE = 27, 32768, 16
     S_START, S_END, STUB = 8192, 14336, 24
+    NP = TOKENS // PAGE
+    # Delta = -6120 is not a multiple of the page size, so every new page from
+    # the one holding s_start on is fresh
+    new_pages = -(-(TOKENS + STUB - (S_END - S_START)) // PAGE)
+    FRESH = new_pages - S_START // PAGE
+    distinct = args.steps <= MAX_DISTINCT_SEQS
+    NSEQ = args.steps if distinct else 1
+    SPARE = max(NSEQ, 2) * FRESH
+    POOL_PAGES = SPARE + NSEQ * NP
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    data = random_rows_torch(0, (LAYERS, POOL_PAGES, PAGE, ROW), dev)
-    stub = random_rows_torch(1, (LAYERS, STUB, ROW), dev)
-    table = torch.full((1, TOKENS // PAGE + 8), -1, dtype=torch.int32, device=dev)
+    data = torch.empty((LAYERS, POOL_PAGES, PAGE, ROW), dtype=torch.bfloat16, device=dev)
+    data[:, :SPARE].zero_()
+    for s in range(NSEQ):
+        data[:, SPARE + s * NP:SPARE + (s + 1) * NP] = random_rows_torch(s, (LAYERS, NP, PAGE, ROW), dev)
+    stub = random_rows_torch(1000, (LAYERS, STUB, ROW), dev)
+    table = torch.full((NSEQ, NP + 8), -1, dtype=torch.int32, device=dev)
     pool = L.Pool(data, table)
-    T = permuted_pages(0, TOKENS // PAGE)
+    T0 = permuted_pages(0, NP)                       # sequence 0: the oracle's table
+    tables = [T0 + SPARE] + [permuted_pages(s, NP, start=SPARE + s * NP) for s in range(1, NSEQ)]
     directive = [L.Directive(0, S_START, S_END, stub)]
 
     def restore():
-        pool.seq_set_pages(0, T, TOKENS)
+        pool.seq_set_pages(0, tables[0], TOKENS)
 
+    def set_all():
+        for s in range(1, NSEQ):
+            if s in live:
+                pool.seq_free(s)
+        restore()
+        for s in range(1, NSEQ):
+            pool.seq_set_pages(s, tables[s], TOKENS)
+            live.add(s)
+        torch.cuda.synchronize()
+
+    live = set()
     host_before = None
     if not args.no_cpu_baseline:
         torch.cuda.synchronize()
-        host_before = data.view(torch.int16).cpu().numpy().view(np.uint16)
+        host_before = data[:, SPARE:SPARE + NP].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
     restore()
     pool.splice(directive)
     torch.cuda.synchronize()
-    alg_bytes = pool.last_stats().alg_bytes
+    st = pool.last_stats()
+    alg_bytes = st.alg_bytes
+    assert st.fresh_pages == FRESH and st.planned_on_device == 1, st
     _, _, new_table = pool.seq_get(0)
     gpu_after = None
     if host_before is not None:
@@ -223,30 +260,51 @@ def bench_splice_32k(args):
         phys = torch.from_numpy(new_table.astype(np.int64)[j // PAGE] * PAGE + j % PAGE).to(dev)
         gpu_after = data.view(LAYERS, -1, ROW)[:, phys].view(torch.int16).cpu().numpy().view(np.uint16)
 
-    # throughput: K whole steps, bracketed by synchronize
-    for _ in range(args.warmup):
+    def timed(run, n):
+        torch.cuda.synchronize()
+        quiet_gc()
+        t0 = time.perf_counter()
+        for i in range(n):
+            run(i)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        gc.enable()
+        return (t1 - t0) * 1e3 / n
+
+    def restore_step(_):
         restore()
         pool.splice(directive)
-    torch.cuda.synchronize()
+
+    dirs = [[L.Directive(s, S_START, S_END, stub)] for s in range(NSEQ)]
+
+    def distinct_step(i):
+        pool.splice(dirs[i])
+
+    for _ in range(args.warmup):
+        restore_step(0)
+    # context: one sequence, its table restored before every splice
+    ms_restore = timed(restore_step, args.steps)
+    # throughput: K whole splices, bracketed by synchronize, with the row
+    # kernel timed on a sample of the launches
+    if distinct:
+        set_all()
     pool.profile_read(0)
     pool.set_profiling(True, prof_every(args.steps))
     torch.cuda.synchronize()
-    quiet_gc()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        restore()
-        pool.splice(directive)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    gc.enable()
+    ms_per_step = timed(distinct_step if distinct else restore_step, args.steps)
     pool.set_profiling(False)
     launches, kernel_ms, kernel_bytes = pool.profile_read(0)
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
     value = alg_bytes / (ms_per_step * 1e-3) / 1e9
+    ms_host_plan = None
+    if distinct:
+        set_all()
+        pool.set_splice_planner(L.SPLICE_PLAN_HOST)
+        ms_host_plan = timed(distinct_step, args.steps)
+        pool.set_splice_planner(L.SPLICE_PLAN_AUTO)
 
     # latency: API call to stream completion, MALL flushed before each run
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-    lat = []
+    lat, host = [], []
     quiet_gc()
     for _ in range(args.latency_runs):
         restore()
@@ -254,43 +312,57 @@ def bench_splice_32k(args):
         torch.cuda.synchronize()
         a = time.perf_counter()
         pool.splice(directive)
+        b = time.perf_counter()
         torch.cuda.synchronize()
         lat.append((time.perf_counter() - a) * 1e6)
+        host.append((b - a) * 1e6)
     gc.enable()
     del flush
 
     out = base_line(args, "splice_32k_27layer", value, ms_per_step, {
-        "layers": LAYERS, "tokens": TOKENS, "page_size": PAGE, "pool_pages": POOL_PAGES,
-        "span": [S_START, S_END], "stub_rows": STUB, "delta": STUB - (S_END - S_START),
-        "storage": "bf16 rows c_kv 512 + k_pe 64, rotation in f32", "alg_bytes_per_step": alg_bytes})
+        "layers": LAYERS, "tokens": TOKENS, "page_size": PAGE, "span": [S_START, S_END], "stub_rows": STUB,
+        "delta": STUB - (S_END - S_START), "storage": "bf16 rows c_kv 512 + k_pe 64, rotation in f32",
+        "alg_bytes_per_step": alg_bytes,
+        "sequences": f"{NSEQ} of this shape, one spliced per step, each on its own randomly permuted pages"
+                     if distinct else "one, its page table restored before every splice (more steps than "
+                                      f"{MAX_DISTINCT_SEQS} distinct sequences)",
+        "pool_pages": POOL_PAGES})
     out["pct_hbm_peak"] = round(100.0 * value / HBM_PEAK_GBS, 2)
+    out["step_with_table_restore_ms"] = round(ms_restore, 5)
+    if ms_host_plan is not None:
+        out["step_host_staged_plan_ms"] = round(ms_host_plan, 5)
     out["splice_latency_us"] = {"median": round(statistics.median(lat), 1), "min": round(min(lat), 1),
-                                "max": round(max(lat), 1), "runs": len(lat)}
+                                "max": round(max(lat), 1), "runs": len(lat),
+                                "host_call_median": round(statistics.median(host), 1)}
     out["roofline"] = roofline("splice_kernel", "splice_32k_27layer", launches, kernel_ms, kernel_bytes)
     out["copy_ceiling_gbs"] = round(copy_ceiling(torch, dev, alg_bytes // 2), 1)
     out["cpu_baseline"] = None
     if host_before is not None:
-        out["cpu_baseline"] = cpu_baseline_splice(host_before, gpu_after, T, alg_bytes, args.cpu_seconds,
-                                                  LAYERS, TOKENS, PAGE, POOL_PAGES, S_START, S_END, STUB)
+        out["cpu_baseline"] = cpu_baseline_splice(host_before, gpu_after, T0, alg_bytes, args.cpu_seconds,
+                                                  LAYERS, TOKENS, PAGE, 2 * NP, S_START, S_END, STUB)
         del host_before, gpu_after
         out["cpu_baseline_layer_parallel"] = cpu_baseline_layer_parallel(
-            T, alg_bytes, args.cpu_seconds / 2, LAYERS, TOKENS, PAGE, POOL_PAGES, S_START, S_END, STUB)
+            T0, alg_bytes, args.cpu_seconds / 2, LAYERS, TOKENS, PAGE, 2 * NP, S_START, S_END, STUB)
     pool.close()
     return out
 
 
 def cpu_baseline_splice(host_before, gpu_after, T, alg_bytes, seconds, LAYERS, TOKENS, PAGE, POOL_PAGES,
-                        S_START, S_END, STUB):
+                        S_START, S_END, STUB, stub_seed=1000):
     """The oracle, as it stands, on the same splice on the host: repeated
-    until `seconds` have passed; also checks the GPU result against it."""
+    until `seconds` have passed; also checks the GPU result against it.
+    host_before holds the sequence's pages (T is a permutation of them); the
+    oracle's pool adds free pages after them up to POOL_PAGES."""
     import torch
     from oracle import leyline_oracle as O
     from synth import random_rows_torch
 
     st = O.CacheState.empty(0, POOL_PAGES, PAGE, TOKENS // PAGE + 8, with_rows=False)
-    st.layers = [host_before[i] for i in range(LAYERS)]
+    pad = np.zeros((POOL_PAGES - host_before.shape[1], PAGE, ROW), np.uint16)
+    st.layers = [np.concatenate([host_before[i], pad]) for i in range(LAYERS)]
     st.set_pages(0, T, TOKENS)
-    stub_host = random_rows_torch(1, (LAYERS, STUB, ROW), "cuda:0").view(torch.int16).cpu().numpy().view(np.uint16)
+    stub_host = random_rows_torch(stub_seed, (LAYERS, STUB, ROW), "cuda:0").view(torch.int16).cpu().numpy().view(
+        np.uint16)
     d = [O.Directive(0, S_START, S_END, STUB, stub_host)]
     runs, t = 0, 0.0
     new = None
