@@ -212,6 +212,7 @@ struct ll_pool {
   char* d_direct = nullptr;     // tasks, tables and rotation tables of device-planned splices
   size_t direct_cap = 0;
   bool poisoned = false;
+  std::vector<double> theta;    // RoPE frequencies of the pool's band (float64)
   ll_plan_stats last{};
   int32_t prof_every = 0;       // time every n-th launch of each kernel (0: none)
   int64_t prof_tick[3] = {0, 0, 0};
@@ -561,6 +562,23 @@ ll_status upload(ll_pool* p, Staging* s, hipStream_t st) {
   }
   if (e != hipSuccess) return device_fail(p, e, "hipMemcpyAsync(H2D staging)");
   return LL_OK;
+}
+
+// theta_j = base^(-2j/rope_dim), j < rope_dim / 2, in float64.
+std::vector<double> rope_thetas(double base, int rope_dim) {
+  std::vector<double> t(static_cast<size_t>(rope_dim / 2));
+  for (int j = 0; j < rope_dim / 2; ++j) t[static_cast<size_t>(j)] = std::pow(base, -2.0 * j / rope_dim);
+  return t;
+}
+
+// The float32 cos/sin of the angles delta * theta_j (float64 angle, cos and
+// sin, then rounding), from a precomputed theta table.
+void rope_table_from(const std::vector<double>& theta, int64_t delta, float* c, float* s) {
+  for (size_t j = 0; j < theta.size(); ++j) {
+    const double ang = static_cast<double>(delta) * theta[j];
+    c[j] = static_cast<float>(std::cos(ang));
+    s[j] = static_cast<float>(std::sin(ang));
+  }
 }
 
 void rope_table(double base, int rope_dim, int64_t delta, float* c, float* s) {
@@ -957,6 +975,7 @@ ll_status setup_pool(ll_pool* p, ll_pool** out) {
   p->seqs.resize(static_cast<size_t>(d.max_seqs));
   p->free.init(d.num_pages);
   p->page_slot.assign(static_cast<size_t>(d.num_pages), -1);
+  p->theta = rope_thetas(d.rope_base, d.rope_dim);
   hipError_t e = hipMalloc(reinterpret_cast<void**>(&p->d_layers), sizeof(void*) * p->num_planes);
   if (e == hipSuccess)
     e = hipMemcpy(p->d_layers, p->layer_ptrs.data(), sizeof(void*) * p->num_planes, hipMemcpyHostToDevice);
@@ -1357,7 +1376,7 @@ ll_status leyline_splice(ll_pool* p, const ll_directive* dirs, int32_t n, void* 
       cos_out = ddirs[i].cos_;
       sin_out = ddirs[i].sin_;
     }
-    rope_table(p->desc.rope_base, 2 * pairs, pl.delta, cos_out, sin_out);
+    rope_table_from(p->theta, pl.delta, cos_out, sin_out);
     const ll::chunk_t* stub_v = static_cast<const ll::chunk_t*>(d.mode == LL_FORGET ? nullptr : d.r_rows_v);
     const int64_t stub_v_chunks = (d.r_layer_stride_bytes_v ? d.r_layer_stride_bytes_v : r * p->row_bytes) / 16;
     if (!direct && p->gqa) {
@@ -1441,13 +1460,17 @@ ll_status leyline_splice(ll_pool* p, const ll_directive* dirs, int32_t n, void* 
   stats.fresh_pages = need;
   stats.table_entries = n_entries;
   stats.planned_on_device = direct ? 1 : 0;
+  // old pages no new page keeps: released once the call is committed
+  std::vector<int32_t> released;
   for (int32_t i = 0; i < n; ++i) {
     const SeqState& s = p->seqs[dirs[i].seq_id];
     std::vector<char> kept(s.pages.size(), 0);
     for (int32_t x : plans[i].reuse)
       if (x >= 0) kept[x] = 1;
-    for (size_t k = 0; k < kept.size(); ++k) stats.freed_pages += kept[k] ? 0 : 1;
+    for (size_t k = 0; k < kept.size(); ++k)
+      if (!kept[k]) released.push_back(s.pages[k]);
   }
+  stats.freed_pages = static_cast<int64_t>(released.size());
   const int64_t L = p->desc.num_layers;
   stats.alg_bytes = p->num_planes * 2 * p->row_bytes * stats.rows_moved + L * 2 * p->band_bytes * stats.rows_rotated_inplace;
   hipError_t e;
@@ -1539,13 +1562,9 @@ ll_status leyline_splice(ll_pool* p, const ll_directive* dirs, int32_t n, void* 
   // --- commit host state
   for (int32_t pg : fresh) p->free.take(pg);
   p->free.advance_hint();
+  for (int32_t pg : released) p->free.give(pg);
   for (int32_t i = 0; i < n; ++i) {
     SeqState& s = p->seqs[dirs[i].seq_id];
-    std::vector<char> kept(s.pages.size(), 0);
-    for (int32_t x : plans[i].reuse)
-      if (x >= 0) kept[x] = 1;
-    for (size_t k = 0; k < kept.size(); ++k)
-      if (!kept[k]) p->free.give(s.pages[k]);
     s.pages = std::move(new_tables[i]);
     s.len = plans[i].n_new;
     s.next_pos = plans[i].next_pos;

@@ -169,11 +169,16 @@ def _i32_array(values):
     return a, a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
 
 
-def _stream_handle(stream) -> int | None:
+def _stream_handle(stream, device: int) -> int:
+    """The hipStream_t of `stream`, or of the current torch stream of
+    `device` (the device the pool or context lives on) when stream is None."""
+    if stream is not None:
+        return stream.cuda_stream
     import torch
-    if stream is None:
-        stream = torch.cuda.current_stream()
-    return stream.cuda_stream
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is not None:
+        return raw(device)
+    return torch.cuda.current_stream(device).cuda_stream
 
 
 def rope_delta_table(delta: int, rope_dim: int = ROPE_DIM, base: float = 10000.0):
@@ -244,6 +249,7 @@ class Pool:
         self.num_pages, self.page_size = shape[0], shape[1]
         self.max_seqs, self.max_pages_per_seq = page_table.shape
         self.device = layer_list[0].device
+        self._dev = self.device.index or 0
         self._ptrs = (ctypes.c_void_p * self.num_layers)(*[t.data_ptr() for t in layer_list])
         d = _PoolDesc(self.num_layers, self.page_size, self.num_pages, self.max_seqs, self.max_pages_per_seq,
                       KV_LORA_RANK, ROPE_DIM, pairing, rope_base,
@@ -268,12 +274,12 @@ class Pool:
     # -- sequences
     def seq_alloc(self, n_tokens: int, stream=None) -> int:
         sid = ctypes.c_int32()
-        _check(_lib.ll_seq_alloc(self._h, int(n_tokens), ctypes.byref(sid), _stream_handle(stream)))
+        _check(_lib.ll_seq_alloc(self._h, int(n_tokens), ctypes.byref(sid), _stream_handle(stream, self._dev)))
         return sid.value
 
     def seq_set_pages(self, seq: int, pages, n_tokens: int, stream=None) -> None:
         arr, ptr = _i32_array(pages)
-        _check(_lib.ll_seq_set_pages(self._h, int(seq), ptr, int(n_tokens), _stream_handle(stream)))
+        _check(_lib.ll_seq_set_pages(self._h, int(seq), ptr, int(n_tokens), _stream_handle(stream, self._dev)))
 
     def seq_free(self, seq: int) -> None:
         _check(_lib.ll_seq_free(self._h, int(seq)))
@@ -322,7 +328,7 @@ class Pool:
                 raise ValueError("stub_v without stub")
             arr[i] = _Directive(int(d.seq), int(d.mode), int(d.s_start), int(d.s_end), int(r_len), ptr, stride,
                                 ptr_v, stride_v)
-        _check(_lib.leyline_splice(self._h, arr, n, _stream_handle(stream)))
+        _check(_lib.leyline_splice(self._h, arr, n, _stream_handle(stream, self._dev)))
 
     def evict(self, seqs, keep, offsets, stream=None) -> None:
         """keep: uint8 CUDA tensor holding every mask; offsets[i]: start of
@@ -334,7 +340,7 @@ class Pool:
         o_arr = np.ascontiguousarray(np.asarray(offsets, dtype=np.int64))
         _check(_lib.kv_evict_compact(self._h, s_ptr, len(s_arr), keep.data_ptr(),
                                      o_arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
-                                     _stream_handle(stream)))
+                                     _stream_handle(stream, self._dev)))
 
     def rope_rows(self, seq: int, row_begin: int, angles, out=None, stream=None):
         """Turn the RoPE bands of rows [row_begin, row_begin + len(angles)) of
@@ -355,12 +361,12 @@ class Pool:
                 raise ValueError("out must be a bf16 CUDA tensor [num_layers][n][row]")
             ptr, stride = out.data_ptr(), out.stride(0) * 2
         _check(_lib.ll_rope_rows(self._h, int(seq), int(row_begin), int(n), angles.data_ptr() if n else None,
-                                 ptr, stride, _stream_handle(stream)))
+                                 ptr, stride, _stream_handle(stream, self._dev)))
         return out
 
     def ptable_reindex(self, seq: int, keep_pages, stream=None) -> None:
         arr, ptr = _i32_array(keep_pages)
-        _check(_lib.ll_ptable_reindex(self._h, int(seq), ptr, len(arr), _stream_handle(stream)))
+        _check(_lib.ll_ptable_reindex(self._h, int(seq), ptr, len(arr), _stream_handle(stream, self._dev)))
 
     # -- counters
     def last_stats(self) -> PlanStats:
@@ -424,6 +430,7 @@ class GqaPool(Pool):
         self.row = self.heads * self.head_dim
         self.max_seqs, self.max_pages_per_seq = page_table.shape
         self.device = k_list[0].device
+        self._dev = self.device.index or 0
         self._kptrs = (ctypes.c_void_p * self.num_layers)(*[t.data_ptr() for t in k_list])
         self._vptrs = (ctypes.c_void_p * self.num_layers)(*[t.data_ptr() for t in v_list])
         d = _GqaPoolDesc(self.num_layers, self.page_size, self.num_pages, self.max_seqs, self.max_pages_per_seq,
@@ -514,7 +521,7 @@ class KvsMask:
                    torch.empty(logs.n, dtype=torch.int32, device=dev))
         death, status = out
         _check(_lib.kvs_death_times(self._h, logs.logs, logs.n, int(n_pad), logs.keep.data_ptr(), death.data_ptr(),
-                                    status.data_ptr(), _stream_handle(stream)))
+                                    status.data_ptr(), _stream_handle(stream, self.device)))
         self._last_logs = logs  # the kernel reads the keep buffer after this returns
         return death, status
 
@@ -527,7 +534,7 @@ class KvsMask:
         pn, fn = torch.zeros((n, nq), **kw), torch.zeros((n, nq), **kw)
         pi, fi = torch.full((n, nq, nk), -1, **kw), torch.full((n, nq, nk), -1, **kw)
         _check(_lib.kvs_block_mask(self._h, death.data_ptr(), n, n_pad, int(block_q), int(block_k), pn.data_ptr(),
-                                   pi.data_ptr(), fn.data_ptr(), fi.data_ptr(), _stream_handle(stream)))
+                                   pi.data_ptr(), fn.data_ptr(), fi.data_ptr(), _stream_handle(stream, self.device)))
         return pn, pi, fn, fi
 
     def dense_mask(self, death, out=None, stream=None):
@@ -536,5 +543,5 @@ class KvsMask:
         n, n_pad = death.shape
         if out is None:
             out = torch.empty((n, n_pad, n_pad // 32), dtype=torch.int32, device=death.device)
-        _check(_lib.kvs_dense_mask(self._h, death.data_ptr(), n, n_pad, out.data_ptr(), _stream_handle(stream)))
+        _check(_lib.kvs_dense_mask(self._h, death.data_ptr(), n, n_pad, out.data_ptr(), _stream_handle(stream, self.device)))
         return out
