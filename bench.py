@@ -91,7 +91,8 @@ def parse():
 # device helpers and the launch structures.
 KERNEL_SOURCE = {"splice_kernel": "kernels.hip", "evict_move_kernel": "kernels.hip",
                  "gqa_splice_kernel": "kernels_gqa.hip", "plane_evict_kernel": "kernels_gqa.hip",
-                 "kvs_dense_kernel": "kernels_kvs.hip", "rope_rows_kernel": "kernels_rows.hip"}
+                 "kvs_dense_kernel": "kernels_kvs.hip", "rope_rows_kernel": "kernels_rows.hip",
+                 "rope_gather_mla_kernel": "kernels_rows.hip"}
 
 
 def kernel_source_sha(kernel: str) -> str:
@@ -832,7 +833,10 @@ def bench_rope_rows(args):
         "layers": LAYERS, "tokens": TOKENS, "page_size": PAGE, "angles": "-position of each row",
         "mode": "gather to a dense buffer", "alg_bytes_per_step": alg})
     out_line["metric"] = "per-row-angle RoPE rotation: row bytes GB/s"
-    out_line["roofline"] = roofline("rope_rows_kernel", "rope_rows_32k_27layer", launches, kernel_ms, kernel_bytes)
+    # MLA rows at page size 16 are gathered by rope_gather_mla_kernel (the
+    # timed launch also holds the per-row table kernel)
+    out_line["roofline"] = roofline("rope_gather_mla_kernel", "rope_rows_32k_27layer", launches, kernel_ms,
+                                    kernel_bytes)
     out_line["in_place"] = {"ms_per_step": round(ip_ms, 5), "kernel_avg_us": round(ip_kernel_ms * 1e3 / max(1, ip_launches), 2),
                             "alg_bytes": ip_bytes // max(1, ip_launches),
                             "achieved_gbs": round(ip_bytes / max(1e-9, ip_kernel_ms * 1e-3) / 1e9, 1)}

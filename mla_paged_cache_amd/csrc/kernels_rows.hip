@@ -11,6 +11,8 @@
 //  * rope_rows_kernel: the flat gather of the rows (gather mode: whole rows
 //    to a dense buffer; in place: the bands only), two chunks per thread so a
 //    thread holds both halves of its pairs in half-split layout.
+//  * rope_gather_mla_kernel: the gather of MLA rows at page size >= 8, page
+//    by page in the splice kernel's chunk order (copy waves and turn waves).
 #include "device_common.h"
 #include "rows_internal.h"
 
@@ -118,6 +120,96 @@ __global__ __launch_bounds__(256) void rope_rows_kernel(RopeRowsLaunch a) {
   __builtin_nontemporal_store(vb, dst + cb);
 }
 
+// MLA rows gathered page by page.  Within one logical page of P rows the 64
+// c_kv chunks of every row come first, then the 8 k_pe chunks of every row,
+// so that (P >= 8) every wave either only copies (one row's c_kv, 1 KiB
+// contiguous per load instruction) or only turns k_pe chunks; a turning lane
+// reads its row's float32 table.  Two chunks per thread, 256 apart, both loads
+// issued before either store.  The page of a wave is one scalar load.
+template <int PAIRING>
+__global__ __launch_bounds__(256) void rope_gather_mla_kernel(RopeRowsLaunch a) {
+  constexpr int CPT = 2;
+  constexpr uint32_t kRow = kRowChunks;                 // 72
+  constexpr uint32_t kKpe = kRowChunks - kKpeChunk0;   // 8
+  const int64_t b = blockIdx.x;
+  const int plane = static_cast<int>(b / a.blocks_per_plane);
+  const uint32_t c0 = static_cast<uint32_t>((b - static_cast<int64_t>(plane) * a.blocks_per_plane) * 256 * CPT +
+                                            threadIdx.x);
+  const int shift = a.page_shift;
+  const int64_t row_end = a.row_begin + a.n;
+  const chunk_t* layer = a.planes[plane];
+  chunk_t* out = a.out + plane * a.out_plane_chunks;
+  chunk_t v[CPT];
+  const chunk_t* srcs[CPT];
+  int64_t dsts[CPT];
+  bool lives[CPT];
+  int kcs[CPT];
+  int64_t tabs[CPT];
+#pragma unroll
+  for (int u = 0; u < CPT; ++u) {
+    const uint32_t c = c0 + u * 256;
+    // wave-uniform: a page is 72 P chunks, a multiple of 64
+    const uint32_t task = __builtin_amdgcn_readfirstlane((c / kRow) >> shift);
+    const uint32_t lc = c - task * (kRow << shift);
+    uint32_t r, col;
+    if (lc < (static_cast<uint32_t>(kKpeChunk0) << shift)) {
+      r = lc / kKpeChunk0;
+      col = lc - r * kKpeChunk0;
+    } else {
+      const uint32_t k = lc - (static_cast<uint32_t>(kKpeChunk0) << shift);
+      r = k / kKpe;
+      col = kKpeChunk0 + (k - r * kKpe);
+    }
+    const bool in_range = task < a.n_pages;
+    using cptr = const __attribute__((address_space(4))) int32_t*;
+    // n_pages >= 1; past the last page the lanes are dead and read page 0's entry
+    const int32_t page = *reinterpret_cast<cptr>(reinterpret_cast<uintptr_t>(a.pages + (in_range ? task : 0)));
+    const int64_t j = ((a.first_page + task) << shift) + r;
+    lives[u] = in_range && j >= a.row_begin && j < row_end;
+    srcs[u] = layer + ((static_cast<int64_t>(page) << shift) + r) * kRow + col;
+    const int64_t i = j - a.row_begin;
+    dsts[u] = i * kRow + col;
+    kcs[u] = static_cast<int>(col) - kKpeChunk0;
+    tabs[u] = i * 2 * kHalfPairs;
+  }
+#pragma unroll
+  for (int u = 0; u < CPT; ++u) {
+    v[u] = chunk_t{0u, 0u, 0u, 0u};
+    if (lives[u]) v[u] = __builtin_nontemporal_load(srcs[u]);
+  }
+#pragma unroll
+  for (int u = 0; u < CPT; ++u) {
+    if (kcs[u] >= 0) {  // a turn wave: every lane takes part (half-split lanes trade chunks)
+      const int kc = kcs[u];
+      const float* cs = a.tab + (lives[u] ? tabs[u] : 0);
+      const float* sn = cs + kHalfPairs;
+      if constexpr (PAIRING == 0) {
+        if (lives[u]) {
+          float c4[4], s4[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            c4[e] = cs[4 * kc + e];
+            s4[e] = sn[4 * kc + e];
+          }
+          v[u] = rotate_interleaved(v[u], c4, s4);
+        }
+      } else {
+        const chunk_t other = shfl_xor4(v[u]);
+        if (lives[u]) {
+          float c8[8], s8[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            c8[e] = cs[8 * (kc & 3) + e];
+            s8[e] = sn[8 * (kc & 3) + e];
+          }
+          v[u] = rotate_half(v[u], other, kc < 4, c8, s8);
+        }
+      }
+    }
+    if (lives[u]) __builtin_nontemporal_store(v[u], out + dsts[u]);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_rope_table(const RopeTableLaunch& a, hipStream_t s, const Stamp& t) {
@@ -126,10 +218,25 @@ hipError_t launch_rope_table(const RopeTableLaunch& a, hipStream_t s, const Stam
   return dispatch(rope_table_kernel, dim3(static_cast<unsigned>((pairs + 255) / 256)), dim3(256), s, t, true, true, a);
 }
 
+bool rope_gather_by_page(const RopeRowsLaunch& a) {
+  const RowShape& sh = a.shape;
+  return a.out != nullptr && a.page_shift >= 3 && sh.heads == 1 && sh.row_chunks == kRowChunks &&
+         sh.band_off == kKpeChunk0 && (1 << sh.band_shift) == kRowChunks - kKpeChunk0;
+}
+
+int64_t rope_rows_blocks_per_plane(const RopeRowsLaunch& a, int64_t per_row) {
+  if (rope_gather_by_page(a)) return flat_blocks(a.n_pages * (int64_t{kRowChunks} << a.page_shift), 2);
+  return flat_blocks(a.n * per_row);
+}
+
 hipError_t launch_rope_rows(const RopeRowsLaunch& a, int pairing, hipStream_t s, const Stamp& t) {
   const int64_t grid = a.blocks_per_plane * a.num_planes;
   if (grid == 0) return stamp_empty(s, t);
-  void (*k)(RopeRowsLaunch) = pairing == 0 ? rope_rows_kernel<0> : rope_rows_kernel<1>;
+  void (*k)(RopeRowsLaunch);
+  if (rope_gather_by_page(a))
+    k = pairing == 0 ? rope_gather_mla_kernel<0> : rope_gather_mla_kernel<1>;
+  else
+    k = pairing == 0 ? rope_rows_kernel<0> : rope_rows_kernel<1>;
   return dispatch(k, dim3(static_cast<unsigned>(grid)), dim3(256), s, t, true, true, a);
 }
 

@@ -1936,7 +1936,8 @@ ll_status ll_rope_rows(ll_pool* p, int32_t seq, int64_t row_begin, int64_t n_row
   a.tab = p->d_rowtab;
   a.out = static_cast<ll::chunk_t*>(out_dev);
   a.out_plane_chunks = (out_layer_stride_bytes ? out_layer_stride_bytes : n_rows * p->row_bytes) / 16;
-  a.blocks_per_plane = ll::flat_blocks(n_rows * per_row);
+  a.n_pages = n_pages;
+  a.blocks_per_plane = ll::rope_rows_blocks_per_plane(a, per_row);
   ProfRec rec{};
   ll::Stamp ts;
   if (prof_pick(p, 2) && (rc = prof_begin(p, &rec, &ts))) return rc;

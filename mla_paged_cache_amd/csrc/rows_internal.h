@@ -40,9 +40,13 @@ struct RopeRowsLaunch {
   chunk_t* out;                  // gather target, or nullptr for in place
   int64_t out_plane_chunks;      // chunks between planes of out
   int64_t blocks_per_plane;
+  int64_t n_pages;               // logical pages the rows touch (first_page ..)
 };
 
 hipError_t launch_rope_table(const RopeTableLaunch& a, hipStream_t s, const Stamp& t = Stamp{});
 hipError_t launch_rope_rows(const RopeRowsLaunch& a, int pairing, hipStream_t s, const Stamp& t = Stamp{});
+// Blocks per plane of the launch launch_rope_rows picks for `a` (all fields
+// but blocks_per_plane set); per_row: threads per row of the row-unit kernel.
+int64_t rope_rows_blocks_per_plane(const RopeRowsLaunch& a, int64_t per_row);
 
 }  // namespace ll

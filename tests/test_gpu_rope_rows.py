@@ -41,7 +41,7 @@ def _cmp_rows(got, exp, bands, width):
     return int(np.count_nonzero(d))
 
 
-@pytest.mark.parametrize("P,pairing", [(1, 0), (16, 0), (16, 1)])
+@pytest.mark.parametrize("P,pairing", [(1, 0), (8, 1), (16, 0), (16, 1), (32, 0)])
 def test_mla_gather_and_in_place(P, pairing):
     L = need_gpu()
     say(f"rope rows MLA P={P} pairing={pairing}")
