@@ -1276,6 +1276,7 @@ ll_status leyline_splice(ll_pool* p, const ll_directive* dirs, int32_t n, void* 
                 n * 2 * pairs <= ll::kDirectTrigFloats;
   std::vector<int32_t> run_page, run_first;
   std::vector<int32_t> q_fresh0(static_cast<size_t>(n), 0), q_rot0(static_cast<size_t>(n), 0);
+  std::vector<int32_t> n_rot_of(static_cast<size_t>(n), 0);
   for (size_t k = 0; direct && k < fresh.size(); ++k) {
     if (k > 0 && fresh[k] == fresh[k - 1] + 1) continue;
     if (run_page.size() == static_cast<size_t>(ll::kDirectMaxRuns)) direct = false;
@@ -1299,6 +1300,7 @@ ll_status leyline_splice(ll_pool* p, const ll_directive* dirs, int32_t n, void* 
     }
     q_fresh0[i] = static_cast<int32_t>(std::max<int64_t>(f0, 0));
     q_rot0[i] = static_cast<int32_t>(std::max<int64_t>(r0, 0));
+    n_rot_of[i] = static_cast<int32_t>(nr);
   }
   const size_t n_tasks = static_cast<size_t>(n_move_tasks + n_rot_tasks);
   // offsets of the tasks, rotation tables, table writes and tables from the
@@ -1353,6 +1355,116 @@ ll_status leyline_splice(ll_pool* p, const ll_directive* dirs, int32_t n, void* 
     dev_base = sg->dev;
   }
 
+  ProfRec rec{};
+  ll::Stamp ts;
+  auto launch_rows = [&]() -> ll_status {
+    hipError_t e;
+    if (p->gqa) {
+      ll::GqaSpliceLaunch a{};
+      a.planes = reinterpret_cast<const ll::chunk_t* const*>(p->d_layers);
+      a.num_layers = p->desc.num_layers;
+      a.page_shift = p->page_shift;
+      a.row_chunks = static_cast<int32_t>(row_chunks);
+      a.head_chunks = p->head_chunks;
+      a.rot_shift = p->rot_shift;
+      a.heads = p->heads;
+      a.tasks = reinterpret_cast<const ll::SpliceTask*>(dev_base + o_t);
+      a.n_move_tasks = n_move_tasks;
+      a.n_rot_tasks = n_rot_tasks;
+      // one thread per two chunks in K and V planes (row_chunks is even:
+      // head_dim is a multiple of 16)
+      a.move_blocks_per_plane = ll::flat_blocks(n_move_tasks * P * (row_chunks / 2));
+      a.rot_blocks_per_plane = ll::flat_blocks(n_rot_tasks * P * (p->heads << (p->rot_shift - 1)));
+      a.dirs = reinterpret_cast<const ll::GqaDir*>(dev_base + o_d);
+      a.twrites = reinterpret_cast<const ll::TableWrite*>(dev_base + o_w);
+      a.tables = reinterpret_cast<const int32_t*>(dev_base + o_p);
+      a.n_twrites = n;
+      a.max_pages_per_seq = p->desc.max_pages_per_seq;
+      a.page_table = p->desc.page_table;
+      if (prof_pick(p, 0) && (rc = prof_begin(p, &rec, &ts))) return rc;
+      e = ll::launch_gqa_splice(a, p->desc.rope_pairing, st, ts);
+      if (e != hipSuccess) return device_fail(p, e, "gqa_splice_kernel launch");
+    } else {
+      ll::SpliceLaunch a{};
+      a.layers = reinterpret_cast<const ll::chunk_t* const*>(p->d_layers);
+      a.num_layers = p->desc.num_layers;
+      a.page_shift = p->page_shift;
+      a.tasks = reinterpret_cast<const ll::SpliceTask*>(dev_base + o_t);
+      a.n_move_tasks = n_move_tasks;
+      a.n_rot_tasks = n_rot_tasks;
+      a.move_blocks_per_layer = ll::flat_blocks(n_move_tasks * P * ll::kRowChunks, ll::kSpliceChunksPerThread);
+      a.rot_blocks_per_layer = ll::flat_blocks(n_rot_tasks * P * (ll::kRowChunks - ll::kKpeChunk0), ll::kSpliceChunksPerThread);
+      a.dirs = reinterpret_cast<const ll::SpliceDir*>(dev_base + o_d);
+      a.twrites = reinterpret_cast<const ll::TableWrite*>(dev_base + o_w);
+      a.tables = reinterpret_cast<const int32_t*>(dev_base + o_p);
+      a.n_twrites = n;
+      a.max_pages_per_seq = p->desc.max_pages_per_seq;
+      a.page_table = p->desc.page_table;
+      if (prof_pick(p, 0) && (rc = prof_begin(p, &rec, &ts))) return rc;
+      e = ll::launch_splice(a, p->desc.rope_pairing, st, ts);
+      if (e != hipSuccess) return device_fail(p, e, "splice_kernel launch");
+    }
+    return LL_OK;
+  };
+  if (direct) {
+    // the compact plan from per-directive counts; the launches go out before
+    // the host's own tables and counters are made
+    int64_t mb = 0, rb = 0, pk = 0;
+    for (int32_t i = 0; i < n; ++i) {
+      const ll_directive& d = dirs[i];
+      const SplicePlan& pl = plans[i];
+      const int64_t r = d.mode == LL_FORGET ? 0 : d.r_len;
+      float* cos_out = da.trig + 2 * pairs * i;
+      rope_table_from(p->theta, pl.delta, cos_out, cos_out + pairs);
+      ll::DirectDir& dd = da.d[i];
+      dd.stub = static_cast<const ll::chunk_t*>(d.mode == LL_FORGET ? nullptr : d.r_rows);
+      dd.stub_layer_chunks = (d.r_layer_stride_bytes ? d.r_layer_stride_bytes : r * p->row_bytes) / 16;
+      dd.stub_v = p->gqa ? static_cast<const ll::chunk_t*>(d.mode == LL_FORGET ? nullptr : d.r_rows_v) : nullptr;
+      dd.stub_v_layer_chunks =
+          p->gqa ? (d.r_layer_stride_bytes_v ? d.r_layer_stride_bytes_v : r * p->row_bytes) / 16 : 0;
+      dd.seq = d.seq_id;
+      dd.s_start = static_cast<int32_t>(d.s_start);
+      dd.stub_end = static_cast<int32_t>(d.s_start + r);
+      dd.delta = static_cast<int32_t>(pl.delta);
+      dd.n_new = static_cast<int32_t>(pl.n_new);
+      dd.old_pages = static_cast<int32_t>(p->seqs[d.seq_id].pages.size());
+      dd.rotate = (d.mode == LL_AMORTIZE && pl.delta != 0) ? 1 : 0;
+      dd.q_fresh0 = q_fresh0[i];
+      dd.q_rot0 = q_rot0[i];
+      dd.move_base = static_cast<int32_t>(mb);
+      dd.rot_base = static_cast<int32_t>(rb);
+      dd.fresh_base = static_cast<int32_t>(mb);
+      dd.packed_off = static_cast<int32_t>(pk);
+      mb += pl.fresh;
+      rb += n_rot_of[i];
+      pk += static_cast<int64_t>(pl.reuse.size());
+    }
+    da.n_dirs = n;
+    da.page_shift = p->page_shift;
+    da.pairs = pairs;
+    da.n_runs = static_cast<int32_t>(run_page.size());
+    da.max_pages_per_seq = p->desc.max_pages_per_seq;
+    da.gqa = p->gqa ? 1 : 0;
+    da.n_move_tasks = n_move_tasks;
+    da.n_rot_tasks = n_rot_tasks;
+    da.n_entries = n_entries;
+    da.page_table = p->desc.page_table;
+    da.tasks = reinterpret_cast<ll::SpliceTask*>(dev_base + o_t);
+    da.dirs = dev_base + o_d;
+    da.twrites = reinterpret_cast<ll::TableWrite*>(dev_base + o_w);
+    da.tables = reinterpret_cast<int32_t*>(dev_base + o_p);
+    for (size_t k = 0; k < run_page.size(); ++k) {
+      da.run_page[k] = run_page[k];
+      da.run_first[k] = run_first[k];
+    }
+    da.run_first[run_page.size()] = static_cast<int32_t>(fresh.size());
+    int32_t max_new_pages = 0;
+    for (const SplicePlan& pl : plans) max_new_pages = std::max(max_new_pages, static_cast<int32_t>(pl.reuse.size()));
+    hipError_t e = ll::launch_splice_plan(da, max_new_pages, st);
+    if (e != hipSuccess) return device_fail(p, e, "splice_plan_kernel launch");
+    if ((rc = launch_rows())) return rc;
+  }
+
   std::vector<std::vector<int32_t>> new_tables(static_cast<size_t>(n));
   ll_plan_stats stats{};
   size_t cursor = 0;
@@ -1364,24 +1476,13 @@ ll_status leyline_splice(ll_pool* p, const ll_directive* dirs, int32_t n, void* 
     const std::vector<int32_t>& T = s.pages;
     const int64_t old_pages = static_cast<int64_t>(T.size());
     const int64_t r = d.mode == LL_FORGET ? 0 : d.r_len;
-    float* cos_out;
-    float* sin_out;
-    if (direct) {
-      cos_out = da.trig + 2 * pairs * i;
-      sin_out = cos_out + pairs;
-    } else if (p->gqa) {
-      cos_out = gdirs[i].cos_;
-      sin_out = gdirs[i].sin_;
-    } else {
-      cos_out = ddirs[i].cos_;
-      sin_out = ddirs[i].sin_;
-    }
-    rope_table_from(p->theta, pl.delta, cos_out, sin_out);
-    const ll::chunk_t* stub_v = static_cast<const ll::chunk_t*>(d.mode == LL_FORGET ? nullptr : d.r_rows_v);
-    const int64_t stub_v_chunks = (d.r_layer_stride_bytes_v ? d.r_layer_stride_bytes_v : r * p->row_bytes) / 16;
-    if (!direct && p->gqa) {
-      gdirs[i].stub_v = stub_v;
-      gdirs[i].stub_v_layer_chunks = stub_v_chunks;
+    if (!direct) {
+      rope_table_from(p->theta, pl.delta, p->gqa ? gdirs[i].cos_ : ddirs[i].cos_,
+                      p->gqa ? gdirs[i].sin_ : ddirs[i].sin_);
+      if (p->gqa) {
+        gdirs[i].stub_v = static_cast<const ll::chunk_t*>(d.mode == LL_FORGET ? nullptr : d.r_rows_v);
+        gdirs[i].stub_v_layer_chunks = (d.r_layer_stride_bytes_v ? d.r_layer_stride_bytes_v : r * p->row_bytes) / 16;
+      }
     }
     ll::SpliceTask base{};
     base.dir = i;
@@ -1394,26 +1495,6 @@ ll_status leyline_splice(ll_pool* p, const ll_directive* dirs, int32_t n, void* 
     base.stub_layer_chunks = (d.r_layer_stride_bytes ? d.r_layer_stride_bytes : r * p->row_bytes) / 16;
     base.pre_page = base.down_page0 = base.down_page1 = -1;
     base.down_lp0 = -1;
-    if (direct) {
-      ll::DirectDir& dd = da.d[i];
-      dd.stub = base.stub;
-      dd.stub_layer_chunks = base.stub_layer_chunks;
-      dd.stub_v = p->gqa ? stub_v : nullptr;
-      dd.stub_v_layer_chunks = p->gqa ? stub_v_chunks : 0;
-      dd.seq = d.seq_id;
-      dd.s_start = base.s_start;
-      dd.stub_end = base.stub_end;
-      dd.delta = base.delta;
-      dd.n_new = base.n_new;
-      dd.old_pages = static_cast<int32_t>(old_pages);
-      dd.rotate = base.rotate;
-      dd.q_fresh0 = q_fresh0[i];
-      dd.q_rot0 = q_rot0[i];
-      dd.move_base = static_cast<int32_t>(move_at);
-      dd.rot_base = static_cast<int32_t>(rot_at);
-      dd.fresh_base = static_cast<int32_t>(cursor);
-      dd.packed_off = static_cast<int32_t>(packed_at);
-    }
     std::vector<int32_t>& nt = new_tables[i];
     nt.resize(pl.reuse.size());
     for (size_t q = 0; q < pl.reuse.size(); ++q) {
@@ -1473,80 +1554,9 @@ ll_status leyline_splice(ll_pool* p, const ll_directive* dirs, int32_t n, void* 
   stats.freed_pages = static_cast<int64_t>(released.size());
   const int64_t L = p->desc.num_layers;
   stats.alg_bytes = p->num_planes * 2 * p->row_bytes * stats.rows_moved + L * 2 * p->band_bytes * stats.rows_rotated_inplace;
-  hipError_t e;
-  if (direct) {
-    da.n_dirs = n;
-    da.page_shift = p->page_shift;
-    da.pairs = pairs;
-    da.n_runs = static_cast<int32_t>(run_page.size());
-    da.max_pages_per_seq = p->desc.max_pages_per_seq;
-    da.gqa = p->gqa ? 1 : 0;
-    da.n_move_tasks = n_move_tasks;
-    da.n_rot_tasks = n_rot_tasks;
-    da.n_entries = n_entries;
-    da.page_table = p->desc.page_table;
-    da.tasks = reinterpret_cast<ll::SpliceTask*>(dev_base + o_t);
-    da.dirs = dev_base + o_d;
-    da.twrites = reinterpret_cast<ll::TableWrite*>(dev_base + o_w);
-    da.tables = reinterpret_cast<int32_t*>(dev_base + o_p);
-    for (size_t k = 0; k < run_page.size(); ++k) {
-      da.run_page[k] = run_page[k];
-      da.run_first[k] = run_first[k];
-    }
-    da.run_first[run_page.size()] = static_cast<int32_t>(fresh.size());
-    int32_t max_new_pages = 0;
-    for (const auto& nt : new_tables) max_new_pages = std::max(max_new_pages, static_cast<int32_t>(nt.size()));
-    e = ll::launch_splice_plan(da, max_new_pages, st);
-    if (e != hipSuccess) return device_fail(p, e, "splice_plan_kernel launch");
-  } else if ((rc = upload(p, sg, st))) {
-    return rc;
-  }
-  ProfRec rec{};
-  ll::Stamp ts;
-  if (p->gqa) {
-    ll::GqaSpliceLaunch a{};
-    a.planes = reinterpret_cast<const ll::chunk_t* const*>(p->d_layers);
-    a.num_layers = p->desc.num_layers;
-    a.page_shift = p->page_shift;
-    a.row_chunks = static_cast<int32_t>(row_chunks);
-    a.head_chunks = p->head_chunks;
-    a.rot_shift = p->rot_shift;
-    a.heads = p->heads;
-    a.tasks = reinterpret_cast<const ll::SpliceTask*>(dev_base + o_t);
-    a.n_move_tasks = n_move_tasks;
-    a.n_rot_tasks = n_rot_tasks;
-    // one thread per two chunks in K and V planes (row_chunks is even:
-    // head_dim is a multiple of 16)
-    a.move_blocks_per_plane = ll::flat_blocks(n_move_tasks * P * (row_chunks / 2));
-    a.rot_blocks_per_plane = ll::flat_blocks(n_rot_tasks * P * (p->heads << (p->rot_shift - 1)));
-    a.dirs = reinterpret_cast<const ll::GqaDir*>(dev_base + o_d);
-    a.twrites = reinterpret_cast<const ll::TableWrite*>(dev_base + o_w);
-    a.tables = reinterpret_cast<const int32_t*>(dev_base + o_p);
-    a.n_twrites = n;
-    a.max_pages_per_seq = p->desc.max_pages_per_seq;
-    a.page_table = p->desc.page_table;
-    if (prof_pick(p, 0) && (rc = prof_begin(p, &rec, &ts))) return rc;
-    e = ll::launch_gqa_splice(a, p->desc.rope_pairing, st, ts);
-    if (e != hipSuccess) return device_fail(p, e, "gqa_splice_kernel launch");
-  } else {
-    ll::SpliceLaunch a{};
-    a.layers = reinterpret_cast<const ll::chunk_t* const*>(p->d_layers);
-    a.num_layers = p->desc.num_layers;
-    a.page_shift = p->page_shift;
-    a.tasks = reinterpret_cast<const ll::SpliceTask*>(dev_base + o_t);
-    a.n_move_tasks = n_move_tasks;
-    a.n_rot_tasks = n_rot_tasks;
-    a.move_blocks_per_layer = ll::flat_blocks(n_move_tasks * P * ll::kRowChunks, ll::kSpliceChunksPerThread);
-    a.rot_blocks_per_layer = ll::flat_blocks(n_rot_tasks * P * (ll::kRowChunks - ll::kKpeChunk0), ll::kSpliceChunksPerThread);
-    a.dirs = reinterpret_cast<const ll::SpliceDir*>(dev_base + o_d);
-    a.twrites = reinterpret_cast<const ll::TableWrite*>(dev_base + o_w);
-    a.tables = reinterpret_cast<const int32_t*>(dev_base + o_p);
-    a.n_twrites = n;
-    a.max_pages_per_seq = p->desc.max_pages_per_seq;
-    a.page_table = p->desc.page_table;
-    if (prof_pick(p, 0) && (rc = prof_begin(p, &rec, &ts))) return rc;
-    e = ll::launch_splice(a, p->desc.rope_pairing, st, ts);
-    if (e != hipSuccess) return device_fail(p, e, "splice_kernel launch");
+  if (!direct) {
+    if ((rc = upload(p, sg, st))) return rc;
+    if ((rc = launch_rows())) return rc;
   }
   if (rec.start) {
     rec.bytes = stats.alg_bytes + 4 * stats.table_entries;
