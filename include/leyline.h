@@ -221,8 +221,8 @@ ll_status ll_pool_free_pages(const ll_pool* pool, int64_t* n_free);
  * re-prefills, section 2.1); the next position moves back by n - s_start.
  *
  * The host makes the page plan.  With the default planner
- * (ll_pool_set_splice_planner) a batch of at most 8 directives (GQA / MHA
- * pools: at most 512 / rotary_dim) whose fresh pages form at most 128 runs of
+ * (ll_pool_set_splice_planner) a batch of at most 16 directives (GQA / MHA
+ * pools: at most 1024 / rotary_dim) whose fresh pages form at most 256 runs of
  * consecutive page ids travels as kernel arguments: a small kernel expands it
  * into per-page tasks and new page-table rows, reading the old rows from the
  * device page table, and the row kernel (fresh pages, in-place rotation and

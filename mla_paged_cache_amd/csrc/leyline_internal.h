@@ -195,10 +195,11 @@ struct ScanLaunch {
 // splice_plan_kernel expands it, reading the old page tables on the device,
 // into the SpliceTask / SpliceDir (GqaDir) / TableWrite / table arrays the row
 // kernels take, so that the row kernel that follows is the same as on the
-// host-planned path.  Limits keep the arguments under 4 KiB.
-constexpr int kDirectMaxDirs = 8;
-constexpr int kDirectMaxRuns = 128;
-constexpr int kDirectTrigFloats = 512;  // cos and sin of every directive
+// host-planned path.  The limits keep the arguments under 8 KiB (this stack
+// passes kernel arguments of 12 KiB intact).
+constexpr int kDirectMaxDirs = 16;
+constexpr int kDirectMaxRuns = 256;
+constexpr int kDirectTrigFloats = 1024;  // cos and sin of every directive
 
 struct DirectDir {
   const chunk_t* stub;         // K (MLA: whole) rows of R, layer 0
@@ -241,7 +242,7 @@ struct DirectPlanArgs {
   DirectDir d[kDirectMaxDirs];
   float trig[kDirectTrigFloats];  // directive i: cos at 2*pairs*i, sin at 2*pairs*i + pairs
 };
-static_assert(sizeof(DirectPlanArgs) <= 4096, "the direct splice plan must fit the kernel argument space");
+static_assert(sizeof(DirectPlanArgs) <= 8192, "the direct splice plan must fit in 8 KiB of kernel arguments");
 
 // Timing events a launcher stamps from the dispatch packets themselves (no
 // marker packets of their own on the stream): `start` gets the start time of

@@ -6,7 +6,7 @@ expanded on the device from kernel arguments, any other batch (and every batch
 under SPLICE_PLAN_HOST) is staged and uploaded.  Both must give the oracle's
 page tables, lengths, positions and rows (c_kv and stub rows bit-exact, k_pe
 within 1 bf16 ulp; 0 expected), and each call must report the planner the
-rules pick: at most 8 directives (GQA: 512 / rotary_dim), at most 128 runs."""
+rules pick: at most 16 directives (GQA: 1024 / rotary_dim), at most 256 runs."""
 
 import numpy as np
 import pytest
@@ -19,7 +19,7 @@ from test_gpu_gqa import GqaDevicePool
 
 pytestmark = pytest.mark.gpu
 
-MAX_DIRS, MAX_RUNS = 8, 128
+MAX_DIRS, MAX_RUNS = 16, 256
 
 
 def _runs(pages):
@@ -73,13 +73,13 @@ def _directive(rng, seq, n, kind, P, seed):
 
 @pytest.mark.parametrize("P,pairing", [(1, 0), (4, 0), (16, 0), (16, 1)])
 def test_planners_agree_batch_by_batch(P, pairing):
-    """Batches of 1..10 directives of seven kinds over 12 sequences, the
+    """Batches of 1..20 directives of seven kinds over 20 sequences, the
     planner switched at random before each; every sequence compared with the
     oracle after every batch."""
     need_gpu()
     say(f"planners batch by batch, P={P}, pairing={pairing}")
     rng = np_rng(900 + P + pairing, 1)
-    n_seq, max_rows = 12, 700
+    n_seq, max_rows = 20, 700
     lengths = [int(x) for x in rng.integers(0, 300, size=n_seq)]
     max_pages = -(-max_rows // P)
     used = sum(-(-n // P) for n in lengths)
@@ -95,7 +95,7 @@ def test_planners_agree_batch_by_batch(P, pairing):
     name = "half" if pairing else "interleaved"
     seen = {0: 0, 1: 0}
     for b in range(14):
-        k = int(rng.integers(1, 11))
+        k = int(rng.integers(1, 21))
         seqs = [int(x) for x in rng.choice(n_seq, size=k, replace=False)]
         dirs = []
         for i, s in enumerate(seqs):
@@ -120,23 +120,23 @@ def test_planners_agree_batch_by_batch(P, pairing):
 
 
 def test_run_and_batch_limits_pick_the_planner():
-    """Free pages every other page id: a splice needing 128 fresh pages has
-    128 runs (planned on the device), one needing 129 has 129 (staged); 8
-    directives are planned on the device, 9 are staged.  Each compared with
+    """Free pages every other page id: a splice needing 256 fresh pages has
+    256 runs (planned on the device), one needing 257 has 257 (staged); 16
+    directives are planned on the device, 17 are staged.  Each compared with
     the oracle."""
     need_gpu()
     say("planner limits")
-    P, n_seq = 1, 10
+    P, n_seq = 1, 18
     num_pages = 4096
-    dp = DevicePool(1, num_pages, P, n_seq, 1024, seed=931)
+    dp = DevicePool(1, num_pages, P, n_seq, 1100, seed=931)
     # sequence 0 holds the odd pages 1..2047 (1024 rows) and sequence 1 the
     # even pages from 2048 on, so the lowest free pages are 0, 2, 4, ...
     dp.set_pages(0, list(range(1, 2048, 2)), 1024)
     dp.set_pages(1, list(range(2048, 2048 + 512)), 512)
     for s in range(2, n_seq):
-        dp.set_pages(s, list(range(2600 + 40 * s, 2600 + 40 * s + 20)), 20)
+        dp.set_pages(s, list(range(2700 + 40 * s, 2700 + 40 * s + 20)), 20)
     dp.snapshot_rows()
-    for grow, want in ((128, 1), (129, 0)):
+    for grow, want in ((MAX_RUNS, 1), (MAX_RUNS + 1, 0)):
         # `grow` rows inserted at the start: at page size 1 only the stub rows
         # take fresh pages (every downstream row keeps its page, turned in
         # place), so the fresh pages are `grow` isolated even page ids
@@ -146,7 +146,7 @@ def test_run_and_batch_limits_pick_the_planner():
         compare_seq(dp, expected, 1)
         assert_same_free(dp, expected)
         dp.state = expected
-    for k, want in ((8, 1), (9, 0)):
+    for k, want in ((MAX_DIRS, 1), (MAX_DIRS + 1, 0)):
         dirs = [(s, 2, 5, 1, 50 * k + s, O.AMORTIZE) for s in range(1, 1 + k)]
         expected, runs = _mla_splice(dp, dirs, 0)
         assert dp.pool.last_stats().planned_on_device == want, (k, runs)
@@ -157,10 +157,10 @@ def test_run_and_batch_limits_pick_the_planner():
     dp.close()
 
 
-@pytest.mark.parametrize("H,D,rot,limit", [(1, 256, 256, 2), (2, 128, 128, 4)])
+@pytest.mark.parametrize("H,D,rot,limit", [(1, 256, 256, 4), (2, 128, 128, 8)])
 def test_gqa_directive_limit_follows_the_band_width(H, D, rot, limit):
     """GQA pools carry rotary_dim / 2 cos/sin pairs per directive in the
-    kernel arguments: at most 512 / rotary_dim directives are planned on the
+    kernel arguments: at most 1024 / rotary_dim directives are planned on the
     device, one more is staged; both match the oracle."""
     need_gpu()
     say(f"gqa planner limit H={H} D={D} rot={rot}")
