@@ -24,12 +24,15 @@
  * Streams.  `stream` is a hipStream_t passed as void* (NULL: the null stream).
  * Each call enqueues its device work on that stream and returns; the work of a
  * call is ordered after the work of the previous call on the same pool, also
- * across streams.  No call waits for the device, with two exceptions: a
+ * across streams.  No call waits for the device, with three exceptions: a
  * kv_evict_compact whose host-made page plan needs one small device-to-host
- * copy first (see there), and the first call after a device-planned
+ * copy first (see there); the first call after a device-planned
  * kv_evict_compact, which waits for that call's results (a small readback)
- * before it reads or changes the pool's bookkeeping.  A pool is not
- * thread-safe.
+ * before it reads or changes the pool's bookkeeping; and a call that needs a
+ * larger library buffer than any call before it (the staging ring, the
+ * eviction scratch, the device-planned splice's plan space, the per-row
+ * rotation tables), which waits once for the pool's earlier work before it
+ * replaces the buffer.  A pool is not thread-safe.
  *
  * Errors.  Every function returns an ll_status.  All checks run before any
  * state changes, so a call that returns LL_EINVAL, LL_ERANGE, LL_ENOMEM or
