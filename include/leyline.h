@@ -32,7 +32,8 @@
  * larger library buffer than any call before it (the staging ring, the
  * eviction scratch, the device-planned splice's plan space, the per-row
  * rotation tables), which waits once for the pool's earlier work before it
- * replaces the buffer.  A pool is not thread-safe.
+ * replaces the buffer, or that finds the 16 MiB staging ring still held by
+ * uploads the device has not yet consumed.  A pool is not thread-safe.
  *
  * Errors.  Every function returns an ll_status.  All checks run before any
  * state changes, so a call that returns LL_EINVAL, LL_ERANGE, LL_ENOMEM or
