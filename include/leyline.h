@@ -395,8 +395,14 @@ ll_status kvs_block_mask(kvs_ctx* ctx, const int32_t* death_dev, int32_t n, int6
 
 /* Dense bit mask from death times: bits_dev is uint32 [n][n_pad][n_pad / 32]
  * (16-byte aligned; n_pad a multiple of 128); bit b of word w of row q of
- * rollout i is 1 iff query q sees key 32 w + b.  Errors: LL_EINVAL,
- * LL_EUNSUPPORTED, LL_EDEVICE. */
+ * rollout i is 1 iff query q sees key 32 w + b, i.e. k <= q < d_k for any
+ * int32 death times (values at or below k, or at or beyond n_pad, included).
+ * For n_pad <= 262144 the call keeps a context-owned device scratch of
+ * n * (64 + 5 * n_pad / 8) bytes (plus 256 of alignment), reused call after
+ * call: a later call on another stream waits on the device for the last one,
+ * and a call that must grow the scratch first waits on the host for the last
+ * call to finish.  Errors: LL_EINVAL, LL_EUNSUPPORTED, LL_ENOMEM,
+ * LL_EDEVICE. */
 ll_status kvs_dense_mask(kvs_ctx* ctx, const int32_t* death_dev, int32_t n, int64_t n_pad,
                          uint32_t* bits_dev, void* stream);
 

@@ -13,10 +13,21 @@
 //  * kvs_minmax_kernel / kvs_block_kernel: per key block the smallest and
 //    largest death time, then per query block the sorted lists of partial and
 //    full key blocks (FlexAttention-style block mask).
-//  * kvs_dense_kernel: the packed bit mask, one 16-byte store per lane and
-//    row; a wave carries its 64 x 128 keys' bits down a run of rows, adds keys
-//    as the rows reach them and rebuilds the bits (coalesced loads, ballots)
-//    only at rows where one of its keys dies.
+//  * kvs_events_kernel / kvs_dense_ev_kernel: the packed bit mask of rollouts
+//    whose keys die at few distinct times: the distinct death times and per
+//    key a 4-bit code (which of them), once per rollout; then rows walked with
+//    bits added on the diagonal and cleared at each death time -- no loads in
+//    the row loop, so a rollout's rows can be dealt across its waves with a
+//    stride and the resident waves write neighbouring rows.  The waves of a
+//    rollout with more death times take the rebuild walk below instead, in
+//    the same launch.
+//  * kvs_dense_kernel (rebuild walk; every rollout when n_pad is too large
+//    for the pre-pass): one 16-byte store per lane and row; a wave carries
+//    its 64 x 128 keys' bits down a run of rows, adds keys as the rows reach
+//    them and rebuilds the bits (coalesced loads, ballots) only at rows where
+//    one of its keys dies.
+#include <algorithm>
+
 #include "kvs_internal.h"
 
 namespace ll {
@@ -235,14 +246,13 @@ __device__ __forceinline__ word4 wave_bits(const int32_t* d, int64_t n_pad, int6
 // where one of its keys dies (death times take at most one value per eviction
 // event) it recomputes them with wave_bits.  The row loop itself loads
 // nothing, so its stores never wait behind a load.
-__global__ __launch_bounds__(256) void kvs_dense_kernel(KvsDenseLaunch a) {
-  __shared__ uint64_t stage[4][256];
-  const int lane = threadIdx.x & 63;
+// One wave of the rebuild walk: wave gw of the grid, its LDS stage of 256
+// words.  Only wave-level steps (ballots, the wave's own LDS), so waves of one
+// block may take different rollouts and either walk.
+__device__ __forceinline__ void dense_rebuild_wave(const KvsDenseLaunch& a, int64_t gw, int lane, uint64_t* lds) {
   const int64_t strips = a.n_pad >> 7;
   const int64_t groups = (strips + 63) >> 6;
   const int64_t runs = (a.n_pad + a.rows_per_thread - 1) / a.rows_per_thread;
-  const int64_t gw = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) >> 6;
-  if (gw >= static_cast<int64_t>(a.n) * runs * groups) return;
   const int64_t grp = gw % groups;
   const int64_t rest = gw / groups;
   const int64_t run = rest % runs;
@@ -263,7 +273,6 @@ __global__ __launch_bounds__(256) void kvs_dense_kernel(KvsDenseLaunch a) {
         __builtin_nontemporal_store(word4{0u, 0u, 0u, 0u}, out + q * pitch);
     return;
   }
-  uint64_t* lds = stage[threadIdx.x >> 6];
   int32_t death;
   word4 real;
   word4 w = wave_bits(d, a.n_pad, wk0, q_begin, lds, lane, &death, &real);
@@ -276,6 +285,196 @@ __global__ __launch_bounds__(256) void kvs_dense_kernel(KvsDenseLaunch a) {
       w[b >> 5] |= real[b >> 5] & (1u << (b & 31));
     }
     if (active) __builtin_nontemporal_store(w, out + q * pitch);
+  }
+}
+
+__global__ __launch_bounds__(256) void kvs_dense_kernel(KvsDenseLaunch a) {
+  __shared__ uint64_t stage[4][256];
+  const int64_t strips = a.n_pad >> 7;
+  const int64_t groups = (strips + 63) >> 6;
+  const int64_t runs = (a.n_pad + a.rows_per_thread - 1) / a.rows_per_thread;
+  const int64_t gw = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) >> 6;
+  if (gw >= static_cast<int64_t>(a.n) * runs * groups) return;
+  dense_rebuild_wave(a, gw, threadIdx.x & 63, stage[threadIdx.x >> 6]);
+}
+
+// gridDim.y 1024-thread blocks per rollout, each of which builds the set of
+// death times d with k < d < n_pad (the times at which a key that was visible
+// dies) as an n_pad-bit set in LDS -- the whole rollout's, so that every block
+// knows the times -- then its first kDenseMaxEvents members in increasing
+// order and its size (capped at kDenseMaxEvents + 1; block 0 stores them);
+// when it has at most kDenseMaxEvents members, the keys of every gridDim.y-th
+// 1024 get their bits in the five bit sets (visible at some row, code bits
+// 0..3), one ballot per set and 64 keys.
+__global__ __launch_bounds__(1024) void kvs_events_kernel(KvsDenseLaunch a) {
+  extern __shared__ uint32_t set[];
+  __shared__ int32_t part[1024];
+  __shared__ int32_t times[kDenseMaxEvents];
+  const int64_t n_pad = a.n_pad;
+  const int32_t* d = a.death + static_cast<int64_t>(blockIdx.x) * n_pad;
+  const int64_t words = n_pad >> 5;
+  for (int64_t w = threadIdx.x; w < words; w += 1024) set[w] = 0u;
+  __syncthreads();
+  for (int64_t k = threadIdx.x; k < n_pad; k += 1024) {
+    const int32_t x = d[k];
+    // neighbouring keys mostly die together: one LDS atomic per run of equal
+    // times in the wave rather than one per lane on the same word
+    const int32_t left = __shfl_up(x, 1);
+    if (x > k && x < n_pad && ((threadIdx.x & 63) == 0 || left != x)) atomicOr(&set[x >> 5], 1u << (x & 31));
+  }
+  __syncthreads();
+  // thread t owns words [t * per, (t + 1) * per): its count, then an
+  // exclusive scan of the counts in LDS gives each member its rank
+  const int64_t per = (words + 1023) / 1024;
+  const int64_t w0 = threadIdx.x * per;
+  const int64_t w1 = w0 + per < words ? w0 + per : words;
+  int32_t cnt = 0;
+  for (int64_t w = w0; w < w1; ++w) cnt += __popc(set[w]);
+  part[threadIdx.x] = cnt;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {  // inclusive scan, Hillis-Steele
+    const int32_t v = threadIdx.x >= o ? part[threadIdx.x - o] : 0;
+    __syncthreads();
+    part[threadIdx.x] += v;
+    __syncthreads();
+  }
+  int32_t* ev = a.events + static_cast<int64_t>(blockIdx.x) * kDenseEvStride;
+  int32_t rank = part[threadIdx.x] - cnt;
+  for (int64_t w = w0; w < w1 && rank < kDenseMaxEvents; ++w) {
+    uint32_t bitsw = set[w];
+    while (bitsw && rank < kDenseMaxEvents) {
+      const int b = __builtin_ctz(bitsw);
+      bitsw &= bitsw - 1u;
+      const int32_t t = static_cast<int32_t>((w << 5) + b);
+      times[rank] = t;
+      if (blockIdx.y == 0) ev[1 + rank] = t;
+      ++rank;
+    }
+  }
+  if (threadIdx.x == 1023 && blockIdx.y == 0) ev[0] = part[1023] > kDenseMaxEvents ? kDenseMaxEvents + 1 : part[1023];
+  const int32_t total = part[1023];
+  if (total > kDenseMaxEvents) return;  // the rollout takes the rebuild walk
+  // every member is in `times`; give each of the block's keys its visible
+  // bit and code bits, 64 keys per wave and ballot
+  __syncthreads();
+  int32_t evs[kDenseMaxEvents];
+#pragma unroll
+  for (int e = 0; e < kDenseMaxEvents; ++e) evs[e] = e < total ? times[e] : INT32_MAX;
+  uint32_t* pl = a.planes + static_cast<int64_t>(blockIdx.x) * 5 * words;
+  const int lane = threadIdx.x & 63;
+  for (int64_t base = (static_cast<int64_t>(blockIdx.y) * 16 + (threadIdx.x >> 6)) * 64; base < n_pad;
+       base += int64_t{1024} * gridDim.y) {
+    const int64_t k = base + lane;  // n_pad is a multiple of 128: no tail
+    const int32_t x = d[k];
+    const bool ever = x > k;
+    int code = 15;
+    if (ever && x < n_pad) {
+      code = 0;
+#pragma unroll
+      for (int e = 0; e < kDenseMaxEvents; ++e) code += evs[e] < x ? 1 : 0;
+    }
+    const uint64_t m[5] = {__ballot(ever), __ballot(code & 1), __ballot(code & 2), __ballot(code & 4),
+                           __ballot(code & 8)};
+    if (lane < 10) {  // lane 2p + h writes word h of plane p
+      const int p = lane >> 1, h = lane & 1;
+      pl[p * words + (base >> 5) + h] = static_cast<uint32_t>(m[p] >> (32 * h));
+    }
+  }
+}
+
+// Bits [lo, hi] (strip-relative, may reach outside 0..127) of 32-bit word
+// `word` (bits 32 word .. 32 word + 31) of a 128-bit strip.
+__device__ __forceinline__ uint32_t range_word(int32_t lo, int32_t hi, int word) {
+  const int32_t a = lo - 32 * word > 0 ? lo - 32 * word : 0;
+  const int32_t b = hi - 32 * word < 31 ? hi - 32 * word : 31;
+  if (a > b) return 0u;
+  return (0xFFFFFFFFu >> (31 - b)) & (0xFFFFFFFFu << a);
+}
+
+// One wave per (rollout, phase, 64 consecutive strips of 128 keys); lane s
+// writes strip s.  Phase ph takes rows ph, ph + S, ph + 2 S, ... (S = n_pad /
+// rows_per_thread), so that the waves resident at a time write neighbouring
+// rows.  A lane loads its 128 keys' bits from the five bit sets of
+// kvs_events_kernel (visible at some row; the 4-bit code, the index of d_k
+// among the rollout's distinct death times).  Walking its rows it adds the
+// keys the diagonal has reached since the last row and clears, at every death
+// time passed, the keys with that code -- four bit-plane ANDs per word, no
+// loads in the row loop.
+__global__ __launch_bounds__(256) void kvs_dense_ev_kernel(KvsDenseLaunch a) {
+  __shared__ uint64_t stage[4][256];  // the rebuild walk's
+  const int lane = threadIdx.x & 63;
+  const int64_t strips = a.n_pad >> 7;
+  const int64_t groups = (strips + 63) >> 6;
+  const int64_t phases = a.n_pad / a.rows_per_thread;
+  // the wave index, made visibly wave-uniform: everything derived from it
+  // (rollout, phase, rows, the death-time list) then lives in scalar
+  // registers and is read with scalar loads -- a vector load in the row loop
+  // would wait for every store issued before it
+  const uint64_t gw_any = (static_cast<uint64_t>(blockIdx.x) * 256 + threadIdx.x) >> 6;
+  const int64_t gw = static_cast<int64_t>(
+      (static_cast<uint64_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(gw_any >> 32))) << 32) |
+      __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(gw_any)));
+  if (gw >= static_cast<int64_t>(a.n) * phases * groups) return;
+  const int64_t grp = gw % groups;
+  const int64_t rest = gw / groups;
+  const int64_t ph = rest % phases;
+  const int32_t roll = static_cast<int32_t>(rest / phases);
+  using cptr = const __attribute__((address_space(4))) int32_t*;
+  const cptr ev = reinterpret_cast<cptr>(reinterpret_cast<uintptr_t>(a.events + int64_t{roll} * kDenseEvStride));
+  const int32_t n_ev = ev[0];
+  if (n_ev > kDenseMaxEvents) {  // too many death times for the codes: the rebuild walk
+    dense_rebuild_wave(a, gw, lane, stage[threadIdx.x >> 6]);
+    return;
+  }
+  const int64_t s = grp * 64 + lane;
+  const bool active = s < strips;
+  const int64_t words = a.n_pad >> 5;
+  word4* out = reinterpret_cast<word4*>(a.bits + int64_t{roll} * a.n_pad * words) + s;
+  const int64_t pitch = words >> 2;  // word4 per row
+  const int64_t k0 = s << 7;         // first key of the lane's strip
+  // the lane's 128 keys in each of the five bit sets (16 bytes each):
+  // planes[0] visible at some row, planes[1..4] bits 0..3 of the code
+  uint32_t planes[5][4] = {};
+  if (active) {
+    const uint32_t* pl = a.planes + static_cast<int64_t>(roll) * 5 * words + 4 * s;
+#pragma unroll
+    for (int p = 0; p < 5; ++p) {
+      const word4 v = *reinterpret_cast<const word4*>(pl + p * words);
+      planes[p][0] = v.x;
+      planes[p][1] = v.y;
+      planes[p][2] = v.z;
+      planes[p][3] = v.w;
+    }
+  }
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+  int32_t e_next = 0;
+  // rows and keys are below n_pad < 2^31
+  const int32_t step = static_cast<int32_t>(phases);
+  const int32_t k0s = static_cast<int32_t>(k0);
+  int32_t q = static_cast<int32_t>(ph);
+  int32_t q_prev = -1;
+  word4* dst = out + q * pitch;
+  const int64_t dst_step = static_cast<int64_t>(step) * pitch;
+  for (int32_t j = 0; j < a.rows_per_thread; ++j, q += step, dst += dst_step) {
+    // keys q_prev < k <= q of the strip join (those ever visible)
+    const int32_t lo = (q_prev + 1 > k0s ? q_prev + 1 : k0s) - k0s;
+    const int32_t hi = (q < k0s + 127 ? q : k0s + 127) - k0s;
+    if (lo <= hi) {
+#pragma unroll
+      for (int x = 0; x < 4; ++x) w[x] |= planes[0][x] & range_word(lo, hi, x);
+    }
+    // keys whose death time has come leave (times in increasing order)
+    while (e_next < n_ev && ev[1 + e_next] <= q) {
+      const int e = e_next++;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const uint32_t m = ((e & 1) ? planes[1][x] : ~planes[1][x]) & ((e & 2) ? planes[2][x] : ~planes[2][x]) &
+                           ((e & 4) ? planes[3][x] : ~planes[3][x]) & ((e & 8) ? planes[4][x] : ~planes[4][x]);
+        w[x] &= ~m;
+      }
+    }
+    if (active) __builtin_nontemporal_store(word4{w[0], w[1], w[2], w[3]}, dst);
+    q_prev = q;
   }
 }
 
@@ -303,6 +502,16 @@ hipError_t launch_kvs_dense(const KvsDenseLaunch& a, hipStream_t s) {
   const int64_t runs = (a.n_pad + a.rows_per_thread - 1) / a.rows_per_thread;
   const int64_t groups = ((a.n_pad >> 7) + 63) >> 6;
   const int64_t waves = static_cast<int64_t>(a.n) * runs * groups;
+  if (a.events) {
+    // blocks per rollout: enough to fill the chip's CUs, none without keys
+    const int64_t split = std::min<int64_t>(std::max<int64_t>(1, 512 / a.n), (a.n_pad + 1023) / 1024);
+    kvs_events_kernel<<<dim3(static_cast<unsigned>(a.n), static_cast<unsigned>(split)), dim3(1024),
+                        static_cast<size_t>(a.n_pad >> 3), s>>>(a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    kvs_dense_ev_kernel<<<dim3(static_cast<unsigned>((waves + 3) / 4)), dim3(256), 0, s>>>(a);
+    return hipGetLastError();
+  }
   kvs_dense_kernel<<<dim3(static_cast<unsigned>((waves + 3) / 4)), dim3(256), 0, s>>>(a);
   return hipGetLastError();
 }

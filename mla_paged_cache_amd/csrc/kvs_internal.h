@@ -47,12 +47,27 @@ struct KvsBlockLaunch {
   int32_t nq, nk;
 };
 
+// The dense mask of a rollout whose keys die at no more than kDenseMaxEvents
+// distinct times is written by kvs_dense_ev_kernel from per-key death codes;
+// other rollouts by the rebuild walk of kvs_dense_kernel, run by the same
+// launch's waves of that rollout.  events: [n][kDenseEvStride] int32,
+// entry 0 the number of distinct death times d with k < d < n_pad over the
+// rollout's keys (kDenseMaxEvents + 1: more than that), entries 1.. those
+// times in increasing order.  planes: per rollout five bit sets over its keys
+// -- visible at some row (d_k > k), then bits 0..3 of the key's code, the
+// index of d_k among those times (15: no death before n_pad).
+constexpr int kDenseMaxEvents = 15;
+constexpr int kDenseEvStride = 16;
+constexpr int64_t kDenseEvMaxPad = 262144;  // the pre-pass keeps an n_pad-bit set in LDS
+
 struct KvsDenseLaunch {
   const int32_t* death;  // [n][n_pad]
   uint32_t* bits;        // [n][n_pad][n_pad / 32]
   int64_t n_pad;
   int32_t n;
   int32_t rows_per_thread;
+  int32_t* events;       // nullptr: kvs_dense_kernel alone, every rollout by the rebuild walk
+  uint32_t* planes;      // [n][5][n_pad / 32]: per key, visible at some row, then code bits 0..3
 };
 
 hipError_t launch_kvs_death(const KvsDeathLaunch& a, hipStream_t s);

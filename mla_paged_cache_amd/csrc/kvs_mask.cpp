@@ -28,6 +28,11 @@ struct kvs_ctx {
   size_t minmax_cap = 0;     // elements
   hipEvent_t minmax_done = nullptr;
   bool minmax_pending = false;
+  char* events = nullptr;     // dense-mask scratch: distinct death times and key bit sets per rollout
+  size_t events_cap = 0;      // bytes
+  hipEvent_t events_done = nullptr;
+  bool events_pending = false;
+  hipStream_t events_stream = nullptr;  // the stream of the call that recorded events_done
 };
 
 namespace {
@@ -77,6 +82,7 @@ ll_status kvs_ctx_create(int32_t device, kvs_ctx** out) try {
   c->device = device;
   hipError_t e = hipEventCreateWithFlags(&c->staged, hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&c->minmax_done, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&c->events_done, hipEventDisableTiming);
   if (e != hipSuccess) {
     kvs_ctx_destroy(c);
     return dev_fail(e, "kvs_ctx_create");
@@ -92,8 +98,11 @@ void kvs_ctx_destroy(kvs_ctx* c) try {
   DeviceGuard g(c->device);
   if (c->staged_pending) (void)hipEventSynchronize(c->staged);
   if (c->minmax_pending) (void)hipEventSynchronize(c->minmax_done);
+  if (c->events_pending) (void)hipEventSynchronize(c->events_done);
   if (c->staged) (void)hipEventDestroy(c->staged);
   if (c->minmax_done) (void)hipEventDestroy(c->minmax_done);
+  if (c->events_done) (void)hipEventDestroy(c->events_done);
+  if (c->events) (void)hipFree(c->events);
   if (c->host) (void)hipHostFree(c->host);
   if (c->dev) (void)hipFree(c->dev);
   if (c->minmax) (void)hipFree(c->minmax);
@@ -282,8 +291,41 @@ ll_status kvs_dense_mask(kvs_ctx* c, const int32_t* death_dev, int32_t n, int64_
   const int64_t groups = (n_pad / 128 + 63) / 64;  // waves per run of rows
   if (static_cast<int64_t>(n) * runs * groups / 4 >= (int64_t{1} << 31))
     return fail(LL_EUNSUPPORTED, "dense mask too large for one launch");
-  hipError_t e = ll::launch_kvs_dense(a, static_cast<hipStream_t>(stream));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool by_events = n_pad <= ll::kDenseEvMaxPad;
+  if (by_events) {
+    // per rollout its distinct death times (kvs_events_kernel), read by the
+    // two mask kernels; the scratch is reused call after call
+    // [n][kDenseEvStride] int32, then [n][5][n_pad / 32] uint32
+    const size_t ev_bytes = (static_cast<size_t>(n) * ll::kDenseEvStride * sizeof(int32_t) + 255) / 256 * 256;
+    const size_t need = ev_bytes + static_cast<size_t>(n) * 5 * static_cast<size_t>(n_pad / 8);
+    if (need > c->events_cap) {
+      if (c->events_pending) {
+        hipError_t e = hipEventSynchronize(c->events_done);
+        if (e != hipSuccess) return dev_fail(e, "hipEventSynchronize(scratch)");
+        c->events_pending = false;
+      }
+      if (c->events) (void)hipFree(c->events);
+      c->events = nullptr;
+      c->events_cap = 0;
+      if (hipMalloc(reinterpret_cast<void**>(&c->events), need) != hipSuccess)
+        return fail(LL_ENOMEM, "cannot allocate dense-mask scratch");
+      c->events_cap = need;
+    } else if (c->events_pending && st != c->events_stream) {  // same stream: already in order
+      hipError_t e = hipStreamWaitEvent(st, c->events_done, 0);
+      if (e != hipSuccess) return dev_fail(e, "hipStreamWaitEvent(scratch)");
+    }
+    a.events = reinterpret_cast<int32_t*>(c->events);
+    a.planes = reinterpret_cast<uint32_t*>(c->events + ev_bytes);
+  }
+  hipError_t e = ll::launch_kvs_dense(a, st);
   if (e != hipSuccess) return dev_fail(e, "kvs_dense_kernel launch");
+  if (by_events) {
+    e = hipEventRecord(c->events_done, st);
+    if (e != hipSuccess) return dev_fail(e, "hipEventRecord");
+    c->events_pending = true;
+    c->events_stream = st;
+  }
   return LL_OK;
 } catch (...) {
   return host_exception(nullptr);

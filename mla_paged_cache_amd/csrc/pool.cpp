@@ -1468,7 +1468,7 @@ ll_status leyline_splice(ll_pool* p, const ll_directive* dirs, int32_t n, void* 
   std::vector<std::vector<int32_t>> new_tables(static_cast<size_t>(n));
   ll_plan_stats stats{};
   size_t cursor = 0;
-  int64_t packed_at = 0, move_at = 0, rot_at = 0;
+  int64_t packed_at = 0;
   for (int32_t i = 0; i < n; ++i) {
     const ll_directive& d = dirs[i];
     const SplicePlan& pl = plans[i];
@@ -1508,13 +1508,11 @@ ll_status leyline_splice(ll_pool* p, const ll_directive* dirs, int32_t n, void* 
             t.dst_page = nt[q];
             *rot_out++ = t;
           }
-          ++rot_at;
           stats.rows_rotated_inplace += b - a;
         }
         continue;
       }
       nt[q] = fresh[cursor++];
-      ++move_at;
       stats.rows_moved += b - a;
       if (direct) continue;
       ll::SpliceTask t = base;

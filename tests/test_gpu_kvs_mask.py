@@ -188,3 +188,45 @@ def test_engine_eviction_agrees_with_death_times():
         t_prev = e.time
     pool.close()
     ctx.close()
+
+
+def test_dense_mask_of_arbitrary_death_times_both_kernels():
+    """Dense bits of death arrays written directly, not replayed from a log:
+    exactly 15 and 16 distinct death times (the two sides of the per-key code
+    limit), hundreds of distinct times, none, and values outside (k, n_pad)
+    (negative, equal to k, beyond n_pad), all in one batch so that rollouts
+    of both mask kernels share a launch.  Every row bit-exact against the
+    definition visible(q, k) = k <= q < d_k."""
+    L = need_gpu()
+    ctx = L.KvsMask(0)
+    rng = np_rng(4242, 0)
+    for n_pad in (1024, 1152):
+        say(f"kvs dense arbitrary death times n_pad={n_pad}")
+        k = np.arange(n_pad)
+        rolls = []
+        for n_times in (15, 16, 0, 300, 1):
+            times = np.sort(rng.choice(np.arange(1, n_pad), size=n_times, replace=False)) if n_times else np.zeros(0, np.int64)
+            d = np.full(n_pad, n_pad, np.int64)
+            if n_times:
+                dies = rng.random(n_pad) < 0.5
+                pick = times[rng.integers(0, n_times, size=n_pad)]
+                d = np.where(dies & (pick > k), pick, d)
+                d[times - 1] = times      # every time taken: key t - 1 dies at t
+            rolls.append(d)
+        odd = np.full(n_pad, n_pad, np.int64)
+        odd[::7] = -5                     # never visible
+        odd[1::7] = k[1::7]               # d_k = k: never visible
+        odd[2::7] = n_pad + 1000          # beyond the last row
+        odd[3::7] = np.minimum(k[3::7] + 1, n_pad)   # visible on its own row only
+        odd[4::7] = np.where(k[4::7] < 600, 600, n_pad)
+        rolls.append(odd)
+        d_host = np.stack(rolls)
+        got_times = [len(set(int(x) for j, x in enumerate(r) if j < x < n_pad)) for r in d_host]
+        assert got_times[:2] == [15, 16] and got_times[2] == 0 and got_times[3] > 15
+        death = torch.from_numpy(d_host.astype(np.int32)).cuda()
+        bits = ctx.dense_mask(death)
+        torch.cuda.synchronize()
+        got = bits.cpu().numpy().view(np.uint32)
+        for r in range(len(rolls)):
+            assert np.array_equal(got[r], K.dense_bits(K.visibility(d_host[r]))), (n_pad, r, got_times[r])
+    ctx.close()
