@@ -11,7 +11,7 @@ and the trainer reproduces the same eviction pattern with a custom attention
 mask so that one forward pass over the whole rollout sees what each token saw
 when it was generated.
 
-Readings taken where the page is silent (each is listed in the design doc):
+Readings taken where the page is silent:
   * a rollout is T tokens in generation order; the forward pass of token q
     attends to the tokens the cache held right after q was appended;
   * an eviction event (time t, keep) runs after t tokens have been generated

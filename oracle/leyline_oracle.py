@@ -24,7 +24,7 @@ What it follows (pages as published):
     (k_i, v_i) and positions are not reset; "assumptions and limits": 16-token
     blocks in vLLM, block size 1 in the SGLang fork.
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
   * span bounds are half-open and 0-based, [s_start, s_end);
   * RoPE frequencies theta_j = base^(-2j/d), base 10000, d = 64; pairs are
     interleaved (2j, 2j+1) by default, or half-split (j, j + d/2);
