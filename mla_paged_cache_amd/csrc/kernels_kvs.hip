@@ -37,20 +37,26 @@ typedef uint32_t word4 __attribute__((ext_vector_type(4)));
 
 constexpr int kDeathThreads = 1024;
 constexpr int kDeathWaves = kDeathThreads / 64;
-constexpr int kPerThread = 16;  // tokens per thread per tile
+constexpr int kPerThread = 16;  // slices of kDeathThreads rows per tile
+static_assert(kPerThread * kDeathWaves == 4 * 64, "one wave scans the (slice, wave) counts, four per lane");
 
 // One block per rollout.  d is initialised to n_pad (never dropped) for real
 // tokens and to k (never visible) for padding keys.  The block keeps the list
 // of token ids the cache holds, in order, in its scratch row; at an event at
 // time t the rows held are that list followed by the tokens generated since
-// the previous event, and row i is token list'[i].  Per tile of 16 rows per
-// thread, a block-wide exclusive scan of the kept counts (wave64 ballot
-// bit-planes, then the 16 wave totals through LDS) compacts the kept tokens in
-// place -- every write lands at or before the tile being read, and the tile's
-// reads finish before the scan's barrier -- and dropped tokens get d_k = t.
-// A mask whose length differs from the number of rows held sets the status.
+// the previous event, and row i is token list'[i].  A tile is 16 slices of
+// 1024 rows; thread x takes row x of every slice, so each load and store
+// instruction of a wave covers 64 neighbouring rows.  Per slice a ballot of
+// the kept bits, per (slice, wave) its count in LDS, one wave's exclusive scan
+// over those 256 counts in (slice, wave) order, and each kept row's position
+// is the scan's entry plus the kept lanes below it; kept tokens are compacted
+// in place -- a row's position is never past its own index, and every read of
+// the tile finishes before the scan's first barrier -- and dropped tokens get
+// d_k = t.  A mask whose length differs from the number of rows held sets the
+// status.
 __global__ __launch_bounds__(kDeathThreads) void kvs_death_kernel(KvsDeathLaunch a) {
-  __shared__ int32_t wave_total[kDeathWaves];
+  __shared__ int32_t part[kPerThread * kDeathWaves];  // (slice, wave): kept count, then its exclusive prefix
+  __shared__ int32_t tile_total;
   const KvsRollout r = a.rollouts[blockIdx.x];
   const int64_t n_pad = a.n_pad;
   int32_t* d = a.death + static_cast<int64_t>(blockIdx.x) * n_pad;
@@ -65,8 +71,10 @@ __global__ __launch_bounds__(kDeathThreads) void kvs_death_kernel(KvsDeathLaunch
   bool bad = false;
   int64_t held = 0;    // entries of `list`
   int64_t t_prev = 0;  // tokens generated at the previous event
+  KvsEvent next = r.n_events > 0 ? a.events[r.first_event] : KvsEvent{};
   for (int e = 0; e < r.n_events; ++e) {
-    const KvsEvent ev = a.events[r.first_event + e];
+    const KvsEvent ev = next;
+    if (e + 1 < r.n_events) next = a.events[r.first_event + e + 1];  // in flight during this event
     const int64_t t = ev.time;
     const int64_t rows = held + (t - t_prev);
     bad = bad || rows != ev.mask_len;
@@ -74,40 +82,44 @@ __global__ __launch_bounds__(kDeathThreads) void kvs_death_kernel(KvsDeathLaunch
     const uint8_t* m = a.keep + ev.mask_off;
     int64_t carry = 0;
     for (int64_t base = 0; base < len; base += int64_t{kPerThread} * kDeathThreads) {
-      const int64_t i0 = base + int64_t{kPerThread} * threadIdx.x;
       int32_t tok[kPerThread];
-      uint32_t kept = 0;
+      uint64_t bal[kPerThread];
 #pragma unroll
       for (int c = 0; c < kPerThread; ++c) {
-        const int64_t i = i0 + c;
+        const int64_t i = base + int64_t{c} * kDeathThreads + threadIdx.x;
         tok[c] = i < held ? list[i] : static_cast<int32_t>(t_prev + (i - held));
-        if (i < len && m[i] != 0) kept |= 1u << c;
+        bal[c] = __ballot(i < len && m[i] != 0);
       }
-      const int cnt = __popc(kept);
-      int below = 0, total = 0;
+      if (lane == 0) {
 #pragma unroll
-      for (int bit = 0; bit < 5; ++bit) {
-        const uint64_t bal = __ballot((cnt >> bit) & 1);
-        below += __popcll(bal & lanes_below) << bit;
-        total += __popcll(bal) << bit;
+        for (int c = 0; c < kPerThread; ++c) part[c * kDeathWaves + wave] = __popcll(bal[c]);
       }
-      if (lane == 0) wave_total[wave] = total;
       __syncthreads();
-      int wave_below = 0, block_total = 0;
+      if (wave == 0) {  // lane L scans entries 4L .. 4L + 3
+        const int32_t v0 = part[4 * lane], v1 = part[4 * lane + 1], v2 = part[4 * lane + 2], v3 = part[4 * lane + 3];
+        const int32_t own = v0 + v1 + v2 + v3;
+        int32_t incl = own;
 #pragma unroll
-      for (int w = 0; w < kDeathWaves; ++w) {
-        const int x = wave_total[w];
-        wave_below += w < wave ? x : 0;
-        block_total += x;
+        for (int o = 1; o < 64; o <<= 1) {
+          const int32_t y = __shfl_up(incl, o);
+          if (lane >= o) incl += y;
+        }
+        const int32_t excl = incl - own;
+        part[4 * lane] = excl;
+        part[4 * lane + 1] = excl + v0;
+        part[4 * lane + 2] = excl + v0 + v1;
+        part[4 * lane + 3] = excl + v0 + v1 + v2;
+        if (lane == 63) tile_total = incl;
       }
-      int64_t pos = carry + wave_below + below;
+      __syncthreads();
 #pragma unroll
       for (int c = 0; c < kPerThread; ++c) {
-        if (i0 + c >= len) break;
-        if ((kept >> c) & 1u) list[pos++] = tok[c];
+        const int64_t i = base + int64_t{c} * kDeathThreads + threadIdx.x;
+        if (i >= len) break;
+        if ((bal[c] >> lane) & 1ull) list[carry + part[c * kDeathWaves + wave] + __popcll(bal[c] & lanes_below)] = tok[c];
         else d[tok[c]] = static_cast<int32_t>(t);
       }
-      carry += block_total;
+      carry += tile_total;
       __syncthreads();
     }
     held = carry;
@@ -473,7 +485,9 @@ __global__ __launch_bounds__(256) void kvs_dense_ev_kernel(KvsDenseLaunch a) {
         w[x] &= ~m;
       }
     }
-    if (active) __builtin_nontemporal_store(word4{w[0], w[1], w[2], w[3]}, dst);
+    // plain stores: with the rows strided across the rollout's waves they
+    // measure faster than non-temporal ones (the reverse of a per-wave run)
+    if (active) *dst = word4{w[0], w[1], w[2], w[3]};
     q_prev = q;
   }
 }
