@@ -230,3 +230,59 @@ def test_dense_mask_of_arbitrary_death_times_both_kernels():
         for r in range(len(rolls)):
             assert np.array_equal(got[r], K.dense_bits(K.visibility(d_host[r]))), (n_pad, r, got_times[r])
     ctx.close()
+
+
+def test_death_times_of_events_spanning_several_replay_tiles():
+    """Events whose keep masks cover more than 16384 rows, the replay's tile:
+    the kept count carries from tile to tile.  Masks keeping 70% and 50% at
+    random, keeping everything, dropping everything; death times bit-exact,
+    sampled dense rows against the definition."""
+    L = need_gpu()
+    ctx = L.KvsMask(0)
+    n_pad = 40960
+    rng = np_rng(31, 0)
+    t1, t2 = 38000, 40000
+    keep1 = (rng.random(t1) < 0.7).astype(np.uint8)
+    keep2 = (rng.random(int(keep1.sum()) + t2 - t1) < 0.5).astype(np.uint8)
+    rolls = [
+        (t2, [EvictionEvent(t1, keep1), EvictionEvent(t2, keep2)]),
+        (n_pad, [EvictionEvent(20000, np.ones(20000, np.uint8)), EvictionEvent(n_pad, np.zeros(n_pad, np.uint8))]),
+        (33000, [EvictionEvent(16385, (rng.random(16385) < 0.3).astype(np.uint8))]),
+    ]
+    say(f"kvs replay over several tiles, rows per event {[[len(e.keep) for e in ev] for _, ev in rolls]}")
+    death, status = ctx.death_times(rolls, n_pad)
+    torch.cuda.synchronize()
+    assert not status.cpu().numpy().any()
+    d_host = np.stack([K.death_times(n_pad, n, ev) for n, ev in rolls])
+    assert np.array_equal(death.cpu().numpy().astype(np.int64), d_host)
+    bits = ctx.dense_mask(death)
+    torch.cuda.synchronize()
+    rows = np.array([0, 16383, 16384, 20000, 37999, 38000, 39999, 40000, 40959])
+    for r in range(len(rolls)):
+        got = bits[r, torch.from_numpy(rows).cuda()].cpu().numpy().view(np.uint32)
+        assert np.array_equal(got, K.dense_bits(K.visibility_rows(d_host[r], rows))), r
+    ctx.close()
+
+
+def test_dense_mask_beyond_the_pre_pass_limit():
+    """n_pad = 262272, past the 262144 keys whose death-time set fits in LDS:
+    the rebuild walk writes every rollout alone.  One rollout (8.6 GB of
+    bits) with hundreds of distinct death times, never-visible keys and keys
+    visible to the end; sampled rows against the definition."""
+    L = need_gpu()
+    ctx = L.KvsMask(0)
+    n_pad = 262272
+    rng = np_rng(32, 0)
+    k = np.arange(n_pad)
+    d = np.minimum(k + 1 + rng.integers(0, 5000, size=n_pad), n_pad + 7)
+    d[rng.random(n_pad) < 0.1] = n_pad
+    d[rng.random(n_pad) < 0.05] = -1
+    say(f"kvs dense n_pad={n_pad}, rebuild walk only")
+    death = torch.from_numpy(d[None].astype(np.int32)).cuda()
+    bits = ctx.dense_mask(death)
+    torch.cuda.synchronize()
+    rows = np.r_[[0, 127, 128, 131071, 262143, 262144, 262271], rng.integers(0, n_pad, size=5)]
+    got = bits[0, torch.from_numpy(rows).cuda()].cpu().numpy().view(np.uint32)
+    assert np.array_equal(got, K.dense_bits(K.visibility_rows(d, rows)))
+    del bits
+    ctx.close()
