@@ -886,7 +886,7 @@ def bench_kvs_mask(args):
         ctx.death_times(logs, TOKENS, out=(death, status))
         if record:
             marks[1].record()
-        ctx.block_mask(death, 128, 128)
+        ctx.block_mask(death, 128, 128, out=blocks)
         if record:
             marks[2].record()
         ctx.dense_mask(death, out=bits)

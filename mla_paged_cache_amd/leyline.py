@@ -525,14 +525,23 @@ class KvsMask:
         self._last_logs = logs  # the kernel reads the keep buffer after this returns
         return death, status
 
-    def block_mask(self, death, block_q: int, block_k: int, stream=None):
-        """(partial_num [n][nq], partial_idx [n][nq][nk], full_num, full_idx)."""
+    def block_mask(self, death, block_q: int, block_k: int, out=None, stream=None):
+        """(partial_num [n][nq], partial_idx [n][nq][nk], full_num, full_idx).
+        Without `out` the index arrays are new and filled with -1 past each
+        count; with `out` (four int32 tensors of those shapes) the entries past
+        each count are left as they were."""
         import torch
         n, n_pad = death.shape
         nq, nk = -(-n_pad // block_q), -(-n_pad // block_k)
         kw = dict(dtype=torch.int32, device=death.device)
-        pn, fn = torch.zeros((n, nq), **kw), torch.zeros((n, nq), **kw)
-        pi, fi = torch.full((n, nq, nk), -1, **kw), torch.full((n, nq, nk), -1, **kw)
+        if out is None:
+            pn, fn = torch.zeros((n, nq), **kw), torch.zeros((n, nq), **kw)
+            pi, fi = torch.full((n, nq, nk), -1, **kw), torch.full((n, nq, nk), -1, **kw)
+        else:
+            pn, pi, fn, fi = out
+            for x, shape in ((pn, (n, nq)), (pi, (n, nq, nk)), (fn, (n, nq)), (fi, (n, nq, nk))):
+                if tuple(x.shape) != shape or x.dtype != torch.int32 or not x.is_contiguous() or x.device != death.device:
+                    raise ValueError(f"block_mask out: need contiguous int32 {shape} on {death.device}")
         _check(_lib.kvs_block_mask(self._h, death.data_ptr(), n, n_pad, int(block_q), int(block_k), pn.data_ptr(),
                                    pi.data_ptr(), fn.data_ptr(), fi.data_ptr(), _stream_handle(stream, self.device)))
         return pn, pi, fn, fi

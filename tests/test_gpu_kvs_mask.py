@@ -62,6 +62,15 @@ def test_small_batches_all_outputs():
         assert np.array_equal(death.cpu().numpy().astype(np.int64), d_host)
         for bq, bk in ((16, 16), (32, 64), (64, 16), (128, 128)):
             _check_blocks(ctx, death, d_host, bq, bk)
+        # caller-owned outputs (uninitialised): same counts, same lists up to them
+        ref = [x.cpu().numpy() for x in ctx.block_mask(death, 32, 64)]
+        out = tuple(torch.empty(x.shape, dtype=torch.int32, device="cuda") for x in ref)
+        got = [x.cpu().numpy() for x in ctx.block_mask(death, 32, 64, out=out)]
+        assert np.array_equal(got[0], ref[0]) and np.array_equal(got[2], ref[2])
+        for r in range(len(rolls)):
+            for i in range(ref[0].shape[1]):
+                assert np.array_equal(got[1][r, i, :ref[0][r, i]], ref[1][r, i, :ref[0][r, i]])
+                assert np.array_equal(got[3][r, i, :ref[2][r, i]], ref[3][r, i, :ref[2][r, i]])
         bits = ctx.dense_mask(death)
         torch.cuda.synchronize()
         got = bits.cpu().numpy().view(np.uint32)
