@@ -460,6 +460,7 @@ __global__ __launch_bounds__(256) void kvs_dense_ev_kernel(KvsDenseLaunch a) {
   }
   uint32_t w[4] = {0u, 0u, 0u, 0u};
   int32_t e_next = 0;
+  int32_t t_next = n_ev > 0 ? ev[1] : INT32_MAX;  // the next death time, kept in a register
   // rows and keys are below n_pad < 2^31
   const int32_t step = static_cast<int32_t>(phases);
   const int32_t k0s = static_cast<int32_t>(k0);
@@ -476,7 +477,7 @@ __global__ __launch_bounds__(256) void kvs_dense_ev_kernel(KvsDenseLaunch a) {
       for (int x = 0; x < 4; ++x) w[x] |= planes[0][x] & range_word(lo, hi, x);
     }
     // keys whose death time has come leave (times in increasing order)
-    while (e_next < n_ev && ev[1 + e_next] <= q) {
+    while (t_next <= q) {
       const int e = e_next++;
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
@@ -484,6 +485,7 @@ __global__ __launch_bounds__(256) void kvs_dense_ev_kernel(KvsDenseLaunch a) {
                            ((e & 4) ? planes[3][x] : ~planes[3][x]) & ((e & 8) ? planes[4][x] : ~planes[4][x]);
         w[x] &= ~m;
       }
+      t_next = e_next < n_ev ? ev[1 + e_next] : INT32_MAX;
     }
     // plain stores: with the rows strided across the rollout's waves they
     // measure faster than non-temporal ones (the reverse of a per-wave run)
