@@ -54,13 +54,17 @@ static_assert(kPerThread * kDeathWaves == 4 * 64, "one wave scans the (slice, wa
 // the tile finishes before the scan's first barrier -- and dropped tokens get
 // d_k = t.  A mask whose length differs from the number of rows held sets the
 // status.
+// LDS_LIST: the list lives in dynamic LDS (n_pad entries) instead of the
+// block's global scratch row, when it fits.
+template <bool LDS_LIST>
 __global__ __launch_bounds__(kDeathThreads) void kvs_death_kernel(KvsDeathLaunch a) {
+  extern __shared__ int32_t lds_list[];
   __shared__ int32_t part[kPerThread * kDeathWaves];  // (slice, wave): kept count, then its exclusive prefix
   __shared__ int32_t tile_total;
   const KvsRollout r = a.rollouts[blockIdx.x];
   const int64_t n_pad = a.n_pad;
   int32_t* d = a.death + static_cast<int64_t>(blockIdx.x) * n_pad;
-  int32_t* list = a.list + static_cast<int64_t>(blockIdx.x) * n_pad;
+  int32_t* list = LDS_LIST ? lds_list : a.list + static_cast<int64_t>(blockIdx.x) * n_pad;
   for (int64_t k = threadIdx.x; k < n_pad; k += kDeathThreads)
     d[k] = k < r.n_tokens ? static_cast<int32_t>(n_pad) : static_cast<int32_t>(k);
   __syncthreads();
@@ -498,7 +502,17 @@ __global__ __launch_bounds__(256) void kvs_dense_ev_kernel(KvsDenseLaunch a) {
 
 hipError_t launch_kvs_death(const KvsDeathLaunch& a, hipStream_t s) {
   if (a.n == 0) return hipSuccess;
-  kvs_death_kernel<<<dim3(a.n), dim3(kDeathThreads), 0, s>>>(a);
+  // the list in LDS when n_pad entries fit beside the kernel's static LDS
+  int dev = 0, max_lds = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+  if (e != hipSuccess) return e;
+  const int64_t static_lds = int64_t{kPerThread} * kDeathWaves * 4 + 16;
+  const int64_t list_bytes = a.n_pad * 4;
+  if (list_bytes + static_lds <= max_lds)
+    kvs_death_kernel<true><<<dim3(a.n), dim3(kDeathThreads), static_cast<size_t>(list_bytes), s>>>(a);
+  else
+    kvs_death_kernel<false><<<dim3(a.n), dim3(kDeathThreads), 0, s>>>(a);
   return hipGetLastError();
 }
 
