@@ -331,12 +331,25 @@ __global__ __launch_bounds__(1024) void kvs_events_kernel(KvsDenseLaunch a) {
   const int64_t words = n_pad >> 5;
   for (int64_t w = threadIdx.x; w < words; w += 1024) set[w] = 0u;
   __syncthreads();
-  for (int64_t k = threadIdx.x; k < n_pad; k += 1024) {
-    const int32_t x = d[k];
-    // neighbouring keys mostly die together: one LDS atomic per run of equal
-    // times in the wave rather than one per lane on the same word
-    const int32_t left = __shfl_up(x, 1);
-    if (x > k && x < n_pad && ((threadIdx.x & 63) == 0 || left != x)) atomicOr(&set[x >> 5], 1u << (x & 31));
+  // eight loads in flight per thread, then their set bits; n_pad is a
+  // multiple of 128, so a key's validity is uniform over its wave
+  for (int64_t base = 0; base < n_pad; base += 8 * 1024) {
+    int32_t x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int64_t k = base + j * 1024 + threadIdx.x;
+      x[j] = k < n_pad ? d[k] : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int64_t k = base + j * 1024 + threadIdx.x;
+      if (k >= n_pad) break;
+      // neighbouring keys mostly die together: one LDS atomic per run of
+      // equal times in the wave rather than one per lane on the same word
+      const int32_t left = __shfl_up(x[j], 1);
+      if (x[j] > k && x[j] < n_pad && ((threadIdx.x & 63) == 0 || left != x[j]))
+        atomicOr(&set[x[j] >> 5], 1u << (x[j] & 31));
+    }
   }
   __syncthreads();
   // thread t owns words [t * per, (t + 1) * per): its count, then an
