@@ -28,6 +28,7 @@ struct kvs_ctx {
   size_t minmax_cap = 0;     // elements
   hipEvent_t minmax_done = nullptr;
   bool minmax_pending = false;
+  hipStream_t minmax_stream = nullptr;  // the stream of the call that recorded minmax_done
   char* events = nullptr;     // dense-mask scratch: distinct death times and key bit sets per rollout
   size_t events_cap = 0;      // bytes
   hipEvent_t events_done = nullptr;
@@ -243,7 +244,7 @@ ll_status kvs_block_mask(kvs_ctx* c, const int32_t* death_dev, int32_t n, int64_
     if (hipMalloc(reinterpret_cast<void**>(&c->minmax), mm * 2 * sizeof(int2)) != hipSuccess)
       return fail(LL_ENOMEM, "cannot allocate block-mask scratch");
     c->minmax_cap = mm * 2;
-  } else if (c->minmax_pending) {
+  } else if (c->minmax_pending && st != c->minmax_stream) {  // same stream: already in order
     // the scratch is reused: order this call after the last one that used it
     hipError_t e = hipStreamWaitEvent(st, c->minmax_done, 0);
     if (e != hipSuccess) return dev_fail(e, "hipStreamWaitEvent(scratch)");
@@ -266,6 +267,7 @@ ll_status kvs_block_mask(kvs_ctx* c, const int32_t* death_dev, int32_t n, int64_
   e = hipEventRecord(c->minmax_done, st);
   if (e != hipSuccess) return dev_fail(e, "hipEventRecord");
   c->minmax_pending = true;
+  c->minmax_stream = st;
   return LL_OK;
 } catch (...) {
   return host_exception(nullptr);
