@@ -54,8 +54,19 @@ static_assert(kPerThread * kDeathWaves == 4 * 64, "one wave scans the (slice, wa
 // the tile finishes before the scan's first barrier -- and dropped tokens get
 // d_k = t.  A mask whose length differs from the number of rows held sets the
 // status.
+// A barrier that orders LDS traffic only: each wave's LDS operations
+// complete, then the waves meet.  Global stores still in flight are not
+// waited for.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // LDS_LIST: the list lives in dynamic LDS (n_pad entries) instead of the
-// block's global scratch row, when it fits.
+// block's global scratch row, when it fits.  The event loop then shares only
+// LDS between threads (the death times it stores are read by no other thread
+// of the launch), so its barriers need not wait for those stores.
 template <bool LDS_LIST>
 __global__ __launch_bounds__(kDeathThreads) void kvs_death_kernel(KvsDeathLaunch a) {
   extern __shared__ int32_t lds_list[];
@@ -87,18 +98,28 @@ __global__ __launch_bounds__(kDeathThreads) void kvs_death_kernel(KvsDeathLaunch
     int64_t carry = 0;
     for (int64_t base = 0; base < len; base += int64_t{kPerThread} * kDeathThreads) {
       int32_t tok[kPerThread];
+      uint8_t keep[kPerThread];
       uint64_t bal[kPerThread];
+      // every load of the tile issued before the first ballot: indices past
+      // the rows are clamped to row 0 (in bounds: len >= 1, the list has n_pad
+      // entries), so the loads carry no branches and stay in flight together
 #pragma unroll
       for (int c = 0; c < kPerThread; ++c) {
         const int64_t i = base + int64_t{c} * kDeathThreads + threadIdx.x;
-        tok[c] = i < held ? list[i] : static_cast<int32_t>(t_prev + (i - held));
-        bal[c] = __ballot(i < len && m[i] != 0);
+        keep[c] = m[i < len ? i : 0];
+        const int32_t held_tok = list[i < held ? i : 0];
+        tok[c] = i < held ? held_tok : static_cast<int32_t>(t_prev + (i - held));
+      }
+#pragma unroll
+      for (int c = 0; c < kPerThread; ++c) {
+        const int64_t i = base + int64_t{c} * kDeathThreads + threadIdx.x;
+        bal[c] = __ballot(i < len && keep[c] != 0);
       }
       if (lane == 0) {
 #pragma unroll
         for (int c = 0; c < kPerThread; ++c) part[c * kDeathWaves + wave] = __popcll(bal[c]);
       }
-      __syncthreads();
+      if (LDS_LIST) lds_barrier(); else __syncthreads();
       if (wave == 0) {  // lane L scans entries 4L .. 4L + 3
         const int32_t v0 = part[4 * lane], v1 = part[4 * lane + 1], v2 = part[4 * lane + 2], v3 = part[4 * lane + 3];
         const int32_t own = v0 + v1 + v2 + v3;
@@ -115,7 +136,7 @@ __global__ __launch_bounds__(kDeathThreads) void kvs_death_kernel(KvsDeathLaunch
         part[4 * lane + 3] = excl + v0 + v1 + v2;
         if (lane == 63) tile_total = incl;
       }
-      __syncthreads();
+      if (LDS_LIST) lds_barrier(); else __syncthreads();
 #pragma unroll
       for (int c = 0; c < kPerThread; ++c) {
         const int64_t i = base + int64_t{c} * kDeathThreads + threadIdx.x;
@@ -124,7 +145,7 @@ __global__ __launch_bounds__(kDeathThreads) void kvs_death_kernel(KvsDeathLaunch
         else d[tok[c]] = static_cast<int32_t>(t);
       }
       carry += tile_total;
-      __syncthreads();
+      if (LDS_LIST) lds_barrier(); else __syncthreads();
     }
     held = carry;
     t_prev = t;
