@@ -295,3 +295,44 @@ def test_dense_mask_beyond_the_pre_pass_limit():
     assert np.array_equal(got, K.dense_bits(K.visibility_rows(d, rows)))
     del bits
     ctx.close()
+
+
+def test_masks_on_alternating_streams_share_the_scratch():
+    """Dense and block masks of two batches issued back to back on two
+    streams, then on the first again: each call reuses the context's scratch,
+    so a call on the other stream is ordered after the last one on the
+    device.  Every result compared with the definition."""
+    L = need_gpu()
+    ctx = L.KvsMask(0)
+    n_pad = 2048
+    rng = np_rng(33, 0)
+    k = np.arange(n_pad)
+    batches = []
+    for b in range(3):
+        times = np.sort(rng.choice(np.arange(1, n_pad), size=(5, 9, 40)[b], replace=False))
+        d = np.where(rng.random((4, n_pad)) < 0.6, times[rng.integers(0, len(times), size=(4, n_pad))], n_pad)
+        d = np.where(d > k, d, n_pad)
+        batches.append(d)
+    streams = [torch.cuda.Stream(), torch.cuda.Stream(), None]
+    # inputs and outputs made first and kept alive until the end, so that
+    # only the library orders the three calls
+    deaths = [torch.from_numpy(d.astype(np.int32)).cuda() for d in batches]
+    bufs = [(torch.empty((4, n_pad, n_pad // 32), dtype=torch.int32, device="cuda"),
+             tuple(torch.empty(shape, dtype=torch.int32, device="cuda")
+                   for shape in ((4, 32), (4, 32, 32), (4, 32), (4, 32, 32)))) for _ in batches]
+    torch.cuda.synchronize()
+    outs = []
+    for death, st, (bits, blocks) in zip(deaths, streams, bufs):
+        say(f"kvs masks on stream {st}")
+        outs.append((ctx.dense_mask(death, out=bits, stream=st), ctx.block_mask(death, 64, 64, out=blocks, stream=st)))
+    torch.cuda.synchronize()
+    for d, (bits, blocks) in zip(batches, outs):
+        got = bits.cpu().numpy().view(np.uint32)
+        pn, pi, fn, fi = (x.cpu().numpy() for x in blocks)
+        for r in range(d.shape[0]):
+            vis = K.visibility(d[r])
+            assert np.array_equal(got[r], K.dense_bits(vis)), r
+            partial, full = K.block_mask(vis, 64, 64)
+            for i in range(len(partial)):
+                assert list(pi[r, i, :pn[r, i]]) == partial[i] and list(fi[r, i, :fn[r, i]]) == full[i], (r, i)
+    ctx.close()
