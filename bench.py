@@ -70,6 +70,12 @@ sys.path.insert(0, ROOT)
 METRIC = "downstream KV GB/s moved+rotated (% HBM peak); splice latency @32k ctx"
 HBM_PEAK_GBS = 8000.0
 ROW = 576
+# Measured ceiling of the in-place band pattern on MI355X: read and write the
+# 128-byte k_pe line of every 1152-byte row, lines of 8 rows per load
+# instruction, over 0.9 GB of band lines cycled so that no repeat hits the
+# memory-side cache (best of the probe's variants; a contiguous copy of the
+# same bytes runs at 6.2 TB/s).
+INPLACE_CEILING_GBS = 4385.0
 
 
 def parse():
@@ -81,25 +87,28 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--workload", default="splice_32k_27layer",
-                    choices=["splice_32k_27layer", "splice_16x32k_27layer", "evict_256x16k_27layer_p16",
-                             "evict_256x16k_27layer_p1", "splice_32k_llama8b", "kvs_mask_64x32k",
-                             "rope_rows_32k_27layer", "splice_4k_1layer", "evict_32x16k_llama8b_p16"])
+                    choices=["splice_32k_27layer", "splice_32k_27layer_inplace", "splice_16x32k_27layer",
+                             "evict_256x16k_27layer_p16", "evict_256x16k_27layer_p1", "splice_32k_llama8b",
+                             "kvs_mask_64x32k", "rope_rows_32k_27layer", "rope_rows_32k_27layer_inplace",
+                             "splice_4k_1layer", "evict_32x16k_llama8b_p16", "drift_128k_60layer"])
     return ap.parse_args()
 
 
 # The source file of each measured kernel; its hash also covers the shared
 # device helpers and the launch structures.
-KERNEL_SOURCE = {"splice_kernel": "kernels.hip", "evict_move_kernel": "kernels.hip",
+KERNEL_SOURCE = {"splice_kernel": "kernels.hip", "splice_inplace_kernel": "kernels.hip",
+                 "evict_move_kernel": "kernels.hip", "dev_move_kernel": "kernels_alloc.hip",
                  "gqa_splice_kernel": "kernels_gqa.hip", "plane_evict_kernel": "kernels_gqa.hip",
                  "kvs_dense_ev_kernel": "kernels_kvs.hip", "rope_rows_kernel": "kernels_rows.hip",
-                 "rope_gather_mla_kernel": "kernels_rows.hip"}
+                 "rope_gather_mla_kernel": "kernels_rows.hip", "rope_inplace_mla_kernel": "kernels_rows.hip"}
 
 
 def kernel_source_sha(kernel: str) -> str:
     csrc = os.path.join(ROOT, "mla_paged_cache_amd", "csrc")
     src = KERNEL_SOURCE[kernel]
     headers = {"kernels_kvs.hip": ("kvs_internal.h",),
-               "kernels_rows.hip": ("device_common.h", "leyline_internal.h", "rows_internal.h")}.get(
+               "kernels_rows.hip": ("device_common.h", "leyline_internal.h", "rows_internal.h"),
+               "kernels_alloc.hip": ("device_common.h", "leyline_internal.h", "alloc_internal.h")}.get(
         src, ("device_common.h", "leyline_internal.h"))
     h = hashlib.sha256()
     for name in (*headers, src):
@@ -130,14 +139,41 @@ def quiet_gc():
 
 
 def prof_every(steps: int) -> int:
-    """Time about a dozen launches, spread evenly over the timed region: each
-    timed launch costs the stream a few microseconds of event stamps, which
-    would otherwise be charged to every step."""
+    """Time about a dozen launches, spread evenly over a measured region: each
+    timed launch costs the stream a few microseconds of event stamps."""
     return max(1, steps // 12)
 
 
+def kernel_pass(torch, pool, kernel, run, n, prepare=None):
+    """The kernel-timing pass, apart from the timed loop (which stamps no
+    launch): n calls of run(i) with every launch of `kernel` stamped by HIP
+    events on the stream it runs on.  Returns (launches, total_ms,
+    total_bytes, per-launch ms)."""
+    if prepare is not None:
+        prepare()
+    pool.profile_read(kernel)
+    torch.cuda.synchronize()
+    pool.set_profiling(True, 1)
+    quiet_gc()
+    for i in range(n):
+        run(i)
+    torch.cuda.synchronize()
+    gc.enable()
+    pool.set_profiling(False)
+    return pool.profile_read(kernel, samples=n + 8)
+
+
+def pct(samples, q):
+    """q-th percentile (0..100) by linear interpolation."""
+    if not samples:
+        return None
+    return float(np.percentile(np.asarray(samples, dtype=np.float64), q))
+
+
 def copy_ceiling(torch, dev, n_bytes):
-    """Plain device copy of n_bytes (read + write), for context."""
+    """Plain device copy of n_bytes (read + write), for context; at least
+    1 GiB, so that repeats do not run out of the memory-side cache."""
+    n_bytes = max(n_bytes, 1 << 30)
     src = torch.empty(n_bytes, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
     for _ in range(3):
@@ -152,11 +188,11 @@ def copy_ceiling(torch, dev, n_bytes):
     return 2 * n_bytes * 20 / (e0.elapsed_time(e1) * 1e-3) / 1e9
 
 
-def roofline(kernel, workload, launches, kernel_ms, kernel_bytes):
+def roofline(kernel, workload, launches, kernel_ms, kernel_bytes, samples=None):
     k_avg_ms = kernel_ms / max(1, launches)
     per = kernel_bytes // max(1, launches)
     achieved = per / (k_avg_ms * 1e-3) / 1e9 if k_avg_ms > 0 else 0.0
-    return {
+    out = {
         "bound": "hbm",
         "achieved": round(achieved, 2),
         "peak": HBM_PEAK_GBS,
@@ -168,6 +204,10 @@ def roofline(kernel, workload, launches, kernel_ms, kernel_bytes):
         "timed_launches": launches,
         "bytes_per_launch": per,
     }
+    if samples:
+        out["kernel_us"] = {"median": round(pct(samples, 50) * 1e3, 2), "p10": round(pct(samples, 10) * 1e3, 2),
+                            "p90": round(pct(samples, 90) * 1e3, 2), "samples": len(samples)}
+    return out
 
 
 def base_line(args, workload, value, ms_per_step, config):
@@ -190,28 +230,186 @@ def base_line(args, workload, value, ms_per_step, config):
 
 # ------------------------------------------------------------------ splice --
 
+def bench_drift(args):
+    """Long context: one sequence of 131072 tokens, 60 layers, page size 16,
+    randomly permuted pages in a pool of 16384, takes 10 successive seeded
+    AMORTIZE splices (span U[1024, 16384], stub U[8, 64], start
+    U[1024, len - span]) with the rotation in float32 on bf16 storage
+    ("Leyline", section 4.3: the error stays small and grows sub-linearly
+    with fp32 rotation).  A step is one splice; the ten are the workload, so
+    --steps is not used.  Three passes over the same ten directives from the
+    same initial table: the first untimed (its tables are checked against the
+    oracle's page plan, and two layers whose k_pe was stored as
+    bf16(RoPE(i) k) give the drift per number of rotations a row went
+    through); the second times the ten calls back to back (value); the third
+    stamps every launch (roofline, per splice)."""
+    import torch
+    from mla_paged_cache_amd import leyline as L
+    from oracle import leyline_oracle as O
+    from synth import draw_span, np_rng, permuted_pages, random_normal_np, random_rows_np, random_rows_torch
+
+    LAYERS, TOKENS, PAGE, POOL_PAGES, SPLICES = 60, 131072, 16, 16384, 10
+    TRACKED = (0, 59)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    data = random_rows_torch(5, (LAYERS, POOL_PAGES, PAGE, ROW), dev)
+    table = torch.full((1, POOL_PAGES), -1, dtype=torch.int32, device=dev)
+    pool = L.Pool(data, table)
+    T = permuted_pages(5, TOKENS // PAGE)
+    j = np.arange(TOKENS)
+    phys = np.asarray(T, np.int64)[j // PAGE] * PAGE + j % PAGE
+    phys_dev = torch.from_numpy(phys).to(dev)
+
+    def roped(seed, positions):
+        n = len(positions)
+        rows = random_rows_np(seed, (n, ROW))
+        k = random_normal_np(seed, (n, O.ROPE_DIM))
+        rows[:, O.KV_LORA_RANK:] = O.f32_to_bf16(O.rotate_f64(k, positions).astype(np.float32))
+        return rows, k
+
+    k_raw = {}
+    for layer in TRACKED:
+        rows, k_raw[layer] = roped(100 + layer, j)
+        data[layer].view(-1, ROW)[phys_dev] = torch.from_numpy(rows.view(np.int16)).view(torch.bfloat16).to(dev)
+    rng = np_rng(5, 7)
+    plan = O.CacheState.empty(0, POOL_PAGES, PAGE, POOL_PAGES, with_rows=False)
+    plan.set_pages(0, T, TOKENS)
+    dirs, stubs, spans, expected = [], [], [], []
+    origin = np.arange(TOKENS)
+    turns = np.zeros(TOKENS, np.int64)
+    for k in range(SPLICES):
+        n = plan.lengths[0]
+        d = draw_span(rng, n, 1024, 16384, 8, 64)
+        delta = d.r_len - (d.s_end - d.s_start)
+        stub = random_rows_torch(2000 + k, (LAYERS, d.r_len, ROW), dev)
+        for layer in TRACKED:
+            rows, _ = roped(1000 * k + layer, np.arange(d.s_start, d.s_start + d.r_len))
+            stub[layer] = torch.from_numpy(rows.view(np.int16)).view(torch.bfloat16).to(dev)
+        stubs.append(stub)
+        dirs.append([L.Directive(0, d.s_start, d.s_end, stub)])
+        spans.append((d.s_start, d.s_end, d.r_len))
+        kind, index, down = O.splice_sources(n, d.s_start, d.s_end, d.r_len)
+        origin = np.where(kind == 0, origin[np.where(kind == 0, index, 0)], -1)
+        turns = np.where(kind == 0, turns[np.where(kind == 0, index, 0)] + (down & (delta != 0)), 0)
+        # the oracle's page plan only (no rows on the host): the stub is a placeholder
+        plan, _ = O.splice(plan, [O.Directive(0, d.s_start, d.s_end, d.r_len, ())])
+        expected.append((plan.lengths[0], plan.next_pos[0], list(plan.tables[0])))
+
+    def restore():
+        pool.seq_set_pages(0, T, TOKENS)
+        torch.cuda.synchronize()
+
+    # pass 1: untimed; tables against the oracle's plan, drift of two layers
+    restore()
+    per_bytes = []
+    for k in range(SPLICES):
+        pool.splice(dirs[k])
+        n2, pos, pages = pool.seq_get(0)
+        if (n2, pos, list(pages)) != expected[k]:
+            raise SystemExit(f"splice {k}: the GPU page plan differs from the oracle's")
+        per_bytes.append(pool.last_stats().alg_bytes)
+    torch.cuda.synchronize()
+    n = plan.lengths[0]
+    jj = np.arange(n)
+    pages = np.asarray(plan.tables[0], np.int64)
+    ph = torch.from_numpy(pages[jj // PAGE] * PAGE + jj % PAGE).to(dev)
+    keep = origin >= 0
+    drift, glob = {}, {}
+    for layer in TRACKED:
+        got = data[layer].view(-1, ROW)[ph].view(torch.int16).cpu().numpy().view(np.uint16)
+        kpe = O.bf16_to_f32(got[keep, O.KV_LORA_RANK:]).astype(np.float64)
+        fresh = O.rotate_f64(k_raw[layer][origin[keep]], jj[keep])
+        t = turns[keep]
+        glob[layer] = float(np.linalg.norm(kpe - fresh) / np.linalg.norm(fresh))
+        for kk in np.unique(t):
+            m = t == kk
+            err = float(np.linalg.norm(kpe[m] - fresh[m]) / np.linalg.norm(fresh[m]))
+            cur = drift.setdefault(int(kk), {"rows": int(m.sum()), "rel_l2": 0.0})
+            cur["rel_l2"] = max(cur["rel_l2"], err)
+
+    # pass 2: the ten calls back to back, nothing stamped
+    for _ in range(max(1, args.warmup // 5)):
+        restore()
+        for k in range(SPLICES):
+            pool.splice(dirs[k])
+    restore()
+    quiet_gc()
+    t0 = time.perf_counter()
+    for k in range(SPLICES):
+        pool.splice(dirs[k])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    gc.enable()
+    ms_per_splice = (t1 - t0) * 1e3 / SPLICES
+    total = sum(per_bytes)
+    # pass 3: every launch stamped
+    restore()
+    launches, kernel_ms, kernel_bytes, samples = kernel_pass(torch, pool, 0, lambda k: pool.splice(dirs[k]), SPLICES)
+    out = base_line(args, "drift_128k_60layer", total / (ms_per_splice * 1e-3 * SPLICES) / 1e9, ms_per_splice, {
+        "layers": LAYERS, "tokens": TOKENS, "page_size": PAGE, "pool_pages": POOL_PAGES, "splices": SPLICES,
+        "directives": [list(x) for x in spans], "alg_bytes_per_splice": per_bytes,
+        "draws": "span U[1024,16384], stub U[8,64], start U[1024,len-span], seeded",
+        "storage": "bf16 rows c_kv 512 + k_pe 64, rotation in f32"})
+    out["steps"] = SPLICES
+    out["roofline"] = roofline("splice_kernel", "drift_128k_60layer", launches, kernel_ms, kernel_bytes)
+    out["roofline"]["per_splice_gbs"] = [round(b / (ms * 1e-3) / 1e9, 1) for b, ms in zip(per_bytes, samples)]
+    out["drift"] = {"protocol": "k_pe stored as bf16(RoPE_f64(i) k), k ~ N(0,1), layers 0 and 59; relative L2 "
+                                "to float64 RoPE at the final position, the worse layer, per number of rotations",
+                    "by_rotations": {str(k): v for k, v in sorted(drift.items())},
+                    "all_rows": round(max(glob.values()), 6),
+                    "sqrt_law": "1.66e-3 * sqrt(k + 1)"}
+    out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline_drift(T, spans[0], per_bytes[0], LAYERS,
+                                                                               TOKENS, PAGE, POOL_PAGES)
+    pool.close()
+    return out
+
+
+def cpu_baseline_drift(T, span, alg_bytes, LAYERS, TOKENS, PAGE, POOL_PAGES):
+    """The oracle's first splice of the drift workload, in full: all 60
+    layers of the 131072-token sequence, the whole 16384-page pool held on the
+    host (18 GB), run once."""
+    from oracle import leyline_oracle as O
+    st = O.CacheState.empty(0, POOL_PAGES, PAGE, POOL_PAGES, with_rows=False)
+    st.layers = host_pool(LAYERS, POOL_PAGES, PAGE, ROW)
+    st.set_pages(0, T, TOKENS)
+    s0, s1, r = span
+    d = [O.Directive(0, s0, s1, r, [np.full((r, ROW), 0x3F80, np.uint16)] * LAYERS)]
+    a = time.perf_counter()
+    O.splice(st, d)
+    t = time.perf_counter() - a
+    return oracle_line(alg_bytes, 1, t, f"the first of the ten splices in full ({LAYERS} layers, {TOKENS} tokens, "
+                                        f"{POOL_PAGES}-page pool on the host)")
+
+
 MAX_DISTINCT_SEQS = 64
 
 
-def bench_splice_32k(args):
+def bench_splice_32k(args, STUB=24, workload="splice_32k_27layer", kernel="splice_kernel"):
     """The headline.  Every timed step splices its own 32k x 27 sequence: up to
     64 identically shaped sequences, each a random permutation of its own 2048
     pages, sit above a spare region that holds every step's fresh pages, so
     each step's fresh pages are one run of consecutive ids (as in a pool that
     holds the one sequence) and no table restore runs between steps.  The
     JSON also gives, for context, the step that restores one sequence's table
-    before each splice, and the step with the host-staged page plan."""
+    before each splice, and the step with the host-staged page plan.
+
+    With STUB = 0 (splice_32k_27layer_inplace) Delta = -6144 is a whole
+    number of pages: no page is fresh, and every downstream row only has its
+    k_pe band turned in place (splice_inplace_kernel).  Each step's sequence is
+    its own, so the bands it turns are read from HBM, not from the last step's
+    caches."""
     import torch
     from mla_paged_cache_amd import leyline as L
     from synth import permuted_pages, random_rows_torch
 
     LAYERS, TOKENS, PAGE = 27, 32768, 16
-    S_START, S_END, STUB = 8192, 14336, 24
+    S_START, S_END = 8192, 14336
     NP = TOKENS // PAGE
     # Delta = -6120 is not a multiple of the page size, so every new page from
-    # the one holding s_start on is fresh
+    # the one holding s_start on is fresh; Delta = -6144 is, and s_start is on
+    # a page boundary, so then no page is fresh
     new_pages = -(-(TOKENS + STUB - (S_END - S_START)) // PAGE)
-    FRESH = new_pages - S_START // PAGE
+    FRESH = 0 if (STUB - (S_END - S_START)) % PAGE == 0 else new_pages - S_START // PAGE
     distinct = args.steps <= MAX_DISTINCT_SEQS
     NSEQ = args.steps if distinct else 1
     SPARE = max(NSEQ, 2) * FRESH
@@ -222,7 +420,7 @@ def bench_splice_32k(args):
     data[:, :SPARE].zero_()
     for s in range(NSEQ):
         data[:, SPARE + s * NP:SPARE + (s + 1) * NP] = random_rows_torch(s, (LAYERS, NP, PAGE, ROW), dev)
-    stub = random_rows_torch(1000, (LAYERS, STUB, ROW), dev)
+    stub = random_rows_torch(1000, (LAYERS, STUB, ROW), dev) if STUB else None
     table = torch.full((NSEQ, NP + 8), -1, dtype=torch.int32, device=dev)
     pool = L.Pool(data, table)
     T0 = permuted_pages(0, NP)                       # sequence 0: the oracle's table
@@ -285,17 +483,16 @@ def bench_splice_32k(args):
         restore_step(0)
     # context: one sequence, its table restored before every splice
     ms_restore = timed(restore_step, args.steps)
-    # throughput: K whole splices, bracketed by synchronize, with the row
-    # kernel timed on a sample of the launches
+    # throughput: K whole splices, bracketed by synchronize; no launch in
+    # this loop is stamped
+    step = distinct_step if distinct else restore_step
     if distinct:
         set_all()
-    pool.profile_read(0)
-    pool.set_profiling(True, prof_every(args.steps))
-    torch.cuda.synchronize()
-    ms_per_step = timed(distinct_step if distinct else restore_step, args.steps)
-    pool.set_profiling(False)
-    launches, kernel_ms, kernel_bytes = pool.profile_read(0)
+    ms_per_step = timed(step, args.steps)
     value = alg_bytes / (ms_per_step * 1e-3) / 1e9
+    # the row kernel's own time: a separate pass with every launch stamped
+    launches, kernel_ms, kernel_bytes, samples = kernel_pass(torch, pool, 0, step, args.steps,
+                                                             set_all if distinct else None)
     ms_host_plan = None
     if distinct:
         set_all()
@@ -320,10 +517,11 @@ def bench_splice_32k(args):
     gc.enable()
     del flush
 
-    out = base_line(args, "splice_32k_27layer", value, ms_per_step, {
+    out = base_line(args, workload, value, ms_per_step, {
         "layers": LAYERS, "tokens": TOKENS, "page_size": PAGE, "span": [S_START, S_END], "stub_rows": STUB,
         "delta": STUB - (S_END - S_START), "storage": "bf16 rows c_kv 512 + k_pe 64, rotation in f32",
-        "alg_bytes_per_step": alg_bytes,
+        "alg_bytes_per_step": alg_bytes, "fresh_pages": st.fresh_pages,
+        "rows_turned_in_place_per_layer": st.rows_rotated_inplace,
         "sequences": f"{NSEQ} of this shape, one spliced per step, each on its own randomly permuted pages"
                      if distinct else "one, its page table restored before every splice (more steps than "
                                       f"{MAX_DISTINCT_SEQS} distinct sequences)",
@@ -335,7 +533,7 @@ def bench_splice_32k(args):
     out["splice_latency_us"] = {"median": round(statistics.median(lat), 1), "min": round(min(lat), 1),
                                 "max": round(max(lat), 1), "runs": len(lat),
                                 "host_call_median": round(statistics.median(host), 1)}
-    out["roofline"] = roofline("splice_kernel", "splice_32k_27layer", launches, kernel_ms, kernel_bytes)
+    out["roofline"] = roofline(kernel, workload, launches, kernel_ms, kernel_bytes, samples)
     out["copy_ceiling_gbs"] = round(copy_ceiling(torch, dev, alg_bytes // 2), 1)
     out["cpu_baseline"] = None
     if host_before is not None:
@@ -363,7 +561,7 @@ def cpu_baseline_splice(host_before, gpu_after, T, alg_bytes, seconds, LAYERS, T
     st.layers = [np.concatenate([host_before[i], pad]) for i in range(LAYERS)]
     st.set_pages(0, T, TOKENS)
     stub_host = random_rows_torch(stub_seed, (LAYERS, STUB, ROW), "cuda:0").view(torch.int16).cpu().numpy().view(
-        np.uint16)
+        np.uint16) if STUB else None
     d = [O.Directive(0, S_START, S_END, STUB, stub_host)]
     runs, t = 0, 0.0
     new = None
@@ -380,7 +578,7 @@ def cpu_baseline_splice(host_before, gpu_after, T, alg_bytes, seconds, LAYERS, T
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": f"the full 27-layer splice, run {runs} times ({t:.1f} s) by the numpy oracle on one core "
+        "sample": f"the full {LAYERS}-layer splice, run {runs} times ({t:.1f} s) by the numpy oracle on one core "
                   f"({len(os.sched_getaffinity(0))} available, {cpu_model()}); GPU result matched it bit-exactly",
     }
 
@@ -577,15 +775,18 @@ def cpu_baseline_kvs(rolls, seconds, TOKENS):
                        "dense bits (dense bytes counted, as on the GPU line)")
 
 
-def cpu_baseline_rope(seconds, LAYERS, TOKENS, PAGE, POOL_PAGES):
-    """The oracle's per-row gather (angle -p for row p) of the whole sequence,
-    all layers."""
+def cpu_baseline_rope(seconds, LAYERS, TOKENS, PAGE, POOL_PAGES, in_place=False):
+    """The oracle's per-row rotation (angle -p for row p) of the whole
+    sequence, all layers, gathered or in place."""
     from oracle import leyline_oracle as O
     from synth import permuted_pages
     st = O.CacheState.empty(0, POOL_PAGES, PAGE, TOKENS // PAGE + 8, with_rows=False)
     st.layers = host_pool(LAYERS, POOL_PAGES, PAGE, ROW)
     st.set_pages(0, permuted_pages(0, TOKENS // PAGE), TOKENS)
     angles = -np.arange(TOKENS, dtype=np.int64)
+    if in_place:
+        runs, t, _ = timed_oracle(lambda: O.rope_rows(st, 0, 0, angles, in_place=True), seconds)
+        return oracle_line(LAYERS * TOKENS * 2 * 128, runs, t, f"all {TOKENS} rows, all {LAYERS} layers, in place")
     runs, t, _ = timed_oracle(lambda: O.rope_rows(st, 0, 0, angles), seconds)
     return oracle_line(LAYERS * TOKENS * 2 * ROW * 2, runs, t, f"all {TOKENS} rows, all {LAYERS} layers, gathered")
 
@@ -630,7 +831,7 @@ def _oracle_layers_worker(task):
     st.layers = [O.f32_to_bf16(rng.standard_normal((pool_pages, page, ROW), dtype=np.float32))
                  for _ in range(n_layers)]
     st.set_pages(0, T, tokens)
-    stub_rows = O.f32_to_bf16(rng.standard_normal((n_layers, stub, ROW), dtype=np.float32))
+    stub_rows = O.f32_to_bf16(rng.standard_normal((n_layers, stub, ROW), dtype=np.float32)) if stub else None
     d = [O.Directive(0, s_start, s_end, stub, stub_rows)]
     _layer_barrier.wait(timeout=300)
     runs, t = 0, 0.0
@@ -788,60 +989,71 @@ def bench_splice_gqa(args):
 
 # ------------------------------------------------------ per-row rotation --
 
-def bench_rope_rows(args):
-    """All 32768 rows of the 27-layer MLA cache (page size 16, permuted pages)
-    gathered into a dense [27][32768][576] buffer with k_pe turned back by
-    each row's position (angle -p), as VECTOR does before reconstructing V
-    from K.  A step is one ll_rope_rows call (per-row table kernel + row
-    kernel).  The same rows turned in place are timed after it."""
+def bench_rope_rows(args, in_place=False):
+    """Per-row-angle rotation of MLA rows (page size 16, permuted pages), as
+    VECTOR does before reconstructing V from K: every row's k_pe turned back by
+    its position (angle -p).  rope_rows_32k_27layer gathers all 32768 rows of a
+    27-layer sequence into a dense [27][32768][576] buffer (per-row table
+    kernel + row kernel); rope_rows_32k_27layer_inplace turns the same rows in
+    place (one kernel: 128-byte k_pe lines 1152 bytes apart, read and
+    written).  A step is one ll_rope_rows call.  The pool holds 8 such
+    sequences, 8.2 GB, and step i works on sequence i mod 8, so a step's rows
+    (0.9 GB of band lines in place, 1 GB of rows gathered) never sit in the
+    chip's 256 MB memory-side cache from an earlier step."""
     import torch
     from mla_paged_cache_amd import leyline as L
     from synth import permuted_pages, random_rows_torch
 
-    LAYERS, TOKENS, PAGE, POOL_PAGES = 27, 32768, 16, 4096
+    LAYERS, TOKENS, PAGE, NSEQ = 27, 32768, 16, 8
+    NP = TOKENS // PAGE
+    POOL_PAGES = NSEQ * NP
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    data = random_rows_torch(0, (LAYERS, POOL_PAGES, PAGE, ROW), dev)
-    table = torch.full((1, TOKENS // PAGE + 8), -1, dtype=torch.int32, device=dev)
+    data = torch.empty((LAYERS, POOL_PAGES, PAGE, ROW), dtype=torch.bfloat16, device=dev)
+    for q in range(NSEQ):
+        data[:, q * NP:(q + 1) * NP] = random_rows_torch(q, (LAYERS, NP, PAGE, ROW), dev)
+    table = torch.full((NSEQ, NP + 8), -1, dtype=torch.int32, device=dev)
     pool = L.Pool(data, table)
-    pool.seq_set_pages(0, permuted_pages(0, TOKENS // PAGE), TOKENS)
+    perm = permuted_pages(0, POOL_PAGES)
+    for q in range(NSEQ):
+        pool.seq_set_pages(q, perm[q * NP:(q + 1) * NP], TOKENS)
     angles = -torch.arange(TOKENS, dtype=torch.int64, device=dev)
-    out = torch.empty((LAYERS, TOKENS, ROW), dtype=torch.bfloat16, device=dev)
+    out = None if in_place else torch.empty((LAYERS, TOKENS, ROW), dtype=torch.bfloat16, device=dev)
     pool.rope_rows(0, 0, angles, out=out)
     torch.cuda.synchronize()
     alg = pool.last_stats().alg_bytes
 
-    def timed(in_place):
-        for _ in range(args.warmup):
-            pool.rope_rows(0, 0, angles, out=None if in_place else out)
-        torch.cuda.synchronize()
-        pool.profile_read(2)
-        pool.set_profiling(True, prof_every(args.steps))
-        quiet_gc()
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            pool.rope_rows(0, 0, angles, out=None if in_place else out)
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
-        gc.enable()
-        pool.set_profiling(False)
-        return (t1 - t0) * 1e3 / args.steps, pool.profile_read(2)
+    def step(i):
+        pool.rope_rows(i % NSEQ, 0, angles, out=out)
 
-    ms_per_step, (launches, kernel_ms, kernel_bytes) = timed(False)
-    ip_ms, (ip_launches, ip_kernel_ms, ip_bytes) = timed(True)
-    out_line = base_line(args, "rope_rows_32k_27layer", alg / (ms_per_step * 1e-3) / 1e9, ms_per_step, {
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    quiet_gc()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    gc.enable()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    launches, kernel_ms, kernel_bytes, samples = kernel_pass(torch, pool, 2, step, args.steps)
+    name = "rope_rows_32k_27layer_inplace" if in_place else "rope_rows_32k_27layer"
+    out_line = base_line(args, name, alg / (ms_per_step * 1e-3) / 1e9, ms_per_step, {
         "layers": LAYERS, "tokens": TOKENS, "page_size": PAGE, "angles": "-position of each row",
-        "mode": "gather to a dense buffer", "alg_bytes_per_step": alg})
+        "mode": "in place (k_pe bands only)" if in_place else "gather to a dense buffer",
+        "sequences": f"{NSEQ}, step i on sequence i mod {NSEQ}", "pool_pages": POOL_PAGES,
+        "alg_bytes_per_step": alg})
     out_line["metric"] = "per-row-angle RoPE rotation: row bytes GB/s"
-    # MLA rows at page size 16 are gathered by rope_gather_mla_kernel (the
-    # timed launch also holds the per-row table kernel)
-    out_line["roofline"] = roofline("rope_gather_mla_kernel", "rope_rows_32k_27layer", launches, kernel_ms,
-                                    kernel_bytes)
-    out_line["in_place"] = {"ms_per_step": round(ip_ms, 5), "kernel_avg_us": round(ip_kernel_ms * 1e3 / max(1, ip_launches), 2),
-                            "alg_bytes": ip_bytes // max(1, ip_launches),
-                            "achieved_gbs": round(ip_bytes / max(1e-9, ip_kernel_ms * 1e-3) / 1e9, 1)}
+    # MLA rows at page size 16: gathered by rope_gather_mla_kernel (the timed
+    # launch also holds the per-row table kernel), turned in place by
+    # rope_inplace_mla_kernel alone
+    kernel = "rope_inplace_mla_kernel" if in_place else "rope_gather_mla_kernel"
+    out_line["roofline"] = roofline(kernel, name, launches, kernel_ms, kernel_bytes, samples)
+    if in_place:
+        out_line["access_pattern_ceiling_gbs"] = INPLACE_CEILING_GBS
     out_line["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline_rope(
-        args.cpu_seconds, LAYERS, TOKENS, PAGE, POOL_PAGES)
+        args.cpu_seconds, LAYERS, TOKENS, PAGE, NP * 2, in_place)
     pool.close()
     return out_line
 
@@ -1120,6 +1332,13 @@ def main():
         sys.exit(2)
     if args.workload == "splice_32k_27layer":
         out = bench_splice_32k(args)
+    elif args.workload == "splice_32k_27layer_inplace":
+        out = bench_splice_32k(args, STUB=0, workload="splice_32k_27layer_inplace", kernel="splice_inplace_kernel")
+        out["access_pattern_ceiling_gbs"] = INPLACE_CEILING_GBS
+    elif args.workload == "drift_128k_60layer":
+        out = bench_drift(args)
+    elif args.workload == "rope_rows_32k_27layer_inplace":
+        out = bench_rope_rows(args, in_place=True)
     elif args.workload == "splice_4k_1layer":
         out = bench_splice_4k(args)
     elif args.workload == "splice_16x32k_27layer":

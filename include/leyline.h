@@ -148,14 +148,17 @@ typedef struct {
                                    from kernel arguments); 0: the host did */
 } ll_plan_stats;
 
-/* Create a pool over caller-owned device memory.  Checks the descriptor,
+/* [Leyline] section 3: agent edits become block-level operations on a paged
+ * KV store; this is that store.  Create a pool over caller-owned device
+ * memory.  Checks the descriptor,
  * copies the layer pointer array to the device and allocates staging.  All
  * pages start free and no sequence exists.  Errors: LL_EINVAL (bad field or
  * NULL pointer), LL_EUNSUPPORTED (row shape other than 512 + 64),
  * LL_EDEVICE. */
 ll_status ll_pool_create(const ll_pool_desc* desc, ll_pool** out);
 
-/* A GQA / MHA cache (MHA: num_kv_heads = number of attention heads). */
+/* A GQA / MHA cache (MHA: num_kv_heads = number of attention heads);
+ * [Leyline] section 5: the directive carries over to GQA and MHA caches. */
 typedef struct {
   int32_t num_layers;        /* >= 1 */
   int32_t page_size;         /* rows per page: a power of two, 1 .. 256 */
@@ -174,39 +177,48 @@ typedef struct {
   int32_t device;
 } ll_gqa_pool_desc;
 
-/* Create a GQA / MHA pool over caller-owned device memory; the same calls as
+/* [Leyline] section 5 (GQA / MHA) over the block store of section 3.
+ * Create a GQA / MHA pool over caller-owned device memory; the same calls as
  * for an MLA pool then apply to it.  Errors: LL_EINVAL (bad field or NULL
  * pointer), LL_EUNSUPPORTED (head_dim, rotary_dim or row width outside the
  * ranges above), LL_EDEVICE. */
 ll_status ll_pool_create_gqa(const ll_gqa_pool_desc* desc, ll_pool** out);
 
-/* Wait for the pool's device work and free what the library allocated.  The
+/* [Leyline] section 3 (block-level KV store): end of a pool's life.
+ * Wait for the pool's device work and free what the library allocated.  The
  * caller's buffers are not touched.  NULL is ignored. */
 void ll_pool_destroy(ll_pool* pool);
 
-/* New sequence of n_tokens >= 0 rows: the lowest free sequence id and the
+/* [Leyline] section 3 (block-level KV store): a sequence's pages.
+ * New sequence of n_tokens >= 0 rows: the lowest free sequence id and the
  * ceil(n_tokens / page_size) lowest free pages; next position = n_tokens.
  * Row contents are the caller's to write (prefill).  Errors: LL_EINVAL,
  * LL_ERANGE, LL_ENOMEM (no free id or pages). */
 ll_status ll_seq_alloc(ll_pool* pool, int64_t n_tokens, int32_t* seq_id_out, void* stream);
 
-/* Give sequence seq_id (new or existing) an explicit page table: `pages` is a
+/* [Leyline] section 3 (block-level KV store): a sequence's page table.
+ * Give sequence seq_id (new or existing) an explicit page table: `pages` is a
  * host array of ceil(n_tokens / page_size) distinct physical pages, each free
  * or already owned by seq_id.  Pages the sequence held and no longer lists are
  * freed; next position = n_tokens.  Errors: LL_EINVAL, LL_ERANGE. */
 ll_status ll_seq_set_pages(ll_pool* pool, int32_t seq_id, const int32_t* pages,
                            int64_t n_tokens, void* stream);
 
-/* Release a sequence and all of its pages.  Errors: LL_EINVAL. */
+/* [Leyline] section 3 (block-level KV store): release a sequence and all of
+ * its pages.  Errors: LL_EINVAL. */
 ll_status ll_seq_free(ll_pool* pool, int32_t seq_id);
 
-/* Host copy of a sequence's state: length, next RoPE position and up to `cap`
+/* [Leyline] section 2.2 (positions move by Delta) and [KV-streams] "how it
+ * works" (eviction keeps positions), read back from the block store of
+ * [Leyline] section 3.
+ * Host copy of a sequence's state: length, next RoPE position and up to `cap`
  * page-table entries (pages_out may be NULL when cap == 0); *n_pages_out gets
  * the page count.  Errors: LL_EINVAL. */
 ll_status ll_seq_get(const ll_pool* pool, int32_t seq_id, int64_t* len, int64_t* next_position,
                      int32_t* pages_out, int32_t cap, int32_t* n_pages_out);
 
-/* Number of free pages. */
+/* [Leyline] section 3 (block-level KV store): number of free pages.
+ * Errors: LL_EINVAL. */
 ll_status ll_pool_free_pages(const ll_pool* pool, int64_t* n_free);
 
 /* Apply n directives, at most one per sequence ([Leyline] sections 2.1-2.3).
@@ -304,17 +316,33 @@ ll_status ll_rope_rows(ll_pool* pool, int32_t seq_id, int64_t row_begin, int64_t
 ll_status ll_rope_delta_table(double base, int32_t rope_dim, int64_t delta,
                               float* cos_out, float* sin_out);
 
-/* Counters of the last splice / evict / reindex call.  Errors: LL_EINVAL. */
+/* Library bookkeeping, no passage of the pages defines it: counters of the
+ * last splice / evict / reindex / per-row rotation call.  Errors: LL_EINVAL. */
 ll_status ll_last_plan_stats(const ll_pool* pool, ll_plan_stats* out);
 
-/* Who expands a splice batch's page plan (see leyline_splice):
+/* Library bookkeeping, no passage of the pages defines it: the first three
+ * counters of ll_last_plan_stats -- the algorithmic row bytes of the last
+ * call, the rows it wrote to fresh pages (per layer) and the rows it turned in
+ * place (per layer).  Any output pointer may be NULL.  Errors: LL_EINVAL. */
+ll_status ll_last_plan_bytes(const ll_pool* pool, int64_t* alg_bytes, int64_t* rows_moved,
+                             int64_t* rows_rotated_inplace);
+
+/* Library bookkeeping, no passage of the pages defines it: the current length
+ * of each of n sequences seq_ids[i] into lengths_out[i] (host arrays), e.g. to
+ * size keep masks for kv_evict_compact.  Errors: LL_EINVAL (unknown
+ * sequence). */
+ll_status ll_seq_lengths(const ll_pool* pool, const int32_t* seq_ids, int32_t n, int64_t* lengths_out);
+
+/* Library bookkeeping, no passage of the pages defines it.
+ * Who expands a splice batch's page plan (see leyline_splice):
  * LL_SPLICE_PLAN_AUTO (the default) lets the device do it when the batch
  * fits in kernel arguments; LL_SPLICE_PLAN_HOST always stages and uploads the
  * host's tasks.  Results do not depend on the choice.  Errors: LL_EINVAL. */
 typedef enum { LL_SPLICE_PLAN_AUTO = 0, LL_SPLICE_PLAN_HOST = 1 } ll_splice_planner;
 ll_status ll_pool_set_splice_planner(ll_pool* pool, int32_t planner);
 
-/* Kernel timing.  `enable` = n > 0 times every n-th launch (counted from
+/* Library bookkeeping, no passage of the pages defines it.
+ * Kernel timing.  `enable` = n > 0 times every n-th launch (counted from
  * this call; 1: every launch) of the row-moving kernel (kernel 0; on the
  * device-planned eviction path its page-plan kernels too), of the keep-mask
  * scan (kernel 1) and of the per-row rotation (kernel 2: its table and row
@@ -323,11 +351,14 @@ ll_status ll_pool_set_splice_planner(ll_pool* pool, int32_t planner);
  * first kernel, the end of its last); the stamps still cost the stream a few
  * microseconds per timed launch, hence the sampling.
  * ll_profile_read waits for the recorded events, returns the launch count,
- * the summed milliseconds and the summed algorithmic bytes of `kernel`, and
- * clears its record.  Errors: LL_EINVAL, LL_EDEVICE. */
+ * the summed milliseconds and the summed algorithmic bytes of `kernel`, puts
+ * the milliseconds of the first each_cap timed launches, in launch order,
+ * into each_ms (host floats; NULL when each_cap is 0), and clears the
+ * record.  Any other output pointer may be NULL.  Errors: LL_EINVAL,
+ * LL_EDEVICE. */
 ll_status ll_pool_set_profiling(ll_pool* pool, int32_t enable);
 ll_status ll_profile_read(ll_pool* pool, int32_t kernel, int64_t* launches, double* total_ms,
-                          int64_t* total_bytes);
+                          int64_t* total_bytes, float* each_ms, int64_t each_cap);
 
 /* ------------------------------------------------------------------------
  * KV-streams trainer-side attention mask ([KV-streams] "how it works": the
@@ -358,12 +389,13 @@ typedef struct {
                                 its other masks follow back to back */
 } kvs_rollout_log;
 
-/* Create / destroy a context on HIP device `device`.  Errors: LL_EINVAL,
- * LL_EDEVICE. */
+/* [KV-streams] "how it works" (the trainer's mask).  Create / destroy a
+ * context on HIP device `device`.  Errors: LL_EINVAL, LL_EDEVICE. */
 ll_status kvs_ctx_create(int32_t device, kvs_ctx** out);
 void kvs_ctx_destroy(kvs_ctx* ctx);
 
-/* Death times of n rollouts: death_dev is int32 [n][n_pad] (rollout i at
+/* [KV-streams] "how it works": the engine's eviction pattern, replayed.
+ * Death times of n rollouts: death_dev is int32 [n][n_pad] (rollout i at
  * i * n_pad), status_dev int32 [n].  The logs are replayed on the device:
  * the rows held at an event are the tokens held after the previous event
  * followed by the tokens generated since, and the token of row i dies at the
@@ -379,7 +411,8 @@ void kvs_ctx_destroy(kvs_ctx* ctx);
 ll_status kvs_death_times(kvs_ctx* ctx, const kvs_rollout_log* logs, int32_t n, int64_t n_pad,
                           const uint8_t* keep_dev, int32_t* death_dev, int32_t* status_dev, void* stream);
 
-/* Block mask from death times: the n_pad x n_pad mask of each rollout cut
+/* [KV-streams] "how it works": the trainer's custom attention mask, as tiles.
+ * Block mask from death times: the n_pad x n_pad mask of each rollout cut
  * into block_q x block_k tiles (powers of two in [16, 1024]; edge tiles are
  * cut at n_pad).  A tile is full when every entry is visible, empty when none
  * is, partial otherwise.  With nq = ceil(n_pad / block_q) and
@@ -393,7 +426,8 @@ ll_status kvs_block_mask(kvs_ctx* ctx, const int32_t* death_dev, int32_t n, int6
                          int32_t block_q, int32_t block_k, int32_t* partial_num, int32_t* partial_idx,
                          int32_t* full_num, int32_t* full_idx, void* stream);
 
-/* Dense bit mask from death times: bits_dev is uint32 [n][n_pad][n_pad / 32]
+/* [KV-streams] "how it works": the trainer's custom attention mask, as bits.
+ * Dense bit mask from death times: bits_dev is uint32 [n][n_pad][n_pad / 32]
  * (16-byte aligned; n_pad a multiple of 128); bit b of word w of row q of
  * rollout i is 1 iff query q sees key 32 w + b, i.e. k <= q < d_k for any
  * int32 death times (values at or below k, or at or beyond n_pad, included).
@@ -406,10 +440,12 @@ ll_status kvs_block_mask(kvs_ctx* ctx, const int32_t* death_dev, int32_t n, int6
 ll_status kvs_dense_mask(kvs_ctx* ctx, const int32_t* death_dev, int32_t n, int64_t n_pad,
                          uint32_t* bits_dev, void* stream);
 
-/* Message for the calling thread's last failure ("" if none). */
+/* Library bookkeeping, no passage of the pages defines it: message for the
+ * calling thread's last failure ("" if none). */
 const char* ll_last_error(void);
 
-/* Name of a status code. */
+/* Library bookkeeping, no passage of the pages defines it: name of a status
+ * code. */
 const char* ll_status_str(ll_status status);
 
 #ifdef __cplusplus

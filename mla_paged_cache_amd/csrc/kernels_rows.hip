@@ -13,6 +13,8 @@
 //    thread holds both halves of its pairs in half-split layout.
 //  * rope_gather_mla_kernel: the gather of MLA rows at page size >= 8, page
 //    by page in the splice kernel's chunk order (copy waves and turn waves).
+//  * rope_inplace_mla_kernel: MLA rows turned in place, each wave owning 8
+//    rows over all layers and evaluating their cos/sin itself.
 #include "device_common.h"
 #include "rows_internal.h"
 
@@ -210,7 +212,100 @@ __global__ __launch_bounds__(256) void rope_gather_mla_kernel(RopeRowsLaunch a) 
   }
 }
 
+// MLA rows turned in place, the float64 cos/sin computed here (no table
+// kernel).  A wave owns 8 rows (lane = 8 * row + band chunk: each load
+// instruction reads the 128-byte k_pe line of 8 rows) over every layer, in
+// batches of kInPlaceLayerBatch layers whose loads are all issued before their
+// stores; the pairs' float64 cos and sin (the same device sincos as
+// rope_table_kernel, so the same float32 values) are evaluated while the
+// first batch is in flight.  Plain loads and stores: for these lines, 1152
+// bytes apart, that measured best.  STRIDE: the layers are one allocation,
+// layer l at plane0 + l * plane_stride (no per-layer pointer load before a
+// band load: 55 us against 58 us for the 32k x 27 rows).
+template <int PAIRING, bool STRIDE>
+__global__ __launch_bounds__(256) void rope_inplace_mla_kernel(RopeRowsLaunch a, const double* theta) {
+  constexpr int LB = kInPlaceLayerBatch;
+  constexpr int NP = PAIRING == 0 ? 4 : 8;  // pairs a lane turns
+  const int lane = threadIdx.x & 63;
+  const int kc = lane & 7;
+  const int64_t i = (static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6)) * 8 + (lane >> 3);
+  const bool live = i < a.n;
+  const int shift = a.page_shift;
+  const int L = a.num_planes;
+  // pair p0 + e, e < NP: interleaved chunk kc holds pairs 4 kc .. 4 kc + 3;
+  // half-split chunks kc and kc ^ 4 hold x and y of pairs 8 (kc & 3) ..
+  const int p0 = PAIRING == 0 ? 4 * kc : 8 * (kc & 3);
+  // The angle and theta loads go first, then the first batch's plane
+  // pointers and band loads (a lane past the rows reads row row_begin, in
+  // bounds): the sincos below then waits only for its own inputs, and no
+  // branch separates the band loads.
+  const double ang = static_cast<double>(a.angle[live ? i : 0]);
+  double th[NP];
+#pragma unroll
+  for (int e = 0; e < NP; ++e) th[e] = theta[p0 + e];
+  const int64_t j = a.row_begin + (live ? i : 0);
+  const int64_t phys = (static_cast<int64_t>(a.pages[(j >> shift) - a.first_page]) << shift) +
+                       (j & ((int64_t{1} << shift) - 1));
+  const int64_t off = phys * kRowChunks + kKpeChunk0 + kc;
+  // band chunk of layer l (a lane past the rows reads row row_begin's)
+  auto band = [&](int l) -> chunk_t* {
+    if constexpr (STRIDE)
+      return const_cast<chunk_t*>(a.plane0) + l * a.plane_stride + off;
+    else
+      return const_cast<chunk_t*>(a.planes[l]) + off;
+  };
+  chunk_t v[LB];
+#pragma unroll
+  for (int k = 0; k < LB; ++k) v[k] = *band(k < L ? k : L - 1);
+  float c[NP], sn[NP];
+#pragma unroll
+  for (int e = 0; e < NP; ++e) {
+    double sd, cd;
+    sincos(ang * th[e], &sd, &cd);
+    c[e] = static_cast<float>(cd);
+    sn[e] = static_cast<float>(sd);
+  }
+  for (int l0 = 0; l0 < L; l0 += LB) {
+#pragma unroll
+    for (int k = 0; k < LB; ++k) {
+      chunk_t r;
+      if constexpr (PAIRING == 0) {
+        r = rotate_interleaved(v[k], c, sn);
+      } else {
+        const chunk_t other = shfl_xor4(v[k]);
+        r = rotate_half(v[k], other, kc < 4, c, sn);
+      }
+      if (live && l0 + k < L) *band(l0 + k) = r;
+    }
+    if (l0 + LB < L) {
+#pragma unroll
+      for (int k = 0; k < LB; ++k) {
+        const int l = l0 + LB + k;
+        v[k] = *band(l < L ? l : L - 1);
+      }
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_rope_inplace_mla(const RopeRowsLaunch& a, const double* theta, int pairing, hipStream_t s,
+                                   const Stamp& t) {
+  const int64_t waves = (a.n + 7) / 8;
+  if (waves == 0 || a.num_planes == 0) return stamp_empty(s, t);
+  void (*k)(RopeRowsLaunch, const double*);
+  if (a.plane_stride != 0)
+    k = pairing == 0 ? rope_inplace_mla_kernel<0, true> : rope_inplace_mla_kernel<1, true>;
+  else
+    k = pairing == 0 ? rope_inplace_mla_kernel<0, false> : rope_inplace_mla_kernel<1, false>;
+  const dim3 g(static_cast<unsigned>((waves + 3) / 4)), b(256);
+  hipEvent_t start = t.start, stop = t.stop;
+  if (start || stop)
+    hipExtLaunchKernelGGL(k, g, b, 0, s, start, stop, 0, a, theta);
+  else
+    k<<<g, b, 0, s>>>(a, theta);
+  return hipGetLastError();
+}
 
 hipError_t launch_rope_table(const RopeTableLaunch& a, hipStream_t s, const Stamp& t) {
   const int64_t pairs = a.n * a.pairs;

@@ -34,22 +34,24 @@ enum TaskKind : int32_t {
 // thread needs one descriptor load before its data load.  Sources are
 // physical pages, so the kernel never reads the page table it rewrites.  Row
 // indices fit in 32 bits (the pool checks max_pages_per_seq * page_size).
+// The first 16 bytes are all a rotate-in-place task needs.
 struct alignas(16) SpliceTask {
   int32_t dst_page;    // physical page written (or rotated in place)
+  int32_t q;           // new logical page
+  int32_t n_new;       // rows of the sequence after the splice
+  int32_t dir;         // index into the SpliceDir array (cos/sin)
   int32_t pre_page;    // physical page of old logical page q (prefix rows), or -1
   int32_t down_page0;  // physical page of old logical page down_lp0
   int32_t down_page1;  // physical page of down_lp0 + 1, or -1
-  int32_t q;           // new logical page
   int32_t down_lp0;    // first old logical page feeding downstream rows
-  int32_t dir;         // index into the SpliceDir array (cos/sin)
   int32_t rotate;      // 1 when downstream k_pe turns (AMORTIZE, delta != 0)
   int32_t s_start;
   int32_t stub_end;    // s_start + r_len
   int32_t delta;
-  int32_t n_new;
   const chunk_t* stub;         // R rows of layer 0, in 16-byte chunks
   int64_t stub_layer_chunks;   // chunks between layers of R
 };
+static_assert(sizeof(SpliceTask) == 64, "a splice task is four 16-byte words");
 
 // The rotation table of a directive, read only by k_pe chunks.
 struct alignas(16) SpliceDir {
@@ -91,7 +93,7 @@ struct SpliceLaunch {
   int64_t n_move_tasks;
   int64_t n_rot_tasks;
   int64_t move_blocks_per_layer;
-  int64_t rot_blocks_per_layer;
+  int64_t rot_blocks_per_layer;   // kInPlaceRowsPerBlock rotate-task rows per block
   const SpliceDir* dirs;
   const TableWrite* twrites;   // run by the blocks after the row blocks
   const int32_t* tables;
@@ -264,6 +266,11 @@ hipError_t launch_splice_plan(const DirectPlanArgs& a, int32_t max_new_pages, hi
 
 // Chunks each thread of splice_kernel moves.
 constexpr int kSpliceChunksPerThread = 2;
+
+// splice_inplace_kernel: groups of 8 rows per wave (one 128-byte k_pe line
+// per row and lane group), and rows per 256-thread block.
+constexpr int kInPlaceGroups = 8;
+constexpr int kInPlaceRowsPerBlock = kFlatThreads / 64 * 8 * kInPlaceGroups;
 
 // Blocks of kFlatThreads that cover `chunks` chunks of one layer, each thread
 // taking `per_thread` of them.

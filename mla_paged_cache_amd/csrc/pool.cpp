@@ -180,6 +180,9 @@ struct ll_pool {
   int32_t heads = 0, head_chunks = 0, rot_shift = 0;  // GQA row shape
   std::vector<void*> layer_ptrs;  // the planes
   void** d_layers = nullptr;
+  // chunks from one plane to the next when every plane's base is the first
+  // one's plus a multiple of one fixed stride (one caller allocation), else 0
+  int64_t plane_stride_chunks = 0;
   std::vector<SeqState> seqs;
   FreePages free;
   // staging ring: one pinned + one device buffer; calls take consecutive
@@ -970,6 +973,14 @@ ll_status setup_pool(ll_pool* p, ll_pool** out) {
     return fail(LL_EDEVICE, "hipSetDevice(%d) failed", d.device);
   }
   p->num_planes = static_cast<int32_t>(p->layer_ptrs.size());
+  if (p->num_planes > 1) {
+    const intptr_t b0 = reinterpret_cast<intptr_t>(p->layer_ptrs[0]);
+    const intptr_t st = reinterpret_cast<intptr_t>(p->layer_ptrs[1]) - b0;
+    bool even = st > 0 && st % 16 == 0;
+    for (int32_t l = 2; even && l < p->num_planes; ++l)
+      even = reinterpret_cast<intptr_t>(p->layer_ptrs[l]) - b0 == st * l;
+    p->plane_stride_chunks = even ? st / 16 : 0;
+  }
   p->P = d.page_size;
   while ((1 << p->page_shift) < d.page_size) ++p->page_shift;
   p->seqs.resize(static_cast<size_t>(d.max_seqs));
@@ -1393,7 +1404,7 @@ ll_status leyline_splice(ll_pool* p, const ll_directive* dirs, int32_t n, void* 
       a.n_move_tasks = n_move_tasks;
       a.n_rot_tasks = n_rot_tasks;
       a.move_blocks_per_layer = ll::flat_blocks(n_move_tasks * P * ll::kRowChunks, ll::kSpliceChunksPerThread);
-      a.rot_blocks_per_layer = ll::flat_blocks(n_rot_tasks * P * (ll::kRowChunks - ll::kKpeChunk0), ll::kSpliceChunksPerThread);
+      a.rot_blocks_per_layer = (n_rot_tasks * P + ll::kInPlaceRowsPerBlock - 1) / ll::kInPlaceRowsPerBlock;
       a.dirs = reinterpret_cast<const ll::SpliceDir*>(dev_base + o_d);
       a.twrites = reinterpret_cast<const ll::TableWrite*>(dev_base + o_w);
       a.tables = reinterpret_cast<const int32_t*>(dev_base + o_p);
@@ -1903,7 +1914,10 @@ ll_status ll_rope_rows(ll_pool* p, int32_t seq, int64_t row_begin, int64_t n_row
   DeviceGuard g(p->desc.device);
   hipStream_t st = static_cast<hipStream_t>(stream);
   if ((rc = begin_call(p, st))) return rc;
-  const size_t tab_floats = static_cast<size_t>(n_rows) * 2 * sh.pairs;
+  // MLA rows turned in place: one kernel that evaluates its own cos/sin; the
+  // other cases read a per-row table made by rope_table_kernel
+  const bool inplace_mla = !out_dev && !p->gqa;
+  const size_t tab_floats = inplace_mla ? 0 : static_cast<size_t>(n_rows) * 2 * sh.pairs;
   if (tab_floats > p->rowtab_cap) {
     if ((rc = wait_idle(p))) return rc;
     if (p->d_rowtab) (void)hipFree(p->d_rowtab);
@@ -1934,6 +1948,8 @@ ll_status ll_rope_rows(ll_pool* p, int32_t seq, int64_t row_begin, int64_t n_row
   t.pairs = sh.pairs;
   ll::RopeRowsLaunch a{};
   a.planes = reinterpret_cast<const ll::chunk_t* const*>(p->d_layers);
+  a.plane0 = static_cast<const ll::chunk_t*>(p->layer_ptrs[0]);
+  a.plane_stride = p->plane_stride_chunks;
   a.num_planes = static_cast<int32_t>(L);  // MLA layers, or the K planes of a GQA pool
   a.page_shift = p->page_shift;
   a.shape = sh;
@@ -1946,13 +1962,20 @@ ll_status ll_rope_rows(ll_pool* p, int32_t seq, int64_t row_begin, int64_t n_row
   a.out_plane_chunks = (out_layer_stride_bytes ? out_layer_stride_bytes : n_rows * p->row_bytes) / 16;
   a.n_pages = n_pages;
   a.blocks_per_plane = ll::rope_rows_blocks_per_plane(a, per_row);
+  a.angle = angle_dev;
   ProfRec rec{};
   ll::Stamp ts;
   if (prof_pick(p, 2) && (rc = prof_begin(p, &rec, &ts))) return rc;
-  hipError_t e = ll::launch_rope_table(t, st, ll::Stamp{ts.start, nullptr});
-  if (e != hipSuccess) return device_fail(p, e, "rope_table_kernel launch");
-  e = ll::launch_rope_rows(a, p->desc.rope_pairing, st, ll::Stamp{nullptr, ts.stop});
-  if (e != hipSuccess) return device_fail(p, e, "rope_rows_kernel launch");
+  hipError_t e;
+  if (inplace_mla) {
+    e = ll::launch_rope_inplace_mla(a, t.theta, p->desc.rope_pairing, st, ts);
+    if (e != hipSuccess) return device_fail(p, e, "rope_inplace_mla_kernel launch");
+  } else {
+    e = ll::launch_rope_table(t, st, ll::Stamp{ts.start, nullptr});
+    if (e != hipSuccess) return device_fail(p, e, "rope_table_kernel launch");
+    e = ll::launch_rope_rows(a, p->desc.rope_pairing, st, ll::Stamp{nullptr, ts.stop});
+    if (e != hipSuccess) return device_fail(p, e, "rope_rows_kernel launch");
+  }
   ll_plan_stats stats{};
   stats.alg_bytes = out_dev ? L * n_rows * 2 * p->row_bytes : L * n_rows * 2 * p->band_bytes;
   stats.rows_rotated_inplace = out_dev ? 0 : n_rows;
@@ -1975,6 +1998,31 @@ ll_status ll_last_plan_stats(const ll_pool* p, ll_plan_stats* out) {
   return LL_OK;
 }
 
+ll_status ll_last_plan_bytes(const ll_pool* p, int64_t* alg_bytes, int64_t* rows_moved,
+                             int64_t* rows_rotated_inplace) {
+  ll_plan_stats s{};
+  if (ll_status rc = ll_last_plan_stats(p, &s)) return rc;
+  if (alg_bytes) *alg_bytes = s.alg_bytes;
+  if (rows_moved) *rows_moved = s.rows_moved;
+  if (rows_rotated_inplace) *rows_rotated_inplace = s.rows_rotated_inplace;
+  return LL_OK;
+}
+
+ll_status ll_seq_lengths(const ll_pool* p, const int32_t* seq_ids, int32_t n, int64_t* lengths_out) try {
+  if (!p) return fail(LL_EINVAL, "pool is NULL");
+  if (n < 0 || (n > 0 && (!seq_ids || !lengths_out))) return fail(LL_EINVAL, "bad arguments");
+  ll_status rc = settle(const_cast<ll_pool*>(p));
+  if (rc) return rc;
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t s = seq_ids[i];
+    if (s < 0 || s >= p->desc.max_seqs || !p->seqs[s].used) return fail(LL_EINVAL, "entry %d: unknown sequence %d", i, s);
+    lengths_out[i] = p->seqs[s].len;
+  }
+  return LL_OK;
+} catch (...) {
+  return host_exception(const_cast<ll_pool*>(p));
+}
+
 ll_status ll_pool_set_splice_planner(ll_pool* p, int32_t planner) {
   if (!p) return fail(LL_EINVAL, "pool is NULL");
   if (planner != LL_SPLICE_PLAN_AUTO && planner != LL_SPLICE_PLAN_HOST)
@@ -1990,8 +2038,9 @@ ll_status ll_pool_set_profiling(ll_pool* p, int32_t enable) {
   return LL_OK;
 }
 
-ll_status ll_profile_read(ll_pool* p, int32_t kernel, int64_t* launches, double* total_ms, int64_t* total_bytes) try {
-  if (!p || kernel < 0 || kernel > 2) return fail(LL_EINVAL, "bad argument");
+ll_status ll_profile_read(ll_pool* p, int32_t kernel, int64_t* launches, double* total_ms, int64_t* total_bytes,
+                          float* each_ms, int64_t each_cap) try {
+  if (!p || kernel < 0 || kernel > 2 || each_cap < 0 || (each_cap > 0 && !each_ms)) return fail(LL_EINVAL, "bad argument");
   if (ll_status rc = settle(p)) return rc;
   DeviceGuard g(p->desc.device);
   int64_t cnt = 0, bytes = 0;
@@ -2003,6 +2052,7 @@ ll_status ll_profile_read(ll_pool* p, int32_t kernel, int64_t* launches, double*
     if (e != hipSuccess) return fail(LL_EDEVICE, "profile events: %s", hipGetErrorString(e));
     ms += t;
     bytes += r.bytes;
+    if (cnt < each_cap) each_ms[cnt] = t;
     ++cnt;
     p->spare_events.push_back(r.start);
     p->spare_events.push_back(r.stop);

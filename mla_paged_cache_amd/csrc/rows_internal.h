@@ -29,6 +29,9 @@ struct RopeTableLaunch {
 
 struct RopeRowsLaunch {
   const chunk_t* const* planes;  // device array: the planes that carry bands come first
+  const int64_t* angle;          // [n] angle steps of each row (read by the in-place MLA kernel)
+  const chunk_t* plane0;         // plane 0 (host copy of planes[0])
+  int64_t plane_stride;          // chunks between consecutive planes when uniform, else 0
   int32_t num_planes;            // planes taking part (MLA: L; GQA: the L K planes)
   int32_t page_shift;
   RowShape shape;
@@ -43,7 +46,14 @@ struct RopeRowsLaunch {
   int64_t n_pages;               // logical pages the rows touch (first_page ..)
 };
 
+// Layers whose loads rope_inplace_mla_kernel issues before their stores.
+constexpr int kInPlaceLayerBatch = 9;
+
 hipError_t launch_rope_table(const RopeTableLaunch& a, hipStream_t s, const Stamp& t = Stamp{});
+// MLA rows in place (a.out == nullptr, MLA row shape): one kernel that also
+// evaluates the rows' float64 cos/sin from theta (device [32] float64).
+hipError_t launch_rope_inplace_mla(const RopeRowsLaunch& a, const double* theta, int pairing, hipStream_t s,
+                                   const Stamp& t = Stamp{});
 hipError_t launch_rope_rows(const RopeRowsLaunch& a, int pairing, hipStream_t s, const Stamp& t = Stamp{});
 // Blocks per plane of the launch launch_rope_rows picks for `a` (all fields
 // but blocks_per_plane set); per_row: threads per row of the row-unit kernel.

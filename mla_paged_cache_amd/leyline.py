@@ -31,7 +31,7 @@ EXPORTS = (
     "ll_rope_delta_table", "ll_last_plan_stats", "ll_pool_set_profiling", "ll_profile_read",
     "ll_last_error", "ll_status_str", "ll_pool_create_gqa",
     "kvs_ctx_create", "kvs_ctx_destroy", "kvs_death_times", "kvs_block_mask", "kvs_dense_mask",
-    "ll_rope_rows", "ll_pool_set_splice_planner",
+    "ll_rope_rows", "ll_pool_set_splice_planner", "ll_last_plan_bytes", "ll_seq_lengths",
 )
 
 
@@ -133,9 +133,11 @@ def _load():
         "ll_ptable_reindex": (i32, [vp, i32, P(i32), i32, vp]),
         "ll_rope_delta_table": (i32, [ctypes.c_double, i32, i64, P(ctypes.c_float), P(ctypes.c_float)]),
         "ll_last_plan_stats": (i32, [vp, P(_PlanStats)]),
+        "ll_last_plan_bytes": (i32, [vp, P(i64), P(i64), P(i64)]),
+        "ll_seq_lengths": (i32, [vp, P(i32), i32, P(i64)]),
         "ll_pool_set_profiling": (i32, [vp, i32]),
         "ll_pool_set_splice_planner": (i32, [vp, i32]),
-        "ll_profile_read": (i32, [vp, i32, P(i64), P(ctypes.c_double), P(i64)]),
+        "ll_profile_read": (i32, [vp, i32, P(i64), P(ctypes.c_double), P(i64), P(ctypes.c_float), i64]),
         "ll_rope_rows": (i32, [vp, i32, i64, i64, vp, vp, i64, vp]),
         "kvs_ctx_create": (i32, [i32, P(vp)]),
         "kvs_ctx_destroy": (None, [vp]),
@@ -167,6 +169,17 @@ def _check(status: int) -> None:
 def _i32_array(values):
     a = np.ascontiguousarray(np.asarray(values, dtype=np.int32))
     return a, a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def _require(t, name: str, dtype, shape, device) -> None:
+    """Raise ValueError unless `t` is a contiguous tensor of `dtype` and
+    exactly `shape` on `device` (checked before any kernel sees its pointer)."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
+    if t.dtype != dtype or t.device != device or not t.is_contiguous() or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: need a contiguous {dtype} tensor of shape {tuple(shape)} on {device}, got "
+                         f"{t.dtype} {tuple(t.shape)} on {t.device}{'' if t.is_contiguous() else ' (not contiguous)'}")
 
 
 def _stream_handle(stream, device: int) -> int:
@@ -302,8 +315,8 @@ class Pool:
     def _stub(self, st):
         """(r_len, pointer, layer stride in bytes) of one stub tensor."""
         import torch
-        if st.dtype != torch.bfloat16 or not st.is_cuda or st.shape[-1] != ROW:
-            raise ValueError("stub must be a bf16 CUDA tensor [..., r_len, 576]")
+        if st.dtype != torch.bfloat16 or st.device != self.device or st.shape[-1] != ROW:
+            raise ValueError(f"stub must be a bf16 tensor [..., r_len, 576] on {self.device}")
         if st.dim() == 2:
             st = st.unsqueeze(0)
         if st.shape[0] != self.num_layers or st.stride(2) != 1 or st.stride(1) != ROW:
@@ -334,10 +347,22 @@ class Pool:
         """keep: uint8 CUDA tensor holding every mask; offsets[i]: start of
         sequence seqs[i]'s mask in it (its length is the sequence length)."""
         import torch
-        if keep.dtype != torch.uint8 or not keep.is_cuda or not keep.is_contiguous():
-            raise ValueError("keep must be a contiguous uint8 CUDA tensor")
+        if not isinstance(keep, torch.Tensor) or keep.dtype != torch.uint8 or keep.device != self.device \
+                or not keep.is_contiguous():
+            raise ValueError(f"keep must be a contiguous uint8 tensor on {self.device}")
         s_arr, s_ptr = _i32_array(seqs)
-        o_arr = np.ascontiguousarray(np.asarray(offsets, dtype=np.int64))
+        o_arr = np.ascontiguousarray(np.asarray(offsets, dtype=np.int64).reshape(-1))
+        if len(o_arr) != len(s_arr):
+            raise ValueError(f"{len(s_arr)} sequences but {len(o_arr)} mask offsets")
+        if len(s_arr):
+            lens = np.zeros(len(s_arr), np.int64)
+            _check(_lib.ll_seq_lengths(self._h, s_ptr, len(s_arr), lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))))
+            # a negative offset is the library's to refuse (LL_EINVAL)
+            past = (o_arr >= 0) & (o_arr + lens > keep.numel())
+            if past.any():
+                i = int(np.argmax(past))
+                raise ValueError(f"mask of sequence {int(s_arr[i])}: bytes [{int(o_arr[i])}, {int(o_arr[i] + lens[i])}) "
+                                 f"outside keep's {keep.numel()}")
         _check(_lib.kv_evict_compact(self._h, s_ptr, len(s_arr), keep.data_ptr(),
                                      o_arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
                                      _stream_handle(stream, self._dev)))
@@ -349,16 +374,18 @@ class Pool:
         rows are gathered into [L][n][row] bf16 and returned, the pool left
         as it was."""
         import torch
-        if angles.dtype != torch.int64 or not angles.is_cuda or not angles.is_contiguous():
-            raise ValueError("angles must be a contiguous int64 CUDA tensor")
+        if not isinstance(angles, torch.Tensor) or angles.dtype != torch.int64 or angles.device != self.device \
+                or angles.dim() != 1 or not angles.is_contiguous():
+            raise ValueError(f"angles must be a contiguous 1-D int64 tensor on {self.device}")
         n = angles.numel()
         ptr, stride = None, 0
         if out is not None:
+            shape = (self.num_layers, n, self.heads, self.head_dim) if self.gqa else (self.num_layers, n, ROW)
             if out is True:
-                shape = (self.num_layers, n, self.heads, self.head_dim) if self.gqa else (self.num_layers, n, ROW)
-                out = torch.empty(shape, dtype=torch.bfloat16, device=angles.device)
-            if out.dtype != torch.bfloat16 or not out.is_cuda or out.shape[0] != self.num_layers:
-                raise ValueError("out must be a bf16 CUDA tensor [num_layers][n][row]")
+                out = torch.empty(shape, dtype=torch.bfloat16, device=self.device)
+            if not isinstance(out, torch.Tensor) or out.dtype != torch.bfloat16 or out.device != self.device \
+                    or tuple(out.shape) != shape or not out[0].is_contiguous() or out.stride(0) < out[0].numel():
+                raise ValueError(f"out must be a bf16 tensor {shape} on {self.device} with contiguous layers")
             ptr, stride = out.data_ptr(), out.stride(0) * 2
         _check(_lib.ll_rope_rows(self._h, int(seq), int(row_begin), int(n), angles.data_ptr() if n else None,
                                  ptr, stride, _stream_handle(stream, self._dev)))
@@ -385,11 +412,17 @@ class Pool:
         """Time every `every`-th launch of each profiled kernel while enabled."""
         _check(_lib.ll_pool_set_profiling(self._h, max(1, int(every)) if enable else 0))
 
-    def profile_read(self, kernel: int = 0):
+    def profile_read(self, kernel: int = 0, samples: int = 0):
         """(launches, total_ms, total_bytes) of kernel 0 (row moves), 1 (keep
-        scan) or 2 (per-row rotation)."""
+        scan) or 2 (per-row rotation); with samples = k > 0 a fourth item, the
+        milliseconds of the first k timed launches."""
         n, ms, b = ctypes.c_int64(), ctypes.c_double(), ctypes.c_int64()
-        _check(_lib.ll_profile_read(self._h, kernel, ctypes.byref(n), ctypes.byref(ms), ctypes.byref(b)))
+        each = np.zeros(max(0, int(samples)), np.float32)
+        _check(_lib.ll_profile_read(self._h, kernel, ctypes.byref(n), ctypes.byref(ms), ctypes.byref(b),
+                                    each.ctypes.data_as(ctypes.POINTER(ctypes.c_float)) if samples else None,
+                                    len(each)))
+        if samples:
+            return n.value, ms.value, b.value, each[:min(n.value, len(each))].astype(float).tolist()
         return n.value, ms.value, b.value
 
 
@@ -444,8 +477,8 @@ class GqaPool(Pool):
 
     def _stub(self, st):
         import torch
-        if st.dtype != torch.bfloat16 or not st.is_cuda or tuple(st.shape[-2:]) != (self.heads, self.head_dim):
-            raise ValueError("stub rows must be bf16 CUDA tensors [..., r_len, H, D]")
+        if st.dtype != torch.bfloat16 or st.device != self.device or tuple(st.shape[-2:]) != (self.heads, self.head_dim):
+            raise ValueError(f"stub rows must be bf16 tensors [..., r_len, H, D] on {self.device}")
         if st.dim() == 3:
             st = st.unsqueeze(0)
         if st.shape[0] != self.num_layers or st.stride(3) != 1 or st.stride(2) != self.head_dim \
@@ -471,10 +504,12 @@ class KvsMask:
     engine passed to its eviction call (uint8 over the rows held then)."""
 
     def __init__(self, device: int = 0):
+        import torch
         h = ctypes.c_void_p()
         _check(_lib.kvs_ctx_create(int(device), ctypes.byref(h)))
         self._h = h
         self.device = device
+        self._tdev = torch.device("cuda", device)
 
     def close(self):
         if getattr(self, "_h", None):
@@ -486,6 +521,12 @@ class KvsMask:
             self.close()
         except Exception:
             pass
+
+    def _check_death(self, death):
+        import torch
+        if not isinstance(death, torch.Tensor) or death.dim() != 2:
+            raise ValueError("death must be a 2-D int32 tensor [n][n_pad]")
+        _require(death, "death", torch.int32, tuple(death.shape), self._tdev)
 
     def upload_logs(self, rollouts):
         """Marshal eviction logs once: rollouts is a list of (n_tokens,
@@ -515,11 +556,13 @@ class KvsMask:
         tensors."""
         import torch
         logs = rollouts if isinstance(rollouts, _Logs) else self.upload_logs(rollouts)
-        dev = torch.device("cuda", self.device)
+        dev = self._tdev
         if out is None:
             out = (torch.empty((logs.n, n_pad), dtype=torch.int32, device=dev),
                    torch.empty(logs.n, dtype=torch.int32, device=dev))
         death, status = out
+        _require(death, "death", torch.int32, (logs.n, n_pad), dev)
+        _require(status, "status", torch.int32, (logs.n,), dev)
         _check(_lib.kvs_death_times(self._h, logs.logs, logs.n, int(n_pad), logs.keep.data_ptr(), death.data_ptr(),
                                     status.data_ptr(), _stream_handle(stream, self.device)))
         self._last_logs = logs  # the kernel reads the keep buffer after this returns
@@ -531,6 +574,7 @@ class KvsMask:
         count; with `out` (four int32 tensors of those shapes) the entries past
         each count are left as they were."""
         import torch
+        self._check_death(death)
         n, n_pad = death.shape
         nq, nk = -(-n_pad // block_q), -(-n_pad // block_k)
         kw = dict(dtype=torch.int32, device=death.device)
@@ -549,8 +593,10 @@ class KvsMask:
     def dense_mask(self, death, out=None, stream=None):
         """uint32 bits [n][n_pad][n_pad / 32] (as an int32 tensor)."""
         import torch
+        self._check_death(death)
         n, n_pad = death.shape
         if out is None:
             out = torch.empty((n, n_pad, n_pad // 32), dtype=torch.int32, device=death.device)
+        _require(out, "out", torch.int32, (n, n_pad, n_pad // 32), self._tdev)
         _check(_lib.kvs_dense_mask(self._h, death.data_ptr(), n, n_pad, out.data_ptr(), _stream_handle(stream, self.device)))
         return out

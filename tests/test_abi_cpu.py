@@ -32,9 +32,34 @@ def lib():
 
 def test_header_declares_the_path_entry_points():
     names = _declared()
-    for n in ("leyline_splice", "kv_evict_compact", "ll_ptable_reindex", "ll_pool_create"):
+    for n in ("leyline_splice", "kv_evict_compact", "ll_ptable_reindex", "ll_pool_create", "ll_last_plan_bytes",
+              "ll_rope_delta_table", "ll_last_error"):
         assert n in names
-    assert len(names) == 24
+    assert len(names) == 26
+
+
+CITATION = re.compile(r"\[Leyline\] section|\[KV-streams\] \"|VECTOR|no passage of the pages")
+
+
+def test_every_declaration_cites_its_passage_or_says_it_has_none():
+    """Each function declaration is preceded (after the previous declaration
+    ends) by a comment that names the page section defining the operation, or
+    says that it is library bookkeeping with no passage behind it.  Two
+    declarations with nothing between them share the comment before the
+    first."""
+    text = open(HEADER).read()
+    decl = re.compile(r"^(?:ll_status|void|const char\*)\s+\*?\s*([a-z_][a-z0-9_]*)\s*\(", re.M)
+    prev_end, last_comment = 0, None
+    checked = 0
+    for m in decl.finditer(text):
+        between = text[prev_end:m.start()]
+        comments = re.findall(r"/\*.*?\*/", between, flags=re.S)
+        if comments:
+            last_comment = " ".join(comments)
+        assert last_comment and CITATION.search(last_comment), m.group(1)
+        prev_end = text.index(";", m.end()) + 1
+        checked += 1
+    assert checked == len(_declared())
 
 
 def test_splice_planner_setter_checks_its_arguments():

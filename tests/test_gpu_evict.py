@@ -121,6 +121,10 @@ def test_evict_rejects_bad_requests():
         with pytest.raises(L.LeylineError) as ei:
             dp.pool.evict(seqs, keep, offs)
         assert ei.value.status == L.LL_EINVAL
+    # masks that would run past the keep buffer never reach the library
+    for k, offs in ((keep[:69], [0]), (keep, [1])):
+        with pytest.raises(ValueError):
+            dp.pool.evict([0], k, offs)
     assert dp.pool.seq_get(0)[0] == 70
     dp.close()
 

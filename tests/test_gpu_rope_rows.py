@@ -144,6 +144,70 @@ def test_mla_32k_27_layers_back_to_position_free_keys():
         assert rel < 4e-3
     st = dp.pool.last_stats()
     assert st.alg_bytes == layers * n_tok * 2 * 1152
+    # the same turn in place: every layer's bands change (the one-kernel
+    # in-place path, three batches of nine layers), layers 0 and 26 compared
+    dp.pool.rope_rows(0, 0, torch.from_numpy(a).cuda())
+    torch.cuda.synchronize()
+    assert dp.pool.last_stats().alg_bytes == layers * n_tok * 2 * 128
+    new = O.rope_rows(dp.state, 0, 0, a, in_place=True)
+    for li, l in enumerate((0, 26)):
+        got = dp.data[l].view(torch.int16).cpu().numpy().view(np.uint16).reshape(-1, O.ROW)
+        flips += _cmp_rows(got, new.layers[li].reshape(-1, O.ROW), [(512, 64)], O.ROW)
+    say(f"  band values 1 ulp apart: {flips}")
+    dp.close()
+
+
+@pytest.mark.parametrize("pairing", [0, 1])
+def test_mla_in_place_layers_in_separate_allocations(pairing):
+    """Layers that are not one allocation (no common stride): the in-place
+    kernel reads each layer's base from the pool's pointer array."""
+    L = need_gpu()
+    say(f"rope rows MLA in place, separate layer tensors, pairing={pairing}")
+    P, n_tok, layers = 16, 777, 10
+    pages = -(-n_tok // P)
+    host = random_rows_np(21, (layers, 2 * pages, P, O.ROW))
+    tensors = []
+    for l in (3, 0, 7, 1, 9, 2, 8, 4, 6, 5):   # allocated out of order: no single stride
+        tensors.append((l, torch.from_numpy(host[l].view(np.int16)).view(torch.bfloat16).cuda()))
+    data = [t for _, t in sorted(tensors, key=lambda x: x[0])]
+    table = torch.full((1, 2 * pages), -1, dtype=torch.int32, device="cuda")
+    pool = L.Pool(data, table, pairing=pairing)
+    T = permuted_pages(21, 2 * pages)[:pages]
+    pool.seq_set_pages(0, T, n_tok)
+    st = O.CacheState.empty(layers, 2 * pages, P, 2 * pages, with_rows=False)
+    st.layers = [host[l].copy() for l in range(layers)]
+    st.set_pages(0, T, n_tok)
+    a = _angles(17, 500, big=True)
+    pool.rope_rows(0, 111, torch.from_numpy(a).cuda())
+    torch.cuda.synchronize()
+    new = O.rope_rows(st, 0, 111, a, pairing="half" if pairing else "interleaved", in_place=True)
+    flips = 0
+    for l in range(layers):
+        flat = data[l].view(torch.int16).cpu().numpy().view(np.uint16).reshape(-1, O.ROW)
+        flips += _cmp_rows(flat, new.layers[l].reshape(-1, O.ROW), [(512, 64)], O.ROW)
+    say(f"  band values 1 ulp apart: {flips}")
+    pool.close()
+
+
+@pytest.mark.parametrize("P,pairing", [(4, 0), (4, 1), (16, 1)])
+def test_mla_in_place_eleven_layers(P, pairing):
+    """In place over 11 layers (one batch of nine layers and a partial one),
+    rows starting off an 8-row boundary and ending in a partial group."""
+    need_gpu()
+    say(f"rope rows MLA in place, 11 layers, P={P} pairing={pairing}")
+    n_tok = 1000
+    pages = -(-n_tok // P)
+    dp = DevicePool(11, 2 * pages, P, 1, 2 * pages, seed=9, pairing=pairing)
+    dp.set_pages(0, permuted_pages(9, 2 * pages)[:pages], n_tok)
+    dp.snapshot_rows()
+    a = _angles(13, 741, big=True)
+    dp.pool.rope_rows(0, 203, torch.from_numpy(a).cuda())
+    torch.cuda.synchronize()
+    new = O.rope_rows(dp.state, 0, 203, a, pairing="half" if pairing else "interleaved", in_place=True)
+    flips = 0
+    for li in range(11):
+        flat = dp.data[li].view(torch.int16).cpu().numpy().view(np.uint16).reshape(-1, O.ROW)
+        flips += _cmp_rows(flat, new.layers[li].reshape(-1, O.ROW), [(512, 64)], O.ROW)
     say(f"  band values 1 ulp apart: {flips}")
     dp.close()
 

@@ -103,6 +103,25 @@ def test_splice_32k_27_layers_full_compare():
     dp.close()
 
 
+def test_splice_32k_27_layers_inplace_full_compare():
+    """The same sequence spliced with no stub rows: Delta = -6144, a whole
+    number of 16-row pages, so every downstream page is reused and only its
+    k_pe band turns in place (the in-place kernel alone, with the page-table
+    rewrite); every row of every layer compared."""
+    say("splice_32k_27layer_inplace full compare")
+    dp = _pool(27, 4096, 16, 1, 2048, seed=0, host_rows=False)
+    dp.set_pages(0, permuted_pages(0, 2048), 32768)
+    dp.snapshot_rows()
+    expected, _ = _splice_both(dp, [(0, 8192, 14336, 0, 1, O.AMORTIZE)])
+    worst = compare_seq(dp, expected, 0)
+    assert_same_free(dp, expected)
+    st = dp.pool.last_stats()
+    assert st.fresh_pages == 0 and st.rows_moved == 0 and st.rows_rotated_inplace == 32768 - 14336
+    assert st.alg_bytes == 27 * (32768 - 14336) * 2 * 128
+    say(f"  max k_pe ulp = {worst}")
+    dp.close()
+
+
 def _batched(L, n_tokens, n_seqs, seed, oracle_layers=None, host_rows=True):
     rng = np_rng(seed, 4)
     pages_per = n_tokens // 16
