@@ -255,6 +255,24 @@ ll_status ll_pool_free_pages(const ll_pool* pool, int64_t* n_free);
  * pages), LL_EDEVICE. */
 ll_status leyline_splice(ll_pool* pool, const ll_directive* dirs, int32_t n, void* stream);
 
+/* For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The same
+ * splice as leyline_splice (same arguments, results and errors), with the
+ * page plan expanded on the device into a library-owned static device array
+ * of 4 MiB per device instead of the pool's growable plan space: the call
+ * allocates no device or pinned memory, creates no event and times no
+ * launch (ll_pool_set_profiling does not apply to it).  Only batches the
+ * device plans itself qualify -- at most 16 directives (GQA / MHA pools:
+ * 1024 / rotary_dim), fresh pages in at most 256 runs of consecutive ids,
+ * and a plan of at most 4 MiB (about 60 000 page tasks, 64 bytes each, plus
+ * the new page-table rows) -- whatever ll_pool_set_splice_planner says;
+ * other batches return LL_EUNSUPPORTED with nothing changed.  Every call on
+ * a device uses that device's one array and leaves its contents there for
+ * the next call to overwrite: calls on one pool are ordered by the pool, but
+ * calls on different pools of the same device that can overlap in time (on
+ * streams with no ordering between them) race on the array. */
+ll_status leyline_splice_noalloc(ll_pool* pool, const ll_directive* dirs, int32_t n, void* stream);
+
 /* KV-streams eviction ([KV-streams] "how it works"): for each of the n
  * sequences seq_ids[i], keep exactly the rows whose keep byte is nonzero, in
  * order, unchanged (no rotation, no position reset: the next position stays).

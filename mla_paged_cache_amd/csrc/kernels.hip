@@ -20,6 +20,8 @@
 // one 64-byte descriptor load before the data load, non-temporal loads and
 // stores (the in-place band rotation: plain stores).  Only k_pe chunks (8 of
 // every 72) do arithmetic.
+#include <mutex>
+
 #include "device_common.h"
 
 namespace ll {
@@ -483,6 +485,36 @@ hipError_t launch_table_write(const TableLaunch& a, hipStream_t s) {
   if (a.n_twrites == 0) return hipSuccess;
   table_write_kernel<<<dim3(a.n_twrites), dim3(256), 0, s>>>(a);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- scratch --
+// Plan space of the splice that allocates nothing (leyline_splice_noalloc).
+// In host code `scratch` names a host-side stand-in, not device memory: its
+// device address comes from hipGetSymbolAddress, per device, and only that
+// address is ever handed to kernels or copies.
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t noalloc_scratch_init(int device) {
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[device]) return hipSuccess;
+  void* ptr = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return e;
+  g_scratch_ptr[device] = ptr;
+  return hipSuccess;
+}
+
+void* noalloc_scratch(int device) {
+  if (device < 0 || device >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  return g_scratch_ptr[device];
 }
 
 hipError_t launch_splice_plan(const DirectPlanArgs& a, int32_t max_new_pages, hipStream_t s) {

@@ -264,6 +264,15 @@ hipError_t launch_gqa_splice(const GqaSpliceLaunch& a, int pairing, hipStream_t 
 hipError_t launch_plane_evict(const PlaneEvictLaunch& a, hipStream_t s, const Stamp& t = Stamp{});
 hipError_t launch_splice_plan(const DirectPlanArgs& a, int32_t max_new_pages, hipStream_t s);
 
+// The plan space of leyline_splice_noalloc: a file-scope device array in
+// kernels.hip (every device the library runs on holds one copy until the
+// process ends).  noalloc_scratch_init looks up its address on `device` (the
+// current device) once and keeps it; noalloc_scratch returns that address, or
+// nullptr when the lookup has not succeeded on `device`.
+constexpr size_t kNoAllocScratchBytes = size_t{4} << 20;
+hipError_t noalloc_scratch_init(int device);
+void* noalloc_scratch(int device);
+
 // Chunks each thread of splice_kernel moves.
 constexpr int kSpliceChunksPerThread = 2;
 

@@ -987,7 +987,13 @@ ll_status setup_pool(ll_pool* p, ll_pool** out) {
   p->free.init(d.num_pages);
   p->page_slot.assign(static_cast<size_t>(d.num_pages), -1);
   p->theta = rope_thetas(d.rope_base, d.rope_dim);
-  hipError_t e = hipMalloc(reinterpret_cast<void**>(&p->d_layers), sizeof(void*) * p->num_planes);
+  // once per device, with it current: the address of the no-allocation scratch
+  hipError_t e = ll::noalloc_scratch_init(d.device);
+  if (e != hipSuccess) {
+    delete p;
+    return fail(LL_EDEVICE, "hipGetSymbolAddress(no-allocation scratch): %s", hipGetErrorString(e));
+  }
+  e = hipMalloc(reinterpret_cast<void**>(&p->d_layers), sizeof(void*) * p->num_planes);
   if (e == hipSuccess)
     e = hipMemcpy(p->d_layers, p->layer_ptrs.data(), sizeof(void*) * p->num_planes, hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&p->readback_ev, hipEventDisableTiming);
@@ -1246,7 +1252,12 @@ ll_status ll_seq_free(ll_pool* p, int32_t seq) try {
   return host_exception(p);
 }
 
-ll_status leyline_splice(ll_pool* p, const ll_directive* dirs, int32_t n, void* stream) try {
+// The splice.  noalloc: the plan always goes to the device as kernel
+// arguments and its expansion lands in the library's static device scratch
+// (no device or pinned memory is allocated, no event is created, no launch
+// is timed); a batch that the device cannot plan, or whose plan exceeds the
+// scratch, is refused before anything changes.
+static ll_status splice_impl(ll_pool* p, const ll_directive* dirs, int32_t n, void* stream, bool noalloc) {
   ll_status rc = enter(p);
   if (rc) return rc;
   if (n < 0 || (n > 0 && !dirs)) return fail(LL_EINVAL, "bad directive array");
@@ -1283,7 +1294,7 @@ ll_status leyline_splice(ll_pool* p, const ll_directive* dirs, int32_t n, void* 
   // staging and no upload) when the batch is small, its fresh pages form few
   // runs of consecutive ids, and every directive's fresh pages and
   // rotate-in-place pages each form one range of q.
-  bool direct = p->splice_planner == LL_SPLICE_PLAN_AUTO && n <= ll::kDirectMaxDirs &&
+  bool direct = (noalloc || p->splice_planner == LL_SPLICE_PLAN_AUTO) && n <= ll::kDirectMaxDirs &&
                 n * 2 * pairs <= ll::kDirectTrigFloats;
   std::vector<int32_t> run_page, run_first;
   std::vector<int32_t> q_fresh0(static_cast<size_t>(n), 0), q_rot0(static_cast<size_t>(n), 0);
@@ -1321,7 +1332,19 @@ ll_status leyline_splice(ll_pool* p, const ll_directive* dirs, int32_t n, void* 
   size_t o_w = align_up(o_d + n * dir_bytes, 256);
   size_t o_p = align_up(o_w + n * sizeof(ll::TableWrite), 256);
   const size_t direct_bytes = o_p + static_cast<size_t>(n_entries) * 4;
-  if (direct && direct_bytes > p->direct_cap) {
+  char* scratch = nullptr;
+  if (noalloc) {
+    if (!direct)
+      return fail(LL_EUNSUPPORTED,
+                  "leyline_splice_noalloc plans on the device only: at most %d directives (%d on this pool) whose "
+                  "fresh pages form at most %d runs of consecutive ids",
+                  ll::kDirectMaxDirs, ll::kDirectTrigFloats / (2 * pairs), ll::kDirectMaxRuns);
+    if (direct_bytes > ll::kNoAllocScratchBytes)
+      return fail(LL_EUNSUPPORTED, "leyline_splice_noalloc: the plan needs %zu bytes, the scratch holds %zu",
+                  direct_bytes, ll::kNoAllocScratchBytes);
+    scratch = static_cast<char*>(ll::noalloc_scratch(p->desc.device));
+    if (!scratch) return fail(LL_EDEVICE, "the no-allocation scratch of device %d was not found", p->desc.device);
+  } else if (direct && direct_bytes > p->direct_cap) {
     // grows rarely (a larger batch than any before); waits for earlier work
     if ((rc = wait_idle(p))) return rc;
     if (p->d_direct) (void)hipFree(p->d_direct);
@@ -1340,7 +1363,7 @@ ll_status leyline_splice(ll_pool* p, const ll_directive* dirs, int32_t n, void* 
   hipStream_t st = static_cast<hipStream_t>(stream);
   if ((rc = begin_call(p, st))) return rc;
   Staging* sg = nullptr;
-  char* dev_base = p->d_direct;
+  char* dev_base = noalloc ? scratch : p->d_direct;
   ll::DirectPlanArgs da{};
   ll::SpliceDir* ddirs = nullptr;
   ll::GqaDir* gdirs = nullptr;
@@ -1392,7 +1415,7 @@ ll_status leyline_splice(ll_pool* p, const ll_directive* dirs, int32_t n, void* 
       a.n_twrites = n;
       a.max_pages_per_seq = p->desc.max_pages_per_seq;
       a.page_table = p->desc.page_table;
-      if (prof_pick(p, 0) && (rc = prof_begin(p, &rec, &ts))) return rc;
+      if (!noalloc && prof_pick(p, 0) && (rc = prof_begin(p, &rec, &ts))) return rc;
       e = ll::launch_gqa_splice(a, p->desc.rope_pairing, st, ts);
       if (e != hipSuccess) return device_fail(p, e, "gqa_splice_kernel launch");
     } else {
@@ -1411,7 +1434,7 @@ ll_status leyline_splice(ll_pool* p, const ll_directive* dirs, int32_t n, void* 
       a.n_twrites = n;
       a.max_pages_per_seq = p->desc.max_pages_per_seq;
       a.page_table = p->desc.page_table;
-      if (prof_pick(p, 0) && (rc = prof_begin(p, &rec, &ts))) return rc;
+      if (!noalloc && prof_pick(p, 0) && (rc = prof_begin(p, &rec, &ts))) return rc;
       e = ll::launch_splice(a, p->desc.rope_pairing, st, ts);
       if (e != hipSuccess) return device_fail(p, e, "splice_kernel launch");
     }
@@ -1590,6 +1613,16 @@ ll_status leyline_splice(ll_pool* p, const ll_directive* dirs, int32_t n, void* 
   }
   p->last = stats;
   return LL_OK;
+}
+
+ll_status leyline_splice(ll_pool* p, const ll_directive* dirs, int32_t n, void* stream) try {
+  return splice_impl(p, dirs, n, stream, false);
+} catch (...) {
+  return host_exception(p);
+}
+
+ll_status leyline_splice_noalloc(ll_pool* p, const ll_directive* dirs, int32_t n, void* stream) try {
+  return splice_impl(p, dirs, n, stream, true);
 } catch (...) {
   return host_exception(p);
 }

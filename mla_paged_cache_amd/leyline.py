@@ -32,6 +32,7 @@ EXPORTS = (
     "ll_last_error", "ll_status_str", "ll_pool_create_gqa",
     "kvs_ctx_create", "kvs_ctx_destroy", "kvs_death_times", "kvs_block_mask", "kvs_dense_mask",
     "ll_rope_rows", "ll_pool_set_splice_planner", "ll_last_plan_bytes", "ll_seq_lengths",
+    "leyline_splice_noalloc",
 )
 
 
@@ -129,6 +130,7 @@ def _load():
         "ll_seq_get": (i32, [vp, i32, P(i64), P(i64), P(i32), i32, P(i32)]),
         "ll_pool_free_pages": (i32, [vp, P(i64)]),
         "leyline_splice": (i32, [vp, P(_Directive), i32, vp]),
+        "leyline_splice_noalloc": (i32, [vp, P(_Directive), i32, vp]),
         "kv_evict_compact": (i32, [vp, P(i32), i32, vp, P(i64), vp]),
         "ll_ptable_reindex": (i32, [vp, i32, P(i32), i32, vp]),
         "ll_rope_delta_table": (i32, [ctypes.c_double, i32, i64, P(ctypes.c_float), P(ctypes.c_float)]),
@@ -324,7 +326,9 @@ class Pool:
         r_len = st.shape[1]
         return r_len, (st.data_ptr() if r_len else None), st.stride(0) * 2
 
-    def splice(self, directives, stream=None) -> None:
+    def splice(self, directives, stream=None, noalloc: bool = False) -> None:
+        """Apply the directives (leyline_splice; noalloc=True:
+        leyline_splice_noalloc, which allocates no device memory)."""
         n = len(directives)
         arr = (_Directive * max(1, n))()
         for i, d in enumerate(directives):
@@ -341,7 +345,8 @@ class Pool:
                 raise ValueError("stub_v without stub")
             arr[i] = _Directive(int(d.seq), int(d.mode), int(d.s_start), int(d.s_end), int(r_len), ptr, stride,
                                 ptr_v, stride_v)
-        _check(_lib.leyline_splice(self._h, arr, n, _stream_handle(stream, self._dev)))
+        fn = _lib.leyline_splice_noalloc if noalloc else _lib.leyline_splice
+        _check(fn(self._h, arr, n, _stream_handle(stream, self._dev)))
 
     def evict(self, seqs, keep, offsets, stream=None) -> None:
         """keep: uint8 CUDA tensor holding every mask; offsets[i]: start of

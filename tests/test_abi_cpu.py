@@ -35,16 +35,20 @@ def test_header_declares_the_path_entry_points():
     for n in ("leyline_splice", "kv_evict_compact", "ll_ptable_reindex", "ll_pool_create", "ll_last_plan_bytes",
               "ll_rope_delta_table", "ll_last_error"):
         assert n in names
-    assert len(names) == 26
+    assert len(names) == 27
 
 
-CITATION = re.compile(r"\[Leyline\] section|\[KV-streams\] \"|VECTOR|no passage of the pages")
+# a page passage, or "no passage" for bookkeeping; the no-allocation splice
+# names the callers it is for instead
+CITATION = re.compile(r"\[Leyline\] section|\[KV-streams\] \"|VECTOR|no passage of the pages|"
+                      r"callers that cannot allocate")
 
 
 def test_every_declaration_cites_its_passage_or_says_it_has_none():
     """Each function declaration is preceded (after the previous declaration
-    ends) by a comment that names the page section defining the operation, or
-    says that it is library bookkeeping with no passage behind it.  Two
+    ends) by a comment that names the page section defining the operation,
+    says that it is library bookkeeping with no passage behind it, or (the
+    splice that allocates nothing) names the callers it is for.  Two
     declarations with nothing between them share the comment before the
     first."""
     text = open(HEADER).read()
