@@ -97,7 +97,7 @@ def parse():
 # The source file of each measured kernel; its hash also covers the shared
 # device helpers and the launch structures.
 KERNEL_SOURCE = {"splice_kernel": "kernels.hip", "splice_inplace_kernel": "kernels.hip",
-                 "evict_move_kernel": "kernels.hip", "dev_move_kernel": "kernels_alloc.hip",
+                 "evict_move_kernel": "kernels.hip",
                  "gqa_splice_kernel": "kernels_gqa.hip", "plane_evict_kernel": "kernels_gqa.hip",
                  "kvs_dense_ev_kernel": "kernels_kvs.hip", "rope_rows_kernel": "kernels_rows.hip",
                  "rope_gather_mla_kernel": "kernels_rows.hip", "rope_inplace_mla_kernel": "kernels_rows.hip"}
@@ -107,8 +107,7 @@ def kernel_source_sha(kernel: str) -> str:
     csrc = os.path.join(ROOT, "mla_paged_cache_amd", "csrc")
     src = KERNEL_SOURCE[kernel]
     headers = {"kernels_kvs.hip": ("kvs_internal.h",),
-               "kernels_rows.hip": ("device_common.h", "leyline_internal.h", "rows_internal.h"),
-               "kernels_alloc.hip": ("device_common.h", "leyline_internal.h", "alloc_internal.h")}.get(
+               "kernels_rows.hip": ("device_common.h", "leyline_internal.h", "rows_internal.h")}.get(
         src, ("device_common.h", "leyline_internal.h"))
     h = hashlib.sha256()
     for name in (*headers, src):
@@ -136,12 +135,6 @@ def quiet_gc():
     inside the timed host loop and starve the GPU."""
     gc.collect()
     gc.disable()
-
-
-def prof_every(steps: int) -> int:
-    """Time about a dozen launches, spread evenly over a measured region: each
-    timed launch costs the stream a few microseconds of event stamps."""
-    return max(1, steps // 12)
 
 
 def kernel_pass(torch, pool, kernel, run, n, prepare=None):
@@ -617,8 +610,6 @@ def bench_splice_4k(args):
         restore()
         pool.splice(directive)
     torch.cuda.synchronize()
-    pool.profile_read(0)
-    pool.set_profiling(True, prof_every(args.steps))
     quiet_gc()
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -627,10 +618,13 @@ def bench_splice_4k(args):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     gc.enable()
-    pool.set_profiling(False)
-    launches, kernel_ms, kernel_bytes = pool.profile_read(0)
     ms_per_step = (t1 - t0) * 1e3 / args.steps
 
+    def step(_):
+        restore()
+        pool.splice(directive)
+
+    launches, kernel_ms, kernel_bytes, samples = kernel_pass(torch, pool, 0, step, args.steps)
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     lat, call = [], []
     quiet_gc()
@@ -654,7 +648,7 @@ def bench_splice_4k(args):
     out["splice_latency_us"] = {"median": round(statistics.median(lat), 1), "min": round(min(lat), 1),
                                 "max": round(max(lat), 1), "runs": len(lat),
                                 "host_call_median": round(statistics.median(call), 1)}
-    out["roofline"] = roofline("splice_kernel", "splice_4k_1layer", launches, kernel_ms, kernel_bytes)
+    out["roofline"] = roofline("splice_kernel", "splice_4k_1layer", launches, kernel_ms, kernel_bytes, samples)
     out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline_small(
         args.cpu_seconds / 4, alg_bytes, TOKENS, PAGE, POOL_PAGES, S_START, S_END, STUB)
     pool.close()
@@ -905,8 +899,6 @@ def bench_splice_batched(args):
         restore()
         pool.splice(dirs)
     torch.cuda.synchronize()
-    pool.profile_read(0)
-    pool.set_profiling(True, prof_every(args.steps))
     quiet_gc()
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -915,13 +907,17 @@ def bench_splice_batched(args):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     gc.enable()
-    pool.set_profiling(False)
-    launches, kernel_ms, kernel_bytes = pool.profile_read(0)
+
+    def step(_):
+        restore()
+        pool.splice(dirs)
+
+    launches, kernel_ms, kernel_bytes, samples = kernel_pass(torch, pool, 0, step, args.steps)
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     out = base_line(args, "splice_16x32k_27layer", alg_bytes / (ms_per_step * 1e-3) / 1e9, ms_per_step, {
         "layers": LAYERS, "tokens": TOKENS, "sequences": SEQS, "page_size": PAGE, "pool_pages": POOL_PAGES,
         "alg_bytes_per_step": alg_bytes, "restore_in_step": "16 page-table rows"})
-    out["roofline"] = roofline("splice_kernel", "splice_16x32k_27layer", launches, kernel_ms, kernel_bytes)
+    out["roofline"] = roofline("splice_kernel", "splice_16x32k_27layer", launches, kernel_ms, kernel_bytes, samples)
     out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline_batched(
         spans, args.cpu_seconds, LAYERS, TOKENS, PAGE)
     pool.close()
@@ -961,8 +957,6 @@ def bench_splice_gqa(args):
         restore()
         pool.splice(directive)
     torch.cuda.synchronize()
-    pool.profile_read(0)
-    pool.set_profiling(True, prof_every(args.steps))
     quiet_gc()
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -971,8 +965,12 @@ def bench_splice_gqa(args):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     gc.enable()
-    pool.set_profiling(False)
-    launches, kernel_ms, kernel_bytes = pool.profile_read(0)
+
+    def step(_):
+        restore()
+        pool.splice(directive)
+
+    launches, kernel_ms, kernel_bytes, samples = kernel_pass(torch, pool, 0, step, args.steps)
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     out = base_line(args, "splice_32k_llama8b", alg_bytes / (ms_per_step * 1e-3) / 1e9, ms_per_step, {
         "layers": LAYERS, "kv_heads": HEADS, "head_dim": HEAD_DIM, "rotary_dim": HEAD_DIM, "tokens": TOKENS,
@@ -980,7 +978,7 @@ def bench_splice_gqa(args):
         "delta": STUB - (S_END - S_START), "storage": "bf16 K and V planes, rotation in f32",
         "alg_bytes_per_step": alg_bytes})
     out["pct_hbm_peak"] = round(100.0 * out["value"] / HBM_PEAK_GBS, 2)
-    out["roofline"] = roofline("gqa_splice_kernel", "splice_32k_llama8b", launches, kernel_ms, kernel_bytes)
+    out["roofline"] = roofline("gqa_splice_kernel", "splice_32k_llama8b", launches, kernel_ms, kernel_bytes, samples)
     out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline_gqa(
         args.cpu_seconds, HEADS, HEAD_DIM, TOKENS, PAGE, POOL_PAGES, S_START, S_END, STUB)
     pool.close()
@@ -1113,10 +1111,13 @@ def bench_kvs_mask(args):
     quiet_gc()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step(True)
+        step(False)                       # no event in the timed loop
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     gc.enable()
+    for _ in range(args.steps):           # the phases' own times, apart
+        step(True)
+    torch.cuda.synchronize()
     ms = {k: statistics.mean(a.elapsed_time(b) for a, b in v) for k, v in ev.items()}
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     out = base_line(args, "kvs_mask_64x32k", dense_bytes / (ms_per_step * 1e-3) / 1e9, ms_per_step, {
@@ -1182,25 +1183,34 @@ def bench_evict(args, page):
     stats = pool.last_stats()
     alg_bytes = stats.alg_bytes
     times, call_times = [], []
+    seq_arr = np.asarray(seqs, dtype=np.int32)
+
+    def evict_steps(n, timed):
+        quiet_gc()
+        for i in range(n):
+            restore()
+            torch.cuda.synchronize()
+            a = time.perf_counter()
+            pool.evict(seq_arr, keep, offsets)
+            b = time.perf_counter()
+            torch.cuda.synchronize()
+            pool.free_pages()  # settles the host bookkeeping of a device-planned call
+            if timed:
+                times.append(time.perf_counter() - a)
+                call_times.append(b - a)
+        gc.enable()
+
+    evict_steps(args.warmup, False)
+    # timed: no launch stamped
+    evict_steps(args.steps, True)
+    # kernel pass: every launch of the row moves (page size 1: the table
+    # kernel) and of the keep scan stamped
     pool.profile_read(0)
     pool.profile_read(1)
-    quiet_gc()
-    for i in range(args.warmup + args.steps):
-        restore()
-        torch.cuda.synchronize()
-        if i == args.warmup:
-            pool.set_profiling(True, prof_every(args.steps))
-        a = time.perf_counter()
-        pool.evict(seqs, keep, offsets)
-        b = time.perf_counter()
-        torch.cuda.synchronize()
-        pool.free_pages()  # settles the host bookkeeping of a device-planned call
-        if i >= args.warmup:
-            times.append(time.perf_counter() - a)
-            call_times.append(b - a)
-    gc.enable()
+    pool.set_profiling(True, 1)
+    evict_steps(min(args.steps, 10), False)
     pool.set_profiling(False)
-    launches, kernel_ms, kernel_bytes = pool.profile_read(0)
+    launches, kernel_ms, kernel_bytes, samples = pool.profile_read(0, samples=16)
     s_launches, scan_ms, _ = pool.profile_read(1)
     ms_per_step = 1e3 * statistics.median(times)
     name = f"evict_256x16k_27layer_p{page}"
@@ -1209,13 +1219,16 @@ def bench_evict(args, page):
         "mask": "turn drops U[200,2000], p=0.5", "rows_kept": int(masks.sum()),
         "rows_moved_per_layer": stats.rows_moved, "fresh_pages": stats.fresh_pages,
         "alg_bytes_per_step": alg_bytes,
-        "page_plan": "device" if page == 1 or POOL_PAGES - ROLL * per >= ROLL * per else "host",
+        "page_plan": "device",
         "step": "one kv_evict_compact call until its device work and host bookkeeping are done, median"})
     out["metric"] = "KV-streams eviction: row bytes moved GB/s; call latency"
-    out["roofline"] = roofline("evict_move_kernel", name, launches, kernel_ms, kernel_bytes)
-    if out["config"]["page_plan"] == "device":
-        # the timed device work is the page plan (and the moves, none at page size 1)
-        out["roofline"]["kernel"] = "device page plan: fresh_rank/alloc_scan/alloc_tables/table_copy + dev_move"
+    out["roofline"] = roofline("evict_move_kernel", name, launches, kernel_ms, kernel_bytes, samples)
+    if page == 1:
+        # nothing moves at page size 1: the timed kernel writes the new tables
+        # and packs the freed-page bitmap
+        out["roofline"]["kernel"] = "unit_page_kernel (new page tables + freed-page bitmap)"
+    out["step_us"] = {"median": round(1e6 * statistics.median(times), 1), "p10": round(1e6 * pct(times, 10), 1),
+                      "p90": round(1e6 * pct(times, 90), 1)}
     out["keep_scan_us"] = round(scan_ms * 1e3 / max(1, s_launches), 2)
     out["call_return_us"] = round(1e6 * statistics.median(call_times), 1)
     out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline_evict(
@@ -1228,8 +1241,9 @@ def bench_evict_gqa(args):
     """KV-streams eviction on a GQA cache of Llama-3-8B shape: 32 rollouts x
     16384 tokens x 32 layers of K and V planes (8 KV heads x 128), page size
     16, random turn drops (turns U[200,2000], p = 0.5); pool pages 1.5 x the
-    rollouts' (the host makes the page plan).  Restoring the tables between
-    steps is outside the timed call."""
+    rollouts' (fewer than the worst case: the call reads the device's verdict
+    before the row moves).  Restoring the tables between steps is outside the
+    timed call."""
     import torch
     from mla_paged_cache_amd import leyline as L
     from synth import np_rng, permuted_pages, turn_drop_mask
@@ -1268,32 +1282,38 @@ def bench_evict_gqa(args):
     stats = pool.last_stats()
     alg_bytes = stats.alg_bytes
     times = []
+    seq_arr = np.asarray(seqs, dtype=np.int32)
+
+    def evict_steps(n, timed):
+        quiet_gc()
+        for i in range(n):
+            restore()
+            torch.cuda.synchronize()
+            a = time.perf_counter()
+            pool.evict(seq_arr, keep, offsets)
+            torch.cuda.synchronize()
+            pool.free_pages()
+            if timed:
+                times.append(time.perf_counter() - a)
+        gc.enable()
+
+    evict_steps(args.warmup, False)
+    evict_steps(args.steps, True)          # no launch stamped
     pool.profile_read(0)
-    quiet_gc()
-    for i in range(args.warmup + args.steps):
-        restore()
-        torch.cuda.synchronize()
-        if i == args.warmup:
-            pool.set_profiling(True, prof_every(args.steps))
-        a = time.perf_counter()
-        pool.evict(seqs, keep, offsets)
-        torch.cuda.synchronize()
-        pool.free_pages()
-        if i >= args.warmup:
-            times.append(time.perf_counter() - a)
-    gc.enable()
+    pool.set_profiling(True, 1)
+    evict_steps(min(args.steps, 10), False)
     pool.set_profiling(False)
-    launches, kernel_ms, kernel_bytes = pool.profile_read(0)
+    launches, kernel_ms, kernel_bytes, samples = pool.profile_read(0, samples=16)
     ms_per_step = 1e3 * statistics.median(times)
     name = "evict_32x16k_llama8b_p16"
     out = base_line(args, name, alg_bytes / (ms_per_step * 1e-3) / 1e9, ms_per_step, {
         "layers": LAYERS, "kv_heads": HEADS, "head_dim": HEAD_DIM, "rollouts": ROLL, "tokens": TOKENS,
         "page_size": PAGE, "pool_pages": POOL_PAGES, "mask": "turn drops U[200,2000], p=0.5",
         "rows_kept": int(masks.sum()), "rows_moved_per_plane": stats.rows_moved, "fresh_pages": stats.fresh_pages,
-        "alg_bytes_per_step": alg_bytes, "page_plan": "host",
+        "alg_bytes_per_step": alg_bytes, "page_plan": "device",
         "step": "one kv_evict_compact call until its device work and host bookkeeping are done, median"})
     out["metric"] = "KV-streams eviction: row bytes moved GB/s; call latency"
-    out["roofline"] = roofline("plane_evict_kernel", name, launches, kernel_ms, kernel_bytes)
+    out["roofline"] = roofline("plane_evict_kernel", name, launches, kernel_ms, kernel_bytes, samples)
     out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline_evict_gqa(
         masks, args.cpu_seconds, LAYERS, HEADS, HEAD_DIM, TOKENS, PAGE, ROLL)
     pool.close()

@@ -19,23 +19,20 @@ struct AllocLaunch {
   int32_t* rank;              // per new page: its index among the sequence's fresh pages
   int32_t* fresh_count;       // [n]
   int32_t* fresh_base;        // [n]: fresh pages of the sequences before
+  int32_t* moved_count;       // [n]: rows of each sequence's fresh pages
   int32_t* word_base;         // [n_words]: free pages in the words before
   int32_t* new_table;         // per sequence at reuse_off: the new page table
   EvictTask* tasks;           // [fresh pages], in (sequence, page) order
-  int32_t* info;              // [0] fresh pages, [1] 1 if they exceed the free pages
+  int32_t* info;              // [0] fresh pages, [1] 1 if they exceed the free pages,
+                              // [2..3] rows written to fresh pages (64-bit); 16-byte aligned
 };
 
-struct DevMoveLaunch {
-  const chunk_t* const* planes;
-  int32_t num_planes;
-  int32_t page_shift;
-  int32_t row_chunks;
-  const EvictTask* tasks;
-  const int32_t* info;        // info[0]: tasks
-  const int32_t* src_rows;
-};
 
-hipError_t launch_alloc(const AllocLaunch& a, hipStream_t s, const Stamp& t = Stamp{});
-hipError_t launch_dev_move(const DevMoveLaunch& a, int64_t chunk_bound, hipStream_t s, const Stamp& t = Stamp{});
+// fresh_rank + alloc_scan (ends with the verdict in info), then
+// alloc_tables + table_copy (both do nothing when info[1] is set).
+hipError_t launch_alloc_scan(const AllocLaunch& a, hipStream_t s, const Stamp& t = Stamp{});
+hipError_t launch_alloc_tables(const AllocLaunch& a, hipStream_t s, const Stamp& t = Stamp{});
+// Zero n 64-bit words (a kernel, so that it can sit in a captured graph).
+hipError_t launch_zero_words(unsigned long long* w, int64_t n, hipStream_t s);
 
 }  // namespace ll

@@ -9,8 +9,9 @@
 //    with no page to move, with the page-table rewrite itself.
 //  * keep_scan_kernel: per-sequence exclusive prefix sum of a keep mask built
 //    from wave64 ballots, giving each kept row its new index and physical
-//    source row, plus the per-new-page reuse test ("KV-streams", "how it
-//    works").  It serves every pool kind.
+//    source row, plus the per-new-page reuse test and the bitmap of the old
+//    pages no new page keeps ("KV-streams", "how it works").  It serves every
+//    pool kind.
 //  * evict_move_kernel: copies kept rows into fresh pages, no rotation, and
 //    rewrites the page-table rows.
 //  * table_write_kernel: page-table row rewrites on their own.
@@ -388,6 +389,25 @@ __global__ __launch_bounds__(kScanThreads) void keep_scan_kernel(ScanLaunch a) {
   int64_t carry = 0;
   for (int64_t base = 0; base < e.n_old; base += 16 * kScanThreads) {
     const int64_t i0 = base + 16 * static_cast<int64_t>(threadIdx.x);
+    // page size 1: the 16 rows' pages, read with the mask (four 16-byte
+    // loads when the row lies whole and aligned in the table)
+    int32_t pg16[16];
+    if (shift == 0) {
+      if (i0 + 16 <= e.n_old && (reinterpret_cast<uintptr_t>(table + i0) & 15u) == 0) {
+        const chunk_t* t4 = reinterpret_cast<const chunk_t*>(table + i0);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const chunk_t v = t4[q];
+          pg16[4 * q] = static_cast<int32_t>(v.x);
+          pg16[4 * q + 1] = static_cast<int32_t>(v.y);
+          pg16[4 * q + 2] = static_cast<int32_t>(v.z);
+          pg16[4 * q + 3] = static_cast<int32_t>(v.w);
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < 16; ++c) pg16[c] = i0 + c < e.n_old ? table[i0 + c] : 0;
+      }
+    }
     uint32_t bits = 0;
     if (i0 + 16 <= e.n_old && (reinterpret_cast<uintptr_t>(m + i0) & 15u) == 0) {
       const chunk_t v = *reinterpret_cast<const chunk_t*>(m + i0);
@@ -419,28 +439,86 @@ __global__ __launch_bounds__(kScanThreads) void keep_scan_kernel(ScanLaunch a) {
       block_total += x;
     }
     int64_t pos = carry + wave_below + below;
-    for (int c = 0; c < 16; ++c)
-      if ((bits >> c) & 1u) {
+    if (shift == 0) {
+      // page size 1: the row's page is the row; a dropped row frees it
+      for (int c = 0; c < 16; ++c) {
         const int64_t i = i0 + c;
-        out_logical[pos] = static_cast<int32_t>(i);
-        out[pos++] = static_cast<int32_t>((static_cast<int64_t>(table[i >> shift]) << shift) + (i & pmask));
+        if (i >= e.n_old) break;
+        const int32_t pg = pg16[c];
+        if ((bits >> c) & 1u)
+          out[pos++] = pg;
+        else
+          a.freed_bytes[pg] = 1;
       }
+    } else {
+      for (int c = 0; c < 16; ++c)
+        if ((bits >> c) & 1u) {
+          const int64_t i = i0 + c;
+          out_logical[pos] = static_cast<int32_t>(i);
+          out[pos++] = static_cast<int32_t>((static_cast<int64_t>(table[i >> shift]) << shift) + (i & pmask));
+        }
+    }
     carry += block_total;
     __syncthreads();
   }
   // Per new page: reusable iff its live rows are the old rows f .. f+k-1 with
-  // f on a page boundary -- one old page, rows at their old offsets.
+  // f on a page boundary -- one old page, rows at their old offsets.  The old
+  // pages no new page keeps go into the freed bitmap.
   const int64_t P = int64_t{1} << shift;
   const int64_t n_new = carry;
+  if (shift == 0) {
+    if (threadIdx.x == 0) a.counts[blockIdx.x] = n_new;
+    return;
+  }
   const int64_t pages = (n_new + P - 1) >> shift;
+  const int64_t old_pages = (e.n_old + P - 1) >> shift;
   int32_t* reuse = a.reuse + e.reuse_off;
+  uint8_t* kept = a.kept + e.reuse_off;
+  for (int64_t k = threadIdx.x; k < old_pages; k += kScanThreads) kept[k] = 0;
+  __syncthreads();
   for (int64_t q = threadIdx.x; q < pages; q += kScanThreads) {
     const int64_t k = (n_new - (q << shift)) < P ? (n_new - (q << shift)) : P;
     const int64_t f = out_logical[q << shift];
     const int64_t l = out_logical[(q << shift) + k - 1];
-    reuse[q] = ((f & pmask) == 0 && l - f == k - 1) ? static_cast<int32_t>(f >> shift) : -1;
+    const bool keep = (f & pmask) == 0 && l - f == k - 1;
+    reuse[q] = keep ? static_cast<int32_t>(f >> shift) : -1;
+    if (keep) kept[f >> shift] = 1;
   }
+  __syncthreads();
+  for (int64_t k = threadIdx.x; k < old_pages; k += kScanThreads)
+    if (!kept[k]) {
+      const uint32_t pg = static_cast<uint32_t>(table[k]);
+      atomicOr(a.freed + (pg >> 6), 1ull << (pg & 63u));
+    }
   if (threadIdx.x == 0) a.counts[blockIdx.x] = n_new;
+}
+
+__global__ __launch_bounds__(256) void unit_page_kernel(UnitPageLaunch a) {
+  const int64_t b = blockIdx.x;
+  if (b < a.n) {
+    const EvictSeq e = a.seqs[b];
+    const int64_t n_new = a.counts[b];
+    int32_t* dst = a.page_table + static_cast<int64_t>(e.seq) * a.max_pages_per_seq;
+    const int32_t* src = a.src_rows + e.src_off;
+    for (int64_t q = threadIdx.x; q < n_new; q += 256) dst[q] = src[q];
+    if (b == 0 && threadIdx.x < 4) a.info[threadIdx.x] = 0;
+    return;
+  }
+  const int64_t w = (b - a.n) * 256 + threadIdx.x;
+  if (w >= a.n_words) return;
+  const chunk_t* src = reinterpret_cast<const chunk_t*>(a.freed_bytes + 64 * w);
+  unsigned long long word = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const chunk_t v = src[k];
+    const uint32_t x[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if ((x[m] >> (8 * c)) & 0xFFu) word |= 1ull << (16 * k + 4 * m + c);
+  }
+  a.freed[w] = word;
 }
 
 }  // namespace
@@ -449,6 +527,12 @@ __global__ __launch_bounds__(kScanThreads) void keep_scan_kernel(ScanLaunch a) {
 // more registers than the row moves, which then keep their occupancy).  It
 // goes first; the page-table rewrite rides on the last launch.  The two
 // launches touch disjoint pages.
+hipError_t launch_unit_page(const UnitPageLaunch& a, hipStream_t s, const Stamp& t) {
+  const int64_t grid = a.n + (a.n_words + 255) / 256;
+  if (grid == 0) return stamp_empty(s, t);
+  return dispatch(unit_page_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), s, t, true, true, a);
+}
+
 hipError_t launch_splice(const SpliceLaunch& a, int pairing, hipStream_t s, const Stamp& t) {
   const int64_t move = a.move_blocks_per_layer * a.num_layers;
   const int64_t rot = a.rot_blocks_per_layer * a.num_layers;

@@ -7,14 +7,16 @@
 //  * fresh_rank_kernel: per sequence, a block scan over its new pages numbers
 //    the ones that cannot reuse an old page (fresh pages).
 //  * alloc_scan_kernel: one block; exclusive scans of the fresh counts over
-//    the batch and of the free bitmap's word popcounts.
+//    the batch and of the free bitmap's word popcounts; the verdict (fresh
+//    pages, or "short of pages").
 //  * alloc_tables_kernel: per new page, its physical page: the reused old page,
 //    or fresh page f = the f-th lowest free page (binary search over the word
 //    prefix, then the bit inside the word); fresh pages also get a move task.
 //  * table_copy_kernel: the new page-table rows, written after every read of
 //    the old ones.
-//  * dev_move_kernel: the row copy into fresh pages, grid-stride over a task
-//    count that only the device knows.
+// The row moves into fresh pages are evict_move_kernel (kernels.hip) or
+// plane_evict_kernel (kernels_gqa.hip), launched by the host on the exact
+// grid once it has read the verdict.
 #include "alloc_internal.h"
 #include "device_common.h"
 
@@ -53,17 +55,29 @@ __global__ __launch_bounds__(kScanThreads) void fresh_rank_kernel(AllocLaunch a)
   __shared__ int lds[kScanWaves];
   const EvictSeq e = a.seqs[blockIdx.x];
   const int64_t P = int64_t{1} << a.page_shift;
-  const int64_t pages = (a.counts[blockIdx.x] + P - 1) >> a.page_shift;
-  int carry = 0;
+  const int64_t n_new = a.counts[blockIdx.x];
+  const int64_t pages = (n_new + P - 1) >> a.page_shift;
+  int carry = 0, moved = 0;
   for (int64_t base = 0; base < pages; base += kScanThreads) {
     const int64_t q = base + threadIdx.x;
-    const int fresh = (q < pages && a.reuse[e.reuse_off + q] < 0) ? 1 : 0;
-    int total;
-    const int r = block_exclusive_scan(fresh, lds, &total);
+    const bool fresh = q < pages && a.reuse[e.reuse_off + q] < 0;
+    const int64_t live = fresh ? n_new - (q << a.page_shift) : 0;
+    int total, rows_total;
+    const int r = block_exclusive_scan(fresh ? 1 : 0, lds, &total);
+    (void)block_exclusive_scan(static_cast<int>(live < P ? live : P), lds, &rows_total);
     if (q < pages) a.rank[e.reuse_off + q] = carry + r;
     carry += total;
+    moved += rows_total;
   }
-  if (threadIdx.x == 0) a.fresh_count[blockIdx.x] = carry;
+  if (threadIdx.x == 0) {
+    a.fresh_count[blockIdx.x] = carry;
+    a.moved_count[blockIdx.x] = moved;
+  }
+}
+
+// info[2..3]: the rows written to fresh pages, as one 64-bit count.
+__device__ __forceinline__ unsigned long long* moved_rows(const AllocLaunch& a) {
+  return reinterpret_cast<unsigned long long*>(a.info + 2);
 }
 
 __global__ __launch_bounds__(kScanThreads) void alloc_scan_kernel(AllocLaunch a) {
@@ -78,6 +92,13 @@ __global__ __launch_bounds__(kScanThreads) void alloc_scan_kernel(AllocLaunch a)
     carry += total;
   }
   const int fresh = carry;
+  // rows written to fresh pages, over the batch (64-bit)
+  unsigned long long moved = 0;
+  for (int i = threadIdx.x; i < a.n; i += kScanThreads) moved += static_cast<unsigned long long>(a.moved_count[i]);
+  for (int o = 32; o > 0; o >>= 1) moved += __shfl_down(moved, o);
+  __shared__ unsigned long long wave_moved[kScanWaves];
+  if ((threadIdx.x & 63) == 0) wave_moved[threadIdx.x >> 6] = moved;
+  __syncthreads();
   carry = 0;
   for (int base = 0; base < a.n_words; base += kScanThreads) {
     const int w = base + threadIdx.x;
@@ -91,6 +112,9 @@ __global__ __launch_bounds__(kScanThreads) void alloc_scan_kernel(AllocLaunch a)
     const bool short_of_pages = fresh > carry;
     a.info[0] = short_of_pages ? 0 : fresh;
     a.info[1] = short_of_pages ? 1 : 0;
+    unsigned long long sum = 0;
+    for (int w = 0; w < kScanWaves; ++w) sum += wave_moved[w];
+    *moved_rows(a) = short_of_pages ? 0ull : sum;
   }
 }
 
@@ -135,6 +159,11 @@ __global__ __launch_bounds__(256) void alloc_tables_kernel(AllocLaunch a) {
   }
 }
 
+__global__ __launch_bounds__(256) void zero_words_kernel(unsigned long long* w, int64_t n) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n; i += static_cast<int64_t>(gridDim.x) * 256)
+    w[i] = 0ull;
+}
+
 __global__ __launch_bounds__(256) void table_copy_kernel(AllocLaunch a) {
   if (a.info[1]) return;
   const EvictSeq e = a.seqs[blockIdx.x];
@@ -144,49 +173,25 @@ __global__ __launch_bounds__(256) void table_copy_kernel(AllocLaunch a) {
   for (int64_t q = threadIdx.x; q < pages; q += 256) t[q] = a.new_table[e.reuse_off + q];
 }
 
-// blockIdx.y = plane; the x blocks stride over the info[0] * P * row_chunks
-// chunks of the fresh pages (task = page, then row, then chunk).
-template <bool WAVE_TASK>
-__global__ __launch_bounds__(256) void dev_move_kernel(DevMoveLaunch a) {
-  const int shift = a.page_shift;
-  const uint32_t rc = static_cast<uint32_t>(a.row_chunks);
-  const int64_t total = (static_cast<int64_t>(a.info[0]) << shift) * rc;
-  const chunk_t* layer = a.planes[blockIdx.y];
-  for (int64_t c = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; c < total;
-       c += static_cast<int64_t>(gridDim.x) * 256) {
-    const uint32_t row_flat = static_cast<uint32_t>(c / rc);
-    const uint32_t col = static_cast<uint32_t>(c - static_cast<int64_t>(row_flat) * rc);
-    const EvictTask t = load_task<WAVE_TASK>(a.tasks, row_flat >> shift);
-    const uint32_t r = row_flat & ((1u << shift) - 1u);
-    const int64_t j = (static_cast<int64_t>(t.q) << shift) + r;
-    if (j >= t.n_new) continue;
-    const int64_t src_row = a.src_rows[t.src_off + j];
-    const chunk_t v = __builtin_nontemporal_load(layer + src_row * rc + col);
-    __builtin_nontemporal_store(v, const_cast<chunk_t*>(layer) +
-                                       ((static_cast<int64_t>(t.dst_page) << shift) + r) * rc + col);
-  }
-}
-
 }  // namespace
 
-hipError_t launch_alloc(const AllocLaunch& a, hipStream_t s, const Stamp& t) {
-  if (a.n == 0) return stamp_empty(s, t);
+hipError_t launch_alloc_scan(const AllocLaunch& a, hipStream_t s, const Stamp& t) {
   hipError_t e = dispatch(fresh_rank_kernel, dim3(a.n), dim3(kScanThreads), s, t, true, false, a);
   if (e != hipSuccess) return e;
-  if ((e = dispatch(alloc_scan_kernel, dim3(1), dim3(kScanThreads), s, t, false, false, a)) != hipSuccess) return e;
-  if ((e = dispatch(alloc_tables_kernel, dim3(a.n), dim3(256), s, t, false, false, a)) != hipSuccess) return e;
+  return dispatch(alloc_scan_kernel, dim3(1), dim3(kScanThreads), s, t, false, true, a);
+}
+
+hipError_t launch_alloc_tables(const AllocLaunch& a, hipStream_t s, const Stamp& t) {
+  hipError_t e = dispatch(alloc_tables_kernel, dim3(a.n), dim3(256), s, t, true, false, a);
+  if (e != hipSuccess) return e;
   return dispatch(table_copy_kernel, dim3(a.n), dim3(256), s, t, false, true, a);
 }
 
-hipError_t launch_dev_move(const DevMoveLaunch& a, int64_t chunk_bound, hipStream_t s, const Stamp& t) {
-  if (a.num_planes == 0 || chunk_bound == 0) return stamp_empty(s, t);
-  // enough blocks to fill the chip several times over; each strides over the rest
-  const int64_t want = (chunk_bound + 255) / 256;
-  const unsigned gx = static_cast<unsigned>(want < 2048 ? want : 2048);
-  const dim3 grid(gx, static_cast<unsigned>(a.num_planes));
-  void (*k)(DevMoveLaunch) =
-      (int64_t{a.row_chunks} << a.page_shift) % 64 == 0 ? dev_move_kernel<true> : dev_move_kernel<false>;
-  return dispatch(k, grid, dim3(256), s, t, true, true, a);
+hipError_t launch_zero_words(unsigned long long* w, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = (n + 255) / 256;
+  zero_words_kernel<<<dim3(static_cast<unsigned>(blocks < 1024 ? blocks : 1024)), dim3(256), 0, s>>>(w, n);
+  return hipGetLastError();
 }
 
 }  // namespace ll

@@ -188,6 +188,30 @@ struct ScanLaunch {
   int32_t* src_logical;        // out: old logical index of each kept row
   int64_t* counts;             // out: [n_seqs] rows kept
   int32_t* reuse;              // out: per new page, the old logical page it keeps, or -1
+  // page size > 1: the reuse test, and the old pages no new page keeps
+  // OR-ed into `freed` (zeroed before the scan), using `kept` as scratch
+  uint8_t* kept;               // scratch: per old page (at reuse_off), 1 if a new page keeps it
+  unsigned long long* freed;   // out: bitmap over physical pages
+  // page size 1: every kept row keeps its page, so no reuse test and no
+  // src_logical; a dropped row's page gets freed_bytes[page] = 1 (each page
+  // has one writer; zeroed before the scan)
+  uint8_t* freed_bytes;
+};
+
+// Page size 1, after the keep scan: blocks [0, n) write each sequence's new
+// page-table row (its kept rows' pages, i.e. its src_rows, in order); the
+// other blocks pack freed_bytes into the freed bitmap, 64 pages a word.
+struct UnitPageLaunch {
+  const EvictSeq* seqs;
+  int32_t n;
+  const int64_t* counts;
+  const int32_t* src_rows;
+  int32_t* page_table;
+  int32_t max_pages_per_seq;
+  const uint8_t* freed_bytes;  // [64 * n_words]
+  unsigned long long* freed;   // [n_words]
+  int64_t n_words;
+  int32_t* info;               // zeroed (no fresh page, no row moved)
 };
 
 // A splice batch planned on the device.  The host sends the compact plan as
@@ -260,6 +284,7 @@ hipError_t launch_splice(const SpliceLaunch& a, int pairing, hipStream_t s, cons
 hipError_t launch_evict_move(const EvictLaunch& a, hipStream_t s, const Stamp& t = Stamp{});
 hipError_t launch_table_write(const TableLaunch& a, hipStream_t s);
 hipError_t launch_keep_scan(const ScanLaunch& a, hipStream_t s, const Stamp& t = Stamp{});
+hipError_t launch_unit_page(const UnitPageLaunch& a, hipStream_t s, const Stamp& t = Stamp{});
 hipError_t launch_gqa_splice(const GqaSpliceLaunch& a, int pairing, hipStream_t s, const Stamp& t = Stamp{});
 hipError_t launch_plane_evict(const PlaneEvictLaunch& a, hipStream_t s, const Stamp& t = Stamp{});
 hipError_t launch_splice_plan(const DirectPlanArgs& a, int32_t max_new_pages, hipStream_t s);

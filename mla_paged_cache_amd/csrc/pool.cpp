@@ -93,6 +93,27 @@ class FreePages {
       }
     }
   }
+  // Pages marked in `bits` return to the free set, in one pass; false if one
+  // of them was free already or is not a page (the caller then treats the
+  // set as broken).
+  bool give_bits_checked(const uint64_t* bits) {
+    const size_t n = words_.size();
+    if (n && (bits[n - 1] & ~tail_mask())) return false;
+    uint64_t clash = 0;
+    int64_t added = 0;
+    size_t first = n;
+    for (size_t w = 0; w < n; ++w) {
+      const uint64_t b = bits[w];
+      if (!b) continue;
+      clash |= b & words_[w];
+      words_[w] |= b;
+      added += __builtin_popcountll(b);
+      if (first == n) first = w;
+    }
+    count_ += added;
+    hint_ = std::min<int64_t>(hint_, static_cast<int64_t>(first));
+    return clash == 0;
+  }
   // Pages marked in `bits` (all taken now) return to the free set.
   void give_bits(const uint64_t* bits) {
     for (size_t w = 0; w < words_.size(); ++w) {
@@ -110,6 +131,9 @@ class FreePages {
   }
 
  private:
+  // bits of the last word that are pages
+  uint64_t tail_mask() const { return n_ % 64 ? (1ull << (n_ % 64)) - 1 : ~0ull; }
+
   int64_t n_ = 0, count_ = 0, hint_ = 0;
   std::vector<uint64_t> words_;
 };
@@ -119,6 +143,9 @@ struct SeqState {
   int64_t len = 0;
   int64_t next_pos = 0;
   std::vector<int32_t> pages;
+  // pages is out of date: the device page-table row (written by an eviction
+  // the device planned) holds the sequence's table; copied back on demand
+  bool stale = false;
 };
 
 // The region of the staging ring one call fills on the host and sends to the
@@ -222,16 +249,17 @@ struct ll_pool {
   std::vector<ProfRec> prof[3];  // row-moving kernel, keep scan, per-row rotation
   std::vector<hipEvent_t> spare_events;
   std::vector<int32_t> page_slot;  // per physical page: scratch marks of ll_seq_set_pages
-  std::vector<uint64_t> settle_bits;  // pages freed by a settle, one bitmap per host thread
-  // An eviction whose page plan the device made: the host learns its result
-  // from a readback and brings its bookkeeping up to date (settles) at the
-  // start of the next call on the pool.
+  std::vector<int32_t> table_rows;     // host copy of device page-table rows (stale tables)
+  // An eviction at page size 1 (no page is ever fresh): the call returns at
+  // once and the host learns its result -- new lengths and the bitmap of
+  // freed pages -- from a small readback that the next call on the pool
+  // applies (settles) first.
   struct PendingEvict {
     bool active = false;
     hipEvent_t done = nullptr;   // the readback has landed
     std::vector<int32_t> seq_ids;
-    std::vector<int64_t> reuse_off;
-    size_t off_info = 0, off_table = 0, off_reuse = 0;  // in h_readback (counts at 0)
+    size_t off_info = 0, off_freed = 0;  // in h_readback (counts at 0)
+    int64_t n_words = 0;         // words of the freed bitmap
     int64_t prof_index = -1;     // prof[0] entry whose bytes are known only then
   } pending;
 };
@@ -257,131 +285,60 @@ ll_status check_pool(const ll_pool* p) {
   return LL_OK;
 }
 
-// Bring the host bookkeeping up to date with an eviction planned on the
-// device: its new lengths and page tables come from the readback; fresh pages
-// leave the free set and old pages no longer listed return to it.
+// Apply the result of a device-planned eviction to the host bookkeeping, from
+// its readback: counts[i] rows kept by sequence seq_ids[i]; info[0] fresh
+// pages, which are the info[0] lowest free pages (the device picked them from
+// the free set as the call found it, and nothing has changed the free set
+// since); the bitmap of old pages no new page keeps returns to the free set.
+// The new page tables are on the device: the host copies are marked stale.
+ll_status apply_evict(ll_pool* p, const int32_t* seq_ids, size_t n_seqs, const int64_t* counts,
+                      const int32_t* info, const uint64_t* freed, int64_t n_words, int64_t prof_index) {
+  const int64_t P = p->P;
+  auto bad_plan = [p](const char* what) {
+    p->poisoned = true;
+    return fail(LL_EDEVICE, "the device page plan returned %s", what);
+  };
+  if (info[1]) return bad_plan("a shortage the host did not expect");
+  for (size_t i = 0; i < n_seqs; ++i)
+    if (counts[i] < 0 || counts[i] > p->seqs[seq_ids[i]].len) return bad_plan("a bad length");
+  const int64_t fresh = info[0];
+  if (fresh < 0 || fresh > p->free.count() || (P == 1 && fresh != 0)) return bad_plan("a bad fresh-page count");
+  if (n_words != static_cast<int64_t>(p->free.num_words())) return bad_plan("a bitmap of the wrong size");
+  ll_plan_stats stats{};
+  std::vector<int32_t> taken;
+  p->free.lowest(fresh, taken);
+  for (int32_t pg : taken) p->free.take(pg);
+  // freed pages were the sequences' own: none of them may be free now
+  const int64_t before = p->free.count();
+  if (!p->free.give_bits_checked(freed)) return bad_plan("a freed page that was already free");
+  p->free.advance_hint();
+  stats.freed_pages = p->free.count() - before;
+  stats.fresh_pages = fresh;
+  stats.rows_moved = static_cast<int64_t>(*reinterpret_cast<const uint64_t*>(info + 2));
+  for (size_t i = 0; i < n_seqs; ++i) {
+    SeqState& s = p->seqs[seq_ids[i]];
+    s.len = counts[i];
+    s.stale = true;
+    stats.table_entries += ceil_div(counts[i], P);
+  }
+  stats.alg_bytes = p->num_planes * 2 * p->row_bytes * stats.rows_moved;
+  stats.planned_on_device = 1;
+  if (prof_index >= 0 && prof_index < static_cast<int64_t>(p->prof[0].size()))
+    p->prof[0][prof_index].bytes = stats.alg_bytes + 4 * stats.table_entries;
+  p->last = stats;
+  return LL_OK;
+}
+
+// Settle a pending eviction (page size 1): wait for its readback, apply it.
 ll_status settle(ll_pool* p) {
   ll_pool::PendingEvict& pe = p->pending;
   if (!pe.active) return LL_OK;
   pe.active = false;
   hipError_t e = hipEventSynchronize(pe.done);
   if (e != hipSuccess) return device_fail(p, e, "eviction readback");
-  const int64_t* counts = reinterpret_cast<const int64_t*>(p->h_readback);
-  const int32_t* info = reinterpret_cast<const int32_t*>(p->h_readback + pe.off_info);
-  const int32_t* table = reinterpret_cast<const int32_t*>(p->h_readback + pe.off_table);
-  if (info[1]) {
-    p->poisoned = true;
-    return fail(LL_EDEVICE, "the device page plan ran out of free pages");
-  }
-  const int32_t* reuse = reinterpret_cast<const int32_t*>(p->h_readback + pe.off_reuse);
-  const int64_t P = p->P;
-  const size_t n_seqs = pe.seq_ids.size();
-  ll_plan_stats stats{};
-  auto bad_plan = [p](const char* what) {
-    p->poisoned = true;
-    return fail(LL_EDEVICE, "the device page plan returned %s", what);
-  };
-  for (size_t i = 0; i < n_seqs; ++i)
-    if (counts[i] < 0 || counts[i] > p->seqs[pe.seq_ids[i]].len) return bad_plan("a bad length");
-  // Pass 1: fresh pages leave the free set, each checked against the free set
-  // as the call found it (no page of this call has returned to it yet).  At
-  // page size 1 no page is ever fresh.
-  if (P > 1) {
-    for (size_t i = 0; i < n_seqs; ++i) {
-      const int64_t n_new = counts[i];
-      const int32_t* nt = table + pe.reuse_off[i];
-      const int32_t* ru = reuse + pe.reuse_off[i];
-      for (int64_t q = 0, pages = ceil_div(n_new, P); q < pages; ++q) {
-        if (ru[q] >= 0) continue;
-        const int32_t pg = nt[q];
-        if (pg < 0 || pg >= p->desc.num_pages || !p->free.is_free(pg)) return bad_plan("an invalid fresh page");
-        p->free.take(pg);
-        ++stats.fresh_pages;
-        stats.rows_moved += std::min(P, n_new - q * P);
-      }
-    }
-  }
-  // Pass 2: one merge walk per sequence.  Kept old pages appear in `ru` in
-  // increasing order; the old pages between them are freed (marked in `bits`).
-  // A large settle (page size 1 over many rollouts: millions of pages) splits
-  // the sequences over a few host threads, each with a bitmap of its own.
-  int64_t old_total = 0;
-  for (size_t i = 0; i < n_seqs; ++i) old_total += static_cast<int64_t>(p->seqs[pe.seq_ids[i]].pages.size());
-  const unsigned hw = std::max(1u, std::thread::hardware_concurrency());
-  const int T = old_total >= (int64_t{1} << 18) ? static_cast<int>(std::min(8u, hw)) : 1;
-  const size_t W = p->free.num_words();
-  p->settle_bits.assign(static_cast<size_t>(T) * W, 0);
-  std::vector<int64_t> freed(T, 0), entries(T, 0);
-  std::vector<const char*> err(T, nullptr);
-  std::vector<char> oom(T, 0);
-  auto walk_share = [&](int t) {
-    uint64_t* bits = p->settle_bits.data() + static_cast<size_t>(t) * W;
-    for (size_t i = t; i < n_seqs; i += T) {
-      SeqState& s = p->seqs[pe.seq_ids[i]];
-      const int64_t n_new = counts[i];
-      const int64_t pages = ceil_div(n_new, P);
-      const int32_t* nt = table + pe.reuse_off[i];
-      const int32_t* ru = reuse + pe.reuse_off[i];
-      const int32_t* old = s.pages.data();
-      const int64_t old_pages = static_cast<int64_t>(s.pages.size());
-      int64_t k = 0;     // next old logical page not yet classified
-      int64_t kept = 0;  // old pages the sequence keeps
-      for (int64_t q = 0; q < pages; ++q) {
-        const int32_t r = ru[q];
-        if (r < 0) {
-          if (P == 1) {
-            err[t] = "a fresh page at page size 1";
-            return;
-          }
-          continue;
-        }
-        if (r < k || r >= old_pages || nt[q] != old[r]) {
-          err[t] = "an invalid reused page";
-          return;
-        }
-        for (; k < r; ++k) bits[old[k] >> 6] |= 1ull << (old[k] & 63);
-        k = r + 1;
-        ++kept;
-      }
-      for (; k < old_pages; ++k) bits[old[k] >> 6] |= 1ull << (old[k] & 63);
-      freed[t] += old_pages - kept;
-      s.pages.assign(nt, nt + pages);
-      s.len = n_new;
-      entries[t] += pages;
-    }
-  };
-  auto walk = [&](int t) noexcept {
-    try {
-      walk_share(t);
-    } catch (...) {
-      oom[t] = 1;
-    }
-  };
-  std::vector<std::thread> helpers;
-  int started = 1;
-  try {
-    for (; started < T; ++started) helpers.emplace_back(walk, started);
-  } catch (...) {
-    // no thread to be had: the shares not started run here
-  }
-  walk(0);
-  for (int t = started; t < T; ++t) walk(t);
-  for (std::thread& th : helpers) th.join();
-  for (int t = 0; t < T; ++t)
-    if (oom[t]) return host_exception(p);
-  for (int t = 0; t < T; ++t) {
-    if (err[t]) return bad_plan(err[t]);
-    stats.freed_pages += freed[t];
-    stats.table_entries += entries[t];
-  }
-  for (int t = 0; t < T; ++t) p->free.give_bits(p->settle_bits.data() + static_cast<size_t>(t) * W);
-  p->free.advance_hint();
-  stats.alg_bytes = p->num_planes * 2 * p->row_bytes * stats.rows_moved;
-  stats.planned_on_device = 1;
-  if (pe.prof_index >= 0 && pe.prof_index < static_cast<int64_t>(p->prof[0].size()))
-    p->prof[0][pe.prof_index].bytes = stats.alg_bytes + 4 * stats.table_entries;
-  p->last = stats;
-  return LL_OK;
+  return apply_evict(p, pe.seq_ids.data(), pe.seq_ids.size(), reinterpret_cast<const int64_t*>(p->h_readback),
+                     reinterpret_cast<const int32_t*>(p->h_readback + pe.off_info),
+                     reinterpret_cast<const uint64_t*>(p->h_readback + pe.off_freed), pe.n_words, pe.prof_index);
 }
 
 // check_pool, then settle a pending device-planned eviction.
@@ -404,8 +361,15 @@ hipEvent_t take_event(ll_pool* p) {
   return e;
 }
 
-// Drop finished regions from the front of the ring's in-flight list.
+// Drop finished regions from the front of the ring's in-flight list.  Calls on
+// one pool finish in order, so when the newest region is done all are (one
+// query, however many regions a run of small calls left behind).
 void ring_reap(ll_pool* p) {
+  if (!p->ring_inflight.empty() && hipEventQuery(p->ring_inflight.back().done) == hipSuccess) {
+    for (RingRegion& r : p->ring_inflight) p->ring_events.push_back(r.done);
+    p->ring_inflight.clear();
+    return;
+  }
   while (!p->ring_inflight.empty() && hipEventQuery(p->ring_inflight.front().done) == hipSuccess) {
     p->ring_events.push_back(p->ring_inflight.front().done);
     p->ring_inflight.pop_front();
@@ -509,6 +473,43 @@ ll_status wait_idle(ll_pool* p) {
   if (e != hipSuccess) return device_fail(p, e, "hipEventSynchronize");
   return LL_OK;
 }
+
+// Bring the host page tables of `seqs` up to date where an eviction left them
+// stale: wait for the pool's device work, then copy the device page-table rows
+// back -- every stale sequence's, in one copy spanning them (an eviction
+// leaves a whole batch stale, and its tables are usually needed together).
+ll_status fresh_tables(ll_pool* p, const int32_t* seqs, size_t n) {
+  bool any = false;
+  for (size_t i = 0; i < n && !any; ++i) {
+    const int32_t s = seqs[i];
+    any = s >= 0 && s < p->desc.max_seqs && p->seqs[s].used && p->seqs[s].stale;
+  }
+  if (!any) return LL_OK;
+  int32_t lo = INT32_MAX, hi = -1;
+  for (int32_t s = 0; s < p->desc.max_seqs; ++s)
+    if (p->seqs[s].used && p->seqs[s].stale) {
+      lo = std::min(lo, s);
+      hi = s;
+    }
+  if (ll_status rc = wait_idle(p)) return rc;
+  const int64_t w = p->desc.max_pages_per_seq;
+  const size_t count = static_cast<size_t>(hi - lo + 1) * static_cast<size_t>(w);
+  p->table_rows.resize(count);
+  DeviceGuard g(p->desc.device);
+  hipError_t e = hipMemcpy(p->table_rows.data(), p->desc.page_table + static_cast<int64_t>(lo) * w,
+                           count * sizeof(int32_t), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return device_fail(p, e, "hipMemcpy(page-table rows)");
+  for (int32_t s = lo; s <= hi; ++s) {
+    SeqState& st = p->seqs[s];
+    if (!st.used || !st.stale) continue;
+    const int32_t* row = p->table_rows.data() + static_cast<int64_t>(s - lo) * w;
+    st.pages.assign(row, row + ceil_div(st.len, p->P));
+    st.stale = false;
+  }
+  return LL_OK;
+}
+
+ll_status fresh_table(ll_pool* p, int32_t seq) { return fresh_tables(p, &seq, 1); }
 
 // Order this call after the previous call on the pool (any stream; calls on
 // one stream are ordered already).
@@ -742,43 +743,56 @@ ll_status ensure_evict_buffers(ll_pool* p, size_t scratch, size_t readback) {
 }
 
 // Eviction with the page plan made on the device (kernels_alloc.hip): keep
-// scan, fresh-page ranks, lowest-free-first selection from the free bitmap as
-// it stands now, new tables, row moves, then one readback that the next call
-// settles.  Nothing here waits for the device.
+// scan (new indices, sources, per-page reuse, the bitmap of freed old pages),
+// fresh-page ranks and the verdict (fresh pages, or a shortage), a readback of
+// [counts | verdict | freed bitmap], then the new tables and the row moves.
+// At page size > 1 the call waits for that readback only -- tens of
+// microseconds, the scan's time -- so that a shortage returns LL_ENOMEM with
+// nothing changed and the row-move kernel gets an exact grid; the host's books
+// are then brought up to date in the same call.  At page size 1 no page is
+// fresh and nothing moves: the call does not wait, and the next call on the
+// pool applies the readback.
 ll_status evict_device_plan(ll_pool* p, const int32_t* seq_ids, int32_t n, const uint8_t* keep_dev,
-                            const std::vector<ll::EvictSeq>& es, const std::vector<int64_t>& reuse_off,
-                            int64_t total_rows, int64_t total_pages, hipStream_t st) {
+                            const std::vector<ll::EvictSeq>& es, int64_t total_rows, int64_t total_pages,
+                            hipStream_t st) {
   const int64_t P = p->P;
   const int64_t rc_chunks = p->row_bytes / 16;
-  if (total_pages * P * rc_chunks >= (int64_t{1} << 32))
+  if (total_pages * P * rc_chunks >= (int64_t{1} << 32) - 1024)
     return fail(LL_EUNSUPPORTED, "one eviction may move at most 2^32 16-byte chunks per layer");
-  const int32_t n_words = P == 1 ? 0 : static_cast<int32_t>(ceil_div(p->desc.num_pages, 64));
-  // device scratch: [counts n | info 4 | new_table tp | reuse tp] (read back in
-  // one copy), then src_rows rows | src_logical rows | rank tp | fresh_count n |
-  // fresh_base n | word_base n_words | tasks tp
+  const int64_t n_words = static_cast<int64_t>(p->free.num_words());
+  const int32_t n_free_words = P == 1 ? 0 : static_cast<int32_t>(n_words);
+  // device scratch: [counts n | info 16 | freed n_words] (read back in one
+  // copy), then reuse tp | new_table tp | src_rows rows | src_logical rows |
+  // kept tp (bytes) | rank tp | fresh_count n | fresh_base n | moved n |
+  // word_base n_free_words | tasks tp
   const size_t tp = static_cast<size_t>(total_pages), rows = static_cast<size_t>(total_rows);
-  const size_t off_info = align_up(8 * static_cast<size_t>(n), 16);
-  const size_t off_nt = align_up(off_info + 16, 256);
-  const size_t off_reuse = off_nt + 4 * tp;
-  const size_t readback = off_reuse + 4 * tp;
-  const size_t off_src = align_up(readback, 256);
+  const size_t nn = static_cast<size_t>(n);
+  const size_t off_info = align_up(8 * nn, 16);
+  const size_t off_freed = align_up(off_info + 16, 256);
+  const size_t readback = off_freed + 8 * static_cast<size_t>(n_words);
+  const size_t off_reuse = align_up(readback, 256);
+  const size_t off_nt = align_up(off_reuse + 4 * tp, 256);
+  const size_t off_src = align_up(off_nt + 4 * tp, 256);
   const size_t off_logical = align_up(off_src + 4 * rows, 256);
-  const size_t off_rank = align_up(off_logical + 4 * rows, 256);
+  const size_t off_kept = align_up(off_logical + 4 * rows, 256);
+  const size_t off_rank = align_up(off_kept + tp, 256);
   const size_t off_fc = align_up(off_rank + 4 * tp, 256);
-  const size_t off_fb = align_up(off_fc + 4 * static_cast<size_t>(n), 256);
-  const size_t off_wb = align_up(off_fb + 4 * static_cast<size_t>(n), 256);
-  const size_t off_tasks = align_up(off_wb + 4 * static_cast<size_t>(n_words), 256);
-  const size_t scratch = off_tasks + sizeof(ll::EvictTask) * tp + 256;
+  const size_t off_fb = align_up(off_fc + 4 * nn, 256);
+  const size_t off_mv = align_up(off_fb + 4 * nn, 256);
+  const size_t off_wb = align_up(off_mv + 4 * nn, 256);
+  const size_t off_tasks = align_up(off_wb + 4 * static_cast<size_t>(n_free_words), 256);
+  const size_t off_fbytes = align_up(off_tasks + sizeof(ll::EvictTask) * tp, 256);  // page size 1
+  const size_t scratch = off_fbytes + (P == 1 ? 64 * static_cast<size_t>(n_words) : 0) + 256;
   ll_status rc = begin_call(p, st);
   if (rc) return rc;
   if ((rc = ensure_evict_buffers(p, scratch, readback))) return rc;
 
   Staging* sg = nullptr;
-  const size_t words_bytes = 8 * static_cast<size_t>(n_words);
+  const size_t words_bytes = 8 * static_cast<size_t>(n_free_words);
   if ((rc = stage_acquire(p, stage_bytes_for({es.size() * sizeof(ll::EvictSeq), words_bytes}), &sg))) return rc;
   const size_t o_es = stage_put(sg, es.data(), es.size() * sizeof(ll::EvictSeq));
   const size_t o_w = stage_put(sg, nullptr, words_bytes);
-  if (n_words) p->free.copy_words(reinterpret_cast<uint64_t*>(sg->host + o_w));
+  if (n_free_words) p->free.copy_words(reinterpret_cast<uint64_t*>(sg->host + o_w));
   if ((rc = upload(p, sg, st))) return rc;
 
   char* d = p->d_scratch;
@@ -793,10 +807,18 @@ ll_status evict_device_plan(ll_pool* p, const int32_t* seq_ids, int32_t n, const
   sc.reuse = reinterpret_cast<int32_t*>(d + off_reuse);
   sc.src_rows = reinterpret_cast<int32_t*>(d + off_src);
   sc.src_logical = reinterpret_cast<int32_t*>(d + off_logical);
+  sc.kept = reinterpret_cast<uint8_t*>(d + off_kept);
+  sc.freed = reinterpret_cast<unsigned long long*>(d + off_freed);
+  sc.freed_bytes = reinterpret_cast<uint8_t*>(d + off_fbytes);
+  const bool moves = P > 1;
+  // page size > 1 ORs freed pages into the bitmap; page size 1 marks bytes
+  hipError_t e = moves ? ll::launch_zero_words(sc.freed, n_words, st)
+                       : ll::launch_zero_words(reinterpret_cast<unsigned long long*>(sc.freed_bytes), 8 * n_words, st);
+  if (e != hipSuccess) return device_fail(p, e, "zero_words_kernel launch");
   ProfRec rec1{};
   ll::Stamp t1;
   if (prof_pick(p, 1) && (rc = prof_begin(p, &rec1, &t1))) return rc;
-  hipError_t e = ll::launch_keep_scan(sc, st, t1);
+  e = ll::launch_keep_scan(sc, st, t1);
   if (e != hipSuccess) return device_fail(p, e, "keep_scan_kernel launch");
   if (rec1.start) {
     rec1.bytes = total_rows + 4 * total_rows;
@@ -811,51 +833,109 @@ ll_status evict_device_plan(ll_pool* p, const int32_t* seq_ids, int32_t n, const
   al.reuse = sc.reuse;
   al.page_table = p->desc.page_table;
   al.max_pages_per_seq = p->desc.max_pages_per_seq;
-  al.n_words = n_words;
+  al.n_words = n_free_words;
   al.free_words = reinterpret_cast<const uint64_t*>(sg->dev + o_w);
   al.rank = reinterpret_cast<int32_t*>(d + off_rank);
   al.fresh_count = reinterpret_cast<int32_t*>(d + off_fc);
   al.fresh_base = reinterpret_cast<int32_t*>(d + off_fb);
+  al.moved_count = reinterpret_cast<int32_t*>(d + off_mv);
   al.word_base = reinterpret_cast<int32_t*>(d + off_wb);
   al.new_table = reinterpret_cast<int32_t*>(d + off_nt);
   al.tasks = reinterpret_cast<ll::EvictTask*>(d + off_tasks);
   al.info = reinterpret_cast<int32_t*>(d + off_info);
-  // kernel 0's record covers the page plan and the row moves of this path
+  // kernel 0's record: at page size 1 the new tables; above it the row moves
   ProfRec rec{};
   ll::Stamp t0;
   if (prof_pick(p, 0) && (rc = prof_begin(p, &rec, &t0))) return rc;
-  if ((e = ll::launch_alloc(al, st, ll::Stamp{t0.start, nullptr})) != hipSuccess)
-    return device_fail(p, e, "page allocator launch");
-
-  ll::DevMoveLaunch mv{};
-  mv.planes = reinterpret_cast<const ll::chunk_t* const*>(p->d_layers);
-  mv.num_planes = p->num_planes;
-  mv.page_shift = p->page_shift;
-  mv.row_chunks = static_cast<int32_t>(rc_chunks);
-  mv.tasks = al.tasks;
-  mv.info = al.info;
-  mv.src_rows = sc.src_rows;
-  const int64_t chunk_bound = P == 1 ? 0 : total_pages * P * rc_chunks;
-  if ((e = ll::launch_dev_move(mv, chunk_bound, st, ll::Stamp{nullptr, t0.stop})) != hipSuccess)
-    return device_fail(p, e, "dev_move_kernel launch");
-  int64_t prof_index = -1;
-  if (rec.start) {
-    rec.bytes = 0;  // known when the call settles
-    prof_end(p, 0, rec);
-    prof_index = static_cast<int64_t>(p->prof[0].size()) - 1;
+  if (!moves) {
+    // page size 1: the new tables are the kept rows' pages (src_rows)
+    ll::UnitPageLaunch up{};
+    up.seqs = sc.seqs;
+    up.n = n;
+    up.counts = sc.counts;
+    up.src_rows = sc.src_rows;
+    up.page_table = p->desc.page_table;
+    up.max_pages_per_seq = p->desc.max_pages_per_seq;
+    up.freed_bytes = sc.freed_bytes;
+    up.freed = sc.freed;
+    up.n_words = n_words;
+    up.info = al.info;
+    if ((e = ll::launch_unit_page(up, st, t0)) != hipSuccess) return device_fail(p, e, "unit_page_kernel launch");
+    e = hipMemcpyAsync(p->h_readback, d, readback, hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipEventRecord(p->pending.done, st);
+    if (e != hipSuccess) return device_fail(p, e, "eviction readback");
+    int64_t prof_index = -1;
+    if (rec.start) {
+      rec.bytes = 0;  // known when the call settles
+      prof_end(p, 0, rec);
+      prof_index = static_cast<int64_t>(p->prof[0].size()) - 1;
+    }
+    if ((rc = end_call(p, sg, st))) return rc;
+    ll_pool::PendingEvict& pe = p->pending;
+    pe.active = true;
+    pe.seq_ids.assign(seq_ids, seq_ids + n);
+    pe.off_info = off_info;
+    pe.off_freed = off_freed;
+    pe.n_words = n_words;
+    pe.prof_index = prof_index;
+    return LL_OK;
   }
+
+  // page size > 1: the verdict decides, then the exact grid
+  if ((e = ll::launch_alloc_scan(al, st)) != hipSuccess) return device_fail(p, e, "page allocator launch");
   e = hipMemcpyAsync(p->h_readback, d, readback, hipMemcpyDeviceToHost, st);
   if (e == hipSuccess) e = hipEventRecord(p->pending.done, st);
   if (e != hipSuccess) return device_fail(p, e, "eviction readback");
+  e = hipEventSynchronize(p->pending.done);
+  if (e != hipSuccess) return device_fail(p, e, "eviction readback");
+  const int64_t* counts = reinterpret_cast<const int64_t*>(p->h_readback);
+  const int32_t* info = reinterpret_cast<const int32_t*>(p->h_readback + off_info);
+  if (info[1]) {
+    // nothing has changed: the kernels so far wrote scratch only
+    if (rec.start) p->spare_events.insert(p->spare_events.end(), {rec.start, rec.stop});
+    if ((rc = end_call(p, sg, st))) return rc;
+    int64_t need = 0;
+    for (int32_t i = 0; i < n; ++i) need += ceil_div(counts[i], P);
+    return fail(LL_ENOMEM, "the eviction needs more fresh pages than the %lld free (at most %lld new pages)",
+                (long long)p->free.count(), (long long)need);
+  }
+  if (info[0] < 0 || info[0] > total_pages) return device_fail(p, hipErrorUnknown, "eviction verdict out of range");
+  if ((e = ll::launch_alloc_tables(al, st)) != hipSuccess) return device_fail(p, e, "page allocator launch");
+  const int64_t n_tasks = info[0];
+  if (p->gqa) {
+    ll::PlaneEvictLaunch a{};
+    a.planes = reinterpret_cast<const ll::chunk_t* const*>(p->d_layers);
+    a.num_planes = p->num_planes;
+    a.page_shift = p->page_shift;
+    a.row_chunks = static_cast<int32_t>(rc_chunks);
+    a.tasks = al.tasks;
+    a.n_tasks = n_tasks;
+    a.blocks_per_plane = ll::flat_blocks(n_tasks * P * rc_chunks);
+    a.src_rows = sc.src_rows;
+    a.n_twrites = 0;
+    e = ll::launch_plane_evict(a, st, t0);
+    if (e != hipSuccess) return device_fail(p, e, "plane_evict_kernel launch");
+  } else {
+    ll::EvictLaunch a{};
+    a.layers = reinterpret_cast<const ll::chunk_t* const*>(p->d_layers);
+    a.num_layers = p->desc.num_layers;
+    a.page_shift = p->page_shift;
+    a.tasks = al.tasks;
+    a.n_tasks = n_tasks;
+    a.blocks_per_layer = ll::flat_blocks(n_tasks * P * rc_chunks);
+    a.src_rows = sc.src_rows;
+    a.n_twrites = 0;
+    e = ll::launch_evict_move(a, st, t0);
+    if (e != hipSuccess) return device_fail(p, e, "evict_move_kernel launch");
+  }
   if ((rc = end_call(p, sg, st))) return rc;
-  ll_pool::PendingEvict& pe = p->pending;
-  pe.active = true;
-  pe.seq_ids.assign(seq_ids, seq_ids + n);
-  pe.reuse_off = reuse_off;
-  pe.off_info = off_info;
-  pe.off_table = off_nt;
-  pe.off_reuse = off_reuse;
-  pe.prof_index = prof_index;
+  if ((rc = apply_evict(p, seq_ids, static_cast<size_t>(n), counts, info,
+                        reinterpret_cast<const uint64_t*>(p->h_readback + off_freed), n_words, -1)))
+    return rc;
+  if (rec.start) {
+    rec.bytes = p->last.alg_bytes;
+    prof_end(p, 0, rec);
+  }
   return LL_OK;
 }
 
@@ -1137,6 +1217,8 @@ ll_status ll_seq_get(const ll_pool* p, int32_t seq, int64_t* len, int64_t* next_
   if (rc) return rc;
   if (seq < 0 || seq >= p->desc.max_seqs || !p->seqs[seq].used) return fail(LL_EINVAL, "unknown sequence %d", seq);
   if (cap > 0 && !pages_out) return fail(LL_EINVAL, "pages_out is NULL");
+  if (pages_out || n_pages_out)
+    if ((rc = fresh_table(const_cast<ll_pool*>(p), seq))) return rc;
   const SeqState& s = p->seqs[seq];
   if (len) *len = s.len;
   if (next_position) *next_position = s.next_pos;
@@ -1190,6 +1272,7 @@ ll_status ll_seq_set_pages(ll_pool* p, int32_t seq, const int32_t* pages, int64_
   const int64_t need = ceil_div(n_tokens, p->P);
   if (need > p->desc.max_pages_per_seq) return fail(LL_ERANGE, "%lld rows exceed the page-table row", (long long)n_tokens);
   if (need > 0 && !pages) return fail(LL_EINVAL, "pages is NULL");
+  if ((rc = fresh_table(p, seq))) return rc;
   SeqState& s = p->seqs[seq];
   // page_slot marks (reset before returning): -2 owned, -3 listed, -4 both
   std::vector<int32_t>& mark = p->page_slot;
@@ -1244,6 +1327,7 @@ ll_status ll_seq_free(ll_pool* p, int32_t seq) try {
   ll_status rc = enter(p);
   if (rc) return rc;
   if (seq < 0 || seq >= p->desc.max_seqs || !p->seqs[seq].used) return fail(LL_EINVAL, "unknown sequence %d", seq);
+  if ((rc = fresh_table(p, seq))) return rc;
   SeqState& s = p->seqs[seq];
   for (int32_t pg : s.pages) p->free.give(pg);
   s = SeqState();
@@ -1263,6 +1347,11 @@ static ll_status splice_impl(ll_pool* p, const ll_directive* dirs, int32_t n, vo
   if (n < 0 || (n > 0 && !dirs)) return fail(LL_EINVAL, "bad directive array");
   if (n == 0) return LL_OK;
   if ((rc = validate_directives(p, dirs, n))) return rc;
+  {
+    std::vector<int32_t> ids(static_cast<size_t>(n));
+    for (int32_t i = 0; i < n; ++i) ids[i] = dirs[i].seq_id;
+    if ((rc = fresh_tables(p, ids.data(), ids.size()))) return rc;
+  }
 
   // --- plan (host only, no state change yet)
   const int64_t P = p->P;
@@ -1642,224 +1731,26 @@ ll_status kv_evict_compact(ll_pool* p, const int32_t* seq_ids, int32_t n, const 
     seen[s] = 1;
     if (keep_offsets[i] < 0) return fail(LL_EINVAL, "entry %d: negative mask offset", i);
     total_rows += p->seqs[s].len;
-    total_pages += static_cast<int64_t>(p->seqs[s].pages.size());
+    total_pages += ceil_div(p->seqs[s].len, p->P);
   }
   if (total_rows > 0 && !keep_dev) return fail(LL_EINVAL, "keep mask is NULL");
-  const int64_t P = p->P;
   DeviceGuard g(p->desc.device);
   hipStream_t st = static_cast<hipStream_t>(stream);
-
   std::vector<ll::EvictSeq> es(static_cast<size_t>(n));
-  std::vector<int64_t> reuse_off(static_cast<size_t>(n)), src_off(static_cast<size_t>(n));
   {
     int64_t ro = 0, so = 0;
     for (int32_t i = 0; i < n; ++i) {
       const SeqState& s = p->seqs[seq_ids[i]];
       es[i].mask_off = keep_offsets[i];
       es[i].n_old = s.len;
-      es[i].src_off = src_off[i] = so;
-      es[i].reuse_off = reuse_off[i] = ro;
+      es[i].src_off = so;
+      es[i].reuse_off = ro;
       es[i].seq = seq_ids[i];
       so += s.len;
-      ro += static_cast<int64_t>(s.pages.size());
+      ro += ceil_div(s.len, p->P);
     }
   }
-  // When the free pages cover the worst case (every new page fresh; at page
-  // size 1 no page is ever fresh) the device makes the page plan and the call
-  // returns without waiting; otherwise the host makes it after one readback,
-  // so that a shortage is reported exactly.
-  if (P == 1 || p->free.count() >= total_pages)
-    return evict_device_plan(p, seq_ids, n, keep_dev, es, reuse_off, total_rows, total_pages, st);
-
-  // --- scratch: [counts (int64) n | reuse (int32) total_pages | src_rows (int32)
-  //     total_rows | src_logical (int32) total_rows]; the first two come back
-  const size_t off_reuse = align_up(8 * static_cast<size_t>(n), 256);
-  const size_t off_src = align_up(off_reuse + 4 * static_cast<size_t>(total_pages), 256);
-  const size_t off_logical = align_up(off_src + 4 * static_cast<size_t>(total_rows), 256);
-  const size_t scratch = off_logical + 4 * static_cast<size_t>(total_rows) + 256;
-  const size_t readback = off_src;
-  if ((rc = begin_call(p, st))) return rc;
-  if (scratch > p->scratch_cap || readback > p->readback_cap) {
-    if ((rc = wait_idle(p))) return rc;
-    if (scratch > p->scratch_cap) {
-      if (p->d_scratch) (void)hipFree(p->d_scratch);
-      p->d_scratch = nullptr;
-      p->scratch_cap = 0;
-      if (hipMalloc(reinterpret_cast<void**>(&p->d_scratch), scratch) != hipSuccess)
-        return fail(LL_ENOMEM, "cannot allocate %zu bytes of eviction scratch", scratch);
-      p->scratch_cap = scratch;
-    }
-    if (readback > p->readback_cap) {
-      if (p->h_readback) (void)hipHostFree(p->h_readback);
-      p->h_readback = nullptr;
-      p->readback_cap = 0;
-      if (hipHostMalloc(reinterpret_cast<void**>(&p->h_readback), readback, hipHostMallocDefault) != hipSuccess)
-        return fail(LL_ENOMEM, "cannot allocate %zu bytes of pinned readback", readback);
-      p->readback_cap = readback;
-    }
-  }
-
-  Staging* s1 = nullptr;
-  if ((rc = stage_acquire(p, stage_bytes_for({es.size() * sizeof(ll::EvictSeq)}), &s1))) return rc;
-  const size_t o_es = stage_put(s1, es.data(), es.size() * sizeof(ll::EvictSeq));
-  if ((rc = upload(p, s1, st))) return rc;
-  ll::ScanLaunch sc{};
-  sc.keep = keep_dev;
-  sc.seqs = reinterpret_cast<const ll::EvictSeq*>(s1->dev + o_es);
-  sc.n_seqs = n;
-  sc.page_shift = p->page_shift;
-  sc.page_table = p->desc.page_table;
-  sc.max_pages_per_seq = p->desc.max_pages_per_seq;
-  sc.counts = reinterpret_cast<int64_t*>(p->d_scratch);
-  sc.reuse = reinterpret_cast<int32_t*>(p->d_scratch + off_reuse);
-  sc.src_rows = reinterpret_cast<int32_t*>(p->d_scratch + off_src);
-  sc.src_logical = reinterpret_cast<int32_t*>(p->d_scratch + off_logical);
-  ProfRec rec1{};
-  ll::Stamp t1;
-  if (prof_pick(p, 1) && (rc = prof_begin(p, &rec1, &t1))) return rc;
-  hipError_t e = ll::launch_keep_scan(sc, st, t1);
-  if (e != hipSuccess) return fail(LL_EDEVICE, "keep_scan_kernel launch: %s", hipGetErrorString(e));
-  if (rec1.start) {
-    rec1.bytes = total_rows + 4 * total_rows;
-    prof_end(p, 1, rec1);
-  }
-  e = hipMemcpyAsync(p->h_readback, p->d_scratch, readback, hipMemcpyDeviceToHost, st);
-  if (e != hipSuccess) return fail(LL_EDEVICE, "eviction readback: %s", hipGetErrorString(e));
-  if ((rc = end_call(p, s1, st))) return rc;
-  // the host reads the readback next: wait on an event with the system fence
-  e = hipEventRecord(p->readback_ev, st);
-  if (e == hipSuccess) e = hipEventSynchronize(p->readback_ev);
-  if (e != hipSuccess) return fail(LL_EDEVICE, "eviction readback: %s", hipGetErrorString(e));
-  // Nothing has changed yet: the scan only wrote scratch.
-
-  const int64_t* counts = reinterpret_cast<const int64_t*>(p->h_readback);
-  const int32_t* reuse = reinterpret_cast<const int32_t*>(p->h_readback + off_reuse);
-  int64_t need = 0;
-  std::vector<int64_t> n_new(static_cast<size_t>(n));
-  for (int32_t i = 0; i < n; ++i) {
-    const SeqState& s = p->seqs[seq_ids[i]];
-    n_new[i] = counts[i];
-    if (n_new[i] < 0 || n_new[i] > s.len) return fail(LL_EDEVICE, "keep scan returned a bad count");
-    const int64_t pages = ceil_div(n_new[i], P);
-    int64_t prev = -1;
-    for (int64_t q = 0; q < pages; ++q) {
-      const int32_t x = reuse[reuse_off[i] + q];
-      if (x < 0) {
-        ++need;
-        continue;
-      }
-      if (x <= prev || x >= static_cast<int64_t>(s.pages.size())) return fail(LL_EDEVICE, "keep scan returned a bad page plan");
-      prev = x;
-    }
-  }
-  if (need > p->free.count())
-    return fail(LL_ENOMEM, "need %lld fresh pages, %lld free", (long long)need, (long long)p->free.count());
-  std::vector<int32_t> fresh;
-  p->free.lowest(need, fresh);
-
-  std::vector<ll::EvictTask> tasks;
-  TablePlan tp;
-  std::vector<std::vector<int32_t>> new_tables(static_cast<size_t>(n));
-  std::vector<std::vector<char>> kept(static_cast<size_t>(n));
-  ll_plan_stats stats{};
-  size_t cursor = 0;
-  for (int32_t i = 0; i < n; ++i) {
-    const SeqState& s = p->seqs[seq_ids[i]];
-    const int64_t pages = ceil_div(n_new[i], P);
-    std::vector<int32_t>& nt = new_tables[i];
-    nt.resize(static_cast<size_t>(pages));
-    kept[i].assign(s.pages.size(), 0);
-    for (int64_t q = 0; q < pages; ++q) {
-      const int32_t x = reuse[reuse_off[i] + q];
-      if (x >= 0) {
-        nt[q] = s.pages[x];
-        kept[i][x] = 1;
-        continue;
-      }
-      nt[q] = fresh[cursor++];
-      ll::EvictTask t{};
-      t.src_off = src_off[i];
-      t.q = static_cast<int32_t>(q);
-      t.dst_page = nt[q];
-      t.n_new = static_cast<int32_t>(n_new[i]);
-      tasks.push_back(t);
-      stats.rows_moved += std::min(P, n_new[i] - q * P);
-    }
-    for (char k : kept[i]) stats.freed_pages += k ? 0 : 1;
-    tp.add(seq_ids[i], nt);
-  }
-  stats.fresh_pages = need;
-  stats.table_entries = static_cast<int64_t>(tp.packed.size());
-  stats.alg_bytes = p->num_planes * 2 * p->row_bytes * stats.rows_moved;
-  if (static_cast<int64_t>(tasks.size()) * P * (p->row_bytes / 16) >= (int64_t{1} << 32) - 1024)
-    return fail(LL_EUNSUPPORTED, "one eviction may move at most 2^32 16-byte chunks per layer");
-
-  Staging* s2 = nullptr;
-  rc = stage_acquire(p, stage_bytes_for({tasks.size() * sizeof(ll::EvictTask), tp.writes.size() * sizeof(ll::TableWrite),
-                                         tp.packed.size() * 4}),
-                     &s2);
-  if (rc) return rc;
-  const size_t o_t = stage_put(s2, tasks.data(), tasks.size() * sizeof(ll::EvictTask));
-  const size_t o_w = stage_put(s2, tp.writes.data(), tp.writes.size() * sizeof(ll::TableWrite));
-  const size_t o_p = stage_put(s2, tp.packed.data(), tp.packed.size() * 4);
-  if ((rc = upload(p, s2, st))) return rc;
-  const int64_t row_chunks = p->row_bytes / 16;
-  const int64_t n_tasks = static_cast<int64_t>(tasks.size());
-  ProfRec rec{};
-  ll::Stamp ts;
-  if (p->gqa) {
-    ll::PlaneEvictLaunch a{};
-    a.planes = reinterpret_cast<const ll::chunk_t* const*>(p->d_layers);
-    a.num_planes = p->num_planes;
-    a.page_shift = p->page_shift;
-    a.row_chunks = static_cast<int32_t>(row_chunks);
-    a.tasks = reinterpret_cast<const ll::EvictTask*>(s2->dev + o_t);
-    a.n_tasks = n_tasks;
-    a.blocks_per_plane = ll::flat_blocks(n_tasks * P * row_chunks);
-    a.src_rows = sc.src_rows;
-    a.twrites = reinterpret_cast<const ll::TableWrite*>(s2->dev + o_w);
-    a.tables = reinterpret_cast<const int32_t*>(s2->dev + o_p);
-    a.n_twrites = static_cast<int32_t>(tp.writes.size());
-    a.max_pages_per_seq = p->desc.max_pages_per_seq;
-    a.page_table = p->desc.page_table;
-    if (prof_pick(p, 0) && (rc = prof_begin(p, &rec, &ts))) return rc;
-    e = ll::launch_plane_evict(a, st, ts);
-    if (e != hipSuccess) return device_fail(p, e, "plane_evict_kernel launch");
-  } else {
-    ll::EvictLaunch a{};
-    a.layers = reinterpret_cast<const ll::chunk_t* const*>(p->d_layers);
-    a.num_layers = p->desc.num_layers;
-    a.page_shift = p->page_shift;
-    a.tasks = reinterpret_cast<const ll::EvictTask*>(s2->dev + o_t);
-    a.n_tasks = n_tasks;
-    a.blocks_per_layer = ll::flat_blocks(n_tasks * P * row_chunks);
-    a.src_rows = sc.src_rows;
-    a.twrites = reinterpret_cast<const ll::TableWrite*>(s2->dev + o_w);
-    a.tables = reinterpret_cast<const int32_t*>(s2->dev + o_p);
-    a.n_twrites = static_cast<int32_t>(tp.writes.size());
-    a.max_pages_per_seq = p->desc.max_pages_per_seq;
-    a.page_table = p->desc.page_table;
-    if (prof_pick(p, 0) && (rc = prof_begin(p, &rec, &ts))) return rc;
-    e = ll::launch_evict_move(a, st, ts);
-    if (e != hipSuccess) return device_fail(p, e, "evict_move_kernel launch");
-  }
-  if (rec.start) {
-    rec.bytes = stats.alg_bytes + 4 * stats.table_entries;
-    prof_end(p, 0, rec);
-  }
-  if ((rc = end_call(p, s2, st))) return rc;
-
-  for (int32_t pg : fresh) p->free.take(pg);
-  p->free.advance_hint();
-  for (int32_t i = 0; i < n; ++i) {
-    SeqState& s = p->seqs[seq_ids[i]];
-    for (size_t k = 0; k < kept[i].size(); ++k)
-      if (!kept[i][k]) p->free.give(s.pages[k]);
-    s.pages = std::move(new_tables[i]);
-    s.len = n_new[i];
-  }
-  p->last = stats;
-  return LL_OK;
+  return evict_device_plan(p, seq_ids, n, keep_dev, es, total_rows, total_pages, st);
 } catch (...) {
   return host_exception(p);
 }
@@ -1869,6 +1760,7 @@ ll_status ll_ptable_reindex(ll_pool* p, int32_t seq, const int32_t* keep_pages, 
   if (rc) return rc;
   if (seq < 0 || seq >= p->desc.max_seqs || !p->seqs[seq].used) return fail(LL_EINVAL, "unknown sequence %d", seq);
   if (n_keep < 0 || (n_keep > 0 && !keep_pages)) return fail(LL_EINVAL, "bad keep_pages");
+  if ((rc = fresh_table(p, seq))) return rc;
   SeqState& s = p->seqs[seq];
   const int64_t P = p->P;
   const int64_t old_pages = static_cast<int64_t>(s.pages.size());
@@ -1912,6 +1804,7 @@ ll_status ll_rope_rows(ll_pool* p, int32_t seq, int64_t row_begin, int64_t n_row
   ll_status rc = enter(p);
   if (rc) return rc;
   if (seq < 0 || seq >= p->desc.max_seqs || !p->seqs[seq].used) return fail(LL_EINVAL, "unknown sequence %d", seq);
+  if ((rc = fresh_table(p, seq))) return rc;
   const SeqState& s = p->seqs[seq];
   if (row_begin < 0 || n_rows < 0 || row_begin + n_rows > s.len)
     return fail(LL_EINVAL, "rows [%lld, %lld) outside the sequence's %lld rows", (long long)row_begin,

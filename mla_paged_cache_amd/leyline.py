@@ -125,18 +125,18 @@ def _load():
         "ll_pool_create_gqa": (i32, [P(_GqaPoolDesc), P(vp)]),
         "ll_pool_destroy": (None, [vp]),
         "ll_seq_alloc": (i32, [vp, i64, P(i32), vp]),
-        "ll_seq_set_pages": (i32, [vp, i32, P(i32), i64, vp]),
+        "ll_seq_set_pages": (i32, [vp, i32, vp, i64, vp]),
         "ll_seq_free": (i32, [vp, i32]),
         "ll_seq_get": (i32, [vp, i32, P(i64), P(i64), P(i32), i32, P(i32)]),
         "ll_pool_free_pages": (i32, [vp, P(i64)]),
         "leyline_splice": (i32, [vp, P(_Directive), i32, vp]),
         "leyline_splice_noalloc": (i32, [vp, P(_Directive), i32, vp]),
-        "kv_evict_compact": (i32, [vp, P(i32), i32, vp, P(i64), vp]),
-        "ll_ptable_reindex": (i32, [vp, i32, P(i32), i32, vp]),
+        "kv_evict_compact": (i32, [vp, vp, i32, vp, vp, vp]),
+        "ll_ptable_reindex": (i32, [vp, i32, vp, i32, vp]),
         "ll_rope_delta_table": (i32, [ctypes.c_double, i32, i64, P(ctypes.c_float), P(ctypes.c_float)]),
         "ll_last_plan_stats": (i32, [vp, P(_PlanStats)]),
         "ll_last_plan_bytes": (i32, [vp, P(i64), P(i64), P(i64)]),
-        "ll_seq_lengths": (i32, [vp, P(i32), i32, P(i64)]),
+        "ll_seq_lengths": (i32, [vp, vp, i32, vp]),
         "ll_pool_set_profiling": (i32, [vp, i32]),
         "ll_pool_set_splice_planner": (i32, [vp, i32]),
         "ll_profile_read": (i32, [vp, i32, P(i64), P(ctypes.c_double), P(i64), P(ctypes.c_float), i64]),
@@ -169,8 +169,13 @@ def _check(status: int) -> None:
 
 
 def _i32_array(values):
-    a = np.ascontiguousarray(np.asarray(values, dtype=np.int32))
-    return a, a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    """(contiguous int32 array, its address); an int32 ndarray that is
+    already contiguous is used as it is."""
+    if isinstance(values, np.ndarray) and values.dtype == np.int32 and values.flags.c_contiguous:
+        a = values.reshape(-1)
+    else:
+        a = np.ascontiguousarray(np.asarray(values, dtype=np.int32)).reshape(-1)
+    return a, (a.ctypes.data if a.size else None)
 
 
 def _require(t, name: str, dtype, shape, device) -> None:
@@ -356,12 +361,14 @@ class Pool:
                 or not keep.is_contiguous():
             raise ValueError(f"keep must be a contiguous uint8 tensor on {self.device}")
         s_arr, s_ptr = _i32_array(seqs)
-        o_arr = np.ascontiguousarray(np.asarray(offsets, dtype=np.int64).reshape(-1))
+        o_arr = offsets if isinstance(offsets, np.ndarray) and offsets.dtype == np.int64 and offsets.flags.c_contiguous \
+            else np.ascontiguousarray(np.asarray(offsets, dtype=np.int64))
+        o_arr = o_arr.reshape(-1)
         if len(o_arr) != len(s_arr):
             raise ValueError(f"{len(s_arr)} sequences but {len(o_arr)} mask offsets")
         if len(s_arr):
-            lens = np.zeros(len(s_arr), np.int64)
-            _check(_lib.ll_seq_lengths(self._h, s_ptr, len(s_arr), lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))))
+            lens = np.empty(len(s_arr), np.int64)
+            _check(_lib.ll_seq_lengths(self._h, s_ptr, len(s_arr), lens.ctypes.data))
             # a negative offset is the library's to refuse (LL_EINVAL)
             past = (o_arr >= 0) & (o_arr + lens > keep.numel())
             if past.any():
@@ -369,8 +376,7 @@ class Pool:
                 raise ValueError(f"mask of sequence {int(s_arr[i])}: bytes [{int(o_arr[i])}, {int(o_arr[i] + lens[i])}) "
                                  f"outside keep's {keep.numel()}")
         _check(_lib.kv_evict_compact(self._h, s_ptr, len(s_arr), keep.data_ptr(),
-                                     o_arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
-                                     _stream_handle(stream, self._dev)))
+                                     o_arr.ctypes.data if len(o_arr) else None, _stream_handle(stream, self._dev)))
 
     def rope_rows(self, seq: int, row_begin: int, angles, out=None, stream=None):
         """Turn the RoPE bands of rows [row_begin, row_begin + len(angles)) of

@@ -36,18 +36,19 @@ def _rollouts(L, n_roll, n_tok, P, seed, extra_pages=None, oracle_layers=None, h
 
 @pytest.mark.parametrize("P", [16, 1])
 @pytest.mark.parametrize("kind", ["sliding", "turns"])
-@pytest.mark.parametrize("plan", ["device", "host"])
-def test_evict_rollouts_full_compare(P, kind, plan):
+@pytest.mark.parametrize("free", ["plenty", "tight"])
+def test_evict_rollouts_full_compare(P, kind, free):
     """8 rollouts x 16384 tokens x 2 layers; keep masks: drop the oldest half,
-    or drop random turns of 200..2000 tokens with probability 1/2.  With free
-    pages for every page of the rollouts the device makes the page plan (the
-    call does not wait); with fewer (page size 16 only) the host makes it
-    after one readback.  Both must give the oracle's plan."""
-    if plan == "host" and P == 1:
-        pytest.skip("at page size 1 the device always makes the plan")
-    say(f"evict 8 x 16384 x 2, P={P}, {kind}, {plan} plan")
+    or drop random turns of 200..2000 tokens with probability 1/2.  The device
+    makes the page plan; with free pages for every page of the rollouts or
+    with fewer (page size 16 only: then a shortage is possible and the call
+    reads the device's verdict before it goes on).  Both must give the
+    oracle's plan."""
+    if free == "tight" and P == 1:
+        pytest.skip("at page size 1 no page is ever fresh")
+    say(f"evict 8 x 16384 x 2, P={P}, {kind}, {free} free pages")
     pages_per = 16384 // P
-    dp = _rollouts(2, 8, 16384, P, seed=3, extra_pages=None if plan == "device" else 8 * pages_per * 3 // 4)
+    dp = _rollouts(2, 8, 16384, P, seed=3, extra_pages=None if free == "plenty" else 8 * pages_per * 3 // 4)
     dp.snapshot_rows()
     rng = np_rng(3, 5)
     masks = [sliding_window_mask(16384, 8192) if kind == "sliding" else turn_drop_mask(rng, 16384)

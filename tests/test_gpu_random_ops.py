@@ -32,8 +32,9 @@ class Mirror:
         self.L = need_gpu()
         self.P = P
         # about 1600 rows: five sequences of up to 700 rows do not all fit, so
-        # allocations and splices get refused and evictions fall back to the
-        # host page plan now and then
+        # allocations and splices get refused and evictions now and then find
+        # fewer free pages than their worst case (the call then reads the
+        # device's verdict before it goes on)
         self.num_pages = {1: 1600, 4: 400, 16: 100}[P]
         self.max_pages = -(-MAX_LEN * 2 // P)
         self.dp = self.make_pool(seed)
@@ -203,7 +204,7 @@ class Mirror:
         dev = torch.from_numpy(keep).cuda() if len(keep) else torch.zeros(16, dtype=torch.uint8, device="cuda")
         self.keep_alive.append(dev)
         if self.P > 1 and len(self.state.free) < sum(len(self.state.tables[s]) for s in seqs):
-            self.host_plans += 1   # the library plans on the host (see kv_evict_compact)
+            self.host_plans += 1   # a shortage was possible: the call waited for the verdict
         try:
             expected, _ = O.evict(self.state, seqs, masks)
         except O.OracleError:
@@ -231,7 +232,7 @@ class Mirror:
     def pressure(self):
         """A full pool: an allocation and a splice that need more pages than
         are free are refused with nothing changed; an eviction whose worst
-        case exceeds the free pages is planned on the host and succeeds."""
+        case exceeds the free pages succeeds after reading the verdict."""
         for s in sorted(self.live):
             self.dp.pool.seq_free(s)
             self.state.free |= set(self.state.tables.pop(s))
