@@ -97,7 +97,7 @@ def parse():
 # The source file of each measured kernel; its hash also covers the shared
 # device helpers and the launch structures.
 KERNEL_SOURCE = {"splice_kernel": "kernels.hip", "splice_inplace_kernel": "kernels.hip",
-                 "evict_move_kernel": "kernels.hip",
+                 "evict_move_kernel": "kernels.hip", "unit_page_kernel": "kernels.hip",
                  "gqa_splice_kernel": "kernels_gqa.hip", "plane_evict_kernel": "kernels_gqa.hip",
                  "kvs_dense_ev_kernel": "kernels_kvs.hip", "rope_rows_kernel": "kernels_rows.hip",
                  "rope_gather_mla_kernel": "kernels_rows.hip", "rope_inplace_mla_kernel": "kernels_rows.hip"}
@@ -452,15 +452,22 @@ def bench_splice_32k(args, STUB=24, workload="splice_32k_27layer", kernel="splic
         phys = torch.from_numpy(new_table.astype(np.int64)[j // PAGE] * PAGE + j % PAGE).to(dev)
         gpu_after = data.view(LAYERS, -1, ROW)[:, phys].view(torch.int16).cpu().numpy().view(np.uint16)
 
-    def timed(run, n):
+    device_ms = {}
+
+    def timed(run, n, tag=None):
         torch.cuda.synchronize()
         quiet_gc()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
+        e0.record()
         for i in range(n):
             run(i)
+        e1.record()
         torch.cuda.synchronize()
         t1 = time.perf_counter()
         gc.enable()
+        if tag:
+            device_ms[tag] = e0.elapsed_time(e1) / n
         return (t1 - t0) * 1e3 / n
 
     def restore_step(_):
@@ -481,7 +488,7 @@ def bench_splice_32k(args, STUB=24, workload="splice_32k_27layer", kernel="splic
     step = distinct_step if distinct else restore_step
     if distinct:
         set_all()
-    ms_per_step = timed(step, args.steps)
+    ms_per_step = timed(step, args.steps, "step")
     value = alg_bytes / (ms_per_step * 1e-3) / 1e9
     # the row kernel's own time: a separate pass with every launch stamped
     launches, kernel_ms, kernel_bytes, samples = kernel_pass(torch, pool, 0, step, args.steps,
@@ -520,6 +527,10 @@ def bench_splice_32k(args, STUB=24, workload="splice_32k_27layer", kernel="splic
                                       f"{MAX_DISTINCT_SEQS} distinct sequences)",
         "pool_pages": POOL_PAGES})
     out["pct_hbm_peak"] = round(100.0 * value / HBM_PEAK_GBS, 2)
+    # the same loop on the device's clock: one event pair around all the calls
+    # (the events sit on the pool's stream; the first call's host time is
+    # inside the span)
+    out["step_device_us"] = round(device_ms["step"] * 1e3, 2)
     out["step_with_table_restore_ms"] = round(ms_restore, 5)
     if ms_host_plan is not None:
         out["step_host_staged_plan_ms"] = round(ms_host_plan, 5)
@@ -866,57 +877,91 @@ def cpu_baseline_layer_parallel(T, alg_bytes, seconds, LAYERS, TOKENS, PAGE, POO
 def bench_splice_batched(args):
     """16 sequences x 32768 tokens x 27 layers in one pool, one random
     directive each (span U[256,8192], stub U[8,64], start U[1024,len-span]),
-    applied in one call."""
+    applied in one call.  As in the headline, every timed step splices
+    sequences of its own: the pool holds SETS sets of 16 such sequences, each
+    sequence on a random permutation of its own 2048 pages, above a spare
+    region that holds every step's fresh pages.  The tables are restored only
+    after every SETS steps, outside the timed region (which adds up exactly
+    `steps` calls)."""
     import torch
     from mla_paged_cache_amd import leyline as L
     from synth import draw_span, np_rng, permuted_pages, random_rows_torch
 
     LAYERS, TOKENS, PAGE, SEQS = 27, 32768, 16, 16
     per = TOKENS // PAGE
-    POOL_PAGES = 2 * SEQS * per
-    dev = torch.device("cuda:0")
-    data = random_rows_torch(0, (LAYERS, POOL_PAGES, PAGE, ROW), dev)
-    table = torch.full((SEQS, per + 8), -1, dtype=torch.int32, device=dev)
-    pool = L.Pool(data, table)
-    perm = permuted_pages(0, SEQS * per)
     rng = np_rng(0, 4)
-    dirs, spans = [], []
-    for s in range(SEQS):
-        d = draw_span(rng, TOKENS, 256, 8192, 8, 64)
-        stub = random_rows_torch(100 + s, (LAYERS, d.r_len, ROW), dev)
-        dirs.append(L.Directive(s, d.s_start, d.s_end, stub))
-        spans.append((d.s_start, d.s_end, d.r_len))
+    draws = [draw_span(rng, TOKENS, 256, 8192, 8, 64) for _ in range(SEQS)]
+    # fresh pages of one set, at most: every new page from the one holding s_start
+    fresh_bound = sum(-(-(TOKENS + d.r_len - (d.s_end - d.s_start)) // PAGE) - d.s_start // PAGE for d in draws)
+    page_bytes = LAYERS * PAGE * ROW * 2
+    SETS = max(1, min(args.steps, 6, int(160e9 // ((SEQS * per + fresh_bound) * page_bytes))))
+    SPARE = SETS * fresh_bound
+    POOL_PAGES = SPARE + SETS * SEQS * per
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    data = torch.empty((LAYERS, POOL_PAGES, PAGE, ROW), dtype=torch.bfloat16, device=dev)
+    data[:, :SPARE].zero_()
+    for k in range(SETS):
+        lo = SPARE + k * SEQS * per
+        data[:, lo:lo + SEQS * per] = random_rows_torch(k, (LAYERS, SEQS * per, PAGE, ROW), dev)
+    table = torch.full((SETS * SEQS, per + 8), -1, dtype=torch.int32, device=dev)
+    pool = L.Pool(data, table)
+    tables = [permuted_pages(i, per, start=SPARE + i * per) for i in range(SETS * SEQS)]
+    stubs = [random_rows_torch(100 + s, (LAYERS, d.r_len, ROW), dev) for s, d in enumerate(draws)]
+    dirs = [[L.Directive(k * SEQS + s, d.s_start, d.s_end, stubs[s]) for s, d in enumerate(draws)]
+            for k in range(SETS)]
+    spans = [(d.s_start, d.s_end, d.r_len) for d in draws]
 
     def restore():
-        for s in range(SEQS):
-            pool.seq_set_pages(s, perm[s * per:(s + 1) * per], TOKENS)
+        for i in range(SETS * SEQS):
+            pool.seq_set_pages(i, tables[i], TOKENS)
+        torch.cuda.synchronize()
 
     restore()
-    pool.splice(dirs)
+    pool.splice(dirs[0])
     torch.cuda.synchronize()
-    alg_bytes = pool.last_stats().alg_bytes
-    for _ in range(args.warmup):
-        restore()
-        pool.splice(dirs)
-    torch.cuda.synchronize()
-    quiet_gc()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        restore()
-        pool.splice(dirs)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    gc.enable()
+    st = pool.last_stats()
+    alg_bytes = st.alg_bytes
+    assert st.planned_on_device == 1 and st.fresh_pages <= fresh_bound, st
 
-    def step(_):
-        restore()
-        pool.splice(dirs)
+    def chunks(n, run, after=None):
+        """n calls, SETS at a time after a restore; returns the seconds spent
+        inside the chunks (restores excluded)."""
+        spent, done = 0.0, 0
+        while done < n:
+            m = min(SETS, n - done)
+            restore()
+            quiet_gc()
+            t0 = time.perf_counter()
+            for k in range(m):
+                run(k)
+            torch.cuda.synchronize()
+            spent += time.perf_counter() - t0
+            gc.enable()
+            if after is not None:
+                after()
+            done += m
+        return spent
 
-    launches, kernel_ms, kernel_bytes, samples = kernel_pass(torch, pool, 0, step, args.steps)
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    def step(k):
+        pool.splice(dirs[k])
+
+    chunks(args.warmup, step)
+    spent = chunks(args.steps, step)
+    # kernel pass: every launch of the row kernel stamped, same chunks
+    pool.profile_read(0)
+    torch.cuda.synchronize()
+    pool.set_profiling(True, 1)
+    chunks(args.steps, step)
+    pool.set_profiling(False)
+    launches, kernel_ms, kernel_bytes, samples = pool.profile_read(0, samples=args.steps + 8)
+    ms_per_step = spent * 1e3 / args.steps
     out = base_line(args, "splice_16x32k_27layer", alg_bytes / (ms_per_step * 1e-3) / 1e9, ms_per_step, {
         "layers": LAYERS, "tokens": TOKENS, "sequences": SEQS, "page_size": PAGE, "pool_pages": POOL_PAGES,
-        "alg_bytes_per_step": alg_bytes, "restore_in_step": "16 page-table rows"})
+        "sets": SETS, "alg_bytes_per_step": alg_bytes,
+        "layout": "each sequence on a random permutation of its own 2048 pages; fresh pages from a spare region",
+        "step": f"one 16-directive splice call on a set of its own; tables restored after every {SETS} calls, "
+                f"outside the timed region"})
     out["roofline"] = roofline("splice_kernel", "splice_16x32k_27layer", launches, kernel_ms, kernel_bytes, samples)
     out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline_batched(
         spans, args.cpu_seconds, LAYERS, TOKENS, PAGE)
@@ -1222,11 +1267,10 @@ def bench_evict(args, page):
         "page_plan": "device",
         "step": "one kv_evict_compact call until its device work and host bookkeeping are done, median"})
     out["metric"] = "KV-streams eviction: row bytes moved GB/s; call latency"
-    out["roofline"] = roofline("evict_move_kernel", name, launches, kernel_ms, kernel_bytes, samples)
-    if page == 1:
-        # nothing moves at page size 1: the timed kernel writes the new tables
-        # and packs the freed-page bitmap
-        out["roofline"]["kernel"] = "unit_page_kernel (new page tables + freed-page bitmap)"
+    # nothing moves at page size 1: the timed kernel writes the new tables and
+    # packs the freed-page bitmap
+    out["roofline"] = roofline("evict_move_kernel" if page > 1 else "unit_page_kernel", name, launches,
+                               kernel_ms, kernel_bytes, samples)
     out["step_us"] = {"median": round(1e6 * statistics.median(times), 1), "p10": round(1e6 * pct(times, 10), 1),
                       "p90": round(1e6 * pct(times, 90), 1)}
     out["keep_scan_us"] = round(scan_ms * 1e3 / max(1, s_launches), 2)

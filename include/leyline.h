@@ -281,17 +281,18 @@ ll_status leyline_splice_noalloc(ll_pool* pool, const ll_directive* dirs, int32_
  * array).  A device prefix scan gives each kept row its new index; rows move
  * only where a new page cannot reuse an old one (at page size 1 none move).
  *
- * Page plan.  When the free pages cover the worst case (every new page of the
- * batch fresh; at page size 1 no page is ever fresh) the device makes the
- * plan -- fresh pages are the lowest free pages in (batch position, page)
- * order, found by rank/select on the free bitmap -- and writes the rows and
- * page tables; the call returns without waiting and the pool's host
- * bookkeeping (lengths, tables, free set, ll_last_plan_stats) catches up at
- * the start of the next call on the pool (above 256 Ki old pages it briefly
- * uses up to 8 host threads for that).  Otherwise the call waits once for
- * a small device-to-host copy of the per-page plan inputs and the host makes
- * the same plan, so that a shortage returns LL_ENOMEM with nothing changed.
- * Errors: LL_EINVAL, LL_ENOMEM, LL_EDEVICE. */
+ * Page plan, always made on the device: fresh pages are the lowest free
+ * pages in (batch position, page) order, found by rank/select on the free
+ * bitmap.  Page size > 1: the call waits once for a small device-to-host
+ * copy of the device's verdict (fresh pages needed, and whether they exceed
+ * the free ones); a shortage returns LL_ENOMEM with nothing changed,
+ * otherwise the rows move and the tables are rewritten on the device and the
+ * call returns without waiting for them.  Page size 1 (nothing moves, no
+ * page is fresh): the call returns without waiting at all, and the pool's
+ * host bookkeeping (lengths, free set, ll_last_plan_stats) catches up when
+ * the pool is next used.  Host copies of the rewritten page tables are
+ * fetched from the device only when read (ll_seq_get, a later call on that
+ * sequence).  Errors: LL_EINVAL, LL_ENOMEM, LL_EDEVICE. */
 ll_status kv_evict_compact(ll_pool* pool, const int32_t* seq_ids, int32_t n,
                            const uint8_t* keep_dev, const int64_t* keep_offsets, void* stream);
 
@@ -420,9 +421,14 @@ void kvs_ctx_destroy(kvs_ctx* ctx);
  * event's time when keep byte i is 0.  status_dev[i] is
  * 0, or 1 when some event's mask_len differs from the number of rows the
  * cache held at that time (the rollout's death times are then unspecified).
- * The host arrays are read before the call returns; the call first waits
- * for the previous kvs_death_times call of the same context to finish on the
- * device (it reuses that call's staging).  Errors: LL_EINVAL
+ * The host arrays are read before the call returns.  The context stages
+ * the logs in four regions taken in turn; a call waits on the host only when
+ * its region's last user (the call four calls earlier) has not finished.
+ * When n_pad token ids do not fit in a block's LDS (n_pad above about 40 000
+ * on this device) the replay keeps them in a context-owned scratch of
+ * n * n_pad int32: a call on another stream then waits on the device for the
+ * last such call, and one that must grow the scratch waits on the host.
+ * Errors: LL_EINVAL
  * (n_pad outside [1, 2^31 - 2], n_tokens > n_pad, event times not increasing
  * inside (0, n_tokens], mask_len outside [0, time], NULL pointers),
  * LL_ENOMEM, LL_EDEVICE. */

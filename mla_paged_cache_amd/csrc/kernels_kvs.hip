@@ -534,17 +534,15 @@ __global__ __launch_bounds__(256) void kvs_dense_ev_kernel(KvsDenseLaunch a) {
 
 }  // namespace
 
+bool kvs_death_list_in_lds(int64_t n_pad, int max_lds) {
+  const int64_t static_lds = int64_t{kPerThread} * kDeathWaves * 4 + 16;
+  return n_pad * 4 + static_lds <= max_lds;
+}
+
 hipError_t launch_kvs_death(const KvsDeathLaunch& a, hipStream_t s) {
   if (a.n == 0) return hipSuccess;
-  // the list in LDS when n_pad entries fit beside the kernel's static LDS
-  int dev = 0, max_lds = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e == hipSuccess) e = hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
-  if (e != hipSuccess) return e;
-  const int64_t static_lds = int64_t{kPerThread} * kDeathWaves * 4 + 16;
-  const int64_t list_bytes = a.n_pad * 4;
-  if (list_bytes + static_lds <= max_lds)
-    kvs_death_kernel<true><<<dim3(a.n), dim3(kDeathThreads), static_cast<size_t>(list_bytes), s>>>(a);
+  if (a.list_in_lds)
+    kvs_death_kernel<true><<<dim3(a.n), dim3(kDeathThreads), static_cast<size_t>(a.n_pad * 4), s>>>(a);
   else
     kvs_death_kernel<false><<<dim3(a.n), dim3(kDeathThreads), 0, s>>>(a);
   return hipGetLastError();

@@ -29,10 +29,16 @@ struct KvsDeathLaunch {
   const uint8_t* keep;
   int32_t* death;        // [n][n_pad]
   int32_t* status;       // [n]
-  int32_t* list;         // scratch [n][n_pad]: token ids the cache holds
+  int32_t* list;         // scratch [n][n_pad]: token ids the cache holds (null when in LDS)
   int64_t n_pad;
   int32_t n;
+  int32_t list_in_lds;   // kvs_death_list_in_lds(n_pad, the device's LDS per block)
 };
+
+// Whether kvs_death_kernel keeps a rollout's list of held token ids in LDS
+// (n_pad int32 entries beside its static LDS, within max_lds bytes per
+// block) rather than in the global list scratch.
+bool kvs_death_list_in_lds(int64_t n_pad, int max_lds);
 
 struct KvsBlockLaunch {
   const int32_t* death;  // [n][n_pad]

@@ -15,15 +15,28 @@
 #include "host_common.h"
 #include "kvs_internal.h"
 
+// One staging region of the event logs: pinned host memory, its device copy,
+// and the event recorded after the replay kernel that reads it.
+struct KvsStage {
+  char* host = nullptr;
+  char* dev = nullptr;
+  size_t cap = 0;
+  hipEvent_t done = nullptr;
+  bool pending = false;
+};
+
+constexpr int kKvsStages = 4;
+
 struct kvs_ctx {
   int32_t device = 0;
-  char* host = nullptr;      // pinned staging for the event logs
-  char* dev = nullptr;       // its device copy
-  size_t cap = 0;
-  hipEvent_t staged = nullptr;  // the last upload's consumer has finished
-  bool staged_pending = false;
-  int32_t* list = nullptr;   // death-time scratch: held token ids per rollout
+  int max_lds = 0;           // the device's LDS bytes per block
+  KvsStage stage[kKvsStages];  // taken in turn; a call waits only if its region is still in flight
+  int next_stage = 0;
+  int32_t* list = nullptr;   // death-time scratch of the global-list replay: held token ids per rollout
   size_t list_cap = 0;       // elements
+  hipEvent_t list_done = nullptr;  // the last global-list replay has finished
+  bool list_pending = false;
+  hipStream_t list_stream = nullptr;
   int2* minmax = nullptr;    // block-mask scratch
   size_t minmax_cap = 0;     // elements
   hipEvent_t minmax_done = nullptr;
@@ -81,7 +94,10 @@ ll_status kvs_ctx_create(int32_t device, kvs_ctx** out) try {
   if (!g.ok()) return fail(LL_EDEVICE, "hipSetDevice(%d) failed", device);
   kvs_ctx* c = new kvs_ctx();
   c->device = device;
-  hipError_t e = hipEventCreateWithFlags(&c->staged, hipEventDisableTiming);
+  hipError_t e = hipDeviceGetAttribute(&c->max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, device);
+  for (int i = 0; i < kKvsStages && e == hipSuccess; ++i)
+    e = hipEventCreateWithFlags(&c->stage[i].done, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&c->list_done, hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&c->minmax_done, hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&c->events_done, hipEventDisableTiming);
   if (e != hipSuccess) {
@@ -97,15 +113,20 @@ ll_status kvs_ctx_create(int32_t device, kvs_ctx** out) try {
 void kvs_ctx_destroy(kvs_ctx* c) try {
   if (!c) return;
   DeviceGuard g(c->device);
-  if (c->staged_pending) (void)hipEventSynchronize(c->staged);
+  for (KvsStage& S : c->stage)
+    if (S.pending) (void)hipEventSynchronize(S.done);
+  if (c->list_pending) (void)hipEventSynchronize(c->list_done);
   if (c->minmax_pending) (void)hipEventSynchronize(c->minmax_done);
   if (c->events_pending) (void)hipEventSynchronize(c->events_done);
-  if (c->staged) (void)hipEventDestroy(c->staged);
+  for (KvsStage& S : c->stage) {
+    if (S.done) (void)hipEventDestroy(S.done);
+    if (S.host) (void)hipHostFree(S.host);
+    if (S.dev) (void)hipFree(S.dev);
+  }
+  if (c->list_done) (void)hipEventDestroy(c->list_done);
   if (c->minmax_done) (void)hipEventDestroy(c->minmax_done);
   if (c->events_done) (void)hipEventDestroy(c->events_done);
   if (c->events) (void)hipFree(c->events);
-  if (c->host) (void)hipHostFree(c->host);
-  if (c->dev) (void)hipFree(c->dev);
   if (c->minmax) (void)hipFree(c->minmax);
   if (c->list) (void)hipFree(c->list);
   delete c;
@@ -148,36 +169,52 @@ ll_status kvs_death_times(kvs_ctx* c, const kvs_rollout_log* logs, int32_t n, in
   const size_t roll_bytes = sizeof(ll::KvsRollout) * static_cast<size_t>(n);
   const size_t ev_off = (roll_bytes + 255) / 256 * 256;
   const size_t need = ev_off + sizeof(ll::KvsEvent) * static_cast<size_t>(std::max<int64_t>(n_events, 1));
-  // the staging buffer is reused: wait until the previous call's kernel has read it
-  if (c->staged_pending) {
-    hipError_t e = hipEventSynchronize(c->staged);
+  // The held-token list lives in LDS when it fits; otherwise in the
+  // context's list scratch, which one replay at a time may use.
+  const bool in_lds = ll::kvs_death_list_in_lds(n_pad, c->max_lds);
+  if (!in_lds) {
+    const size_t list_need = static_cast<size_t>(n) * static_cast<size_t>(n_pad);
+    if (list_need > c->list_cap) {
+      if (c->list_pending) {  // the last replay that used it must finish before it is freed
+        hipError_t e = hipEventSynchronize(c->list_done);
+        if (e != hipSuccess) return dev_fail(e, "hipEventSynchronize(list scratch)");
+        c->list_pending = false;
+      }
+      if (c->list) (void)hipFree(c->list);
+      c->list = nullptr;
+      c->list_cap = 0;
+      if (hipMalloc(reinterpret_cast<void**>(&c->list), list_need * sizeof(int32_t)) != hipSuccess)
+        return fail(LL_ENOMEM, "cannot allocate %zu bytes of death-time scratch", list_need * sizeof(int32_t));
+      c->list_cap = list_need;
+    } else if (c->list_pending && c->list_stream != st) {
+      hipError_t e = hipStreamWaitEvent(st, c->list_done, 0);
+      if (e != hipSuccess) return dev_fail(e, "hipStreamWaitEvent(list scratch)");
+    }
+  }
+  // the staging region of this call: wait only while the call that used it
+  // last (kKvsStages calls ago) has not finished
+  KvsStage& S = c->stage[c->next_stage];
+  if (S.pending) {
+    hipError_t e = hipEventSynchronize(S.done);
     if (e != hipSuccess) return dev_fail(e, "hipEventSynchronize(staging)");
-    c->staged_pending = false;
+    S.pending = false;
   }
-  const size_t list_need = static_cast<size_t>(n) * static_cast<size_t>(n_pad);
-  if (list_need > c->list_cap) {  // the previous call has finished: its scratch is free
-    if (c->list) (void)hipFree(c->list);
-    c->list = nullptr;
-    c->list_cap = 0;
-    if (hipMalloc(reinterpret_cast<void**>(&c->list), list_need * sizeof(int32_t)) != hipSuccess)
-      return fail(LL_ENOMEM, "cannot allocate %zu bytes of death-time scratch", list_need * sizeof(int32_t));
-    c->list_cap = list_need;
-  }
-  if (need > c->cap) {
-    if (c->host) (void)hipHostFree(c->host);
-    if (c->dev) (void)hipFree(c->dev);
-    c->host = nullptr;
-    c->dev = nullptr;
-    c->cap = 0;
+  if (need > S.cap) {
+    if (S.host) (void)hipHostFree(S.host);
+    if (S.dev) (void)hipFree(S.dev);
+    S.host = nullptr;
+    S.dev = nullptr;
+    S.cap = 0;
     const size_t cap = std::max<size_t>(need * 2, size_t{1} << 16);
-    if (hipHostMalloc(reinterpret_cast<void**>(&c->host), cap, hipHostMallocDefault) != hipSuccess ||
-        hipMalloc(reinterpret_cast<void**>(&c->dev), cap) != hipSuccess)
+    if (hipHostMalloc(reinterpret_cast<void**>(&S.host), cap, hipHostMallocDefault) != hipSuccess ||
+        hipMalloc(reinterpret_cast<void**>(&S.dev), cap) != hipSuccess)
       return fail(LL_ENOMEM, "cannot allocate %zu bytes of staging", cap);
-    std::memset(c->host, 0, cap);  // fault the pinned pages in once
-    c->cap = cap;
+    std::memset(S.host, 0, cap);  // fault the pinned pages in once
+    S.cap = cap;
   }
-  ll::KvsRollout* rolls = reinterpret_cast<ll::KvsRollout*>(c->host);
-  ll::KvsEvent* evs = reinterpret_cast<ll::KvsEvent*>(c->host + ev_off);
+  c->next_stage = (c->next_stage + 1) % kKvsStages;
+  ll::KvsRollout* rolls = reinterpret_cast<ll::KvsRollout*>(S.host);
+  ll::KvsEvent* evs = reinterpret_cast<ll::KvsEvent*>(S.host + ev_off);
   int64_t at = 0;
   for (int32_t i = 0; i < n; ++i) {
     const kvs_rollout_log& l = logs[i];
@@ -194,22 +231,29 @@ ll_status kvs_death_times(kvs_ctx* c, const kvs_rollout_log* logs, int32_t n, in
       off += l.mask_len[e];
     }
   }
-  hipError_t e = hipMemcpyAsync(c->dev, c->host, need, hipMemcpyHostToDevice, st);
+  hipError_t e = hipMemcpyAsync(S.dev, S.host, need, hipMemcpyHostToDevice, st);
   if (e != hipSuccess) return dev_fail(e, "hipMemcpyAsync(event log)");
   ll::KvsDeathLaunch a{};
-  a.rollouts = reinterpret_cast<const ll::KvsRollout*>(c->dev);
-  a.events = reinterpret_cast<const ll::KvsEvent*>(c->dev + ev_off);
+  a.rollouts = reinterpret_cast<const ll::KvsRollout*>(S.dev);
+  a.events = reinterpret_cast<const ll::KvsEvent*>(S.dev + ev_off);
   a.keep = keep_dev;
   a.death = death_dev;
   a.status = status_dev;
-  a.list = c->list;
+  a.list = in_lds ? nullptr : c->list;
+  a.list_in_lds = in_lds ? 1 : 0;
   a.n_pad = n_pad;
   a.n = n;
   e = ll::launch_kvs_death(a, st);
   if (e != hipSuccess) return dev_fail(e, "kvs_death_kernel launch");
-  e = hipEventRecord(c->staged, st);
+  e = hipEventRecord(S.done, st);
   if (e != hipSuccess) return dev_fail(e, "hipEventRecord");
-  c->staged_pending = true;
+  S.pending = true;
+  if (!in_lds) {
+    e = hipEventRecord(c->list_done, st);
+    if (e != hipSuccess) return dev_fail(e, "hipEventRecord");
+    c->list_pending = true;
+    c->list_stream = st;
+  }
   return LL_OK;
 } catch (...) {
   return host_exception(nullptr);

@@ -17,7 +17,6 @@
 #include <deque>
 #include <memory>
 #include <string>
-#include <thread>
 #include <utility>
 #include <vector>
 
@@ -323,8 +322,11 @@ ll_status apply_evict(ll_pool* p, const int32_t* seq_ids, size_t n_seqs, const i
   }
   stats.alg_bytes = p->num_planes * 2 * p->row_bytes * stats.rows_moved;
   stats.planned_on_device = 1;
+  // page size 1: the timed kernel reads the kept rows' pages (4 B each) and
+  // the freed-page bytes (one per pool page) and writes the table entries
+  // (4 B each) and the freed-page bitmap
   if (prof_index >= 0 && prof_index < static_cast<int64_t>(p->prof[0].size()))
-    p->prof[0][prof_index].bytes = stats.alg_bytes + 4 * stats.table_entries;
+    p->prof[0][prof_index].bytes = 8 * stats.table_entries + 72 * n_words;
   p->last = stats;
   return LL_OK;
 }

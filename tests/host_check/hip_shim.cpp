@@ -84,6 +84,10 @@ hipError_t hipSetDevice(int d) {
   return hipSuccess;
 }
 const char* hipGetErrorString(hipError_t) { return "error in the HIP stand-in"; }
+hipError_t hipDeviceGetAttribute(int* v, hipDeviceAttribute_t attr, int) {
+  *v = attr == hipDeviceAttributeMaxSharedMemoryPerBlock ? 160 * 1024 : 0;
+  return hipSuccess;
+}
 
 }  // extern "C"
 
@@ -296,7 +300,11 @@ hipError_t launch_rope_inplace_mla(const RopeRowsLaunch&, const double*, int, hi
 }
 int64_t rope_rows_blocks_per_plane(const RopeRowsLaunch&, int64_t) { return 1; }
 
-hipError_t launch_kvs_death(const KvsDeathLaunch&, hipStream_t) { return hipSuccess; }
+bool kvs_death_list_in_lds(int64_t n_pad, int max_lds) { return n_pad * 4 + 1040 <= max_lds; }
+hipError_t launch_kvs_death(const KvsDeathLaunch& a, hipStream_t) {
+  // the list scratch must exist exactly when the list is not in LDS
+  return (a.list_in_lds != 0) == (a.list == nullptr) ? hipSuccess : hipErrorInvalidValue;
+}
 hipError_t launch_kvs_block(const KvsBlockLaunch&, hipStream_t) { return hipSuccess; }
 hipError_t launch_kvs_dense(const KvsDenseLaunch&, hipStream_t) { return hipSuccess; }
 

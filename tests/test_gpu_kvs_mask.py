@@ -298,35 +298,39 @@ def test_dense_mask_beyond_the_pre_pass_limit():
 
 
 def test_masks_on_alternating_streams_share_the_scratch():
-    """Dense and block masks of two batches issued back to back on two
-    streams, then on the first again: each call reuses the context's scratch,
-    so a call on the other stream is ordered after the last one on the
-    device.  Every result compared with the definition."""
+    """Dense and block masks of three batches issued back to back on two
+    streams, then on the first again.  The first batch is long (24 rollouts
+    of 16384: 805 MB of mask bits), the later ones short, so the later calls
+    would overwrite the shared scratch while the first still reads it unless
+    the library orders them after it on the device.  Every result compared
+    with the definition (the long batch on sampled rows and query blocks)."""
     L = need_gpu()
     ctx = L.KvsMask(0)
-    n_pad = 2048
     rng = np_rng(33, 0)
-    k = np.arange(n_pad)
+    shapes = [(24, 16384), (4, 2048), (4, 2048)]
     batches = []
-    for b in range(3):
-        times = np.sort(rng.choice(np.arange(1, n_pad), size=(5, 9, 40)[b], replace=False))
-        d = np.where(rng.random((4, n_pad)) < 0.6, times[rng.integers(0, len(times), size=(4, n_pad))], n_pad)
-        d = np.where(d > k, d, n_pad)
-        batches.append(d)
+    for b, (n, n_pad) in enumerate(shapes):
+        k = np.arange(n_pad)
+        times = np.sort(rng.choice(np.arange(1, n_pad), size=(9, 5, 40)[b], replace=False))
+        d = np.where(rng.random((n, n_pad)) < 0.6, times[rng.integers(0, len(times), size=(n, n_pad))], n_pad)
+        batches.append(np.where(d > k, d, n_pad))
     streams = [torch.cuda.Stream(), torch.cuda.Stream(), None]
     # inputs and outputs made first and kept alive until the end, so that
     # only the library orders the three calls
     deaths = [torch.from_numpy(d.astype(np.int32)).cuda() for d in batches]
-    bufs = [(torch.empty((4, n_pad, n_pad // 32), dtype=torch.int32, device="cuda"),
-             tuple(torch.empty(shape, dtype=torch.int32, device="cuda")
-                   for shape in ((4, 32), (4, 32, 32), (4, 32), (4, 32, 32)))) for _ in batches]
+    bufs = []
+    for n, n_pad in shapes:
+        nb = n_pad // 64
+        bufs.append((torch.empty((n, n_pad, n_pad // 32), dtype=torch.int32, device="cuda"),
+                     tuple(torch.empty(sh, dtype=torch.int32, device="cuda")
+                           for sh in ((n, nb), (n, nb, nb), (n, nb), (n, nb, nb)))))
     torch.cuda.synchronize()
     outs = []
     for death, st, (bits, blocks) in zip(deaths, streams, bufs):
-        say(f"kvs masks on stream {st}")
+        say(f"kvs masks {tuple(death.shape)} on stream {st}")
         outs.append((ctx.dense_mask(death, out=bits, stream=st), ctx.block_mask(death, 64, 64, out=blocks, stream=st)))
     torch.cuda.synchronize()
-    for d, (bits, blocks) in zip(batches, outs):
+    for d, (bits, blocks) in zip(batches[1:], outs[1:]):
         got = bits.cpu().numpy().view(np.uint32)
         pn, pi, fn, fi = (x.cpu().numpy() for x in blocks)
         for r in range(d.shape[0]):
@@ -335,4 +339,49 @@ def test_masks_on_alternating_streams_share_the_scratch():
             partial, full = K.block_mask(vis, 64, 64)
             for i in range(len(partial)):
                 assert list(pi[r, i, :pn[r, i]]) == partial[i] and list(fi[r, i, :fn[r, i]]) == full[i], (r, i)
+    d = batches[0]
+    n, n_pad = d.shape
+    bits, blocks = outs[0]
+    rows = np.array([0, 1, 63, 64, 2047, 4096, 9999, n_pad - 1])
+    idx = torch.from_numpy(rows).cuda()
+    pn, pi, fn, fi = (x.cpu().numpy() for x in blocks)
+    nk = n_pad // 64
+    for r in range(n):
+        got = bits[r, idx].cpu().numpy().view(np.uint32)
+        assert np.array_equal(got, K.dense_bits(K.visibility_rows(d[r], rows))), r
+        for i in (0, 1, 100, nk - 1):
+            cls = [K.tile_class(d[r], i * 64, i * 64 + 64, j * 64, j * 64 + 64) for j in range(nk)]
+            assert list(pi[r, i, :pn[r, i]]) == [j for j in range(nk) if cls[j] == "partial"], (r, i)
+            assert list(fi[r, i, :fn[r, i]]) == [j for j in range(nk) if cls[j] == "full"], (r, i)
+    ctx.close()
+
+
+def test_death_times_on_alternating_streams_share_the_list_scratch():
+    """Death times past the LDS list (n_pad = 50000 keeps each rollout's held
+    tokens in the context's list scratch): a long call of 64 rollouts on one
+    stream, a short one on another right after it, then three more on the
+    first stream (the staging ring's regions taken in turn).  The short call
+    reuses the list rows the long one is still replaying unless the library
+    orders it after that call on the device.  Bit-exact against the oracle."""
+    L = need_gpu()
+    ctx = L.KvsMask(0)
+    n_pad = 50000
+    calls = [(0, _logs(91, [n_pad - 7 * i for i in range(64)], ["window", "half", "pick"] * 22, budget=12000,
+                       turn_lo=64, turn_hi=512, every=4)),
+             (1, _logs(92, [n_pad, n_pad - 1000], ["pick", "half"], budget=9000, turn_lo=64, turn_hi=512, every=3))]
+    calls += [(0, _logs(93 + c, [n_pad - 300 * c], ["pick"], budget=5000, turn_lo=32, turn_hi=256, every=5))
+              for c in range(3)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    logs = [ctx.upload_logs(rolls) for _, rolls in calls]
+    outs = [(torch.empty((len(rolls), n_pad), dtype=torch.int32, device="cuda"),
+             torch.empty(len(rolls), dtype=torch.int32, device="cuda")) for _, rolls in calls]
+    torch.cuda.synchronize()
+    for (si, rolls), lg, out in zip(calls, logs, outs):
+        say(f"kvs death times, {len(rolls)} rollouts of up to {n_pad} on stream {si}")
+        ctx.death_times(lg, n_pad, stream=streams[si], out=out)
+    torch.cuda.synchronize()
+    for (_, rolls), (death, status) in zip(calls, outs):
+        assert not status.cpu().numpy().any()
+        want = np.stack([K.death_times(n_pad, n, ev) for n, ev in rolls])
+        assert np.array_equal(death.cpu().numpy().astype(np.int64), want)
     ctx.close()

@@ -334,6 +334,10 @@ def test_kvs_host_validation_under_sanitizers(driver):
         want.append(f"kvs {EINVAL}")
     ops.append(kvs_line(0, [(0, [])]))
     want.append(f"kvs {EINVAL}")
+    # n_pad beyond the LDS list: the context's list scratch, grown, then reused
+    for n_pad, n in [(50000, 1), (60000, 2), (50000, 2), (1000, 1), (70000, 1)]:
+        ops.append(kvs_line(n_pad, [(n_pad - 5, [(100, 50), (n_pad - 10, min(3000, n_pad - 10))])] * n))
+        want.append("kvs 0")
     for n, n_pad, bq, bk, exp in [(2, 256, 16, 32, "0 0"), (1, 1024, 1024, 16, "0 0"), (3, 100, 64, 64, f"0 {EINVAL}"),
                                   (2, 256, 8, 32, f"{EINVAL} 0"), (2, 256, 48, 32, f"{EINVAL} 0"),
                                   (2, 384, 2048, 16, f"{EINVAL} 0")]:
