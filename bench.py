@@ -2,8 +2,8 @@
 
 Default workload (the headline): a DeepSeek-V2-Lite shaped MLA cache, 27
 layers, one sequence of 32768 tokens, rows c_kv 512 + k_pe 64 bf16 ~ N(0,1),
-page size 16, pages randomly permuted in a pool of 4096 pages; one AMORTIZE
-splice drops three 2048-token tool turns [8192, 14336) for a 24-row stub
+page size 16, the sequence on a random permutation of its own 2048 pages; one
+AMORTIZE splice drops three 2048-token tool turns [8192, 14336) for a 24-row stub
 (Delta = -6120), moving and rotating every downstream row ("Leyline: KV Cache
 Directives for Agentic Inference", sections 2.1-2.3).
 
@@ -13,8 +13,10 @@ rotates k_pe and rewrites the page table) on a sequence of its own: the pool
 holds one such sequence per timed step (up to 64; beyond that one sequence
 has its page table restored before every splice, which also serves as the
 context figure `step_with_table_restore_ms`).  `value` is the row bytes the
-splice must move per step divided by the wall time per step.  The roofline object times the row kernel alone with HIP events
-recorded on the stream it runs on; its `traffic` is the HBM traffic per launch
+splice must move per step divided by the wall time per step; no launch in the
+timed loop is stamped.  The roofline object times the row kernel alone, in a
+separate pass, with HIP events recorded on the stream it runs on (percentiles
+in `kernel_us`); its `traffic` is the HBM traffic per launch
 from the rocprofv3 counter summary in profiles/, used only while that summary
 was taken on the current kernel source.  The CPU baseline runs the oracle on
 the same workload on the host and checks the GPU result against it; a second
@@ -1285,8 +1287,8 @@ def bench_evict_gqa(args):
     """KV-streams eviction on a GQA cache of Llama-3-8B shape: 32 rollouts x
     16384 tokens x 32 layers of K and V planes (8 KV heads x 128), page size
     16, random turn drops (turns U[200,2000], p = 0.5); pool pages 1.5 x the
-    rollouts' (fewer than the worst case: the call reads the device's verdict
-    before the row moves).  Restoring the tables between steps is outside the
+    rollouts' (fewer than if every new page were fresh: the device's verdict
+    decides before the rows move).  Restoring the tables between steps is outside the
     timed call."""
     import torch
     from mla_paged_cache_amd import leyline as L

@@ -33,8 +33,8 @@ class Mirror:
         self.P = P
         # about 1600 rows: five sequences of up to 700 rows do not all fit, so
         # allocations and splices get refused and evictions now and then find
-        # fewer free pages than their worst case (the call then reads the
-        # device's verdict before it goes on)
+        # fewer free pages than they would need if every new page were fresh
+        # (the device's verdict then decides)
         self.num_pages = {1: 1600, 4: 400, 16: 100}[P]
         self.max_pages = -(-MAX_LEN * 2 // P)
         self.dp = self.make_pool(seed)
@@ -43,7 +43,7 @@ class Mirror:
         self.keep_alive = []
         self.live = set()
         self.seed = seed * 100000
-        self.host_plans = 0
+        self.short_evictions = 0
         # splice planner per call: its own stream of draws, so the operations
         # themselves do not depend on it
         self.plan_rng = np.random.default_rng(seed + 1)
@@ -204,7 +204,7 @@ class Mirror:
         dev = torch.from_numpy(keep).cuda() if len(keep) else torch.zeros(16, dtype=torch.uint8, device="cuda")
         self.keep_alive.append(dev)
         if self.P > 1 and len(self.state.free) < sum(len(self.state.tables[s]) for s in seqs):
-            self.host_plans += 1   # a shortage was possible: the call waited for the verdict
+            self.short_evictions += 1   # a shortage was possible: the verdict decided
         try:
             expected, _ = O.evict(self.state, seqs, masks)
         except O.OracleError:
@@ -261,7 +261,7 @@ class Mirror:
             self.check_books()
             self.check_rows()
             assert len(self.state.free) < sum(len(self.state.tables[s]) for s in (0, 1))
-            self.host_plans += 1
+            self.short_evictions += 1
         # whole pages kept or dropped (every new page a reuse), and one row
         # dropped 3 pages before the end (a few fresh pages)
         m0 = np.repeat(self.rng.integers(0, 2, size=-(-big // self.P)), self.P)[:big].astype(np.uint8)
@@ -349,7 +349,7 @@ def test_random_operation_sequences(P, kind):
     for x in log:
         kinds[x.split(" ")[0].rstrip(":")] = kinds.get(x.split(" ")[0].rstrip(":"), 0) + 1
     say(f"  {len(log)} operations {kinds}; {refused} refused as the oracle refused them; "
-        f"{m.host_plans} evictions planned on the host; splices planned on the device "
+        f"{m.short_evictions} evictions short of their all-fresh need; splices planned on the device "
         f"{m.splice_planned[1]}, staged {m.splice_planned[0]}")
     assert m.splice_planned[0] and m.splice_planned[1]
     m.pressure()
