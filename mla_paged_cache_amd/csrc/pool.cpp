@@ -98,17 +98,17 @@ class FreePages {
   bool give_bits_checked(const uint64_t* bits) {
     const size_t n = words_.size();
     if (n && (bits[n - 1] & ~tail_mask())) return false;
+    // branch-free: freed words come in any order of zero and non-zero
     uint64_t clash = 0;
     int64_t added = 0;
-    size_t first = n;
     for (size_t w = 0; w < n; ++w) {
       const uint64_t b = bits[w];
-      if (!b) continue;
       clash |= b & words_[w];
       words_[w] |= b;
       added += __builtin_popcountll(b);
-      if (first == n) first = w;
     }
+    size_t first = 0;
+    while (first < n && !bits[first]) ++first;
     count_ += added;
     hint_ = std::min<int64_t>(hint_, static_cast<int64_t>(first));
     return clash == 0;
