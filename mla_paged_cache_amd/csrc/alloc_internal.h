@@ -23,6 +23,8 @@ struct AllocLaunch {
   int32_t* word_base;         // [n_words]: free pages in the words before
   int32_t* new_table;         // per sequence at reuse_off: the new page table
   EvictTask* tasks;           // [fresh pages], in (sequence, page) order
+  const int32_t* src_logical; // old logical row of every kept row (keep scan), or null: tasks
+                              // then always point at src_rows
   int32_t* info;              // [0] fresh pages, [1] 1 if they exceed the free pages,
                               // [2..3] rows written to fresh pages (64-bit); 16-byte aligned
 };

@@ -241,7 +241,14 @@ __global__ __launch_bounds__(kFlatThreads) void evict_move_kernel(EvictLaunch a)
   const uint32_t r = row_flat & ((1u << shift) - 1u);
   const int64_t j = (static_cast<int64_t>(t.q) << shift) + r;
   if (j >= t.n_new) return;
-  const int64_t src_row = a.src_rows[t.src_off + j];
+  int64_t src_row;
+  if (t.src_off0 >= 0) {
+    const int32_t o = t.src_off0 + static_cast<int32_t>(r);
+    const int32_t P = 1 << shift;
+    src_row = o < P ? (static_cast<int64_t>(t.src_page0) << shift) + o : (static_cast<int64_t>(t.src_page1) << shift) + (o - P);
+  } else {
+    src_row = a.src_rows[t.src_off + j];
+  }
   const chunk_t* layer = a.layers[l];
   const chunk_t v = __builtin_nontemporal_load(layer + src_row * kRowChunks + col);
   __builtin_nontemporal_store(v, const_cast<chunk_t*>(layer) +

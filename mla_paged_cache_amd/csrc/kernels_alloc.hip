@@ -153,6 +153,23 @@ __global__ __launch_bounds__(256) void alloc_tables_kernel(AllocLaunch a) {
       t.q = static_cast<int32_t>(q);
       t.dst_page = page;
       t.n_new = static_cast<int32_t>(n_new);
+      t.src_page0 = -1;
+      t.src_page1 = -1;
+      t.src_off0 = -1;
+      if (a.src_logical) {
+        // live rows that are consecutive old rows lie in at most two old
+        // pages: the row kernel then needs no per-row source lookup
+        const int64_t j0 = q << a.page_shift;
+        const int64_t k = n_new - j0 < P ? n_new - j0 : P;
+        const int32_t first = a.src_logical[e.src_off + j0];
+        const int32_t last = a.src_logical[e.src_off + j0 + k - 1];
+        if (last - first == k - 1) {
+          const int32_t off = first & static_cast<int32_t>(P - 1);
+          t.src_page0 = old_t[first >> a.page_shift];
+          t.src_page1 = off + k > P ? old_t[(first >> a.page_shift) + 1] : -1;
+          t.src_off0 = off;
+        }
+      }
       a.tasks[f] = t;
     }
     a.new_table[e.reuse_off + q] = page;

@@ -82,8 +82,14 @@ struct alignas(16) EvictTask {
   int32_t q;           // new logical page
   int32_t dst_page;    // physical page written
   int32_t n_new;       // rows after the eviction
-  int32_t pad[3];
+  // when the page's live rows are consecutive old rows: the old page of the
+  // first, the next old page (-1 when they all lie in the first) and the
+  // first row's offset in its page; src_off0 = -1: read src_rows instead
+  int32_t src_page0;
+  int32_t src_page1;
+  int32_t src_off0;
 };
+static_assert(sizeof(EvictTask) == 32, "an eviction task is two 16-byte words");
 
 struct SpliceLaunch {
   const chunk_t* const* layers;  // device array [num_layers] of pool bases

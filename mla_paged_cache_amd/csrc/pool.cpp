@@ -844,6 +844,7 @@ ll_status evict_device_plan(ll_pool* p, const int32_t* seq_ids, int32_t n, const
   al.word_base = reinterpret_cast<int32_t*>(d + off_wb);
   al.new_table = reinterpret_cast<int32_t*>(d + off_nt);
   al.tasks = reinterpret_cast<ll::EvictTask*>(d + off_tasks);
+  al.src_logical = sc.src_logical;
   al.info = reinterpret_cast<int32_t*>(d + off_info);
   // kernel 0's record: at page size 1 the new tables; above it the row moves
   ProfRec rec{};

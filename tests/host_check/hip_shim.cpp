@@ -264,7 +264,7 @@ hipError_t launch_alloc_tables(const AllocLaunch& a, hipStream_t, const Stamp&) 
           page = w * 64 + __builtin_ctzll(bits);
         }
         a.tasks[a.fresh_base[b] + a.rank[e.reuse_off + q]] = EvictTask{e.src_off, static_cast<int32_t>(q), page,
-                                                                         static_cast<int32_t>(n_new), {0, 0, 0}};
+                                                                         static_cast<int32_t>(n_new), -1, -1, -1};
       }
       a.new_table[e.reuse_off + q] = page;
     }
