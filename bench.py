@@ -132,10 +132,12 @@ def profiled_traffic(kernel: str, workload: str):
 
 
 def quiet_gc():
-    """Collect now and keep Python's cyclic collector off until the timed
-    region ends: its pauses (tens of ms with torch loaded) would otherwise land
-    inside the timed host loop and starve the GPU."""
-    gc.collect()
+    """Keep Python's cyclic collector off until the timed region ends: its
+    pauses (tens of ms with torch loaded) would otherwise land inside the timed
+    host loop and starve the GPU.  No collection is forced here: a full
+    collection right before a loop walks every Python object and leaves the
+    host caches cold, and the loop's first call then took 123 us on the host
+    instead of 48-59 us (the GPU idles meanwhile)."""
     gc.disable()
 
 
