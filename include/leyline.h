@@ -424,14 +424,15 @@ void kvs_ctx_destroy(kvs_ctx* ctx);
  * The host arrays are read before the call returns.  The context stages
  * the logs in four regions taken in turn; a call waits on the host only when
  * its region's last user (the call four calls earlier) has not finished.
- * When n_pad token ids do not fit in a block's LDS (n_pad above about 40 000
- * on this device) the replay keeps them in a context-owned scratch of
- * n * n_pad int32: a call on another stream then waits on the device for the
- * last such call, and one that must grow the scratch waits on the host.
+ * The replay keeps 8 bytes per 32 mask rows and 4 per event in a
+ * context-owned scratch: a call on another stream waits on the device for
+ * the last call,
+ * and one that must grow the scratch waits on the host for it.
  * Errors: LL_EINVAL
  * (n_pad outside [1, 2^31 - 2], n_tokens > n_pad, event times not increasing
  * inside (0, n_tokens], mask_len outside [0, time], NULL pointers),
- * LL_ENOMEM, LL_EDEVICE. */
+ * LL_EUNSUPPORTED (n * ceil(n_pad / 256) of 2^31 or more), LL_ENOMEM,
+ * LL_EDEVICE. */
 ll_status kvs_death_times(kvs_ctx* ctx, const kvs_rollout_log* logs, int32_t n, int64_t n_pad,
                           const uint8_t* keep_dev, int32_t* death_dev, int32_t* status_dev, void* stream);
 

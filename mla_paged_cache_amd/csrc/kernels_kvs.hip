@@ -6,10 +6,13 @@
 // Token k's death time d_k is the time of the eviction event that dropped it
 // (n_pad if none, k for padding keys); query q sees key k iff k <= q < d_k.
 //
-//  * kvs_death_kernel: replays a rollout's eviction log -- per event, the rows
-//    held are the block's list of held tokens plus the tokens generated since;
-//    a block prefix scan over the keep mask compacts the list in place and
-//    dropped tokens get the event's time.
+//  * kvs_rank_kernel / kvs_chain_kernel: the eviction log replayed in
+//    parallel.  One block per event ranks its keep mask (kept rows before
+//    each group of 32 rows, by a block prefix scan, with the group's keep
+//    bits); then one thread per token follows the
+//    token's row from event to event -- the held rows of an event are the
+//    survivors of the one before, in order, followed by the tokens generated
+//    since -- until an event drops it (its death time) or the log ends.
 //  * kvs_minmax_kernel / kvs_block_kernel: per key block the smallest and
 //    largest death time, then per query block the sorted lists of partial and
 //    full key blocks (FlexAttention-style block mask).
@@ -35,122 +38,158 @@ namespace {
 
 typedef uint32_t word4 __attribute__((ext_vector_type(4)));
 
-constexpr int kDeathThreads = 1024;
-constexpr int kDeathWaves = kDeathThreads / 64;
-constexpr int kPerThread = 16;  // slices of kDeathThreads rows per tile
-static_assert(kPerThread * kDeathWaves == 4 * 64, "one wave scans the (slice, wave) counts, four per lane");
 
-// One block per rollout.  d is initialised to n_pad (never dropped) for real
-// tokens and to k (never visible) for padding keys.  The block keeps the list
-// of token ids the cache holds, in order, in its scratch row; at an event at
-// time t the rows held are that list followed by the tokens generated since
-// the previous event, and row i is token list'[i].  A tile is 16 slices of
-// 1024 rows; thread x takes row x of every slice, so each load and store
-// instruction of a wave covers 64 neighbouring rows.  Per slice a ballot of
-// the kept bits, per (slice, wave) its count in LDS, one wave's exclusive scan
-// over those 256 counts in (slice, wave) order, and each kept row's position
-// is the scan's entry plus the kept lanes below it; kept tokens are compacted
-// in place -- a row's position is never past its own index, and every read of
-// the tile finishes before the scan's first barrier -- and dropped tokens get
-// d_k = t.  A mask whose length differs from the number of rows held sets the
-// status.
-// A barrier that orders LDS traffic only: each wave's LDS operations
-// complete, then the waves meet.  Global stores still in flight are not
-// waited for.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+// Bit b of the result: byte b of the 16 is nonzero.
+__device__ __forceinline__ uint32_t nonzero_bytes16(word4 v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t out = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      if ((w[q] >> (8 * c)) & 0xFFu) out |= 1u << (4 * q + c);
+  return out;
 }
 
-// LDS_LIST: the list lives in dynamic LDS (n_pad entries) instead of the
-// block's global scratch row, when it fits.  The event loop then shares only
-// LDS between threads (the death times it stores are read by no other thread
-// of the launch), so its barriers need not wait for those stores.
-template <bool LDS_LIST>
-__global__ __launch_bounds__(kDeathThreads) void kvs_death_kernel(KvsDeathLaunch a) {
-  extern __shared__ int32_t lds_list[];
-  __shared__ int32_t part[kPerThread * kDeathWaves];  // (slice, wave): kept count, then its exclusive prefix
-  __shared__ int32_t tile_total;
-  const KvsRollout r = a.rollouts[blockIdx.x];
-  const int64_t n_pad = a.n_pad;
-  int32_t* d = a.death + static_cast<int64_t>(blockIdx.x) * n_pad;
-  int32_t* list = LDS_LIST ? lds_list : a.list + static_cast<int64_t>(blockIdx.x) * n_pad;
-  for (int64_t k = threadIdx.x; k < n_pad; k += kDeathThreads)
-    d[k] = k < r.n_tokens ? static_cast<int32_t>(n_pad) : static_cast<int32_t>(k);
-  __syncthreads();
+// One block per event.  Each thread takes a group of 32 mask rows per tile:
+// the 16-byte-aligned lines that hold them (three at most, each holding at
+// least one of the mask's bytes, so never a page the mask does not touch),
+// their nonzero bytes as bits, shifted to the group's first row.  The counts
+// (0..32) are scanned across the wave with one ballot per bit of the count,
+// then across the waves through LDS.  Group g of the event gets {kept rows
+// before it, its 32 keep bits}: a row's rank is the first plus the kept rows
+// below it in the second.
+constexpr int kRankThreads = 512;
+constexpr int kRankWaves = kRankThreads / 64;
 
+__global__ __launch_bounds__(kRankThreads) void kvs_rank_kernel(KvsDeathLaunch a) {
+  __shared__ int32_t wave_total[kRankWaves];
+  const KvsEvent ev = a.events[blockIdx.x];
+  const uint8_t* m = a.keep + ev.mask_off;
+  uint2* out = a.rank + ev.rank_off;
+  const int64_t len = ev.mask_len;
+  const uintptr_t end = reinterpret_cast<uintptr_t>(m) + static_cast<uintptr_t>(len);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const uint64_t lanes_below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-  bool bad = false;
-  int64_t held = 0;    // entries of `list`
-  int64_t t_prev = 0;  // tokens generated at the previous event
-  KvsEvent next = r.n_events > 0 ? a.events[r.first_event] : KvsEvent{};
-  for (int e = 0; e < r.n_events; ++e) {
-    const KvsEvent ev = next;
-    if (e + 1 < r.n_events) next = a.events[r.first_event + e + 1];  // in flight during this event
-    const int64_t t = ev.time;
-    const int64_t rows = held + (t - t_prev);
-    bad = bad || rows != ev.mask_len;
-    const int64_t len = rows < ev.mask_len ? rows : ev.mask_len;
-    const uint8_t* m = a.keep + ev.mask_off;
-    int64_t carry = 0;
-    for (int64_t base = 0; base < len; base += int64_t{kPerThread} * kDeathThreads) {
-      int32_t tok[kPerThread];
-      uint8_t keep[kPerThread];
-      uint64_t bal[kPerThread];
-      // every load of the tile issued before the first ballot: indices past
-      // the rows are clamped to row 0 (in bounds: len >= 1, the list has n_pad
-      // entries), so the loads carry no branches and stay in flight together
-#pragma unroll
-      for (int c = 0; c < kPerThread; ++c) {
-        const int64_t i = base + int64_t{c} * kDeathThreads + threadIdx.x;
-        keep[c] = m[i < len ? i : 0];
-        const int32_t held_tok = list[i < held ? i : 0];
-        tok[c] = i < held ? held_tok : static_cast<int32_t>(t_prev + (i - held));
-      }
-#pragma unroll
-      for (int c = 0; c < kPerThread; ++c) {
-        const int64_t i = base + int64_t{c} * kDeathThreads + threadIdx.x;
-        bal[c] = __ballot(i < len && keep[c] != 0);
-      }
-      if (lane == 0) {
-#pragma unroll
-        for (int c = 0; c < kPerThread; ++c) part[c * kDeathWaves + wave] = __popcll(bal[c]);
-      }
-      if (LDS_LIST) lds_barrier(); else __syncthreads();
-      if (wave == 0) {  // lane L scans entries 4L .. 4L + 3
-        const int32_t v0 = part[4 * lane], v1 = part[4 * lane + 1], v2 = part[4 * lane + 2], v3 = part[4 * lane + 3];
-        const int32_t own = v0 + v1 + v2 + v3;
-        int32_t incl = own;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const int32_t y = __shfl_up(incl, o);
-          if (lane >= o) incl += y;
-        }
-        const int32_t excl = incl - own;
-        part[4 * lane] = excl;
-        part[4 * lane + 1] = excl + v0;
-        part[4 * lane + 2] = excl + v0 + v1;
-        part[4 * lane + 3] = excl + v0 + v1 + v2;
-        if (lane == 63) tile_total = incl;
-      }
-      if (LDS_LIST) lds_barrier(); else __syncthreads();
-#pragma unroll
-      for (int c = 0; c < kPerThread; ++c) {
-        const int64_t i = base + int64_t{c} * kDeathThreads + threadIdx.x;
-        if (i >= len) break;
-        if ((bal[c] >> lane) & 1ull) list[carry + part[c * kDeathWaves + wave] + __popcll(bal[c] & lanes_below)] = tok[c];
-        else d[tok[c]] = static_cast<int32_t>(t);
-      }
-      carry += tile_total;
-      if (LDS_LIST) lds_barrier(); else __syncthreads();
+  int64_t carry = 0;
+  for (int64_t base = 0; base < len; base += 32 * kRankThreads) {
+    const int64_t i0 = base + 32 * static_cast<int64_t>(threadIdx.x);
+    uint32_t bits = 0;
+    if (i0 < len) {
+      const uintptr_t start = reinterpret_cast<uintptr_t>(m + i0);
+      const uintptr_t a0 = start & ~uintptr_t{15};
+      const int sk = static_cast<int>(start & 15u);
+      uint64_t nz = nonzero_bytes16(*reinterpret_cast<const word4*>(a0));
+      if (a0 + 16 < end) nz |= static_cast<uint64_t>(nonzero_bytes16(*reinterpret_cast<const word4*>(a0 + 16))) << 16;
+      if (sk && a0 + 32 < end) nz |= static_cast<uint64_t>(nonzero_bytes16(*reinterpret_cast<const word4*>(a0 + 32))) << 32;
+      bits = static_cast<uint32_t>(nz >> sk);
+      if (len - i0 < 32) bits &= (1u << (len - i0)) - 1u;
     }
-    held = carry;
-    t_prev = t;
+    const int cnt = __popc(bits);
+    int below = 0, total = 0;
+#pragma unroll
+    for (int bit = 0; bit < 6; ++bit) {
+      const uint64_t bal = __ballot((cnt >> bit) & 1);
+      below += __popcll(bal & lanes_below) << bit;
+      total += __popcll(bal) << bit;
+    }
+    if (lane == 0) wave_total[wave] = total;
+    __syncthreads();
+    int wave_below = 0, block_total = 0;
+#pragma unroll
+    for (int w = 0; w < kRankWaves; ++w) {
+      const int x = wave_total[w];
+      wave_below += w < wave ? x : 0;
+      block_total += x;
+    }
+    if (i0 < len) out[i0 >> 5] = make_uint2(static_cast<uint32_t>(carry + wave_below + below), bits);
+    carry += block_total;
+    __syncthreads();
   }
-  if (threadIdx.x == 0) a.status[blockIdx.x] = bad ? 1 : 0;
+  if (threadIdx.x == 0) a.kept[blockIdx.x] = static_cast<int32_t>(carry);
+}
+
+constexpr int kChainLdsEvents = 128;
+
+// A rollout's events, from LDS (LDS = true: staged by the block) or from the
+// event array.
+template <bool LDS>
+struct ChainEvents {
+  const KvsEvent* ev;
+  const int32_t* kept;
+  const int64_t* s_time;
+  const int64_t* s_len;
+  const int64_t* s_roff;
+  const int32_t* s_kept;
+  __device__ int64_t time(int e) const { return LDS ? s_time[e] : ev[e].time; }
+  __device__ int64_t len(int e) const { return LDS ? s_len[e] : ev[e].mask_len; }
+  __device__ int64_t roff(int e) const { return LDS ? s_roff[e] : ev[e].rank_off; }
+  __device__ int64_t held_after(int e) const { return LDS ? s_kept[e] : kept[e]; }
+};
+
+template <bool LDS>
+__device__ int32_t chain_death(const KvsDeathLaunch& a, const ChainEvents<LDS>& E, int n_events, int64_t k) {
+  int lo = 0, hi = n_events;  // the first event with time > k
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (E.time(mid) > k)
+      hi = mid;
+    else
+      lo = mid + 1;
+  }
+  if (lo >= n_events) return static_cast<int32_t>(a.n_pad);
+  int64_t row = (lo ? E.held_after(lo - 1) : 0) + (k - (lo ? E.time(lo - 1) : 0));
+  for (int e = lo; e < n_events; ++e) {
+    if (row >= E.len(e)) break;
+    const uint2 g = a.rank[E.roff(e) + (row >> 5)];
+    const uint32_t below = g.y & ((1u << (row & 31)) - 1u);
+    if (!((g.y >> (row & 31)) & 1u)) return static_cast<int32_t>(E.time(e));
+    row = g.x + __popc(below);
+  }
+  return static_cast<int32_t>(a.n_pad);
+}
+
+__global__ __launch_bounds__(kChainThreads) void kvs_chain_kernel(KvsDeathLaunch a) {
+  __shared__ int64_t s_time[kChainLdsEvents], s_len[kChainLdsEvents], s_roff[kChainLdsEvents];
+  __shared__ int32_t s_kept[kChainLdsEvents];
+  const int64_t r = blockIdx.x / a.chain_blocks;
+  const int64_t kb = blockIdx.x - r * a.chain_blocks;
+  const KvsRollout ro = a.rollouts[r];
+  const KvsEvent* ev = a.events + ro.first_event;
+  const int32_t* kept = a.kept + ro.first_event;
+  // up to kChainLdsEvents events staged in LDS: the walk's event reads then
+  // wait on LDS, not memory
+  const bool staged = ro.n_events <= kChainLdsEvents;
+  if (staged)
+    for (int e = threadIdx.x; e < ro.n_events; e += kChainThreads) {
+      const KvsEvent x = ev[e];
+      s_time[e] = x.time;
+      s_len[e] = x.mask_len;
+      s_roff[e] = x.rank_off;
+      s_kept[e] = kept[e];
+    }
+  __syncthreads();
+  if (kb == 0) {  // the rollout's status: its threads check the events in turn
+    bool bad = false;
+    for (int e = threadIdx.x; e < ro.n_events; e += kChainThreads) {
+      const int64_t held = e ? kept[e - 1] : 0;
+      const int64_t t_prev = e ? ev[e - 1].time : 0;
+      bad = bad || held + (ev[e].time - t_prev) != ev[e].mask_len;
+    }
+    bad = __syncthreads_or(bad);
+    if (threadIdx.x == 0) a.status[r] = bad ? 1 : 0;
+  }
+  const int64_t k = kb * kChainThreads + threadIdx.x;
+  if (k >= a.n_pad) return;
+  int32_t d;
+  if (k >= ro.n_tokens)
+    d = static_cast<int32_t>(k);
+  else if (staged)
+    d = chain_death<true>(a, ChainEvents<true>{ev, kept, s_time, s_len, s_roff, s_kept}, ro.n_events, k);
+  else
+    d = chain_death<false>(a, ChainEvents<false>{ev, kept, nullptr, nullptr, nullptr, nullptr}, ro.n_events, k);
+  a.death[r * a.n_pad + k] = d;
 }
 
 // Smallest and largest death time of each key block: one wave per block.
@@ -534,17 +573,14 @@ __global__ __launch_bounds__(256) void kvs_dense_ev_kernel(KvsDenseLaunch a) {
 
 }  // namespace
 
-bool kvs_death_list_in_lds(int64_t n_pad, int max_lds) {
-  const int64_t static_lds = int64_t{kPerThread} * kDeathWaves * 4 + 16;
-  return n_pad * 4 + static_lds <= max_lds;
-}
-
 hipError_t launch_kvs_death(const KvsDeathLaunch& a, hipStream_t s) {
   if (a.n == 0) return hipSuccess;
-  if (a.list_in_lds)
-    kvs_death_kernel<true><<<dim3(a.n), dim3(kDeathThreads), static_cast<size_t>(a.n_pad * 4), s>>>(a);
-  else
-    kvs_death_kernel<false><<<dim3(a.n), dim3(kDeathThreads), 0, s>>>(a);
+  if (a.n_events > 0) {
+    kvs_rank_kernel<<<dim3(static_cast<unsigned>(a.n_events)), dim3(kRankThreads), 0, s>>>(a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  kvs_chain_kernel<<<dim3(static_cast<unsigned>(a.n * a.chain_blocks)), dim3(kChainThreads), 0, s>>>(a);
   return hipGetLastError();
 }
 

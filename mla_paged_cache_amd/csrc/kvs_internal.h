@@ -20,25 +20,30 @@ struct alignas(16) KvsEvent {
   int64_t time;          // tokens generated when the event ran
   int64_t mask_len;      // rows the keep mask covers
   int64_t mask_off;      // bytes into the keep buffer
-  int64_t pad;
+  int64_t rank_off;      // groups of 32 rows into the rank scratch
 };
 
+// Death times in two launches.  kvs_rank_kernel, one block per event: for
+// each group g of 32 rows of the event's keep mask, rank[rank_off + g] =
+// {kept rows before the group, the group's keep bits}, and kept[event] =
+// rows kept.  kvs_chain_kernel, one
+// thread per (rollout, token): the token's row at the first event after its
+// birth is (rows kept by the event before) + (tokens generated since); at
+// each event it either dies (d = the event's time) or moves to the row its
+// rank gives in the next event's list, where the survivors come first.
 struct KvsDeathLaunch {
   const KvsRollout* rollouts;
   const KvsEvent* events;
   const uint8_t* keep;
   int32_t* death;        // [n][n_pad]
   int32_t* status;       // [n]
-  int32_t* list;         // scratch [n][n_pad]: token ids the cache holds (null when in LDS)
+  uint2* rank;           // scratch: per group of 32 event rows, as above
+  int32_t* kept;         // scratch [n_events]
   int64_t n_pad;
+  int64_t chain_blocks;  // blocks of kvs_chain_kernel per rollout: ceil(n_pad / 256)
   int32_t n;
-  int32_t list_in_lds;   // kvs_death_list_in_lds(n_pad, the device's LDS per block)
+  int32_t n_events;
 };
-
-// Whether kvs_death_kernel keeps a rollout's list of held token ids in LDS
-// (n_pad int32 entries beside its static LDS, within max_lds bytes per
-// block) rather than in the global list scratch.
-bool kvs_death_list_in_lds(int64_t n_pad, int max_lds);
 
 struct KvsBlockLaunch {
   const int32_t* death;  // [n][n_pad]
@@ -77,6 +82,7 @@ struct KvsDenseLaunch {
 };
 
 hipError_t launch_kvs_death(const KvsDeathLaunch& a, hipStream_t s);
+constexpr int kChainThreads = 256;
 hipError_t launch_kvs_block(const KvsBlockLaunch& a, hipStream_t s);
 hipError_t launch_kvs_dense(const KvsDenseLaunch& a, hipStream_t s);
 

@@ -29,14 +29,13 @@ constexpr int kKvsStages = 4;
 
 struct kvs_ctx {
   int32_t device = 0;
-  int max_lds = 0;           // the device's LDS bytes per block
   KvsStage stage[kKvsStages];  // taken in turn; a call waits only if its region is still in flight
   int next_stage = 0;
-  int32_t* list = nullptr;   // death-time scratch of the global-list replay: held token ids per rollout
-  size_t list_cap = 0;       // elements
-  hipEvent_t list_done = nullptr;  // the last global-list replay has finished
-  bool list_pending = false;
-  hipStream_t list_stream = nullptr;
+  char* rank = nullptr;      // death-time scratch: rows kept per event, then the ranks of every mask row
+  size_t rank_cap = 0;       // bytes
+  hipEvent_t rank_done = nullptr;  // the last death-time call that used it has finished
+  bool rank_pending = false;
+  hipStream_t rank_stream = nullptr;
   int2* minmax = nullptr;    // block-mask scratch
   size_t minmax_cap = 0;     // elements
   hipEvent_t minmax_done = nullptr;
@@ -94,10 +93,10 @@ ll_status kvs_ctx_create(int32_t device, kvs_ctx** out) try {
   if (!g.ok()) return fail(LL_EDEVICE, "hipSetDevice(%d) failed", device);
   kvs_ctx* c = new kvs_ctx();
   c->device = device;
-  hipError_t e = hipDeviceGetAttribute(&c->max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, device);
+  hipError_t e = hipSuccess;
   for (int i = 0; i < kKvsStages && e == hipSuccess; ++i)
     e = hipEventCreateWithFlags(&c->stage[i].done, hipEventDisableTiming);
-  if (e == hipSuccess) e = hipEventCreateWithFlags(&c->list_done, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&c->rank_done, hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&c->minmax_done, hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&c->events_done, hipEventDisableTiming);
   if (e != hipSuccess) {
@@ -115,7 +114,7 @@ void kvs_ctx_destroy(kvs_ctx* c) try {
   DeviceGuard g(c->device);
   for (KvsStage& S : c->stage)
     if (S.pending) (void)hipEventSynchronize(S.done);
-  if (c->list_pending) (void)hipEventSynchronize(c->list_done);
+  if (c->rank_pending) (void)hipEventSynchronize(c->rank_done);
   if (c->minmax_pending) (void)hipEventSynchronize(c->minmax_done);
   if (c->events_pending) (void)hipEventSynchronize(c->events_done);
   for (KvsStage& S : c->stage) {
@@ -123,12 +122,12 @@ void kvs_ctx_destroy(kvs_ctx* c) try {
     if (S.host) (void)hipHostFree(S.host);
     if (S.dev) (void)hipFree(S.dev);
   }
-  if (c->list_done) (void)hipEventDestroy(c->list_done);
+  if (c->rank_done) (void)hipEventDestroy(c->rank_done);
   if (c->minmax_done) (void)hipEventDestroy(c->minmax_done);
   if (c->events_done) (void)hipEventDestroy(c->events_done);
   if (c->events) (void)hipFree(c->events);
   if (c->minmax) (void)hipFree(c->minmax);
-  if (c->list) (void)hipFree(c->list);
+  if (c->rank) (void)hipFree(c->rank);
   delete c;
 } catch (...) {
   return;
@@ -162,6 +161,15 @@ ll_status kvs_death_times(kvs_ctx* c, const kvs_rollout_log* logs, int32_t n, in
   }
   if (any_mask && !keep_dev) return fail(LL_EINVAL, "keep masks are NULL");
   if (n_events >= (int64_t{1} << 31)) return fail(LL_EUNSUPPORTED, "too many events");
+  const int64_t chain_blocks = (n_pad + ll::kChainThreads - 1) / ll::kChainThreads;
+  if (static_cast<int64_t>(n) * chain_blocks >= (int64_t{1} << 31))
+    return fail(LL_EUNSUPPORTED, "n * ceil(n_pad / 256) must stay below 2^31");
+  // the rank scratch: rows kept per event, then 8 bytes per group of 32 mask rows
+  const size_t kept_bytes = (sizeof(int32_t) * static_cast<size_t>(n_events) + 255) / 256 * 256;
+  size_t rank_groups = 0;
+  for (int32_t i = 0; i < n; ++i)
+    for (int32_t e = 0; e < logs[i].n_events; ++e) rank_groups += (static_cast<size_t>(logs[i].mask_len[e]) + 31) / 32;
+  const size_t rank_need = kept_bytes + 8 * rank_groups;
 
   DeviceGuard g(c->device);
   if (!g.ok()) return fail(LL_EDEVICE, "hipSetDevice(%d) failed", c->device);
@@ -169,27 +177,24 @@ ll_status kvs_death_times(kvs_ctx* c, const kvs_rollout_log* logs, int32_t n, in
   const size_t roll_bytes = sizeof(ll::KvsRollout) * static_cast<size_t>(n);
   const size_t ev_off = (roll_bytes + 255) / 256 * 256;
   const size_t need = ev_off + sizeof(ll::KvsEvent) * static_cast<size_t>(std::max<int64_t>(n_events, 1));
-  // The held-token list lives in LDS when it fits; otherwise in the
-  // context's list scratch, which one replay at a time may use.
-  const bool in_lds = ll::kvs_death_list_in_lds(n_pad, c->max_lds);
-  if (!in_lds) {
-    const size_t list_need = static_cast<size_t>(n) * static_cast<size_t>(n_pad);
-    if (list_need > c->list_cap) {
-      if (c->list_pending) {  // the last replay that used it must finish before it is freed
-        hipError_t e = hipEventSynchronize(c->list_done);
-        if (e != hipSuccess) return dev_fail(e, "hipEventSynchronize(list scratch)");
-        c->list_pending = false;
-      }
-      if (c->list) (void)hipFree(c->list);
-      c->list = nullptr;
-      c->list_cap = 0;
-      if (hipMalloc(reinterpret_cast<void**>(&c->list), list_need * sizeof(int32_t)) != hipSuccess)
-        return fail(LL_ENOMEM, "cannot allocate %zu bytes of death-time scratch", list_need * sizeof(int32_t));
-      c->list_cap = list_need;
-    } else if (c->list_pending && c->list_stream != st) {
-      hipError_t e = hipStreamWaitEvent(st, c->list_done, 0);
-      if (e != hipSuccess) return dev_fail(e, "hipStreamWaitEvent(list scratch)");
+  // The rank scratch: one call at a time may use it.  A call on another
+  // stream waits on the device for the last one; growing it waits on the host.
+  if (rank_need > c->rank_cap) {
+    if (c->rank_pending) {
+      hipError_t e = hipEventSynchronize(c->rank_done);
+      if (e != hipSuccess) return dev_fail(e, "hipEventSynchronize(rank scratch)");
+      c->rank_pending = false;
     }
+    if (c->rank) (void)hipFree(c->rank);
+    c->rank = nullptr;
+    c->rank_cap = 0;
+    const size_t cap = std::max<size_t>(rank_need + rank_need / 4, size_t{1} << 16);
+    if (hipMalloc(reinterpret_cast<void**>(&c->rank), cap) != hipSuccess)
+      return fail(LL_ENOMEM, "cannot allocate %zu bytes of death-time scratch", cap);
+    c->rank_cap = cap;
+  } else if (c->rank_pending && c->rank_stream != st) {
+    hipError_t e = hipStreamWaitEvent(st, c->rank_done, 0);
+    if (e != hipSuccess) return dev_fail(e, "hipStreamWaitEvent(rank scratch)");
   }
   // the staging region of this call: wait only while the call that used it
   // last (kKvsStages calls ago) has not finished
@@ -215,7 +220,7 @@ ll_status kvs_death_times(kvs_ctx* c, const kvs_rollout_log* logs, int32_t n, in
   c->next_stage = (c->next_stage + 1) % kKvsStages;
   ll::KvsRollout* rolls = reinterpret_cast<ll::KvsRollout*>(S.host);
   ll::KvsEvent* evs = reinterpret_cast<ll::KvsEvent*>(S.host + ev_off);
-  int64_t at = 0;
+  int64_t at = 0, rank_off = 0;
   for (int32_t i = 0; i < n; ++i) {
     const kvs_rollout_log& l = logs[i];
     rolls[i].n_tokens = l.n_tokens;
@@ -227,8 +232,9 @@ ll_status kvs_death_times(kvs_ctx* c, const kvs_rollout_log* logs, int32_t n, in
       ev.time = l.event_time[e];
       ev.mask_len = l.mask_len[e];
       ev.mask_off = off;
-      ev.pad = 0;
+      ev.rank_off = rank_off;
       off += l.mask_len[e];
+      rank_off += (l.mask_len[e] + 31) / 32;
     }
   }
   hipError_t e = hipMemcpyAsync(S.dev, S.host, need, hipMemcpyHostToDevice, st);
@@ -239,21 +245,20 @@ ll_status kvs_death_times(kvs_ctx* c, const kvs_rollout_log* logs, int32_t n, in
   a.keep = keep_dev;
   a.death = death_dev;
   a.status = status_dev;
-  a.list = in_lds ? nullptr : c->list;
-  a.list_in_lds = in_lds ? 1 : 0;
+  a.kept = reinterpret_cast<int32_t*>(c->rank);
+  a.rank = reinterpret_cast<uint2*>(c->rank + kept_bytes);
   a.n_pad = n_pad;
+  a.chain_blocks = chain_blocks;
   a.n = n;
+  a.n_events = static_cast<int32_t>(n_events);
   e = ll::launch_kvs_death(a, st);
-  if (e != hipSuccess) return dev_fail(e, "kvs_death_kernel launch");
+  if (e != hipSuccess) return dev_fail(e, "kvs_rank_kernel / kvs_chain_kernel launch");
   e = hipEventRecord(S.done, st);
+  if (e == hipSuccess) e = hipEventRecord(c->rank_done, st);
   if (e != hipSuccess) return dev_fail(e, "hipEventRecord");
   S.pending = true;
-  if (!in_lds) {
-    e = hipEventRecord(c->list_done, st);
-    if (e != hipSuccess) return dev_fail(e, "hipEventRecord");
-    c->list_pending = true;
-    c->list_stream = st;
-  }
+  c->rank_pending = true;
+  c->rank_stream = st;
   return LL_OK;
 } catch (...) {
   return host_exception(nullptr);

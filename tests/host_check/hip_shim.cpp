@@ -300,10 +300,16 @@ hipError_t launch_rope_inplace_mla(const RopeRowsLaunch&, const double*, int, hi
 }
 int64_t rope_rows_blocks_per_plane(const RopeRowsLaunch&, int64_t) { return 1; }
 
-bool kvs_death_list_in_lds(int64_t n_pad, int max_lds) { return n_pad * 4 + 1040 <= max_lds; }
 hipError_t launch_kvs_death(const KvsDeathLaunch& a, hipStream_t) {
-  // the list scratch must exist exactly when the list is not in LDS
-  return (a.list_in_lds != 0) == (a.list == nullptr) ? hipSuccess : hipErrorInvalidValue;
+  // the scratch must hold every event's groups of 32 rows behind the
+  // per-event counts
+  int64_t need = 0;
+  for (int32_t e = 0; e < a.n_events; ++e) {
+    if (a.events[e].rank_off != need) return hipErrorInvalidValue;
+    need += (a.events[e].mask_len + 31) / 32;
+  }
+  if (a.n_events == 0) return hipSuccess;  // no event: neither scratch array is read
+  return a.rank && a.kept && (reinterpret_cast<uintptr_t>(a.rank) & 15) == 0 ? hipSuccess : hipErrorInvalidValue;
 }
 hipError_t launch_kvs_block(const KvsBlockLaunch&, hipStream_t) { return hipSuccess; }
 hipError_t launch_kvs_dense(const KvsDenseLaunch&, hipStream_t) { return hipSuccess; }
