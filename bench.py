@@ -36,10 +36,19 @@ Other workloads (one JSON line each, not the headline):
                                      32768 tokens: death times from the
                                      eviction logs, 128 x 128 block mask and the
                                      dense bit mask (8.6 GB written)
+  --workload splice_32k_27layer_inplace
+                                     the headline shape with no stub: Delta =
+                                     -6144 is a whole number of pages, so every
+                                     downstream row only has its k_pe band
+                                     turned in place (127 MB)
+  --workload drift_128k_60layer      131072 tokens x 60 layers, ten successive
+                                     seeded splices; per-splice GB/s and the
+                                     k_pe drift per number of rotations
   --workload rope_rows_32k_27layer   per-row-angle rotation: all 32768 rows of
                                      the 27-layer MLA cache gathered with k_pe
-                                     turned back by its position (2.04 GB), and
-                                     the same rows turned in place
+                                     turned back by its position (2.04 GB)
+  --workload rope_rows_32k_27layer_inplace
+                                     the same rows' bands turned in place
   --workload evict_32x16k_llama8b_p16
                                      KV-streams eviction of 32 rollouts x
                                      16384 tokens on a Llama-3-8B shaped GQA
