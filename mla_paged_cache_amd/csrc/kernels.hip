@@ -17,10 +17,13 @@
 //  * table_write_kernel: page-table row rewrites on their own.
 //
 // The row kernels are bound by HBM bandwidth (0.08 flop per byte), so they
-// are flat 16-byte gathers: 256-thread blocks, each block inside one layer,
-// one 64-byte descriptor load before the data load, non-temporal loads and
-// stores (the in-place band rotation: plain stores).  Only k_pe chunks (8 of
-// every 72) do arithmetic.
+// are flat 16-byte gathers, one chunk per thread, each block inside one layer
+// (splice: 256-thread blocks; eviction: one wave per block), one 64-byte
+// descriptor load before the data load, non-temporal loads, and stores with
+// the streaming cache policy through a buffer descriptor on the wave's
+// destination page (page size >= 8; smaller pages: non-temporal stores).  The
+// in-place band rotation keeps plain stores.  Only k_pe chunks (8 of every
+// 72) do arithmetic.
 #include <mutex>
 
 #include "device_common.h"
@@ -134,12 +137,12 @@ __global__ __launch_bounds__(kFlatThreads) void splice_inplace_kernel(SpliceLaun
     if (live[i]) *ptr[i] = v[i];
 }
 
-// Flat gather, two chunks per thread: block k of a layer covers chunks
-// 512 k .. 512 k + 511, thread t taking chunks 512 k + t and 512 k + 256 + t;
-// both loads are issued before either store, so a wave keeps twice the bytes
-// in flight.  Blocks [0, L * move_blocks_per_layer) move rows of fresh
-// pages.  Within one page-task of P rows the 72 * P chunks are ordered c_kv
-// first (chunk 64 * row + k, k < 64) and then k_pe (64 * P + 8 * row + k,
+// Flat gather, one chunk per thread: block k of a layer covers chunks 256 k ..
+// 256 k + 255.  (Two chunks per thread, both loads issued before either store,
+// measured slower with the streaming stores: 182-184 us against 180.5 us for
+// the 32k x 27 splice.)  Blocks [0, L * move_blocks_per_layer) move rows of
+// fresh pages.  Within one page-task of P rows the 72 * P chunks are ordered
+// c_kv first (chunk 64 * row + k, k < 64) and then k_pe (64 * P + 8 * row + k,
 // k < 8): for P >= 8 every wave is then either a pure copy wave or a pure
 // rotate wave, and the rotation code is skipped by the copy waves.  The
 // remaining blocks rewrite page-table rows (no block reads the table).
@@ -148,13 +151,13 @@ template <int PAIRING, bool WAVE_TASK>
 __global__ __launch_bounds__(kFlatThreads) void splice_kernel(SpliceLaunch a) {
   constexpr int CPT = kSpliceChunksPerThread;
   const int64_t b = blockIdx.x;
-  const int64_t move_blocks = a.move_blocks_per_layer * a.num_layers;
+  const int64_t bpl = a.move_blocks_per_layer;
+  const int64_t move_blocks = bpl * a.num_layers;
   if (b >= move_blocks) {
     table_write_block(a.twrites, a.tables, a.page_table, a.max_pages_per_seq, b - move_blocks);
     return;
   }
   const int64_t bb = b;
-  const int64_t bpl = a.move_blocks_per_layer;
   const int l = static_cast<int>(bb / bpl);
   const uint32_t c0 = static_cast<uint32_t>((bb - static_cast<int64_t>(l) * bpl) * kFlatThreads * CPT + threadIdx.x);
   const int shift = a.page_shift;
@@ -164,6 +167,8 @@ __global__ __launch_bounds__(kFlatThreads) void splice_kernel(SpliceLaunch a) {
   chunk_t v[CPT];
   const chunk_t* srcs[CPT];
   int64_t dsts[CPT];
+  const chunk_t* dpage[CPT];
+  uint32_t doff[CPT];
   bool lives[CPT], rots[CPT];
   int kcs[CPT], dirs[CPT];
 #pragma unroll
@@ -201,6 +206,8 @@ __global__ __launch_bounds__(kFlatThreads) void splice_kernel(SpliceLaunch a) {
     }
     srcs[u] = src + col;
     dsts[u] = dst_row * kRowChunks + col;
+    dpage[u] = layer + (static_cast<int64_t>(t.dst_page) << shift) * kRowChunks;
+    doff[u] = (r * kRowChunks + col) * 16u;
     lives[u] = live;
     rots[u] = rot;
     kcs[u] = static_cast<int>(col) - kKpeChunk0;
@@ -215,23 +222,27 @@ __global__ __launch_bounds__(kFlatThreads) void splice_kernel(SpliceLaunch a) {
   for (int u = 0; u < CPT; ++u) {
     if (!WAVE_TASK || kcs[u] >= 0)
       v[u] = rotate_kpe<PAIRING>(v[u], lives[u] && rots[u] && kcs[u] >= 0, kcs[u], a.dirs + dirs[u]);
-    if (lives[u]) __builtin_nontemporal_store(v[u], const_cast<chunk_t*>(layer) + dsts[u]);
+    if constexpr (WAVE_TASK) {  // the destination page is wave-uniform
+      if (lives[u]) store_chunk_policy(v[u], dpage[u], doff[u], (static_cast<uint32_t>(kRowChunks) << shift) * 16u);
+    } else {
+      if (lives[u]) __builtin_nontemporal_store(v[u], const_cast<chunk_t*>(layer) + dsts[u]);
+    }
   }
 }
 
 // Flat copy of the kept rows that land in fresh pages (rotation off), then
 // the page-table rewrites in the blocks after the row blocks.
 template <bool WAVE_TASK>
-__global__ __launch_bounds__(kFlatThreads) void evict_move_kernel(EvictLaunch a) {
+__global__ __launch_bounds__(kEvictThreads) void evict_move_kernel(EvictLaunch a) {
   const int64_t b = blockIdx.x;
-  const int64_t move_blocks = a.blocks_per_layer * a.num_layers;
+  const int64_t bpl = a.blocks_per_layer;
+  const int64_t move_blocks = bpl * a.num_layers;
   if (b >= move_blocks) {
     table_write_block(a.twrites, a.tables, a.page_table, a.max_pages_per_seq, b - move_blocks);
     return;
   }
-  const int l = static_cast<int>(b / a.blocks_per_layer);
-  const uint32_t c = static_cast<uint32_t>((b - static_cast<int64_t>(l) * a.blocks_per_layer) * kFlatThreads +
-                                           threadIdx.x);
+  const int l = static_cast<int>(b / bpl);
+  const uint32_t c = static_cast<uint32_t>((b - static_cast<int64_t>(l) * bpl) * kEvictThreads + threadIdx.x);
   const int shift = a.page_shift;
   const uint32_t row_flat = c / kRowChunks;
   const uint32_t col = c - row_flat * kRowChunks;
@@ -251,8 +262,13 @@ __global__ __launch_bounds__(kFlatThreads) void evict_move_kernel(EvictLaunch a)
   }
   const chunk_t* layer = a.layers[l];
   const chunk_t v = __builtin_nontemporal_load(layer + src_row * kRowChunks + col);
-  __builtin_nontemporal_store(v, const_cast<chunk_t*>(layer) +
-                                     ((static_cast<int64_t>(t.dst_page) << shift) + r) * kRowChunks + col);
+  if constexpr (WAVE_TASK) {  // the destination page is wave-uniform
+    store_chunk_policy(v, layer + (static_cast<int64_t>(t.dst_page) << shift) * kRowChunks, (r * kRowChunks + col) * 16u,
+                       (static_cast<uint32_t>(kRowChunks) << shift) * 16u);
+  } else {
+    __builtin_nontemporal_store(v, const_cast<chunk_t*>(layer) +
+                                       ((static_cast<int64_t>(t.dst_page) << shift) + r) * kRowChunks + col);
+  }
 }
 
 __global__ __launch_bounds__(256) void table_write_kernel(TableLaunch a) {
@@ -569,7 +585,7 @@ hipError_t launch_evict_move(const EvictLaunch& a, hipStream_t s, const Stamp& t
   const int64_t grid = a.blocks_per_layer * a.num_layers + a.n_twrites;
   if (grid == 0) return stamp_empty(s, t);
   void (*k)(EvictLaunch) = a.page_shift >= 3 ? evict_move_kernel<true> : evict_move_kernel<false>;
-  return dispatch(k, dim3(static_cast<unsigned>(grid)), dim3(kFlatThreads), s, t, true, true, a);
+  return dispatch(k, dim3(static_cast<unsigned>(grid)), dim3(kEvictThreads), s, t, true, true, a);
 }
 
 hipError_t launch_table_write(const TableLaunch& a, hipStream_t s) {

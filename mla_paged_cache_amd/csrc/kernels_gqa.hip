@@ -188,16 +188,16 @@ __global__ __launch_bounds__(kFlatThreads) void gqa_splice_kernel(GqaSpliceLaunc
 // Eviction on K / V planes: flat copy of the kept rows that land in fresh
 // pages, then the page-table rewrites.
 template <bool WAVE_TASK>
-__global__ __launch_bounds__(kFlatThreads) void plane_evict_kernel(PlaneEvictLaunch a) {
+__global__ __launch_bounds__(kEvictThreads) void plane_evict_kernel(PlaneEvictLaunch a) {
   const int64_t b = blockIdx.x;
-  const int64_t move_blocks = a.blocks_per_plane * a.num_planes;
+  const int64_t bpp = a.blocks_per_plane;
+  const int64_t move_blocks = bpp * a.num_planes;
   if (b >= move_blocks) {
     table_write_block(a.twrites, a.tables, a.page_table, a.max_pages_per_seq, b - move_blocks);
     return;
   }
-  const int plane = static_cast<int>(b / a.blocks_per_plane);
-  const uint32_t c = static_cast<uint32_t>((b - static_cast<int64_t>(plane) * a.blocks_per_plane) * kFlatThreads +
-                                           threadIdx.x);
+  const int plane = static_cast<int>(b / bpp);
+  const uint32_t c = static_cast<uint32_t>((b - static_cast<int64_t>(plane) * bpp) * kEvictThreads + threadIdx.x);
   const int shift = a.page_shift;
   const uint32_t rc = static_cast<uint32_t>(a.row_chunks);
   const uint32_t row_flat = c / rc;
@@ -218,7 +218,12 @@ __global__ __launch_bounds__(kFlatThreads) void plane_evict_kernel(PlaneEvictLau
   }
   const chunk_t* layer = a.planes[plane];
   const chunk_t v = __builtin_nontemporal_load(layer + src_row * rc + col);
-  __builtin_nontemporal_store(v, const_cast<chunk_t*>(layer) + ((static_cast<int64_t>(t.dst_page) << shift) + r) * rc + col);
+  if constexpr (WAVE_TASK) {  // the destination page is wave-uniform
+    store_chunk_policy(v, layer + (static_cast<int64_t>(t.dst_page) << shift) * rc, (r * rc + col) * 16u,
+                       (rc << shift) * 16u);
+  } else {
+    __builtin_nontemporal_store(v, const_cast<chunk_t*>(layer) + ((static_cast<int64_t>(t.dst_page) << shift) + r) * rc + col);
+  }
 }
 
 }  // namespace
@@ -249,7 +254,7 @@ hipError_t launch_plane_evict(const PlaneEvictLaunch& a, hipStream_t s, const St
   if (grid == 0) return stamp_empty(s, t);
   void (*k)(PlaneEvictLaunch) =
       (int64_t{a.row_chunks} << a.page_shift) % 64 == 0 ? plane_evict_kernel<true> : plane_evict_kernel<false>;
-  return dispatch(k, dim3(static_cast<unsigned>(grid)), dim3(kFlatThreads), s, t, true, true, a);
+  return dispatch(k, dim3(static_cast<unsigned>(grid)), dim3(kEvictThreads), s, t, true, true, a);
 }
 
 }  // namespace ll

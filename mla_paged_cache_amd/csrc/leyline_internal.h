@@ -305,17 +305,21 @@ hipError_t noalloc_scratch_init(int device);
 void* noalloc_scratch(int device);
 
 // Chunks each thread of splice_kernel moves.
-constexpr int kSpliceChunksPerThread = 2;
+constexpr int kSpliceChunksPerThread = 1;
+
+// Threads per block of the eviction's row copies (evict_move_kernel,
+// plane_evict_kernel): one wave per block.
+constexpr int kEvictThreads = 64;
 
 // splice_inplace_kernel: groups of 8 rows per wave (one 128-byte k_pe line
 // per row and lane group), and rows per 256-thread block.
 constexpr int kInPlaceGroups = 8;
 constexpr int kInPlaceRowsPerBlock = kFlatThreads / 64 * 8 * kInPlaceGroups;
 
-// Blocks of kFlatThreads that cover `chunks` chunks of one layer, each thread
-// taking `per_thread` of them.
-inline int64_t flat_blocks(int64_t chunks, int per_thread = 1) {
-  const int64_t per_block = int64_t{kFlatThreads} * per_thread;
+// Blocks of `threads` threads that cover `chunks` chunks of one layer, each
+// thread taking `per_thread` of them.
+inline int64_t flat_blocks(int64_t chunks, int per_thread = 1, int threads = kFlatThreads) {
+  const int64_t per_block = int64_t{threads} * per_thread;
   return (chunks + per_block - 1) / per_block;
 }
 

@@ -913,7 +913,7 @@ ll_status evict_device_plan(ll_pool* p, const int32_t* seq_ids, int32_t n, const
     a.row_chunks = static_cast<int32_t>(rc_chunks);
     a.tasks = al.tasks;
     a.n_tasks = n_tasks;
-    a.blocks_per_plane = ll::flat_blocks(n_tasks * P * rc_chunks);
+    a.blocks_per_plane = ll::flat_blocks(n_tasks * P * rc_chunks, 1, ll::kEvictThreads);
     a.src_rows = sc.src_rows;
     a.n_twrites = 0;
     e = ll::launch_plane_evict(a, st, t0);
@@ -925,7 +925,7 @@ ll_status evict_device_plan(ll_pool* p, const int32_t* seq_ids, int32_t n, const
     a.page_shift = p->page_shift;
     a.tasks = al.tasks;
     a.n_tasks = n_tasks;
-    a.blocks_per_layer = ll::flat_blocks(n_tasks * P * rc_chunks);
+    a.blocks_per_layer = ll::flat_blocks(n_tasks * P * rc_chunks, 1, ll::kEvictThreads);
     a.src_rows = sc.src_rows;
     a.n_twrites = 0;
     e = ll::launch_evict_move(a, st, t0);
