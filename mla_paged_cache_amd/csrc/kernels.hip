@@ -250,15 +250,14 @@ __global__ __launch_bounds__(kEvictThreads) void evict_move_kernel(EvictLaunch a
   if (ti >= a.n_tasks) return;
   const EvictTask t = load_task<WAVE_TASK>(a.tasks, ti);
   const uint32_t r = row_flat & ((1u << shift) - 1u);
-  const int64_t j = (static_cast<int64_t>(t.q) << shift) + r;
-  if (j >= t.n_new) return;
+  if (static_cast<int32_t>(r) >= t.rows) return;
   int64_t src_row;
   if (t.src_off0 >= 0) {
     const int32_t o = t.src_off0 + static_cast<int32_t>(r);
     const int32_t P = 1 << shift;
-    src_row = o < P ? (static_cast<int64_t>(t.src_page0) << shift) + o : (static_cast<int64_t>(t.src_page1) << shift) + (o - P);
+    src_row = o < P ? (static_cast<int64_t>(t.src0) << shift) + o : (static_cast<int64_t>(t.src1) << shift) + (o - P);
   } else {
-    src_row = a.src_rows[t.src_off + j];
+    src_row = a.src_rows[static_cast<int64_t>(t.src0) + r];
   }
   const chunk_t* layer = a.layers[l];
   const chunk_t v = __builtin_nontemporal_load(layer + src_row * kRowChunks + col);

@@ -148,26 +148,25 @@ __global__ __launch_bounds__(256) void alloc_tables_kernel(AllocLaunch a) {
     } else {
       const int32_t f = base + a.rank[e.reuse_off + q];
       page = select_free(a, f);
+      // src_rows entries of one call number less than the pool's rows (< 2^31)
+      const int64_t j0 = q << a.page_shift;
+      const int64_t k = n_new - j0 < P ? n_new - j0 : P;
       EvictTask t{};
-      t.src_off = e.src_off;
-      t.q = static_cast<int32_t>(q);
       t.dst_page = page;
-      t.n_new = static_cast<int32_t>(n_new);
-      t.src_page0 = -1;
-      t.src_page1 = -1;
+      t.rows = static_cast<int16_t>(k);
       t.src_off0 = -1;
+      t.src0 = static_cast<int32_t>(e.src_off + j0);
+      t.src1 = -1;
       if (a.src_logical) {
         // live rows that are consecutive old rows lie in at most two old
         // pages: the row kernel then needs no per-row source lookup
-        const int64_t j0 = q << a.page_shift;
-        const int64_t k = n_new - j0 < P ? n_new - j0 : P;
         const int32_t first = a.src_logical[e.src_off + j0];
         const int32_t last = a.src_logical[e.src_off + j0 + k - 1];
         if (last - first == k - 1) {
           const int32_t off = first & static_cast<int32_t>(P - 1);
-          t.src_page0 = old_t[first >> a.page_shift];
-          t.src_page1 = off + k > P ? old_t[(first >> a.page_shift) + 1] : -1;
-          t.src_off0 = off;
+          t.src0 = old_t[first >> a.page_shift];
+          t.src1 = off + k > P ? old_t[(first >> a.page_shift) + 1] : -1;
+          t.src_off0 = static_cast<int16_t>(off);
         }
       }
       a.tasks[f] = t;

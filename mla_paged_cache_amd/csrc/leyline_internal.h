@@ -76,20 +76,21 @@ struct alignas(16) EvictSeq {
   int32_t pad[3];
 };
 
-// One fresh destination page of an eviction.
+// One fresh destination page of an eviction: 16 bytes, so that the copy
+// kernels' task reads (every XCD reads every task on every layer pass) take
+// half the lines a 32-byte task did.
 struct alignas(16) EvictTask {
-  int64_t src_off;     // where this sequence's src_rows start
-  int32_t q;           // new logical page
-  int32_t dst_page;    // physical page written
-  int32_t n_new;       // rows after the eviction
-  // when the page's live rows are consecutive old rows: the old page of the
-  // first, the next old page (-1 when they all lie in the first) and the
-  // first row's offset in its page; src_off0 = -1: read src_rows instead
-  int32_t src_page0;
-  int32_t src_page1;
-  int32_t src_off0;
+  int32_t dst_page;  // physical page written
+  int16_t rows;      // live rows of the page (1..P)
+  // when the page's live rows are consecutive old rows: src_off0 = the first
+  // row's offset in its old page src0, src1 = the next old page (-1 when
+  // they all lie in src0); src_off0 = -1: row r of the page reads its source
+  // row from src_rows[src0 + r]
+  int16_t src_off0;
+  int32_t src0;
+  int32_t src1;
 };
-static_assert(sizeof(EvictTask) == 32, "an eviction task is two 16-byte words");
+static_assert(sizeof(EvictTask) == 16, "an eviction task is one 16-byte word");
 
 struct SpliceLaunch {
   const chunk_t* const* layers;  // device array [num_layers] of pool bases

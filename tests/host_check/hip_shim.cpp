@@ -263,8 +263,9 @@ hipError_t launch_alloc_tables(const AllocLaunch& a, hipStream_t, const Stamp&) 
           for (; f > 0; --f) bits &= bits - 1;
           page = w * 64 + __builtin_ctzll(bits);
         }
-        a.tasks[a.fresh_base[b] + a.rank[e.reuse_off + q]] = EvictTask{e.src_off, static_cast<int32_t>(q), page,
-                                                                         static_cast<int32_t>(n_new), -1, -1, -1};
+        const int64_t rows = std::min<int64_t>(P, n_new - q * P);
+        a.tasks[a.fresh_base[b] + a.rank[e.reuse_off + q]] =
+            EvictTask{page, static_cast<int16_t>(rows), -1, static_cast<int32_t>(e.src_off + q * P), -1};
       }
       a.new_table[e.reuse_off + q] = page;
     }
