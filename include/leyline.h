@@ -360,6 +360,24 @@ ll_status ll_seq_lengths(const ll_pool* pool, const int32_t* seq_ids, int32_t n,
 typedef enum { LL_SPLICE_PLAN_AUTO = 0, LL_SPLICE_PLAN_HOST = 1 } ll_splice_planner;
 ll_status ll_pool_set_splice_planner(ll_pool* pool, int32_t planner);
 
+/* Library setting, no passage of the pages defines it: the page plan's reuse
+ * rule ([Leyline] section 2.3 decomposes an edit into block-level operations;
+ * keeping an old page whose rows stay at their offsets is this library's).
+ * on = 1 (the default): a new page keeps an old one when all its live rows are
+ * rows of that page at unchanged offsets, as described at the top of this
+ * file.  on = 0: no new page keeps an old one -- every page of a sequence that
+ * leyline_splice (AMORTIZE or FORGET), leyline_splice_noalloc or
+ * kv_evict_compact rewrites is fresh (lowest free pages first, in batch
+ * order), every live row is written into it (downstream k_pe turned as
+ * always) and every old page of the sequence is freed; row values, lengths
+ * and positions are the same as with reuse on, only the physical pages differ
+ * (a compaction of the sequence into the lowest free pages).  Such calls need
+ * as many free pages as the new pages of their sequences.  Applies to calls
+ * made after it; ll_ptable_reindex moves no rows and is not affected.
+ * Errors: LL_EINVAL (on not 0 or 1), LL_EUNSUPPORTED (on = 0 on a pool of
+ * page size 1, where a page is one row). */
+ll_status ll_pool_set_page_reuse(ll_pool* pool, int32_t on);
+
 /* Library bookkeeping, no passage of the pages defines it.
  * Kernel timing.  `enable` = n > 0 times every n-th launch (counted from
  * this call; 1: every launch) of the row-moving kernel (kernel 0; on the

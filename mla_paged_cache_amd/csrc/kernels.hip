@@ -321,6 +321,7 @@ __global__ __launch_bounds__(256) void splice_plan_kernel(DirectPlanArgs a) {
       reuse = q;
     else
       reuse = ((lo - delta) & (P - 1)) == 0 ? (lo - delta) >> shift : -1;
+    if (!a.page_reuse) reuse = -1;  // page reuse off: every new page is fresh
     // the host checked that its plan puts fresh and rotated pages in the
     // ranges it sent; the guards only keep every access inside the buffers
     if (reuse >= D.old_pages) reuse = D.old_pages - 1;
@@ -502,7 +503,7 @@ __global__ __launch_bounds__(kScanThreads) void keep_scan_kernel(ScanLaunch a) {
     const int64_t k = (n_new - (q << shift)) < P ? (n_new - (q << shift)) : P;
     const int64_t f = out_logical[q << shift];
     const int64_t l = out_logical[(q << shift) + k - 1];
-    const bool keep = (f & pmask) == 0 && l - f == k - 1;
+    const bool keep = a.page_reuse && (f & pmask) == 0 && l - f == k - 1;
     reuse[q] = keep ? static_cast<int32_t>(f >> shift) : -1;
     if (keep) kept[f >> shift] = 1;
   }

@@ -203,6 +203,7 @@ struct ScanLaunch {
   // src_logical; a dropped row's page gets freed_bytes[page] = 1 (each page
   // has one writer; zeroed before the scan)
   uint8_t* freed_bytes;
+  int32_t page_reuse;          // 0: no new page keeps an old one (every new page is fresh)
 };
 
 // Page size 1, after the keep scan: blocks [0, n) write each sequence's new
@@ -262,6 +263,8 @@ struct DirectPlanArgs {
   int32_t n_runs;
   int32_t max_pages_per_seq;
   int32_t gqa;
+  int32_t page_reuse;          // 0: every new page is fresh
+  int32_t pad0;
   int64_t n_move_tasks;
   int64_t n_rot_tasks;
   int64_t n_entries;           // length of the packed table array

@@ -238,6 +238,7 @@ struct ll_pool {
   bool unevented = false;
   hipEvent_t lazy_ev = nullptr;
   int32_t splice_planner = LL_SPLICE_PLAN_AUTO;
+  bool page_reuse = true;       // false: every new page of a rewritten sequence is fresh
   char* d_direct = nullptr;     // tasks, tables and rotation tables of device-planned splices
   size_t direct_cap = 0;
   bool poisoned = false;
@@ -713,6 +714,7 @@ void plan_splice(const ll_pool* p, const ll_directive& d, const SeqState& s, Spl
       const int64_t src0 = a - delta;  // first source row, page-aligned iff delta % P == 0
       if ((src0 & (P - 1)) == 0) reuse = src0 / P;
     }
+    if (!p->page_reuse) reuse = -1;
     out->reuse[q] = static_cast<int32_t>(reuse);
     if (reuse < 0) ++out->fresh;
     else if (has_down && delta != 0 && d.mode == LL_AMORTIZE) out->inplace[q] = 1;
@@ -812,6 +814,7 @@ ll_status evict_device_plan(ll_pool* p, const int32_t* seq_ids, int32_t n, const
   sc.kept = reinterpret_cast<uint8_t*>(d + off_kept);
   sc.freed = reinterpret_cast<unsigned long long*>(d + off_freed);
   sc.freed_bytes = reinterpret_cast<uint8_t*>(d + off_fbytes);
+  sc.page_reuse = p->page_reuse ? 1 : 0;
   const bool moves = P > 1;
   // page size > 1 ORs freed pages into the bitmap; page size 1 marks bytes
   hipError_t e = moves ? ll::launch_zero_words(sc.freed, n_words, st)
@@ -1571,6 +1574,7 @@ static ll_status splice_impl(ll_pool* p, const ll_directive* dirs, int32_t n, vo
     da.n_runs = static_cast<int32_t>(run_page.size());
     da.max_pages_per_seq = p->desc.max_pages_per_seq;
     da.gqa = p->gqa ? 1 : 0;
+    da.page_reuse = p->page_reuse ? 1 : 0;
     da.n_move_tasks = n_move_tasks;
     da.n_rot_tasks = n_rot_tasks;
     da.n_entries = n_entries;
@@ -1957,6 +1961,14 @@ ll_status ll_pool_set_splice_planner(ll_pool* p, int32_t planner) {
   if (planner != LL_SPLICE_PLAN_AUTO && planner != LL_SPLICE_PLAN_HOST)
     return fail(LL_EINVAL, "unknown splice planner %d", planner);
   p->splice_planner = planner;
+  return LL_OK;
+}
+
+ll_status ll_pool_set_page_reuse(ll_pool* p, int32_t on) {
+  if (ll_status rc = enter(p)) return rc;
+  if (on != 0 && on != 1) return fail(LL_EINVAL, "page reuse must be 0 or 1, not %d", on);
+  if (!on && p->P == 1) return fail(LL_EUNSUPPORTED, "at page size 1 a page is one row: there is nothing to compact");
+  p->page_reuse = on != 0;
   return LL_OK;
 }
 

@@ -31,7 +31,7 @@ EXPORTS = (
     "ll_rope_delta_table", "ll_last_plan_stats", "ll_pool_set_profiling", "ll_profile_read",
     "ll_last_error", "ll_status_str", "ll_pool_create_gqa",
     "kvs_ctx_create", "kvs_ctx_destroy", "kvs_death_times", "kvs_block_mask", "kvs_dense_mask",
-    "ll_rope_rows", "ll_pool_set_splice_planner", "ll_last_plan_bytes", "ll_seq_lengths",
+    "ll_rope_rows", "ll_pool_set_splice_planner", "ll_pool_set_page_reuse", "ll_last_plan_bytes", "ll_seq_lengths",
     "leyline_splice_noalloc",
 )
 
@@ -139,6 +139,7 @@ def _load():
         "ll_seq_lengths": (i32, [vp, vp, i32, vp]),
         "ll_pool_set_profiling": (i32, [vp, i32]),
         "ll_pool_set_splice_planner": (i32, [vp, i32]),
+        "ll_pool_set_page_reuse": (i32, [vp, i32]),
         "ll_profile_read": (i32, [vp, i32, P(i64), P(ctypes.c_double), P(i64), P(ctypes.c_float), i64]),
         "ll_rope_rows": (i32, [vp, i32, i64, i64, vp, vp, i64, vp]),
         "kvs_ctx_create": (i32, [i32, P(vp)]),
@@ -418,6 +419,12 @@ class Pool:
         from kernel arguments) or SPLICE_PLAN_HOST (always staged and
         uploaded)."""
         _check(_lib.ll_pool_set_splice_planner(self._h, int(planner)))
+
+    def set_page_reuse(self, on: bool) -> None:
+        """True (default): a new page keeps an old one whose rows stay at their
+        offsets.  False: every page of a rewritten sequence is fresh (the
+        sequence is compacted into the lowest free pages); not on page size 1."""
+        _check(_lib.ll_pool_set_page_reuse(self._h, 1 if on else 0))
 
     def set_profiling(self, enable: bool, every: int = 1) -> None:
         """Time every `every`-th launch of each profiled kernel while enabled."""

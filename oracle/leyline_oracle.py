@@ -364,11 +364,15 @@ def _validate_directives(state: CacheState, directives):
 # Step a3: the page plan (reuse rule, lowest-free-first allocation, release)
 # ---------------------------------------------------------------------------
 
-def page_plan(old_table, P: int, kind: np.ndarray, index: np.ndarray):
+def page_plan(old_table, P: int, kind: np.ndarray, index: np.ndarray, reuse_pages: bool = True):
     """For each new logical page q, the old logical page it reuses, or -1 if it
     must be fresh.  A page is reused iff each of its live rows is an old row of
-    one and the same old page, sitting at the same offset it will occupy."""
+    one and the same old page, sitting at the same offset it will occupy.
+    With reuse_pages False (the library's page-reuse setting turned off) no
+    page is reused: every new page is fresh."""
     n_new = len(kind)
+    if not reuse_pages:
+        return [-1] * (-(-n_new // P))
     plan = []
     for q in range(-(-n_new // P)):
         lo, hi = q * P, min(q * P + P, n_new)
@@ -383,7 +387,7 @@ def page_plan(old_table, P: int, kind: np.ndarray, index: np.ndarray):
     return plan
 
 
-def _apply(state: CacheState, requests, rotate_by, pairing, base):
+def _apply(state: CacheState, requests, rotate_by, pairing, base, reuse_pages=True):
     """Carry out planned requests on a copy of `state`.
 
     requests: list of (seq, n_new, kind, index, downstream, stub, next_pos).
@@ -396,7 +400,7 @@ def _apply(state: CacheState, requests, rotate_by, pairing, base):
     plans = []
     need = 0
     for (seq, n_new, kind, index, downstream, stub, npos) in requests:
-        plan = page_plan(state.tables[seq], P, kind, index)
+        plan = page_plan(state.tables[seq], P, kind, index, reuse_pages)
         plans.append(plan)
         need += sum(1 for x in plan if x < 0)
     if need > len(free_sorted):
@@ -462,9 +466,11 @@ def _move_rows(old: CacheState, new: CacheState, seq, new_t, plan, n_new, kind, 
 # Entry points: splice (Leyline AMORTIZE / FORGET) and eviction (KV-streams)
 # ---------------------------------------------------------------------------
 
-def splice(state: CacheState, directives, pairing: str = "interleaved", base: float = 10000.0):
+def splice(state: CacheState, directives, pairing: str = "interleaved", base: float = 10000.0,
+           reuse_pages: bool = True):
     """Apply a batch of directives, one per sequence.  Returns (new_state,
-    plans), plans[i][q] = reused old logical page or -1 for a fresh page."""
+    plans), plans[i][q] = reused old logical page or -1 for a fresh page.
+    reuse_pages False: every new page is fresh (see page_plan)."""
     _validate_directives(state, directives)
     requests, rotate_by = [], {}
     for d in directives:
@@ -483,12 +489,13 @@ def splice(state: CacheState, directives, pairing: str = "interleaved", base: fl
         rotate_by[d.seq] = delta
         requests.append((d.seq, n + delta, kind, index, downstream, d.stub,
                          state.next_pos[d.seq] + delta))
-    return _apply(state, requests, rotate_by, pairing, base)
+    return _apply(state, requests, rotate_by, pairing, base, reuse_pages)
 
 
-def evict(state: CacheState, seqs, masks):
+def evict(state: CacheState, seqs, masks, reuse_pages: bool = True):
     """KV-streams eviction: keep exactly the rows whose mask entry is nonzero,
-    in their order, unchanged (no rotation, no position reset)."""
+    in their order, unchanged (no rotation, no position reset).  reuse_pages
+    False: every new page is fresh (see page_plan)."""
     if len(set(seqs)) != len(seqs):
         raise InvalidRequest("sequence appears twice in one batch")
     requests = []
@@ -502,7 +509,7 @@ def evict(state: CacheState, seqs, masks):
         n_new = len(src)
         requests.append((seq, n_new, np.zeros(n_new, np.int64), src.astype(np.int64),
                          np.zeros(n_new, bool), None, state.next_pos[seq]))
-    return _apply(state, requests, {}, "interleaved", 10000.0)
+    return _apply(state, requests, {}, "interleaved", 10000.0, reuse_pages)
 
 
 def ptable_reindex(state: CacheState, seq: int, keep_pages):

@@ -12,6 +12,7 @@
 //   evict k (s mask)*k   (mask: 0/1 string, "-" when empty)
 //                                             -> "evict <status> <fresh> <freed>"
 //   reindex s k p_1 .. p_k                    -> "reindex <status>"
+//   reuse on                                  -> "reuse <status>"   (page reuse on / off)
 //   rope s r0 n in_place                      -> "rope <status>"
 //   books                                     -> "seq s <status> len pos k p_1 .. p_k" per row,
 //                                                then "free <n>"
@@ -334,6 +335,10 @@ int main() {
       std::vector<int32_t> keep(static_cast<size_t>(k));
       for (auto& p : keep) in >> p;
       std::printf("reindex %d\n", ll_ptable_reindex(g.pool, s, keep.data(), k, nullptr));
+    } else if (op == "reuse") {
+      int32_t on = 1;
+      in >> on;
+      std::printf("reuse %d\n", ll_pool_set_page_reuse(g.pool, on));
     } else if (op == "rope") {
       int32_t s = 0, in_place = 1;
       int64_t r0 = 0, n = 0;

@@ -145,6 +145,7 @@ hipError_t launch_splice_plan(const DirectPlanArgs& a, int32_t, hipStream_t) {
         reuse = q;
       else
         reuse = ((lo - D.delta) % P) == 0 ? (lo - D.delta) / P : -1;
+      if (!a.page_reuse) reuse = -1;
       int32_t page;
       if (reuse >= 0) {
         page = T[reuse];
@@ -190,7 +191,7 @@ hipError_t launch_keep_scan(const ScanLaunch& a, hipStream_t, const Stamp&) {
       const int64_t k = std::min(P, pos - (q << shift));
       const int64_t f = a.src_logical[e.src_off + (q << shift)];
       const int64_t l = a.src_logical[e.src_off + (q << shift) + k - 1];
-      const bool keep = (f & (P - 1)) == 0 && l - f == k - 1;
+      const bool keep = a.page_reuse && (f & (P - 1)) == 0 && l - f == k - 1;
       a.reuse[e.reuse_off + q] = keep ? static_cast<int32_t>(f >> shift) : -1;
       if (keep) kept[f >> shift] = 1;
     }

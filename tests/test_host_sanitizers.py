@@ -77,6 +77,7 @@ class Model:
         self.max_pages = -(-max_len * 2 // P)
         self.st = O.CacheState.empty(layers, self.num_pages, P, self.max_pages, with_rows=False)
         self.rng = np.random.default_rng(seed)
+        self.reuse = True       # the pool's page-reuse setting
         self.ops, self.expect = [], []
         self.emit(f"pool {kind} {layers} {P} {self.num_pages} {max_seqs} {self.max_pages}", "pool 0")
 
@@ -163,7 +164,7 @@ class Model:
             toks.append(toks[0])
         op = f"splice {int(self.rng.integers(0, 2))} {int(self.rng.integers(0, 2))} {len(ds)} " + " ".join(toks)
         try:
-            new, plans = O.splice(self.st, ds)
+            new, plans = O.splice(self.st, ds, reuse_pages=self.reuse)
         except O.OracleError as e:
             self.emit(op, f"splice {CODE[type(e)]} 0 0")
             return
@@ -206,12 +207,21 @@ class Model:
         toks = [f"{s} {''.join(map(str, m)) or '-'}" for s, m in zip(seqs, masks)]
         op = f"evict {len(seqs)} " + " ".join(toks)
         try:
-            new, plans = O.evict(self.st, seqs, masks)
+            new, plans = O.evict(self.st, seqs, masks, reuse_pages=self.reuse)
         except O.OracleError as e:
             self.emit(op, f"evict {CODE[type(e)]} 0 0")
             return
         self.emit(op, f"evict 0 {self.fresh(plans)} {self.freed(plans, seqs)}")
         self.st = new
+
+    def set_reuse(self):
+        """Page reuse on or off (off is refused at page size 1)."""
+        on = int(self.rng.random() < 0.6)
+        if not on and self.P == 1:
+            self.emit("reuse 0", f"reuse {EUNSUPPORTED}")
+            return
+        self.reuse = bool(on)
+        self.emit(f"reuse {on}", "reuse 0")
 
     def reindex(self):
         cand = [s for s in self.live() if self.st.lengths[s] > 0]
@@ -278,7 +288,7 @@ class Model:
 def test_random_operations_under_sanitizers(driver, kind, P):
     m = Model(kind, P, seed=900 + P + (50 if kind == "gqa" else 0))
     ops = [m.alloc, m.alloc, m.free, m.set_pages, m.splice, m.splice, m.splice, m.evict, m.evict, m.evict,
-           m.reindex, m.rope, m.lengths]
+           m.reindex, m.rope, m.lengths, m.set_reuse]
     for i in range(260):
         ops[int(m.rng.integers(0, len(ops)))]()
         m.books()

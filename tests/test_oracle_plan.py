@@ -286,6 +286,96 @@ def test_ptable_reindex():
         O.ptable_reindex(st, 0, [6, 7])
 
 
+# ------------------------------------------------ page reuse turned off --
+# The library's page-reuse setting (off: every page of a rewritten sequence
+# is fresh).  The row values are those of the brute-force rebuilds above
+# whatever the placement; the placement is pinned to the lowest free pages in
+# batch order, and every old page of a rewritten sequence returns to the free
+# set.
+
+def _check_compacted(before, after, seqs, plans):
+    assert all(x == -1 for pl in plans for x in pl)
+    lowest = sorted(before.free)
+    at = 0
+    for s in seqs:
+        k = len(after.tables[s])
+        assert after.tables[s] == lowest[at:at + k]
+        at += k
+    released = set().union(*(set(before.tables[s]) for s in seqs)) if seqs else set()
+    assert after.free == (before.free - set(lowest[:at])) | released
+
+
+@pytest.mark.parametrize("P", [2, 4, 16])
+def test_splice_without_page_reuse_matches_list_rebuild(P):
+    cases = 0
+    for n in sorted({0, 1, P - 1, P, P + 1, 2 * P + 1, 3 * P}):
+        for s0, s1 in itertools.combinations_with_replacement(range(n + 1), 2):
+            if P == 16 and (s0 % 3 or s1 % 5) and not (s0 == s1 or s1 == n):
+                continue
+            for r in sorted({0, 1, P + 1}):
+                st = _make_state(P, [n, 5], num_pages=4 * (-(-n // P)) + 8, layers=1, seed=cases)
+                stub = random_rows_np(20_000 + cases, (1, r, O.ROW)) if r else None
+                new, plans = O.splice(st, [O.Directive(0, s0, s1, r, stub)], reuse_pages=False)
+                old_log = list(st.logical_rows(0, 0)) if n else []
+                delta = r - (s1 - s0)
+                rebuilt = old_log[:s0] + [stub[0][k] for k in range(r)] + old_log[s1:]
+                got = new.logical_rows(0, 0) if new.lengths[0] else np.zeros((0, O.ROW), np.uint16)
+                assert new.lengths[0] == len(rebuilt)
+                for j, row in enumerate(rebuilt):
+                    assert np.array_equal(got[j][:KV], row[:KV])
+                    want = row[KV:] if j < s0 + r else O.rotate_kpe_bf16(row[KV:], delta)
+                    assert np.array_equal(got[j][KV:], want)
+                _check_compacted(st, new, [0], plans)
+                assert new.tables[1] == st.tables[1]       # the other sequence is untouched
+                # the same rows as with page reuse on, row for row
+                on, _ = O.splice(st, [O.Directive(0, s0, s1, r, stub)])
+                if on.lengths[0]:
+                    assert np.array_equal(on.logical_rows(0, 0), got)
+                cases += 1
+    assert cases > 20
+
+
+def test_forget_and_batches_without_page_reuse():
+    P = 4
+    st = _make_state(P, [30, 17, 9], num_pages=60, layers=1, seed=5)
+    # FORGET keeps the prefix rows, now in fresh pages
+    new, plans = O.splice(st, [O.Directive(0, 13, 30, 0, None, mode=O.FORGET)], reuse_pages=False)
+    assert new.lengths[0] == 13
+    assert np.array_equal(new.logical_rows(0, 0), st.logical_rows(0, 0)[:13])
+    _check_compacted(st, new, [0], plans)
+    # a batch: fresh pages go out in request order
+    stub = random_rows_np(6, (1, 3, O.ROW))
+    dirs = [O.Directive(2, 1, 4, 3, stub), O.Directive(0, 10, 12, 0, None)]
+    new, plans = O.splice(st, dirs, reuse_pages=False)
+    _check_compacted(st, new, [2, 0], plans)
+    # too few free pages: refused, state unchanged
+    tight = _make_state(P, [30], num_pages=9, layers=1, seed=6)
+    with pytest.raises(O.OutOfPages):
+        O.splice(tight, [O.Directive(0, 0, 0, 0, None)], reuse_pages=False)
+
+
+@pytest.mark.parametrize("P", [2, 4, 16])
+def test_evict_without_page_reuse_matches_masked_list(P):
+    rng = np.random.default_rng(50 + P)
+    for trial in range(30):
+        n = [int(rng.integers(0, 5 * P + 3)) for _ in range(3)]
+        st = _make_state(P, n, num_pages=3 * sum(-(-k // P) for k in n) + 12, layers=1, seed=trial)
+        masks = [(rng.random(k) < rng.random()).astype(np.uint8) for k in n]
+        order = [int(x) for x in rng.permutation(3)]
+        new, plans = O.evict(st, order, [masks[s] for s in order], reuse_pages=False)
+        for s in range(3):
+            old = st.logical_rows(s, 0) if n[s] else np.zeros((0, O.ROW), np.uint16)
+            got = new.logical_rows(s, 0) if new.lengths[s] else np.zeros((0, O.ROW), np.uint16)
+            assert np.array_equal(got, old[np.flatnonzero(masks[s])])
+            assert new.next_pos[s] == st.next_pos[s]
+        _check_compacted(st, new, order, plans)
+    # keep everything: a pure compaction into the lowest free pages
+    st = _make_state(P, [3 * P + 1], num_pages=20, layers=1, seed=99)
+    new, plans = O.evict(st, [0], [np.ones(3 * P + 1, np.uint8)], reuse_pages=False)
+    assert np.array_equal(new.logical_rows(0, 0), st.logical_rows(0, 0))
+    _check_compacted(st, new, [0], plans)
+
+
 # -------------------------------------------- pins catch planted mistakes --
 
 def test_pins_catch_a_planted_sign_error(monkeypatch):
