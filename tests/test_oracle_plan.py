@@ -236,6 +236,26 @@ def test_evict_matches_masked_list_and_cumsum(P):
         _check_page_accounting(st, new, [0])
 
 
+@pytest.mark.parametrize("P", [1, 2, 4, 16])
+def test_evict_every_mask_of_short_sequences(P):
+    """All 2^n keep masks of sequences of n <= 12 rows: the kept rows in order,
+    the reuse rule against the content search, the page accounting."""
+    for n in range(13):
+        st = _make_state(P, [n], num_pages=2 * (-(-n // P)) + 4, layers=1, seed=n + 31 * P)
+        old = st.logical_rows(0, 0) if n else np.zeros((0, O.ROW), np.uint16)
+        old_pages = _old_pages(st, 0, 0)
+        for bits in range(1 << n):
+            keep = np.array([(bits >> i) & 1 for i in range(n)], np.uint8)
+            new, plans = O.evict(st, [0], [keep])
+            rebuilt = old[np.flatnonzero(keep)]
+            got = new.logical_rows(0, 0) if new.lengths[0] else np.zeros((0, O.ROW), np.uint16)
+            assert np.array_equal(got, rebuilt), (P, n, bits)
+            for q, reuse in enumerate(plans[0]):
+                b = _brute_reuse(old_pages, list(rebuilt), P, q, len(rebuilt))
+                assert (reuse if reuse >= 0 else None) == b, (P, n, bits, q)
+            _check_page_accounting(st, new, [0])
+
+
 def test_evict_special_cases():
     P = 16
     st = _make_state(P, [200], num_pages=40, layers=1, seed=7)
