@@ -72,7 +72,7 @@ def test_splice_matches_list_rebuild_exhaustive(P):
         for s0, s1 in itertools.combinations_with_replacement(range(n + 1), 2):
             if P == 16 and (s0 % 3 or s1 % 5) and not (s0 == s1 or s1 == n):
                 continue  # thin the P=16 grid; the boundary cases stay in
-            for r in sorted({0, 1, P + 1}):
+            for r in sorted({0, 1, 2, 3, P + 1}):
                 st = _make_state(P, [n], num_pages=3 * (-(-n // P)) + 6, layers=1, seed=cases)
                 stub = random_rows_np(10_000 + cases, (1, r, O.ROW)) if r else None
                 d = O.Directive(0, s0, s1, r, stub)
