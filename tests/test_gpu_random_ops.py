@@ -1,8 +1,10 @@
 """Random sequences of pool operations against the oracle, checked after every
 operation: batched splices ("Leyline", sections 2.1-2.3; AMORTIZE and
 FORGET; the page plan expanded on the device or staged by the host, picked at
-random per call), evictions ("KV-streams", "how it works"; device and host page
-plans), page-granular reindex, per-row rotation in place ("VECTOR", method),
+random per call), evictions ("KV-streams", "how it works"; the device's page
+plan, with page shortages that its verdict decides), page reuse on or off
+for each splice and eviction (picked at random above page size 1),
+page-granular reindex, per-row rotation in place ("VECTOR", method),
 sequence alloc / set_pages / free, and requests that must fail and leave the
 pool as it was.  Page sizes 1, 4 and 16; MLA pools and GQA pools.
 
@@ -48,6 +50,16 @@ class Mirror:
         # themselves do not depend on it
         self.plan_rng = np.random.default_rng(seed + 1)
         self.splice_planned = {0: 0, 1: 0}
+        # page reuse per splice / eviction (off for a quarter of the calls
+        # above page size 1): a stream of draws of its own too
+        self.reuse_rng = np.random.default_rng(seed + 2)
+        self.reuse_off_calls = 0
+
+    def reuse_for_call(self):
+        reuse = self.P == 1 or self.reuse_rng.random() >= 0.25
+        self.dp.pool.set_page_reuse(reuse)
+        self.reuse_off_calls += not reuse
+        return reuse
 
     @property
     def state(self):
@@ -169,8 +181,9 @@ class Mirror:
             kw, host = self.stub(r) if r else ({}, None)
             lib.append(self.L.Directive(s, s0, s1, mode=mode, **kw))
             ora.append(O.Directive(s, s0, s1, r, host, mode))
+        reuse = self.reuse_for_call()
         try:
-            expected, _ = O.splice(self.state, ora, pairing=self.pairing, base=self.base)
+            expected, _ = O.splice(self.state, ora, pairing=self.pairing, base=self.base, reuse_pages=reuse)
         except O.OracleError:
             with pytest.raises(self.L.LeylineError):
                 self.dp.pool.splice(lib)
@@ -179,7 +192,7 @@ class Mirror:
         self.dp.pool.splice(lib)
         self.splice_planned[self.dp.pool.last_stats().planned_on_device] += 1
         self.state = expected
-        return f"splice {[(d.seq, d.s_start, d.s_end, d.r_len, d.mode) for d in ora]}"
+        return f"splice {[(d.seq, d.s_start, d.s_end, d.r_len, d.mode) for d in ora]} reuse {reuse}"
 
     def op_evict(self):
         if not self.live:
@@ -205,15 +218,16 @@ class Mirror:
         self.keep_alive.append(dev)
         if self.P > 1 and len(self.state.free) < sum(len(self.state.tables[s]) for s in seqs):
             self.short_evictions += 1   # a shortage was possible: the verdict decided
+        reuse = self.reuse_for_call()
         try:
-            expected, _ = O.evict(self.state, seqs, masks)
+            expected, _ = O.evict(self.state, seqs, masks, reuse_pages=reuse)
         except O.OracleError:
             with pytest.raises(self.L.LeylineError):
                 self.dp.pool.evict(seqs, dev, offsets)
             return "evict: refused"
         self.dp.pool.evict(seqs, dev, offsets)
         self.state = expected
-        return f"evict {seqs}"
+        return f"evict {seqs} reuse {reuse}"
 
     def op_reindex(self):
         cand = [s for s in sorted(self.live) if self.state.lengths[s] > 0]
@@ -233,6 +247,7 @@ class Mirror:
         """A full pool: an allocation and a splice that need more pages than
         are free are refused with nothing changed; an eviction whose worst
         case exceeds the free pages succeeds after reading the verdict."""
+        self.dp.pool.set_page_reuse(True)
         for s in sorted(self.live):
             self.dp.pool.seq_free(s)
             self.state.free |= set(self.state.tables.pop(s))
@@ -350,8 +365,9 @@ def test_random_operation_sequences(P, kind):
         kinds[x.split(" ")[0].rstrip(":")] = kinds.get(x.split(" ")[0].rstrip(":"), 0) + 1
     say(f"  {len(log)} operations {kinds}; {refused} refused as the oracle refused them; "
         f"{m.short_evictions} evictions short of their all-fresh need; splices planned on the device "
-        f"{m.splice_planned[1]}, staged {m.splice_planned[0]}")
+        f"{m.splice_planned[1]}, staged {m.splice_planned[0]}; page reuse off for {m.reuse_off_calls} calls")
     assert m.splice_planned[0] and m.splice_planned[1]
+    assert P == 1 or m.reuse_off_calls > 0
     m.pressure()
     m.keep_alive.clear()
     m.dp.close()
