@@ -176,9 +176,12 @@ def pct(samples, q):
     return float(np.percentile(np.asarray(samples, dtype=np.float64), q))
 
 
-def copy_ceiling(torch, dev, n_bytes):
-    """Plain device copy of n_bytes (read + write), for context; at least
-    1 GiB, so that repeats do not run out of the memory-side cache."""
+def torch_copy_rate(torch, dev, n_bytes):
+    """torch's own device copy (`dst.copy_(src)`, rocclr's copy kernel) of
+    n_bytes read + written, GB/s, for context -- not a ceiling: hand-written
+    copies run faster.  At least 1 GiB, so that repeats do not run out of the
+    memory-side cache.  The counter runs also use this copy to calibrate
+    FETCH_SIZE and WRITE_SIZE."""
     n_bytes = max(n_bytes, 1 << 30)
     src = torch.empty(n_bytes, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
@@ -561,7 +564,7 @@ def bench_splice_32k(args, STUB=24, workload="splice_32k_27layer", kernel="splic
                                 "max": round(max(lat), 1), "runs": len(lat),
                                 "host_call_median": round(statistics.median(host), 1)}
     out["roofline"] = roofline(kernel, workload, launches, kernel_ms, kernel_bytes, samples)
-    out["copy_ceiling_gbs"] = round(copy_ceiling(torch, dev, alg_bytes // 2), 1)
+    out["torch_copy_gbs"] = round(torch_copy_rate(torch, dev, alg_bytes // 2), 1)
     out["cpu_baseline"] = None
     if host_before is not None:
         out["cpu_baseline"] = cpu_baseline_splice(host_before, gpu_after, T0, alg_bytes, args.cpu_seconds,
