@@ -101,7 +101,8 @@ def parse():
                     choices=["splice_32k_27layer", "splice_32k_27layer_inplace", "splice_16x32k_27layer",
                              "evict_256x16k_27layer_p16", "evict_256x16k_27layer_p1", "splice_32k_llama8b",
                              "kvs_mask_64x32k", "rope_rows_32k_27layer", "rope_rows_32k_27layer_inplace",
-                             "splice_4k_1layer", "evict_32x16k_llama8b_p16", "drift_128k_60layer"])
+                             "splice_4k_1layer", "evict_32x16k_llama8b_p16", "drift_128k_60layer",
+                             "compact_128x16k_27layer_p16"])
     return ap.parse_args()
 
 
@@ -726,21 +727,21 @@ def host_pool(n_arrays, pool_pages, page, width):
     return [np.full((pool_pages, page, width), 0x3F80, np.uint16) for _ in range(n_arrays)]
 
 
-def cpu_baseline_evict(masks, page, seconds, LAYERS, TOKENS, ROLL):
+def cpu_baseline_evict(masks, page, seconds, LAYERS, TOKENS, ROLL, reuse=True):
     """The oracle's eviction on 8 of the rollouts (all layers, the same masks,
-    the same pool shape per rollout)."""
+    the same pool shape per rollout; reuse False: page reuse off)."""
     from oracle import leyline_oracle as O
     from synth import permuted_pages
     k = 8
     per = TOKENS // page
-    pool_pages = k * per + (k * per // 2 if page > 1 else 0)
+    pool_pages = k * per + (k * per if not reuse else (k * per // 2 if page > 1 else 0))
     st = O.CacheState.empty(0, pool_pages, page, per, with_rows=False)
     st.layers = host_pool(LAYERS, pool_pages, page, ROW)
     perm = permuted_pages(0, k * per)
     for r in range(k):
         st.set_pages(r, perm[r * per:(r + 1) * per], TOKENS)
     ms = [masks[r * TOKENS:(r + 1) * TOKENS] for r in range(k)]
-    runs, t, (_, plans) = timed_oracle(lambda: O.evict(st, list(range(k)), ms), seconds)
+    runs, t, (_, plans) = timed_oracle(lambda: O.evict(st, list(range(k)), ms, reuse_pages=reuse), seconds)
     nb = sum(O.algorithmic_bytes(pl, int(m.sum()), page, np.zeros(int(m.sum()), np.int64),
                                  np.zeros(int(m.sum()), bool), 0, LAYERS, rotate=False) for pl, m in zip(plans, ms))
     return oracle_line(nb, runs, t, f"{k} of the {ROLL} rollouts, all {LAYERS} layers, the same masks",
@@ -1212,18 +1213,23 @@ def bench_kvs_mask(args):
 
 # ------------------------------------------------------------------- evict --
 
-def bench_evict(args, page):
+def bench_evict(args, page, compact=False):
     """256 rollouts x 16384 tokens x 27 layers; per-rollout keep masks from
     random turn drops (turns U[200,2000], each dropped with p = 0.5); one
     eviction call for all rollouts.  Restoring the tables between steps is
-    outside the timed call."""
+    outside the timed call.
+
+    compact=True (compact_128x16k_27layer_p16): page reuse off and every row
+    kept, so the call compacts the rollouts into the lowest free pages and
+    every row moves; 128 rollouts, pool pages twice theirs (every new page is
+    fresh)."""
     import torch
     from mla_paged_cache_amd import leyline as L
     from synth import np_rng, permuted_pages, turn_drop_mask
 
-    LAYERS, ROLL, TOKENS = 27, 256, 16384
+    LAYERS, ROLL, TOKENS = 27, (128 if compact else 256), 16384
     per = TOKENS // page
-    extra = ROLL * per // 2 if page > 1 else 0
+    extra = ROLL * per if compact else (ROLL * per // 2 if page > 1 else 0)
     POOL_PAGES = ROLL * per + extra
     dev = torch.device("cuda:0")
     data = torch.empty((LAYERS, POOL_PAGES, page, ROW), dtype=torch.int16, device=dev)
@@ -1239,7 +1245,11 @@ def bench_evict(args, page):
     pool = L.Pool(data, table)
     perm = permuted_pages(0, ROLL * per)
     rng = np_rng(0, 6)
-    masks = np.concatenate([turn_drop_mask(rng, TOKENS) for _ in range(ROLL)])
+    if compact:
+        pool.set_page_reuse(False)
+        masks = np.ones(ROLL * TOKENS, np.uint8)
+    else:
+        masks = np.concatenate([turn_drop_mask(rng, TOKENS) for _ in range(ROLL)])
     keep = torch.from_numpy(masks).to(dev)
     offsets = np.arange(ROLL, dtype=np.int64) * TOKENS
     seqs = list(range(ROLL))
@@ -1284,10 +1294,11 @@ def bench_evict(args, page):
     launches, kernel_ms, kernel_bytes, samples = pool.profile_read(0, samples=16)
     s_launches, scan_ms, _ = pool.profile_read(1)
     ms_per_step = 1e3 * statistics.median(times)
-    name = f"evict_256x16k_27layer_p{page}"
+    name = "compact_128x16k_27layer_p16" if compact else f"evict_256x16k_27layer_p{page}"
     out = base_line(args, name, alg_bytes / (ms_per_step * 1e-3) / 1e9, ms_per_step, {
         "layers": LAYERS, "rollouts": ROLL, "tokens": TOKENS, "page_size": page, "pool_pages": POOL_PAGES,
-        "mask": "turn drops U[200,2000], p=0.5", "rows_kept": int(masks.sum()),
+        "mask": "every row kept, page reuse off (a compaction)" if compact else "turn drops U[200,2000], p=0.5",
+        "rows_kept": int(masks.sum()),
         "rows_moved_per_layer": stats.rows_moved, "fresh_pages": stats.fresh_pages,
         "alg_bytes_per_step": alg_bytes,
         "page_plan": "device",
@@ -1302,7 +1313,7 @@ def bench_evict(args, page):
     out["keep_scan_us"] = round(scan_ms * 1e3 / max(1, s_launches), 2)
     out["call_return_us"] = round(1e6 * statistics.median(call_times), 1)
     out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline_evict(
-        masks, page, args.cpu_seconds, LAYERS, TOKENS, ROLL)
+        masks, page, args.cpu_seconds, LAYERS, TOKENS, ROLL, reuse=not compact)
     pool.close()
     return out
 
@@ -1406,7 +1417,7 @@ def cpu_baseline_evict_gqa(masks, seconds, LAYERS, HEADS, HEAD_DIM, TOKENS, PAGE
     for r in range(k):
         st.set_pages(r, perm[r * per:(r + 1) * per], TOKENS)
     ms = [masks[r * TOKENS:(r + 1) * TOKENS] for r in range(k)]
-    runs, t, (_, plans) = timed_oracle(lambda: O.evict(st, list(range(k)), ms), seconds)
+    runs, t, (_, plans) = timed_oracle(lambda: O.evict(st, list(range(k)), ms, reuse_pages=reuse), seconds)
     nb = sum(O.algorithmic_bytes(pl, int(m.sum()), PAGE, np.zeros(int(m.sum()), np.int64),
                                  np.zeros(int(m.sum()), bool), 0, layers, rotate=False, specs=specs)
              for pl, m in zip(plans, ms))
@@ -1441,6 +1452,8 @@ def main():
         out = bench_kvs_mask(args)
     elif args.workload == "rope_rows_32k_27layer":
         out = bench_rope_rows(args)
+    elif args.workload == "compact_128x16k_27layer_p16":
+        out = bench_evict(args, 16, compact=True)
     else:
         out = bench_evict(args, 16 if args.workload.endswith("p16") else 1)
     print(json.dumps(out), flush=True)
