@@ -18,12 +18,12 @@
 //    full key blocks (FlexAttention-style block mask).
 //  * kvs_events_kernel / kvs_dense_ev_kernel: the packed bit mask of rollouts
 //    whose keys die at few distinct times: the distinct death times and per
-//    key a 4-bit code (which of them), once per rollout; then rows walked with
-//    bits added on the diagonal and cleared at each death time -- no loads in
-//    the row loop, so a rollout's rows can be dealt across its waves with a
-//    stride and the resident waves write neighbouring rows.  The waves of a
-//    rollout with more death times take the rebuild walk below instead, in
-//    the same launch.
+//    key a 4-bit code (which of them), once per rollout; then one wave per
+//    run of 8 whole rows, its bits built at the run's first row from the
+//    codes and carried down the run -- added on the diagonal, cleared at each
+//    death time, no vector loads in the row loop -- so the grid writes the
+//    mask in address order.  The waves of a rollout with more death times
+//    take the rebuild walk below instead, in the same launch.
 //  * kvs_dense_kernel (rebuild walk; every rollout when n_pad is too large
 //    for the pre-pass): one 16-byte store per lane and row; a wave carries
 //    its 64 x 128 keys' bits down a run of rows, adds keys as the rows reach
@@ -480,94 +480,145 @@ __device__ __forceinline__ uint32_t range_word(int32_t lo, int32_t hi, int word)
   return (0xFFFFFFFFu >> (31 - b)) & (0xFFFFFFFFu << a);
 }
 
-// One wave per (rollout, phase, 64 consecutive strips of 128 keys); lane s
-// writes strip s.  Phase ph takes rows ph, ph + S, ph + 2 S, ... (S = n_pad /
-// rows_per_thread), so that the waves resident at a time write neighbouring
-// rows.  A lane loads its 128 keys' bits from the five bit sets of
-// kvs_events_kernel (visible at some row; the 4-bit code, the index of d_k
-// among the rollout's distinct death times).  Walking its rows it adds the
-// keys the diagonal has reached since the last row and clears, at every death
-// time passed, the keys with that code -- four bit-plane ANDs per word, no
-// loads in the row loop.
+// Rows per wave of kvs_dense_ev_kernel, and the groups of 64 strips whose
+// bits a lane holds at once.
+constexpr int kDenseRun = 8;
+constexpr int kDenseHold = 4;
+
+// 16-byte store with cache policy sc0 | nt | sc1 (gfx950 bits 1, 2 and 16 of
+// a buffer instruction's cache-policy operand) through a buffer descriptor
+// based at the wave-uniform `base`, `bytes` long: lanes at or past `bytes`
+// store nothing.
+__device__ __forceinline__ void stream_store(word4 v, const void* base, uint32_t off, uint32_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p >> 32));
+  void* ub = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(ub, 0, static_cast<int>(bytes), 0x00020000);
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, static_cast<int>(off), 0, 19);
+}
+
+// One wave per (rollout, run of kDenseRun consecutive rows): the wave writes
+// whole rows, so a block's four waves fill 4 * kDenseRun consecutive rows and
+// the grid's write front moves through the mask in address order.  Lane l
+// holds strips l, l + 64, ... (128 keys each) of up to kDenseHold groups of 64
+// strips.  From the five bit sets of kvs_events_kernel (visible at some row;
+// the 4-bit code, the index of d_k among the rollout's distinct death times)
+// it builds a strip's bits at the run's first row q0 -- visible, k <= q0, and
+// not dead: code >= the number of death times <= q0, a bit-serial compare of
+// the code planes -- then walks the run's rows adding key q on the diagonal
+// and clearing, at each death time passed, the keys with that code.  The row
+// loop loads nothing but scalar event times, so its stores never wait behind
+// a vector load.  A rollout with more than kDenseMaxEvents death times is
+// written by the rebuild walk, dealt over the same rollout's waves.
 __global__ __launch_bounds__(256) void kvs_dense_ev_kernel(KvsDenseLaunch a) {
   __shared__ uint64_t stage[4][256];  // the rebuild walk's
   const int lane = threadIdx.x & 63;
   const int64_t strips = a.n_pad >> 7;
   const int64_t groups = (strips + 63) >> 6;
-  const int64_t phases = a.n_pad / a.rows_per_thread;
-  // the wave index, made visibly wave-uniform: everything derived from it
-  // (rollout, phase, rows, the death-time list) then lives in scalar
-  // registers and is read with scalar loads -- a vector load in the row loop
-  // would wait for every store issued before it
+  const int64_t runs = a.n_pad / kDenseRun;  // waves per rollout
+  // the wave index, made visibly wave-uniform: the rollout, rows and the
+  // death-time list then live in scalar registers and scalar loads
   const uint64_t gw_any = (static_cast<uint64_t>(blockIdx.x) * 256 + threadIdx.x) >> 6;
   const int64_t gw = static_cast<int64_t>(
       (static_cast<uint64_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(gw_any >> 32))) << 32) |
       __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(gw_any)));
-  if (gw >= static_cast<int64_t>(a.n) * phases * groups) return;
-  const int64_t grp = gw % groups;
-  const int64_t rest = gw / groups;
-  const int64_t ph = rest % phases;
-  const int32_t roll = static_cast<int32_t>(rest / phases);
+  if (gw >= static_cast<int64_t>(a.n) * runs) return;
+  const int64_t run = gw % runs;
+  const int32_t roll = static_cast<int32_t>(gw / runs);
   using cptr = const __attribute__((address_space(4))) int32_t*;
   const cptr ev = reinterpret_cast<cptr>(reinterpret_cast<uintptr_t>(a.events + int64_t{roll} * kDenseEvStride));
   const int32_t n_ev = ev[0];
   if (n_ev > kDenseMaxEvents) {  // too many death times for the codes: the rebuild walk
-    dense_rebuild_wave(a, gw, lane, stage[threadIdx.x >> 6]);
+    const int64_t rb_waves = (a.n_pad + a.rows_per_thread - 1) / a.rows_per_thread * groups;
+    for (int64_t j = run; j < rb_waves; j += runs)
+      dense_rebuild_wave(a, int64_t{roll} * rb_waves + j, lane, stage[threadIdx.x >> 6]);
     return;
   }
-  const int64_t s = grp * 64 + lane;
-  const bool active = s < strips;
   const int64_t words = a.n_pad >> 5;
-  word4* out = reinterpret_cast<word4*>(a.bits + int64_t{roll} * a.n_pad * words) + s;
-  const int64_t pitch = words >> 2;  // word4 per row
-  const int64_t k0 = s << 7;         // first key of the lane's strip
-  // the lane's 128 keys in each of the five bit sets (16 bytes each):
-  // planes[0] visible at some row, planes[1..4] bits 0..3 of the code
-  uint32_t planes[5][4] = {};
-  if (active) {
-    const uint32_t* pl = a.planes + static_cast<int64_t>(roll) * 5 * words + 4 * s;
-#pragma unroll
-    for (int p = 0; p < 5; ++p) {
-      const word4 v = *reinterpret_cast<const word4*>(pl + p * words);
-      planes[p][0] = v.x;
-      planes[p][1] = v.y;
-      planes[p][2] = v.z;
-      planes[p][3] = v.w;
-    }
-  }
-  uint32_t w[4] = {0u, 0u, 0u, 0u};
-  int32_t e_next = 0;
-  int32_t t_next = n_ev > 0 ? ev[1] : INT32_MAX;  // the next death time, kept in a register
+  const int64_t row_bytes = a.n_pad >> 3;
   // rows and keys are below n_pad < 2^31
-  const int32_t step = static_cast<int32_t>(phases);
-  const int32_t k0s = static_cast<int32_t>(k0);
-  int32_t q = static_cast<int32_t>(ph);
-  int32_t q_prev = -1;
-  word4* dst = out + q * pitch;
-  const int64_t dst_step = static_cast<int64_t>(step) * pitch;
-  for (int32_t j = 0; j < a.rows_per_thread; ++j, q += step, dst += dst_step) {
-    // keys q_prev < k <= q of the strip join (those ever visible)
-    const int32_t lo = (q_prev + 1 > k0s ? q_prev + 1 : k0s) - k0s;
-    const int32_t hi = (q < k0s + 127 ? q : k0s + 127) - k0s;
-    if (lo <= hi) {
+  const int32_t q0 = static_cast<int32_t>(run * kDenseRun);
+  const char* out = reinterpret_cast<const char*>(a.bits) + (int64_t{roll} * a.n_pad + q0) * row_bytes;
+  const uint32_t* pl_roll = a.planes + static_cast<int64_t>(roll) * 5 * words;
+  int32_t e0 = 0;  // death times at or before q0
 #pragma unroll
-      for (int x = 0; x < 4; ++x) w[x] |= planes[0][x] & range_word(lo, hi, x);
-    }
-    // keys whose death time has come leave (times in increasing order)
-    while (t_next <= q) {
-      const int e = e_next++;
+  for (int e = 0; e < kDenseMaxEvents; ++e) e0 += (e < n_ev && ev[1 + e] <= q0) ? 1 : 0;
+  for (int64_t g0 = 0; g0 < groups; g0 += kDenseHold) {
+    uint32_t vis[kDenseHold][4], code[kDenseHold][4][4];
+    int32_t k0[kDenseHold];
+#pragma unroll
+    for (int h = 0; h < kDenseHold; ++h) {
+      const int64_t s = (g0 + h) * 64 + lane;
+      k0[h] = static_cast<int32_t>(s << 7);
+      word4 p[5] = {};
+      if (s < strips) {
+#pragma unroll
+        for (int c = 0; c < 5; ++c) p[c] = *reinterpret_cast<const word4*>(pl_roll + c * words + 4 * s);
+      }
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
-        const uint32_t m = ((e & 1) ? planes[1][x] : ~planes[1][x]) & ((e & 2) ? planes[2][x] : ~planes[2][x]) &
-                           ((e & 4) ? planes[3][x] : ~planes[3][x]) & ((e & 8) ? planes[4][x] : ~planes[4][x]);
-        w[x] &= ~m;
+        vis[h][x] = p[0][x];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) code[h][b][x] = p[1 + b][x];
       }
-      t_next = e_next < n_ev ? ev[1 + e_next] : INT32_MAX;
     }
-    // plain stores: with the rows strided across the rollout's waves they
-    // measure faster than non-temporal ones (the reverse of a per-wave run)
-    if (active) *dst = word4{w[0], w[1], w[2], w[3]};
-    q_prev = q;
+    uint32_t w[kDenseHold][4];
+#pragma unroll
+    for (int h = 0; h < kDenseHold; ++h)
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        // dead at q0: code < e0, compared from the top bit down
+        uint32_t lt = 0u, eq = 0xFFFFFFFFu;
+#pragma unroll
+        for (int b = 3; b >= 0; --b) {
+          if ((e0 >> b) & 1) {
+            lt |= eq & ~code[h][b][x];
+            eq &= code[h][b][x];
+          } else {
+            eq &= ~code[h][b][x];
+          }
+        }
+        w[h][x] = vis[h][x] & range_word(0, q0 - k0[h], x) & ~lt;
+      }
+    int32_t e_next = e0;
+    int32_t t_next = e0 < n_ev ? ev[1 + e0] : INT32_MAX;
+    for (int j = 0; j < kDenseRun; ++j) {
+      const int32_t q = q0 + j;
+      if (j > 0) {
+        // key q joins (if it is ever visible)
+#pragma unroll
+        for (int h = 0; h < kDenseHold; ++h) {
+          const int32_t b = q - k0[h];
+          if (b >= 0 && b < 128) {
+#pragma unroll
+            for (int x = 0; x < 4; ++x) w[h][x] |= vis[h][x] & ((b >> 5) == x ? 1u << (b & 31) : 0u);
+          }
+        }
+        // keys whose death time has come leave (times in increasing order)
+        while (t_next <= q) {
+          const int e = e_next++;
+#pragma unroll
+          for (int h = 0; h < kDenseHold; ++h)
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+              const uint32_t mk = ((e & 1) ? code[h][0][x] : ~code[h][0][x]) &
+                                  ((e & 2) ? code[h][1][x] : ~code[h][1][x]) &
+                                  ((e & 4) ? code[h][2][x] : ~code[h][2][x]) &
+                                  ((e & 8) ? code[h][3][x] : ~code[h][3][x]);
+              w[h][x] &= ~mk;
+            }
+          t_next = e_next < n_ev ? ev[1 + e_next] : INT32_MAX;
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < kDenseHold; ++h) {
+        const int64_t g = g0 + h;
+        if (g < groups)
+          stream_store(word4{w[h][0], w[h][1], w[h][2], w[h][3]}, out + j * row_bytes + g * 1024, lane * 16,
+                       static_cast<uint32_t>(min<int64_t>(64, strips - g * 64) * 16));
+      }
+    }
   }
 }
 
@@ -597,9 +648,6 @@ hipError_t launch_kvs_block(const KvsBlockLaunch& a, hipStream_t s) {
 
 hipError_t launch_kvs_dense(const KvsDenseLaunch& a, hipStream_t s) {
   if (a.n == 0) return hipSuccess;
-  const int64_t runs = (a.n_pad + a.rows_per_thread - 1) / a.rows_per_thread;
-  const int64_t groups = ((a.n_pad >> 7) + 63) >> 6;
-  const int64_t waves = static_cast<int64_t>(a.n) * runs * groups;
   if (a.events) {
     // blocks per rollout: enough to fill the chip's CUs, none without keys
     const int64_t split = std::min<int64_t>(std::max<int64_t>(1, 512 / a.n), (a.n_pad + 1023) / 1024);
@@ -607,9 +655,14 @@ hipError_t launch_kvs_dense(const KvsDenseLaunch& a, hipStream_t s) {
                         static_cast<size_t>(a.n_pad >> 3), s>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    kvs_dense_ev_kernel<<<dim3(static_cast<unsigned>((waves + 3) / 4)), dim3(256), 0, s>>>(a);
+    // four runs of kDenseRun rows per block: n_pad / kDenseRun is a multiple of 16
+    const int64_t run_waves = static_cast<int64_t>(a.n) * (a.n_pad / kDenseRun);
+    kvs_dense_ev_kernel<<<dim3(static_cast<unsigned>(run_waves / 4)), dim3(256), 0, s>>>(a);
     return hipGetLastError();
   }
+  const int64_t runs = (a.n_pad + a.rows_per_thread - 1) / a.rows_per_thread;
+  const int64_t groups = ((a.n_pad >> 7) + 63) >> 6;
+  const int64_t waves = static_cast<int64_t>(a.n) * runs * groups;
   kvs_dense_kernel<<<dim3(static_cast<unsigned>((waves + 3) / 4)), dim3(256), 0, s>>>(a);
   return hipGetLastError();
 }

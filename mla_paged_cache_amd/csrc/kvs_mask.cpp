@@ -340,7 +340,10 @@ ll_status kvs_dense_mask(kvs_ctx* c, const int32_t* death_dev, int32_t n, int64_
   a.rows_per_thread = 128;
   const int64_t runs = (n_pad + a.rows_per_thread - 1) / a.rows_per_thread;
   const int64_t groups = (n_pad / 128 + 63) / 64;  // waves per run of rows
-  if (static_cast<int64_t>(n) * runs * groups / 4 >= (int64_t{1} << 31))
+  // blocks of the rebuild-walk launch, and of the run-of-rows launch (four
+  // runs of 8 rows per block) when the pre-pass applies
+  if (static_cast<int64_t>(n) * runs * groups / 4 >= (int64_t{1} << 31) ||
+      (n_pad <= ll::kDenseEvMaxPad && static_cast<int64_t>(n) * (n_pad / 32) >= (int64_t{1} << 31)))
     return fail(LL_EUNSUPPORTED, "dense mask too large for one launch");
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool by_events = n_pad <= ll::kDenseEvMaxPad;

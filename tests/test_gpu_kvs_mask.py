@@ -297,6 +297,44 @@ def test_dense_mask_beyond_the_pre_pass_limit():
     ctx.close()
 
 
+def test_dense_mask_of_wide_rows_both_walks():
+    """n_pad = 163840: rows of 20 KiB, more than the 4 x 64 strips of 128 keys
+    a lane of the code walk holds at once (five passes over a wave's run of 8
+    rows), and more rebuild-walk waves than the rollout has runs of 8 rows
+    (the waves of a rollout with too many death times take several).  One
+    rollout with exactly 15 distinct death times (the code walk), one with
+    hundreds (the rebuild walk), one with none; sampled rows -- the first and
+    last row of runs, rows on each side of death times, the last rows --
+    against the definition visible(q, k) = k <= q < d_k."""
+    L = need_gpu()
+    ctx = L.KvsMask(0)
+    n_pad = 163840
+    rng = np_rng(33, 0)
+    k = np.arange(n_pad)
+    times = np.sort(rng.choice(np.arange(1, n_pad), size=15, replace=False))
+    d15 = np.full(n_pad, n_pad, np.int64)
+    pick = times[rng.integers(0, 15, size=n_pad)]
+    d15 = np.where((rng.random(n_pad) < 0.6) & (pick > k), pick, d15)
+    d15[times - 1] = times
+    d15[rng.random(n_pad) < 0.05] = -3
+    dmany = np.minimum(k + 1 + rng.integers(0, 3000, size=n_pad), n_pad + 5)
+    dmany[rng.random(n_pad) < 0.1] = n_pad
+    dnone = np.full(n_pad, n_pad, np.int64)
+    d_host = np.stack([d15, dmany, dnone])
+    assert len(set(int(x) for j, x in enumerate(d15) if j < x < n_pad)) == 15
+    say(f"kvs dense n_pad={n_pad}: code walk in five passes, rebuild walk over several runs per wave")
+    death = torch.from_numpy(d_host.astype(np.int32)).cuda()
+    bits = ctx.dense_mask(death)
+    torch.cuda.synchronize()
+    rows = np.unique(np.r_[[0, 7, 8, 32767, 32768, 131071, 131072, 131080, n_pad - 9, n_pad - 8, n_pad - 1],
+                          times - 1, times, np.minimum(times + 1, n_pad - 1), rng.integers(0, n_pad, size=24)])
+    for r in range(3):
+        got = bits[r, torch.from_numpy(rows).cuda()].cpu().numpy().view(np.uint32)
+        assert np.array_equal(got, K.dense_bits(K.visibility_rows(d_host[r], rows))), r
+    del bits
+    ctx.close()
+
+
 def test_masks_on_alternating_streams_share_the_scratch():
     """Dense and block masks of three batches issued back to back on two
     streams, then on the first again.  The first batch is long (24 rollouts
