@@ -147,6 +147,53 @@ def test_textworld_shaped_batch_32k():
     ctx.close()
 
 
+@pytest.mark.slow
+def test_bench_shaped_batch_64x32k():
+    """The trainer-mask workload as it is timed: 64 rollouts of 32768 tokens
+    (turns U[64, 512], compaction every 10 turns, budget 8192, the three
+    strategies in turn; the same seeds), logs uploaded once, then death
+    times, the 128 x 128 block mask and the dense mask into caller-owned
+    outputs, twice (the second call reuses the outputs and the scratch).
+    Death times of every rollout bit-exact; sampled query blocks of every
+    rollout; dense rows of every rollout sampled at run edges, event times
+    and at random, against the definition."""
+    L = need_gpu()
+    ctx = L.KvsMask(0)
+    n_pad = 32768
+    strategies = ("window", "half", "pick")
+    rolls = [(n_pad, compaction_log(np_rng(0, 10 + i), n_pad, strategies[i % 3], 8192, 64, 512, 10))
+             for i in range(64)]
+    say("kvs 64 x 32k, the timed workload's launches")
+    logs = ctx.upload_logs(rolls)
+    death, status = ctx.death_times(logs, n_pad)
+    bits = ctx.dense_mask(death)
+    blocks = ctx.block_mask(death, 128, 128)
+    ctx.death_times(logs, n_pad, out=(death, status))
+    ctx.block_mask(death, 128, 128, out=blocks)
+    ctx.dense_mask(death, out=bits)
+    torch.cuda.synchronize()
+    assert not status.cpu().numpy().any()
+    d_host = np.stack([K.death_times(n_pad, n, ev) for n, ev in rolls])
+    assert np.array_equal(death.cpu().numpy().astype(np.int64), d_host)
+    _check_blocks(ctx, death, d_host, 128, 128, full_check=False, sample=[0, 100, 255])
+    pn, pi, fn, fi = (x.cpu().numpy() for x in blocks)
+    for r in range(0, 64, 9):  # the timed call's own block lists, as in the check above
+        for i in (1, 128):
+            q0, q1 = i * 128, i * 128 + 128
+            cls = [K.tile_class(d_host[r], q0, q1, j * 128, j * 128 + 128) for j in range(256)]
+            assert list(pi[r, i, :pn[r, i]]) == [j for j, c in enumerate(cls) if c == "partial"], (r, i)
+            assert list(fi[r, i, :fn[r, i]]) == [j for j, c in enumerate(cls) if c == "full"], (r, i)
+    rng = np_rng(64, 32)
+    for r in range(64):
+        times = np.array([e.time for e in rolls[r][1] if e.time < n_pad], np.int64)
+        rows = np.unique(np.r_[[0, 7, 8, n_pad - 8, n_pad - 1], times - 1, times,
+                              rng.integers(0, n_pad, size=6)])
+        got = bits[r, torch.from_numpy(rows).cuda()].cpu().numpy().view(np.uint32)
+        assert np.array_equal(got, K.dense_bits(K.visibility_rows(d_host[r], rows))), r
+    del bits
+    ctx.close()
+
+
 def test_engine_eviction_agrees_with_death_times():
     """A one-layer MLA pool (page size 16) whose rows carry their token id in
     the first two bf16 slots; tokens are appended event by event and each
