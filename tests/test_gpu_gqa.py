@@ -195,8 +195,10 @@ def test_gqa_llama8b_shape_32k_splice():
 @pytest.mark.parametrize("P,plan", [(16, "device"), (16, "host"), (1, "device")])
 def test_gqa_evict_turn_drops(P, plan):
     """KV-streams eviction on a GQA pool: two sequences of 4096 tokens, random
-    turn drops; K and V rows move unchanged.  With free pages for every page of
-    both sequences the device makes the page plan, with fewer the host."""
+    turn drops; K and V rows move unchanged.  The device makes the page plan,
+    with free pages for every page of both sequences or with fewer (a
+    shortage is then possible and the call reads the device's verdict before
+    the rows move)."""
     say(f"gqa evict P={P}, {plan} plan")
     L_ = need_gpu()
     H, D, rot = 8, 64, 64
@@ -221,6 +223,54 @@ def test_gqa_evict_turn_drops(P, plan):
     assert st.alg_bytes == 2 * 2 * 2 * H * D * 2 * st.rows_moved
     dp.close()
     del L_
+
+
+@pytest.mark.slow
+def test_gqa_evict_llama8b_shape_32_rollouts():
+    """The GQA eviction workload as it is timed: 32 rollouts x 16384 tokens x
+    32 layers of K and V planes (8 KV heads x 128), page size 16, pool pages
+    1.5 x the rollouts', random turn drops (the same seeds), one call.  Page
+    tables of all 32 rollouts and the free count against the oracle; K and V
+    rows of 8 rollouts on layers 0 and 31 equal the kept rows captured before
+    the call."""
+    need_gpu()
+    layers, H, D, P, n_roll, n_tok = 32, 8, 128, 16, 32, 16384
+    per = n_tok // P
+    say(f"gqa evict {n_roll} x {n_tok} x {layers} (K and V, {H} x {D}), P={P}")
+    dp = GqaDevicePool(layers, n_roll * per * 3 // 2, P, n_roll, per, H, D, D, seed=0, pairing=1, base=500000.0,
+                       host_rows=False, oracle_layers=[])
+    perm = permuted_pages(0, n_roll * per)
+    for s in range(n_roll):
+        dp.set_pages(s, perm[s * per:(s + 1) * per], n_tok)
+    rng = np_rng(0, 7)
+    masks = [turn_drop_mask(rng, n_tok) for _ in range(n_roll)]
+    check = list(range(0, n_roll, 4))
+    j = np.arange(n_tok)
+    before = {}
+    for s in check:
+        phys = torch.from_numpy(np.asarray(dp.state.tables[s], np.int64)[j // P] * P + j % P).to("cuda")
+        before[s] = [t[l].reshape(-1, H * D)[phys].view(torch.int16).cpu().numpy()
+                     for l in (0, layers - 1) for t in (dp.k, dp.v)]
+    keep = torch.from_numpy(np.concatenate(masks)).to("cuda")
+    expected, _ = O.evict(dp.state, list(range(n_roll)), masks)
+    dp.pool.evict(list(range(n_roll)), keep, np.arange(n_roll, dtype=np.int64) * n_tok)
+    torch.cuda.synchronize()
+    for s in range(n_roll):
+        n, pos, pages = dp.pool.seq_get(s)
+        assert n == expected.lengths[s] and pos == expected.next_pos[s]
+        assert list(pages) == list(expected.tables[s])
+        assert np.array_equal(dp.table[s, :len(pages)].cpu().numpy(), pages)
+    assert dp.pool.free_pages() == len(expected.free)
+    for s in check:
+        n, _, pages = dp.pool.seq_get(s)
+        jj = np.arange(n)
+        phys = torch.from_numpy(pages.astype(np.int64)[jj // P] * P + jj % P).to("cuda")
+        kept = np.flatnonzero(masks[s])
+        got = [t[l].reshape(-1, H * D)[phys].view(torch.int16).cpu().numpy()
+               for l in (0, layers - 1) for t in (dp.k, dp.v)]
+        for a, b in zip(got, before[s]):
+            assert np.array_equal(a, b[kept]), s
+    dp.close()
 
 
 def test_gqa_evict_then_splice():

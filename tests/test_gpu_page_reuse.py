@@ -137,3 +137,46 @@ def test_page_reuse_off_is_refused_at_page_size_1():
     assert e.value.status == L.LL_EUNSUPPORTED
     dp.pool.set_page_reuse(True)
     dp.close()
+
+
+@pytest.mark.slow
+def test_compaction_128_rollouts_27_layers():
+    """The compaction workload as it is timed: 128 rollouts x 16384 tokens x
+    27 layers at page size 16, pool pages twice the rollouts', page reuse
+    off, every row kept, one call: every row moves into the lowest free
+    pages.  Page tables of all 128 rollouts and the free count against the
+    oracle with reuse off; rows of 16 rollouts on layers 0 and 26 equal the
+    rows captured before the call."""
+    need_gpu()
+    P, n_roll, n_tok, layers = 16, 128, 16384, 27
+    per = n_tok // P
+    say(f"compaction {n_roll} x {n_tok} x {layers}, page reuse off, every row kept")
+    dp = DevicePool(layers, 2 * n_roll * per, P, n_roll, per, seed=0, host_rows=False, oracle_layers=[])
+    perm = permuted_pages(0, n_roll * per)
+    for s in range(n_roll):
+        dp.set_pages(s, perm[s * per:(s + 1) * per], n_tok)
+    dp.pool.set_page_reuse(False)
+    check = list(range(0, n_roll, 8))
+    before = {}
+    j = np.arange(n_tok)
+    for s in check:
+        phys = torch.from_numpy(np.asarray(dp.state.tables[s], np.int64)[j // P] * P + j % P).to("cuda")
+        before[s] = [dp.data[l].view(-1, O.ROW)[phys].view(torch.int16).cpu().numpy() for l in (0, layers - 1)]
+    masks = [np.ones(n_tok, np.uint8)] * n_roll
+    expected, plans = _evict(dp, list(range(n_roll)), masks, reuse=False)
+    assert all(x < 0 for pl in plans for x in pl)
+    st = dp.pool.last_stats()
+    assert st.rows_moved == n_roll * n_tok and st.fresh_pages == n_roll * per
+    for s in range(n_roll):
+        n, pos, pages = dp.pool.seq_get(s)
+        assert n == expected.lengths[s] and pos == expected.next_pos[s]
+        assert list(pages) == expected.tables[s]
+        assert np.array_equal(dp.table[s, :len(pages)].cpu().numpy(), pages)
+    assert dp.pool.free_pages() == len(expected.free)
+    for s in check:
+        _, _, pages = dp.pool.seq_get(s)
+        phys = torch.from_numpy(pages.astype(np.int64)[j // P] * P + j % P).to("cuda")
+        for li, l in enumerate((0, layers - 1)):
+            got = dp.data[l].view(-1, O.ROW)[phys].view(torch.int16).cpu().numpy()
+            assert np.array_equal(got, before[s][li]), (s, l)
+    dp.close()
