@@ -4,7 +4,8 @@
 // changes).  Each layer has a K plane and a V plane of rows H x D bf16.
 //
 //  * gqa_splice_kernel: the splice's flat gather over all K and V planes (two
-//    16-byte chunks per thread), turning the RoPE band of every K head of
+//    16-byte chunks per thread in K planes, one in V planes), turning the
+//    RoPE band of every K head of
 //    downstream rows by R(Delta), plus in-place band rotation of reused pages
 //    and the page-table rewrites.
 //  * plane_evict_kernel: the eviction's copy of kept rows into fresh pages
@@ -57,15 +58,16 @@ __device__ __forceinline__ void rotate_pair(chunk_t& xa, chunk_t& xb, int w, int
 // In a K plane each thread moves one unit of two chunks of a row: unit w of
 // head h is band chunks (w, w + half) for w < half, else two chunks of the
 // head's non-band part, one from each of its halves, so each load instruction
-// of a wave reads whole 128-byte runs.  In a V plane (a plain copy) unit w is
-// chunks w and w + row_chunks / 2 of the row.
+// of a wave reads whole 128-byte runs.  In a V plane (a plain copy) each
+// thread moves one chunk.
 //
-// Blocks [0, 2 L * move_blocks_per_plane) write the rows of fresh pages, even
-// blocks in K planes and odd blocks in V planes (a K block that turns first
-// stages its table behind a barrier; V blocks in between keep the memory
-// streams busy meanwhile), the next L * rot_blocks_per_plane turn the
-// RoPE bands of reused pages' downstream rows in place (K planes only; units
-// (row, head, w < half)), and the remaining blocks rewrite page-table rows.
+// Blocks [0, 3 L * move_blocks_per_plane) write the rows of fresh pages in
+// groups of three: one block in a layer's K plane, then two in its V plane
+// (a K block that turns first stages its table behind a barrier; the V blocks
+// keep the memory streams busy meanwhile), the next L * rot_blocks_per_plane
+// turn the RoPE bands of reused pages' downstream rows in place (K planes
+// only; units (row, head, w < half)), and the remaining blocks rewrite
+// page-table rows.
 // WAVE_TASK: every wave lies inside one page task in every block range.
 // BLOCK_TASK: so does every block; a K-plane block whose task turns then
 // stages the directive's cos/sin table in LDS once.
@@ -73,16 +75,23 @@ template <int PAIRING, bool WAVE_TASK, bool BLOCK_TASK>
 __global__ __launch_bounds__(kFlatThreads) void gqa_splice_kernel(GqaSpliceLaunch a) {
   __shared__ float tab[2 * kMaxBandPairs];
   const int64_t b = blockIdx.x;
-  const int64_t move_blocks = 2 * a.move_blocks_per_plane * a.num_layers;
+  const int64_t move_blocks = 3 * a.move_blocks_per_plane * a.num_layers;
   const int64_t rot_blocks = a.rot_blocks_per_plane * a.num_layers;
   if (b >= move_blocks + rot_blocks) {
     table_write_block(a.twrites, a.tables, a.page_table, a.max_pages_per_seq, b - move_blocks - rot_blocks);
     return;
   }
   const bool in_place = b >= move_blocks;
-  const bool v_move = !in_place && (b & 1);
-  const int64_t bb = in_place ? b - move_blocks : (b >> 1);
-  const int64_t bpp = in_place ? a.rot_blocks_per_plane : a.move_blocks_per_plane;
+  // move range: groups of three blocks, one of the layer's K plane and two
+  // of its V plane (a V block covers half the chunks of a K block)
+  bool v_move = false;
+  int64_t bb = b - move_blocks;
+  if (!in_place) {
+    const int64_t grp = b / 3, m = b - grp * 3;
+    v_move = m != 0;
+    bb = v_move ? 2 * grp + m - 1 : grp;
+  }
+  const int64_t bpp = in_place ? a.rot_blocks_per_plane : (v_move ? 2 : 1) * a.move_blocks_per_plane;
   const int plane = static_cast<int>(bb / bpp) + (v_move ? a.num_layers : 0);
   const uint32_t u = static_cast<uint32_t>((bb - static_cast<int64_t>(bb / bpp) * bpp) * kFlatThreads + threadIdx.x);
   const int shift = a.page_shift;
@@ -105,10 +114,9 @@ __global__ __launch_bounds__(kFlatThreads) void gqa_splice_kernel(GqaSpliceLaunc
     col_b = col_a + half;
     band_unit = true;
   } else if (v_move) {
-    const uint32_t ru = rc >> 1;
-    row_flat = u / ru;
-    col_a = u - row_flat * ru;
-    col_b = col_a + ru;
+    row_flat = u / rc;
+    col_a = u - row_flat * rc;
+    col_b = col_a;
   } else {
     const uint32_t ru = rc >> 1;
     row_flat = u / ru;
@@ -159,7 +167,7 @@ __global__ __launch_bounds__(kFlatThreads) void gqa_splice_kernel(GqaSpliceLaunc
   chunk_t va = chunk_t{0u, 0u, 0u, 0u}, vb = va;
   if (live) {
     va = __builtin_nontemporal_load(src + col_a);
-    vb = __builtin_nontemporal_load(src + col_b);
+    if (!v_move) vb = __builtin_nontemporal_load(src + col_b);
   }
   if (k_plane) {
     const bool on = live && rot && band_unit;
@@ -181,7 +189,7 @@ __global__ __launch_bounds__(kFlatThreads) void gqa_splice_kernel(GqaSpliceLaunc
   if (live) {
     chunk_t* dst = const_cast<chunk_t*>(layer) + dst_row * rc;
     __builtin_nontemporal_store(va, dst + col_a);
-    __builtin_nontemporal_store(vb, dst + col_b);
+    if (!v_move) __builtin_nontemporal_store(vb, dst + col_b);
   }
 }
 
@@ -228,12 +236,12 @@ __global__ __launch_bounds__(kEvictThreads) void plane_evict_kernel(PlaneEvictLa
 }  // namespace
 
 hipError_t launch_gqa_splice(const GqaSpliceLaunch& a, int pairing, hipStream_t s, const Stamp& t) {
-  const int64_t grid = (2 * a.move_blocks_per_plane + a.rot_blocks_per_plane) * a.num_layers + a.n_twrites;
+  const int64_t grid = (3 * a.move_blocks_per_plane + a.rot_blocks_per_plane) * a.num_layers + a.n_twrites;
   if (grid == 0) return stamp_empty(s, t);
   const dim3 g(static_cast<unsigned>(grid)), blk(kFlatThreads);
   // one task per wave (per block) when a page's units are a whole number of
-  // waves (blocks) in both the move and the in-place ranges (K and V planes
-  // have the same units per page)
+  // waves (blocks) in both the move and the in-place ranges (a V page's
+  // chunks are twice a K page's units, so then they are too)
   const int64_t move_units = int64_t{a.row_chunks / 2} << a.page_shift;
   const int64_t band_units = (int64_t{a.heads} << (a.rot_shift - 1)) << a.page_shift;
   const bool wave_task = move_units % 64 == 0 && band_units % 64 == 0;

@@ -156,7 +156,7 @@ struct GqaSpliceLaunch {
   const SpliceTask* tasks;     // move tasks, then rotate-in-place tasks
   int64_t n_move_tasks;
   int64_t n_rot_tasks;
-  int64_t move_blocks_per_plane;  // per K and per V plane, one thread per 2 chunks
+  int64_t move_blocks_per_plane;  // per K plane (one thread per 2 chunks); a V plane takes twice as many
   int64_t rot_blocks_per_plane;   // per K plane, one thread per 2 band chunks
   const GqaDir* dirs;
   const TableWrite* twrites;
