@@ -288,6 +288,36 @@ def test_dense_mask_of_arbitrary_death_times_both_kernels():
     ctx.close()
 
 
+def test_dense_mask_at_the_smallest_pad():
+    """n_pad = 128, the smallest: rows of 16 bytes (one strip of 128 keys, one
+    active lane per wave, runs of 8 rows), death arrays written directly --
+    causal (no death), 3 distinct death times, 20 (the rebuild walk), no key
+    ever visible, every key visible on its own row only -- in one batch;
+    every bit row against the definition."""
+    L = need_gpu()
+    ctx = L.KvsMask(0)
+    n_pad = 128
+    k = np.arange(n_pad)
+    rng = np_rng(128, 0)
+    few = np.full(n_pad, n_pad, np.int64)
+    times3 = np.array([9, 64, 127])
+    pick = times3[rng.integers(0, 3, size=n_pad)]
+    few = np.where(pick > k, pick, few)
+    many = np.minimum(k + 1 + rng.integers(0, 40, size=n_pad), n_pad + 1)
+    d_host = np.stack([np.full(n_pad, n_pad, np.int64), few, many, np.full(n_pad, -1, np.int64),
+                       np.minimum(k + 1, n_pad)])
+    counts = [len(set(int(x) for j, x in enumerate(r) if j < x < n_pad)) for r in d_host]
+    assert counts[1] == 3 and counts[2] > 15
+    say(f"kvs dense n_pad={n_pad}, distinct death times {counts}")
+    death = torch.from_numpy(d_host.astype(np.int32)).cuda()
+    bits = ctx.dense_mask(death)
+    torch.cuda.synchronize()
+    got = bits.cpu().numpy().view(np.uint32)
+    for r in range(len(d_host)):
+        assert np.array_equal(got[r], K.dense_bits(K.visibility(d_host[r]))), (r, counts[r])
+    ctx.close()
+
+
 def test_death_times_of_events_spanning_several_replay_tiles():
     """Events whose keep masks cover more than 16384 rows, the replay's tile:
     the kept count carries from tile to tile.  Masks keeping 70% and 50% at
