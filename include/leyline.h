@@ -478,8 +478,10 @@ ll_status kvs_block_mask(kvs_ctx* ctx, const int32_t* death_dev, int32_t n, int6
  * n * (64 + 5 * n_pad / 8) bytes (plus 256 of alignment), reused call after
  * call: a later call on another stream waits on the device for the last one,
  * and a call that must grow the scratch first waits on the host for the last
- * call to finish.  Errors: LL_EINVAL, LL_EUNSUPPORTED, LL_ENOMEM,
- * LL_EDEVICE. */
+ * call to finish.  Errors: LL_EINVAL, LL_ENOMEM, LL_EDEVICE, and
+ * LL_EUNSUPPORTED when one launch cannot cover the mask: n * n_pad / 32
+ * blocks (n_pad <= 262144), or n * ceil(n_pad / 128) * ceil(n_pad / 8192) / 4
+ * blocks, reach 2^31. */
 ll_status kvs_dense_mask(kvs_ctx* ctx, const int32_t* death_dev, int32_t n, int64_t n_pad,
                          uint32_t* bits_dev, void* stream);
 
