@@ -118,7 +118,7 @@ KERNEL_SOURCE = {"splice_kernel": "kernels.hip", "splice_inplace_kernel": "kerne
 def kernel_source_sha(kernel: str) -> str:
     csrc = os.path.join(ROOT, "mla_paged_cache_amd", "csrc")
     src = KERNEL_SOURCE[kernel]
-    headers = {"kernels_kvs.hip": ("kvs_internal.h",),
+    headers = {"kernels_kvs.hip": ("device_common.h", "leyline_internal.h", "kvs_internal.h"),
                "kernels_rows.hip": ("device_common.h", "leyline_internal.h", "rows_internal.h")}.get(
         src, ("device_common.h", "leyline_internal.h"))
     h = hashlib.sha256()

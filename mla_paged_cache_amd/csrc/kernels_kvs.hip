@@ -31,12 +31,13 @@
 //    one of its keys dies.
 #include <algorithm>
 
+#include "device_common.h"
 #include "kvs_internal.h"
 
 namespace ll {
 namespace {
 
-typedef uint32_t word4 __attribute__((ext_vector_type(4)));
+using word4 = chunk_t;
 
 
 // Bit b of the result: byte b of the 16 is nonzero.
@@ -485,19 +486,6 @@ __device__ __forceinline__ uint32_t range_word(int32_t lo, int32_t hi, int word)
 constexpr int kDenseRun = 8;
 constexpr int kDenseHold = 4;
 
-// 16-byte store with cache policy sc0 | nt | sc1 (gfx950 bits 1, 2 and 16 of
-// a buffer instruction's cache-policy operand) through a buffer descriptor
-// based at the wave-uniform `base`, `bytes` long: lanes at or past `bytes`
-// store nothing.
-__device__ __forceinline__ void stream_store(word4 v, const void* base, uint32_t off, uint32_t bytes) {
-  const uint64_t p = reinterpret_cast<uint64_t>(base);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p));
-  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p >> 32));
-  void* ub = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
-  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(ub, 0, static_cast<int>(bytes), 0x00020000);
-  __builtin_amdgcn_raw_buffer_store_b128(v, r, static_cast<int>(off), 0, 19);
-}
-
 // One wave per (rollout, run of kDenseRun consecutive rows): the wave writes
 // whole rows, so a block's four waves fill 4 * kDenseRun consecutive rows and
 // the grid's write front moves through the mask in address order.  Lane l
@@ -615,8 +603,11 @@ __global__ __launch_bounds__(256) void kvs_dense_ev_kernel(KvsDenseLaunch a) {
       for (int h = 0; h < kDenseHold; ++h) {
         const int64_t g = g0 + h;
         if (g < groups)
-          stream_store(word4{w[h][0], w[h][1], w[h][2], w[h][3]}, out + j * row_bytes + g * 1024, lane * 16,
-                       static_cast<uint32_t>(min<int64_t>(64, strips - g * 64) * 16));
+          // sc0 | nt | sc1 through a descriptor on the wave's 1 KiB of the row:
+          // lanes past the row's last strip store nothing
+          store_chunk_policy(word4{w[h][0], w[h][1], w[h][2], w[h][3]},
+                             reinterpret_cast<const chunk_t*>(out + j * row_bytes + g * 1024), lane * 16,
+                             static_cast<uint32_t>(min<int64_t>(64, strips - g * 64) * 16));
       }
     }
   }
