@@ -378,6 +378,18 @@ ll_status ll_pool_set_splice_planner(ll_pool* pool, int32_t planner);
  * page size 1, where a page is one row). */
 ll_status ll_pool_set_page_reuse(ll_pool* pool, int32_t on);
 
+/* Library setting, no passage of the pages defines it.
+ * Work-items one dispatch of a row-moving kernel may hold.  A dispatch packet
+ * counts them in 32 bits, so 0 (the default) means 2^32 - 1.  A splice,
+ * eviction or per-row gather whose grid would hold more is issued as several
+ * dispatches in order on the same stream: the splice's in-place band
+ * rotation on its own, then ranges of whole page tasks over every layer (the
+ * page-table rewrites in the last one); the gather by ranges of whole layers.
+ * Results do not depend on the split.  A smaller limit (at least 1024) splits
+ * smaller launches the same way; it exists to exercise the split.  Applies to
+ * calls made after it.  Errors: LL_EINVAL (out of range). */
+ll_status ll_pool_set_dispatch_limit(ll_pool* pool, int64_t max_items);
+
 /* Library bookkeeping, no passage of the pages defines it.
  * Kernel timing.  `enable` = n > 0 times every n-th launch (counted from
  * this call; 1: every launch) of the row-moving kernel (kernel 0; on the

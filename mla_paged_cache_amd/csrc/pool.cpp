@@ -195,6 +195,32 @@ class DeviceGuard {
 
 }  // namespace
 
+namespace {
+
+// A dispatch packet counts its work-items in 32 bits.  A row kernel whose
+// grid would pass that (every layer of a batch that moves more than 2^32
+// 16-byte chunks in all) is issued as several dispatches in order on one
+// stream, each over a range of whole page tasks and every layer; the
+// page-table rewrites ride in the last one.
+constexpr int64_t kMaxDispatchItems = int64_t{0xFFFFFFFF};
+
+// Page tasks per dispatch: `units_per_task` units of each task in each of
+// `planes` planes, `units_per_block` units per block of `block_threads`
+// threads, `extra_blocks` more blocks in the dispatch.  At least one.
+int64_t tasks_per_dispatch(int64_t limit, int64_t units_per_task, int64_t planes, int64_t block_threads,
+                           int64_t units_per_block, int64_t extra_blocks) {
+  const int64_t blocks = limit / block_threads - extra_blocks;
+  return std::max<int64_t>(1, blocks / planes * units_per_block / units_per_task);
+}
+
+// The timing events of the part of a split launch: the first part stamps the
+// start, the last the stop.
+ll::Stamp part_stamp(const ll::Stamp& t, bool first, bool last) {
+  return ll::Stamp{first ? t.start : nullptr, last ? t.stop : nullptr};
+}
+
+}  // namespace
+
 struct ll_pool {
   ll_pool_desc desc{};       // GQA pools: kv_lora_rank 0, rope_dim = rotary_dim
   int page_shift = 0;
@@ -239,6 +265,7 @@ struct ll_pool {
   hipEvent_t lazy_ev = nullptr;
   int32_t splice_planner = LL_SPLICE_PLAN_AUTO;
   bool page_reuse = true;       // false: every new page of a rewritten sequence is fresh
+  int64_t dispatch_items = kMaxDispatchItems;  // work-items one row-kernel dispatch may hold
   char* d_direct = nullptr;     // tasks, tables and rotation tables of device-planned splices
   size_t direct_cap = 0;
   bool poisoned = false;
@@ -916,11 +943,19 @@ ll_status evict_device_plan(ll_pool* p, const int32_t* seq_ids, int32_t n, const
     a.row_chunks = static_cast<int32_t>(rc_chunks);
     a.tasks = al.tasks;
     a.n_tasks = n_tasks;
-    a.blocks_per_plane = ll::flat_blocks(n_tasks * P * rc_chunks, 1, ll::kEvictThreads);
     a.src_rows = sc.src_rows;
     a.n_twrites = 0;
-    e = ll::launch_plane_evict(a, st, t0);
-    if (e != hipSuccess) return device_fail(p, e, "plane_evict_kernel launch");
+    // ranges of whole tasks over every plane (src0 indexes src_rows globally)
+    const int64_t per = tasks_per_dispatch(p->dispatch_items, P * rc_chunks, a.num_planes, ll::kEvictThreads,
+                                           ll::kEvictThreads, 0);
+    for (int64_t k0 = 0; k0 == 0 || k0 < n_tasks; k0 += per) {  // one launch when there is no task
+      const int64_t cnt = std::min(per, n_tasks - k0);
+      a.tasks = al.tasks + k0;
+      a.n_tasks = cnt;
+      a.blocks_per_plane = ll::flat_blocks(cnt * P * rc_chunks, 1, ll::kEvictThreads);
+      e = ll::launch_plane_evict(a, st, part_stamp(t0, k0 == 0, k0 + cnt == n_tasks));
+      if (e != hipSuccess) return device_fail(p, e, "plane_evict_kernel launch");
+    }
   } else {
     ll::EvictLaunch a{};
     a.layers = reinterpret_cast<const ll::chunk_t* const*>(p->d_layers);
@@ -928,11 +963,18 @@ ll_status evict_device_plan(ll_pool* p, const int32_t* seq_ids, int32_t n, const
     a.page_shift = p->page_shift;
     a.tasks = al.tasks;
     a.n_tasks = n_tasks;
-    a.blocks_per_layer = ll::flat_blocks(n_tasks * P * rc_chunks, 1, ll::kEvictThreads);
     a.src_rows = sc.src_rows;
     a.n_twrites = 0;
-    e = ll::launch_evict_move(a, st, t0);
-    if (e != hipSuccess) return device_fail(p, e, "evict_move_kernel launch");
+    const int64_t per = tasks_per_dispatch(p->dispatch_items, P * rc_chunks, a.num_layers, ll::kEvictThreads,
+                                           ll::kEvictThreads, 0);
+    for (int64_t k0 = 0; k0 == 0 || k0 < n_tasks; k0 += per) {  // one launch when there is no task
+      const int64_t cnt = std::min(per, n_tasks - k0);
+      a.tasks = al.tasks + k0;
+      a.n_tasks = cnt;
+      a.blocks_per_layer = ll::flat_blocks(cnt * P * rc_chunks, 1, ll::kEvictThreads);
+      e = ll::launch_evict_move(a, st, part_stamp(t0, k0 == 0, k0 + cnt == n_tasks));
+      if (e != hipSuccess) return device_fail(p, e, "evict_move_kernel launch");
+    }
   }
   if ((rc = end_call(p, sg, st))) return rc;
   if ((rc = apply_evict(p, seq_ids, static_cast<size_t>(n), counts, info,
@@ -1511,8 +1553,37 @@ static ll_status splice_impl(ll_pool* p, const ll_directive* dirs, int32_t n, vo
       a.max_pages_per_seq = p->desc.max_pages_per_seq;
       a.page_table = p->desc.page_table;
       if (!noalloc && prof_pick(p, 0) && (rc = prof_begin(p, &rec, &ts))) return rc;
-      e = ll::launch_gqa_splice(a, p->desc.rope_pairing, st, ts);
-      if (e != hipSuccess) return device_fail(p, e, "gqa_splice_kernel launch");
+      const int64_t L = a.num_layers;
+      if ((3 * a.move_blocks_per_plane + a.rot_blocks_per_plane) * L + n <= p->dispatch_items / ll::kFlatThreads) {
+        e = ll::launch_gqa_splice(a, p->desc.rope_pairing, st, ts);
+        if (e != hipSuccess) return device_fail(p, e, "gqa_splice_kernel launch");
+      } else {
+        // the in-place bands on their own, then ranges of whole move tasks
+        // over the K and V planes of every layer; the table rewrites ride in
+        // the last launch
+        ll::GqaSpliceLaunch part = a;
+        if (n_rot_tasks > 0) {
+          part.move_blocks_per_plane = 0;
+          part.n_twrites = n_move_tasks == 0 ? n : 0;
+          e = ll::launch_gqa_splice(part, p->desc.rope_pairing, st, part_stamp(ts, true, n_move_tasks == 0));
+          if (e != hipSuccess) return device_fail(p, e, "gqa_splice_kernel launch");
+        }
+        const int64_t units = P * (row_chunks / 2);
+        const int64_t per = tasks_per_dispatch(p->dispatch_items, units, 3 * L, ll::kFlatThreads, ll::kFlatThreads, n);
+        for (int64_t k0 = 0; k0 < n_move_tasks; k0 += per) {
+          const int64_t cnt = std::min(per, n_move_tasks - k0);
+          const bool last = k0 + cnt == n_move_tasks;
+          part = a;
+          part.tasks = a.tasks + k0;
+          part.n_move_tasks = cnt;
+          part.n_rot_tasks = 0;
+          part.rot_blocks_per_plane = 0;
+          part.move_blocks_per_plane = ll::flat_blocks(cnt * units);
+          part.n_twrites = last ? n : 0;
+          e = ll::launch_gqa_splice(part, p->desc.rope_pairing, st, part_stamp(ts, k0 == 0 && n_rot_tasks == 0, last));
+          if (e != hipSuccess) return device_fail(p, e, "gqa_splice_kernel launch");
+        }
+      }
     } else {
       ll::SpliceLaunch a{};
       a.layers = reinterpret_cast<const ll::chunk_t* const*>(p->d_layers);
@@ -1530,8 +1601,37 @@ static ll_status splice_impl(ll_pool* p, const ll_directive* dirs, int32_t n, vo
       a.max_pages_per_seq = p->desc.max_pages_per_seq;
       a.page_table = p->desc.page_table;
       if (!noalloc && prof_pick(p, 0) && (rc = prof_begin(p, &rec, &ts))) return rc;
-      e = ll::launch_splice(a, p->desc.rope_pairing, st, ts);
-      if (e != hipSuccess) return device_fail(p, e, "splice_kernel launch");
+      const int64_t L = a.num_layers;
+      if (a.move_blocks_per_layer * L + n <= p->dispatch_items / ll::kFlatThreads) {
+        e = ll::launch_splice(a, p->desc.rope_pairing, st, ts);
+        if (e != hipSuccess) return device_fail(p, e, "splice_kernel launch");
+      } else {
+        // as above: the in-place bands, then ranges of whole move tasks over
+        // every layer, the table rewrites in the last launch
+        ll::SpliceLaunch part = a;
+        if (n_rot_tasks > 0) {
+          part.move_blocks_per_layer = 0;
+          part.n_twrites = n_move_tasks == 0 ? n : 0;
+          e = ll::launch_splice(part, p->desc.rope_pairing, st, part_stamp(ts, true, n_move_tasks == 0));
+          if (e != hipSuccess) return device_fail(p, e, "splice_inplace_kernel launch");
+        }
+        const int64_t units = P * ll::kRowChunks;
+        const int64_t per = tasks_per_dispatch(p->dispatch_items, units, L, ll::kFlatThreads,
+                                               int64_t{ll::kFlatThreads} * ll::kSpliceChunksPerThread, n);
+        for (int64_t k0 = 0; k0 < n_move_tasks; k0 += per) {
+          const int64_t cnt = std::min(per, n_move_tasks - k0);
+          const bool last = k0 + cnt == n_move_tasks;
+          part = a;
+          part.tasks = a.tasks + k0;
+          part.n_move_tasks = cnt;
+          part.n_rot_tasks = 0;
+          part.rot_blocks_per_layer = 0;
+          part.move_blocks_per_layer = ll::flat_blocks(cnt * units, ll::kSpliceChunksPerThread);
+          part.n_twrites = last ? n : 0;
+          e = ll::launch_splice(part, p->desc.rope_pairing, st, part_stamp(ts, k0 == 0 && n_rot_tasks == 0, last));
+          if (e != hipSuccess) return device_fail(p, e, "splice_kernel launch");
+        }
+      }
     }
     return LL_OK;
   };
@@ -1906,8 +2006,18 @@ ll_status ll_rope_rows(ll_pool* p, int32_t seq, int64_t row_begin, int64_t n_row
   } else {
     e = ll::launch_rope_table(t, st, ll::Stamp{ts.start, nullptr});
     if (e != hipSuccess) return device_fail(p, e, "rope_table_kernel launch");
-    e = ll::launch_rope_rows(a, p->desc.rope_pairing, st, ll::Stamp{nullptr, ts.stop});
-    if (e != hipSuccess) return device_fail(p, e, "rope_rows_kernel launch");
+    // ranges of whole planes, each within one dispatch
+    const int64_t per = std::max<int64_t>(1, p->dispatch_items / 256 / std::max<int64_t>(1, a.blocks_per_plane));
+    ll::RopeRowsLaunch part = a;
+    for (int64_t l0 = 0; l0 < a.num_planes; l0 += per) {
+      const int64_t cnt = std::min<int64_t>(per, a.num_planes - l0);
+      part.planes = a.planes + l0;
+      part.plane0 = static_cast<const ll::chunk_t*>(p->layer_ptrs[static_cast<size_t>(l0)]);
+      part.num_planes = static_cast<int32_t>(cnt);
+      part.out = a.out + l0 * a.out_plane_chunks;
+      e = ll::launch_rope_rows(part, p->desc.rope_pairing, st, ll::Stamp{nullptr, l0 + cnt == a.num_planes ? ts.stop : nullptr});
+      if (e != hipSuccess) return device_fail(p, e, "rope_rows_kernel launch");
+    }
   }
   ll_plan_stats stats{};
   stats.alg_bytes = out_dev ? L * n_rows * 2 * p->row_bytes : L * n_rows * 2 * p->band_bytes;
@@ -1969,6 +2079,16 @@ ll_status ll_pool_set_page_reuse(ll_pool* p, int32_t on) {
   if (on != 0 && on != 1) return fail(LL_EINVAL, "page reuse must be 0 or 1, not %d", on);
   if (!on && p->P == 1) return fail(LL_EUNSUPPORTED, "at page size 1 a page is one row: there is nothing to compact");
   p->page_reuse = on != 0;
+  return LL_OK;
+}
+
+ll_status ll_pool_set_dispatch_limit(ll_pool* p, int64_t max_items) {
+  if (ll_status rc = enter(p)) return rc;
+  if (max_items < 0 || max_items > kMaxDispatchItems)
+    return fail(LL_EINVAL, "the dispatch limit must lie in [0, 2^32 - 1], not %lld", (long long)max_items);
+  if (max_items != 0 && max_items < 1024)
+    return fail(LL_EINVAL, "the dispatch limit must be at least 1024 work-items, not %lld", (long long)max_items);
+  p->dispatch_items = max_items == 0 ? kMaxDispatchItems : max_items;
   return LL_OK;
 }
 

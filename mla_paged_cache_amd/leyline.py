@@ -32,7 +32,7 @@ EXPORTS = (
     "ll_last_error", "ll_status_str", "ll_pool_create_gqa",
     "kvs_ctx_create", "kvs_ctx_destroy", "kvs_death_times", "kvs_block_mask", "kvs_dense_mask",
     "ll_rope_rows", "ll_pool_set_splice_planner", "ll_pool_set_page_reuse", "ll_last_plan_bytes", "ll_seq_lengths",
-    "leyline_splice_noalloc",
+    "leyline_splice_noalloc", "ll_pool_set_dispatch_limit",
 )
 
 
@@ -140,6 +140,7 @@ def _load():
         "ll_pool_set_profiling": (i32, [vp, i32]),
         "ll_pool_set_splice_planner": (i32, [vp, i32]),
         "ll_pool_set_page_reuse": (i32, [vp, i32]),
+        "ll_pool_set_dispatch_limit": (i32, [vp, i64]),
         "ll_profile_read": (i32, [vp, i32, P(i64), P(ctypes.c_double), P(i64), P(ctypes.c_float), i64]),
         "ll_rope_rows": (i32, [vp, i32, i64, i64, vp, vp, i64, vp]),
         "kvs_ctx_create": (i32, [i32, P(vp)]),
@@ -425,6 +426,12 @@ class Pool:
         offsets.  False: every page of a rewritten sequence is fresh (the
         sequence is compacted into the lowest free pages); not on page size 1."""
         _check(_lib.ll_pool_set_page_reuse(self._h, 1 if on else 0))
+
+    def set_dispatch_limit(self, max_items: int = 0) -> None:
+        """Work-items per dispatch of a row-moving kernel (0: the packet's
+        2^32 - 1; at least 1024 otherwise).  Larger launches are issued as
+        several dispatches; results do not change."""
+        _check(_lib.ll_pool_set_dispatch_limit(self._h, int(max_items)))
 
     def set_profiling(self, enable: bool, every: int = 1) -> None:
         """Time every `every`-th launch of each profiled kernel while enabled."""

@@ -35,7 +35,7 @@ def test_header_declares_the_path_entry_points():
     for n in ("leyline_splice", "kv_evict_compact", "ll_ptable_reindex", "ll_pool_create", "ll_last_plan_bytes",
               "ll_rope_delta_table", "ll_last_error"):
         assert n in names
-    assert len(names) == 28
+    assert len(names) == 29
 
 
 # a page passage, or "no passage" for bookkeeping; the no-allocation splice
