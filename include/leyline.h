@@ -250,9 +250,11 @@ ll_status ll_pool_free_pages(const ll_pool* pool, int64_t* n_free);
  * kernel.  Both planners give the same result.  n == 0 is a no-op.  Errors:
  * LL_EINVAL (bad span, unknown or repeated sequence, r_rows (GQA: or
  * r_rows_v) NULL with r_len > 0, r_rows_v given to an MLA pool, misaligned
- * pointer or stride), LL_EUNSUPPORTED (reserved mode),
- * LL_ERANGE (n' exceeds max_pages_per_seq pages), LL_ENOMEM (too few free
- * pages), LL_EDEVICE. */
+ * pointer or stride), LL_EUNSUPPORTED (reserved mode, or a call that would
+ * write 2^32 or more 16-byte chunks into one layer: 64 GiB of rows per
+ * layer), LL_ERANGE (n' exceeds max_pages_per_seq pages), LL_ENOMEM (too
+ * few free pages), LL_EDEVICE.  A call may move more than 2^32 chunks over
+ * all its layers (ll_pool_set_dispatch_limit). */
 ll_status leyline_splice(ll_pool* pool, const ll_directive* dirs, int32_t n, void* stream);
 
 /* For callers that cannot allocate device memory: code under HIP graph
@@ -292,7 +294,9 @@ ll_status leyline_splice_noalloc(ll_pool* pool, const ll_directive* dirs, int32_
  * host bookkeeping (lengths, free set, ll_last_plan_stats) catches up when
  * the pool is next used.  Host copies of the rewritten page tables are
  * fetched from the device only when read (ll_seq_get, a later call on that
- * sequence).  Errors: LL_EINVAL, LL_ENOMEM, LL_EDEVICE. */
+ * sequence).  Errors: LL_EINVAL, LL_EUNSUPPORTED (the sequences' pages
+ * hold 2^32 or more 16-byte chunks per layer: 64 GiB of rows per layer),
+ * LL_ENOMEM, LL_EDEVICE. */
 ll_status kv_evict_compact(ll_pool* pool, const int32_t* seq_ids, int32_t n,
                            const uint8_t* keep_dev, const int64_t* keep_offsets, void* stream);
 
