@@ -339,6 +339,10 @@ int main() {
       int32_t on = 1;
       in >> on;
       std::printf("reuse %d\n", ll_pool_set_page_reuse(g.pool, on));
+    } else if (op == "limit") {
+      int64_t items = 0;
+      in >> items;
+      std::printf("limit %d\n", ll_pool_set_dispatch_limit(g.pool, items));
     } else if (op == "rope") {
       int32_t s = 0, in_place = 1;
       int64_t r0 = 0, n = 0;

@@ -223,6 +223,13 @@ class Model:
         self.reuse = bool(on)
         self.emit(f"reuse {on}", "reuse 0")
 
+    def set_limit(self):
+        """Work-items per row-kernel dispatch: the packet's own limit, or one
+        low enough that every moving call runs as many dispatches (the books
+        must not change)."""
+        items = int(self.rng.choice([0, 1024, 5000]))
+        self.emit(f"limit {items}", "limit 0")
+
     def reindex(self):
         cand = [s for s in self.live() if self.st.lengths[s] > 0]
         if not cand:
@@ -288,7 +295,7 @@ class Model:
 def test_random_operations_under_sanitizers(driver, kind, P):
     m = Model(kind, P, seed=900 + P + (50 if kind == "gqa" else 0))
     ops = [m.alloc, m.alloc, m.free, m.set_pages, m.splice, m.splice, m.splice, m.evict, m.evict, m.evict,
-           m.reindex, m.rope, m.lengths, m.set_reuse]
+           m.reindex, m.rope, m.lengths, m.set_reuse, m.set_limit]
     for i in range(260):
         ops[int(m.rng.integers(0, len(ops)))]()
         m.books()
